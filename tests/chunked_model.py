@@ -1,0 +1,130 @@
+"""Chunked (WY/UT-transform) form of the gated delta rule, in float64 numpy.
+
+Test helper only.  It is an independent, blocked restatement of the
+recurrence that the GPU kernels implement, used to show on the CPU that
+"chunked equals sequential" (against the token-by-token oracle) for the
+forward and the backward, before any kernel runs.
+
+Per chunk of L tokens with start state S (d_v x d_k):
+    gam = inclusive cumsum of g inside the chunk,  Gam = exp(gam)
+    D[t,s] = exp(gam_t - gam_s) for s <= t
+    A = strictly-lower( beta_t D[t,s] k_t.k_s ),   Tinv = (I + A)^-1
+    M = Tinv diag(beta)
+    R = V - diag(Gam) K S^T          Delta = M R
+    P = lower( D * (scale Q) K^T )
+    O = diag(Gam) (scale Q) S^T + P Delta
+    S' = Gam_L S + (diag(dec) Delta)^T K,  dec_t = exp(gam_L - gam_t)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _chunk_fwd(Q, K, V, gg, bb, S):
+    L = Q.shape[0]
+    gam = np.cumsum(gg)
+    Gam = np.exp(gam)
+    diff = gam[:, None] - gam[None, :]
+    low = np.tril(np.ones((L, L), dtype=bool))
+    D = np.where(low, np.exp(np.where(low, diff, 0.0)), 0.0)
+    KK = K @ K.T
+    A = np.tril(bb[:, None] * D * KK, -1)
+    Tinv = np.linalg.inv(np.eye(L) + A)
+    M = Tinv * bb[None, :]
+    R = V - Gam[:, None] * (K @ S.T)
+    Dl = M @ R
+    P = D * (Q @ K.T)
+    O = Gam[:, None] * (Q @ S.T) + P @ Dl
+    dec = np.exp(gam[-1] - gam)
+    Snew = Gam[-1] * S + (dec[:, None] * Dl).T @ K
+    cache = dict(gam=gam, Gam=Gam, D=D, KK=KK, A=A, Tinv=Tinv, M=M, R=R, Dl=Dl, P=P, dec=dec)
+    return O, Snew, cache
+
+
+def chunked_fwd(q, k, v, g, beta, cu, scale, S0=None, C=64):
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1:]
+    G = Hv // Hk
+    N = len(cu) - 1
+    o = np.zeros((T, Hv, dv))
+    Sf = np.zeros((N, Hv, dv, dk))
+    for n in range(N):
+        for h in range(Hv):
+            kh = h // G
+            S = np.zeros((dv, dk)) if S0 is None else S0[n, h].astype(np.float64).copy()
+            for c0 in range(cu[n], cu[n + 1], C):
+                c1 = min(c0 + C, cu[n + 1])
+                O, S, _ = _chunk_fwd(scale * q[c0:c1, kh], k[c0:c1, kh], v[c0:c1, h],
+                                     g[c0:c1, h], beta[c0:c1, h], S)
+                o[c0:c1, h] = O
+            Sf[n, h] = S
+    return o, Sf
+
+
+def chunked_bwd(q, k, v, g, beta, cu, scale, dout, S0=None, dS_final=None, C=64):
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1:]
+    G = Hv // Hk
+    N = len(cu) - 1
+    dq = np.zeros_like(q, dtype=np.float64)
+    dkk = np.zeros_like(k, dtype=np.float64)
+    dvv = np.zeros((T, Hv, dv))
+    dg = np.zeros((T, Hv))
+    dbeta = np.zeros((T, Hv))
+    dS0 = np.zeros((N, Hv, dv, dk))
+    for n in range(N):
+        for h in range(Hv):
+            kh = h // G
+            starts = list(range(cu[n], cu[n + 1], C))
+            S = np.zeros((dv, dk)) if S0 is None else S0[n, h].astype(np.float64).copy()
+            states = []
+            for c0 in starts:                       # forward: chunk-start states
+                c1 = min(c0 + C, cu[n + 1])
+                states.append(S)
+                _, S, _ = _chunk_fwd(scale * q[c0:c1, kh], k[c0:c1, kh], v[c0:c1, h],
+                                     g[c0:c1, h], beta[c0:c1, h], S)
+            dS = np.zeros((dv, dk)) if dS_final is None else dS_final[n, h].astype(np.float64).copy()
+            for ci in reversed(range(len(starts))):
+                c0 = starts[ci]
+                c1 = min(c0 + C, cu[n + 1])
+                S = states[ci]
+                Q = scale * q[c0:c1, kh]
+                K = k[c0:c1, kh]
+                bb = beta[c0:c1, h]
+                dO = dout[c0:c1, h]
+                _, _, c = _chunk_fwd(Q, K, v[c0:c1, h], g[c0:c1, h], bb, S)
+                Gam, D, A, Tinv, M, R, Dl, P, dec = (c[x] for x in
+                                                     ("Gam", "D", "A", "Tinv", "M", "R", "Dl", "P", "dec"))
+                L = c1 - c0
+                dSp = dS
+                # sequential part
+                dDl = P.T @ dO + dec[:, None] * (K @ dSp.T)
+                dR = M.T @ dDl
+                dS = Gam[-1] * dSp + dO.T @ (Gam[:, None] * Q) - (Gam[:, None] * dR).T @ K
+                # chunk-parallel part
+                dM = dDl @ R.T
+                dP = np.tril(dO @ Dl.T)
+                dTinv = np.tril(dM * bb[None, :], -1)
+                dA = np.tril(-(Tinv.T @ dTinv @ Tinv.T), -1)
+                dbe = (dM * Tinv).sum(axis=0) + (dA * D * c["KK"]).sum(axis=1)
+                dQ = Gam[:, None] * (dO @ S) + (dP * D) @ K
+                WA = dA * bb[:, None] * D
+                dK = ((dP * D).T @ Q - Gam[:, None] * (dR @ S) + dec[:, None] * (Dl @ dSp)
+                      + WA @ K + WA.T @ K)
+                dgam = np.zeros(L)
+                dgam += ((dO * (Gam[:, None] * (Q @ S.T))).sum(axis=1)
+                         - (dR * (Gam[:, None] * (K @ S.T))).sum(axis=1))
+                E = dP * P
+                dgam += E.sum(axis=1) - E.sum(axis=0)
+                EA = dA * A
+                dgam += EA.sum(axis=1) - EA.sum(axis=0)
+                z = dec * ((Dl @ dSp) * K).sum(axis=1)
+                dgam -= z
+                dgam[-1] += z.sum() + Gam[-1] * (dSp * S).sum()
+                dg[c0:c1, h] = np.cumsum(dgam[::-1])[::-1]
+                dbeta[c0:c1, h] = dbe
+                dvv[c0:c1, h] = dR
+                dq[c0:c1, kh] += scale * dQ
+                dkk[c0:c1, kh] += dK
+            dS0[n, h] = dS
+    return dq, dkk, dvv, dg, dbeta, dS0

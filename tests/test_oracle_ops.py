@@ -1,0 +1,223 @@
+"""Pins for the oracle's conv, gate and gated norm, and the composed layer
+(CPU only): hand-worked values, textbook/library routines, invariants and
+finite differences."""
+import os
+
+import numpy as np
+import pytest
+import scipy.special as sp
+import torch
+import torch.nn.functional as F
+
+import oracle
+from gated_deltanet_layer_causal_amd import inputs as gi
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ conv
+def test_conv_hand_worked():
+    rows = {}
+    for line in open(os.path.join(GOLD, "conv_hand_5tok.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            parts = line.split()
+            rows[parts[0]] = np.array([float(x) for x in parts[1:]])
+    x = np.arange(1.0, 6.0).reshape(5, 1)
+    w = np.array([[0.5, 0.0, -1.0, 2.0]])
+    for case, cu in (("single", [0, 5]), ("split", [0, 2, 5])):
+        y = oracle.conv_fwd(x, w, cu, 0, 1)
+        u = rows[case]
+        np.testing.assert_allclose(y[:, 0], u * sp.expit(u), rtol=1e-15)
+
+
+def test_conv_matches_numpy_convolve_and_l2():
+    """I8: per channel, the pre-activation equals numpy.convolve(x_c, w_c[::-1])[:L]
+    restarted at every sequence; q/k heads are then unit-normalised."""
+    rng = np.random.default_rng(0)
+    hk, hv, d = 2, 3, 4
+    C = 2 * hk * d + hv * d
+    lens = [9, 2, 14]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = cu[-1]
+    x = rng.standard_normal((T, C))
+    w = 0.25 * rng.standard_normal((C, 4))
+    y = oracle.conv_fwd(x, w, cu, 2 * hk * d, d, eps=1e-6)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        u = np.stack([np.convolve(x[a:b, c], w[c, ::-1])[: b - a] for c in range(C)], axis=1)
+        act = u * sp.expit(u)
+        qk = act[:, : 2 * hk * d].reshape(b - a, 2 * hk, d)
+        nrm = np.sqrt((np.linalg.norm(qk, axis=-1, keepdims=True)) ** 2 + 1e-6)
+        ref = np.concatenate([(qk / nrm).reshape(b - a, -1), act[:, 2 * hk * d:]], axis=1)
+        np.testing.assert_allclose(y[a:b], ref, rtol=1e-12, atol=1e-14)
+    # q/k heads have unit norm up to eps
+    nr = np.linalg.norm(y[:, : 2 * hk * d].reshape(T, 2 * hk, d), axis=-1)
+    assert np.all(nr <= 1.0) and np.all(nr > 0.9)
+
+
+def test_conv_permutation_equivariant_over_heads():
+    """Permuting whole heads of the input permutes the output the same way
+    (the channel layout is a permutation only)."""
+    rng = np.random.default_rng(1)
+    hk, d = 3, 4
+    C = 2 * hk * d
+    x = rng.standard_normal((11, C))
+    w = rng.standard_normal((C, 4))
+    perm_heads = np.array([2, 0, 1, 4, 5, 3])
+    perm = (perm_heads[:, None] * d + np.arange(d)).reshape(-1)
+    y = oracle.conv_fwd(x, w, [0, 11], C, d)
+    yp = oracle.conv_fwd(x[:, perm], w[perm], [0, 11], C, d)
+    np.testing.assert_array_equal(yp, y[:, perm])
+
+
+# ------------------------------------------------------------------ gate
+def test_gate_closed_form():
+    """g = -exp(A_log) softplus(a + dt_bias) with A_log = log A (Megatron page,
+    review: A_log stores log(A)); beta = sigmoid(b)."""
+    rng = np.random.default_rng(2)
+    T, H = 50, 5
+    a = 4 * rng.standard_normal((T, H))
+    a[0, 0], a[1, 0] = 60.0, -60.0
+    b = 3 * rng.standard_normal((T, H))
+    A = rng.uniform(1, 16, H)
+    dt = rng.standard_normal(H)
+    g, beta = oracle.gate_fwd(a, b, np.log(A), dt)
+    np.testing.assert_allclose(g, -A * np.logaddexp(0.0, a + dt), rtol=1e-14)
+    np.testing.assert_allclose(beta, sp.expit(b), rtol=1e-15)
+    assert np.all(g < 0)
+
+
+def test_gate_backward_finite_differences():
+    rng = np.random.default_rng(3)
+    T, H = 7, 3
+    a, b = rng.standard_normal((T, H)), rng.standard_normal((T, H))
+    Al, dt = np.log(rng.uniform(1, 16, H)), rng.standard_normal(H)
+    dg, dbeta = rng.standard_normal((T, H)), rng.standard_normal((T, H))
+    da, db, dAl, ddt = oracle.gate_bwd(a, b, Al, dt, dg, dbeta)
+
+    def L(a_, b_, Al_, dt_):
+        g, be = oracle.gate_fwd(a_, b_, Al_, dt_)
+        return float((g * dg).sum() + (be * dbeta).sum())
+
+    h = 1e-6
+    for name, grad, idx in (("a", da, 0), ("b", db, 1), ("A_log", dAl, 2), ("dt", ddt, 3)):
+        base = [a, b, Al, dt]
+        num = np.zeros_like(grad)
+        for i in np.ndindex(grad.shape):
+            p, m = [x.copy() for x in base], [x.copy() for x in base]
+            p[idx][i] += h
+            m[idx][i] -= h
+            num[i] = (L(*p) - L(*m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-7, atol=1e-8, err_msg=name)
+
+
+# ------------------------------------------------------------------ gated norm
+@pytest.mark.parametrize("act", [oracle.ACT_SILU, oracle.ACT_SIGMOID])
+def test_norm_matches_torch_rms_norm(act):
+    """Zero-centred RMSNorm (Megatron page: --apply-layernorm-1p; prime-rl page:
+    ZeroCenteredRMSNorm) scales by (1 + w); the gate's activation is a kwarg
+    (prime-rl page: "silu"/"sigmoid")."""
+    rng = np.random.default_rng(4)
+    o = rng.standard_normal((13, 3, 16))
+    z = rng.standard_normal((13, 3, 16))
+    w = 0.1 * rng.standard_normal(16)
+    y = oracle.norm_fwd(o, z, w, act)
+    ot = torch.from_numpy(o)
+    ref = F.rms_norm(ot, (16,), weight=torch.from_numpy(1.0 + w), eps=1e-6)
+    zt = torch.from_numpy(z)
+    ref = ref * (F.silu(zt) if act == oracle.ACT_SILU else torch.sigmoid(zt))
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_norm_plain_rmsnorm_and_scale_invariance():
+    rng = np.random.default_rng(5)
+    o = rng.standard_normal((20, 32))
+    z = np.full_like(o, 800.0)           # sigmoid(z) == 1 in double
+    y = oracle.norm_fwd(o, z, np.zeros(32), oracle.ACT_SIGMOID, eps=0.0)
+    rms = np.sqrt((o ** 2).mean(axis=1, keepdims=True))
+    np.testing.assert_allclose(y, o / rms, rtol=1e-14)
+    y2 = oracle.norm_fwd(7.5 * o, z, np.zeros(32), oracle.ACT_SIGMOID, eps=0.0)
+    np.testing.assert_allclose(y2, y, rtol=1e-14)
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_SILU, oracle.ACT_SIGMOID])
+def test_norm_backward_finite_differences(act):
+    rng = np.random.default_rng(6)
+    o, z = rng.standard_normal((4, 6)), rng.standard_normal((4, 6))
+    w, dy = 0.1 * rng.standard_normal(6), rng.standard_normal((4, 6))
+    do, dz, dw = oracle.norm_bwd(o, z, w, dy, act)
+
+    def L(o_, z_, w_):
+        return float((oracle.norm_fwd(o_, z_, w_, act) * dy).sum())
+
+    h = 1e-6
+    for name, grad, idx in (("o", do, 0), ("z", dz, 1), ("w", dw, 2)):
+        base = [o, z, w]
+        num = np.zeros_like(grad)
+        for i in np.ndindex(grad.shape):
+            p, m = [x.copy() for x in base], [x.copy() for x in base]
+            p[idx][i] += h
+            m[idx][i] -= h
+            num[i] = (L(*p) - L(*m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-7, atol=1e-8, err_msg=name)
+
+
+# ------------------------------------------------------------------ conv backward
+def test_conv_backward_finite_differences():
+    rng = np.random.default_rng(7)
+    hk, hv, d = 1, 1, 3
+    C = 2 * hk * d + hv * d
+    lens = [5, 3]
+    cu = np.array([0, 5, 8], dtype=np.int32)
+    x = rng.standard_normal((8, C))
+    w = 0.5 * rng.standard_normal((C, 4))
+    dy = rng.standard_normal((8, C))
+    dx, dw = oracle.conv_bwd(x, w, cu, 2 * hk * d, d, dy)
+
+    def L(x_, w_):
+        return float((oracle.conv_fwd(x_, w_, cu, 2 * hk * d, d) * dy).sum())
+
+    h = 1e-6
+    for name, grad, idx in (("x", dx, 0), ("w", dw, 1)):
+        base = [x, w]
+        num = np.zeros_like(grad)
+        for i in np.ndindex(grad.shape):
+            p, m = [a.copy() for a in base], [a.copy() for a in base]
+            p[idx][i] += h
+            m[idx][i] -= h
+            num[i] = (L(*p) - L(*m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-7, atol=1e-8, err_msg=name)
+
+
+# ------------------------------------------------------------------ whole layer
+def test_layer_backward_finite_differences():
+    """Directional central differences through conv -> gate -> delta -> norm
+    for every layer input (x, w_conv, a, b, A_log, dt_bias, z, w_norm, S0)."""
+    w = gi.Workload("fd", 10, 1, 2, 4, "fp32", seq="varlen", init_state=True, final_state=True,
+                    seed=5)
+    inp = gi.make_inputs(w, seqlens=[6, 4], A_range=(0.05, 0.5))
+    inp = {k: (v.astype(np.float64) if isinstance(v, np.ndarray) and v.dtype == np.float32 else v)
+           for k, v in inp.items()}
+    hk, hv, d, sc = 1, 2, 4, 0.5
+    fwd = oracle.layer_fwd(inp, hk, hv, d, sc)
+    bwd = oracle.layer_bwd(inp, fwd, hk, hv, d, sc)
+
+    def L(key, val):
+        x = dict(inp)
+        x[key] = val
+        f = oracle.layer_fwd(x, hk, hv, d, sc)
+        return float((f["out"] * inp["dy"]).sum() + (f["S_final"] * inp["dS_T"]).sum())
+
+    rng = np.random.default_rng(8)
+    pairs = (("x", "dx"), ("w_conv", "dw_conv"), ("a", "da"), ("b", "db"), ("A_log", "dA_log"),
+             ("dt_bias", "ddt_bias"), ("z", "dz"), ("w_norm", "dw_norm"), ("S0", "dS0"))
+    # z's gradient is dz from the norm; layer_bwd reports it under "dz"
+    for key, gkey in pairs:
+        x0 = inp[key]
+        for _ in range(2):
+            u = rng.standard_normal(x0.shape)
+            h = 1e-6
+            num = (L(key, x0 + h * u) - L(key, x0 - h * u)) / (2 * h)
+            ana = float((bwd[gkey] * u).sum())
+            assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (key, num, ana)
