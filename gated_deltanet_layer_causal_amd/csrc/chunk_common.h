@@ -1,0 +1,162 @@
+// Shared pieces of the chunked gated delta rule kernels (forward and backward).
+//
+// Chunked (WY/UT) form used by every kernel.  For a chunk of L <= 64 tokens of
+// one sequence and one value head, with S the d_v x d_k state entering it:
+//   gam_t = g_1 + ... + g_t (inside the chunk),  Gam_t = exp(gam_t)
+//   D[t,s] = exp(gam_t - gam_s) for s <= t
+//   A[t,s] = beta_t D[t,s] (k_t . k_s) for s < t,   Tinv = (I + A)^-1
+//   M = Tinv diag(beta)
+//   R = V - diag(Gam) K S^T,   Delta = M R               (the delta-rule writes)
+//   P = D o (scale Q K^T)  (s <= t)
+//   O = diag(Gam) scale Q S^T + P Delta
+//   S_next = Gam_L S + (diag(dec) Delta)^T K,  dec_t = exp(gam_L - gam_t)
+// which reproduces the token-by-token recurrence exactly in exact arithmetic.
+// Only differences gam_t - gam_s with s <= t are exponentiated, so with
+// g <= 0 every exponential is <= 1 and never overflows.
+#pragma once
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+
+template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };
+
+// Workspace layout (byte offsets; every region 256-byte aligned).
+struct ChunkLayout {
+  int64_t nt_max;     // upper bound on the number of chunks: T/64 + n_seq
+  size_t seq_off;     // int32 [n_seq + 1]: first chunk of each sequence; [n_seq] = #chunks
+  size_t gcum;        // fp32 [T][hv]: in-chunk cumulative gate
+  size_t mw, pw;      // T [nt_max][hv][64][64]: M = Tinv diag(beta), P
+  size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
+  size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
+  size_t total_fwd, total_bwd;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline ChunkLayout chunk_layout(const gdn_shape& s) {
+  ChunkLayout L;
+  const size_t es = s.dtype == GDN_BF16 ? 2 : 4;
+  const int64_t T = s.total_tokens;
+  L.nt_max = T / CHUNK + s.n_seq;
+  size_t off = 0;
+  L.seq_off = off; off = align256(off + sizeof(int32_t) * (size_t)(s.n_seq + 1));
+  L.gcum = off; off = align256(off + sizeof(float) * (size_t)T * s.hv);
+  L.mw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
+  L.pw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
+  L.total_fwd = off;
+  L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
+  L.dh = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
+  L.rw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
+  L.dlw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
+  L.ddw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
+  L.total_bwd = off;
+  return L;
+}
+
+// Largest n in [0, n_seq) with off[n] <= c (off non-decreasing).
+__device__ __forceinline__ int upper_index(const int32_t* off, int n_seq, int64_t c) {
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)off[mid] <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Chunk c -> (first token, length) using the per-sequence chunk offsets.
+__device__ __forceinline__ void chunk_span(const int32_t* seq_off, const int32_t* cu, int n_seq,
+                                           int64_t c, int64_t& t0, int& L) {
+  const int n = upper_index(seq_off, n_seq, c);
+  t0 = (int64_t)cu[n] + (int64_t)CHUNK * (c - seq_off[n]);
+  const int64_t rem = (int64_t)cu[n + 1] - t0;
+  L = rem < CHUNK ? (int)rem : CHUNK;
+}
+
+// Stage rows [0, 64) x [0, W) of a token-major tensor into LDS (row stride ld_s),
+// zero-filling rows >= L.  Source row r is at src + r * ld_g.
+template <typename T, int W>
+__device__ __forceinline__ void stage_rows(T* dst, int ld_s, const T* src, int64_t ld_g, int L,
+                                           int tid) {
+  constexpr int G8 = W / 8;
+  for (int i = tid; i < CHUNK * G8; i += 256) {
+    const int r = i / G8, c8 = (i % G8) * 8;
+    f8 v;
+    if (r < L) v = load8(src + (int64_t)r * ld_g + c8);
+    else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v.v[j] = 0.f;
+    }
+    store8(dst + r * ld_s + c8, v);
+  }
+}
+
+// (I + A)^-1 for strictly lower-triangular A (64 x 64, fp32 in LDS, row
+// stride 68), written to Ti.  Blocked: the four 16 x 16 diagonal blocks are
+// inverted by forward substitution (one lane per column), then block
+// (i, j), i > j, is  -Dinv_i * sum_{m=j}^{i-1} A_im Ti_mj,  level by level.
+// Uses X (16 x 17 fp32) as scratch.  Ends with a barrier.
+__device__ __forceinline__ void invert_unit_lower(const float (*A)[68], float (*Ti)[68],
+                                                  float (*X)[17], int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  // zero the strictly upper block triangle
+  for (int i = tid; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;
+    if ((c >> 4) > (r >> 4)) Ti[r][c] = 0.f;
+  }
+  if (lane < 16) {
+    const int b = wave * 16, j = lane;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float acc = (t == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < t; ++s) acc -= A[b + t][b + s] * x[s];
+      x[t] = acc;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) Ti[b + t][b + j] = x[t];
+  }
+  __syncthreads();
+  const int r = tid >> 4, cc = tid & 15;
+  for (int lv = 1; lv < 4; ++lv) {
+    for (int i = lv; i < 4; ++i) {
+      const int j = i - lv;
+      float acc = 0.f;
+      for (int m = j; m < i; ++m) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += A[16 * i + r][16 * m + u] * Ti[16 * m + u][16 * j + cc];
+      }
+      X[r][cc] = acc;
+      __syncthreads();
+      float out = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) out += Ti[16 * i + r][16 * i + u] * X[u][cc];
+      Ti[16 * i + r][16 * j + cc] = -out;
+      __syncthreads();
+    }
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Inclusive suffix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_suffix_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += y;
+  }
+  return x;
+}
+
+}  // namespace gdn

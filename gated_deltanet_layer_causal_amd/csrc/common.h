@@ -1,0 +1,179 @@
+// Device-side helpers shared by the libgdn kernels (gfx950 / CDNA4).
+//
+// Storage types: bf16 (__bf16) or fp32 for token tensors; all arithmetic is
+// fp32.  Matrix products use MFMA: v_mfma_f32_16x16x32_bf16 for bf16 operands
+// and v_mfma_f32_16x16x4_f32 for fp32 operands (true fp32 arithmetic).
+//
+// MFMA 16x16 output layout (both instructions): lane l of the 64-wide wave
+// holds C[4*(l/16) + i][l%16], i = 0..3.  Operand A is read row = l%16,
+// operand B column = l%16; the K index a lane supplies is k0 + 8*(l/16) + j
+// (bf16, j = 0..7) or k0 + l/16 (fp32).  A and B always use the same K map,
+// so the contraction is exact whatever order the hardware sums in.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// ---- 8-element vector load/store of a storage type, converted to/from fp32
+struct f8 { float v[8]; };
+
+__device__ __forceinline__ f8 load8(const bf16* p) {
+  uint4 raw = *reinterpret_cast<const uint4*>(p);
+  f8 r;
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.v[2 * i] = __uint_as_float(w[i] << 16);
+    r.v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+  return r;
+}
+__device__ __forceinline__ f8 load8(const float* p) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  f8 r;
+  r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+  r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+  return r;
+}
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  bf16 x = (bf16)a, y = (bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ __forceinline__ void store8(bf16* p, const f8& r) {
+  uint4 raw;
+  raw.x = pack2_bf16(r.v[0], r.v[1]);
+  raw.y = pack2_bf16(r.v[2], r.v[3]);
+  raw.z = pack2_bf16(r.v[4], r.v[5]);
+  raw.w = pack2_bf16(r.v[6], r.v[7]);
+  *reinterpret_cast<uint4*>(p) = raw;
+}
+__device__ __forceinline__ void store8(float* p, const f8& r) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(r.v[0], r.v[1], r.v[2], r.v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(r.v[4], r.v[5], r.v[6], r.v[7]);
+}
+// 4 consecutive elements (used to write an MFMA column strip transposed)
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  uint2 raw;
+  raw.x = pack2_bf16(a, b);
+  raw.y = pack2_bf16(c, d);
+  *reinterpret_cast<uint2*>(p) = raw;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// ---- MFMA operand fragments -------------------------------------------------
+// Mma<T>::frag is the per-lane operand of one MFMA step over KS values of K.
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KS = 32;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static floatx4 mma(const frag& a, const frag& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // Element (r, k0 + kk) for this lane's K slots, r fixed, contiguous K.
+  template <typename S>
+  __device__ __forceinline__ static frag kc(const S* row, int k0, int lane) {
+    const S* p = row + k0 + 8 * (lane >> 4);
+    if constexpr (sizeof(S) == 2) {
+      return *reinterpret_cast<const frag*>(p);
+    } else {
+      f8 v = load8(p);
+      frag f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = (bf16)v.v[j];
+      return f;
+    }
+  }
+  // K strided by ld: element (k) at col[k * ld].
+  template <typename S>
+  __device__ __forceinline__ static frag ks(const S* col, int ld, int k0, int lane) {
+    const S* p = col + (int64_t)(k0 + 8 * (lane >> 4)) * ld;
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (bf16)to_f(p[(int64_t)j * ld]);
+    return f;
+  }
+  // Same, with a per-K scale factor sc[k] applied before rounding.
+  template <typename S>
+  __device__ __forceinline__ static frag kc_scaled(const S* row, int k0, int lane, const float* sc) {
+    const int kb = k0 + 8 * (lane >> 4);
+    f8 v = load8(row + kb);
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (bf16)(v.v[j] * sc[kb + j]);
+    return f;
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KS = 4;
+  typedef float frag;
+  __device__ __forceinline__ static floatx4 mma(const frag& a, const frag& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  template <typename S>
+  __device__ __forceinline__ static frag kc(const S* row, int k0, int lane) {
+    return to_f(row[k0 + (lane >> 4)]);
+  }
+  template <typename S>
+  __device__ __forceinline__ static frag ks(const S* col, int ld, int k0, int lane) {
+    return to_f(col[(int64_t)(k0 + (lane >> 4)) * ld]);
+  }
+  template <typename S>
+  __device__ __forceinline__ static frag kc_scaled(const S* row, int k0, int lane, const float* sc) {
+    const int k = k0 + (lane >> 4);
+    return to_f(row[k]) * sc[k];
+  }
+};
+
+// One 16x16 output tile: acc += A[m0:m0+16, 0:K] * B[0:K, n0:n0+16].
+// A is given as row pointers (KC: row-major, K contiguous) or column-strided
+// (KS: element (m,k) at A[k*lda + m]); likewise B (KC: element (k,n) at
+// B[n*ldb + k]; KS: at B[k*ldb + n]).
+template <typename MT, bool A_KC, bool B_KC, typename SA, typename SB>
+__device__ __forceinline__ floatx4 tile_mma(floatx4 acc, const SA* A, int lda, const SB* B, int ldb,
+                                            int m0, int n0, int K, int lane) {
+  typedef Mma<MT> M;
+  const int r = lane & 15;
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += M::KS) {
+    typename M::frag a, b;
+    if constexpr (A_KC) a = M::kc(A + (int64_t)(m0 + r) * lda, k0, lane);
+    else a = M::ks(A + (m0 + r), lda, k0, lane);
+    if constexpr (B_KC) b = M::kc(B + (int64_t)(n0 + r) * ldb, k0, lane);
+    else b = M::ks(B + (n0 + r), ldb, k0, lane);
+    acc = M::mma(a, b, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// Sum over the 16 lanes that share (l / 16) ... i.e. lanes with equal l>>4
+// hold the same output rows; reduce a per-lane value over the 16 columns.
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,64 @@
+// Internal launchers (host side).  The exported C entry points in api.hip
+// validate arguments and then call these; launchers assume valid input.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/libgdn.h"
+
+namespace gdn {
+
+// out[i] = sum over p (in order) of partials[p * width + i]
+hipError_t launch_reduce_partials(const float* partials, int64_t n_part, int64_t width, float* out,
+                                  hipStream_t st);
+
+constexpr int CONV_TT = 64;      // tokens per conv run (one wave)
+constexpr int CONV_RUNS_PER_BLOCK = 4;
+constexpr int CHUNK = 64;
+
+inline int64_t conv_runs(int64_t T) { return (T + CONV_TT - 1) / CONV_TT; }
+inline int64_t conv_partials(int64_t T) {
+  return (conv_runs(T) + CONV_RUNS_PER_BLOCK - 1) / CONV_RUNS_PER_BLOCK;
+}
+
+hipError_t launch_conv_fwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
+                           const int32_t* cu, int l2, float eps, void* y, int64_t ldy,
+                           hipStream_t st);
+hipError_t launch_conv_bwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
+                           const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
+                           void* dx, int64_t lddx, float* dw, float* partials, hipStream_t st);
+
+constexpr int GATE_TB = 256;     // tokens per gate-backward block
+inline int64_t gate_partials(int64_t T) { return (T + GATE_TB - 1) / GATE_TB; }
+hipError_t launch_gate_fwd(const gdn_shape& s, const void* a, const void* b, const float* A_log,
+                           const float* dt_bias, float* g, float* beta, hipStream_t st);
+hipError_t launch_gate_bwd(const gdn_shape& s, const void* a, const void* b, const float* A_log,
+                           const float* dt_bias, const float* dg, const float* dbeta, void* da,
+                           void* db, float* dA_log, float* ddt_bias, float* partials,
+                           hipStream_t st);
+
+constexpr int NORM_BLOCKS_MAX = 1024;
+int64_t norm_blocks(int64_t rows, int32_t dv);
+hipError_t launch_norm_fwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
+                           const float* w, float eps, int act, void* y, hipStream_t st);
+hipError_t launch_norm_bwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
+                           const float* w, float eps, int act, const void* dy, void* dout,
+                           void* dz, float* dw, float* partials, hipStream_t st);
+
+// Chunked gated delta rule.
+struct ChunkWs;  // layout of the chunk workspace (chunk.hip)
+size_t chunk_fwd_ws_bytes(const gdn_shape& s);
+size_t chunk_bwd_ws_bytes(const gdn_shape& s);
+hipError_t launch_chunk_fwd(const gdn_shape& s, const void* q, const void* k, const void* v,
+                            int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
+                            const float* beta, float scale, const float* S0, float* S_final,
+                            const int32_t* cu, void* o, void* ws, hipStream_t st);
+hipError_t launch_chunk_bwd(const gdn_shape& s, const void* q, const void* k, const void* v,
+                            int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
+                            const float* beta, float scale, const float* S0, const int32_t* cu,
+                            const void* dout, const float* dS_final, void* dq, void* dk, void* dv,
+                            int64_t lddq, int64_t lddk, int64_t lddv, float* dg, float* dbeta,
+                            float* dS0, void* ws, hipStream_t st);
+
+}  // namespace gdn

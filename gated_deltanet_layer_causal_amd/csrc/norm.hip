@@ -1,0 +1,170 @@
+// Gated zero-centred RMSNorm: y = o * rsqrt(mean(o^2) + eps) * (1 + w) * act(z).
+// HBM-bound.  A row of dv elements is owned by dv/8 adjacent lanes (8
+// elements = one 16-byte bf16 vector each); the row's sums are shuffle
+// reductions over those lanes.  The backward's dw column sums are
+// accumulated per lane, combined per block in LDS in a fixed order, and the
+// per-block partials are added by a second kernel in block order.
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ float act_f(int act, float z, float sg) { return act == 0 ? z * sg : sg; }
+__device__ __forceinline__ float act_df(int act, float z, float sg) {
+  return act == 0 ? sg * (1.f + z * (1.f - sg)) : sg * (1.f - sg);
+}
+
+template <typename T, int DV>
+__global__ void __launch_bounds__(256) norm_fwd_kernel(const T* __restrict__ o,
+                                                       const T* __restrict__ z,
+                                                       const float* __restrict__ w, int64_t rows,
+                                                       float eps, int act, T* __restrict__ y) {
+  constexpr int LPR = DV / 8;
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int seg = (int)(gt % LPR);
+  float wp[8];
+  {
+    f8 wv = load8(w + seg * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wp[i] = 1.f + wv.v[i];
+  }
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x / LPR;
+  for (int64_t r = gt / LPR; r < rows; r += stride) {
+    f8 ov = load8(o + r * DV + seg * 8);
+    f8 zv = load8(z + r * DV + seg * 8);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += ov.v[i] * ov.v[i];
+    ss = row_sum<LPR>(ss);
+    const float rho = rsqrtf(ss * (1.f / DV) + eps);
+    f8 out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float sg = sigmoidf_(zv.v[i]);
+      out.v[i] = ov.v[i] * rho * wp[i] * act_f(act, zv.v[i], sg);
+    }
+    store8(y + r * DV + seg * 8, out);
+  }
+}
+
+template <typename T, int DV>
+__global__ void __launch_bounds__(256) norm_bwd_kernel(
+    const T* __restrict__ o, const T* __restrict__ z, const float* __restrict__ w, int64_t rows,
+    float eps, int act, const T* __restrict__ dy, T* __restrict__ dout, T* __restrict__ dz,
+    float* __restrict__ partials) {
+  constexpr int LPR = DV / 8;
+  __shared__ float red[256][9];
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int seg = (int)(gt % LPR);
+  float wp[8], dwa[8];
+  {
+    f8 wv = load8(w + seg * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wp[i] = 1.f + wv.v[i];
+      dwa[i] = 0.f;
+    }
+  }
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x / LPR;
+  for (int64_t r = gt / LPR; r < rows; r += stride) {
+    f8 ov = load8(o + r * DV + seg * 8);
+    f8 zv = load8(z + r * DV + seg * 8);
+    f8 dyv = load8(dy + r * DV + seg * 8);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += ov.v[i] * ov.v[i];
+    ss = row_sum<LPR>(ss);
+    const float rho = rsqrtf(ss * (1.f / DV) + eps);
+    float n[8], dn[8], sg[8];
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sg[i] = sigmoidf_(zv.v[i]);
+      n[i] = ov.v[i] * rho;
+      float av = act_f(act, zv.v[i], sg[i]);
+      dn[i] = dyv.v[i] * wp[i] * av;
+      m += dn[i] * n[i];
+      dwa[i] += dyv.v[i] * n[i] * av;
+    }
+    m = row_sum<LPR>(m) * (1.f / DV);
+    f8 go, gz;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      go.v[i] = rho * (dn[i] - n[i] * m);
+      gz.v[i] = dyv.v[i] * n[i] * wp[i] * act_df(act, zv.v[i], sg[i]);
+    }
+    store8(dout + r * DV + seg * 8, go);
+    store8(dz + r * DV + seg * 8, gz);
+  }
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[tid][i] = dwa[i];
+  __syncthreads();
+  // column c = seg*8 + i is held by threads tid with tid % LPR == seg
+  if (tid < DV) {
+    const int sg_ = tid / 8, i = tid % 8;
+    float acc = 0.f;
+    for (int t = sg_; t < 256; t += LPR) acc += red[t][i];
+    partials[(int64_t)blockIdx.x * DV + tid] = acc;
+  }
+}
+
+int64_t norm_blocks(int64_t rows, int32_t dv) {
+  const int64_t rows_per_block = 256 / (dv / 8);
+  int64_t b = (rows + rows_per_block - 1) / rows_per_block;
+  if (b > NORM_BLOCKS_MAX) b = NORM_BLOCKS_MAX;
+  return b < 1 ? 1 : b;
+}
+
+template <typename T>
+static hipError_t norm_fwd_t(int64_t rows, int32_t dv, const void* o, const void* z, const float* w,
+                             float eps, int act, void* y, hipStream_t st) {
+  const unsigned nb = (unsigned)norm_blocks(rows, dv);
+  if (dv == 128)
+    hipLaunchKernelGGL((norm_fwd_kernel<T, 128>), dim3(nb), dim3(256), 0, st, (const T*)o,
+                       (const T*)z, w, rows, eps, act, (T*)y);
+  else
+    hipLaunchKernelGGL((norm_fwd_kernel<T, 32>), dim3(nb), dim3(256), 0, st, (const T*)o,
+                       (const T*)z, w, rows, eps, act, (T*)y);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t norm_bwd_t(int64_t rows, int32_t dv, const void* o, const void* z, const float* w,
+                             float eps, int act, const void* dy, void* dout, void* dz, float* dw,
+                             float* partials, hipStream_t st) {
+  const int64_t nb = norm_blocks(rows, dv);
+  if (dv == 128)
+    hipLaunchKernelGGL((norm_bwd_kernel<T, 128>), dim3((unsigned)nb), dim3(256), 0, st,
+                       (const T*)o, (const T*)z, w, rows, eps, act, (const T*)dy, (T*)dout,
+                       (T*)dz, partials);
+  else
+    hipLaunchKernelGGL((norm_bwd_kernel<T, 32>), dim3((unsigned)nb), dim3(256), 0, st,
+                       (const T*)o, (const T*)z, w, rows, eps, act, (const T*)dy, (T*)dout,
+                       (T*)dz, partials);
+  return launch_reduce_partials(partials, nb, dv, dw, st);
+}
+
+hipError_t launch_norm_fwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
+                           const float* w, float eps, int act, void* y, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  return dt == GDN_BF16 ? norm_fwd_t<bf16>(rows, dv, o, z, w, eps, act, y, st)
+                        : norm_fwd_t<float>(rows, dv, o, z, w, eps, act, y, st);
+}
+
+hipError_t launch_norm_bwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
+                           const float* w, float eps, int act, const void* dy, void* dout,
+                           void* dz, float* dw, float* partials, hipStream_t st) {
+  return dt == GDN_BF16
+             ? norm_bwd_t<bf16>(rows, dv, o, z, w, eps, act, dy, dout, dz, dw, partials, st)
+             : norm_bwd_t<float>(rows, dv, o, z, w, eps, act, dy, dout, dz, dw, partials, st);
+}
+
+}  // namespace gdn

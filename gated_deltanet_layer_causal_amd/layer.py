@@ -1,0 +1,119 @@
+"""Gated DeltaNet layer core on top of libgdn: conv -> gate -> chunked gated
+delta rule -> gated norm, forward and backward.
+
+This module only allocates outputs/workspace with torch and calls the C ABI
+in order; every step of the computation runs in the HIP kernels.
+
+Token tensors: x [T, C] (q | k | v channels), z [T, Hv, d], output [T, Hv, d].
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+from . import capi as L
+
+
+@dataclasses.dataclass
+class CoreConfig:
+    hk: int
+    hv: int
+    d: int
+    dtype: torch.dtype = torch.bfloat16
+    scale: Optional[float] = None        # default d ** -0.5
+    act: int = L.GDN_ACT_SILU            # output-gate activation
+    l2_eps: float = 1e-6
+    norm_eps: float = 1e-6
+
+    @property
+    def channels(self):
+        return 2 * self.hk * self.d + self.hv * self.d
+
+    @property
+    def q_scale(self):
+        return self.d ** -0.5 if self.scale is None else self.scale
+
+
+class GDNCore:
+    """Holds the workspace for one layer shape and runs forward/backward."""
+
+    def __init__(self, cfg: CoreConfig, device="cuda"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self._ws = None
+        L.load()
+
+    def shape(self, T: int, n_seq: int) -> L.Shape:
+        c = self.cfg
+        return L.make_shape(n_seq, T, c.hk, c.hv, c.d, c.dtype)
+
+    def workspace(self, shape: L.Shape, rows: int) -> torch.Tensor:
+        need = max(L.gdn_conv_bwd_workspace(shape), L.gdn_gate_bwd_workspace(shape),
+                   L.gdn_chunk_fwd_workspace(shape), L.gdn_chunk_bwd_workspace(shape),
+                   L.gdn_gated_norm_bwd_workspace(rows, self.cfg.d), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def split(self, y):
+        c = self.cfg
+        q = y[:, : c.hk * c.d]
+        k = y[:, c.hk * c.d: 2 * c.hk * c.d]
+        v = y[:, 2 * c.hk * c.d:]
+        return q, k, v
+
+    def forward(self, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, S0=None,
+                want_final=False):
+        c = self.cfg
+        T = x.shape[0]
+        n_seq = cu_seqlens.numel() - 1
+        sh = self.shape(T, n_seq)
+        ws = self.workspace(sh, T * c.hv)
+        dev, dt = x.device, c.dtype
+        y = torch.empty((T, c.channels), dtype=dt, device=dev)
+        L.gdn_conv_fwd(sh, x, w_conv, cu_seqlens, y, True, c.l2_eps)
+        g = torch.empty((T, c.hv), dtype=torch.float32, device=dev)
+        beta = torch.empty_like(g)
+        L.gdn_gate_fwd(sh, a, b, A_log, dt_bias, g, beta)
+        q, k, v = self.split(y)
+        o = torch.empty((T, c.hv, c.d), dtype=dt, device=dev)
+        Sf = torch.empty((n_seq, c.hv, c.d, c.d), dtype=torch.float32, device=dev) if want_final else None
+        L.gdn_chunk_fwd(sh, q, k, v, g, beta, c.q_scale, S0, Sf, cu_seqlens, o, ws)
+        out = torch.empty_like(o)
+        L.gdn_gated_norm_fwd(o, z, w_norm, out, c.norm_eps, c.act)
+        return {"y": y, "g": g, "beta": beta, "o": o, "out": out, "S_final": Sf}
+
+    def backward(self, saved, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, dout,
+                 S0=None, dS_final=None):
+        c = self.cfg
+        T = x.shape[0]
+        n_seq = cu_seqlens.numel() - 1
+        sh = self.shape(T, n_seq)
+        ws = self.workspace(sh, T * c.hv)
+        dev, dt = x.device, c.dtype
+        do = torch.empty((T, c.hv, c.d), dtype=dt, device=dev)
+        dz = torch.empty_like(do)
+        dw_norm = torch.empty(c.d, dtype=torch.float32, device=dev)
+        L.gdn_gated_norm_bwd(saved["o"], z, w_norm, dout, do, dz, dw_norm, ws, c.norm_eps, c.act)
+        dy = torch.empty((T, c.channels), dtype=dt, device=dev)
+        dq, dk, dv = self.split(dy)
+        dg = torch.empty((T, c.hv), dtype=torch.float32, device=dev)
+        dbeta = torch.empty_like(dg)
+        dS0 = torch.empty((n_seq, c.hv, c.d, c.d), dtype=torch.float32, device=dev)
+        q, k, v = self.split(saved["y"])
+        L.gdn_chunk_bwd(sh, q, k, v, saved["g"], saved["beta"], c.q_scale, S0, cu_seqlens, do,
+                        dS_final, dq, dk, dv, dg, dbeta, dS0, ws)
+        da = torch.empty((T, c.hv), dtype=dt, device=dev)
+        db = torch.empty_like(da)
+        dA_log = torch.empty(c.hv, dtype=torch.float32, device=dev)
+        ddt = torch.empty_like(dA_log)
+        L.gdn_gate_bwd(sh, a, b, A_log, dt_bias, dg, dbeta, da, db, dA_log, ddt, ws)
+        dx = torch.empty((T, c.channels), dtype=dt, device=dev)
+        dw_conv = torch.empty((c.channels, 4), dtype=torch.float32, device=dev)
+        L.gdn_conv_bwd(sh, x, w_conv, cu_seqlens, dy, dx, dw_conv, ws, True, c.l2_eps)
+        return {"do": do, "dz": dz, "dw_norm": dw_norm, "dy_conv": dy, "dg": dg, "dbeta": dbeta,
+                "dS0": dS0, "da": da, "db": db, "dA_log": dA_log, "ddt_bias": ddt, "dx": dx,
+                "dw_conv": dw_conv}

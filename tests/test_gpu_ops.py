@@ -1,0 +1,190 @@
+"""Per-op GPU parity against the CPU oracle (run through the C ABI).
+
+Every op is fed bit-identical inputs on both sides: inputs come from the
+seeded generator, or from an earlier oracle op rounded to the storage dtype.
+Shapes are small enough for the oracle yet span several 64-token chunks,
+ragged tails, a length-1 sequence and grouped value heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_layer_causal_amd import inputs as gi
+from gated_deltanet_layer_causal_amd import capi as L
+from tests.gpu_util import (DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_close, dev, host)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (hk, hv, d, dtype, lens, A_range, S0/final)
+    "fp32_tiny": (1, 2, 32, "fp32", [64], (1.0, 16.0), False),
+    "fp32_ragged": (1, 2, 32, "fp32", [100, 37, 1, 70], (0.02, 0.2), True),
+    "bf16_g2_mild": (2, 4, 128, "bf16", [150, 64, 1, 90], (0.01, 0.1), True),
+    "bf16_g3_strong": (2, 6, 128, "bf16", [200, 7, 130], (1.0, 16.0), False),
+    "bf16_d32": (2, 4, 32, "bf16", [129, 64], (0.05, 0.5), True),
+}
+
+
+def _tol(dtype, grad=False):
+    if dtype == "fp32":
+        return TOL_FP32
+    return GRAD_TOL_BF16 if grad else FWD_TOL_BF16
+
+
+def _rnd(a, dtype):
+    a = np.asarray(a, dtype=np.float32)
+    return gi.round_bf16(a) if dtype == "bf16" else a
+
+
+def _tdt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def _case(name, seed=7):
+    hk, hv, d, dtype, lens, A_range, state = CASES[name]
+    w = gi.Workload(name, sum(lens), hk, hv, d, dtype, seq="varlen", init_state=state,
+                    final_state=state, seed=seed)
+    inp = gi.make_inputs(w, seqlens=lens, A_range=A_range)
+    return w, inp
+
+
+def _shape(w, inp):
+    return L.make_shape(inp["N"], inp["T"], w.hk, w.hv, w.d,
+                        L.GDN_BF16 if w.dtype == "bf16" else L.GDN_FP32)
+
+
+# ------------------------------------------------------------------ conv
+@pytest.mark.parametrize("name", list(CASES))
+def test_conv_fwd_bwd(name):
+    w, inp = _case(name)
+    dt = w.dtype
+    cu = inp["cu_seqlens"]
+    n_l2 = 2 * w.hk * w.d
+    y_ref = oracle.conv_fwd(inp["x"], inp["w_conv"], cu, n_l2, w.d)
+    rng = np.random.default_rng(3)
+    dy = _rnd(rng.standard_normal(y_ref.shape), dt)
+    dx_ref, dw_ref = oracle.conv_bwd(inp["x"], inp["w_conv"], cu, n_l2, w.d, dy)
+
+    sh = _shape(w, inp)
+    x = dev(inp["x"], _tdt(dt))
+    wc = dev(inp["w_conv"])
+    cut = torch.from_numpy(cu).to(DEV)
+    y = torch.empty_like(x)
+    L.gdn_conv_fwd(sh, x, wc, cut, y)
+    dyt = dev(dy, _tdt(dt))
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(wc)
+    ws = torch.empty(max(L.gdn_conv_bwd_workspace(sh), 16), dtype=torch.uint8, device=DEV)
+    L.gdn_conv_bwd(sh, x, wc, cut, dyt, dx, dw, ws)
+    torch.cuda.synchronize()
+    assert_close("y", host(y), y_ref, _tol(dt))
+    assert_close("dx", host(dx), dx_ref, _tol(dt, True))
+    assert_close("dw", host(dw), dw_ref, _tol(dt, True))
+
+
+# ------------------------------------------------------------------ gate
+@pytest.mark.parametrize("name", ["fp32_tiny", "bf16_g3_strong"])
+def test_gate_fwd_bwd(name):
+    w, inp = _case(name)
+    dt = w.dtype
+    g_ref, b_ref = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    rng = np.random.default_rng(4)
+    dg = rng.standard_normal(g_ref.shape).astype(np.float32)
+    dbeta = rng.standard_normal(g_ref.shape).astype(np.float32)
+    ref = oracle.gate_bwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], dg, dbeta)
+    sh = _shape(w, inp)
+    a, b = dev(inp["a"], _tdt(dt)), dev(inp["b"], _tdt(dt))
+    Al, dtb = dev(inp["A_log"]), dev(inp["dt_bias"])
+    g = torch.empty(a.shape, dtype=torch.float32, device=DEV)
+    beta = torch.empty_like(g)
+    L.gdn_gate_fwd(sh, a, b, Al, dtb, g, beta)
+    da, db = torch.empty_like(a), torch.empty_like(b)
+    dAl, ddt = torch.empty_like(Al), torch.empty_like(dtb)
+    ws = torch.empty(L.gdn_gate_bwd_workspace(sh), dtype=torch.uint8, device=DEV)
+    L.gdn_gate_bwd(sh, a, b, Al, dtb, dev(dg), dev(dbeta), da, db, dAl, ddt, ws)
+    torch.cuda.synchronize()
+    tol = TOL_FP32 if dt == "fp32" else FWD_TOL_BF16
+    assert_close("g", host(g), g_ref, TOL_FP32)
+    assert_close("beta", host(beta), b_ref, TOL_FP32)
+    for nm, got, r in (("da", da, ref[0]), ("db", db, ref[1]), ("dA_log", dAl, ref[2]),
+                       ("ddt_bias", ddt, ref[3])):
+        assert_close(nm, host(got), r, tol if nm in ("da", "db") else TOL_FP32 * 10)
+
+
+# ------------------------------------------------------------------ gated norm
+@pytest.mark.parametrize("name", ["fp32_tiny", "bf16_g2_mild", "bf16_d32"])
+@pytest.mark.parametrize("act", [L.GDN_ACT_SILU, L.GDN_ACT_SIGMOID])
+def test_gated_norm_fwd_bwd(name, act):
+    w, inp = _case(name)
+    dt = w.dtype
+    rng = np.random.default_rng(5)
+    o = _rnd(rng.standard_normal(inp["z"].shape), dt)
+    y_ref = oracle.norm_fwd(o, inp["z"], inp["w_norm"], act)
+    do_ref, dz_ref, dw_ref = oracle.norm_bwd(o, inp["z"], inp["w_norm"], inp["dy"], act)
+    ot, zt = dev(o, _tdt(dt)), dev(inp["z"], _tdt(dt))
+    wn = dev(inp["w_norm"])
+    y = torch.empty_like(ot)
+    L.gdn_gated_norm_fwd(ot, zt, wn, y, act=act)
+    dyt = dev(inp["dy"], _tdt(dt))
+    do, dz, dw = torch.empty_like(ot), torch.empty_like(ot), torch.empty_like(wn)
+    ws = torch.empty(L.gdn_gated_norm_bwd_workspace(o.size // w.d, w.d), dtype=torch.uint8, device=DEV)
+    L.gdn_gated_norm_bwd(ot, zt, wn, dyt, do, dz, dw, ws, act=act)
+    torch.cuda.synchronize()
+    assert_close("y", host(y), y_ref, _tol(dt))
+    assert_close("do", host(do), do_ref, _tol(dt, True))
+    assert_close("dz", host(dz), dz_ref, _tol(dt, True))
+    assert_close("dw", host(dw), dw_ref, _tol(dt, True))
+
+
+# ------------------------------------------------------------------ chunked delta rule
+def _delta_inputs(name, seed=7):
+    w, inp = _case(name, seed)
+    dt = w.dtype
+    cu = inp["cu_seqlens"]
+    y = _rnd(oracle.conv_fwd(inp["x"], inp["w_conv"], cu, 2 * w.hk * w.d, w.d), dt)
+    g, beta = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    g, beta = g.astype(np.float32), beta.astype(np.float32)
+    return w, inp, y, g, beta
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_chunk_fwd_bwd(name):
+    w, inp, y, g, beta = _delta_inputs(name)
+    dt, cu, hk, hv, d = w.dtype, inp["cu_seqlens"], w.hk, w.hv, w.d
+    scale = d ** -0.5
+    T = inp["T"]
+    q, k, v = gi.split_qkv(y, hk, hv, d)
+    S0 = inp["S0"]
+    o_ref, Sf_ref = oracle.delta_fwd(q, k, v, g, beta, cu, scale, S0)
+    rng = np.random.default_rng(6)
+    dout = _rnd(rng.standard_normal(o_ref.shape), dt)
+    dSf = inp["dS_T"]
+    ref = oracle.delta_bwd(q, k, v, g, beta, cu, scale, dout, S0, dSf)
+
+    sh = _shape(w, inp)
+    yt = dev(y, _tdt(dt))
+    qt, kt, vt = yt[:, : hk * d], yt[:, hk * d: 2 * hk * d], yt[:, 2 * hk * d:]
+    gt, bt = dev(g), dev(beta)
+    cut = torch.from_numpy(cu).to(DEV)
+    S0t = dev(S0) if S0 is not None else None
+    Sf = torch.empty((inp["N"], hv, d, d), dtype=torch.float32, device=DEV)
+    o = torch.empty((T, hv, d), dtype=_tdt(dt), device=DEV)
+    ws = torch.empty(max(L.gdn_chunk_fwd_workspace(sh), L.gdn_chunk_bwd_workspace(sh)),
+                     dtype=torch.uint8, device=DEV)
+    L.gdn_chunk_fwd(sh, qt, kt, vt, gt, bt, scale, S0t, Sf, cut, o, ws)
+    dy = torch.empty_like(yt)
+    dq, dk, dv = dy[:, : hk * d], dy[:, hk * d: 2 * hk * d], dy[:, 2 * hk * d:]
+    dg = torch.empty_like(gt)
+    db = torch.empty_like(bt)
+    dS0 = torch.empty_like(Sf)
+    dSft = dev(dSf) if dSf is not None else None
+    L.gdn_chunk_bwd(sh, qt, kt, vt, gt, bt, scale, S0t, cut, dev(dout, _tdt(dt)), dSft, dq, dk, dv,
+                    dg, db, dS0, ws)
+    torch.cuda.synchronize()
+    assert_close("o", host(o), o_ref, _tol(dt))
+    assert_close("S_final", host(Sf), Sf_ref, _tol(dt))
+    got = (host(dq).reshape(T, hk, d), host(dk).reshape(T, hk, d), host(dv).reshape(T, hv, d),
+           host(dg), host(db), host(dS0))
+    for nm, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref):
+        assert_close(nm, a, r, _tol(dt, True))
