@@ -35,15 +35,15 @@ struct RevSmem {
   T dSb[BV][D + Pad<T>::v];       // dS' block (v-major)
   T dDt[BV][CHUNK + Pad<T>::v];   // dDelta^T
   T dRg[BV][CHUNK + Pad<T>::v];   // (diag(Gam) dR)^T
-  float gam[CHUNK];
+  double gam[CHUNK];
 };
 
 template <typename T, int D, int BV>
 __global__ void __launch_bounds__(256) chunk_rev_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
-    const float* __restrict__ gcum, const T* __restrict__ Mw, const T* __restrict__ Pw,
-    const T* __restrict__ dout, const float* __restrict__ dS_final, float* __restrict__ dS0,
+    const double* __restrict__ gcum, const typename Compute<T>::type* __restrict__ Mw,
+    const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ dout, const float* __restrict__ dS_final, float* __restrict__ dS0,
     T* __restrict__ dhst, T* __restrict__ ddw, T* __restrict__ dvo, int64_t lddv) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RevSmem<T, D, BV>& sm = *reinterpret_cast<RevSmem<T, D, BV>*>(smem_raw);
@@ -92,12 +92,12 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
     // scaled copy of dO for the state gradient
     for (int i = tid; i < CHUNK * BV; i += 256) {
       const int t = i / BV, vv = i % BV;
-      sm.dOg[t][vv] = from_f<T>(scale * __expf(sm.gam[t]) * to_f(sm.dO[t][vv]));
+      sm.dOg[t][vv] = from_f<T>(scale * dexp<T>(sm.gam[t]) * to_f(sm.dO[t][vv]));
     }
     // Phase A: dDelta = P^T dO + diag(dec) K dS'^T
-    const T* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
-    const T* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
-    const float gl = sm.gam[CHUNK - 1];
+    const auto* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+    const auto* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+    const double gl = sm.gam[CHUNK - 1];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
       const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
       float dd[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dd[e] = pt[e] + __expf(gl - sm.gam[tb + e]) * kd[e];
+      for (int e = 0; e < 4; ++e) dd[e] = pt[e] + dexp<T>(gl - sm.gam[tb + e]) * kd[e];
       store4(&sm.dDt[vv][tb], dd[0], dd[1], dd[2], dd[3]);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -126,7 +126,7 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
       float rg[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        rg[e] = __expf(sm.gam[tb + e]) * dr[e];
+        rg[e] = dexp<T>(sm.gam[tb + e]) * dr[e];
         if (tb + e < L) dvo[(t0 + tb + e) * lddv + (int64_t)h * D + v0 + vv] = from_f<T>(dr[e]);
       }
       store4(&sm.dRg[vv][tb], rg[0], rg[1], rg[2], rg[3]);
@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
     __syncthreads();
 
     // Phase C: dS^T = Gam_L dS'^T + Q^T (scale diag(Gam) dO) - K^T (diag(Gam) dR)
-    const float GL = __expf(gl);
+    const float GL = dexp<T>(gl);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
@@ -181,7 +181,8 @@ struct GradSmem {
   T WA[CHUNK][CHUNK + Pad<T>::v];
   T dPD[CHUNK][CHUNK + Pad<T>::v];
   float X[16][17];
-  float gam[CHUNK], bet[CHUNK];
+  double gam[CHUNK];
+  float bet[CHUNK];
   float rowA[CHUNK], rowB[CHUNK];
   float colA[4][CHUNK], colB[4][CHUNK], rowX[4][CHUNK];
   float zp[4][64];
@@ -192,7 +193,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256) chunk_grad_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G,
-    float scale, const float* __restrict__ gcum, const float* __restrict__ beta,
+    float scale, const double* __restrict__ gcum, const float* __restrict__ beta,
     const T* __restrict__ hst, const T* __restrict__ dhst, const T* __restrict__ Rw,
     const T* __restrict__ Dlw, const T* __restrict__ ddw, const T* __restrict__ dout,
     const T* __restrict__ dvo, int64_t lddv, T* __restrict__ dq, T* __restrict__ dk, int64_t lddq,
@@ -260,7 +261,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = rbase + e;
-        sm.Sc1[t][s] = (s < t) ? sm.bet[t] * __expf(sm.gam[t] - sm.gam[s]) * kk[j][e] : 0.f;
+        sm.Sc1[t][s] = (s < t) ? sm.bet[t] * dexp<T>(sm.gam[t] - sm.gam[s]) * kk[j][e] : 0.f;
       }
     }
     __syncthreads();
@@ -318,7 +319,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
           float wa = 0.f;
           if (s < t) {
             const float dAv = -da[e];
-            const float Dts = __expf(sm.gam[t] - sm.gam[s]);
+            const float Dts = dexp<T>(sm.gam[t] - sm.gam[s]);
             const float Ats = sm.bet[t] * Dts * kk[j][e];
             const float EA = dAv * Ats;
             ra[e] += EA;
@@ -363,7 +364,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
           const int t = rbase + e;
           float v = 0.f;
           if (s <= t) {
-            const float Dts = __expf(sm.gam[t] - sm.gam[s]);
+            const float Dts = dexp<T>(sm.gam[t] - sm.gam[s]);
             const float E = dp[e] * Dts * scale * qk[j][e];
             ra[e] += E;
             ca[j] -= E;
@@ -390,7 +391,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
     {
       const T* Sg = hst + ((int64_t)c * Hv + h) * D * D;   // [k][v]
       const T* dSg = dhst + ((int64_t)c * Hv + h) * D * D;
-      const float gl = sm.gam[CHUNK - 1];
+      const double gl = sm.gam[CHUNK - 1];
       float rx[4][4];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -415,8 +416,8 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * tt + rsub + e;
-          const float Gm = __expf(sm.gam[t]);
-          const float dec = __expf(gl - sm.gam[t]);
+          const float Gm = dexp<T>(sm.gam[t]);
+          const float dec = dexp<T>(gl - sm.gam[t]);
           const float qv = to_f(sm.Qt[kc][t]), kv = to_f(sm.Kt[kc][t]);
           dQa[i][e] += Gm * x1[e];
           dKa[i][e] += scale * pq[e] - Gm * x2[e] + dec * x3[e];
@@ -457,7 +458,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
       float zsum = 0.f, ips = 0.f;
       for (int i = 0; i < 4 * 64; ++i) zsum += (&sm.zp[0][0])[i];
       for (int i = 0; i < 256; ++i) ips += sm.ip[i];
-      if (t == L - 1) dgm += zsum + __expf(sm.gam[CHUNK - 1]) * ips;
+      if (t == L - 1) dgm += zsum + dexp<T>(sm.gam[CHUNK - 1]) * ips;
       if (t >= L) dgm = 0.f;
       const float dgs = wave_suffix_scan(dgm, lane);
       if (t < L) {
@@ -505,8 +506,9 @@ static hipError_t chunk_bwd_t(const gdn_shape& s, const void* q, const void* k, 
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, dim3(D / BV, s.hv, s.n_seq), dim3(256), shm, st, (const T*)q,
                        (const T*)k, ldq, ldk, cu, seq_off, s.hv, s.hv / s.hk, scale,
-                       (const float*)(ws + Ly.gcum), (const T*)(ws + Ly.mw),
-                       (const T*)(ws + Ly.pw), (const T*)dout, dS_final, dS0, (T*)(ws + Ly.dh),
+                       (const double*)(ws + Ly.gcum),
+                       (const typename Compute<T>::type*)(ws + Ly.mw),
+                       (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)dout, dS_final, dS0, (T*)(ws + Ly.dh),
                        (T*)(ws + Ly.ddw), (T*)dv, lddv);
   }
   if (Ly.nt_max > 0 && s.total_tokens > 0) {
@@ -515,7 +517,7 @@ static hipError_t chunk_bwd_t(const gdn_shape& s, const void* q, const void* k, 
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm, st, (const T*)q,
                        (const T*)k, ldq, ldk, cu, seq_off, s.n_seq, s.hv, s.hv / s.hk, scale,
-                       (const float*)(ws + Ly.gcum), beta, (const T*)(ws + Ly.h),
+                       (const double*)(ws + Ly.gcum), beta, (const T*)(ws + Ly.h),
                        (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw), (const T*)(ws + Ly.dlw),
                        (const T*)(ws + Ly.ddw), (const T*)dout, (const T*)dv, lddv, (T*)dq,
                        (T*)dk, lddq, lddk, dg, dbeta);

@@ -21,11 +21,24 @@ namespace gdn {
 
 template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };
 
+// MFMA operand type of the forward-state kernels for a storage type: fp16 for
+// bf16 storage (bf16 inputs convert exactly; 11-bit mantissa for the
+// intermediates), fp32 for fp32 storage.
+template <typename T> struct Compute { typedef fp16 type; };
+template <> struct Compute<float> { typedef float type; };
+
+// exp of an in-chunk gate-sum difference.  The sums are kept in fp64: with
+// strong decay they reach several hundred inside one chunk, where an fp32
+// difference would lose ~3e-5 relative accuracy.  fp32 storage evaluates the
+// exponential in fp64 too.
+template <typename T> __device__ __forceinline__ float dexp(double x) { return __expf((float)x); }
+template <> __device__ __forceinline__ float dexp<float>(double x) { return (float)exp(x); }
+
 // Workspace layout (byte offsets; every region 256-byte aligned).
 struct ChunkLayout {
   int64_t nt_max;     // upper bound on the number of chunks: T/64 + n_seq
   size_t seq_off;     // int32 [n_seq + 1]: first chunk of each sequence; [n_seq] = #chunks
-  size_t gcum;        // fp32 [T][hv]: in-chunk cumulative gate
+  size_t gcum;        // fp64 [T][hv]: in-chunk cumulative gate
   size_t mw, pw;      // T [nt_max][hv][64][64]: M = Tinv diag(beta), P
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
   size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
@@ -41,7 +54,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.nt_max = T / CHUNK + s.n_seq;
   size_t off = 0;
   L.seq_off = off; off = align256(off + sizeof(int32_t) * (size_t)(s.n_seq + 1));
-  L.gcum = off; off = align256(off + sizeof(float) * (size_t)T * s.hv);
+  L.gcum = off; off = align256(off + sizeof(double) * (size_t)T * s.hv);
   L.mw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.pw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.total_fwd = off;
@@ -76,8 +89,8 @@ __device__ __forceinline__ void chunk_span(const int32_t* seq_off, const int32_t
 
 // Stage rows [0, 64) x [0, W) of a token-major tensor into LDS (row stride ld_s),
 // zero-filling rows >= L.  Source row r is at src + r * ld_g.
-template <typename T, int W>
-__device__ __forceinline__ void stage_rows(T* dst, int ld_s, const T* src, int64_t ld_g, int L,
+template <typename TD, int W, typename TS>
+__device__ __forceinline__ void stage_rows(TD* dst, int ld_s, const TS* src, int64_t ld_g, int L,
                                            int tid) {
   constexpr int G8 = W / 8;
   for (int i = tid; i < CHUNK * G8; i += 256) {
@@ -140,10 +153,10 @@ __device__ __forceinline__ void invert_unit_lower(const float (*A)[68], float (*
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+__device__ __forceinline__ double wave_incl_scan(double x, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    float y = __shfl_up(x, off, 64);
+    double y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
   return x;

@@ -41,12 +41,13 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t* __restr
 // MFMA operands M = Tinv diag(beta) and P written to the workspace.
 template <typename T, int D>
 struct PrepSmem {
-  T K[CHUNK][D + Pad<T>::v];
-  T Q[CHUNK][D + Pad<T>::v];
+  typedef typename Compute<T>::type CT;
+  CT K[CHUNK][D + Pad<CT>::v];
+  CT Q[CHUNK][D + Pad<CT>::v];
   float A[CHUNK][68];
   float Ti[CHUNK][68];
   float X[16][17];
-  float gam[CHUNK];
+  double gam[CHUNK];
   float bet[CHUNK];
 };
 
@@ -55,10 +56,12 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G, float scale,
-    float* __restrict__ gcum, T* __restrict__ Mw, T* __restrict__ Pw) {
+    double* __restrict__ gcum, typename Compute<T>::type* __restrict__ Mw,
+    typename Compute<T>::type* __restrict__ Pw) {
+  typedef typename Compute<T>::type CT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   PrepSmem<T, D>& sm = *reinterpret_cast<PrepSmem<T, D>*>(smem_raw);
-  constexpr int LD = D + Pad<T>::v;
+  constexpr int LD = D + Pad<CT>::v;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x;
   const int kh = blockIdx.y;
@@ -67,16 +70,16 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   int L;
   chunk_span(seq_off, cu, n_seq, c, t0, L);
 
-  stage_rows<T, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-  stage_rows<T, D>(&sm.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+  stage_rows<CT, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
+  stage_rows<CT, D>(&sm.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
   __syncthreads();
 
   // wave w owns rows [16w, 16w+16) of the 64 x 64 products
   floatx4 kk[4], qk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    kk[j] = tile_mma<T, true, true>(zero4(), &sm.K[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
-    qk[j] = tile_mma<T, true, true>(zero4(), &sm.Q[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
+    kk[j] = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
+    qk[j] = tile_mma<CT, true, true>(zero4(), &sm.Q[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
   }
   const int rbase = 16 * wave + 4 * (lane >> 4);
   const int ccol = lane & 15;
@@ -84,30 +87,29 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   for (int hh = 0; hh < G; ++hh) {
     const int h = kh * G + hh;
     if (wave == 0) {
-      const float gl = lane < L ? g[(t0 + lane) * Hv + h] : 0.f;
+      const double gl = lane < L ? (double)g[(t0 + lane) * Hv + h] : 0.0;
       const float bl = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
-      const float gm = wave_incl_scan(gl, lane);
+      const double gm = wave_incl_scan(gl, lane);
       sm.gam[lane] = gm;
       sm.bet[lane] = bl;
       if (lane < L) gcum[(t0 + lane) * Hv + h] = gm;
     }
     __syncthreads();
-    T* Pout = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+    CT* Pout = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = 16 * j + ccol;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = rbase + e;
-        const float dfs = sm.gam[t] - sm.gam[s <= t ? s : t];   // masked before exp
-        const float dec = __expf(dfs);
+        const float dec = dexp<T>(sm.gam[t] - sm.gam[s <= t ? s : t]);  // masked before exp
         sm.A[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
-        Pout[t * CHUNK + s] = from_f<T>((s <= t) ? dec * scale * qk[j][e] : 0.f);
+        Pout[t * CHUNK + s] = from_f<CT>((s <= t) ? dec * scale * qk[j][e] : 0.f);
       }
     }
     __syncthreads();
     invert_unit_lower(sm.A, sm.Ti, sm.X, tid);
-    T* Mout = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+    CT* Mout = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
     for (int i = tid; i < CHUNK * 8; i += 256) {
       const int t = i >> 3, s8 = (i & 7) * 8;
       f8 v;
@@ -130,26 +132,29 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
 //   per chunk and head), R and Delta.
 template <typename T, int D, int BV>
 struct StateSmem {
-  T K[CHUNK][D + Pad<T>::v];
-  T Q[CHUNK][D + Pad<T>::v];
-  T V[CHUNK][BV + Pad<T>::v];
-  T Sb[BV][D + Pad<T>::v];       // S block (v-major), MFMA B operand of K S^T
-  T Rt[BV][CHUNK + Pad<T>::v];   // R^T
-  T Dt[BV][CHUNK + Pad<T>::v];   // Delta^T
-  T Dst[BV][CHUNK + Pad<T>::v];  // (diag(dec) Delta)^T
-  float gam[CHUNK];
+  typedef typename Compute<T>::type CT;
+  CT K[CHUNK][D + Pad<CT>::v];
+  CT Q[CHUNK][D + Pad<CT>::v];
+  CT V[CHUNK][BV + Pad<CT>::v];
+  CT Sb[BV][D + Pad<CT>::v];       // S block (v-major), MFMA B operand of K S^T
+  CT Rt[BV][CHUNK + Pad<CT>::v];   // R^T
+  CT Dt[BV][CHUNK + Pad<CT>::v];   // Delta^T
+  CT Dst[BV][CHUNK + Pad<CT>::v];  // (diag(dec) Delta)^T
+  double gam[CHUNK];
 };
 
 template <typename T, int D, int BV, int MODE>
 __global__ void __launch_bounds__(256) chunk_state_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t ldq,
     int64_t ldk, int64_t ldv, const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off,
-    int Hv, int G, float scale, const float* __restrict__ gcum, const T* __restrict__ Mw,
-    const T* __restrict__ Pw, const float* __restrict__ S0, float* __restrict__ S_final,
-    T* __restrict__ o, T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw) {
+    int Hv, int G, float scale, const double* __restrict__ gcum,
+    const typename Compute<T>::type* __restrict__ Mw, const typename Compute<T>::type* __restrict__ Pw,
+    const float* __restrict__ S0, float* __restrict__ S_final, T* __restrict__ o,
+    T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw) {
+  typedef typename Compute<T>::type CT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   StateSmem<T, D, BV>& sm = *reinterpret_cast<StateSmem<T, D, BV>*>(smem_raw);
-  constexpr int LD = D + Pad<T>::v, LDV = BV + Pad<T>::v, LDC = CHUNK + Pad<T>::v;
+  constexpr int LD = D + Pad<CT>::v, LDV = BV + Pad<CT>::v, LDC = CHUNK + Pad<CT>::v;
   constexpr int NVT = BV / 16;                      // value tiles
   constexpr int NS = (D / 16) * NVT / 4;            // state tiles per wave
   constexpr int NA = (CHUNK / 16) * NVT / 4;        // token x value tiles per wave
@@ -178,9 +183,9 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
     const int64_t t0 = (int64_t)cu[n] + CHUNK * (c - c_begin);
     const int L = (int64_t)cu[n + 1] - t0 < CHUNK ? (int)((int64_t)cu[n + 1] - t0) : CHUNK;
     __syncthreads();
-    stage_rows<T, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-    if (MODE == 0) stage_rows<T, D>(&sm.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
-    stage_rows<T, BV>(&sm.V[0][0], LDV, v + t0 * ldv + (int64_t)h * D + v0, ldv, L, tid);
+    stage_rows<CT, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
+    if (MODE == 0) stage_rows<CT, D>(&sm.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+    stage_rows<CT, BV>(&sm.V[0][0], LDV, v + t0 * ldv + (int64_t)h * D + v0, ldv, L, tid);
     if (tid < CHUNK) sm.gam[tid] = gcum[(t0 + (tid < L ? tid : L - 1)) * Hv + h];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -200,16 +205,16 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-      floatx4 ks = tile_mma<T, true, true>(zero4(), &sm.K[0][0], LD, &sm.Sb[0][0], LD, 16 * tt,
+      floatx4 ks = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.Sb[0][0], LD, 16 * tt,
                                            16 * vt, D, lane);
       if (MODE == 0)
-        oq[i] = tile_mma<T, true, true>(zero4(), &sm.Q[0][0], LD, &sm.Sb[0][0], LD, 16 * tt,
+        oq[i] = tile_mma<CT, true, true>(zero4(), &sm.Q[0][0], LD, &sm.Sb[0][0], LD, 16 * tt,
                                         16 * vt, D, lane);
       const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
       float r[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float Gm = __expf(sm.gam[tb + e]);
+        const float Gm = dexp<T>(sm.gam[tb + e]);
         r[e] = to_f(sm.V[tb + e][vv]) - Gm * ks[e];
         if (MODE == 0) oq[i][e] *= Gm * scale;
       }
@@ -223,17 +228,17 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
     __syncthreads();
 
     // Phase B: Delta = M R
-    const T* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
-    const float gl = sm.gam[CHUNK - 1];
+    const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+    const double gl = sm.gam[CHUNK - 1];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-      floatx4 dl = tile_mma<T, true, true>(zero4(), Mc, CHUNK, &sm.Rt[0][0], LDC, 16 * tt, 16 * vt,
+      floatx4 dl = tile_mma<CT, true, true>(zero4(), Mc, CHUNK, &sm.Rt[0][0], LDC, 16 * tt, 16 * vt,
                                            CHUNK, lane);
       const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
       float ds[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ds[e] = __expf(gl - sm.gam[tb + e]) * dl[e];
+      for (int e = 0; e < 4; ++e) ds[e] = dexp<T>(gl - sm.gam[tb + e]) * dl[e];
       store4(&sm.Dt[vv][tb], dl[0], dl[1], dl[2], dl[3]);
       store4(&sm.Dst[vv][tb], ds[0], ds[1], ds[2], ds[3]);
       if (MODE == 1) {
@@ -246,11 +251,11 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
 
     // Phase C: O = oq + P Delta;  S^T <- Gam_L S^T + K^T (diag(dec) Delta)
     if (MODE == 0) {
-      const T* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+      const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-        floatx4 ov = tile_mma<T, true, true>(oq[i], Pc, CHUNK, &sm.Dt[0][0], LDC, 16 * tt, 16 * vt,
+        floatx4 ov = tile_mma<CT, true, true>(oq[i], Pc, CHUNK, &sm.Dt[0][0], LDC, 16 * tt, 16 * vt,
                                              CHUNK, lane);
         const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
 #pragma unroll
@@ -258,13 +263,13 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
           if (tb + e < L) o[(t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv] = from_f<T>(ov[e]);
       }
     }
-    const float GL = __expf(gl);
+    const float GL = dexp<T>(gl);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[i][e] *= GL;
-      S[i] = tile_mma<T, false, true>(S[i], &sm.K[0][0], LD, &sm.Dst[0][0], LDC, 16 * kt, 16 * vt,
+      S[i] = tile_mma<CT, false, true>(S[i], &sm.K[0][0], LD, &sm.Dst[0][0], LDC, 16 * kt, 16 * vt,
                                       CHUNK, lane);
     }
   }
@@ -295,8 +300,9 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL((chunk_prep_kernel<T, D>), dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm,
                        st, (const T*)q, (const T*)k, ldq, ldk, g, beta, cu, seq_off, s.n_seq, s.hv,
-                       s.hv / s.hk, scale, (float*)(ws + Ly.gcum), (T*)(ws + Ly.mw),
-                       (T*)(ws + Ly.pw));
+                       s.hv / s.hk, scale, (double*)(ws + Ly.gcum),
+                       (typename Compute<T>::type*)(ws + Ly.mw),
+                       (typename Compute<T>::type*)(ws + Ly.pw));
   }
   return hipGetLastError();
 }
@@ -312,8 +318,9 @@ static hipError_t chunk_state(const gdn_shape& s, const void* q, const void* k, 
   hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   hipLaunchKernelGGL(kern, dim3(D / BV, s.hv, s.n_seq), dim3(256), shm, st, (const T*)q,
                      (const T*)k, (const T*)v, ldq, ldk, ldv, cu, (const int32_t*)(ws + Ly.seq_off),
-                     s.hv, s.hv / s.hk, scale, (const float*)(ws + Ly.gcum),
-                     (const T*)(ws + Ly.mw), (const T*)(ws + Ly.pw), S0, S_final, (T*)o,
+                     s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum),
+                     (const typename Compute<T>::type*)(ws + Ly.mw),
+                     (const typename Compute<T>::type*)(ws + Ly.pw), S0, S_final, (T*)o,
                      (T*)(ws + Ly.h), (T*)(ws + Ly.rw), (T*)(ws + Ly.dlw));
   return hipGetLastError();
 }

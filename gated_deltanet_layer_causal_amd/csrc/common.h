@@ -4,7 +4,8 @@
 // fp32.  Matrix products use MFMA: v_mfma_f32_16x16x32_bf16 for bf16 operands
 // and v_mfma_f32_16x16x4_f32 for fp32 operands (true fp32 arithmetic).
 //
-// MFMA 16x16 output layout (both instructions): lane l of the 64-wide wave
+// fp16 operands use v_mfma_f32_16x16x32_f16 (same rate, 11-bit mantissa).
+// MFMA 16x16 output layout (all three instructions): lane l of the 64-wide wave
 // holds C[4*(l/16) + i][l%16], i = 0..3.  Operand A is read row = l%16,
 // operand B column = l%16; the K index a lane supplies is k0 + 8*(l/16) + j
 // (bf16, j = 0..7) or k0 + l/16 (fp32).  A and B always use the same K map,
@@ -16,15 +17,19 @@
 namespace gdn {
 
 typedef __bf16 bf16;
+typedef _Float16 fp16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 fp16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(fp16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ fp16 from_f<fp16>(float x) { return (fp16)x; }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
@@ -40,6 +45,13 @@ __device__ __forceinline__ f8 load8(const bf16* p) {
     r.v[2 * i] = __uint_as_float(w[i] << 16);
     r.v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
+  return r;
+}
+__device__ __forceinline__ f8 load8(const fp16* p) {
+  fp16x8 raw = *reinterpret_cast<const fp16x8*>(p);
+  f8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.v[i] = (float)raw[i];
   return r;
 }
 __device__ __forceinline__ f8 load8(const float* p) {
@@ -62,6 +74,12 @@ __device__ __forceinline__ void store8(bf16* p, const f8& r) {
   raw.w = pack2_bf16(r.v[6], r.v[7]);
   *reinterpret_cast<uint4*>(p) = raw;
 }
+__device__ __forceinline__ void store8(fp16* p, const f8& r) {
+  fp16x8 raw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) raw[i] = (fp16)r.v[i];
+  *reinterpret_cast<fp16x8*>(p) = raw;
+}
 __device__ __forceinline__ void store8(float* p, const f8& r) {
   reinterpret_cast<float4*>(p)[0] = make_float4(r.v[0], r.v[1], r.v[2], r.v[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(r.v[4], r.v[5], r.v[6], r.v[7]);
@@ -73,6 +91,11 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   raw.y = pack2_bf16(c, d);
   *reinterpret_cast<uint2*>(p) = raw;
 }
+__device__ __forceinline__ void store4(fp16* p, float a, float b, float c, float d) {
+  typedef _Float16 fp16x4 __attribute__((ext_vector_type(4)));
+  fp16x4 raw = {(fp16)a, (fp16)b, (fp16)c, (fp16)d};
+  *reinterpret_cast<fp16x4*>(p) = raw;
+}
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
@@ -81,23 +104,27 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 // Mma<T>::frag is the per-lane operand of one MFMA step over KS values of K.
 template <typename T> struct Mma;
 
-template <> struct Mma<bf16> {
+// 16-bit operands (bf16 or fp16): same lane layout, 8 K values per lane.
+template <typename E, typename V> struct Mma16 {
   static constexpr int KS = 32;
-  typedef bf16x8 frag;
+  typedef V frag;
   __device__ __forceinline__ static floatx4 mma(const frag& a, const frag& b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    if constexpr (sizeof(E) == 2 && __is_same(E, bf16))
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   // Element (r, k0 + kk) for this lane's K slots, r fixed, contiguous K.
   template <typename S>
   __device__ __forceinline__ static frag kc(const S* row, int k0, int lane) {
     const S* p = row + k0 + 8 * (lane >> 4);
-    if constexpr (sizeof(S) == 2) {
+    if constexpr (__is_same(S, E)) {
       return *reinterpret_cast<const frag*>(p);
     } else {
       f8 v = load8(p);
       frag f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = (bf16)v.v[j];
+      for (int j = 0; j < 8; ++j) f[j] = (E)v.v[j];
       return f;
     }
   }
@@ -107,20 +134,12 @@ template <> struct Mma<bf16> {
     const S* p = col + (int64_t)(k0 + 8 * (lane >> 4)) * ld;
     frag f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = (bf16)to_f(p[(int64_t)j * ld]);
-    return f;
-  }
-  // Same, with a per-K scale factor sc[k] applied before rounding.
-  template <typename S>
-  __device__ __forceinline__ static frag kc_scaled(const S* row, int k0, int lane, const float* sc) {
-    const int kb = k0 + 8 * (lane >> 4);
-    f8 v = load8(row + kb);
-    frag f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = (bf16)(v.v[j] * sc[kb + j]);
+    for (int j = 0; j < 8; ++j) f[j] = (E)to_f(p[(int64_t)j * ld]);
     return f;
   }
 };
+template <> struct Mma<bf16> : Mma16<bf16, bf16x8> {};
+template <> struct Mma<fp16> : Mma16<fp16, fp16x8> {};
 
 template <> struct Mma<float> {
   static constexpr int KS = 4;
@@ -135,11 +154,6 @@ template <> struct Mma<float> {
   template <typename S>
   __device__ __forceinline__ static frag ks(const S* col, int ld, int k0, int lane) {
     return to_f(col[(int64_t)(k0 + (lane >> 4)) * ld]);
-  }
-  template <typename S>
-  __device__ __forceinline__ static frag kc_scaled(const S* row, int k0, int lane, const float* sc) {
-    const int k = k0 + (lane >> 4);
-    return to_f(row[k]) * sc[k];
   }
 };
 
@@ -166,8 +180,8 @@ __device__ __forceinline__ floatx4 tile_mma(floatx4 acc, const SA* A, int lda, c
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
-// Sum over the 16 lanes that share (l / 16) ... i.e. lanes with equal l>>4
-// hold the same output rows; reduce a per-lane value over the 16 columns.
+// Row sum of an MFMA output tile: the 16 lanes with equal l>>4 hold the same
+// 4 rows (columns l%16); reduce a per-lane value over those 16 lanes.
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1, 64);
   x += __shfl_xor(x, 2, 64);

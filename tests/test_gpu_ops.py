@@ -12,7 +12,8 @@ import torch
 import oracle
 from gated_deltanet_layer_causal_amd import inputs as gi
 from gated_deltanet_layer_causal_amd import capi as L
-from tests.gpu_util import (DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_close, dev, host)
+from tests.gpu_util import (DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_close, dev, host,
+                            rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -182,9 +183,12 @@ def test_chunk_fwd_bwd(name):
     L.gdn_chunk_bwd(sh, qt, kt, vt, gt, bt, scale, S0t, cut, dev(dout, _tdt(dt)), dSft, dq, dk, dv,
                     dg, db, dS0, ws)
     torch.cuda.synchronize()
-    assert_close("o", host(o), o_ref, _tol(dt))
-    assert_close("S_final", host(Sf), Sf_ref, _tol(dt))
     got = (host(dq).reshape(T, hk, d), host(dk).reshape(T, hk, d), host(dv).reshape(T, hv, d),
            host(dg), host(db), host(dS0))
-    for nm, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref):
-        assert_close(nm, a, r, _tol(dt, True))
+    checks = [("o", host(o), o_ref, _tol(dt)), ("S_final", host(Sf), Sf_ref, _tol(dt))]
+    checks += [(nm, a, r, _tol(dt, True))
+               for nm, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref)]
+    report = {nm: rel_err(a, r) for nm, a, r, _ in checks}
+    print(name, " ".join(f"{k}={v:.2e}" for k, v in report.items()))
+    for nm, a, r, tol in checks:
+        assert_close(nm, a, r, tol)
