@@ -1,0 +1,226 @@
+"""Throughput of the Gated DeltaNet layer core (forward + backward) on one GPU.
+
+One step = conv -> gate -> chunked gated delta rule -> gated norm forward,
+then the four backward calls, over one batch of synthetic input already
+resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload flash64k]
+
+Per-call durations are measured with HIP events recorded on the stream the
+calls are launched on (torch's current stream) across the timed steps; the
+dominant call is reported against its roofline with the algorithmic work
+per token of that call (bytes for HBM-bound calls, flops for MFMA-bound ones).
+The CPU oracle is timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd+bwd tokens/s (16k/48v heads, d=128, 64k tok); % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+
+# Algorithmic work per token of each call (E = bytes per element of the
+# token tensors).  HBM-bound calls count the bytes they must read and write.
+# The chunk phases count the dense contraction flops of their formulas in the
+# chunked WY/UT form (chunk C = 64, head dim d, per value head unless noted):
+#   fwd_states : K S^T, Q S^T, S update (3 x 2 d^2) + M R, P Delta (2 x 2 C d)
+#   bwd_states : K S^T, S update (2 x 2 d^2) + M R (2 C d)
+#   bwd_reverse: K dS'^T, Q^T dO, K^T dR (3 x 2 d^2) + P^T dO, M^T dDelta (2 x 2 C d)
+#   bwd_grads  : dO S, dR S, Delta dS' (3 x 2 d^2); dM, dP, (dP o D) K,
+#                (dP o D)^T Q, (dA o bD) K, (dA o bD)^T K (6 x 2 C d);
+#                Tinv products (2 x 2 C^2); per key head K K^T, Q K^T (2 x 2 C d)
+# The preparation phase is bandwidth-bound: it reads q, k, g, beta and
+# writes the in-chunk gate sums and the two 64 x 64 factors per chunk.
+def algorithmic_per_token(name, hk, hv, d, E):
+    C = 2 * hk * d + hv * d
+    C64 = 64
+    if name == "conv_fwd":
+        return "hbm", 2 * C * E                       # read x, write y
+    if name == "conv_bwd":
+        return "hbm", 3 * C * E                       # read x, dy; write dx
+    if name == "gate_fwd":
+        return "hbm", hv * (2 * E + 8)                # read a, b; write g, beta
+    if name == "gate_bwd":
+        return "hbm", hv * (2 * E + 8 + 2 * E)        # read a, b, dg, dbeta; write da, db
+    if name == "norm_fwd":
+        return "hbm", 3 * hv * d * E                  # read o, z; write y
+    if name == "norm_bwd":
+        return "hbm", 5 * hv * d * E                  # read o, z, dy; write do, dz
+    if name in ("chunk_prepare", "chunk_prepare_b"):
+        return "hbm", 2 * hk * d * E + hv * (4 + 4 + 8 + 2 * C64 * E)
+    if name == "chunk_fwd_states":
+        return "mfma", hv * (6 * d * d + 4 * C64 * d)
+    if name == "chunk_bwd_states":
+        return "mfma", hv * (4 * d * d + 2 * C64 * d)
+    if name == "chunk_bwd_reverse":
+        return "mfma", hv * (6 * d * d + 4 * C64 * d)
+    if name == "chunk_bwd_grads":
+        return "mfma", hv * (6 * d * d + 12 * C64 * d + 4 * C64 * C64) + hk * 4 * C64 * d
+    raise KeyError(name)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="flash64k")
+    p.add_argument("--seed", type=int, default=1005)
+    p.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+def make_gpu_inputs(w, seed, dev):
+    """Synthetic inputs with the workload's distributions, drawn on the GPU
+    from a seeded generator (same distributions as the numpy generator)."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    bf = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    T, C, Hv, d = w.T, w.channels, w.hv, w.d
+
+    def n(shape, std=1.0, dt=torch.float32):
+        return (torch.randn(shape, generator=g, device=dev) * std).to(dt)
+
+    A = torch.rand(Hv, generator=g, device=dev) * (w.A_range[1] - w.A_range[0]) + w.A_range[0]
+    inp = {
+        "x": n((T, C), dt=bf), "w_conv": n((C, 4), 0.25), "a": n((T, Hv), dt=bf),
+        "b": n((T, Hv), dt=bf), "A_log": torch.log(A), "dt_bias": torch.zeros(Hv, device=dev),
+        "z": n((T, Hv, d), dt=bf), "w_norm": n((d,), 0.1), "dy": n((T, Hv, d), dt=bf),
+        "cu_seqlens": torch.tensor([0, T], dtype=torch.int32, device=dev),
+    }
+    if w.init_state:
+        inp["S0"] = n((1, Hv, d, d), 0.1)
+    if w.final_state:
+        inp["dS_T"] = n((1, Hv, d, d))
+    return inp
+
+
+class EventTimer:
+    """Records a HIP event before and after each named call on the current stream."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.pairs = {}
+        self.active = False
+
+    def __call__(self, name, phase):
+        if not self.active:
+            return
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record(self.torch.cuda.current_stream())
+        self.pairs.setdefault(name, []).append(ev)  # begin, end, begin, end, ...
+
+    def mean_ms(self):
+        out = {}
+        for name, evs in self.pairs.items():
+            ts = [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs) - 1, 2)]
+            out[name] = sum(ts) / len(ts)
+        return out
+
+
+def cpu_baseline(w, sample_T):
+    import numpy as np
+    import oracle
+    from gated_deltanet_layer_causal_amd import inputs as gi
+    inp = gi.make_inputs(w, T=sample_T)
+    t0 = time.perf_counter()
+    f = oracle.layer_fwd(inp, w.hk, w.hv, w.d, w.d ** -0.5, round_fn=gi.round_bf16)
+    oracle.layer_bwd(inp, f, w.hk, w.hv, w.d, w.d ** -0.5, round_fn=gi.round_bf16)
+    dt = time.perf_counter() - t0
+    return {"value": sample_T / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"layer fwd+bwd on the first {sample_T} tokens of the {w.name} shape "
+                      f"({w.hk}k/{w.hv}v heads, d={w.d}), fp64 token-by-token, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the layer core is head-parallel; a multi-GPU run would shard heads, see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from gated_deltanet_layer_causal_amd import inputs as gi
+    from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore
+
+    w = gi.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=dt), device=dev)
+    inp = make_gpu_inputs(w, args.seed, dev)
+    args_f = (inp["x"], inp["w_conv"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], inp["z"],
+              inp["w_norm"], inp["cu_seqlens"])
+    timer = EventTimer()
+
+    def step():
+        f = core.forward(*args_f, S0=inp.get("S0"), want_final=w.final_state, timer=timer)
+        core.backward(f, *args_f, inp["dy"], S0=inp.get("S0"), dS_final=inp.get("dS_T"),
+                      timer=timer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.active = True
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    timer.active = False
+    ms = start.elapsed_time(stop) / args.steps
+    value = w.T / (ms / 1e3)
+    per_call = timer.mean_ms()
+
+    E = 2 if w.dtype == "bf16" else 4
+    dom = max(per_call, key=per_call.get)
+    bound, per_tok = algorithmic_per_token(dom, w.hk, w.hv, w.d, E)
+    if bound == "hbm":
+        achieved = per_tok * w.T / (per_call[dom] / 1e3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = per_tok * w.T / (per_call[dom] / 1e3) / 1e12
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        unit = "TFLOP/s"
+    calls = {}
+    for name, t in sorted(per_call.items(), key=lambda kv: -kv[1]):
+        b, pt = algorithmic_per_token(name, w.hk, w.hv, w.d, E)
+        rate = pt * w.T / (t / 1e3) / (1e9 if b == "hbm" else 1e12)
+        pk = HBM_PEAK_GBS if b == "hbm" else (BF16_PEAK_TFLOPS if E == 2 else FP32_PEAK_TFLOPS)
+        calls[name] = {"ms": round(t, 4), "bound": b, "achieved": round(rate, 2),
+                       "frac": round(rate / pk, 4)}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded on-device draws with the workload's distributions)",
+        "config": {"workload": f"{w.name}: GDN layer core fwd+bwd, {w.hk} k-heads / {w.hv} v-heads, "
+                               f"d={w.d}, {w.T} tokens, single sequence, chunk 64",
+                   "tokens": w.T, "hk": w.hk, "hv": w.hv, "d": w.d, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                     "ms_per_launch": round(per_call[dom], 4)},
+        "calls": calls,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

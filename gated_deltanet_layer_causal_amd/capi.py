@@ -24,7 +24,8 @@ EXPORTS = (
     "gdn_status_string", "gdn_conv_fwd", "gdn_conv_bwd", "gdn_conv_bwd_workspace", "gdn_gate_fwd",
     "gdn_gate_bwd", "gdn_gate_bwd_workspace", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace",
     "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd",
-    "gdn_gated_norm_bwd_workspace",
+    "gdn_gated_norm_bwd_workspace", "gdn_chunk_prepare", "gdn_chunk_fwd_states",
+    "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse", "gdn_chunk_bwd_grads",
 )
 
 
@@ -63,6 +64,12 @@ def load(path: str = LIB_PATH):
     lib.gdn_chunk_fwd.argtypes = [SP, V, V, V, I64, I64, I64, V, V, F, V, V, V, V, V, c_size_t, V]
     lib.gdn_chunk_bwd.argtypes = [SP, V, V, V, I64, I64, I64, V, V, F, V, V, V, V, V, V, V, I64,
                                   I64, I64, V, V, V, V, c_size_t, V]
+    lib.gdn_chunk_prepare.argtypes = [SP, V, V, I64, I64, V, V, F, V, V, c_size_t, V]
+    lib.gdn_chunk_fwd_states.argtypes = [SP, V, V, V, I64, I64, I64, F, V, V, V, V, V, c_size_t, V]
+    lib.gdn_chunk_bwd_states.argtypes = [SP, V, V, V, I64, I64, I64, F, V, V, V, c_size_t, V]
+    lib.gdn_chunk_bwd_reverse.argtypes = [SP, V, V, I64, I64, F, V, V, V, V, I64, V, V, c_size_t, V]
+    lib.gdn_chunk_bwd_grads.argtypes = [SP, V, V, I64, I64, V, F, V, V, V, I64, V, V, I64, I64, V,
+                                        V, V, c_size_t, V]
     lib.gdn_gated_norm_fwd.argtypes = [I64, c_int32, c_int, V, V, V, F, c_int, V, V]
     lib.gdn_gated_norm_bwd.argtypes = [I64, c_int32, c_int, V, V, V, F, c_int, V, V, V, V, V,
                                        c_size_t, V]
@@ -73,7 +80,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_gated_norm_bwd_workspace.argtypes = [I64, c_int32]
     lib.gdn_gated_norm_bwd_workspace.restype = c_size_t
     for name in ("gdn_conv_fwd", "gdn_conv_bwd", "gdn_gate_fwd", "gdn_gate_bwd", "gdn_chunk_fwd",
-                 "gdn_chunk_bwd", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd"):
+                 "gdn_chunk_bwd", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd", "gdn_chunk_prepare",
+                 "gdn_chunk_fwd_states", "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse",
+                 "gdn_chunk_bwd_grads"):
         getattr(lib, name).restype = c_int
     _lib = lib
     return lib
@@ -173,6 +182,38 @@ def gdn_chunk_bwd(shape, q, k, v, g, beta, scale, S0, cu_seqlens, dout, dS_final
                                               _p(dk), _p(dv), _ld(dq), _ld(dk), _ld(dv), _p(dg),
                                               _p(dbeta), _p(dS0), _p(ws), ws.numel(),
                                               _stream(stream)))
+
+
+def gdn_chunk_prepare(shape, q, k, g, beta, scale, cu_seqlens, ws, stream=None):
+    _ok("gdn_chunk_prepare", load().gdn_chunk_prepare(byref(shape), _p(q), _p(k), _ld(q), _ld(k),
+                                                      _p(g), _p(beta), scale, _p(cu_seqlens),
+                                                      _p(ws), ws.numel(), _stream(stream)))
+
+
+def gdn_chunk_fwd_states(shape, q, k, v, scale, S0, S_final, cu_seqlens, o, ws, stream=None):
+    _ok("gdn_chunk_fwd_states", load().gdn_chunk_fwd_states(
+        byref(shape), _p(q), _p(k), _p(v), _ld(q), _ld(k), _ld(v), scale, _p(S0), _p(S_final),
+        _p(cu_seqlens), _p(o), _p(ws), ws.numel(), _stream(stream)))
+
+
+def gdn_chunk_bwd_states(shape, q, k, v, scale, S0, cu_seqlens, ws, stream=None):
+    _ok("gdn_chunk_bwd_states", load().gdn_chunk_bwd_states(
+        byref(shape), _p(q), _p(k), _p(v), _ld(q), _ld(k), _ld(v), scale, _p(S0), _p(cu_seqlens),
+        _p(ws), ws.numel(), _stream(stream)))
+
+
+def gdn_chunk_bwd_reverse(shape, q, k, scale, cu_seqlens, dout, dS_final, dv, dS0, ws, stream=None):
+    _ok("gdn_chunk_bwd_reverse", load().gdn_chunk_bwd_reverse(
+        byref(shape), _p(q), _p(k), _ld(q), _ld(k), scale, _p(cu_seqlens), _p(dout), _p(dS_final),
+        _p(dv), _ld(dv), _p(dS0), _p(ws), ws.numel(), _stream(stream)))
+
+
+def gdn_chunk_bwd_grads(shape, q, k, beta, scale, cu_seqlens, dout, dv, dq, dk, dg, dbeta, ws,
+                        stream=None):
+    _ok("gdn_chunk_bwd_grads", load().gdn_chunk_bwd_grads(
+        byref(shape), _p(q), _p(k), _ld(q), _ld(k), _p(beta), scale, _p(cu_seqlens), _p(dout),
+        _p(dv), _ld(dv), _p(dq), _p(dk), _ld(dq), _ld(dk), _p(dg), _p(dbeta), _p(ws), ws.numel(),
+        _stream(stream)))
 
 
 def gdn_gated_norm_fwd(o, z, w, y, eps=1e-6, act=GDN_ACT_SILU, stream=None):

@@ -180,6 +180,87 @@ gdn_status gdn_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const
                                    (hipStream_t)stream));
 }
 
+// ---- chunk phases -----------------------------------------------------------
+namespace {
+gdn_status check_chunk_common(const gdn_shape* s, const void* q, const void* k, int64_t ldq,
+                              int64_t ldk, const void* cu, const void* ws, size_t ws_bytes,
+                              size_t need) {
+  GDN_TRY(check_shape(s));
+  GDN_TRY(chunk_supported(s));
+  GDN_TRY(check_ptrs({q, k, ws}));
+  if (!cu) return GDN_ERR_INVALID_ARG;
+  GDN_TRY(check_ld(ldq, (int64_t)s->hk * s->dk));
+  GDN_TRY(check_ld(ldk, (int64_t)s->hk * s->dk));
+  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
+}  // namespace
+
+gdn_status gdn_chunk_prepare(const gdn_shape* s, const void* q, const void* k, int64_t ldq,
+                             int64_t ldk, const float* g, const float* beta, float scale,
+                             const int32_t* cu, void* ws, size_t ws_bytes, void* stream) {
+  GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
+                             s ? chunk_fwd_ws_bytes(*s) : 0));
+  if (!g || !beta) return GDN_ERR_INVALID_ARG;
+  return launched(launch_chunk_prepare(*s, q, k, ldq, ldk, g, beta, scale, cu, ws,
+                                       (hipStream_t)stream));
+}
+
+gdn_status gdn_chunk_fwd_states(const gdn_shape* s, const void* q, const void* k, const void* v,
+                                int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                const float* S0, float* S_final, const int32_t* cu, void* o,
+                                void* ws, size_t ws_bytes, void* stream) {
+  GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
+                             s ? chunk_fwd_ws_bytes(*s) : 0));
+  GDN_TRY(check_ptrs({v, o}));
+  GDN_TRY(check_ld(ldv, (int64_t)s->hv * s->dv));
+  if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return GDN_ERR_ALIGNMENT;
+  return launched(launch_chunk_fwd_states(*s, q, k, v, ldq, ldk, ldv, scale, S0, S_final, cu, o,
+                                          ws, (hipStream_t)stream));
+}
+
+gdn_status gdn_chunk_bwd_states(const gdn_shape* s, const void* q, const void* k, const void* v,
+                                int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                const float* S0, const int32_t* cu, void* ws, size_t ws_bytes,
+                                void* stream) {
+  GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
+                             s ? chunk_bwd_ws_bytes(*s) : 0));
+  GDN_TRY(check_ptrs({v}));
+  GDN_TRY(check_ld(ldv, (int64_t)s->hv * s->dv));
+  if (S0 && !aligned16(S0)) return GDN_ERR_ALIGNMENT;
+  return launched(launch_chunk_bwd_states(*s, q, k, v, ldq, ldk, ldv, scale, S0, cu, ws,
+                                          (hipStream_t)stream));
+}
+
+gdn_status gdn_chunk_bwd_reverse(const gdn_shape* s, const void* q, const void* k, int64_t ldq,
+                                 int64_t ldk, float scale, const int32_t* cu, const void* dout,
+                                 const float* dS_final, void* dv, int64_t lddv, float* dS0,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
+                             s ? chunk_bwd_ws_bytes(*s) : 0));
+  GDN_TRY(check_ptrs({dout, dv}));
+  GDN_TRY(check_ld(lddv, (int64_t)s->hv * s->dv));
+  if ((dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0))) return GDN_ERR_ALIGNMENT;
+  return launched(launch_chunk_bwd_reverse(*s, q, k, ldq, ldk, scale, cu, dout, dS_final, dv, lddv,
+                                           dS0, ws, (hipStream_t)stream));
+}
+
+gdn_status gdn_chunk_bwd_grads(const gdn_shape* s, const void* q, const void* k, int64_t ldq,
+                               int64_t ldk, const float* beta, float scale, const int32_t* cu,
+                               const void* dout, const void* dv, int64_t lddv, void* dq, void* dk,
+                               int64_t lddq, int64_t lddk, float* dg, float* dbeta, void* ws,
+                               size_t ws_bytes, void* stream) {
+  GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
+                             s ? chunk_bwd_ws_bytes(*s) : 0));
+  GDN_TRY(check_ptrs({dout, dv, dq, dk}));
+  if (!beta || !dg || !dbeta) return GDN_ERR_INVALID_ARG;
+  GDN_TRY(check_ld(lddv, (int64_t)s->hv * s->dv));
+  GDN_TRY(check_ld(lddq, (int64_t)s->hk * s->dk));
+  GDN_TRY(check_ld(lddk, (int64_t)s->hk * s->dk));
+  return launched(launch_chunk_bwd_grads(*s, q, k, ldq, ldk, beta, scale, cu, dout, dv, lddv, dq,
+                                         dk, lddq, lddk, dg, dbeta, ws, (hipStream_t)stream));
+}
+
 gdn_status gdn_gated_norm_fwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
                               const float* w, float eps, gdn_act act, void* y, void* stream) {
   if (rows < 0 || (dt != GDN_BF16 && dt != GDN_FP32) || (act != GDN_ACT_SILU && act != GDN_ACT_SIGMOID))

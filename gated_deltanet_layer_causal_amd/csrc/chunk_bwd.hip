@@ -20,11 +20,6 @@
 
 namespace gdn {
 
-hipError_t chunk_bwd_recompute(const gdn_shape& s, const void* q, const void* k, const void* v,
-                               int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
-                               const float* beta, float scale, const float* S0, const int32_t* cu,
-                               void* ws, hipStream_t st);
-
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BV>
 struct RevSmem {
@@ -485,44 +480,55 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-static hipError_t chunk_bwd_t(const gdn_shape& s, const void* q, const void* k, const void* v,
-                              int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
-                              const float* beta, float scale, const float* S0, const int32_t* cu,
-                              const void* dout, const float* dS_final, void* dq, void* dk,
-                              void* dv, int64_t lddq, int64_t lddk, int64_t lddv, float* dg,
-                              float* dbeta, float* dS0, void* wsv, hipStream_t st) {
-  constexpr int BV = 32;
-  static_assert(sizeof(GradSmem<T, D>) <= 160 * 1024, "gradient kernel LDS budget");
-  static_assert(sizeof(RevSmem<T, D, BV>) <= 160 * 1024, "reverse kernel LDS budget");
+constexpr int REV_BV = 32;
+
+hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                    int64_t ldk, float scale, const int32_t* cu, const void* dout,
+                                    const float* dS_final, void* dv, int64_t lddv, float* dS0,
+                                    void* wsv, hipStream_t st) {
   char* ws = (char*)wsv;
   const ChunkLayout Ly = chunk_layout(s);
-  hipError_t e = chunk_bwd_recompute(s, q, k, v, ldq, ldk, ldv, g, beta, scale, S0, cu, ws, st);
-  if (e != hipSuccess) return e;
-  const int32_t* seq_off = (const int32_t*)(ws + Ly.seq_off);
-  {
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    constexpr int D = decltype(c)::d;
+    constexpr int BV = REV_BV;
+    static_assert(sizeof(RevSmem<T, D, BV>) <= 160 * 1024, "reverse kernel LDS budget");
     const size_t shm = sizeof(RevSmem<T, D, BV>);
     auto kern = chunk_rev_kernel<T, D, BV>;
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, dim3(D / BV, s.hv, s.n_seq), dim3(256), shm, st, (const T*)q,
-                       (const T*)k, ldq, ldk, cu, seq_off, s.hv, s.hv / s.hk, scale,
-                       (const double*)(ws + Ly.gcum),
+                       (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.hv,
+                       s.hv / s.hk, scale, (const double*)(ws + Ly.gcum),
                        (const typename Compute<T>::type*)(ws + Ly.mw),
-                       (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)dout, dS_final, dS0, (T*)(ws + Ly.dh),
-                       (T*)(ws + Ly.ddw), (T*)dv, lddv);
-  }
-  if (Ly.nt_max > 0 && s.total_tokens > 0) {
+                       (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)dout, dS_final,
+                       dS0, (T*)(ws + Ly.dh), (T*)(ws + Ly.ddw), (T*)dv, lddv);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                  int64_t ldk, const float* beta, float scale, const int32_t* cu,
+                                  const void* dout, const void* dv, int64_t lddv, void* dq,
+                                  void* dk, int64_t lddq, int64_t lddk, float* dg, float* dbeta,
+                                  void* wsv, hipStream_t st) {
+  char* ws = (char*)wsv;
+  const ChunkLayout Ly = chunk_layout(s);
+  if (Ly.nt_max == 0 || s.total_tokens == 0) return hipSuccess;
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    constexpr int D = decltype(c)::d;
+    static_assert(sizeof(GradSmem<T, D>) <= 160 * 1024, "gradient kernel LDS budget");
     const size_t shm = sizeof(GradSmem<T, D>);
     auto kern = chunk_grad_kernel<T, D>;
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm, st, (const T*)q,
-                       (const T*)k, ldq, ldk, cu, seq_off, s.n_seq, s.hv, s.hv / s.hk, scale,
-                       (const double*)(ws + Ly.gcum), beta, (const T*)(ws + Ly.h),
-                       (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw), (const T*)(ws + Ly.dlw),
-                       (const T*)(ws + Ly.ddw), (const T*)dout, (const T*)dv, lddv, (T*)dq,
-                       (T*)dk, lddq, lddk, dg, dbeta);
-  }
-  return hipGetLastError();
+                       (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
+                       s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), beta,
+                       (const T*)(ws + Ly.h), (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw),
+                       (const T*)(ws + Ly.dlw), (const T*)(ws + Ly.ddw), (const T*)dout,
+                       (const T*)dv, lddv, (T*)dq, (T*)dk, lddq, lddk, dg, dbeta);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_chunk_bwd(const gdn_shape& s, const void* q, const void* k, const void* v,
@@ -531,15 +537,14 @@ hipError_t launch_chunk_bwd(const gdn_shape& s, const void* q, const void* k, co
                             const void* dout, const float* dS_final, void* dq, void* dk, void* dv,
                             int64_t lddq, int64_t lddk, int64_t lddv, float* dg, float* dbeta,
                             float* dS0, void* ws, hipStream_t st) {
-#define GDN_BWD(TT, DD)                                                                          \
-  return chunk_bwd_t<TT, DD>(s, q, k, v, ldq, ldk, ldv, g, beta, scale, S0, cu, dout, dS_final, \
-                             dq, dk, dv, lddq, lddk, lddv, dg, dbeta, dS0, ws, st);
-  if (s.dtype == GDN_BF16) {
-    if (s.dk == 128) { GDN_BWD(bf16, 128) } else { GDN_BWD(bf16, 32) }
-  } else {
-    GDN_BWD(float, 32)
-  }
-#undef GDN_BWD
+  hipError_t e = launch_chunk_prepare(s, q, k, ldq, ldk, g, beta, scale, cu, ws, st);
+  if (e == hipSuccess) e = launch_chunk_bwd_states(s, q, k, v, ldq, ldk, ldv, scale, S0, cu, ws, st);
+  if (e == hipSuccess)
+    e = launch_chunk_bwd_reverse(s, q, k, ldq, ldk, scale, cu, dout, dS_final, dv, lddv, dS0, ws, st);
+  if (e == hipSuccess)
+    e = launch_chunk_bwd_grads(s, q, k, ldq, ldk, beta, scale, cu, dout, dv, lddv, dq, dk, lddq,
+                               lddk, dg, dbeta, ws, st);
+  return e;
 }
 
 }  // namespace gdn

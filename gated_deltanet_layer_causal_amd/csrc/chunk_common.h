@@ -67,6 +67,14 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   return L;
 }
 
+// Instantiation selector for the chunk kernels: bf16 storage at head dim 32
+// or 128, fp32 storage at head dim 32 (the only combinations validated).
+template <typename T, int D> struct ChunkCfg { typedef T type; static constexpr int d = D; };
+template <typename F> hipError_t dispatch_chunk(const gdn_shape& s, F&& f) {
+  if (s.dtype == GDN_BF16) return s.dk == 128 ? f(ChunkCfg<bf16, 128>{}) : f(ChunkCfg<bf16, 32>{});
+  return f(ChunkCfg<float, 32>{});
+}
+
 // Largest n in [0, n_seq) with off[n] <= c (off non-decreasing).
 __device__ __forceinline__ int upper_index(const int32_t* off, int n_seq, int64_t c) {
   int lo = 0, hi = n_seq - 1;

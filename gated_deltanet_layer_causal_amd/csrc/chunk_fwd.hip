@@ -284,8 +284,7 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-constexpr int state_bv() { return D == 128 ? 32 : 32; }
+constexpr int STATE_BV = 32;  // value rows of the state owned by one workgroup
 
 template <typename T, int D>
 static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
@@ -312,7 +311,7 @@ static hipError_t chunk_state(const gdn_shape& s, const void* q, const void* k, 
                               int64_t ldq, int64_t ldk, int64_t ldv, float scale, const float* S0,
                               float* S_final, const int32_t* cu, void* o, const ChunkLayout& Ly,
                               char* ws, hipStream_t st) {
-  constexpr int BV = state_bv<T, D>();
+  constexpr int BV = STATE_BV;
   const size_t shm = sizeof(StateSmem<T, D, BV>);
   auto kern = chunk_state_kernel<T, D, BV, MODE>;
   hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
@@ -328,46 +327,46 @@ static hipError_t chunk_state(const gdn_shape& s, const void* q, const void* k, 
 size_t chunk_fwd_ws_bytes(const gdn_shape& s) { return chunk_layout(s).total_fwd; }
 size_t chunk_bwd_ws_bytes(const gdn_shape& s) { return chunk_layout(s).total_bwd; }
 
-template <typename T, int D>
-static hipError_t chunk_fwd_t(const gdn_shape& s, const void* q, const void* k, const void* v,
-                              int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
-                              const float* beta, float scale, const float* S0, float* S_final,
-                              const int32_t* cu, void* o, void* ws, hipStream_t st) {
+hipError_t launch_chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                int64_t ldk, const float* g, const float* beta, float scale,
+                                const int32_t* cu, void* ws, hipStream_t st) {
   const ChunkLayout Ly = chunk_layout(s);
-  hipError_t e = chunk_prepare<T, D>(s, q, k, ldq, ldk, g, beta, scale, cu, Ly, (char*)ws, st);
-  if (e != hipSuccess) return e;
-  return chunk_state<T, D, 0>(s, q, k, v, ldq, ldk, ldv, scale, S0, S_final, cu, o, Ly, (char*)ws, st);
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    return chunk_prepare<T, decltype(c)::d>(s, q, k, ldq, ldk, g, beta, scale, cu, Ly, (char*)ws, st);
+  });
+}
+
+hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
+                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                   const float* S0, float* S_final, const int32_t* cu, void* o,
+                                   void* ws, hipStream_t st) {
+  const ChunkLayout Ly = chunk_layout(s);
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    return chunk_state<T, decltype(c)::d, 0>(s, q, k, v, ldq, ldk, ldv, scale, S0, S_final, cu, o,
+                                             Ly, (char*)ws, st);
+  });
+}
+
+hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
+                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                   const float* S0, const int32_t* cu, void* ws, hipStream_t st) {
+  const ChunkLayout Ly = chunk_layout(s);
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    return chunk_state<T, decltype(c)::d, 1>(s, q, k, v, ldq, ldk, ldv, scale, S0, nullptr, cu,
+                                             nullptr, Ly, (char*)ws, st);
+  });
 }
 
 hipError_t launch_chunk_fwd(const gdn_shape& s, const void* q, const void* k, const void* v,
                             int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
                             const float* beta, float scale, const float* S0, float* S_final,
                             const int32_t* cu, void* o, void* ws, hipStream_t st) {
-  if (s.dtype == GDN_BF16)
-    return s.dk == 128 ? chunk_fwd_t<bf16, 128>(s, q, k, v, ldq, ldk, ldv, g, beta, scale, S0, S_final, cu, o, ws, st)
-                       : chunk_fwd_t<bf16, 32>(s, q, k, v, ldq, ldk, ldv, g, beta, scale, S0, S_final, cu, o, ws, st);
-  return s.dk == 128 ? chunk_fwd_t<float, 128>(s, q, k, v, ldq, ldk, ldv, g, beta, scale, S0, S_final, cu, o, ws, st)
-                     : chunk_fwd_t<float, 32>(s, q, k, v, ldq, ldk, ldv, g, beta, scale, S0, S_final, cu, o, ws, st);
-}
-
-// Backward recompute pieces used by chunk_bwd.hip.
-hipError_t chunk_bwd_recompute(const gdn_shape& s, const void* q, const void* k, const void* v,
-                               int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
-                               const float* beta, float scale, const float* S0, const int32_t* cu,
-                               void* ws, hipStream_t st) {
-  const ChunkLayout Ly = chunk_layout(s);
-  hipError_t e;
-#define GDN_RECOMP(TT, DD)                                                                        \
-  e = chunk_prepare<TT, DD>(s, q, k, ldq, ldk, g, beta, scale, cu, Ly, (char*)ws, st);            \
-  if (e != hipSuccess) return e;                                                                  \
-  return chunk_state<TT, DD, 1>(s, q, k, v, ldq, ldk, ldv, scale, S0, nullptr, cu, nullptr, Ly,   \
-                                (char*)ws, st);
-  if (s.dtype == GDN_BF16) {
-    if (s.dk == 128) { GDN_RECOMP(bf16, 128) } else { GDN_RECOMP(bf16, 32) }
-  } else {
-    if (s.dk == 128) { GDN_RECOMP(float, 128) } else { GDN_RECOMP(float, 32) }
-  }
-#undef GDN_RECOMP
+  hipError_t e = launch_chunk_prepare(s, q, k, ldq, ldk, g, beta, scale, cu, ws, st);
+  if (e != hipSuccess) return e;
+  return launch_chunk_fwd_states(s, q, k, v, ldq, ldk, ldv, scale, S0, S_final, cu, o, ws, st);
 }
 
 }  // namespace gdn

@@ -54,6 +54,25 @@ hipError_t launch_chunk_fwd(const gdn_shape& s, const void* q, const void* k, co
                             int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
                             const float* beta, float scale, const float* S0, float* S_final,
                             const int32_t* cu, void* o, void* ws, hipStream_t st);
+hipError_t launch_chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                int64_t ldk, const float* g, const float* beta, float scale,
+                                const int32_t* cu, void* ws, hipStream_t st);
+hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
+                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                   const float* S0, float* S_final, const int32_t* cu, void* o,
+                                   void* ws, hipStream_t st);
+hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
+                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                   const float* S0, const int32_t* cu, void* ws, hipStream_t st);
+hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                    int64_t ldk, float scale, const int32_t* cu, const void* dout,
+                                    const float* dS_final, void* dv, int64_t lddv, float* dS0,
+                                    void* ws, hipStream_t st);
+hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                  int64_t ldk, const float* beta, float scale, const int32_t* cu,
+                                  const void* dout, const void* dv, int64_t lddv, void* dq,
+                                  void* dk, int64_t lddq, int64_t lddk, float* dg, float* dbeta,
+                                  void* ws, hipStream_t st);
 hipError_t launch_chunk_bwd(const gdn_shape& s, const void* q, const void* k, const void* v,
                             int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
                             const float* beta, float scale, const float* S0, const int32_t* cu,

@@ -8,8 +8,8 @@ Token tensors: x [T, C] (q | k | v channels), z [T, Hv, d], output [T, Hv, d].
 """
 from __future__ import annotations
 
+import contextlib
 import dataclasses
-import math
 from typing import Optional
 
 import torch
@@ -35,6 +35,16 @@ class CoreConfig:
     @property
     def q_scale(self):
         return self.d ** -0.5 if self.scale is None else self.scale
+
+
+@contextlib.contextmanager
+def _timed(timer, name):
+    """Optional hook (e.g. HIP events) around one C-ABI call."""
+    if timer is not None:
+        timer(name, "begin")
+    yield
+    if timer is not None:
+        timer(name, "end")
 
 
 class GDNCore:
@@ -66,7 +76,7 @@ class GDNCore:
         return q, k, v
 
     def forward(self, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, S0=None,
-                want_final=False):
+                want_final=False, timer=None):
         c = self.cfg
         T = x.shape[0]
         n_seq = cu_seqlens.numel() - 1
@@ -74,20 +84,26 @@ class GDNCore:
         ws = self.workspace(sh, T * c.hv)
         dev, dt = x.device, c.dtype
         y = torch.empty((T, c.channels), dtype=dt, device=dev)
-        L.gdn_conv_fwd(sh, x, w_conv, cu_seqlens, y, True, c.l2_eps)
+        with _timed(timer, "conv_fwd"):
+            L.gdn_conv_fwd(sh, x, w_conv, cu_seqlens, y, True, c.l2_eps)
         g = torch.empty((T, c.hv), dtype=torch.float32, device=dev)
         beta = torch.empty_like(g)
-        L.gdn_gate_fwd(sh, a, b, A_log, dt_bias, g, beta)
+        with _timed(timer, "gate_fwd"):
+            L.gdn_gate_fwd(sh, a, b, A_log, dt_bias, g, beta)
         q, k, v = self.split(y)
         o = torch.empty((T, c.hv, c.d), dtype=dt, device=dev)
         Sf = torch.empty((n_seq, c.hv, c.d, c.d), dtype=torch.float32, device=dev) if want_final else None
-        L.gdn_chunk_fwd(sh, q, k, v, g, beta, c.q_scale, S0, Sf, cu_seqlens, o, ws)
+        with _timed(timer, "chunk_prepare"):
+            L.gdn_chunk_prepare(sh, q, k, g, beta, c.q_scale, cu_seqlens, ws)
+        with _timed(timer, "chunk_fwd_states"):
+            L.gdn_chunk_fwd_states(sh, q, k, v, c.q_scale, S0, Sf, cu_seqlens, o, ws)
         out = torch.empty_like(o)
-        L.gdn_gated_norm_fwd(o, z, w_norm, out, c.norm_eps, c.act)
+        with _timed(timer, "norm_fwd"):
+            L.gdn_gated_norm_fwd(o, z, w_norm, out, c.norm_eps, c.act)
         return {"y": y, "g": g, "beta": beta, "o": o, "out": out, "S_final": Sf}
 
     def backward(self, saved, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, dout,
-                 S0=None, dS_final=None):
+                 S0=None, dS_final=None, timer=None):
         c = self.cfg
         T = x.shape[0]
         n_seq = cu_seqlens.numel() - 1
@@ -97,23 +113,34 @@ class GDNCore:
         do = torch.empty((T, c.hv, c.d), dtype=dt, device=dev)
         dz = torch.empty_like(do)
         dw_norm = torch.empty(c.d, dtype=torch.float32, device=dev)
-        L.gdn_gated_norm_bwd(saved["o"], z, w_norm, dout, do, dz, dw_norm, ws, c.norm_eps, c.act)
+        with _timed(timer, "norm_bwd"):
+            L.gdn_gated_norm_bwd(saved["o"], z, w_norm, dout, do, dz, dw_norm, ws, c.norm_eps,
+                                 c.act)
         dy = torch.empty((T, c.channels), dtype=dt, device=dev)
         dq, dk, dv = self.split(dy)
         dg = torch.empty((T, c.hv), dtype=torch.float32, device=dev)
         dbeta = torch.empty_like(dg)
         dS0 = torch.empty((n_seq, c.hv, c.d, c.d), dtype=torch.float32, device=dev)
         q, k, v = self.split(saved["y"])
-        L.gdn_chunk_bwd(sh, q, k, v, saved["g"], saved["beta"], c.q_scale, S0, cu_seqlens, do,
-                        dS_final, dq, dk, dv, dg, dbeta, dS0, ws)
+        with _timed(timer, "chunk_prepare_b"):
+            L.gdn_chunk_prepare(sh, q, k, saved["g"], saved["beta"], c.q_scale, cu_seqlens, ws)
+        with _timed(timer, "chunk_bwd_states"):
+            L.gdn_chunk_bwd_states(sh, q, k, v, c.q_scale, S0, cu_seqlens, ws)
+        with _timed(timer, "chunk_bwd_reverse"):
+            L.gdn_chunk_bwd_reverse(sh, q, k, c.q_scale, cu_seqlens, do, dS_final, dv, dS0, ws)
+        with _timed(timer, "chunk_bwd_grads"):
+            L.gdn_chunk_bwd_grads(sh, q, k, saved["beta"], c.q_scale, cu_seqlens, do, dv, dq, dk, dg,
+                                  dbeta, ws)
         da = torch.empty((T, c.hv), dtype=dt, device=dev)
         db = torch.empty_like(da)
         dA_log = torch.empty(c.hv, dtype=torch.float32, device=dev)
         ddt = torch.empty_like(dA_log)
-        L.gdn_gate_bwd(sh, a, b, A_log, dt_bias, dg, dbeta, da, db, dA_log, ddt, ws)
+        with _timed(timer, "gate_bwd"):
+            L.gdn_gate_bwd(sh, a, b, A_log, dt_bias, dg, dbeta, da, db, dA_log, ddt, ws)
         dx = torch.empty((T, c.channels), dtype=dt, device=dev)
         dw_conv = torch.empty((c.channels, 4), dtype=torch.float32, device=dev)
-        L.gdn_conv_bwd(sh, x, w_conv, cu_seqlens, dy, dx, dw_conv, ws, True, c.l2_eps)
+        with _timed(timer, "conv_bwd"):
+            L.gdn_conv_bwd(sh, x, w_conv, cu_seqlens, dy, dx, dw_conv, ws, True, c.l2_eps)
         return {"do": do, "dz": dz, "dw_norm": dw_norm, "dy_conv": dy, "dg": dg, "dbeta": dbeta,
                 "dS0": dS0, "da": da, "db": db, "dA_log": dA_log, "ddt_bias": ddt, "dx": dx,
                 "dw_conv": dw_conv}

@@ -142,6 +142,47 @@ gdn_status gdn_chunk_bwd(const gdn_shape* shape, const void* q, const void* k, c
 size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
 
 /* ---------------------------------------------------------------------------
+ * The chunk calls above, split into their phases (same arguments, same
+ * workspace).  Each phase reads what the previous phases left in `ws`, so
+ * they must run in this order on one stream with the same shape, inputs and
+ * workspace; gdn_chunk_fwd / gdn_chunk_bwd are exactly these sequences.
+ * Besides letting a caller time or schedule the phases separately, every
+ * phase after gdn_chunk_prepare is a single kernel launch.
+ *   forward : gdn_chunk_prepare -> gdn_chunk_fwd_states
+ *   backward: gdn_chunk_prepare -> gdn_chunk_bwd_states -> gdn_chunk_bwd_reverse
+ *             -> gdn_chunk_bwd_grads
+ * gdn_chunk_prepare: chunk table from cu_seqlens; per (chunk, value head)
+ *   the in-chunk gate sums and the WY/UT factors M = (I + A)^-1 diag(beta)
+ *   and P (masked decayed scale * Q K^T), A = strictly-lower(beta D K K^T).
+ * gdn_chunk_fwd_states: sequential pass over chunks; writes o, S_final.
+ * gdn_chunk_bwd_states: same pass, storing chunk-start states and R, Delta.
+ * gdn_chunk_bwd_reverse: reverse pass over chunks; writes dv, dS0 and the
+ *   chunk-end state gradients.
+ * gdn_chunk_bwd_grads: chunk-parallel gradients; writes dq, dk, dg, dbeta
+ *   (reads dv written by the reverse phase).
+ * ------------------------------------------------------------------------- */
+gdn_status gdn_chunk_prepare(const gdn_shape* shape, const void* q, const void* k, int64_t ldq,
+                             int64_t ldk, const float* g, const float* beta, float scale,
+                             const int32_t* cu_seqlens, void* ws, size_t ws_bytes, void* stream);
+gdn_status gdn_chunk_fwd_states(const gdn_shape* shape, const void* q, const void* k,
+                                const void* v, int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                const float* S0, float* S_final, const int32_t* cu_seqlens,
+                                void* o, void* ws, size_t ws_bytes, void* stream);
+gdn_status gdn_chunk_bwd_states(const gdn_shape* shape, const void* q, const void* k,
+                                const void* v, int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                const float* S0, const int32_t* cu_seqlens, void* ws,
+                                size_t ws_bytes, void* stream);
+gdn_status gdn_chunk_bwd_reverse(const gdn_shape* shape, const void* q, const void* k, int64_t ldq,
+                                 int64_t ldk, float scale, const int32_t* cu_seqlens,
+                                 const void* dout, const float* dS_final, void* dv, int64_t lddv,
+                                 float* dS0, void* ws, size_t ws_bytes, void* stream);
+gdn_status gdn_chunk_bwd_grads(const gdn_shape* shape, const void* q, const void* k, int64_t ldq,
+                               int64_t ldk, const float* beta, float scale,
+                               const int32_t* cu_seqlens, const void* dout, const void* dv,
+                               int64_t lddv, void* dq, void* dk, int64_t lddq, int64_t lddk,
+                               float* dg, float* dbeta, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Gated zero-centred RMSNorm over rows of length dv (Megatron page,
  * "--apply-layernorm-1p": zero-centred RMSNorm; prime-rl page, "Summary":
  * ZeroCenteredRMSNorm and the "silu"/"sigmoid" gate activation kwarg):
