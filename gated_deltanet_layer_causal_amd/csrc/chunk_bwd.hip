@@ -23,34 +23,47 @@ namespace gdn {
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BV>
 struct RevSmem {
-  T K[CHUNK][D + Pad<T>::v];
-  T Q[CHUNK][D + Pad<T>::v];
-  T dO[CHUNK][BV + Pad<T>::v];
-  T dOg[CHUNK][BV + Pad<T>::v];   // scale * Gam_t * dO
+  T K[CHUNK][D + Pad<T>::v];      // K rows (A operand of K dS'^T)
+  T Kt[D][CHUNK + Pad<T>::v];     // K^T
+  T Qt[D][CHUNK + Pad<T>::v];     // Q^T
+  T dOt[BV][CHUNK + Pad<T>::v];   // dO^T block
+  T dOgt[BV][CHUNK + Pad<T>::v];  // (scale diag(Gam) dO)^T
   T dSb[BV][D + Pad<T>::v];       // dS' block (v-major)
   T dDt[BV][CHUNK + Pad<T>::v];   // dDelta^T
   T dRg[BV][CHUNK + Pad<T>::v];   // (diag(Gam) dR)^T
   double gam[CHUNK];
 };
 
+// Reverse pass, one workgroup per (value-row block, value head, sequence),
+// chunks in reverse order; chunk c-1's inputs are prefetched into registers
+// while chunk c computes.  Wave w owns token rows [16w, 16w+16) of the
+// (token x value) products; the P^T and M^T rows it needs are gathered from
+// the preparation's workspace straight into registers.
 template <typename T, int D, int BV>
 __global__ void __launch_bounds__(256) chunk_rev_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
     const double* __restrict__ gcum, const typename Compute<T>::type* __restrict__ Mw,
-    const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ dout, const float* __restrict__ dS_final, float* __restrict__ dS0,
-    T* __restrict__ dhst, T* __restrict__ ddw, T* __restrict__ dvo, int64_t lddv) {
+    const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ dout,
+    const float* __restrict__ dS_final, float* __restrict__ dS0, T* __restrict__ dhst,
+    T* __restrict__ ddw, T* __restrict__ dvo, int64_t lddv, int n_items) {
+  typedef typename Compute<T>::type CT;
+  typedef Mma<T> MM;
+  typedef FragKS<T, CT> FG;   // gathered rows of P^T, M^T
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RevSmem<T, D, BV>& sm = *reinterpret_cast<RevSmem<T, D, BV>*>(smem_raw);
-  constexpr int LD = D + Pad<T>::v, LDV = BV + Pad<T>::v, LDC = CHUNK + Pad<T>::v;
+  constexpr int LD = D + Pad<T>::v, LDC = CHUNK + Pad<T>::v;
+  constexpr int KS = MM::KS;
   constexpr int NVT = BV / 16;
   constexpr int NS = (D / 16) * NVT / 4;
-  constexpr int NA = (CHUNK / 16) * NVT / 4;
+  constexpr int NKD = D / KS, NKC = CHUNK / KS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int vb = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+  const int item = xcd_item(blockIdx.x, n_items);
+  const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
   const int kh = h / G;
   const int v0 = vb * BV;
-  const int rsub = 4 * (lane >> 4), ccol = lane & 15;
+  const int rsub = 4 * (lane >> 4), ccol = lane & 15, r16 = lane & 15;
+  const int trow = 16 * wave;
   const int64_t HvD = (int64_t)Hv * D;
 
   floatx4 dS[NS];  // dS^T tiles (d_k x BV)
@@ -64,15 +77,50 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
       dS[i][e] = dS_final ? dS_final[(((int64_t)n * Hv + h) * D + vv) * D + kk] : 0.f;
     }
   }
+
+  RowPrefetch<T, D> pk, pq;
+  RowPrefetch<T, BV> pdo;
+  typename FG::raw pP[NKC], pM[NKC];
+  double pg = 0.0;
+  auto prefetch = [&](int64_t c, int64_t t0, int L) {
+    pk.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
+    pq.load(q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+    pdo.load(dout + t0 * HvD + (int64_t)h * D + v0, HvD, L, tid);
+    const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + trow + r16;
+    const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + trow + r16;
+#pragma unroll
+    for (int s = 0; s < NKC; ++s) {
+      pP[s] = FG::load(Pc, CHUNK, s * KS, lane);   // P^T row t = column t of P
+      pM[s] = FG::load(Mc, CHUNK, s * KS, lane);
+    }
+    const int tg = tid & (CHUNK - 1);
+    pg = gcum[(t0 + (tg < L ? tg : L - 1)) * Hv + h];
+  };
   const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
+  auto span = [&](int64_t c, int64_t& t0, int& L) {
+    t0 = (int64_t)cu[n] + CHUNK * (c - c_begin);
+    const int64_t rem = (int64_t)cu[n + 1] - t0;
+    L = rem < CHUNK ? (int)rem : CHUNK;
+  };
+  if (c_begin < c_end) {
+    int64_t t0;
+    int L;
+    span(c_end - 1, t0, L);
+    prefetch(c_end - 1, t0, L);
+  }
   for (int64_t c = c_end - 1; c >= c_begin; --c) {
-    const int64_t t0 = (int64_t)cu[n] + CHUNK * (c - c_begin);
-    const int L = (int64_t)cu[n + 1] - t0 < CHUNK ? (int)((int64_t)cu[n + 1] - t0) : CHUNK;
+    int64_t t0;
+    int L;
+    span(c, t0, L);
     __syncthreads();
-    stage_rows<T, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-    stage_rows<T, D>(&sm.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
-    stage_rows<T, BV>(&sm.dO[0][0], LDV, dout + t0 * HvD + (int64_t)h * D + v0, HvD, L, tid);
-    if (tid < CHUNK) sm.gam[tid] = gcum[(t0 + (tid < L ? tid : L - 1)) * Hv + h];
+    pk.store(&sm.K[0][0], LD, tid);
+    store_rows_transposed(pk, &sm.Kt[0][0], LDC, tid);
+    store_rows_transposed(pq, &sm.Qt[0][0], LDC, tid);
+    store_rows_transposed(pdo, &sm.dOt[0][0], LDC, tid);
+    if (tid < CHUNK) sm.gam[tid] = pg;
+    typename FG::raw cP[NKC], cM[NKC];
+#pragma unroll
+    for (int s = 0; s < NKC; ++s) { cP[s] = pP[s]; cM[s] = pM[s]; }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
@@ -82,25 +130,32 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) hp[(int64_t)e * D] = from_f<T>(dS[i][e]);
     }
+    if (c - 1 >= c_begin) {
+      int64_t t1;
+      int L1;
+      span(c - 1, t1, L1);
+      prefetch(c - 1, t1, L1);
+    }
     __syncthreads();
 
-    // scaled copy of dO for the state gradient
+    // scaled copy of dO^T for the state gradient
     for (int i = tid; i < CHUNK * BV; i += 256) {
-      const int t = i / BV, vv = i % BV;
-      sm.dOg[t][vv] = from_f<T>(scale * dexp<T>(sm.gam[t]) * to_f(sm.dO[t][vv]));
+      const int vv = i / CHUNK, t = i % CHUNK;
+      sm.dOgt[vv][t] = from_f<T>(scale * dexp<T>(sm.gam[t]) * to_f(sm.dOt[vv][t]));
     }
     // Phase A: dDelta = P^T dO + diag(dec) K dS'^T
-    const auto* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
-    const auto* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
     const double gl = sm.gam[CHUNK - 1];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-      floatx4 pt = tile_mma<T, false, false>(zero4(), Pc, CHUNK, &sm.dO[0][0], LDV, 16 * tt,
-                                             16 * vt, CHUNK, lane);
-      floatx4 kd = tile_mma<T, true, true>(zero4(), &sm.K[0][0], LD, &sm.dSb[0][0], LD, 16 * tt,
-                                           16 * vt, D, lane);
-      const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
+    for (int vt = 0; vt < NVT; ++vt) {
+      floatx4 pt = zero4(), kd = zero4();
+#pragma unroll
+      for (int s = 0; s < NKC; ++s)
+        pt = MM::mma(FG::cvt(cP[s]), MM::kc(&sm.dOt[16 * vt + r16][0], s * KS, lane), pt);
+#pragma unroll
+      for (int s = 0; s < NKD; ++s)
+        kd = MM::mma(MM::kc(&sm.K[trow + r16][0], s * KS, lane),
+                     MM::kc(&sm.dSb[16 * vt + r16][0], s * KS, lane), kd);
+      const int vv = 16 * vt + ccol, tb = trow + rsub;
       float dd[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) dd[e] = pt[e] + dexp<T>(gl - sm.gam[tb + e]) * kd[e];
@@ -113,11 +168,12 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
 
     // Phase B: dR = M^T dDelta  (this is dv)
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-      floatx4 dr = tile_mma<T, false, true>(zero4(), Mc, CHUNK, &sm.dDt[0][0], LDC, 16 * tt,
-                                            16 * vt, CHUNK, lane);
-      const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
+    for (int vt = 0; vt < NVT; ++vt) {
+      floatx4 dr = zero4();
+#pragma unroll
+      for (int s = 0; s < NKC; ++s)
+        dr = MM::mma(FG::cvt(cM[s]), MM::kc(&sm.dDt[16 * vt + r16][0], s * KS, lane), dr);
+      const int vv = 16 * vt + ccol, tb = trow + rsub;
       float rg[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -133,14 +189,16 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
+      floatx4 qd = zero4(), kr = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dS[i][e] *= GL;
-      dS[i] = tile_mma<T, false, false>(dS[i], &sm.Q[0][0], LD, &sm.dOg[0][0], LDV, 16 * kt,
-                                        16 * vt, CHUNK, lane);
-      floatx4 kr = tile_mma<T, false, true>(zero4(), &sm.K[0][0], LD, &sm.dRg[0][0], LDC, 16 * kt,
-                                            16 * vt, CHUNK, lane);
+      for (int s = 0; s < NKC; ++s) {
+        qd = MM::mma(MM::kc(&sm.Qt[16 * kt + r16][0], s * KS, lane),
+                     MM::kc(&sm.dOgt[16 * vt + r16][0], s * KS, lane), qd);
+        kr = MM::mma(MM::kc(&sm.Kt[16 * kt + r16][0], s * KS, lane),
+                     MM::kc(&sm.dRg[16 * vt + r16][0], s * KS, lane), kr);
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dS[i][e] -= kr[e];
+      for (int e = 0; e < 4; ++e) dS[i][e] = GL * dS[i][e] + qd[e] - kr[e];
     }
   }
   if (dS0) {
@@ -154,7 +212,12 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Chunk-parallel gradients: one workgroup per (chunk, key head).
+// Chunk-parallel gradients: one workgroup per (chunk, key head), looping over
+// the key head's value heads in ascending order so dq and dk accumulate in
+// registers without atomics.  Per value head: Tinv is recomputed in fp32
+// (blocked inverse), then the 64 x 64 gradient matrices, then the
+// (token x key) products.  The global tiles of the next phase are loaded
+// into registers one phase ahead.
 template <typename T, int D>
 struct GradSmem {
   T Kt[D][CHUNK + Pad<T>::v];      // K^T (k-major)
@@ -167,11 +230,8 @@ struct GradSmem {
       T B2[CHUNK][D + Pad<T>::v];
       T B3[CHUNK][D + Pad<T>::v];
     } t;
-    struct {
-      T Krm[CHUNK][D + Pad<T>::v];  // only while forming K K^T and Q K^T
-      T Qrm[CHUNK][D + Pad<T>::v];
-    } s;
-    float Y[CHUNK][68];            // dTinv Tinv^T (B1/B2 are free while it lives)
+    T Krm[CHUNK][D + Pad<T>::v];   // K rows, only while forming K K^T
+    float Y[CHUNK][68];            // dTinv Tinv^T (B1/B2 are dead while it lives)
   } u;
   T WA[CHUNK][CHUNK + Pad<T>::v];
   T dPD[CHUNK][CHUNK + Pad<T>::v];
@@ -180,24 +240,35 @@ struct GradSmem {
   float bet[CHUNK];
   float rowA[CHUNK], rowB[CHUNK];
   float colA[4][CHUNK], colB[4][CHUNK], rowX[4][CHUNK];
-  float zp[4][64];
-  float ip[256];
+  float red[2][4];                 // per-wave partial sums: z, <dS', S>
 };
 
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256) chunk_grad_kernel(
+__global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G,
     float scale, const double* __restrict__ gcum, const float* __restrict__ beta,
-    const T* __restrict__ hst, const T* __restrict__ dhst, const T* __restrict__ Rw,
-    const T* __restrict__ Dlw, const T* __restrict__ ddw, const T* __restrict__ dout,
-    const T* __restrict__ dvo, int64_t lddv, T* __restrict__ dq, T* __restrict__ dk, int64_t lddq,
-    int64_t lddk, float* __restrict__ dg, float* __restrict__ dbeta) {
+    const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ hst,
+    const T* __restrict__ dhst, const T* __restrict__ Rw, const T* __restrict__ Dlw,
+    const T* __restrict__ ddw, const T* __restrict__ dout, const T* __restrict__ dvo, int64_t lddv,
+    T* __restrict__ dq, T* __restrict__ dk, int64_t lddq, int64_t lddk, float* __restrict__ dg,
+    float* __restrict__ dbeta, void* __restrict__ sink) {
+  typedef typename Compute<T>::type CT;
+  typedef Mma<T> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   GradSmem<T, D>& sm = *reinterpret_cast<GradSmem<T, D>*>(smem_raw);
   constexpr int LD = D + Pad<T>::v, LDC = CHUNK + Pad<T>::v;
+  constexpr int KS = MM::KS;
+  constexpr int NKD = D / KS;
   constexpr int NQ = (CHUNK / 16) * (D / 16) / 4;  // (t x k) tiles per wave
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x;
   const int kh = blockIdx.y;
   if (c >= seq_off[n_seq]) return;
@@ -205,49 +276,60 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
   int L;
   chunk_span(seq_off, cu, n_seq, c, t0, L);
   const int rbase = 16 * wave + 4 * (lane >> 4), ccol = lane & 15, rsub = 4 * (lane >> 4);
+  const int r16 = lane & 15;
   const int64_t HvD = (int64_t)Hv * D;
 
-  // Stage K, Q (row-major for the Gram products) and their transposes.
-  for (int i = tid; i < CHUNK * (D / 8); i += 256) {
-    const int r = i / (D / 8), c8 = (i % (D / 8)) * 8;
-    f8 kv, qv;
-    if (r < L) {
-      kv = load8(k + (t0 + r) * ldk + (int64_t)kh * D + c8);
-      qv = load8(q + (t0 + r) * ldq + (int64_t)kh * D + c8);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kv.v[j] = qv.v[j] = 0.f;
-    }
-    store8(&sm.u.s.Krm[r][c8], kv);
-    store8(&sm.u.s.Qrm[r][c8], qv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sm.Kt[c8 + j][r] = from_f<T>(kv.v[j]);
-      sm.Qt[c8 + j][r] = from_f<T>(qv.v[j]);
-    }
+  // Stage K rows (for K K^T) and the transposes of K and Q.
+  {
+    RowPrefetch<T, D> pk, pq;
+    pk.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
+    pq.load(q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+    pk.store(&sm.u.Krm[0][0], LD, tid);
+    store_rows_transposed(pk, &sm.Kt[0][0], LDC, tid);
+    store_rows_transposed(pq, &sm.Qt[0][0], LDC, tid);
   }
   __syncthreads();
-  floatx4 kk[4], qk[4];
+  floatx4 kk[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kk[j] = tile_mma<T, true, true>(zero4(), &sm.u.s.Krm[0][0], LD, &sm.u.s.Krm[0][0], LD,
-                                    16 * wave, 16 * j, D, lane);
-    qk[j] = tile_mma<T, true, true>(zero4(), &sm.u.s.Qrm[0][0], LD, &sm.u.s.Krm[0][0], LD,
-                                    16 * wave, 16 * j, D, lane);
-  }
+  for (int j = 0; j < 4; ++j)
+    kk[j] = tile_mma<T, true, true>(zero4(), &sm.u.Krm[0][0], LD, &sm.u.Krm[0][0], LD, 16 * wave,
+                                    16 * j, D, lane);
   floatx4 dQa[NQ], dKa[NQ];
 #pragma unroll
   for (int i = 0; i < NQ; ++i) dQa[i] = dKa[i] = zero4();
   __syncthreads();
 
+  // prefetch registers: P2 tiles (dDelta, R) and P4 tiles (dO, Delta, dR)
+  RowPrefetch<T, D> f_dd, f_r, f_do, f_dl, f_dr;
+  auto prefetch_p2 = [&](int h) {
+    const int64_t base = t0 * HvD + (int64_t)h * D;
+    f_dd.load(ddw + base, HvD, L, tid);
+    f_r.load(Rw + base, HvD, L, tid);
+  };
+  prefetch_p2(kh * G);
+
   for (int hh = 0; hh < G; ++hh) {
     const int h = kh * G + hh;
-    // ---- P0: gate values for the chunk
+    // Address arithmetic derived from a laundered thread index stays inside
+    // the loop instead of being hoisted (and spilled) as loop invariants.
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int rbase = 16 * wave + 4 * (lane >> 4), ccol = lane & 15, rsub = 4 * (lane >> 4);
+    const int r16 = lane & 15;
+    // ---- P0: gate values for the chunk; P values at this lane's positions
     if (wave == 0) {
       sm.gam[lane] = gcum[(t0 + (lane < L ? lane : L - 1)) * Hv + h];
       sm.bet[lane] = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
     }
     if (tid < CHUNK) { sm.rowA[tid] = 0.f; sm.rowB[tid] = 0.f; }
+    CT pval[4][4];
+    {
+      const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pval[j][e] = Pc[(rbase + e) * CHUNK + 16 * j + ccol];
+    }
     __syncthreads();
     // ---- P1: A, then Tinv
 #pragma unroll
@@ -262,11 +344,15 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
     __syncthreads();
     invert_unit_lower(sm.Sc1, sm.Tm, sm.X, tid);
     // ---- P2: dM = dDelta R^T
+    f_dd.store(&sm.u.t.B1[0][0], LD, tid);
+    f_r.store(&sm.u.t.B2[0][0], LD, tid);
     {
       const int64_t base = t0 * HvD + (int64_t)h * D;
-      stage_rows<T, D>(&sm.u.t.B1[0][0], LD, ddw + base, HvD, L, tid);
-      stage_rows<T, D>(&sm.u.t.B2[0][0], LD, Rw + base, HvD, L, tid);
+      f_do.load(dout + base, HvD, L, tid);
+      f_dl.load(Dlw + base, HvD, L, tid);
+      f_dr.load(dvo + t0 * lddv + (int64_t)h * D, lddv, L, tid);
     }
+    issue_fence();
     __syncthreads();
     {
       float cb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -281,6 +367,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
           cb[j] += dm[e] * sm.Tm[t][s];
           sm.Sc1[t][s] = (s < t) ? dm[e] * sm.bet[s] : 0.f;
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -298,6 +385,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
                                           16 * j, CHUNK, lane);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.u.Y[rbase + e][16 * j + ccol] = y[e];
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     {
@@ -324,6 +412,7 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
           }
           sm.WA[t][s] = from_f<T>(wa);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -340,12 +429,11 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
     }
     __syncthreads();
     // ---- P4: dP = dO Delta^T
-    {
-      const int64_t base = t0 * HvD + (int64_t)h * D;
-      stage_rows<T, D>(&sm.u.t.B1[0][0], LD, dout + base, HvD, L, tid);
-      stage_rows<T, D>(&sm.u.t.B2[0][0], LD, Dlw + base, HvD, L, tid);
-      stage_rows<T, D>(&sm.u.t.B3[0][0], LD, dvo + t0 * lddv + (int64_t)h * D, lddv, L, tid);
-    }
+    f_do.store(&sm.u.t.B1[0][0], LD, tid);
+    f_dl.store(&sm.u.t.B2[0][0], LD, tid);
+    f_dr.store(&sm.u.t.B3[0][0], LD, tid);
+    prefetch_p2(hh + 1 < G ? h + 1 : h);   // unconditional: re-reads on the last head
+    issue_fence();
     __syncthreads();
     {
       float ca[4] = {0.f, 0.f, 0.f, 0.f}, ra[4] = {0.f, 0.f, 0.f, 0.f};
@@ -360,13 +448,14 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
           float v = 0.f;
           if (s <= t) {
             const float Dts = dexp<T>(sm.gam[t] - sm.gam[s]);
-            const float E = dp[e] * Dts * scale * qk[j][e];
+            const float E = dp[e] * to_f(pval[j][e]);
             ra[e] += E;
             ca[j] -= E;
             v = dp[e] * Dts;
           }
           sm.dPD[t][s] = from_f<T>(v);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -382,7 +471,9 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
       }
     }
     __syncthreads();
-    // ---- P5: (t x k) products
+    // ---- P5: (token x key) products; tile (tt, kt), wave w owns tiles
+    //      w*NQ .. w*NQ+NQ-1 (tt fastest), so the S / dS' columns it reads
+    //      from memory change only when kt does.
     {
       const T* Sg = hst + ((int64_t)c * Hv + h) * D * D;   // [k][v]
       const T* dSg = dhst + ((int64_t)c * Hv + h) * D * D;
@@ -392,21 +483,44 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) rx[a][e] = 0.f;
-      float zs = 0.f;
+      float zs = 0.f, ipv = 0.f;
+      typename MM::frag sf[NKD], dsf[NKD];
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
         const int id = wave * NQ + i, tt = id % 4, kt = id / 4;
-        floatx4 x1 = tile_mma<T, true, true>(zero4(), &sm.u.t.B1[0][0], LD, Sg, D, 16 * tt, 16 * kt, D, lane);
-        floatx4 x2 = tile_mma<T, true, true>(zero4(), &sm.u.t.B3[0][0], LD, Sg, D, 16 * tt, 16 * kt, D, lane);
-        floatx4 x3 = tile_mma<T, true, true>(zero4(), &sm.u.t.B2[0][0], LD, dSg, D, 16 * tt, 16 * kt, D, lane);
+        if (i == 0 || tt == 0) {
+#pragma unroll
+          for (int s = 0; s < NKD; ++s) {
+            sf[s] = MM::kc(Sg + (int64_t)(16 * kt + r16) * D, s * KS, lane);
+            dsf[s] = MM::kc(dSg + (int64_t)(16 * kt + r16) * D, s * KS, lane);
+          }
+          if (tt == 0) {   // each (v, k) element once over the workgroup
+#pragma unroll
+            for (int s = 0; s < NKD; ++s) {
+              if constexpr (KS == 4) {
+                ipv += to_f(sf[s]) * to_f(dsf[s]);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ipv += (float)sf[s][j] * (float)dsf[s][j];
+              }
+            }
+          }
+        }
+        floatx4 x1 = zero4(), x2 = zero4(), x3 = zero4();
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) {
+          x1 = MM::mma(MM::kc(&sm.u.t.B1[16 * tt + r16][0], s * KS, lane), sf[s], x1);
+          x2 = MM::mma(MM::kc(&sm.u.t.B3[16 * tt + r16][0], s * KS, lane), sf[s], x2);
+          x3 = MM::mma(MM::kc(&sm.u.t.B2[16 * tt + r16][0], s * KS, lane), dsf[s], x3);
+        }
         floatx4 pq = tile_mma<T, false, true>(zero4(), &sm.dPD[0][0], LDC, &sm.Qt[0][0], LDC, 16 * tt,
                                               16 * kt, CHUNK, lane);
-        dQa[i] = tile_mma<T, true, true>(dQa[i], &sm.dPD[0][0], LDC, &sm.Kt[0][0], LDC, 16 * tt, 16 * kt,
-                                         CHUNK, lane);
-        dKa[i] = tile_mma<T, true, true>(dKa[i], &sm.WA[0][0], LDC, &sm.Kt[0][0], LDC, 16 * tt, 16 * kt,
-                                         CHUNK, lane);
-        dKa[i] = tile_mma<T, false, true>(dKa[i], &sm.WA[0][0], LDC, &sm.Kt[0][0], LDC, 16 * tt, 16 * kt,
-                                          CHUNK, lane);
+        dQa[i] = tile_mma<T, true, true>(dQa[i], &sm.dPD[0][0], LDC, &sm.Kt[0][0], LDC, 16 * tt,
+                                         16 * kt, CHUNK, lane);
+        dKa[i] = tile_mma<T, true, true>(dKa[i], &sm.WA[0][0], LDC, &sm.Kt[0][0], LDC, 16 * tt,
+                                         16 * kt, CHUNK, lane);
+        dKa[i] = tile_mma<T, false, true>(dKa[i], &sm.WA[0][0], LDC, &sm.Kt[0][0], LDC, 16 * tt,
+                                          16 * kt, CHUNK, lane);
         const int kc = 16 * kt + ccol;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -420,8 +534,8 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
           rx[tt][e] += Gm * scale * x1[e] * qv - Gm * x2[e] * kv - z;
           zs += z;
         }
+        __builtin_amdgcn_sched_barrier(0);  // bound live ranges: one tile at a time
       }
-      // per-wave row partials over this wave's k columns
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -429,15 +543,9 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
           const float x = sum16(rx[a][e]);
           if (ccol == 0) sm.rowX[wave][16 * a + rsub + e] = x;
         }
-      sm.zp[wave][lane] = zs;
-      // <dS', S> for the Gam_L term
-      float ipv = 0.f;
-      for (int i = tid; i < D * D / 8; i += 256) {
-        f8 a = load8(Sg + i * 8), b = load8(dSg + i * 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ipv += a.v[j] * b.v[j];
-      }
-      sm.ip[tid] = ipv;
+      zs = wave_sum(zs);
+      ipv = wave_sum(ipv);
+      if (lane == 0) { sm.red[0][wave] = zs; sm.red[1][wave] = ipv; }
     }
     __syncthreads();
     // ---- P6: assemble dgam -> dg (reverse cumsum), dbeta
@@ -450,9 +558,8 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
         dgm += sm.colA[w][t] + sm.rowX[w][t];
         db += sm.colB[w][t];
       }
-      float zsum = 0.f, ips = 0.f;
-      for (int i = 0; i < 4 * 64; ++i) zsum += (&sm.zp[0][0])[i];
-      for (int i = 0; i < 256; ++i) ips += sm.ip[i];
+      const float zsum = sm.red[0][0] + sm.red[0][1] + sm.red[0][2] + sm.red[0][3];
+      const float ips = sm.red[1][0] + sm.red[1][1] + sm.red[1][2] + sm.red[1][3];
       if (t == L - 1) dgm += zsum + dexp<T>(sm.gam[CHUNK - 1]) * ips;
       if (t >= L) dgm = 0.f;
       const float dgs = wave_suffix_scan(dgm, lane);
@@ -463,6 +570,9 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
     }
     __syncthreads();
   }
+  // Never taken: keeps the last prefetch live on the exit path (see the
+  // state kernel).
+  if (G < 0) *reinterpret_cast<Raw8<T>*>(sink) = f_dd.r[0];
   // write dq = scale * dQa, dk = dKa
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
@@ -471,10 +581,10 @@ __global__ void __launch_bounds__(256) chunk_grad_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * tt + rsub + e;
-      if (t < L) {
-        dq[(t0 + t) * lddq + (int64_t)kh * D + kc] = from_f<T>(scale * dQa[i][e]);
-        dk[(t0 + t) * lddk + (int64_t)kh * D + kc] = from_f<T>(dKa[i][e]);
-      }
+      *row_or_sink(dq + (t0 + t) * lddq + (int64_t)kh * D + kc, t < L, sink, tid) =
+          from_f<T>(scale * dQa[i][e]);
+      *row_or_sink(dk + (t0 + t) * lddk + (int64_t)kh * D + kc, t < L, sink, tid) =
+          from_f<T>(dKa[i][e]);
     }
   }
 }
@@ -496,12 +606,13 @@ hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const voi
     const size_t shm = sizeof(RevSmem<T, D, BV>);
     auto kern = chunk_rev_kernel<T, D, BV>;
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(kern, dim3(D / BV, s.hv, s.n_seq), dim3(256), shm, st, (const T*)q,
-                       (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.hv,
-                       s.hv / s.hk, scale, (const double*)(ws + Ly.gcum),
+    const int n_items = (D / BV) * s.hv * s.n_seq;
+    hipLaunchKernelGGL(kern, dim3(n_items), dim3(256), shm, st, (const T*)q, (const T*)k, ldq,
+                       ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
+                       (const double*)(ws + Ly.gcum),
                        (const typename Compute<T>::type*)(ws + Ly.mw),
                        (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)dout, dS_final,
-                       dS0, (T*)(ws + Ly.dh), (T*)(ws + Ly.ddw), (T*)dv, lddv);
+                       dS0, (T*)(ws + Ly.dh), (T*)(ws + Ly.ddw), (T*)dv, lddv, n_items);
     return hipGetLastError();
   });
 }
@@ -524,9 +635,10 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
     hipLaunchKernelGGL(kern, dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm, st, (const T*)q,
                        (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
                        s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), beta,
-                       (const T*)(ws + Ly.h), (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw),
-                       (const T*)(ws + Ly.dlw), (const T*)(ws + Ly.ddw), (const T*)dout,
-                       (const T*)dv, lddv, (T*)dq, (T*)dk, lddq, lddk, dg, dbeta);
+                       (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)(ws + Ly.h),
+                       (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw), (const T*)(ws + Ly.dlw),
+                       (const T*)(ws + Ly.ddw), (const T*)dout, (const T*)dv, lddv, (T*)dq,
+                       (T*)dk, lddq, lddk, dg, dbeta, (void*)(ws + Ly.sink));
     return hipGetLastError();
   });
 }

@@ -42,10 +42,21 @@ struct ChunkLayout {
   size_t mw, pw;      // T [nt_max][hv][64][64]: M = Tinv diag(beta), P
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
   size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
+  size_t sink;        // SINK_ELEMS scratch floats: target of stores for padding rows
   size_t total_fwd, total_bwd;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Stores for rows past the end of a sequence (padding rows of the last
+// chunk) go to a scratch "sink" instead of being skipped: every store is then
+// unconditional, which keeps the compiler's memory-counter waits exact so
+// that prefetched loads stay in flight across the chunk.  Nothing reads it.
+constexpr int SINK_ELEMS = 4096;
+template <typename T>
+__device__ __forceinline__ T* row_or_sink(T* p, bool valid, void* sink, int tid) {
+  return valid ? p : reinterpret_cast<T*>(sink) + (tid & (SINK_ELEMS - 1));
+}
 
 inline ChunkLayout chunk_layout(const gdn_shape& s) {
   ChunkLayout L;
@@ -54,6 +65,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.nt_max = T / CHUNK + s.n_seq;
   size_t off = 0;
   L.seq_off = off; off = align256(off + sizeof(int32_t) * (size_t)(s.n_seq + 1));
+  L.sink = off; off = align256(off + sizeof(float) * SINK_ELEMS);
   L.gcum = off; off = align256(off + sizeof(double) * (size_t)T * s.hv);
   L.mw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.pw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
@@ -111,6 +123,150 @@ __device__ __forceinline__ void stage_rows(TD* dst, int ld_s, const TS* src, int
     }
     store8(dst + r * ld_s + c8, v);
   }
+}
+
+// ---- register prefetch ------------------------------------------------------
+// The sequential kernels load chunk c+1 into registers while chunk c computes,
+// so global-memory latency leaves the critical path.  Raw copies keep the
+// storage type; conversion happens when the registers are consumed.
+
+// 8 consecutive storage elements (one 16-byte vector; two for fp32).
+template <typename T> struct Raw8 { uint4 v[sizeof(T) / 2]; };
+template <typename T> __device__ __forceinline__ Raw8<T> ld_raw8(const T* p) {
+  Raw8<T> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = reinterpret_cast<const uint4*>(p)[i];
+  return r;
+}
+template <typename T> __device__ __forceinline__ Raw8<T> zero_raw8() {
+  Raw8<T> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = make_uint4(0, 0, 0, 0);
+  return r;
+}
+template <typename T> __device__ __forceinline__ f8 raw_f8(const Raw8<T>& r) {
+  return load8(reinterpret_cast<const T*>(&r.v[0]));
+}
+
+// Rows [0, 64) x [0, W) of a token-major tensor, 8 elements per item, items
+// spread over the 256 threads.  Loads are unconditional (rows >= L re-read
+// row L-1, which is valid memory) so that no wait is forced at load time;
+// rows >= L are zeroed when the registers are stored.
+template <typename T, int W> struct RowPrefetch {
+  static constexpr int ITEMS = CHUNK * W / 8;
+  static constexpr int NI = ITEMS / 256;
+  static_assert(ITEMS % 256 == 0, "row prefetch covers whole rows per thread");
+  Raw8<T> r[NI];
+  int L;
+  __device__ __forceinline__ void load(const T* src, int64_t ld, int L_, int tid) {
+    L = L_;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int i = tid + 256 * j;
+      const int row = i / (W / 8), c8 = (i % (W / 8)) * 8;
+      r[j] = ld_raw8(src + (int64_t)(row < L ? row : L - 1) * ld + c8);
+    }
+  }
+  __device__ __forceinline__ f8 value(int j, int row) const {
+    f8 v = raw_f8(r[j]);
+    if (row >= L) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v.v[u] = 0.f;
+    }
+    return v;
+  }
+  template <typename TD>
+  __device__ __forceinline__ void store(TD* dst, int ld_s, int tid) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int i = tid + 256 * j;
+      const int row = i / (W / 8);
+      store8(dst + row * ld_s + (i % (W / 8)) * 8, value(j, row));
+    }
+  }
+};
+
+// One MFMA A/B fragment read from memory with contiguous K, kept raw until
+// use.  16-bit operands: 8 values (16 bytes) of storage type S converted to
+// CT; fp32 operands: one value.
+template <typename CT, typename S> struct FragKC {
+  typedef uint4 raw;
+  __device__ __forceinline__ static raw load(const S* row, int k0, int lane) {
+    return *reinterpret_cast<const uint4*>(row + k0 + 8 * (lane >> 4));
+  }
+  __device__ __forceinline__ static typename Mma<CT>::frag cvt(const raw& r) {
+    if constexpr (__is_same(S, CT)) {
+      return __builtin_bit_cast(typename Mma<CT>::frag, r);
+    } else {
+      f8 v = load8(reinterpret_cast<const S*>(&r));
+      typename Mma<CT>::frag f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = (CT)v.v[j];
+      return f;
+    }
+  }
+};
+template <> struct FragKC<float, float> {
+  typedef float raw;
+  __device__ __forceinline__ static raw load(const float* row, int k0, int lane) {
+    return row[k0 + (lane >> 4)];
+  }
+  __device__ __forceinline__ static float cvt(const raw& r) { return r; }
+};
+
+// Same, for a fragment whose K index is strided by ld in memory (8 scalar
+// loads for 16-bit operands; the raw values stay untouched until use).
+template <typename MT, typename S> struct FragKS {
+  struct raw { S x[8]; };
+  __device__ __forceinline__ static raw load(const S* col, int ld, int k0, int lane) {
+    raw r;
+    const S* p = col + (int64_t)(k0 + 8 * (lane >> 4)) * ld;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.x[j] = p[(int64_t)j * ld];
+    return r;
+  }
+  __device__ __forceinline__ static typename Mma<MT>::frag cvt(const raw& r) {
+    typename Mma<MT>::frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (MT)to_f(r.x[j]);
+    return f;
+  }
+};
+template <typename S> struct FragKS<float, S> {
+  typedef S raw;
+  __device__ __forceinline__ static raw load(const S* col, int ld, int k0, int lane) {
+    return col[(int64_t)(k0 + (lane >> 4)) * ld];
+  }
+  __device__ __forceinline__ static float cvt(const raw& r) { return to_f(r); }
+};
+
+// Transposed staging of prefetched rows: dst[col][row] (row stride ld_s).
+template <typename T, int W, typename TD>
+__device__ __forceinline__ void store_rows_transposed(const RowPrefetch<T, W>& p, TD* dst, int ld_s,
+                                                      int tid) {
+#pragma unroll
+  for (int j = 0; j < RowPrefetch<T, W>::NI; ++j) {
+    const int i = tid + 256 * j;
+    const int row = i / (W / 8), c8 = (i % (W / 8)) * 8;
+    const f8 v = p.value(j, row);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[(c8 + u) * ld_s + row] = from_f<TD>(v.v[u]);
+  }
+}
+
+// Keeps already-issued prefetch loads where they are: neither the optimizer
+// nor the machine scheduler may move memory operations or instructions across
+// it (otherwise the loads get sunk next to their first use).
+__device__ __forceinline__ void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup -> work item so that consecutive work items (the value-row
+// blocks of one head) run on the same XCD: workgroups are dealt to the 8
+// XCDs round-robin, so item = xcd * (n / 8) + (block / 8) when n % 8 == 0.
+__device__ __forceinline__ int xcd_item(int block, int n) {
+  return (n % 8 == 0) ? (block % 8) * (n / 8) + block / 8 : block;
 }
 
 // (I + A)^-1 for strictly lower-triangular A (64 x 64, fp32 in LDS, row

@@ -124,9 +124,11 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
 // ---------------------------------------------------------------------------
 // Sequential state pass, one workgroup per (value-row block, value head,
 // sequence).  The state block S[vb*BV : vb*BV+BV, :] lives in MFMA
-// accumulators as S^T tiles (d_k rows x BV columns) for the whole sequence;
-// each chunk stages K (and Q) in LDS and reads M, P rows straight from the
-// workspace.
+// accumulators as S^T tiles (d_k rows x BV columns) for the whole sequence.
+// Wave w owns token rows [16w, 16w+16) of every (token x value) product, so
+// its A operands (Q, M, P rows) come straight from memory into registers;
+// K is staged in LDS because the state update reads it transposed.
+// Chunk c+1's inputs are loaded into registers while chunk c computes.
 //   MODE 0 (forward): writes o and S_final.
 //   MODE 1 (backward recompute): writes the chunk-start states h ([dk][dv]
 //   per chunk and head), R and Delta.
@@ -134,8 +136,6 @@ template <typename T, int D, int BV>
 struct StateSmem {
   typedef typename Compute<T>::type CT;
   CT K[CHUNK][D + Pad<CT>::v];
-  CT Q[CHUNK][D + Pad<CT>::v];
-  CT V[CHUNK][BV + Pad<CT>::v];
   CT Sb[BV][D + Pad<CT>::v];       // S block (v-major), MFMA B operand of K S^T
   CT Rt[BV][CHUNK + Pad<CT>::v];   // R^T
   CT Dt[BV][CHUNK + Pad<CT>::v];   // Delta^T
@@ -150,20 +150,27 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
     int Hv, int G, float scale, const double* __restrict__ gcum,
     const typename Compute<T>::type* __restrict__ Mw, const typename Compute<T>::type* __restrict__ Pw,
     const float* __restrict__ S0, float* __restrict__ S_final, T* __restrict__ o,
-    T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw) {
+    T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw, void* __restrict__ sink,
+    int n_items) {
   typedef typename Compute<T>::type CT;
+  typedef Mma<CT> MM;
+  typedef FragKC<CT, T> FQ;     // Q rows (storage type)
+  typedef FragKC<CT, CT> FM;    // M, P rows (compute type)
   extern __shared__ __align__(16) unsigned char smem_raw[];
   StateSmem<T, D, BV>& sm = *reinterpret_cast<StateSmem<T, D, BV>*>(smem_raw);
-  constexpr int LD = D + Pad<CT>::v, LDV = BV + Pad<CT>::v, LDC = CHUNK + Pad<CT>::v;
-  constexpr int NVT = BV / 16;                      // value tiles
+  constexpr int LD = D + Pad<CT>::v, LDC = CHUNK + Pad<CT>::v;
+  constexpr int KS = MM::KS;
+  constexpr int NVT = BV / 16;                      // value tiles per wave (rows fixed)
   constexpr int NS = (D / 16) * NVT / 4;            // state tiles per wave
-  constexpr int NA = (CHUNK / 16) * NVT / 4;        // token x value tiles per wave
-  static_assert(NS >= 1 && NA >= 1, "tile split");
+  constexpr int NKD = D / KS, NKC = CHUNK / KS;     // MFMA steps over d_k and over the chunk
+  static_assert(NS >= 1, "tile split");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int vb = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+  const int item = xcd_item(blockIdx.x, n_items);
+  const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
   const int kh = h / G;
   const int v0 = vb * BV;
-  const int rsub = 4 * (lane >> 4), ccol = lane & 15;
+  const int rsub = 4 * (lane >> 4), ccol = lane & 15, r16 = lane & 15;
+  const int trow = 16 * wave;                       // this wave's token rows
   const int64_t HvD = (int64_t)Hv * D;
 
   floatx4 S[NS];
@@ -178,15 +185,56 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
     }
   }
 
+  // ---- prefetch registers for one chunk
+  struct Pref {
+    RowPrefetch<T, D> k;                   // K rows -> LDS
+    typename FQ::raw q[NKD];               // Q fragments (MODE 0)
+    typename FM::raw m[NKC], p[NKC];       // M, P fragments
+    T v[NVT][4];                           // V at this lane's output positions (raw)
+    double g;                              // gam[tid & 63]
+    int L;
+    int64_t t0;
+  };
   const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    const int64_t t0 = (int64_t)cu[n] + CHUNK * (c - c_begin);
-    const int L = (int64_t)cu[n + 1] - t0 < CHUNK ? (int)((int64_t)cu[n + 1] - t0) : CHUNK;
-    __syncthreads();
-    stage_rows<CT, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-    if (MODE == 0) stage_rows<CT, D>(&sm.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
-    stage_rows<CT, BV>(&sm.V[0][0], LDV, v + t0 * ldv + (int64_t)h * D + v0, ldv, L, tid);
-    if (tid < CHUNK) sm.gam[tid] = gcum[(t0 + (tid < L ? tid : L - 1)) * Hv + h];
+  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
+  auto prefetch = [&](Pref& P, int64_t c) {
+    P.t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - P.t0;
+    const int L = rem < CHUNK ? (int)rem : CHUNK;
+    const int64_t t0 = P.t0;
+    P.L = L;
+    P.k.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
+    const int tq = trow + r16 < L ? trow + r16 : L - 1;   // clamp: rows >= L never reach outputs
+    if (MODE == 0) {
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) P.q[s] = FQ::load(q + (t0 + tq) * ldq + (int64_t)kh * D, s * KS, lane);
+    }
+    const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + (trow + r16) * CHUNK;
+    const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + (trow + r16) * CHUNK;
+#pragma unroll
+    for (int s = 0; s < NKC; ++s) {
+      P.m[s] = FM::load(Mc, s * KS, lane);
+      if (MODE == 0) P.p[s] = FM::load(Pc, s * KS, lane);
+    }
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = trow + rsub + e;
+        P.v[vt][e] = v[(t0 + (t < L ? t : L - 1)) * ldv + (int64_t)h * D + v0 + 16 * vt + ccol];
+      }
+    const int tg = tid & (CHUNK - 1);
+    P.g = gcum[(t0 + (tg < L ? tg : L - 1)) * Hv + h];
+  };
+
+  // One chunk from prefetched registers `cur`; issues the prefetch of chunk
+  // c + 1 into `nxt` before computing.
+  auto step = [&](int64_t c, Pref& cur, Pref& nxt) {
+    const int L = cur.L;
+    const int64_t t0 = cur.t0;
+    __syncthreads();  // previous chunk's LDS reads are done
+    cur.k.store(&sm.K[0][0], LD, tid);
+    sm.gam[tid & (CHUNK - 1)] = cur.g;  // the four waves write identical values
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
@@ -198,44 +246,50 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
         for (int e = 0; e < 4; ++e) hp[(int64_t)e * D] = from_f<T>(S[i][e]);
       }
     }
+    prefetch(nxt, c + 1 < c_end ? c + 1 : c);  // unconditional (re-reads the last chunk at the end)
+    issue_fence();
     __syncthreads();
 
     // Phase A: R = V - diag(Gam) K S^T   (and the Q S^T part of O)
-    floatx4 oq[NA];
+    floatx4 oq[NVT];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-      floatx4 ks = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.Sb[0][0], LD, 16 * tt,
-                                           16 * vt, D, lane);
-      if (MODE == 0)
-        oq[i] = tile_mma<CT, true, true>(zero4(), &sm.Q[0][0], LD, &sm.Sb[0][0], LD, 16 * tt,
-                                        16 * vt, D, lane);
-      const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
+    for (int vt = 0; vt < NVT; ++vt) {
+      floatx4 ks = zero4();
+      oq[vt] = zero4();
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) {
+        const typename MM::frag b = MM::kc(&sm.Sb[16 * vt + r16][0], s * KS, lane);
+        ks = MM::mma(MM::kc(&sm.K[trow + r16][0], s * KS, lane), b, ks);
+        if (MODE == 0) oq[vt] = MM::mma(FQ::cvt(cur.q[s]), b, oq[vt]);
+      }
+      const int vv = 16 * vt + ccol, tb = trow + rsub;
       float r[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float Gm = dexp<T>(sm.gam[tb + e]);
-        r[e] = to_f(sm.V[tb + e][vv]) - Gm * ks[e];
-        if (MODE == 0) oq[i][e] *= Gm * scale;
+        const float vin = tb + e < L ? to_f(cur.v[vt][e]) : 0.f;
+        r[e] = vin - Gm * ks[e];
+        if (MODE == 0) oq[vt][e] *= Gm * scale;
       }
       store4(&sm.Rt[vv][tb], r[0], r[1], r[2], r[3]);
       if (MODE == 1) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (tb + e < L) Rw[(t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv] = from_f<T>(r[e]);
+          *row_or_sink(Rw + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
+              from_f<T>(r[e]);
       }
     }
     __syncthreads();
 
     // Phase B: Delta = M R
-    const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
     const double gl = sm.gam[CHUNK - 1];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-      floatx4 dl = tile_mma<CT, true, true>(zero4(), Mc, CHUNK, &sm.Rt[0][0], LDC, 16 * tt, 16 * vt,
-                                           CHUNK, lane);
-      const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
+    for (int vt = 0; vt < NVT; ++vt) {
+      floatx4 dl = zero4();
+#pragma unroll
+      for (int s = 0; s < NKC; ++s)
+        dl = MM::mma(FM::cvt(cur.m[s]), MM::kc(&sm.Rt[16 * vt + r16][0], s * KS, lane), dl);
+      const int vv = 16 * vt + ccol, tb = trow + rsub;
       float ds[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) ds[e] = dexp<T>(gl - sm.gam[tb + e]) * dl[e];
@@ -244,23 +298,25 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
       if (MODE == 1) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (tb + e < L) Dlw[(t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv] = from_f<T>(dl[e]);
+          *row_or_sink(Dlw + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
+              from_f<T>(dl[e]);
       }
     }
     __syncthreads();
 
     // Phase C: O = oq + P Delta;  S^T <- Gam_L S^T + K^T (diag(dec) Delta)
     if (MODE == 0) {
-      const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
 #pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const int id = wave * NA + i, tt = id / NVT, vt = id % NVT;
-        floatx4 ov = tile_mma<CT, true, true>(oq[i], Pc, CHUNK, &sm.Dt[0][0], LDC, 16 * tt, 16 * vt,
-                                             CHUNK, lane);
-        const int vv = 16 * vt + ccol, tb = 16 * tt + rsub;
+      for (int vt = 0; vt < NVT; ++vt) {
+        floatx4 ov = oq[vt];
+#pragma unroll
+        for (int s = 0; s < NKC; ++s)
+          ov = MM::mma(FM::cvt(cur.p[s]), MM::kc(&sm.Dt[16 * vt + r16][0], s * KS, lane), ov);
+        const int vv = 16 * vt + ccol, tb = trow + rsub;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (tb + e < L) o[(t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv] = from_f<T>(ov[e]);
+          *row_or_sink(o + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
+              from_f<T>(ov[e]);
       }
     }
     const float GL = dexp<T>(gl);
@@ -270,8 +326,25 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[i][e] *= GL;
       S[i] = tile_mma<CT, false, true>(S[i], &sm.K[0][0], LD, &sm.Dst[0][0], LDC, 16 * kt, 16 * vt,
-                                      CHUNK, lane);
+                                       CHUNK, lane);
     }
+  };
+
+  Pref A, B;
+  if (c_begin < c_end) prefetch(A, c_begin);
+  for (int64_t c = c_begin; c < c_end; c += 2) {
+    step(c, A, B);
+    if (c + 1 < c_end) step(c + 1, B, A);
+  }
+  // Never taken (chunk offsets are non-negative): gives both prefetch buffers
+  // a use on the loop-exit path, so their loads are not sunk into the branch
+  // that runs the second step of a pair (which would serialise them).
+  if (c_end < 0) {
+    T* sk = reinterpret_cast<T*>(sink);
+    *reinterpret_cast<Raw8<T>*>(sk) = A.k.r[0];
+    *reinterpret_cast<Raw8<T>*>(sk + 64) = B.k.r[0];
+    sk[128] = A.v[0][0];
+    sk[129] = B.v[0][0];
   }
   if (MODE == 0 && S_final) {
 #pragma unroll
@@ -315,12 +388,14 @@ static hipError_t chunk_state(const gdn_shape& s, const void* q, const void* k, 
   const size_t shm = sizeof(StateSmem<T, D, BV>);
   auto kern = chunk_state_kernel<T, D, BV, MODE>;
   hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  hipLaunchKernelGGL(kern, dim3(D / BV, s.hv, s.n_seq), dim3(256), shm, st, (const T*)q,
-                     (const T*)k, (const T*)v, ldq, ldk, ldv, cu, (const int32_t*)(ws + Ly.seq_off),
-                     s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum),
+  const int n_items = (D / BV) * s.hv * s.n_seq;
+  hipLaunchKernelGGL(kern, dim3(n_items), dim3(256), shm, st, (const T*)q, (const T*)k,
+                     (const T*)v, ldq, ldk, ldv, cu, (const int32_t*)(ws + Ly.seq_off), s.hv,
+                     s.hv / s.hk, scale, (const double*)(ws + Ly.gcum),
                      (const typename Compute<T>::type*)(ws + Ly.mw),
                      (const typename Compute<T>::type*)(ws + Ly.pw), S0, S_final, (T*)o,
-                     (T*)(ws + Ly.h), (T*)(ws + Ly.rw), (T*)(ws + Ly.dlw));
+                     (T*)(ws + Ly.h), (T*)(ws + Ly.rw), (T*)(ws + Ly.dlw), (void*)(ws + Ly.sink),
+                     n_items);
   return hipGetLastError();
 }
 
