@@ -79,7 +79,23 @@ def parse():
     p.add_argument("--seed", type=int, default=1005)
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain bf16 device copy of MIB MiB three times (reference "
+                        "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for counter calibration."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 2, "bytes_written": n * 2,
+                                           "kib": n * 2 / 1024, "launches": 3}}), flush=True)
 
 
 def make_gpu_inputs(w, seed, dev):
@@ -153,6 +169,9 @@ def main():
               "(the layer core is head-parallel; a multi-GPU run would shard heads, see the "
               "design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from gated_deltanet_layer_causal_amd import inputs as gi
     from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore

@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
     const double* __restrict__ gcum, const typename Compute<T>::type* __restrict__ Mw,
     const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ dout,
     const float* __restrict__ dS_final, float* __restrict__ dS0, T* __restrict__ dhst,
-    T* __restrict__ ddw, T* __restrict__ dvo, int64_t lddv, int n_items) {
+    T* __restrict__ ddw, T* __restrict__ dvo, int64_t lddv, void* __restrict__ sink, int n_items) {
   typedef typename Compute<T>::type CT;
   typedef Mma<T> MM;
   typedef FragKS<T, CT> FG;   // gathered rows of P^T, M^T
@@ -78,49 +78,45 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
     }
   }
 
-  RowPrefetch<T, D> pk, pq;
-  RowPrefetch<T, BV> pdo;
-  typename FG::raw pP[NKC], pM[NKC];
-  double pg = 0.0;
-  auto prefetch = [&](int64_t c, int64_t t0, int L) {
-    pk.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-    pq.load(q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
-    pdo.load(dout + t0 * HvD + (int64_t)h * D + v0, HvD, L, tid);
+  struct Pref {
+    RowPrefetch<T, D, true> k, q;     // rows fastest across lanes: stored transposed
+    RowPrefetch<T, BV, true> dO;
+    typename FG::raw P[NKC], M[NKC];
+    double g;
+    int L;
+    int64_t t0;
+  };
+  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
+  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
+  auto prefetch = [&](Pref& F, int64_t c) {
+    F.t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - F.t0;
+    const int L = rem < CHUNK ? (int)rem : CHUNK;
+    const int64_t t0 = F.t0;
+    F.L = L;
+    F.k.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
+    F.q.load(q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+    F.dO.load(dout + t0 * HvD + (int64_t)h * D + v0, HvD, L, tid);
     const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + trow + r16;
     const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + trow + r16;
 #pragma unroll
     for (int s = 0; s < NKC; ++s) {
-      pP[s] = FG::load(Pc, CHUNK, s * KS, lane);   // P^T row t = column t of P
-      pM[s] = FG::load(Mc, CHUNK, s * KS, lane);
+      F.P[s] = FG::load(Pc, CHUNK, s * KS, lane);   // P^T row t = column t of P
+      F.M[s] = FG::load(Mc, CHUNK, s * KS, lane);
     }
     const int tg = tid & (CHUNK - 1);
-    pg = gcum[(t0 + (tg < L ? tg : L - 1)) * Hv + h];
+    F.g = gcum[(t0 + (tg < L ? tg : L - 1)) * Hv + h];
   };
-  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
-  auto span = [&](int64_t c, int64_t& t0, int& L) {
-    t0 = (int64_t)cu[n] + CHUNK * (c - c_begin);
-    const int64_t rem = (int64_t)cu[n + 1] - t0;
-    L = rem < CHUNK ? (int)rem : CHUNK;
-  };
-  if (c_begin < c_end) {
-    int64_t t0;
-    int L;
-    span(c_end - 1, t0, L);
-    prefetch(c_end - 1, t0, L);
-  }
-  for (int64_t c = c_end - 1; c >= c_begin; --c) {
-    int64_t t0;
-    int L;
-    span(c, t0, L);
+
+  auto step = [&](int64_t c, Pref& cur, Pref& nxt) {
+    const int64_t t0 = cur.t0;
+    const int L = cur.L;
     __syncthreads();
-    pk.store(&sm.K[0][0], LD, tid);
-    store_rows_transposed(pk, &sm.Kt[0][0], LDC, tid);
-    store_rows_transposed(pq, &sm.Qt[0][0], LDC, tid);
-    store_rows_transposed(pdo, &sm.dOt[0][0], LDC, tid);
-    if (tid < CHUNK) sm.gam[tid] = pg;
-    typename FG::raw cP[NKC], cM[NKC];
-#pragma unroll
-    for (int s = 0; s < NKC; ++s) { cP[s] = pP[s]; cM[s] = pM[s]; }
+    cur.k.store(&sm.K[0][0], LD, tid);
+    store_rows_transposed(cur.k, &sm.Kt[0][0], LDC, tid);
+    store_rows_transposed(cur.q, &sm.Qt[0][0], LDC, tid);
+    store_rows_transposed(cur.dO, &sm.dOt[0][0], LDC, tid);
+    sm.gam[tid & (CHUNK - 1)] = cur.g;  // the four waves write identical values
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
@@ -130,12 +126,8 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) hp[(int64_t)e * D] = from_f<T>(dS[i][e]);
     }
-    if (c - 1 >= c_begin) {
-      int64_t t1;
-      int L1;
-      span(c - 1, t1, L1);
-      prefetch(c - 1, t1, L1);
-    }
+    prefetch(nxt, c - 1 >= c_begin ? c - 1 : c);  // unconditional (re-reads at the start)
+    issue_fence();
     __syncthreads();
 
     // scaled copy of dO^T for the state gradient
@@ -150,7 +142,7 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
       floatx4 pt = zero4(), kd = zero4();
 #pragma unroll
       for (int s = 0; s < NKC; ++s)
-        pt = MM::mma(FG::cvt(cP[s]), MM::kc(&sm.dOt[16 * vt + r16][0], s * KS, lane), pt);
+        pt = MM::mma(FG::cvt(cur.P[s]), MM::kc(&sm.dOt[16 * vt + r16][0], s * KS, lane), pt);
 #pragma unroll
       for (int s = 0; s < NKD; ++s)
         kd = MM::mma(MM::kc(&sm.K[trow + r16][0], s * KS, lane),
@@ -162,7 +154,8 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
       store4(&sm.dDt[vv][tb], dd[0], dd[1], dd[2], dd[3]);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (tb + e < L) ddw[(t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv] = from_f<T>(dd[e]);
+        *row_or_sink(ddw + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
+            from_f<T>(dd[e]);
     }
     __syncthreads();
 
@@ -172,13 +165,14 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
       floatx4 dr = zero4();
 #pragma unroll
       for (int s = 0; s < NKC; ++s)
-        dr = MM::mma(FG::cvt(cM[s]), MM::kc(&sm.dDt[16 * vt + r16][0], s * KS, lane), dr);
+        dr = MM::mma(FG::cvt(cur.M[s]), MM::kc(&sm.dDt[16 * vt + r16][0], s * KS, lane), dr);
       const int vv = 16 * vt + ccol, tb = trow + rsub;
       float rg[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         rg[e] = dexp<T>(sm.gam[tb + e]) * dr[e];
-        if (tb + e < L) dvo[(t0 + tb + e) * lddv + (int64_t)h * D + v0 + vv] = from_f<T>(dr[e]);
+        *row_or_sink(dvo + (t0 + tb + e) * lddv + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
+            from_f<T>(dr[e]);
       }
       store4(&sm.dRg[vv][tb], rg[0], rg[1], rg[2], rg[3]);
     }
@@ -200,6 +194,19 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) dS[i][e] = GL * dS[i][e] + qd[e] - kr[e];
     }
+  };
+
+  Pref A, B;
+  if (c_begin < c_end) prefetch(A, c_end - 1);
+  for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
+    step(c, A, B);
+    if (c - 1 >= c_begin) step(c - 1, B, A);
+  }
+  // Never taken: keeps both prefetch buffers live on the loop-exit path.
+  if (c_end < 0) {
+    T* sk = reinterpret_cast<T*>(sink);
+    *reinterpret_cast<Raw8<T>*>(sk) = A.k.r[0];
+    *reinterpret_cast<Raw8<T>*>(sk + 64) = B.k.r[0];
   }
   if (dS0) {
 #pragma unroll
@@ -281,7 +288,7 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
 
   // Stage K rows (for K K^T) and the transposes of K and Q.
   {
-    RowPrefetch<T, D> pk, pq;
+    RowPrefetch<T, D, true> pk, pq;
     pk.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
     pq.load(q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
     pk.store(&sm.u.Krm[0][0], LD, tid);
@@ -612,7 +619,8 @@ hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const voi
                        (const double*)(ws + Ly.gcum),
                        (const typename Compute<T>::type*)(ws + Ly.mw),
                        (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)dout, dS_final,
-                       dS0, (T*)(ws + Ly.dh), (T*)(ws + Ly.ddw), (T*)dv, lddv, n_items);
+                       dS0, (T*)(ws + Ly.dh), (T*)(ws + Ly.ddw), (T*)dv, lddv,
+                       (void*)(ws + Ly.sink), n_items);
     return hipGetLastError();
   });
 }

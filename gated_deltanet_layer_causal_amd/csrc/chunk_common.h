@@ -152,18 +152,26 @@ template <typename T> __device__ __forceinline__ f8 raw_f8(const Raw8<T>& r) {
 // spread over the 256 threads.  Loads are unconditional (rows >= L re-read
 // row L-1, which is valid memory) so that no wait is forced at load time;
 // rows >= L are zeroed when the registers are stored.
-template <typename T, int W> struct RowPrefetch {
+// ROWFAST = false: consecutive lanes take consecutive 8-element column blocks
+// of a row (coalesced loads; for row-major LDS staging).  ROWFAST = true:
+// consecutive lanes take consecutive rows of one column block, so that a
+// transposed LDS store writes consecutive addresses (no bank conflicts).
+template <typename T, int W, bool ROWFAST = false> struct RowPrefetch {
   static constexpr int ITEMS = CHUNK * W / 8;
   static constexpr int NI = ITEMS / 256;
   static_assert(ITEMS % 256 == 0, "row prefetch covers whole rows per thread");
   Raw8<T> r[NI];
   int L;
+  __device__ __forceinline__ static int row_of(int i) { return ROWFAST ? i % CHUNK : i / (W / 8); }
+  __device__ __forceinline__ static int col_of(int i) {
+    return ROWFAST ? (i / CHUNK) * 8 : (i % (W / 8)) * 8;
+  }
   __device__ __forceinline__ void load(const T* src, int64_t ld, int L_, int tid) {
     L = L_;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int i = tid + 256 * j;
-      const int row = i / (W / 8), c8 = (i % (W / 8)) * 8;
+      const int row = row_of(i), c8 = col_of(i);
       r[j] = ld_raw8(src + (int64_t)(row < L ? row : L - 1) * ld + c8);
     }
   }
@@ -180,8 +188,8 @@ template <typename T, int W> struct RowPrefetch {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int i = tid + 256 * j;
-      const int row = i / (W / 8);
-      store8(dst + row * ld_s + (i % (W / 8)) * 8, value(j, row));
+      const int row = row_of(i);
+      store8(dst + row * ld_s + col_of(i), value(j, row));
     }
   }
 };
@@ -241,13 +249,13 @@ template <typename S> struct FragKS<float, S> {
 };
 
 // Transposed staging of prefetched rows: dst[col][row] (row stride ld_s).
-template <typename T, int W, typename TD>
-__device__ __forceinline__ void store_rows_transposed(const RowPrefetch<T, W>& p, TD* dst, int ld_s,
-                                                      int tid) {
+template <typename T, int W, bool RF, typename TD>
+__device__ __forceinline__ void store_rows_transposed(const RowPrefetch<T, W, RF>& p, TD* dst,
+                                                      int ld_s, int tid) {
 #pragma unroll
-  for (int j = 0; j < RowPrefetch<T, W>::NI; ++j) {
+  for (int j = 0; j < RowPrefetch<T, W, RF>::NI; ++j) {
     const int i = tid + 256 * j;
-    const int row = i / (W / 8), c8 = (i % (W / 8)) * 8;
+    const int row = RowPrefetch<T, W, RF>::row_of(i), c8 = RowPrefetch<T, W, RF>::col_of(i);
     const f8 v = p.value(j, row);
 #pragma unroll
     for (int u = 0; u < 8; ++u) dst[(c8 + u) * ld_s + row] = from_f<TD>(v.v[u]);
