@@ -245,9 +245,11 @@ struct GradSmem {
   float X[16][17];
   double gam[CHUNK];
   float bet[CHUNK];
-  float rowA[CHUNK], rowB[CHUNK];
-  float colA[4][CHUNK], colB[4][CHUNK], rowX[4][CHUNK];
-  float red[2][4];                 // per-wave partial sums: z, <dS', S>
+  float rowB[CHUNK];
+  float colB[4][CHUNK], rowX[4][CHUNK], rowZ[4][CHUNK];
+  float segE[4][CHUNK];            // per-(row block, column) totals of E
+  float boxE[4][CHUNK];            // per-(column block, token) parts of the box sums
+  float red[4];                    // per-wave partial sums of <dS', S>
 };
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -328,7 +330,7 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
       sm.gam[lane] = gcum[(t0 + (lane < L ? lane : L - 1)) * Hv + h];
       sm.bet[lane] = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
     }
-    if (tid < CHUNK) { sm.rowA[tid] = 0.f; sm.rowB[tid] = 0.f; }
+    if (tid < CHUNK) sm.rowB[tid] = 0.f;
     CT pval[4][4];
     {
       const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
@@ -395,9 +397,11 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
+    // E[t][s] = dA[t][s] A[t][s] + dP[t][s] P[t][s] (s < t) collects in
+    // Esm (the dead Sc1 storage, stride 65) for the box sums of P6.
+    float(*Esm)[CHUNK + 1] = reinterpret_cast<float(*)[CHUNK + 1]>(&sm.Sc1[0][0]);
     {
-      float ca[4] = {0.f, 0.f, 0.f, 0.f};
-      float ra[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
+      float rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         floatx4 da = tile_mma<T, false, false>(zero4(), &sm.Tm[0][0], 68, &sm.u.Y[0][0], 68,
@@ -406,32 +410,23 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = rbase + e;
-          float wa = 0.f;
+          float wa = 0.f, EA = 0.f;
           if (s < t) {
             const float dAv = -da[e];
             const float Dts = dexp<T>(sm.gam[t] - sm.gam[s]);
-            const float Ats = sm.bet[t] * Dts * kk[j][e];
-            const float EA = dAv * Ats;
-            ra[e] += EA;
-            ca[j] -= EA;
+            EA = dAv * (sm.bet[t] * Dts * kk[j][e]);
             rb[e] += dAv * Dts * kk[j][e];
             wa = dAv * sm.bet[t] * Dts;
           }
           sm.WA[t][s] = from_f<T>(wa);
+          Esm[t][s] = EA;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = sum16(ra[e]), y = sum16(rb[e]);
-        if (ccol == 0) { sm.rowA[rbase + e] += x; sm.rowB[rbase + e] += y; }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = ca[j];
-        x += __shfl_xor(x, 16, 64);
-        x += __shfl_xor(x, 32, 64);
-        if (lane < 16) sm.colA[wave][16 * j + lane] = x;
+        const float y = sum16(rb[e]);
+        if (ccol == 0) sm.rowB[rbase + e] += y;
       }
     }
     __syncthreads();
@@ -443,7 +438,6 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
     issue_fence();
     __syncthreads();
     {
-      float ca[4] = {0.f, 0.f, 0.f, 0.f}, ra[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         floatx4 dp = tile_mma<T, true, true>(zero4(), &sm.u.t.B1[0][0], LD, &sm.u.t.B2[0][0], LD,
@@ -453,28 +447,11 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
         for (int e = 0; e < 4; ++e) {
           const int t = rbase + e;
           float v = 0.f;
-          if (s <= t) {
-            const float Dts = dexp<T>(sm.gam[t] - sm.gam[s]);
-            const float E = dp[e] * to_f(pval[j][e]);
-            ra[e] += E;
-            ca[j] -= E;
-            v = dp[e] * Dts;
-          }
+          if (s <= t) v = dp[e] * dexp<T>(sm.gam[t] - sm.gam[s]);
+          if (s < t) Esm[t][s] += dp[e] * to_f(pval[j][e]);  // same lane wrote it in P3
           sm.dPD[t][s] = from_f<T>(v);
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = sum16(ra[e]);
-        if (ccol == 0) sm.rowA[rbase + e] += x;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = ca[j];
-        x += __shfl_xor(x, 16, 64);
-        x += __shfl_xor(x, 32, 64);
-        if (lane < 16) sm.colA[wave][16 * j + lane] += x;
       }
     }
     __syncthreads();
@@ -485,12 +462,12 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
       const T* Sg = hst + ((int64_t)c * Hv + h) * D * D;   // [k][v]
       const T* dSg = dhst + ((int64_t)c * Hv + h) * D * D;
       const double gl = sm.gam[CHUNK - 1];
-      float rx[4][4];
+      float rx[4][4], rz[4][4];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rx[a][e] = 0.f;
-      float zs = 0.f, ipv = 0.f;
+        for (int e = 0; e < 4; ++e) rx[a][e] = rz[a][e] = 0.f;
+      float ipv = 0.f;
       typename MM::frag sf[NKD], dsf[NKD];
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
@@ -537,9 +514,8 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
           const float qv = to_f(sm.Qt[kc][t]), kv = to_f(sm.Kt[kc][t]);
           dQa[i][e] += Gm * x1[e];
           dKa[i][e] += scale * pq[e] - Gm * x2[e] + dec * x3[e];
-          const float z = dec * x3[e] * kv;
-          rx[tt][e] += Gm * scale * x1[e] * qv - Gm * x2[e] * kv - z;
-          zs += z;
+          rx[tt][e] += Gm * scale * x1[e] * qv - Gm * x2[e] * kv;
+          rz[tt][e] += dec * x3[e] * kv;
         }
         __builtin_amdgcn_sched_barrier(0);  // bound live ranges: one tile at a time
       }
@@ -547,29 +523,72 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x = sum16(rx[a][e]);
-          if (ccol == 0) sm.rowX[wave][16 * a + rsub + e] = x;
+          const float x = sum16(rx[a][e]), z = sum16(rz[a][e]);
+          if (ccol == 0) {
+            sm.rowX[wave][16 * a + rsub + e] = x;
+            sm.rowZ[wave][16 * a + rsub + e] = z;
+          }
         }
-      zs = wave_sum(zs);
       ipv = wave_sum(ipv);
-      if (lane == 0) { sm.red[0][wave] = zs; sm.red[1][wave] = ipv; }
+      if (lane == 0) sm.red[wave] = ipv;
     }
     __syncthreads();
-    // ---- P6: assemble dgam -> dg (reverse cumsum), dbeta
+    // ---- P6: assemble dg, dbeta.  With gamma the in-chunk cumulative gate,
+    //      dg_i = sum_{t >= i} dgam_t.  Three parts, each a sum of terms that
+    //      all carry the decay across token i, so no large terms cancel when
+    //      that decay is strong:
+    //      - pair terms E[t][s] (s < t) add to dgam_t and subtract from
+    //        dgam_s; their part of dg_i is the box sum over t >= i > s,
+    //        taken as column suffix sums over rows, then row prefix sums;
+    //      - the chunk-start terms y_t (rowX, and the state term at the last
+    //        token) enter as the suffix sum over t >= i;
+    //      - the decay-to-chunk-end terms z_t enter dgam as -z_t and as
+    //        +sum z at the last token: their part is the prefix sum over t < i.
+    {
+      // column suffix sums within each 16-row block (wave = row block)
+      const int cidx = lane, rb0 = 16 * wave;
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 15; r >= 0; --r) {
+        acc += Esm[rb0 + r][cidx];
+        Esm[rb0 + r][cidx] = acc;
+      }
+      sm.segE[wave][cidx] = acc;
+    }
+    __syncthreads();
+    {
+      // add the later row blocks, then the row-prefix part of each box sum
+      const int cidx = lane, rb0 = 16 * wave;
+      float off = 0.f;
+      for (int w = 3; w > wave; --w) off += sm.segE[w][cidx];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Esm[rb0 + r][cidx] += off;
+    }
+    __syncthreads();
+    {
+      // token i = lane sums columns s < i of the column block owned by this wave
+      const int i = lane, cb0 = 16 * wave;
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (cb0 + s < i) part += Esm[i][cb0 + s];
+      sm.boxE[wave][i] = part;
+    }
+    __syncthreads();
     if (wave == 0) {
       const int t = lane;
-      float dgm = sm.rowA[t];
-      float db = sm.rowB[t];
+      float y = 0.f, db = sm.rowB[t], zt = 0.f;
+      const float box = ((sm.boxE[0][t] + sm.boxE[1][t]) + sm.boxE[2][t]) + sm.boxE[3][t];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        dgm += sm.colA[w][t] + sm.rowX[w][t];
+        y += sm.rowX[w][t];
         db += sm.colB[w][t];
+        zt += sm.rowZ[w][t];
       }
-      const float zsum = sm.red[0][0] + sm.red[0][1] + sm.red[0][2] + sm.red[0][3];
-      const float ips = sm.red[1][0] + sm.red[1][1] + sm.red[1][2] + sm.red[1][3];
-      if (t == L - 1) dgm += zsum + dexp<T>(sm.gam[CHUNK - 1]) * ips;
-      if (t >= L) dgm = 0.f;
-      const float dgs = wave_suffix_scan(dgm, lane);
+      const float ips = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+      if (t == L - 1) y += dexp<T>(sm.gam[CHUNK - 1]) * ips;
+      if (t >= L) { y = 0.f; zt = 0.f; }
+      const float dgs = box + wave_suffix_scan(y, lane) + (wave_incl_scan_f(zt, lane) - zt);
       if (t < L) {
         dg[(t0 + t) * Hv + h] = dgs;
         dbeta[(t0 + t) * Hv + h] = db;

@@ -334,6 +334,15 @@ __device__ __forceinline__ double wave_incl_scan(double x, int lane) {
   return x;
 }
 
+__device__ __forceinline__ float wave_incl_scan_f(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 // Inclusive suffix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_suffix_scan(float x, int lane) {
 #pragma unroll

@@ -111,17 +111,24 @@ def chunked_bwd(q, k, v, g, beta, cu, scale, dout, S0=None, dS_final=None, C=64)
                 WA = dA * bb[:, None] * D
                 dK = ((dP * D).T @ Q - Gam[:, None] * (dR @ S) + dec[:, None] * (Dl @ dSp)
                       + WA @ K + WA.T @ K)
-                dgam = np.zeros(L)
-                dgam += ((dO * (Gam[:, None] * (Q @ S.T))).sum(axis=1)
-                         - (dR * (Gam[:, None] * (K @ S.T))).sum(axis=1))
-                E = dP * P
-                dgam += E.sum(axis=1) - E.sum(axis=0)
-                EA = dA * A
-                dgam += EA.sum(axis=1) - EA.sum(axis=0)
+                # dg_i = sum_{t >= i} dgam_t, assembled from three parts whose
+                # terms all carry the decay across token i:
+                # chunk-start terms y_t (and the state term on the last token)
+                # as a suffix sum
+                y = ((dO * (Gam[:, None] * (Q @ S.T))).sum(axis=1)
+                     - (dR * (Gam[:, None] * (K @ S.T))).sum(axis=1))
+                y[-1] += Gam[-1] * (dSp * S).sum()
+                # pair terms E[t, s] (s < t) add to dgam_t and subtract from
+                # dgam_s: their part of dg_i is the box sum over t >= i > s
+                # (the diagonal of dP o P would cancel exactly: left out)
+                E = np.tril(dP * P, -1) + dA * A
+                colsuf = np.cumsum(E[::-1], axis=0)[::-1]       # sum over rows >= t
+                box = np.array([colsuf[i, :i].sum() for i in range(L)])
+                # dec_t = exp(gam_L - gam_t): its gradient puts -z_t on token t
+                # and +sum(z) on the last token; in dg that is the exclusive
+                # prefix sum of z
                 z = dec * ((Dl @ dSp) * K).sum(axis=1)
-                dgam -= z
-                dgam[-1] += z.sum() + Gam[-1] * (dSp * S).sum()
-                dg[c0:c1, h] = np.cumsum(dgam[::-1])[::-1]
+                dg[c0:c1, h] = box + np.cumsum(y[::-1])[::-1] + (np.cumsum(z) - z)
                 dbeta[c0:c1, h] = dbe
                 dvv[c0:c1, h] = dR
                 dq[c0:c1, kh] += scale * dQ

@@ -1,0 +1,59 @@
+"""Whole layer core (conv -> gate -> chunked gated delta rule -> gated norm,
+forward and backward) on the GPU against the oracle's composed layer.
+
+The oracle composition rounds to the storage dtype exactly at the tensors the
+layer hands between its C-ABI calls (conv output, delta-rule output and the
+gradients passed back), the interface values of the layer."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_layer_causal_amd import capi as L
+from gated_deltanet_layer_causal_amd import inputs as gi
+from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore
+from tests.gpu_util import DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_close, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: workload, seqlens, A range, activation
+    "tiny_fp32": (gi.WORKLOADS["tiny"], [64], None, L.GDN_ACT_SILU),
+    "tiny_fp32_varlen_state": (gi.Workload("tv", 0, 1, 2, 32, "fp32", seq="varlen",
+                                           init_state=True, final_state=True, seed=77),
+                               [40, 1, 90], (0.02, 0.3), L.GDN_ACT_SIGMOID),
+    "bf16_small": (gi.Workload("bs", 0, 2, 6, 128, "bf16", seq="varlen", init_state=True,
+                               final_state=True, seed=78), [300, 65, 7], None, L.GDN_ACT_SILU),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_matches_oracle(name):
+    w, lens, A_range, act = CASES[name]
+    inp = gi.make_inputs(w, seqlens=lens, A_range=A_range)
+    bf = w.dtype == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+    rf = gi.round_bf16 if bf else None
+    core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=tdt, act=act), device=DEV)
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(DEV)
+    args = (dev(inp["x"], tdt), dev(inp["w_conv"]), dev(inp["a"], tdt), dev(inp["b"], tdt),
+            dev(inp["A_log"]), dev(inp["dt_bias"]), dev(inp["z"], tdt), dev(inp["w_norm"]), cu)
+    S0 = dev(inp["S0"]) if inp["S0"] is not None else None
+    dST = dev(inp["dS_T"]) if inp["dS_T"] is not None else None
+    f = core.forward(*args, S0=S0, want_final=True)
+    gb = core.backward(f, *args, dev(inp["dy"], tdt), S0=S0, dS_final=dST)
+    torch.cuda.synchronize()
+    sc = w.d ** -0.5
+    rf_ = f_ = oracle.layer_fwd(inp, w.hk, w.hv, w.d, sc, act=act, round_fn=rf)
+    rb = oracle.layer_bwd(inp, rf_, w.hk, w.hv, w.d, sc, act=act, round_fn=rf)
+    ft = TOL_FP32 if not bf else FWD_TOL_BF16
+    gt = TOL_FP32 if not bf else GRAD_TOL_BF16
+    checks = [(k, f[k], f_[k], ft) for k in ("y", "g", "beta", "o", "out", "S_final")]
+    checks += [(k, gb[k], rb[k], gt) for k in ("do", "dg", "dbeta", "dy_conv", "dx", "dw_conv", "da",
+                                               "db", "dA_log", "ddt_bias", "dz", "dw_norm", "dS0")]
+    # every error is printed before the first assertion, so a failure shows
+    # where along the layer the difference enters
+    errs = {k: rel_err(host(t).reshape(np.shape(r)), r) for k, t, r, _ in checks}
+    print(name, " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    for k, t, r, tol in checks:
+        assert_close(k, host(t).reshape(np.shape(r)), r, tol)
