@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(256) chunk_rev_kernel(
     F.k.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
     F.q.load(q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
     F.dO.load(dout + t0 * HvD + (int64_t)h * D + v0, HvD, L, tid);
-    const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + trow + r16;
+    const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + acc_col<CT>(trow + r16);
     const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + trow + r16;
 #pragma unroll
     for (int s = 0; s < NKC; ++s) {
@@ -337,7 +337,7 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pval[j][e] = Pc[(rbase + e) * CHUNK + 16 * j + ccol];
+        for (int e = 0; e < 4; ++e) pval[j][e] = Pc[(rbase + e) * CHUNK + acc_col<CT>(16 * j + ccol)];
     }
     __syncthreads();
     // ---- P1: A, then Tinv

@@ -1,5 +1,5 @@
-// Chunked gated delta rule: chunk table, WY/UT preparation and the
-// sequential state pass (forward outputs, or the states the backward needs).
+// Chunked gated delta rule: chunk table and WY/UT preparation (the
+// sequential state pass is in chunk_state.hip).
 #include "chunk_common.h"
 
 namespace gdn {
@@ -37,18 +37,26 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t* __restr
 
 // ---------------------------------------------------------------------------
 // Preparation, one workgroup per (chunk, key head): K K^T and Q K^T once
-// (MFMA), then per value head of the group: gam, A, Tinv (fp32), and the
-// MFMA operands M = Tinv diag(beta) and P written to the workspace.
+// (MFMA) and K^T to the workspace, then per value head of the group: gam, A,
+// Tinv (fp32), and the MFMA operands M = Tinv diag(beta), P and
+// W = M diag(Gam) K, with the per-token factors Gam_t and dec_t.
 template <typename T, int D>
 struct PrepSmem {
   typedef typename Compute<T>::type CT;
+  static constexpr int KT_LD = CHUNK + Pad<CT>::v;
   CT K[CHUNK][D + Pad<CT>::v];
-  CT Q[CHUNK][D + Pad<CT>::v];
+  union {
+    CT Q[CHUNK][D + Pad<CT>::v];   // until Q K^T is formed
+    CT Kt[D][KT_LD];               // then K^T
+  } u;
   float A[CHUNK][68];
   float Ti[CHUNK][68];
   float X[16][17];
   double gam[CHUNK];
   float bet[CHUNK];
+  float sbg[CHUNK];                // beta_s Gam_s
+  static_assert(sizeof(CT) * CHUNK * (D + Pad<CT>::v) <= sizeof(float) * CHUNK * 68,
+                "W tile fits in the A storage");
 };
 
 template <typename T, int D>
@@ -57,11 +65,16 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G, float scale,
     double* __restrict__ gcum, typename Compute<T>::type* __restrict__ Mw,
-    typename Compute<T>::type* __restrict__ Pw) {
+    typename Compute<T>::type* __restrict__ Pw, typename Compute<T>::type* __restrict__ Ww,
+    typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
+    typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw) {
   typedef typename Compute<T>::type CT;
+  typedef Mma<CT> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   PrepSmem<T, D>& sm = *reinterpret_cast<PrepSmem<T, D>*>(smem_raw);
   constexpr int LD = D + Pad<CT>::v;
+  constexpr int KT_LD = PrepSmem<T, D>::KT_LD;
+  constexpr int KS = MM::KS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x;
   const int kh = blockIdx.y;
@@ -71,7 +84,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   chunk_span(seq_off, cu, n_seq, c, t0, L);
 
   stage_rows<CT, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-  stage_rows<CT, D>(&sm.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+  stage_rows<CT, D>(&sm.u.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
   __syncthreads();
 
   // wave w owns rows [16w, 16w+16) of the 64 x 64 products
@@ -79,10 +92,42 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     kk[j] = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
-    qk[j] = tile_mma<CT, true, true>(zero4(), &sm.Q[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
+    qk[j] = tile_mma<CT, true, true>(zero4(), &sm.u.Q[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
   }
   const int rbase = 16 * wave + 4 * (lane >> 4);
   const int ccol = lane & 15;
+  const int r16 = lane & 15;
+  {
+    // Q and K rows (compute type, zero past the chunk end, columns in
+    // accumulator order) to the workspace, in 4-element pieces
+    constexpr int PR = D / 4;
+    const int64_t base = ((int64_t)c * (Hv / G) + kh) * CHUNK * D;
+    for (int i = tid; i < CHUNK * PR; i += 256) {
+      const int r = i / PR, c4 = (i % PR) * 4;
+      typedef CT v4 __attribute__((ext_vector_type(4)));
+      const int dst = r * D + acc_col<CT>(c4);
+      *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&sm.u.Q[r][c4]);
+      *reinterpret_cast<v4*>(K16w + base + dst) = *reinterpret_cast<const v4*>(&sm.K[r][c4]);
+    }
+  }
+  __syncthreads();  // Q is dead: its storage takes K^T
+  for (int i = tid; i < CHUNK * D; i += 256) {
+    const int kc = i % D, sr = i / D;
+    sm.u.Kt[kc][sr] = sm.K[sr][kc];
+  }
+  __syncthreads();
+  {
+    // K^T rows of 64 (columns in accumulator order) to the workspace, in
+    // 4-element pieces
+    constexpr int PR = CHUNK / 4;
+    CT* ko = Ktw + ((int64_t)c * (Hv / G) + kh) * D * CHUNK;
+    for (int i = tid; i < D * PR; i += 256) {
+      const int kr = i / PR, c4 = (i % PR) * 4;
+      typedef CT v4 __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
+          *reinterpret_cast<const v4*>(&sm.u.Kt[kr][c4]);
+    }
+  }
 
   for (int hh = 0; hh < G; ++hh) {
     const int h = kh * G + hh;
@@ -93,6 +138,13 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       sm.gam[lane] = gm;
       sm.bet[lane] = bl;
       if (lane < L) gcum[(t0 + lane) * Hv + h] = gm;
+      // gam is flat past the chunk length (g = 0 there), so these are the
+      // factors of token min(t, L - 1)
+      const double glast = __shfl(gm, CHUNK - 1, 64);
+      const float Gm = dexp<T>(gm);
+      sm.sbg[lane] = bl * Gm;
+      Gw[((int64_t)c * Hv + h) * CHUNK + lane] = Gm;
+      Dw[((int64_t)c * Hv + h) * CHUNK + lane] = dexp<T>(glast - gm);
     }
     __syncthreads();
     CT* Pout = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
@@ -104,7 +156,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
         const int t = rbase + e;
         const float dec = dexp<T>(sm.gam[t] - sm.gam[s <= t ? s : t]);  // masked before exp
         sm.A[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
-        Pout[t * CHUNK + s] = from_f<CT>((s <= t) ? dec * scale * qk[j][e] : 0.f);
+        Pout[t * CHUNK + acc_col<CT>(s)] = from_f<CT>((s <= t) ? dec * scale * qk[j][e] : 0.f);
       }
     }
     __syncthreads();
@@ -117,248 +169,46 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       for (int u = 0; u < 8; ++u) v.v[u] = sm.Ti[t][s8 + u] * sm.bet[s8 + u];
       store8(Mout + t * CHUNK + s8, v);
     }
+    // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead
+    // A storage (columns in accumulator order), then all rows go out in
+    // 16-byte pieces.  beta Gam scales the A operand (Tinv columns).
+    {
+      typedef typename MM::frag frag;
+      frag ta[CHUNK / KS];
+#pragma unroll
+      for (int s0 = 0; s0 < CHUNK / KS; ++s0) {
+        if constexpr (KS == 4) {
+          const int sc = s0 * KS + (lane >> 4);
+          ta[s0] = sm.Ti[16 * wave + r16][sc] * sm.sbg[sc];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int sc = s0 * KS + 8 * (lane >> 4) + j;
+            ta[s0][j] = (CT)(sm.Ti[16 * wave + r16][sc] * sm.sbg[sc]);
+          }
+        }
+      }
+      CT (*Wl)[LD] = reinterpret_cast<CT (*)[LD]>(&sm.A[0][0]);
+#pragma unroll
+      for (int kt = 0; kt < D / 16; ++kt) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int s0 = 0; s0 < CHUNK / KS; ++s0)
+          acc = MM::mma(ta[s0], MM::kc(&sm.u.Kt[16 * kt + r16][0], s0 * KS, lane), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Wl[rbase + e][acc_col<CT>(16 * kt + ccol)] = from_f<CT>(acc[e]);
+      }
+      __syncthreads();
+      constexpr int PR = D * (int)sizeof(CT) / 16;
+      uint4* wo = reinterpret_cast<uint4*>(Ww + ((int64_t)c * Hv + h) * CHUNK * D);
+      for (int i = tid; i < CHUNK * PR; i += 256)
+        wo[i] = reinterpret_cast<const uint4*>(&Wl[i / PR][0])[i % PR];
+    }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Sequential state pass, one workgroup per (value-row block, value head,
-// sequence).  The state block S[vb*BV : vb*BV+BV, :] lives in MFMA
-// accumulators as S^T tiles (d_k rows x BV columns) for the whole sequence.
-// Wave w owns token rows [16w, 16w+16) of every (token x value) product, so
-// its A operands (Q, M, P rows) come straight from memory into registers;
-// K is staged in LDS because the state update reads it transposed.
-// Chunk c+1's inputs are loaded into registers while chunk c computes.
-//   MODE 0 (forward): writes o and S_final.
-//   MODE 1 (backward recompute): writes the chunk-start states h ([dk][dv]
-//   per chunk and head), R and Delta.
-template <typename T, int D, int BV>
-struct StateSmem {
-  typedef typename Compute<T>::type CT;
-  CT K[CHUNK][D + Pad<CT>::v];
-  CT Sb[BV][D + Pad<CT>::v];       // S block (v-major), MFMA B operand of K S^T
-  CT Rt[BV][CHUNK + Pad<CT>::v];   // R^T
-  CT Dt[BV][CHUNK + Pad<CT>::v];   // Delta^T
-  CT Dst[BV][CHUNK + Pad<CT>::v];  // (diag(dec) Delta)^T
-  double gam[CHUNK];
-};
-
-template <typename T, int D, int BV, int MODE>
-__global__ void __launch_bounds__(256) chunk_state_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t ldq,
-    int64_t ldk, int64_t ldv, const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off,
-    int Hv, int G, float scale, const double* __restrict__ gcum,
-    const typename Compute<T>::type* __restrict__ Mw, const typename Compute<T>::type* __restrict__ Pw,
-    const float* __restrict__ S0, float* __restrict__ S_final, T* __restrict__ o,
-    T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw, void* __restrict__ sink,
-    int n_items) {
-  typedef typename Compute<T>::type CT;
-  typedef Mma<CT> MM;
-  typedef FragKC<CT, T> FQ;     // Q rows (storage type)
-  typedef FragKC<CT, CT> FM;    // M, P rows (compute type)
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  StateSmem<T, D, BV>& sm = *reinterpret_cast<StateSmem<T, D, BV>*>(smem_raw);
-  constexpr int LD = D + Pad<CT>::v, LDC = CHUNK + Pad<CT>::v;
-  constexpr int KS = MM::KS;
-  constexpr int NVT = BV / 16;                      // value tiles per wave (rows fixed)
-  constexpr int NS = (D / 16) * NVT / 4;            // state tiles per wave
-  constexpr int NKD = D / KS, NKC = CHUNK / KS;     // MFMA steps over d_k and over the chunk
-  static_assert(NS >= 1, "tile split");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int item = xcd_item(blockIdx.x, n_items);
-  const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
-  const int kh = h / G;
-  const int v0 = vb * BV;
-  const int rsub = 4 * (lane >> 4), ccol = lane & 15, r16 = lane & 15;
-  const int trow = 16 * wave;                       // this wave's token rows
-  const int64_t HvD = (int64_t)Hv * D;
-
-  floatx4 S[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-    const int vv = v0 + 16 * vt + ccol;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kk = 16 * kt + rsub + e;
-      S[i][e] = S0 ? S0[(((int64_t)n * Hv + h) * D + vv) * D + kk] : 0.f;
-    }
-  }
-
-  // ---- prefetch registers for one chunk
-  struct Pref {
-    RowPrefetch<T, D> k;                   // K rows -> LDS
-    typename FQ::raw q[NKD];               // Q fragments (MODE 0)
-    typename FM::raw m[NKC], p[NKC];       // M, P fragments
-    T v[NVT][4];                           // V at this lane's output positions (raw)
-    double g;                              // gam[tid & 63]
-    int L;
-    int64_t t0;
-  };
-  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
-  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
-  auto prefetch = [&](Pref& P, int64_t c) {
-    P.t0 = seq_t0 + CHUNK * (c - c_begin);
-    const int64_t rem = seq_t1 - P.t0;
-    const int L = rem < CHUNK ? (int)rem : CHUNK;
-    const int64_t t0 = P.t0;
-    P.L = L;
-    P.k.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-    const int tq = trow + r16 < L ? trow + r16 : L - 1;   // clamp: rows >= L never reach outputs
-    if (MODE == 0) {
-#pragma unroll
-      for (int s = 0; s < NKD; ++s) P.q[s] = FQ::load(q + (t0 + tq) * ldq + (int64_t)kh * D, s * KS, lane);
-    }
-    const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + (trow + r16) * CHUNK;
-    const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + (trow + r16) * CHUNK;
-#pragma unroll
-    for (int s = 0; s < NKC; ++s) {
-      P.m[s] = FM::load(Mc, s * KS, lane);
-      if (MODE == 0) P.p[s] = FM::load(Pc, s * KS, lane);
-    }
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = trow + rsub + e;
-        P.v[vt][e] = v[(t0 + (t < L ? t : L - 1)) * ldv + (int64_t)h * D + v0 + 16 * vt + ccol];
-      }
-    const int tg = tid & (CHUNK - 1);
-    P.g = gcum[(t0 + (tg < L ? tg : L - 1)) * Hv + h];
-  };
-
-  // One chunk from prefetched registers `cur`; issues the prefetch of chunk
-  // c + 1 into `nxt` before computing.
-  auto step = [&](int64_t c, Pref& cur, Pref& nxt) {
-    const int L = cur.L;
-    const int64_t t0 = cur.t0;
-    __syncthreads();  // previous chunk's LDS reads are done
-    cur.k.store(&sm.K[0][0], LD, tid);
-    sm.gam[tid & (CHUNK - 1)] = cur.g;  // the four waves write identical values
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-      const int vv = 16 * vt + ccol, kk = 16 * kt + rsub;
-      store4(&sm.Sb[vv][kk], S[i][0], S[i][1], S[i][2], S[i][3]);
-      if (MODE == 1) {
-        T* hp = hst + (((int64_t)c * Hv + h) * D + kk) * D + v0 + vv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hp[(int64_t)e * D] = from_f<T>(S[i][e]);
-      }
-    }
-    prefetch(nxt, c + 1 < c_end ? c + 1 : c);  // unconditional (re-reads the last chunk at the end)
-    issue_fence();
-    __syncthreads();
-
-    // Phase A: R = V - diag(Gam) K S^T   (and the Q S^T part of O)
-    floatx4 oq[NVT];
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      floatx4 ks = zero4();
-      oq[vt] = zero4();
-#pragma unroll
-      for (int s = 0; s < NKD; ++s) {
-        const typename MM::frag b = MM::kc(&sm.Sb[16 * vt + r16][0], s * KS, lane);
-        ks = MM::mma(MM::kc(&sm.K[trow + r16][0], s * KS, lane), b, ks);
-        if (MODE == 0) oq[vt] = MM::mma(FQ::cvt(cur.q[s]), b, oq[vt]);
-      }
-      const int vv = 16 * vt + ccol, tb = trow + rsub;
-      float r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float Gm = dexp<T>(sm.gam[tb + e]);
-        const float vin = tb + e < L ? to_f(cur.v[vt][e]) : 0.f;
-        r[e] = vin - Gm * ks[e];
-        if (MODE == 0) oq[vt][e] *= Gm * scale;
-      }
-      store4(&sm.Rt[vv][tb], r[0], r[1], r[2], r[3]);
-      if (MODE == 1) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *row_or_sink(Rw + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
-              from_f<T>(r[e]);
-      }
-    }
-    __syncthreads();
-
-    // Phase B: Delta = M R
-    const double gl = sm.gam[CHUNK - 1];
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      floatx4 dl = zero4();
-#pragma unroll
-      for (int s = 0; s < NKC; ++s)
-        dl = MM::mma(FM::cvt(cur.m[s]), MM::kc(&sm.Rt[16 * vt + r16][0], s * KS, lane), dl);
-      const int vv = 16 * vt + ccol, tb = trow + rsub;
-      float ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ds[e] = dexp<T>(gl - sm.gam[tb + e]) * dl[e];
-      store4(&sm.Dt[vv][tb], dl[0], dl[1], dl[2], dl[3]);
-      store4(&sm.Dst[vv][tb], ds[0], ds[1], ds[2], ds[3]);
-      if (MODE == 1) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *row_or_sink(Dlw + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
-              from_f<T>(dl[e]);
-      }
-    }
-    __syncthreads();
-
-    // Phase C: O = oq + P Delta;  S^T <- Gam_L S^T + K^T (diag(dec) Delta)
-    if (MODE == 0) {
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) {
-        floatx4 ov = oq[vt];
-#pragma unroll
-        for (int s = 0; s < NKC; ++s)
-          ov = MM::mma(FM::cvt(cur.p[s]), MM::kc(&sm.Dt[16 * vt + r16][0], s * KS, lane), ov);
-        const int vv = 16 * vt + ccol, tb = trow + rsub;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *row_or_sink(o + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
-              from_f<T>(ov[e]);
-      }
-    }
-    const float GL = dexp<T>(gl);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[i][e] *= GL;
-      S[i] = tile_mma<CT, false, true>(S[i], &sm.K[0][0], LD, &sm.Dst[0][0], LDC, 16 * kt, 16 * vt,
-                                       CHUNK, lane);
-    }
-  };
-
-  Pref A, B;
-  if (c_begin < c_end) prefetch(A, c_begin);
-  for (int64_t c = c_begin; c < c_end; c += 2) {
-    step(c, A, B);
-    if (c + 1 < c_end) step(c + 1, B, A);
-  }
-  // Never taken (chunk offsets are non-negative): gives both prefetch buffers
-  // a use on the loop-exit path, so their loads are not sunk into the branch
-  // that runs the second step of a pair (which would serialise them).
-  if (c_end < 0) {
-    T* sk = reinterpret_cast<T*>(sink);
-    *reinterpret_cast<Raw8<T>*>(sk) = A.k.r[0];
-    *reinterpret_cast<Raw8<T>*>(sk + 64) = B.k.r[0];
-    sk[128] = A.v[0][0];
-    sk[129] = B.v[0][0];
-  }
-  if (MODE == 0 && S_final) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-      const int vv = v0 + 16 * vt + ccol, kk = 16 * kt + rsub;
-      store4(S_final + (((int64_t)n * Hv + h) * D + vv) * D + kk, S[i][0], S[i][1], S[i][2], S[i][3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-constexpr int STATE_BV = 32;  // value rows of the state owned by one workgroup
-
 template <typename T, int D>
 static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
                                 int64_t ldk, const float* g, const float* beta, float scale,
@@ -374,28 +224,13 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        st, (const T*)q, (const T*)k, ldq, ldk, g, beta, cu, seq_off, s.n_seq, s.hv,
                        s.hv / s.hk, scale, (double*)(ws + Ly.gcum),
                        (typename Compute<T>::type*)(ws + Ly.mw),
-                       (typename Compute<T>::type*)(ws + Ly.pw));
+                       (typename Compute<T>::type*)(ws + Ly.pw),
+                       (typename Compute<T>::type*)(ws + Ly.ww),
+                       (typename Compute<T>::type*)(ws + Ly.ktw),
+                       (typename Compute<T>::type*)(ws + Ly.q16w),
+                       (typename Compute<T>::type*)(ws + Ly.k16w), (float*)(ws + Ly.gw),
+                       (float*)(ws + Ly.dw));
   }
-  return hipGetLastError();
-}
-
-template <typename T, int D, int MODE>
-static hipError_t chunk_state(const gdn_shape& s, const void* q, const void* k, const void* v,
-                              int64_t ldq, int64_t ldk, int64_t ldv, float scale, const float* S0,
-                              float* S_final, const int32_t* cu, void* o, const ChunkLayout& Ly,
-                              char* ws, hipStream_t st) {
-  constexpr int BV = STATE_BV;
-  const size_t shm = sizeof(StateSmem<T, D, BV>);
-  auto kern = chunk_state_kernel<T, D, BV, MODE>;
-  hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  const int n_items = (D / BV) * s.hv * s.n_seq;
-  hipLaunchKernelGGL(kern, dim3(n_items), dim3(256), shm, st, (const T*)q, (const T*)k,
-                     (const T*)v, ldq, ldk, ldv, cu, (const int32_t*)(ws + Ly.seq_off), s.hv,
-                     s.hv / s.hk, scale, (const double*)(ws + Ly.gcum),
-                     (const typename Compute<T>::type*)(ws + Ly.mw),
-                     (const typename Compute<T>::type*)(ws + Ly.pw), S0, S_final, (T*)o,
-                     (T*)(ws + Ly.h), (T*)(ws + Ly.rw), (T*)(ws + Ly.dlw), (void*)(ws + Ly.sink),
-                     n_items);
   return hipGetLastError();
 }
 
@@ -409,29 +244,6 @@ hipError_t launch_chunk_prepare(const gdn_shape& s, const void* q, const void* k
   return dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
     return chunk_prepare<T, decltype(c)::d>(s, q, k, ldq, ldk, g, beta, scale, cu, Ly, (char*)ws, st);
-  });
-}
-
-hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
-                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
-                                   const float* S0, float* S_final, const int32_t* cu, void* o,
-                                   void* ws, hipStream_t st) {
-  const ChunkLayout Ly = chunk_layout(s);
-  return dispatch_chunk(s, [&](auto c) {
-    using T = typename decltype(c)::type;
-    return chunk_state<T, decltype(c)::d, 0>(s, q, k, v, ldq, ldk, ldv, scale, S0, S_final, cu, o,
-                                             Ly, (char*)ws, st);
-  });
-}
-
-hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
-                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
-                                   const float* S0, const int32_t* cu, void* ws, hipStream_t st) {
-  const ChunkLayout Ly = chunk_layout(s);
-  return dispatch_chunk(s, [&](auto c) {
-    using T = typename decltype(c)::type;
-    return chunk_state<T, decltype(c)::d, 1>(s, q, k, v, ldq, ldk, ldv, scale, S0, nullptr, cu,
-                                             nullptr, Ly, (char*)ws, st);
   });
 }
 

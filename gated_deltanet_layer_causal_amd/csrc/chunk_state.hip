@@ -1,0 +1,446 @@
+// Chunked gated delta rule: the sequential state pass over the chunks of each
+// sequence (forward outputs, or the states the backward needs).
+//
+// With the preparation's W = M diag(Gam) K, the chunk recurrence is
+//   U     = M V                       (needs no state)
+//   Delta = U - W S^T
+//   S     <- Gam_L S + (diag(dec) Delta)^T K
+// and the outputs O = diag(Gam) scale Q S^T + P Delta (forward) or
+// R = V - diag(Gam) K S^T (backward).  Only the two products through S are
+// sequential; everything else hangs off them.
+//
+// One workgroup per (sequence, value head, block of 16 * NW value rows of the
+// state); wave w owns 16 value rows and keeps its d_k x 16 slice of S^T in
+// MFMA accumulators for the whole sequence.  Its products with S take S
+// straight from those accumulators as the B operand: an accumulator tile
+// holds rows 4 (l / 16) + i of column l % 16 in lane l, so two stacked tiles
+// give every lane eight reduction indices, and the A operand is read from
+// LDS in the same (permuted) reduction order (AccOrder; the preparation
+// stores those operands with their columns in that order, acc_col).
+//
+// The chunk's shared operands (W, K^T, Q or K, M, P, V, Gam, dec) are copied
+// from memory straight into LDS (global_load_lds, no registers), into one of
+// two buffers: chunk c + 1 streams into one while chunk c computes from the
+// other, so a chunk step has a single barrier.  A direct copy writes 64
+// consecutive 16-byte pieces per wave, so the LDS tiles are unpadded and
+// bank conflicts are avoided by permuting the 16-byte pieces of each row
+// (Tile).  Every address that varies by lane is computed once: copies go
+// through buffer resources (uniform base, per-lane offset) and LDS reads use
+// per-lane offsets plus constants.
+#include "chunk_common.h"
+
+namespace gdn {
+
+// Reduction order of an MFMA step whose B operand comes from accumulator
+// tiles x[0..] (rows = reduction index).
+//  16-bit operands (32 per step): step p uses tiles 2p and 2p + 1; lane l's
+//    slot j holds reduction index 16 (2p + j / 4) + 4 (l / 16) + j % 4.
+//  fp32 operands (4 per step): step p holds index 16 (p / 4) + 4 (l / 16) + p % 4.
+template <typename CT> struct AccOrder {
+  typedef typename Mma<CT>::frag frag;
+  __device__ __forceinline__ static frag from_acc(const floatx4* x, int p) {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[j] = (CT)x[2 * p][j];
+      f[4 + j] = (CT)x[2 * p + 1][j];
+    }
+    return f;
+  }
+};
+template <> struct AccOrder<float> {
+  typedef float frag;
+  __device__ __forceinline__ static frag from_acc(const floatx4* x, int p) { return x[p >> 2][p & 3]; }
+};
+
+// Piece permutation of LDS row r (RP 16-byte pieces per row): reads by 16
+// consecutive rows then touch RP (RP <= 8) or 16 different piece slots.
+// With RP <= 8 it depends on r mod RP only, so a direct copy (64 pieces per
+// wave = 64 / RP whole rows) needs the same per-lane source offset in every
+// copy instruction.
+template <int RP> __device__ __forceinline__ int row_swz(int r) {
+  if constexpr (RP == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return r & (RP - 1);
+}
+
+// An LDS tile of ROWS rows of COLS elements of type E, unpadded, with the
+// 16-byte pieces of row r permuted: piece q lives at slot q ^ swz(r), where
+// swz = row_swz (SWZ_SHIFT = 0) or (r >> SWZ_SHIFT) mod RP.
+template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
+  static constexpr int EPP = 16 / sizeof(E);         // elements per piece
+  static constexpr int RP = COLS / EPP;              // pieces per row
+  static constexpr int PIECES = ROWS * RP;
+  static_assert(RP == 4 || RP == 8 || RP == 16, "pieces per row");
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (SWZ_SHIFT == 0) return row_swz<RP>(r);
+    else return (r >> SWZ_SHIFT) & (RP - 1);
+  }
+  // element offset of (r, col)
+  __device__ __forceinline__ static int at(int r, int col) {
+    return (r * RP + ((col / EPP) ^ swz(r))) * EPP + col % EPP;
+  }
+  // byte offset, within the source tile, of the piece that LDS slot s holds
+  __device__ __forceinline__ static uint32_t source_bytes(int s) {
+    const int r = s / RP;
+    return (uint32_t)(r * RP + ((s % RP) ^ swz(r))) * 16u;
+  }
+  // Copy J (64 slots from 64 J) reads source_bytes(64 J + lane) =
+  // 1024 J + lane_bytes(J, lane); lane_bytes depends on J only through
+  // J mod 4 for RP = 16 and not at all for RP <= 8 (row_swz tiles).
+  __device__ __forceinline__ static uint32_t lane_bytes(int J, int lane) {
+    return source_bytes(64 * (RP == 16 ? (J & 3) : 0) + lane) - 1024u * (RP == 16 ? (J & 3) : 0);
+  }
+};
+
+template <typename T, int D, int NW, int MODE> struct StateBuf {
+  typedef typename Compute<T>::type CT;
+  static constexpr int BV = 16 * NW;
+  typedef Tile<CT, CHUNK, D> TW;        // W, and Q / K rows
+  typedef Tile<CT, D, CHUNK> TKt;       // K^T
+  typedef Tile<CT, CHUNK, CHUNK> TM;    // M, P
+  typedef Tile<T, CHUNK, BV, 3> TV;     // value rows (storage type)
+  CT W[TW::PIECES * TW::EPP];
+  CT Kt[TKt::PIECES * TKt::EPP];
+  CT X[TW::PIECES * TW::EPP];
+  CT M[TM::PIECES * TM::EPP];
+  CT P[MODE == 0 ? TM::PIECES * TM::EPP : 8];
+  T V[TV::PIECES * TV::EPP];
+  float G[CHUNK], Dc[CHUNK];            // Gam_t, dec_t
+} __attribute__((aligned(16)));
+
+// Direct copy of one 16-byte piece per lane from a buffer into LDS: the
+// wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
+// Buffer accesses are range-checked against the descriptor's size on the
+// per-lane offset (loads past it read zero, stores past it are dropped).
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                            uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, uint32_t voff, float x) {
+  if constexpr (sizeof(T) == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<T>(x)), rs, voff, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), rs, voff, 0, 0);
+  }
+}
+
+template <typename T, int D, int NW, int MODE>
+__global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
+    const T* __restrict__ v, int64_t ldv, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
+    const typename Compute<T>::type* __restrict__ Mw, const typename Compute<T>::type* __restrict__ Pw,
+    const typename Compute<T>::type* __restrict__ Ww, const typename Compute<T>::type* __restrict__ Ktw,
+    const typename Compute<T>::type* __restrict__ Xw, const float* __restrict__ Gw,
+    const float* __restrict__ Dw, const float* __restrict__ S0, float* __restrict__ S_final,
+    T* __restrict__ o, T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw, int n_items) {
+  typedef typename Compute<T>::type CT;
+  typedef Mma<CT> MM;
+  typedef AccOrder<CT> AO;
+  typedef typename MM::frag frag;
+  typedef StateBuf<T, D, NW, MODE> SB;
+  typedef typename SB::TW TW;
+  typedef typename SB::TKt TKt;
+  typedef typename SB::TM TM;
+  typedef typename SB::TV TV;
+  constexpr int THREADS = 64 * NW;
+  constexpr int BV = SB::BV;
+  constexpr int KS = MM::KS;
+  constexpr int NSD = D / KS;       // MFMA steps over d_k
+  constexpr int NSC = CHUNK / KS;   // MFMA steps over the chunk
+  constexpr int NKT = D / 16;       // state tiles per wave
+  constexpr int NV = KS == 4 ? 1 : 8;   // operand values per lane per step
+  static_assert(TW::PIECES % THREADS == 0 && TKt::PIECES % THREADS == 0 &&
+                TM::PIECES % THREADS == 0 && TV::PIECES % THREADS == 0,
+                "direct copies cover whole waves");
+  __shared__ SB bufA, bufB;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_ = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave_;
+  const int item = xcd_item(blockIdx.x, n_items);
+  const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
+  const int kh = h / G, Hk = Hv / G;
+  const int v0 = vb * BV;
+  const int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
+  const int vcol = 16 * wave + c16;                 // value row of S this lane's columns hold
+  const int64_t HvD = (int64_t)Hv * D;
+
+  floatx4 S[NKT];   // S^T tiles: rows k = 16 kt + g4 + i, column v0 + vcol
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[kt][i] = S0 ? S0[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] : 0.f;
+
+  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
+  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
+
+  // ---- per-lane offsets, the same for every chunk
+  // copies: copy J = j NW + wave of a tile reads 1024 J + lane_bytes, which
+  // depends only on the tile's pieces per row (and on J mod 4 for 16)
+  uint32_t c16p[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) c16p[a] = Tile<float, 64, 64>::lane_bytes(a, lane);
+  const uint32_t c8p = Tile<float, 64, 32>::lane_bytes(0, lane);
+  const uint32_t c4p = Tile<float, 64, 16>::lane_bytes(0, lane);
+  // stores: byte offset of this lane's first row (g4) and column
+  const uint32_t so = (uint32_t)(((int64_t)g4 * HvD + vcol) * sizeof(T));
+  const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
+  // reads: element offsets of this lane's operand values for MFMA step p
+  // (row c16 of a 16-row tile; tile index and buffer enter as constants)
+  // (16-bit: the eight values are the 16-byte piece 4 p + g of the row, the
+  // columns being stored in accumulator order)
+  int rw[NSD], rk[NSC], rm[NSC];
+#pragma unroll
+  for (int p = 0; p < NSD; ++p)
+    rw[p] = KS == 4 ? TW::at(c16, 16 * (p >> 2) + g4 + (p & 3)) : TW::at(c16, 32 * p + 8 * g);
+#pragma unroll
+  for (int p = 0; p < NSC; ++p) {
+    rk[p] = KS == 4 ? TKt::at(c16, 16 * (p >> 2) + g4 + (p & 3)) : TKt::at(c16, 32 * p + 8 * g);
+    rm[p] = TM::at(c16, p * KS + (KS == 4 ? g : 8 * g));
+  }
+  // K^T and P rows both hold CHUNK elements, so rk addresses P as well
+
+  // ---- chunk c's operands into buffer B (value rows past a sequence end
+  // re-read its last row)
+  auto fetch = [&](SB& B, int64_t c) __attribute__((always_inline)) {
+    // LDS destinations derived from a laundered wave index are formed here
+    // (one scalar add each) instead of being hoisted into scalar registers.
+    int wave = wave_;
+    asm volatile("" : "+s"(wave));
+    const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - t0;
+    const int Lc = rem < CHUNK ? (int)rem : CHUNK;
+    const int64_t ch = (int64_t)c * Hv + h, ck_ = (int64_t)c * Hk + kh;
+    // the per-copy part (1024 J) goes into the base address, so that the
+    // range check sees only the per-lane offset
+    auto tile = [&](auto tt, CT* dst, const CT* src) __attribute__((always_inline)) {
+      typedef decltype(tt) TT;
+#pragma unroll
+      for (int j = 0; j < TT::PIECES / THREADS; ++j) {
+        const int J = j * NW + wave;
+        const auto rs = buffer_of(reinterpret_cast<const char*>(src) + 1024 * J, 1024);
+        copy_to_lds(rs, dst + J * 64 * TT::EPP, TT::RP == 16 ? c16p[J & 3] : TT::RP == 8 ? c8p : c4p, 0);
+      }
+    };
+    tile(TW{}, B.W, Ww + ch * CHUNK * D);
+    tile(TW{}, B.X, Xw + ck_ * CHUNK * D);
+    tile(TKt{}, B.Kt, Ktw + ck_ * D * CHUNK);
+    tile(TM{}, B.M, Mw + ch * CHUNK * CHUNK);
+    if constexpr (MODE == 0) tile(TM{}, B.P, Pw + ch * CHUNK * CHUNK);
+    {
+      const uint32_t ldb = (uint32_t)(ldv * sizeof(T));
+      const auto rs = buffer_of(v + t0 * ldv + (int64_t)h * D + v0, (uint32_t)Lc * ldb);
+#pragma unroll
+      for (int j = 0; j < TV::PIECES / THREADS; ++j) {
+        const int s = (j * NW + wave) * 64 + lane, r = s / TV::RP;
+        const uint32_t off = (uint32_t)(r < Lc ? r : Lc - 1) * ldb +
+                             (uint32_t)((s % TV::RP) ^ TV::swz(r)) * 16u;
+        copy_to_lds(rs, B.V + (j * NW + wave) * 64 * TV::EPP, off, 0);
+      }
+    }
+    if (wave == 0 && lane < 16) {   // Gam and dec, 64 floats each
+      copy_to_lds(buffer_of(Gw + ch * CHUNK, CHUNK * 4), B.G, 16u * lane, 0);
+      copy_to_lds(buffer_of(Dw + ch * CHUNK, CHUNK * 4), B.Dc, 16u * lane, 0);
+    }
+  };
+
+  // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).
+  auto arow = [&](const CT* base, int o, int tile_elems) __attribute__((always_inline)) -> frag {
+    if constexpr (KS == 4) return base[tile_elems + o];
+    else return *reinterpret_cast<const frag*>(base + tile_elems + o);
+  };
+
+  // ---- one chunk from buffer B
+  auto compute = [&](const SB& B, int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - t0;
+    const int L = rem < CHUNK ? (int)rem : CHUNK;
+
+    // -S^T as B operands, straight from the accumulators
+    frag sbn[NSD];
+#pragma unroll
+    for (int p = 0; p < NSD; ++p) sbn[p] = -AO::from_acc(S, p);
+    if constexpr (MODE == 1) {
+      // chunk-start state, [d_k][d_v] per (chunk, head)
+      const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
+      const uint32_t hb = (uint32_t)((g4 * D + vcol) * sizeof(T));
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store_elem<T>(rs, hb + (uint32_t)((16 * kt + i) * D * sizeof(T)), S[kt][i]);
+    }
+
+    // Delta = W (-S^T) + M V
+    floatx4 Dl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      Dl[tt] = zero4();
+#pragma unroll
+      for (int p = 0; p < NSD; ++p) Dl[tt] = MM::mma(arow(B.W, rw[p], 16 * tt * D), sbn[p], Dl[tt]);
+    }
+    {
+      frag bv[NSC];
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) {
+        if constexpr (KS == 4) {
+          bv[p] = to_f(B.V[TV::at(p * KS + g, vcol)]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NV; ++j) bv[p][j] = (CT)to_f(B.V[TV::at(p * KS + 8 * g + j, vcol)]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) {
+          frag ma;
+          if constexpr (KS == 4) ma = B.M[16 * tt * CHUNK + rm[p]];
+          else ma = *reinterpret_cast<const frag*>(B.M + 16 * tt * CHUNK + rm[p]);
+          Dl[tt] = MM::mma(ma, bv[p], Dl[tt]);
+        }
+    }
+
+    // X (-S^T): Q (MODE 0) or K (MODE 1) rows
+    floatx4 xs[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      xs[tt] = zero4();
+#pragma unroll
+      for (int p = 0; p < NSD; ++p) xs[tt] = MM::mma(arow(B.X, rw[p], 16 * tt * D), sbn[p], xs[tt]);
+    }
+
+    // state update: S^T <- Gam_L S^T + K^T diag(dec) Delta
+    {
+      floatx4 ds[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const float4 dc = *reinterpret_cast<const float4*>(&B.Dc[16 * tt + g4]);
+        ds[tt][0] = dc.x * Dl[tt][0];
+        ds[tt][1] = dc.y * Dl[tt][1];
+        ds[tt][2] = dc.z * Dl[tt][2];
+        ds[tt][3] = dc.w * Dl[tt][3];
+      }
+      frag dsf[NSC];
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) dsf[p] = AO::from_acc(ds, p);
+      const float GL = B.G[CHUNK - 1];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[kt][i] *= GL;
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) S[kt] = MM::mma(arow(B.Kt, rk[p], 16 * kt * CHUNK), dsf[p], S[kt]);
+      }
+    }
+
+    if constexpr (MODE == 0) {
+      // O = diag(Gam) scale Q S^T + P Delta
+      frag duf[NSC];
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) duf[p] = AO::from_acc(Dl, p);
+      // rows past the sequence end fall outside the buffer: dropped
+      const auto rs = buffer_of(o + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        floatx4 ov = zero4();
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) ov = MM::mma(arow(B.P, rk[p], 16 * tt * CHUNK), duf[p], ov);
+        const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
+        const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store_elem<T>(rs, so + (uint32_t)(16 * tt + i) * rowb, ov[i] - scale * gv[i] * xs[tt][i]);
+      }
+    } else {
+      // R = V - diag(Gam) K S^T and Delta
+      // rows past the sequence end fall outside the buffers: dropped
+      const auto rr = buffer_of(Rw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+      const auto rd = buffer_of(Dlw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
+        const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * tt + g4 + i;
+          const uint32_t off = so + (uint32_t)(16 * tt + i) * rowb;
+          store_elem<T>(rr, off, to_f(B.V[TV::at(t, vcol)]) + gv[i] * xs[tt][i]);
+          store_elem<T>(rd, off, Dl[tt][i]);
+        }
+      }
+    }
+  };
+
+  if (c_begin < c_end) fetch(bufA, c_begin);
+  __syncthreads();
+  for (int64_t c = c_begin; c < c_end; c += 2) {
+    fetch(bufB, c + 1 < c_end ? c + 1 : c);   // a repeat of chunk c at the end
+    compute(bufA, c);
+    __syncthreads();   // waits for this wave's copies; then every wave's are visible
+    if (c + 1 < c_end) {
+      fetch(bufA, c + 2 < c_end ? c + 2 : c + 1);
+      compute(bufB, c + 1);
+      __syncthreads();
+    }
+  }
+
+  if (MODE == 0 && S_final) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S_final[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] = S[kt][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+constexpr int STATE_NW = 2;   // waves (16 value rows of the state each) per workgroup
+
+template <typename T, int D, int MODE>
+static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, float scale,
+                              const float* S0, float* S_final, const int32_t* cu, void* o,
+                              const ChunkLayout& Ly, char* ws, hipStream_t st) {
+  constexpr int NW = STATE_NW, BV = 16 * NW;
+  typedef typename Compute<T>::type CT;
+  auto kern = chunk_state_kernel<T, D, NW, MODE>;
+  const int n_items = (D / BV) * s.hv * s.n_seq;
+  hipLaunchKernelGGL(kern, dim3(n_items), dim3(64 * NW), 0, st, (const T*)v, ldv, cu,
+                     (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
+                     (const CT*)(ws + Ly.mw), (const CT*)(ws + Ly.pw), (const CT*)(ws + Ly.ww),
+                     (const CT*)(ws + Ly.ktw), (const CT*)(ws + (MODE == 0 ? Ly.q16w : Ly.k16w)),
+                     (const float*)(ws + Ly.gw), (const float*)(ws + Ly.dw), S0, S_final, (T*)o,
+                     (T*)(ws + Ly.h), (T*)(ws + Ly.rw), (T*)(ws + Ly.dlw), n_items);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
+                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                   const float* S0, float* S_final, const int32_t* cu, void* o,
+                                   void* ws, hipStream_t st) {
+  const ChunkLayout Ly = chunk_layout(s);
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    return chunk_state<T, decltype(c)::d, 0>(s, v, ldv, scale, S0, S_final, cu, o, Ly, (char*)ws,
+                                             st);
+  });
+}
+
+hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
+                                   int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                   const float* S0, const int32_t* cu, void* ws, hipStream_t st) {
+  const ChunkLayout Ly = chunk_layout(s);
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    return chunk_state<T, decltype(c)::d, 1>(s, v, ldv, scale, S0, nullptr, cu, nullptr, Ly,
+                                             (char*)ws, st);
+  });
+}
+
+}  // namespace gdn

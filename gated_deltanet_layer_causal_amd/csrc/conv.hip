@@ -239,21 +239,52 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
   }
 }
 
-__global__ void reduce_partials_kernel(const float* __restrict__ partials, int64_t n_part,
-                                       int64_t width, float* __restrict__ out) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= width) return;
+// out[i] = sum over p of partials[p * width + i] in a fixed order: thread
+// group j of RED_G adds p = j, j + RED_G, ... (eight loads in flight), then
+// the group sums are added in group order.  Columns i < split go to out0[i],
+// the rest to out1[i - split].
+constexpr int RED_G = 16;
+
+__global__ void __launch_bounds__(64 * RED_G) reduce_partials_kernel(
+    const float* __restrict__ partials, int64_t n_part, int64_t width, float* __restrict__ out0,
+    int64_t split, float* __restrict__ out1) {
+  __shared__ float part[RED_G][64];
+  const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + col;
   float acc = 0.f;
-  for (int64_t p = 0; p < n_part; ++p) acc += partials[p * width + i];
-  out[i] = acc;
+  if (i < width) {
+    int64_t p = grp;
+    for (; p + 7 * RED_G < n_part; p += 8 * RED_G) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = partials[(p + u * RED_G) * width + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; p < n_part; p += RED_G) acc += partials[p * width + i];
+  }
+  part[grp][col] = acc;
+  __syncthreads();
+  if (grp == 0 && i < width) {
+    float sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < RED_G; ++g) sum += part[g][col];
+    if (i < split) out0[i] = sum;
+    else out1[i - split] = sum;
+  }
+}
+
+hipError_t launch_reduce_partials(const float* partials, int64_t n_part, int64_t width,
+                                  float* out0, int64_t split, float* out1, hipStream_t st) {
+  if (width > 0)
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((width + 63) / 64)),
+                       dim3(64 * RED_G), 0, st, partials, n_part, width, out0, split, out1);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_partials(const float* partials, int64_t n_part, int64_t width,
                                   float* out, hipStream_t st) {
-  if (width > 0)
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((width + 255) / 256)), dim3(256), 0,
-                       st, partials, n_part, width, out);
-  return hipGetLastError();
+  return launch_reduce_partials(partials, n_part, width, out, width, out, st);
 }
 
 template <typename T, int D>

@@ -70,16 +70,6 @@ __global__ void __launch_bounds__(256) gate_bwd_kernel(
   }
 }
 
-__global__ void gate_reduce_kernel(const float* __restrict__ partials, int64_t np, int H,
-                                   float* __restrict__ dA_log, float* __restrict__ ddt) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= 2 * H) return;
-  float acc = 0.f;
-  for (int64_t p = 0; p < np; ++p) acc += partials[p * 2 * H + i];
-  if (i < H) dA_log[i] = acc;
-  else ddt[i - H] = acc;
-}
-
 hipError_t launch_gate_fwd(const gdn_shape& s, const void* a, const void* b, const float* A_log,
                            const float* dt_bias, float* g, float* beta, hipStream_t st) {
   const int64_t n = s.total_tokens * s.hv;
@@ -110,9 +100,9 @@ hipError_t launch_gate_bwd(const gdn_shape& s, const void* a, const void* b, con
                          (const float*)a, (const float*)b, A_log, dt_bias, dg, dbeta,
                          s.total_tokens, s.hv, (float*)da, (float*)db, partials);
   }
-  hipLaunchKernelGGL(gate_reduce_kernel, dim3((2 * s.hv + 255) / 256), dim3(256), 0, st, partials,
-                     np, s.hv, dA_log, ddt_bias);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce_partials(partials, np, 2 * (int64_t)s.hv, dA_log, s.hv, ddt_bias, st);
 }
 
 }  // namespace gdn

@@ -9,9 +9,12 @@
 
 namespace gdn {
 
-// out[i] = sum over p (in order) of partials[p * width + i]
+// out[i] = sum over p of partials[p * width + i], added in a fixed order
 hipError_t launch_reduce_partials(const float* partials, int64_t n_part, int64_t width, float* out,
                                   hipStream_t st);
+// as above, with columns i >= split written to out1[i - split]
+hipError_t launch_reduce_partials(const float* partials, int64_t n_part, int64_t width,
+                                  float* out0, int64_t split, float* out1, hipStream_t st);
 
 constexpr int CONV_TT = 64;      // tokens per conv run (one wave)
 constexpr int CONV_RUNS_PER_BLOCK = 4;
@@ -29,7 +32,7 @@ hipError_t launch_conv_bwd(const gdn_shape& s, const void* x, int64_t ldx, const
                            const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
                            void* dx, int64_t lddx, float* dw, float* partials, hipStream_t st);
 
-constexpr int GATE_TB = 256;     // tokens per gate-backward block
+constexpr int GATE_TB = 64;      // tokens per gate-backward block
 inline int64_t gate_partials(int64_t T) { return (T + GATE_TB - 1) / GATE_TB; }
 hipError_t launch_gate_fwd(const gdn_shape& s, const void* a, const void* b, const float* A_log,
                            const float* dt_bias, float* g, float* beta, hipStream_t st);
