@@ -202,7 +202,17 @@ gdn_status gdn_chunk_prepare(const gdn_shape* s, const void* q, const void* k, i
   GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
                              s ? chunk_fwd_ws_bytes(*s) : 0));
   if (!g || !beta) return GDN_ERR_INVALID_ARG;
-  return launched(launch_chunk_prepare(*s, q, k, ldq, ldk, g, beta, scale, cu, ws,
+  return launched(launch_chunk_prepare(*s, q, k, ldq, ldk, g, beta, scale, cu, ws, false,
+                                       (hipStream_t)stream));
+}
+
+gdn_status gdn_chunk_prepare_bwd(const gdn_shape* s, const void* q, const void* k, int64_t ldq,
+                                 int64_t ldk, const float* g, const float* beta, float scale,
+                                 const int32_t* cu, void* ws, size_t ws_bytes, void* stream) {
+  GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
+                             s ? chunk_bwd_ws_bytes(*s) : 0));
+  if (!g || !beta) return GDN_ERR_INVALID_ARG;
+  return launched(launch_chunk_prepare(*s, q, k, ldq, ldk, g, beta, scale, cu, ws, true,
                                        (hipStream_t)stream));
 }
 

@@ -5,7 +5,7 @@
 //   dDelta = P^T dO + diag(dec) K dS'^T
 //   dR     = M^T dDelta                        (= dv)
 //   dS     = Gam_L dS' + (scale Q)^T diag(Gam) dO - K^T diag(Gam) dR
-// is the sequential part (reverse over chunks, chunk_rev_kernel).  The rest
+// is the sequential part (reverse over chunks, chunk_rev.hip).  The rest
 // is chunk-parallel (chunk_grad_kernel):
 //   dM = dDelta R^T,  dTinv = strictly-lower(dM diag(beta)),
 //   dA = strictly-lower(-Tinv^T dTinv Tinv^T),  dP = lower(dO Delta^T)
@@ -21,210 +21,6 @@
 namespace gdn {
 
 // ---------------------------------------------------------------------------
-template <typename T, int D, int BV>
-struct RevSmem {
-  T K[CHUNK][D + Pad<T>::v];      // K rows (A operand of K dS'^T)
-  T Kt[D][CHUNK + Pad<T>::v];     // K^T
-  T Qt[D][CHUNK + Pad<T>::v];     // Q^T
-  T dOt[BV][CHUNK + Pad<T>::v];   // dO^T block
-  T dOgt[BV][CHUNK + Pad<T>::v];  // (scale diag(Gam) dO)^T
-  T dSb[BV][D + Pad<T>::v];       // dS' block (v-major)
-  T dDt[BV][CHUNK + Pad<T>::v];   // dDelta^T
-  T dRg[BV][CHUNK + Pad<T>::v];   // (diag(Gam) dR)^T
-  double gam[CHUNK];
-};
-
-// Reverse pass, one workgroup per (value-row block, value head, sequence),
-// chunks in reverse order; chunk c-1's inputs are prefetched into registers
-// while chunk c computes.  Wave w owns token rows [16w, 16w+16) of the
-// (token x value) products; the P^T and M^T rows it needs are gathered from
-// the preparation's workspace straight into registers.
-template <typename T, int D, int BV>
-__global__ void __launch_bounds__(256) chunk_rev_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
-    const double* __restrict__ gcum, const typename Compute<T>::type* __restrict__ Mw,
-    const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ dout,
-    const float* __restrict__ dS_final, float* __restrict__ dS0, T* __restrict__ dhst,
-    T* __restrict__ ddw, T* __restrict__ dvo, int64_t lddv, void* __restrict__ sink, int n_items) {
-  typedef typename Compute<T>::type CT;
-  typedef Mma<T> MM;
-  typedef FragKS<T, CT> FG;   // gathered rows of P^T, M^T
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  RevSmem<T, D, BV>& sm = *reinterpret_cast<RevSmem<T, D, BV>*>(smem_raw);
-  constexpr int LD = D + Pad<T>::v, LDC = CHUNK + Pad<T>::v;
-  constexpr int KS = MM::KS;
-  constexpr int NVT = BV / 16;
-  constexpr int NS = (D / 16) * NVT / 4;
-  constexpr int NKD = D / KS, NKC = CHUNK / KS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int item = xcd_item(blockIdx.x, n_items);
-  const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
-  const int kh = h / G;
-  const int v0 = vb * BV;
-  const int rsub = 4 * (lane >> 4), ccol = lane & 15, r16 = lane & 15;
-  const int trow = 16 * wave;
-  const int64_t HvD = (int64_t)Hv * D;
-
-  floatx4 dS[NS];  // dS^T tiles (d_k x BV)
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-    const int vv = v0 + 16 * vt + ccol;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kk = 16 * kt + rsub + e;
-      dS[i][e] = dS_final ? dS_final[(((int64_t)n * Hv + h) * D + vv) * D + kk] : 0.f;
-    }
-  }
-
-  struct Pref {
-    RowPrefetch<T, D, true> k, q;     // rows fastest across lanes: stored transposed
-    RowPrefetch<T, BV, true> dO;
-    typename FG::raw P[NKC], M[NKC];
-    double g;
-    int L;
-    int64_t t0;
-  };
-  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
-  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
-  auto prefetch = [&](Pref& F, int64_t c) {
-    F.t0 = seq_t0 + CHUNK * (c - c_begin);
-    const int64_t rem = seq_t1 - F.t0;
-    const int L = rem < CHUNK ? (int)rem : CHUNK;
-    const int64_t t0 = F.t0;
-    F.L = L;
-    F.k.load(k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-    F.q.load(q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
-    F.dO.load(dout + t0 * HvD + (int64_t)h * D + v0, HvD, L, tid);
-    const CT* Pc = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + acc_col<CT>(trow + r16);
-    const CT* Mc = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK + trow + r16;
-#pragma unroll
-    for (int s = 0; s < NKC; ++s) {
-      F.P[s] = FG::load(Pc, CHUNK, s * KS, lane);   // P^T row t = column t of P
-      F.M[s] = FG::load(Mc, CHUNK, s * KS, lane);
-    }
-    const int tg = tid & (CHUNK - 1);
-    F.g = gcum[(t0 + (tg < L ? tg : L - 1)) * Hv + h];
-  };
-
-  auto step = [&](int64_t c, Pref& cur, Pref& nxt) {
-    const int64_t t0 = cur.t0;
-    const int L = cur.L;
-    __syncthreads();
-    cur.k.store(&sm.K[0][0], LD, tid);
-    store_rows_transposed(cur.k, &sm.Kt[0][0], LDC, tid);
-    store_rows_transposed(cur.q, &sm.Qt[0][0], LDC, tid);
-    store_rows_transposed(cur.dO, &sm.dOt[0][0], LDC, tid);
-    sm.gam[tid & (CHUNK - 1)] = cur.g;  // the four waves write identical values
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-      const int vv = 16 * vt + ccol, kk = 16 * kt + rsub;
-      store4(&sm.dSb[vv][kk], dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
-      T* hp = dhst + (((int64_t)c * Hv + h) * D + kk) * D + v0 + vv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hp[(int64_t)e * D] = from_f<T>(dS[i][e]);
-    }
-    prefetch(nxt, c - 1 >= c_begin ? c - 1 : c);  // unconditional (re-reads at the start)
-    issue_fence();
-    __syncthreads();
-
-    // scaled copy of dO^T for the state gradient
-    for (int i = tid; i < CHUNK * BV; i += 256) {
-      const int vv = i / CHUNK, t = i % CHUNK;
-      sm.dOgt[vv][t] = from_f<T>(scale * dexp<T>(sm.gam[t]) * to_f(sm.dOt[vv][t]));
-    }
-    // Phase A: dDelta = P^T dO + diag(dec) K dS'^T
-    const double gl = sm.gam[CHUNK - 1];
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      floatx4 pt = zero4(), kd = zero4();
-#pragma unroll
-      for (int s = 0; s < NKC; ++s)
-        pt = MM::mma(FG::cvt(cur.P[s]), MM::kc(&sm.dOt[16 * vt + r16][0], s * KS, lane), pt);
-#pragma unroll
-      for (int s = 0; s < NKD; ++s)
-        kd = MM::mma(MM::kc(&sm.K[trow + r16][0], s * KS, lane),
-                     MM::kc(&sm.dSb[16 * vt + r16][0], s * KS, lane), kd);
-      const int vv = 16 * vt + ccol, tb = trow + rsub;
-      float dd[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dd[e] = pt[e] + dexp<T>(gl - sm.gam[tb + e]) * kd[e];
-      store4(&sm.dDt[vv][tb], dd[0], dd[1], dd[2], dd[3]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *row_or_sink(ddw + (t0 + tb + e) * HvD + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
-            from_f<T>(dd[e]);
-    }
-    __syncthreads();
-
-    // Phase B: dR = M^T dDelta  (this is dv)
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      floatx4 dr = zero4();
-#pragma unroll
-      for (int s = 0; s < NKC; ++s)
-        dr = MM::mma(FG::cvt(cur.M[s]), MM::kc(&sm.dDt[16 * vt + r16][0], s * KS, lane), dr);
-      const int vv = 16 * vt + ccol, tb = trow + rsub;
-      float rg[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rg[e] = dexp<T>(sm.gam[tb + e]) * dr[e];
-        *row_or_sink(dvo + (t0 + tb + e) * lddv + (int64_t)h * D + v0 + vv, tb + e < L, sink, tid) =
-            from_f<T>(dr[e]);
-      }
-      store4(&sm.dRg[vv][tb], rg[0], rg[1], rg[2], rg[3]);
-    }
-    __syncthreads();
-
-    // Phase C: dS^T = Gam_L dS'^T + Q^T (scale diag(Gam) dO) - K^T (diag(Gam) dR)
-    const float GL = dexp<T>(gl);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-      floatx4 qd = zero4(), kr = zero4();
-#pragma unroll
-      for (int s = 0; s < NKC; ++s) {
-        qd = MM::mma(MM::kc(&sm.Qt[16 * kt + r16][0], s * KS, lane),
-                     MM::kc(&sm.dOgt[16 * vt + r16][0], s * KS, lane), qd);
-        kr = MM::mma(MM::kc(&sm.Kt[16 * kt + r16][0], s * KS, lane),
-                     MM::kc(&sm.dRg[16 * vt + r16][0], s * KS, lane), kr);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dS[i][e] = GL * dS[i][e] + qd[e] - kr[e];
-    }
-  };
-
-  Pref A, B;
-  if (c_begin < c_end) prefetch(A, c_end - 1);
-  for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
-    step(c, A, B);
-    if (c - 1 >= c_begin) step(c - 1, B, A);
-  }
-  // Never taken: keeps both prefetch buffers live on the loop-exit path.
-  if (c_end < 0) {
-    T* sk = reinterpret_cast<T*>(sink);
-    *reinterpret_cast<Raw8<T>*>(sk) = A.k.r[0];
-    *reinterpret_cast<Raw8<T>*>(sk + 64) = B.k.r[0];
-  }
-  if (dS0) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int id = wave * NS + i, kt = id / NVT, vt = id % NVT;
-      const int vv = v0 + 16 * vt + ccol, kk = 16 * kt + rsub;
-      store4(dS0 + (((int64_t)n * Hv + h) * D + vv) * D + kk, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Chunk-parallel gradients: one workgroup per (chunk, key head), looping over
-// the key head's value heads in ascending order so dq and dk accumulate in
-// registers without atomics.  Per value head: Tinv is recomputed in fp32
-// (blocked inverse), then the 64 x 64 gradient matrices, then the
-// (token x key) products.  The global tiles of the next phase are loaded
-// into registers one phase ahead.
 template <typename T, int D>
 struct GradSmem {
   T Kt[D][CHUNK + Pad<T>::v];      // K^T (k-major)
@@ -616,34 +412,6 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
 }
 
 // ---------------------------------------------------------------------------
-constexpr int REV_BV = 32;
-
-hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
-                                    int64_t ldk, float scale, const int32_t* cu, const void* dout,
-                                    const float* dS_final, void* dv, int64_t lddv, float* dS0,
-                                    void* wsv, hipStream_t st) {
-  char* ws = (char*)wsv;
-  const ChunkLayout Ly = chunk_layout(s);
-  return dispatch_chunk(s, [&](auto c) {
-    using T = typename decltype(c)::type;
-    constexpr int D = decltype(c)::d;
-    constexpr int BV = REV_BV;
-    static_assert(sizeof(RevSmem<T, D, BV>) <= 160 * 1024, "reverse kernel LDS budget");
-    const size_t shm = sizeof(RevSmem<T, D, BV>);
-    auto kern = chunk_rev_kernel<T, D, BV>;
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    const int n_items = (D / BV) * s.hv * s.n_seq;
-    hipLaunchKernelGGL(kern, dim3(n_items), dim3(256), shm, st, (const T*)q, (const T*)k, ldq,
-                       ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
-                       (const double*)(ws + Ly.gcum),
-                       (const typename Compute<T>::type*)(ws + Ly.mw),
-                       (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)dout, dS_final,
-                       dS0, (T*)(ws + Ly.dh), (T*)(ws + Ly.ddw), (T*)dv, lddv,
-                       (void*)(ws + Ly.sink), n_items);
-    return hipGetLastError();
-  });
-}
-
 hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
                                   int64_t ldk, const float* beta, float scale, const int32_t* cu,
                                   const void* dout, const void* dv, int64_t lddv, void* dq,
@@ -676,7 +444,7 @@ hipError_t launch_chunk_bwd(const gdn_shape& s, const void* q, const void* k, co
                             const void* dout, const float* dS_final, void* dq, void* dk, void* dv,
                             int64_t lddq, int64_t lddk, int64_t lddv, float* dg, float* dbeta,
                             float* dS0, void* ws, hipStream_t st) {
-  hipError_t e = launch_chunk_prepare(s, q, k, ldq, ldk, g, beta, scale, cu, ws, st);
+  hipError_t e = launch_chunk_prepare(s, q, k, ldq, ldk, g, beta, scale, cu, ws, true, st);
   if (e == hipSuccess) e = launch_chunk_bwd_states(s, q, k, v, ldq, ldk, ldv, scale, S0, cu, ws, st);
   if (e == hipSuccess)
     e = launch_chunk_bwd_reverse(s, q, k, ldq, ldk, scale, cu, dout, dS_final, dv, lddv, dS0, ws, st);

@@ -59,6 +59,8 @@ struct ChunkLayout {
   size_t ktw;         // CT [nt_max][hk][dk][64]: K^T of each chunk
   size_t q16w, k16w;  // CT [nt_max][hk][64][dk]: Q and K rows of each chunk (zero past its end)
   size_t gw, dw;      // fp32 [nt_max][hv][64]: Gam_t and dec_t (clamped to the chunk length)
+  size_t kb, ktb, qtb; // T [nt_max][hk]: K rows [64][dk], K^T and Q^T [dk][64] (backward)
+  size_t ptb, mtb;    // T [nt_max][hv][64][64]: P^T, M^T (backward)
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
   size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
   size_t sink;        // SINK_ELEMS scratch floats: target of stores for padding rows
@@ -95,6 +97,11 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.gw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.dw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.total_fwd = off;
+  L.kb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * CHUNK * s.dk);
+  L.ktb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
+  L.qtb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
+  L.ptb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
+  L.mtb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.dh = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.rw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);

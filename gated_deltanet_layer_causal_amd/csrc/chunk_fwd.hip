@@ -59,7 +59,7 @@ struct PrepSmem {
                 "W tile fits in the A storage");
 };
 
-template <typename T, int D>
+template <typename T, int D, bool BWD>
 __global__ void __launch_bounds__(256) chunk_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -67,7 +67,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     double* __restrict__ gcum, typename Compute<T>::type* __restrict__ Mw,
     typename Compute<T>::type* __restrict__ Pw, typename Compute<T>::type* __restrict__ Ww,
     typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
-    typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw) {
+    typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw,
+    T* __restrict__ Kb, T* __restrict__ Ktb, T* __restrict__ Qtb, T* __restrict__ Ptb,
+    T* __restrict__ Mtb) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -108,6 +110,19 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       const int dst = r * D + acc_col<CT>(c4);
       *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&sm.u.Q[r][c4]);
       *reinterpret_cast<v4*>(K16w + base + dst) = *reinterpret_cast<const v4*>(&sm.K[r][c4]);
+      if constexpr (BWD) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Kb[base + dst + u] = from_f<T>(to_f(sm.K[r][c4 + u]));
+      }
+    }
+    if constexpr (BWD) {
+      // Q^T in the storage type, columns (tokens) in accumulator order
+      T* qo = Qtb + base;
+      for (int i = tid; i < D * (CHUNK / 4); i += 256) {
+        const int kr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qo[kr * CHUNK + acc_col<T>(t4) + u] = from_f<T>(to_f(sm.u.Q[t4 + u][kr]));
+      }
     }
   }
   __syncthreads();  // Q is dead: its storage takes K^T
@@ -126,6 +141,11 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       typedef CT v4 __attribute__((ext_vector_type(4)));
       *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
           *reinterpret_cast<const v4*>(&sm.u.Kt[kr][c4]);
+      if constexpr (BWD) {
+        T* kb = Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kb[u] = from_f<T>(to_f(sm.u.Kt[kr][c4 + u]));
+      }
     }
   }
 
@@ -156,7 +176,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
         const int t = rbase + e;
         const float dec = dexp<T>(sm.gam[t] - sm.gam[s <= t ? s : t]);  // masked before exp
         sm.A[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
-        Pout[t * CHUNK + acc_col<CT>(s)] = from_f<CT>((s <= t) ? dec * scale * qk[j][e] : 0.f);
+        const float pv = (s <= t) ? dec * scale * qk[j][e] : 0.f;
+        Pout[t * CHUNK + acc_col<CT>(s)] = from_f<CT>(pv);
+        if constexpr (BWD) Ptb[((int64_t)c * Hv + h) * CHUNK * CHUNK + s * CHUNK + acc_col<T>(t)] = from_f<T>(pv);
       }
     }
     __syncthreads();
@@ -168,6 +190,16 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) v.v[u] = sm.Ti[t][s8 + u] * sm.bet[s8 + u];
       store8(Mout + t * CHUNK + s8, v);
+    }
+    if constexpr (BWD) {
+      // M^T in the storage type, columns (tokens t) in accumulator order
+      T* mo = Mtb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+      for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
+        const int sr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
+        const float b = sm.bet[sr];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mo[sr * CHUNK + acc_col<T>(t4) + u] = from_f<T>(sm.Ti[t4 + u][sr] * b);
+      }
     }
     // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead
     // A storage (columns in accumulator order), then all rows go out in
@@ -209,7 +241,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool BWD>
 static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
                                 int64_t ldk, const float* g, const float* beta, float scale,
                                 const int32_t* cu, const ChunkLayout& Ly, char* ws,
@@ -218,9 +250,9 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
   hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, st, cu, s.n_seq, seq_off);
   if (Ly.nt_max > 0 && s.total_tokens > 0) {
     const size_t shm = sizeof(PrepSmem<T, D>);
-    hipFuncSetAttribute((const void*)chunk_prep_kernel<T, D>,
+    hipFuncSetAttribute((const void*)chunk_prep_kernel<T, D, BWD>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL((chunk_prep_kernel<T, D>), dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm,
+    hipLaunchKernelGGL((chunk_prep_kernel<T, D, BWD>), dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm,
                        st, (const T*)q, (const T*)k, ldq, ldk, g, beta, cu, seq_off, s.n_seq, s.hv,
                        s.hv / s.hk, scale, (double*)(ws + Ly.gcum),
                        (typename Compute<T>::type*)(ws + Ly.mw),
@@ -229,7 +261,9 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        (typename Compute<T>::type*)(ws + Ly.ktw),
                        (typename Compute<T>::type*)(ws + Ly.q16w),
                        (typename Compute<T>::type*)(ws + Ly.k16w), (float*)(ws + Ly.gw),
-                       (float*)(ws + Ly.dw));
+                       (float*)(ws + Ly.dw), BWD ? (T*)(ws + Ly.kb) : nullptr,
+                       BWD ? (T*)(ws + Ly.ktb) : nullptr, BWD ? (T*)(ws + Ly.qtb) : nullptr,
+                       BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (T*)(ws + Ly.mtb) : nullptr);
   }
   return hipGetLastError();
 }
@@ -239,11 +273,13 @@ size_t chunk_bwd_ws_bytes(const gdn_shape& s) { return chunk_layout(s).total_bwd
 
 hipError_t launch_chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
                                 int64_t ldk, const float* g, const float* beta, float scale,
-                                const int32_t* cu, void* ws, hipStream_t st) {
+                                const int32_t* cu, void* ws, bool bwd, hipStream_t st) {
   const ChunkLayout Ly = chunk_layout(s);
   return dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
-    return chunk_prepare<T, decltype(c)::d>(s, q, k, ldq, ldk, g, beta, scale, cu, Ly, (char*)ws, st);
+    constexpr int D = decltype(c)::d;
+    return bwd ? chunk_prepare<T, D, true>(s, q, k, ldq, ldk, g, beta, scale, cu, Ly, (char*)ws, st)
+               : chunk_prepare<T, D, false>(s, q, k, ldq, ldk, g, beta, scale, cu, Ly, (char*)ws, st);
   });
 }
 
@@ -251,7 +287,7 @@ hipError_t launch_chunk_fwd(const gdn_shape& s, const void* q, const void* k, co
                             int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
                             const float* beta, float scale, const float* S0, float* S_final,
                             const int32_t* cu, void* o, void* ws, hipStream_t st) {
-  hipError_t e = launch_chunk_prepare(s, q, k, ldq, ldk, g, beta, scale, cu, ws, st);
+  hipError_t e = launch_chunk_prepare(s, q, k, ldq, ldk, g, beta, scale, cu, ws, false, st);
   if (e != hipSuccess) return e;
   return launch_chunk_fwd_states(s, q, k, v, ldq, ldk, ldv, scale, S0, S_final, cu, o, ws, st);
 }

@@ -1,0 +1,290 @@
+// Chunked gated delta rule, backward: the reverse pass over the chunks of
+// each sequence.  Per chunk, given dO and the gradient dS' of the state
+// leaving it:
+//   dDelta = P^T dO + diag(dec) K dS'^T
+//   dR     = M^T dDelta                                  (= dv)
+//   dS     = Gam_L dS' + (scale Q)^T diag(Gam) dO - K^T diag(Gam) dR
+// It stores dS' per chunk (for the chunk-parallel gradients), dDelta and dv,
+// and dS0 at the sequence start.
+//
+// Same structure as the state pass (chunk_state.hip): one workgroup per
+// (sequence, value head, block of 16 * NW value rows); wave w keeps its
+// d_k x 16 slice of dS'^T in MFMA accumulators and feeds it straight back as
+// B operand; the chunk operands (K rows, K^T, Q^T, P^T, M^T from the
+// backward preparation, columns in accumulator order; the dO rows of the
+// block; Gam, dec) stream into one of two LDS buffers by direct copies while
+// the other buffer computes.  Operands are in the storage type (bf16 keeps
+// the range of dS).
+#include "chunk_stream.h"
+
+namespace gdn {
+
+template <typename T, int D, int NW> struct RevBuf {
+  static constexpr int BV = 16 * NW;
+  typedef Tile<T, CHUNK, D> TK;        // K rows
+  typedef Tile<T, D, CHUNK> TKt;       // K^T, Q^T
+  typedef Tile<T, CHUNK, CHUNK> TM;    // P^T, M^T
+  typedef Tile<T, CHUNK, BV, 3> TO;    // dO rows of this block
+  T K[TK::PIECES * TK::EPP];
+  T Kt[TKt::PIECES * TKt::EPP];
+  T Qt[TKt::PIECES * TKt::EPP];
+  T Pt[TM::PIECES * TM::EPP];
+  T Mt[TM::PIECES * TM::EPP];
+  T dO[TO::PIECES * TO::EPP];
+  float G[CHUNK], Dc[CHUNK];           // Gam_t, dec_t
+} __attribute__((aligned(16)));
+
+template <typename T, int D, int NW>
+__global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
+    const T* __restrict__ Kb, const T* __restrict__ Ktb, const T* __restrict__ Qtb,
+    const T* __restrict__ Ptb, const T* __restrict__ Mtb, const float* __restrict__ Gw,
+    const float* __restrict__ Dw, const T* __restrict__ dout, const float* __restrict__ dS_final,
+    float* __restrict__ dS0, T* __restrict__ dhst, T* __restrict__ ddw, T* __restrict__ dvo,
+    int64_t lddv, int n_items) {
+  typedef Mma<T> MM;
+  typedef AccOrder<T> AO;
+  typedef typename MM::frag frag;
+  typedef RevBuf<T, D, NW> RB;
+  typedef typename RB::TK TK;
+  typedef typename RB::TKt TKt;
+  typedef typename RB::TM TM;
+  typedef typename RB::TO TO;
+  constexpr int BV = RB::BV;
+  constexpr int KS = MM::KS;
+  constexpr int NSD = D / KS;       // MFMA steps over d_k
+  constexpr int NSC = CHUNK / KS;   // MFMA steps over the chunk
+  constexpr int NKT = D / 16;       // gradient tiles per wave
+  static_assert(TK::PIECES % (64 * NW) == 0 && TKt::PIECES % (64 * NW) == 0 &&
+                TM::PIECES % (64 * NW) == 0 && TO::PIECES % (64 * NW) == 0,
+                "direct copies cover whole waves");
+  __shared__ RB bufA, bufB;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_ = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave_;
+  const int item = xcd_item(blockIdx.x, n_items);
+  const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
+  const int kh = h / G, Hk = Hv / G;
+  const int v0 = vb * BV;
+  const int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
+  const int vcol = 16 * wave + c16;
+  const int64_t HvD = (int64_t)Hv * D;
+
+  floatx4 dS[NKT];   // dS'^T tiles: rows k = 16 kt + g4 + i, column v0 + vcol
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dS[kt][i] = dS_final ? dS_final[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] : 0.f;
+
+  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
+  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
+
+  CopyLanes cl;
+  cl.init(lane, wave, NW);
+  const uint32_t so = (uint32_t)(((int64_t)g4 * HvD + vcol) * sizeof(T));   // rows of ddw
+  const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
+  const uint32_t sv = (uint32_t)(((int64_t)g4 * lddv + vcol) * sizeof(T));  // rows of dv
+  const uint32_t rowv = (uint32_t)(lddv * sizeof(T));
+  // LDS read offsets (as in the state pass)
+  int rw[NSD], rk[NSC];
+#pragma unroll
+  for (int p = 0; p < NSD; ++p)
+    rw[p] = KS == 4 ? TK::at(c16, 16 * (p >> 2) + g4 + (p & 3)) : TK::at(c16, 32 * p + 8 * g);
+#pragma unroll
+  for (int p = 0; p < NSC; ++p)
+    rk[p] = KS == 4 ? TKt::at(c16, 16 * (p >> 2) + g4 + (p & 3)) : TKt::at(c16, 32 * p + 8 * g);
+
+  auto fetch = [&](RB& B, int64_t c) __attribute__((always_inline)) {
+    int wave = wave_;
+    asm volatile("" : "+s"(wave));
+    const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - t0;
+    const int Lc = rem < CHUNK ? (int)rem : CHUNK;
+    const int64_t ch = (int64_t)c * Hv + h, ck = (int64_t)c * Hk + kh;
+    copy_tile<TK, NW>(B.K, Kb + ck * CHUNK * D, cl, wave);
+    copy_tile<TKt, NW>(B.Kt, Ktb + ck * D * CHUNK, cl, wave);
+    copy_tile<TKt, NW>(B.Qt, Qtb + ck * D * CHUNK, cl, wave);
+    copy_tile<TM, NW>(B.Pt, Ptb + ch * CHUNK * CHUNK, cl, wave);
+    copy_tile<TM, NW>(B.Mt, Mtb + ch * CHUNK * CHUNK, cl, wave);
+    {
+      // dO rows past the sequence end re-read its last row (their products
+      // meet zero rows and columns of P^T, Q^T)
+      const auto rs = buffer_of(dout + t0 * HvD + (int64_t)h * D + v0, (uint32_t)Lc * rowb);
+#pragma unroll
+      for (int j = 0; j < TO::PIECES / (64 * NW); ++j) {
+        const int s = (j * NW + wave) * 64 + lane, r = s / TO::RP;
+        const uint32_t off = (uint32_t)(r < Lc ? r : Lc - 1) * rowb +
+                             (uint32_t)((s % TO::RP) ^ TO::swz(r)) * 16u;
+        copy_to_lds(rs, B.dO + (j * NW + wave) * 64 * TO::EPP, off, 0);
+      }
+    }
+    if (wave == 0 && lane < 16) {
+      copy_to_lds(buffer_of(Gw + ch * CHUNK, CHUNK * 4), B.G, 16u * lane, 0);
+      copy_to_lds(buffer_of(Dw + ch * CHUNK, CHUNK * 4), B.Dc, 16u * lane, 0);
+    }
+  };
+
+  auto arow = [&](const T* base, int o, int tile_elems) __attribute__((always_inline)) -> frag {
+    if constexpr (KS == 4) return base[tile_elems + o];
+    else return *reinterpret_cast<const frag*>(base + tile_elems + o);
+  };
+
+  auto compute = [&](const RB& B, int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - t0;
+    const int L = rem < CHUNK ? (int)rem : CHUNK;
+
+    // dS'^T as B operands; dS' to the workspace ([d_k][d_v] per chunk, head)
+    frag sb[NSD];
+#pragma unroll
+    for (int p = 0; p < NSD; ++p) sb[p] = AO::from_acc(dS, p);
+    {
+      const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
+      const uint32_t hb = (uint32_t)((g4 * D + vcol) * sizeof(T));
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store_elem<T>(rs, hb + (uint32_t)((16 * kt + i) * D * sizeof(T)), dS[kt][i]);
+    }
+
+    // dO as B operands over the chunk index, plain and scaled by scale Gam_t
+    frag ob[NSC], gob[NSC];
+#pragma unroll
+    for (int p = 0; p < NSC; ++p) {
+      if constexpr (KS == 4) {
+        const int t = 16 * (p >> 2) + g4 + (p & 3);
+        const float x = to_f(B.dO[TO::at(t, vcol)]);
+        ob[p] = x;
+        gob[p] = scale * B.G[t] * x;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = 16 * (2 * p + j / 4) + g4 + (j & 3);
+          const float x = to_f(B.dO[TO::at(t, vcol)]);
+          ob[p][j] = from_f<T>(x);
+          gob[p][j] = from_f<T>(scale * B.G[t] * x);
+        }
+      }
+    }
+
+    // dDelta = P^T dO + diag(dec) K dS'^T
+    floatx4 dd[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      floatx4 kd = zero4(), pt = zero4();
+#pragma unroll
+      for (int p = 0; p < NSD; ++p) kd = MM::mma(arow(B.K, rw[p], 16 * tt * D), sb[p], kd);
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) pt = MM::mma(arow(B.Pt, rk[p], 16 * tt * CHUNK), ob[p], pt);
+      const float4 dc = *reinterpret_cast<const float4*>(&B.Dc[16 * tt + g4]);
+      dd[tt][0] = pt[0] + dc.x * kd[0];
+      dd[tt][1] = pt[1] + dc.y * kd[1];
+      dd[tt][2] = pt[2] + dc.z * kd[2];
+      dd[tt][3] = pt[3] + dc.w * kd[3];
+    }
+    {
+      // rows past the sequence end fall outside the buffer: dropped
+      const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_elem<T>(rs, so + (uint32_t)(16 * tt + i) * rowb, dd[tt][i]);
+    }
+
+    // dR = M^T dDelta (= dv); then -diag(Gam) dR as B operands
+    floatx4 gr[4];
+    {
+      frag df[NSC];
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) df[p] = AO::from_acc(dd, p);
+      const auto rs = buffer_of(dvo + t0 * lddv + (int64_t)h * D + v0, (uint32_t)L * rowv);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        floatx4 dr = zero4();
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) dr = MM::mma(arow(B.Mt, rk[p], 16 * tt * CHUNK), df[p], dr);
+        const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
+        gr[tt][0] = -gm.x * dr[0];
+        gr[tt][1] = -gm.y * dr[1];
+        gr[tt][2] = -gm.z * dr[2];
+        gr[tt][3] = -gm.w * dr[3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_elem<T>(rs, sv + (uint32_t)(16 * tt + i) * rowv, dr[i]);
+      }
+    }
+
+    // dS^T = Gam_L dS'^T + Q^T (scale diag(Gam) dO) - K^T (diag(Gam) dR)
+    {
+      frag gf[NSC];
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) gf[p] = AO::from_acc(gr, p);
+      const float GL = B.G[CHUNK - 1];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[kt][i] *= GL;
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) {
+          dS[kt] = MM::mma(arow(B.Qt, rk[p], 16 * kt * CHUNK), gob[p], dS[kt]);
+          dS[kt] = MM::mma(arow(B.Kt, rk[p], 16 * kt * CHUNK), gf[p], dS[kt]);
+        }
+      }
+    }
+  };
+
+  if (c_begin < c_end) fetch(bufA, c_end - 1);
+  __syncthreads();
+  for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
+    fetch(bufB, c - 1 >= c_begin ? c - 1 : c);   // a repeat of chunk c at the start
+    compute(bufA, c);
+    __syncthreads();   // waits for this wave's copies; then every wave's are visible
+    if (c - 1 >= c_begin) {
+      fetch(bufA, c - 2 >= c_begin ? c - 2 : c - 1);
+      compute(bufB, c - 1);
+      __syncthreads();
+    }
+  }
+
+  if (dS0) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dS0[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] = dS[kt][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+constexpr int REV_NW = 2;
+
+template <typename T, int D>
+static hipError_t chunk_rev(const gdn_shape& s, float scale, const int32_t* cu, const void* dout,
+                            const float* dS_final, void* dv, int64_t lddv, float* dS0,
+                            const ChunkLayout& Ly, char* ws, hipStream_t st) {
+  constexpr int NW = REV_NW, BV = 16 * NW;
+  const int n_items = (D / BV) * s.hv * s.n_seq;
+  hipLaunchKernelGGL((chunk_rev_kernel<T, D, NW>), dim3(n_items), dim3(64 * NW), 0, st, cu,
+                     (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
+                     (const T*)(ws + Ly.kb), (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb),
+                     (const T*)(ws + Ly.ptb), (const T*)(ws + Ly.mtb), (const float*)(ws + Ly.gw),
+                     (const float*)(ws + Ly.dw), (const T*)dout, dS_final, dS0, (T*)(ws + Ly.dh),
+                     (T*)(ws + Ly.ddw), (T*)dv, lddv, n_items);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                    int64_t ldk, float scale, const int32_t* cu, const void* dout,
+                                    const float* dS_final, void* dv, int64_t lddv, float* dS0,
+                                    void* ws, hipStream_t st) {
+  const ChunkLayout Ly = chunk_layout(s);
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    return chunk_rev<T, decltype(c)::d>(s, scale, cu, dout, dS_final, dv, lddv, dS0, Ly, (char*)ws,
+                                        st);
+  });
+}
+
+}  // namespace gdn

@@ -27,70 +27,9 @@
 // (Tile).  Every address that varies by lane is computed once: copies go
 // through buffer resources (uniform base, per-lane offset) and LDS reads use
 // per-lane offsets plus constants.
-#include "chunk_common.h"
+#include "chunk_stream.h"
 
 namespace gdn {
-
-// Reduction order of an MFMA step whose B operand comes from accumulator
-// tiles x[0..] (rows = reduction index).
-//  16-bit operands (32 per step): step p uses tiles 2p and 2p + 1; lane l's
-//    slot j holds reduction index 16 (2p + j / 4) + 4 (l / 16) + j % 4.
-//  fp32 operands (4 per step): step p holds index 16 (p / 4) + 4 (l / 16) + p % 4.
-template <typename CT> struct AccOrder {
-  typedef typename Mma<CT>::frag frag;
-  __device__ __forceinline__ static frag from_acc(const floatx4* x, int p) {
-    frag f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[j] = (CT)x[2 * p][j];
-      f[4 + j] = (CT)x[2 * p + 1][j];
-    }
-    return f;
-  }
-};
-template <> struct AccOrder<float> {
-  typedef float frag;
-  __device__ __forceinline__ static frag from_acc(const floatx4* x, int p) { return x[p >> 2][p & 3]; }
-};
-
-// Piece permutation of LDS row r (RP 16-byte pieces per row): reads by 16
-// consecutive rows then touch RP (RP <= 8) or 16 different piece slots.
-// With RP <= 8 it depends on r mod RP only, so a direct copy (64 pieces per
-// wave = 64 / RP whole rows) needs the same per-lane source offset in every
-// copy instruction.
-template <int RP> __device__ __forceinline__ int row_swz(int r) {
-  if constexpr (RP == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return r & (RP - 1);
-}
-
-// An LDS tile of ROWS rows of COLS elements of type E, unpadded, with the
-// 16-byte pieces of row r permuted: piece q lives at slot q ^ swz(r), where
-// swz = row_swz (SWZ_SHIFT = 0) or (r >> SWZ_SHIFT) mod RP.
-template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
-  static constexpr int EPP = 16 / sizeof(E);         // elements per piece
-  static constexpr int RP = COLS / EPP;              // pieces per row
-  static constexpr int PIECES = ROWS * RP;
-  static_assert(RP == 4 || RP == 8 || RP == 16, "pieces per row");
-  __device__ __forceinline__ static int swz(int r) {
-    if constexpr (SWZ_SHIFT == 0) return row_swz<RP>(r);
-    else return (r >> SWZ_SHIFT) & (RP - 1);
-  }
-  // element offset of (r, col)
-  __device__ __forceinline__ static int at(int r, int col) {
-    return (r * RP + ((col / EPP) ^ swz(r))) * EPP + col % EPP;
-  }
-  // byte offset, within the source tile, of the piece that LDS slot s holds
-  __device__ __forceinline__ static uint32_t source_bytes(int s) {
-    const int r = s / RP;
-    return (uint32_t)(r * RP + ((s % RP) ^ swz(r))) * 16u;
-  }
-  // Copy J (64 slots from 64 J) reads source_bytes(64 J + lane) =
-  // 1024 J + lane_bytes(J, lane); lane_bytes depends on J only through
-  // J mod 4 for RP = 16 and not at all for RP <= 8 (row_swz tiles).
-  __device__ __forceinline__ static uint32_t lane_bytes(int J, int lane) {
-    return source_bytes(64 * (RP == 16 ? (J & 3) : 0) + lane) - 1024u * (RP == 16 ? (J & 3) : 0);
-  }
-};
 
 template <typename T, int D, int NW, int MODE> struct StateBuf {
   typedef typename Compute<T>::type CT;
@@ -107,27 +46,6 @@ template <typename T, int D, int NW, int MODE> struct StateBuf {
   T V[TV::PIECES * TV::EPP];
   float G[CHUNK], Dc[CHUNK];            // Gam_t, dec_t
 } __attribute__((aligned(16)));
-
-// Direct copy of one 16-byte piece per lane from a buffer into LDS: the
-// wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
-// Buffer accesses are range-checked against the descriptor's size on the
-// per-lane offset (loads past it read zero, stores past it are dropped).
-__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
-                                            uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-template <typename T>
-__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, uint32_t voff, float x) {
-  if constexpr (sizeof(T) == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<T>(x)), rs, voff, 0, 0);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), rs, voff, 0, 0);
-  }
-}
 
 template <typename T, int D, int NW, int MODE>
 __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
@@ -181,13 +99,8 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
   const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
 
   // ---- per-lane offsets, the same for every chunk
-  // copies: copy J = j NW + wave of a tile reads 1024 J + lane_bytes, which
-  // depends only on the tile's pieces per row (and on J mod 4 for 16)
-  uint32_t c16p[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) c16p[a] = Tile<float, 64, 64>::lane_bytes(a, lane);
-  const uint32_t c8p = Tile<float, 64, 32>::lane_bytes(0, lane);
-  const uint32_t c4p = Tile<float, 64, 16>::lane_bytes(0, lane);
+  CopyLanes cl;
+  cl.init(lane, wave, NW);
   // stores: byte offset of this lane's first row (g4) and column
   const uint32_t so = (uint32_t)(((int64_t)g4 * HvD + vcol) * sizeof(T));
   const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
@@ -217,22 +130,11 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     const int64_t rem = seq_t1 - t0;
     const int Lc = rem < CHUNK ? (int)rem : CHUNK;
     const int64_t ch = (int64_t)c * Hv + h, ck_ = (int64_t)c * Hk + kh;
-    // the per-copy part (1024 J) goes into the base address, so that the
-    // range check sees only the per-lane offset
-    auto tile = [&](auto tt, CT* dst, const CT* src) __attribute__((always_inline)) {
-      typedef decltype(tt) TT;
-#pragma unroll
-      for (int j = 0; j < TT::PIECES / THREADS; ++j) {
-        const int J = j * NW + wave;
-        const auto rs = buffer_of(reinterpret_cast<const char*>(src) + 1024 * J, 1024);
-        copy_to_lds(rs, dst + J * 64 * TT::EPP, TT::RP == 16 ? c16p[J & 3] : TT::RP == 8 ? c8p : c4p, 0);
-      }
-    };
-    tile(TW{}, B.W, Ww + ch * CHUNK * D);
-    tile(TW{}, B.X, Xw + ck_ * CHUNK * D);
-    tile(TKt{}, B.Kt, Ktw + ck_ * D * CHUNK);
-    tile(TM{}, B.M, Mw + ch * CHUNK * CHUNK);
-    if constexpr (MODE == 0) tile(TM{}, B.P, Pw + ch * CHUNK * CHUNK);
+    copy_tile<TW, NW>(B.W, Ww + ch * CHUNK * D, cl, wave);
+    copy_tile<TW, NW>(B.X, Xw + ck_ * CHUNK * D, cl, wave);
+    copy_tile<TKt, NW>(B.Kt, Ktw + ck_ * D * CHUNK, cl, wave);
+    copy_tile<TM, NW>(B.M, Mw + ch * CHUNK * CHUNK, cl, wave);
+    if constexpr (MODE == 0) copy_tile<TM, NW>(B.P, Pw + ch * CHUNK * CHUNK, cl, wave);
     {
       const uint32_t ldb = (uint32_t)(ldv * sizeof(T));
       const auto rs = buffer_of(v + t0 * ldv + (int64_t)h * D + v0, (uint32_t)Lc * ldb);

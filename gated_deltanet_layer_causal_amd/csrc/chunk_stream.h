@@ -1,0 +1,127 @@
+// Pieces shared by the sequential chunk kernels (state pass and reverse
+// pass): MFMA operands taken straight from accumulator tiles, LDS tiles that
+// are filled by direct global -> LDS copies, and range-checked buffer stores.
+#pragma once
+#include "chunk_common.h"
+
+namespace gdn {
+
+// Reduction order of an MFMA step whose B operand comes from accumulator
+// tiles x[0..] (rows = reduction index).
+//  16-bit operands (32 per step): step p uses tiles 2p and 2p + 1; lane l's
+//    slot j holds reduction index 16 (2p + j / 4) + 4 (l / 16) + j % 4.
+//  fp32 operands (4 per step): step p holds index 16 (p / 4) + 4 (l / 16) + p % 4.
+template <typename CT> struct AccOrder {
+  typedef typename Mma<CT>::frag frag;
+  __device__ __forceinline__ static frag from_acc(const floatx4* x, int p) {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[j] = (CT)x[2 * p][j];
+      f[4 + j] = (CT)x[2 * p + 1][j];
+    }
+    return f;
+  }
+};
+template <> struct AccOrder<float> {
+  typedef float frag;
+  __device__ __forceinline__ static frag from_acc(const floatx4* x, int p) { return x[p >> 2][p & 3]; }
+};
+
+// Piece permutation of LDS row r (RP 16-byte pieces per row): reads by 16
+// consecutive rows then touch RP (RP <= 8) or 16 different piece slots.
+// With RP <= 8 it depends on r mod RP only, so a direct copy (64 pieces per
+// wave = 64 / RP whole rows) needs the same per-lane source offset in every
+// copy instruction.
+template <int RP> __device__ __forceinline__ int row_swz(int r) {
+  if constexpr (RP == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return r & (RP - 1);
+}
+
+// An LDS tile of ROWS rows of COLS elements of type E, unpadded, with the
+// 16-byte pieces of row r permuted: piece q lives at slot q ^ swz(r), where
+// swz = row_swz (SWZ_SHIFT = 0) or (r >> SWZ_SHIFT) mod RP.
+template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
+  static constexpr int EPP = 16 / sizeof(E);         // elements per piece
+  static constexpr int RP = COLS / EPP;              // pieces per row
+  static constexpr int PIECES = ROWS * RP;
+  static_assert(RP == 4 || RP == 8 || RP == 16, "pieces per row");
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (SWZ_SHIFT == 0) return row_swz<RP>(r);
+    else return (r >> SWZ_SHIFT) & (RP - 1);
+  }
+  // element offset of (r, col)
+  __device__ __forceinline__ static int at(int r, int col) {
+    return (r * RP + ((col / EPP) ^ swz(r))) * EPP + col % EPP;
+  }
+  // byte offset, within the source tile, of the piece that LDS slot s holds
+  __device__ __forceinline__ static uint32_t source_bytes(int s) {
+    const int r = s / RP;
+    return (uint32_t)(r * RP + ((s % RP) ^ swz(r))) * 16u;
+  }
+  // Copy J (64 slots from 64 J) reads source_bytes(64 J + lane) =
+  // 1024 J + lane_bytes(J, lane); lane_bytes depends on J only through
+  // J mod 4 for RP = 16 and not at all for RP <= 8 (row_swz tiles).
+  __device__ __forceinline__ static uint32_t lane_bytes(int J, int lane) {
+    return source_bytes(64 * (RP == 16 ? (J & 3) : 0) + lane) - 1024u * (RP == 16 ? (J & 3) : 0);
+  }
+};
+
+// Direct copy of one 16-byte piece per lane from a buffer into LDS: the
+// wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
+// Buffer accesses are range-checked against the descriptor's size on the
+// per-lane offset (loads past it read zero, stores past it are dropped).
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                            uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, uint32_t voff, float x) {
+  if constexpr (sizeof(T) == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<T>(x)), rs, voff, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), rs, voff, 0, 0);
+  }
+}
+
+// Per-lane source offsets of direct copies: copy J of a tile with RP pieces
+// per row reads 1024 J + lane_pattern; the pattern depends only on RP (and on
+// J mod 4 when RP = 16).  With copy J = j NW + wave, the RP = 16 pattern of
+// copy j is q16[j mod 4], resolved once per wave.
+struct CopyLanes {
+  uint32_t q16[4], p8, p4;
+  __device__ __forceinline__ void init(int lane, int wave, int NW) {
+    uint32_t p16[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) p16[a] = Tile<float, 64, 64>::lane_bytes(a, lane);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int a = (m * NW + wave) & 3;
+      q16[m] = a == 0 ? p16[0] : a == 1 ? p16[1] : a == 2 ? p16[2] : p16[3];
+    }
+    p8 = Tile<float, 64, 32>::lane_bytes(0, lane);
+    p4 = Tile<float, 64, 16>::lane_bytes(0, lane);
+  }
+  template <int RP> __device__ __forceinline__ uint32_t get(int j) const {
+    return RP == 16 ? q16[j & 3] : RP == 8 ? p8 : p4;
+  }
+};
+
+// Copy a dense tile (rows contiguous in memory) into LDS with NW waves; the
+// per-copy part of the source offset goes into the buffer base, so the range
+// check sees only the per-lane offset.
+template <typename TT, int NW, typename E>
+__device__ __forceinline__ void copy_tile(E* dst, const E* src, const CopyLanes& cl, int wave) {
+#pragma unroll
+  for (int j = 0; j < TT::PIECES / (64 * NW); ++j) {
+    const int J = j * NW + wave;
+    const auto rs = buffer_of(reinterpret_cast<const char*>(src) + 1024 * J, 1024);
+    copy_to_lds(rs, dst + J * 64 * TT::EPP, cl.template get<TT::RP>(j), 0);
+  }
+}
+
+}  // namespace gdn

@@ -57,9 +57,10 @@ hipError_t launch_chunk_fwd(const gdn_shape& s, const void* q, const void* k, co
                             int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
                             const float* beta, float scale, const float* S0, float* S_final,
                             const int32_t* cu, void* o, void* ws, hipStream_t st);
+// bwd: also write the operands of the reverse pass (backward workspace)
 hipError_t launch_chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
                                 int64_t ldk, const float* g, const float* beta, float scale,
-                                const int32_t* cu, void* ws, hipStream_t st);
+                                const int32_t* cu, void* ws, bool bwd, hipStream_t st);
 hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
                                    int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                    const float* S0, float* S_final, const int32_t* cu, void* o,

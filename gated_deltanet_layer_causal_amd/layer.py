@@ -123,7 +123,7 @@ class GDNCore:
         dS0 = torch.empty((n_seq, c.hv, c.d, c.d), dtype=torch.float32, device=dev)
         q, k, v = self.split(saved["y"])
         with _timed(timer, "chunk_prepare_b"):
-            L.gdn_chunk_prepare(sh, q, k, saved["g"], saved["beta"], c.q_scale, cu_seqlens, ws)
+            L.gdn_chunk_prepare_bwd(sh, q, k, saved["g"], saved["beta"], c.q_scale, cu_seqlens, ws)
         with _timed(timer, "chunk_bwd_states"):
             L.gdn_chunk_bwd_states(sh, q, k, v, c.q_scale, S0, cu_seqlens, ws)
         with _timed(timer, "chunk_bwd_reverse"):

@@ -149,11 +149,13 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
  * Besides letting a caller time or schedule the phases separately, every
  * phase after gdn_chunk_prepare is a single kernel launch.
  *   forward : gdn_chunk_prepare -> gdn_chunk_fwd_states
- *   backward: gdn_chunk_prepare -> gdn_chunk_bwd_states -> gdn_chunk_bwd_reverse
+ *   backward: gdn_chunk_prepare_bwd -> gdn_chunk_bwd_states -> gdn_chunk_bwd_reverse
  *             -> gdn_chunk_bwd_grads
  * gdn_chunk_prepare: chunk table from cu_seqlens; per (chunk, value head)
  *   the in-chunk gate sums and the WY/UT factors M = (I + A)^-1 diag(beta)
  *   and P (masked decayed scale * Q K^T), A = strictly-lower(beta D K K^T).
+ * gdn_chunk_prepare_bwd: the same, plus the transposed operands the reverse
+ *   phase reads (backward workspace size).
  * gdn_chunk_fwd_states: sequential pass over chunks; writes o, S_final.
  * gdn_chunk_bwd_states: same pass, storing chunk-start states and R, Delta.
  * gdn_chunk_bwd_reverse: reverse pass over chunks; writes dv, dS0 and the
@@ -164,6 +166,10 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
 gdn_status gdn_chunk_prepare(const gdn_shape* shape, const void* q, const void* k, int64_t ldq,
                              int64_t ldk, const float* g, const float* beta, float scale,
                              const int32_t* cu_seqlens, void* ws, size_t ws_bytes, void* stream);
+gdn_status gdn_chunk_prepare_bwd(const gdn_shape* shape, const void* q, const void* k,
+                                 int64_t ldq, int64_t ldk, const float* g, const float* beta,
+                                 float scale, const int32_t* cu_seqlens, void* ws, size_t ws_bytes,
+                                 void* stream);
 gdn_status gdn_chunk_fwd_states(const gdn_shape* shape, const void* q, const void* k,
                                 const void* v, int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                 const float* S0, float* S_final, const int32_t* cu_seqlens,
