@@ -25,7 +25,7 @@ EXPORTS = (
     "gdn_gate_bwd", "gdn_gate_bwd_workspace", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace",
     "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd",
     "gdn_gated_norm_bwd_workspace", "gdn_chunk_prepare", "gdn_chunk_prepare_bwd",
-    "gdn_chunk_fwd_states",
+    "gdn_chunk_fwd_states", "gdn_chunk_fwd_states_save",
     "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse", "gdn_chunk_bwd_grads",
 )
 
@@ -68,6 +68,7 @@ def load(path: str = LIB_PATH):
     lib.gdn_chunk_prepare.argtypes = [SP, V, V, I64, I64, V, V, F, V, V, c_size_t, V]
     lib.gdn_chunk_prepare_bwd.argtypes = [SP, V, V, I64, I64, V, V, F, V, V, c_size_t, V]
     lib.gdn_chunk_fwd_states.argtypes = [SP, V, V, V, I64, I64, I64, F, V, V, V, V, V, c_size_t, V]
+    lib.gdn_chunk_fwd_states_save.argtypes = lib.gdn_chunk_fwd_states.argtypes
     lib.gdn_chunk_bwd_states.argtypes = [SP, V, V, V, I64, I64, I64, F, V, V, V, c_size_t, V]
     lib.gdn_chunk_bwd_reverse.argtypes = [SP, V, V, I64, I64, F, V, V, V, V, I64, V, V, c_size_t, V]
     lib.gdn_chunk_bwd_grads.argtypes = [SP, V, V, I64, I64, V, F, V, V, V, I64, V, V, I64, I64, V,
@@ -83,7 +84,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_gated_norm_bwd_workspace.restype = c_size_t
     for name in ("gdn_conv_fwd", "gdn_conv_bwd", "gdn_gate_fwd", "gdn_gate_bwd", "gdn_chunk_fwd",
                  "gdn_chunk_bwd", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd", "gdn_chunk_prepare",
-                 "gdn_chunk_prepare_bwd", "gdn_chunk_fwd_states", "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse",
+                 "gdn_chunk_prepare_bwd", "gdn_chunk_fwd_states", "gdn_chunk_fwd_states_save",
+                 "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse",
                  "gdn_chunk_bwd_grads"):
         getattr(lib, name).restype = c_int
     _lib = lib
@@ -200,6 +202,12 @@ def gdn_chunk_prepare_bwd(shape, q, k, g, beta, scale, cu_seqlens, ws, stream=No
 
 def gdn_chunk_fwd_states(shape, q, k, v, scale, S0, S_final, cu_seqlens, o, ws, stream=None):
     _ok("gdn_chunk_fwd_states", load().gdn_chunk_fwd_states(
+        byref(shape), _p(q), _p(k), _p(v), _ld(q), _ld(k), _ld(v), scale, _p(S0), _p(S_final),
+        _p(cu_seqlens), _p(o), _p(ws), ws.numel(), _stream(stream)))
+
+
+def gdn_chunk_fwd_states_save(shape, q, k, v, scale, S0, S_final, cu_seqlens, o, ws, stream=None):
+    _ok("gdn_chunk_fwd_states_save", load().gdn_chunk_fwd_states_save(
         byref(shape), _p(q), _p(k), _p(v), _ld(q), _ld(k), _ld(v), scale, _p(S0), _p(S_final),
         _p(cu_seqlens), _p(o), _p(ws), ws.numel(), _stream(stream)))
 

@@ -229,6 +229,20 @@ gdn_status gdn_chunk_fwd_states(const gdn_shape* s, const void* q, const void* k
                                           ws, (hipStream_t)stream));
 }
 
+gdn_status gdn_chunk_fwd_states_save(const gdn_shape* s, const void* q, const void* k,
+                                     const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
+                                     float scale, const float* S0, float* S_final,
+                                     const int32_t* cu, void* o, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  GDN_TRY(check_chunk_common(s, q, k, ldq, ldk, cu, ws, ws_bytes,
+                             s ? chunk_bwd_ws_bytes(*s) : 0));
+  GDN_TRY(check_ptrs({v, o}));
+  GDN_TRY(check_ld(ldv, (int64_t)s->hv * s->dv));
+  if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return GDN_ERR_ALIGNMENT;
+  return launched(launch_chunk_fwd_states_save(*s, q, k, v, ldq, ldk, ldv, scale, S0, S_final, cu,
+                                               o, ws, (hipStream_t)stream));
+}
+
 gdn_status gdn_chunk_bwd_states(const gdn_shape* s, const void* q, const void* k, const void* v,
                                 int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                 const float* S0, const int32_t* cu, void* ws, size_t ws_bytes,

@@ -334,6 +334,23 @@ hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void
   });
 }
 
+hipError_t launch_chunk_fwd_states_save(const gdn_shape& s, const void* q, const void* k,
+                                        const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
+                                        float scale, const float* S0, float* S_final,
+                                        const int32_t* cu, void* o, void* ws, hipStream_t st) {
+  // the forward pass, then the pass that stores the backward's states (two
+  // launches over the same staged operands measured faster than one kernel
+  // doing both, which runs out of registers and LDS)
+  const ChunkLayout Ly = chunk_layout(s);
+  return dispatch_chunk(s, [&](auto c) {
+    using T = typename decltype(c)::type;
+    constexpr int D = decltype(c)::d;
+    hipError_t e = chunk_state<T, D, 0>(s, v, ldv, scale, S0, S_final, cu, o, Ly, (char*)ws, st);
+    if (e != hipSuccess) return e;
+    return chunk_state<T, D, 1>(s, v, ldv, scale, S0, nullptr, cu, nullptr, Ly, (char*)ws, st);
+  });
+}
+
 hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
                                    int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                    const float* S0, const int32_t* cu, void* ws, hipStream_t st) {

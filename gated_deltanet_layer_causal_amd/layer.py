@@ -48,12 +48,20 @@ def _timed(timer, name):
 
 
 class GDNCore:
-    """Holds the workspace for one layer shape and runs forward/backward."""
+    """Runs the layer core's forward and backward for one configuration.
+
+    Training flow (save_states=True, the default): the forward runs the
+    backward-mode chunk preparation and the state pass that also stores the
+    chunk-start states, R and Delta in a per-call chunk workspace, which the
+    backward then consumes (reverse pass + chunk gradients only).  With
+    save_states=False the forward keeps only its outputs and the backward
+    recomputes the preparation and the states."""
 
     def __init__(self, cfg: CoreConfig, device="cuda"):
         self.cfg = cfg
         self.device = torch.device(device)
-        self._ws = None
+        self._ws = None        # conv / gate / norm scratch
+        self._ws_chunk = None  # chunk scratch of calls that do not save states
         L.load()
 
     def shape(self, T: int, n_seq: int) -> L.Shape:
@@ -62,11 +70,18 @@ class GDNCore:
 
     def workspace(self, shape: L.Shape, rows: int) -> torch.Tensor:
         need = max(L.gdn_conv_bwd_workspace(shape), L.gdn_gate_bwd_workspace(shape),
-                   L.gdn_chunk_fwd_workspace(shape), L.gdn_chunk_bwd_workspace(shape),
                    L.gdn_gated_norm_bwd_workspace(rows, self.cfg.d), 256)
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
+
+    def chunk_workspace(self, shape: L.Shape, fresh: bool) -> torch.Tensor:
+        need = L.gdn_chunk_bwd_workspace(shape)
+        if fresh:
+            return torch.empty(need, dtype=torch.uint8, device=self.device)
+        if self._ws_chunk is None or self._ws_chunk.numel() < need:
+            self._ws_chunk = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws_chunk
 
     def split(self, y):
         c = self.cfg
@@ -76,12 +91,13 @@ class GDNCore:
         return q, k, v
 
     def forward(self, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, S0=None,
-                want_final=False, timer=None):
+                want_final=False, timer=None, save_states=True):
         c = self.cfg
         T = x.shape[0]
         n_seq = cu_seqlens.numel() - 1
         sh = self.shape(T, n_seq)
         ws = self.workspace(sh, T * c.hv)
+        wc = self.chunk_workspace(sh, fresh=save_states)
         dev, dt = x.device, c.dtype
         y = torch.empty((T, c.channels), dtype=dt, device=dev)
         with _timed(timer, "conv_fwd"):
@@ -93,14 +109,23 @@ class GDNCore:
         q, k, v = self.split(y)
         o = torch.empty((T, c.hv, c.d), dtype=dt, device=dev)
         Sf = torch.empty((n_seq, c.hv, c.d, c.d), dtype=torch.float32, device=dev) if want_final else None
-        with _timed(timer, "chunk_prepare"):
-            L.gdn_chunk_prepare(sh, q, k, g, beta, c.q_scale, cu_seqlens, ws)
-        with _timed(timer, "chunk_fwd_states"):
-            L.gdn_chunk_fwd_states(sh, q, k, v, c.q_scale, S0, Sf, cu_seqlens, o, ws)
+        if save_states:
+            with _timed(timer, "chunk_prepare"):
+                L.gdn_chunk_prepare_bwd(sh, q, k, g, beta, c.q_scale, cu_seqlens, wc)
+            with _timed(timer, "chunk_fwd_states"):
+                L.gdn_chunk_fwd_states_save(sh, q, k, v, c.q_scale, S0, Sf, cu_seqlens, o, wc)
+        else:
+            with _timed(timer, "chunk_prepare"):
+                L.gdn_chunk_prepare(sh, q, k, g, beta, c.q_scale, cu_seqlens, wc)
+            with _timed(timer, "chunk_fwd_states"):
+                L.gdn_chunk_fwd_states(sh, q, k, v, c.q_scale, S0, Sf, cu_seqlens, o, wc)
         out = torch.empty_like(o)
         with _timed(timer, "norm_fwd"):
             L.gdn_gated_norm_fwd(o, z, w_norm, out, c.norm_eps, c.act)
-        return {"y": y, "g": g, "beta": beta, "o": o, "out": out, "S_final": Sf}
+        saved = {"y": y, "g": g, "beta": beta, "o": o, "out": out, "S_final": Sf}
+        if save_states:
+            saved["chunk_ws"] = wc
+        return saved
 
     def backward(self, saved, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, dout,
                  S0=None, dS_final=None, timer=None):
@@ -122,15 +147,19 @@ class GDNCore:
         dbeta = torch.empty_like(dg)
         dS0 = torch.empty((n_seq, c.hv, c.d, c.d), dtype=torch.float32, device=dev)
         q, k, v = self.split(saved["y"])
-        with _timed(timer, "chunk_prepare_b"):
-            L.gdn_chunk_prepare_bwd(sh, q, k, saved["g"], saved["beta"], c.q_scale, cu_seqlens, ws)
-        with _timed(timer, "chunk_bwd_states"):
-            L.gdn_chunk_bwd_states(sh, q, k, v, c.q_scale, S0, cu_seqlens, ws)
+        wc = saved.get("chunk_ws")
+        if wc is None:
+            wc = self.chunk_workspace(sh, fresh=False)
+            with _timed(timer, "chunk_prepare_b"):
+                L.gdn_chunk_prepare_bwd(sh, q, k, saved["g"], saved["beta"], c.q_scale, cu_seqlens,
+                                        wc)
+            with _timed(timer, "chunk_bwd_states"):
+                L.gdn_chunk_bwd_states(sh, q, k, v, c.q_scale, S0, cu_seqlens, wc)
         with _timed(timer, "chunk_bwd_reverse"):
-            L.gdn_chunk_bwd_reverse(sh, q, k, c.q_scale, cu_seqlens, do, dS_final, dv, dS0, ws)
+            L.gdn_chunk_bwd_reverse(sh, q, k, c.q_scale, cu_seqlens, do, dS_final, dv, dS0, wc)
         with _timed(timer, "chunk_bwd_grads"):
             L.gdn_chunk_bwd_grads(sh, q, k, saved["beta"], c.q_scale, cu_seqlens, do, dv, dq, dk, dg,
-                                  dbeta, ws)
+                                  dbeta, wc)
         da = torch.empty((T, c.hv), dtype=dt, device=dev)
         db = torch.empty_like(da)
         dA_log = torch.empty(c.hv, dtype=torch.float32, device=dev)

@@ -157,6 +157,13 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
  * gdn_chunk_prepare_bwd: the same, plus the transposed operands the reverse
  *   phase reads (backward workspace size).
  * gdn_chunk_fwd_states: sequential pass over chunks; writes o, S_final.
+ * gdn_chunk_fwd_states_save: the same after gdn_chunk_prepare_bwd, also
+ *   storing the chunk-start states, R and Delta in the (backward-size)
+ *   workspace, i.e. what gdn_chunk_bwd_states would recompute (two kernel
+ *   launches: the forward pass, then the state pass).  A training
+ *   step can then run its backward as gdn_chunk_bwd_reverse ->
+ *   gdn_chunk_bwd_grads on that workspace (same inputs, workspace untouched
+ *   in between), skipping the preparation and the state pass.
  * gdn_chunk_bwd_states: same pass, storing chunk-start states and R, Delta.
  * gdn_chunk_bwd_reverse: reverse pass over chunks; writes dv, dS0 and the
  *   chunk-end state gradients.
@@ -174,6 +181,11 @@ gdn_status gdn_chunk_fwd_states(const gdn_shape* shape, const void* q, const voi
                                 const void* v, int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                 const float* S0, float* S_final, const int32_t* cu_seqlens,
                                 void* o, void* ws, size_t ws_bytes, void* stream);
+gdn_status gdn_chunk_fwd_states_save(const gdn_shape* shape, const void* q, const void* k,
+                                     const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
+                                     float scale, const float* S0, float* S_final,
+                                     const int32_t* cu_seqlens, void* o, void* ws,
+                                     size_t ws_bytes, void* stream);
 gdn_status gdn_chunk_bwd_states(const gdn_shape* shape, const void* q, const void* k,
                                 const void* v, int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                 const float* S0, const int32_t* cu_seqlens, void* ws,

@@ -27,8 +27,10 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("save_states", [True, False], ids=["saved", "recompute"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_layer_matches_oracle(name):
+def test_layer_matches_oracle(name, save_states):
+    """Both backward flows: states saved by the forward, or recomputed."""
     w, lens, A_range, act = CASES[name]
     inp = gi.make_inputs(w, seqlens=lens, A_range=A_range)
     bf = w.dtype == "bf16"
@@ -40,7 +42,7 @@ def test_layer_matches_oracle(name):
             dev(inp["A_log"]), dev(inp["dt_bias"]), dev(inp["z"], tdt), dev(inp["w_norm"]), cu)
     S0 = dev(inp["S0"]) if inp["S0"] is not None else None
     dST = dev(inp["dS_T"]) if inp["dS_T"] is not None else None
-    f = core.forward(*args, S0=S0, want_final=True)
+    f = core.forward(*args, S0=S0, want_final=True, save_states=save_states)
     gb = core.backward(f, *args, dev(inp["dy"], tdt), S0=S0, dS_final=dST)
     torch.cuda.synchronize()
     sc = w.d ** -0.5
@@ -54,6 +56,6 @@ def test_layer_matches_oracle(name):
     # every error is printed before the first assertion, so a failure shows
     # where along the layer the difference enters
     errs = {k: rel_err(host(t).reshape(np.shape(r)), r) for k, t, r, _ in checks}
-    print(name, " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    print(name, "saved" if save_states else "recompute", " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
     for k, t, r, tol in checks:
         assert_close(k, host(t).reshape(np.shape(r)), r, tol)
