@@ -26,7 +26,7 @@ struct GradSmem {
   T Kt[D][CHUNK + Pad<T>::v];      // K^T (k-major)
   T Qt[D][CHUNK + Pad<T>::v];      // Q^T
   float Tm[CHUNK][68];             // Tinv
-  float Sc1[CHUNK][68];            // A, then dTinv
+  float Sc1[CHUNK][68];            // dTinv, then the pair terms E
   union {
     struct {
       T B1[CHUNK][D + Pad<T>::v];
@@ -38,7 +38,6 @@ struct GradSmem {
   } u;
   T WA[CHUNK][CHUNK + Pad<T>::v];
   T dPD[CHUNK][CHUNK + Pad<T>::v];
-  float X[16][17];
   double gam[CHUNK];
   float bet[CHUNK];
   float rowB[CHUNK];
@@ -59,7 +58,8 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G,
     float scale, const double* __restrict__ gcum, const float* __restrict__ beta,
-    const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ hst,
+    const typename Compute<T>::type* __restrict__ Pw, const float* __restrict__ Tiw,
+    const T* __restrict__ hst,
     const T* __restrict__ dhst, const T* __restrict__ Rw, const T* __restrict__ Dlw,
     const T* __restrict__ ddw, const T* __restrict__ dout, const T* __restrict__ dvo, int64_t lddv,
     T* __restrict__ dq, T* __restrict__ dk, int64_t lddq, int64_t lddk, float* __restrict__ dg,
@@ -121,7 +121,16 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
     const int lane = tid & 63;
     const int rbase = 16 * wave + 4 * (lane >> 4), ccol = lane & 15, rsub = 4 * (lane >> 4);
     const int r16 = lane & 15;
-    // ---- P0: gate values for the chunk; P values at this lane's positions
+    // ---- P0: gate values for the chunk; P values at this lane's positions;
+    //      Tinv of this (chunk, head) as the preparation formed it
+    {
+      const float4* src = reinterpret_cast<const float4*>(Tiw + ((int64_t)c * Hv + h) * CHUNK * CHUNK);
+#pragma unroll
+      for (int j = 0; j < CHUNK * (CHUNK / 4) / 256; ++j) {
+        const int i = tid + 256 * j;
+        *reinterpret_cast<float4*>(&sm.Tm[i / (CHUNK / 4)][(i % (CHUNK / 4)) * 4]) = src[i];
+      }
+    }
     if (wave == 0) {
       sm.gam[lane] = gcum[(t0 + (lane < L ? lane : L - 1)) * Hv + h];
       sm.bet[lane] = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
@@ -136,18 +145,6 @@ __global__ void __launch_bounds__(256, 1) chunk_grad_kernel(
         for (int e = 0; e < 4; ++e) pval[j][e] = Pc[(rbase + e) * CHUNK + acc_col<CT>(16 * j + ccol)];
     }
     __syncthreads();
-    // ---- P1: A, then Tinv
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = 16 * j + ccol;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = rbase + e;
-        sm.Sc1[t][s] = (s < t) ? sm.bet[t] * dexp<T>(sm.gam[t] - sm.gam[s]) * kk[j][e] : 0.f;
-      }
-    }
-    __syncthreads();
-    invert_unit_lower(sm.Sc1, sm.Tm, sm.X, tid);
     // ---- P2: dM = dDelta R^T
     f_dd.store(&sm.u.t.B1[0][0], LD, tid);
     f_r.store(&sm.u.t.B2[0][0], LD, tid);
@@ -430,7 +427,8 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
     hipLaunchKernelGGL(kern, dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm, st, (const T*)q,
                        (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
                        s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), beta,
-                       (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)(ws + Ly.h),
+                       (const typename Compute<T>::type*)(ws + Ly.pw), (const float*)(ws + Ly.tiw),
+                       (const T*)(ws + Ly.h),
                        (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw), (const T*)(ws + Ly.dlw),
                        (const T*)(ws + Ly.ddw), (const T*)dout, (const T*)dv, lddv, (T*)dq,
                        (T*)dk, lddq, lddk, dg, dbeta, (void*)(ws + Ly.sink));

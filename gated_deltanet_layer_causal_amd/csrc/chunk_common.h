@@ -61,6 +61,7 @@ struct ChunkLayout {
   size_t gw, dw;      // fp32 [nt_max][hv][64]: Gam_t and dec_t (clamped to the chunk length)
   size_t kb, ktb, qtb; // T [nt_max][hk]: K rows [64][dk], K^T and Q^T [dk][64] (backward)
   size_t ptb, mtb;    // T [nt_max][hv][64][64]: P^T, M^T (backward)
+  size_t tiw;         // fp32 [nt_max][hv][64][64]: Tinv (backward)
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
   size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
   size_t sink;        // SINK_ELEMS scratch floats: target of stores for padding rows
@@ -102,6 +103,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.qtb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.ptb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.mtb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
+  L.tiw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.dh = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.rw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
@@ -161,24 +163,6 @@ __device__ __forceinline__ void stage_rows(TD* dst, int ld_s, const TS* src, int
 // The sequential kernels load chunk c+1 into registers while chunk c computes,
 // so global-memory latency leaves the critical path.  Raw copies keep the
 // storage type; conversion happens when the registers are consumed.
-
-// 8 consecutive storage elements (one 16-byte vector; two for fp32).
-template <typename T> struct Raw8 { uint4 v[sizeof(T) / 2]; };
-template <typename T> __device__ __forceinline__ Raw8<T> ld_raw8(const T* p) {
-  Raw8<T> r;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = reinterpret_cast<const uint4*>(p)[i];
-  return r;
-}
-template <typename T> __device__ __forceinline__ Raw8<T> zero_raw8() {
-  Raw8<T> r;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = make_uint4(0, 0, 0, 0);
-  return r;
-}
-template <typename T> __device__ __forceinline__ f8 raw_f8(const Raw8<T>& r) {
-  return load8(reinterpret_cast<const T*>(&r.v[0]));
-}
 
 // Rows [0, 64) x [0, W) of a token-major tensor, 8 elements per item, items
 // spread over the 256 threads.  Loads are unconditional (rows >= L re-read

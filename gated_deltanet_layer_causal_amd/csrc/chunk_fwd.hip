@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
     typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw,
     T* __restrict__ Kb, T* __restrict__ Ktb, T* __restrict__ Qtb, T* __restrict__ Ptb,
-    T* __restrict__ Mtb) {
+    T* __restrict__ Mtb, float* __restrict__ Tiw) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -192,6 +192,10 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       store8(Mout + t * CHUNK + s8, v);
     }
     if constexpr (BWD) {
+      // Tinv (fp32) for the chunk gradients
+      float4* to = reinterpret_cast<float4*>(Tiw + ((int64_t)c * Hv + h) * CHUNK * CHUNK);
+      for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256)
+        to[i] = *reinterpret_cast<const float4*>(&sm.Ti[i / (CHUNK / 4)][(i % (CHUNK / 4)) * 4]);
       // M^T in the storage type, columns (tokens t) in accumulator order
       T* mo = Mtb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
       for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
@@ -263,7 +267,8 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        (typename Compute<T>::type*)(ws + Ly.k16w), (float*)(ws + Ly.gw),
                        (float*)(ws + Ly.dw), BWD ? (T*)(ws + Ly.kb) : nullptr,
                        BWD ? (T*)(ws + Ly.ktb) : nullptr, BWD ? (T*)(ws + Ly.qtb) : nullptr,
-                       BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (T*)(ws + Ly.mtb) : nullptr);
+                       BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (T*)(ws + Ly.mtb) : nullptr,
+                       BWD ? (float*)(ws + Ly.tiw) : nullptr);
   }
   return hipGetLastError();
 }

@@ -100,6 +100,24 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
+// 8 consecutive storage elements (one 16-byte vector; two for fp32).
+template <typename T> struct Raw8 { uint4 v[sizeof(T) / 2]; };
+template <typename T> __device__ __forceinline__ Raw8<T> ld_raw8(const T* p) {
+  Raw8<T> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = reinterpret_cast<const uint4*>(p)[i];
+  return r;
+}
+template <typename T> __device__ __forceinline__ Raw8<T> zero_raw8() {
+  Raw8<T> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = make_uint4(0, 0, 0, 0);
+  return r;
+}
+template <typename T> __device__ __forceinline__ f8 raw_f8(const Raw8<T>& r) {
+  return load8(reinterpret_cast<const T*>(&r.v[0]));
+}
+
 // ---- MFMA operand fragments -------------------------------------------------
 // Mma<T>::frag is the per-lane operand of one MFMA step over KS values of K.
 template <typename T> struct Mma;
