@@ -26,23 +26,66 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GDN fwd+bwd tokens/s (16k/48v heads, d=128, 64k tok); % MFMA/HBM peak"
+FORWARD_CALLS = ("conv_fwd", "gate_fwd", "chunk_prepare", "chunk_fwd_states", "norm_fwd")
+# calls that launch more than one kernel (not used for the single-kernel roofline)
+MULTI_KERNEL_CALLS = ("chunk_fwd_states", "chunk_prepare", "chunk_prepare_b", "conv_bwd",
+                      "norm_bwd", "gate_bwd")
+# HIP sources of the kernel behind each single-kernel call (HBM traffic taken
+# from committed counter summaries is used only while these are unchanged)
+KERNEL_SOURCES = {
+    "chunk_bwd_grads": ["chunk_bwd.hip", "chunk_common.h", "common.h", "launch.h"],
+    "chunk_bwd_reverse": ["chunk_rev.hip", "chunk_stream.h", "chunk_common.h", "common.h",
+                          "launch.h"],
+    "chunk_bwd_states": ["chunk_state.hip", "chunk_stream.h", "chunk_common.h", "common.h",
+                         "launch.h"],
+    "conv_fwd": ["conv.hip", "common.h", "launch.h"],
+    "norm_fwd": ["norm.hip", "common.h", "launch.h"],
+    "gate_fwd": ["gate.hip", "common.h", "launch.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_flash64k.txt")
+
+
+def sources_digest(call):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(call, []):
+        with open(os.path.join(ROOT, "gated_deltanet_layer_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(call):
+    """HBM bytes per launch of `call` from the committed counter summary, or
+    None when there is none or the kernel's sources changed since."""
+    if call not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("call="):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split())
+        if kv.get("call") == call and kv.get("sources") == sources_digest(call):
+            return float(kv["hbm_bytes_per_launch"])
+    return None
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 
 # Algorithmic work per token of each call (E = bytes per element of the
 # token tensors).  HBM-bound calls count the bytes they must read and write.
-# The chunk phases count the dense contraction flops of their formulas in the
-# chunked WY/UT form (chunk C = 64, head dim d, per value head unless noted):
-#   fwd_states : K S^T, Q S^T, S update (3 x 2 d^2) + M R, P Delta (2 x 2 C d)
-#   bwd_states : K S^T, S update (2 x 2 d^2) + M R (2 C d)
+# The chunk phases count the dense contraction flops of the products they
+# form (chunk C = 64, head dim d, per value head unless noted):
+#   fwd_states : W S^T, Q S^T, S update (3 x 2 d^2) + M V, P Delta (2 x 2 C d)
+#   bwd_states : W S^T, K S^T, S update (3 x 2 d^2) + M V (2 C d)
+#   fwd_states_save: both of the above
 #   bwd_reverse: K dS'^T, Q^T dO, K^T dR (3 x 2 d^2) + P^T dO, M^T dDelta (2 x 2 C d)
 #   bwd_grads  : dO S, dR S, Delta dS' (3 x 2 d^2); dM, dP, (dP o D) K,
 #                (dP o D)^T Q, (dA o bD) K, (dA o bD)^T K (6 x 2 C d);
 #                Tinv products (2 x 2 C^2); per key head K K^T, Q K^T (2 x 2 C d)
-# The preparation phase is bandwidth-bound: it reads q, k, g, beta and
-# writes the in-chunk gate sums and the two 64 x 64 factors per chunk.
-def algorithmic_per_token(name, hk, hv, d, E):
+# The preparation is bandwidth-bound: it reads q, k, g, beta and writes the
+# gate sums, per value head M, P, W, Gam, dec (and, in backward mode, P^T,
+# M^T, Tinv), per key head K^T and fp16 Q, K rows (backward mode: K, K^T,
+# Q^T in the storage type).
+def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     C = 2 * hk * d + hv * d
     C64 = 64
     if name == "conv_fwd":
@@ -57,12 +100,18 @@ def algorithmic_per_token(name, hk, hv, d, E):
         return "hbm", 3 * hv * d * E                  # read o, z; write y
     if name == "norm_bwd":
         return "hbm", 5 * hv * d * E                  # read o, z, dy; write do, dz
-    if name in ("chunk_prepare", "chunk_prepare_b"):
-        return "hbm", 2 * hk * d * E + hv * (4 + 4 + 8 + 2 * C64 * E)
+    fwd_bytes = 2 * hk * d * E + 3 * hk * d * E + hv * (4 + 4 + 8 + 2 * C64 * E + d * E + 8)
+    bwd_extra = 3 * hk * d * E + hv * (2 * C64 * E + 4 * C64)
+    if name == "chunk_prepare":
+        return "hbm", fwd_bytes + (bwd_extra if saved else 0)
+    if name == "chunk_prepare_b":
+        return "hbm", fwd_bytes + bwd_extra
+    fwd_states = hv * (6 * d * d + 4 * C64 * d)
+    bwd_states = hv * (6 * d * d + 2 * C64 * d)
     if name == "chunk_fwd_states":
-        return "mfma", hv * (6 * d * d + 4 * C64 * d)
+        return "mfma", fwd_states + (bwd_states if saved else 0)
     if name == "chunk_bwd_states":
-        return "mfma", hv * (4 * d * d + 2 * C64 * d)
+        return "mfma", bwd_states
     if name == "chunk_bwd_reverse":
         return "mfma", hv * (6 * d * d + 4 * C64 * d)
     if name == "chunk_bwd_grads":
@@ -207,7 +256,8 @@ def main():
     per_call = timer.mean_ms()
 
     E = 2 if w.dtype == "bf16" else 4
-    dom = max(per_call, key=per_call.get)
+    single = {k: v for k, v in per_call.items() if k not in MULTI_KERNEL_CALLS}
+    dom = max(single, key=single.get)
     bound, per_tok = algorithmic_per_token(dom, w.hk, w.hv, w.d, E)
     if bound == "hbm":
         achieved = per_tok * w.T / (per_call[dom] / 1e3) / 1e9
@@ -216,6 +266,8 @@ def main():
         achieved = per_tok * w.T / (per_call[dom] / 1e3) / 1e12
         peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
         unit = "TFLOP/s"
+    fwd_ms = sum(t for k, t in per_call.items() if k in FORWARD_CALLS)
+    bwd_ms = sum(t for k, t in per_call.items() if k not in FORWARD_CALLS)
     calls = {}
     for name, t in sorted(per_call.items(), key=lambda kv: -kv[1]):
         b, pt = algorithmic_per_token(name, w.hk, w.hv, w.d, E)
@@ -232,8 +284,10 @@ def main():
                                f"d={w.d}, {w.T} tokens, single sequence, chunk 64",
                    "tokens": w.T, "hk": w.hk, "hv": w.hv, "d": w.d, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
-                     "ms_per_launch": round(per_call[dom], 4)},
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom),
+                     "kernel": dom, "ms_per_launch": round(per_call[dom], 4)},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
         "calls": calls,
     }
     if not args.no_cpu:

@@ -31,7 +31,26 @@ template <> __device__ __forceinline__ float from_f<float>(float x) { return x; 
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ fp16 from_f<fp16>(float x) { return (fp16)x; }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Lane swaps within rows of 16 lanes (DPP), and the sum over aligned groups
+// of N = 4, 8 or 16 lanes built from them (every lane gets the group sum).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int N> __device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+  x += dpp_f<0xB1>(x);                         // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_f<0x4E>(x);                         // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (N >= 8) x += dpp_f<0x141>(x);  // row_half_mirror: the other quad of 8
+  if constexpr (N >= 16) x += dpp_f<0x140>(x); // row_mirror: the other half of 16
+  return x;
+}
+
+// sigmoid with the hardware reciprocal (about 1 ulp) instead of an IEEE
+// division sequence; e^-x = inf gives rcp(inf) = 0 as it should
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 // ---- 8-element vector load/store of a storage type, converted to/from fp32
 struct f8 { float v[8]; };

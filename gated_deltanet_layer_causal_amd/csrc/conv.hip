@@ -29,9 +29,7 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int n_seq, int64_t t)
 template <int D>
 __device__ __forceinline__ float group_sum(float x) {
   // lanes of one head: D/8 consecutive lanes
-#pragma unroll
-  for (int off = 1; off < D / 8; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  return lane_group_sum<D / 8>(x);
 }
 
 template <typename T>

@@ -11,9 +11,7 @@ namespace gdn {
 
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  return lane_group_sum<LPR>(x);
 }
 
 __device__ __forceinline__ float act_f(int act, float z, float sg) { return act == 0 ? z * sg : sg; }
