@@ -28,16 +28,14 @@ if ROOT not in sys.path:
 METRIC = "GDN fwd+bwd tokens/s (16k/48v heads, d=128, 64k tok); % MFMA/HBM peak"
 FORWARD_CALLS = ("conv_fwd", "gate_fwd", "chunk_prepare", "chunk_fwd_states", "norm_fwd")
 # calls that launch more than one kernel (not used for the single-kernel roofline)
-MULTI_KERNEL_CALLS = ("chunk_fwd_states", "chunk_prepare", "chunk_prepare_b", "conv_bwd",
-                      "norm_bwd", "gate_bwd")
+MULTI_KERNEL_CALLS = ("chunk_fwd_states", "chunk_prepare", "chunk_prepare_b", "chunk_bwd_states",
+                      "conv_bwd", "norm_bwd", "gate_bwd")
 # HIP sources of the kernel behind each single-kernel call (HBM traffic taken
 # from committed counter summaries is used only while these are unchanged)
 KERNEL_SOURCES = {
     "chunk_bwd_grads": ["chunk_bwd.hip", "chunk_common.h", "common.h", "launch.h"],
     "chunk_bwd_reverse": ["chunk_rev.hip", "chunk_stream.h", "chunk_common.h", "common.h",
                           "launch.h"],
-    "chunk_bwd_states": ["chunk_state.hip", "chunk_stream.h", "chunk_common.h", "common.h",
-                         "launch.h"],
     "conv_fwd": ["conv.hip", "common.h", "launch.h"],
     "norm_fwd": ["norm.hip", "common.h", "launch.h"],
     "gate_fwd": ["gate.hip", "common.h", "launch.h"],
@@ -106,12 +104,18 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
         return "hbm", fwd_bytes + (bwd_extra if saved else 0)
     if name == "chunk_prepare_b":
         return "hbm", fwd_bytes + bwd_extra
+    # products formed per v-head token: the forward pass without saved
+    # states (W S^T, Q S^T, update; M V, P Delta); the saved-state pass (W S^T,
+    # update; M V) and the chunk-parallel outputs (K S^T, Q S^T; M R, P Delta),
+    # whose O part the recompute flow leaves out
     fwd_states = hv * (6 * d * d + 4 * C64 * d)
-    bwd_states = hv * (6 * d * d + 2 * C64 * d)
+    save_pass = hv * (4 * d * d + 2 * C64 * d)
+    outputs = hv * (4 * d * d + 4 * C64 * d)
+    outputs_no_o = hv * (2 * d * d + 2 * C64 * d)
     if name == "chunk_fwd_states":
-        return "mfma", fwd_states + (bwd_states if saved else 0)
+        return "mfma", (save_pass + outputs) if saved else fwd_states
     if name == "chunk_bwd_states":
-        return "mfma", bwd_states
+        return "mfma", save_pass + outputs_no_o
     if name == "chunk_bwd_reverse":
         return "mfma", hv * (6 * d * d + 4 * C64 * d)
     if name == "chunk_bwd_grads":

@@ -28,7 +28,7 @@ template <typename T> struct Compute { typedef fp16 type; };
 template <> struct Compute<float> { typedef float type; };
 
 // Column order of the operands that the sequential kernels read as MFMA A
-// operands in accumulator order (W, Q and K rows, K^T, P).  With 16-bit
+// operands in accumulator order (W, Q rows, K^T, M, P).  With 16-bit
 // operands a step covers columns 32 p + 16 h + 4 g + i (h, i < 2, 4) for lane
 // group g, so each block of 32 columns is stored as [g][h][i]: column
 // 16 h + 4 g + i at position 8 g + 4 h + i, and a lane's eight values are one
@@ -54,10 +54,10 @@ struct ChunkLayout {
   int64_t nt_max;     // upper bound on the number of chunks: T/64 + n_seq
   size_t seq_off;     // int32 [n_seq + 1]: first chunk of each sequence; [n_seq] = #chunks
   size_t gcum;        // fp64 [T][hv]: in-chunk cumulative gate
-  size_t mw, pw;      // CT [nt_max][hv][64][64]: M = Tinv diag(beta), P
+  size_t mw, pw;      // CT [nt_max][hv][64][64]: M = Tinv diag(beta), P (accumulator column order)
   size_t ww;          // CT [nt_max][hv][64][dk]: W = M diag(Gam) K
   size_t ktw;         // CT [nt_max][hk][dk][64]: K^T of each chunk
-  size_t q16w, k16w;  // CT [nt_max][hk][64][dk]: Q and K rows of each chunk (zero past its end)
+  size_t q16w;        // CT [nt_max][hk][64][dk]: Q rows of each chunk (zero past its end)
   size_t gw, dw;      // fp32 [nt_max][hv][64]: Gam_t and dec_t (clamped to the chunk length)
   size_t kb, ktb, qtb; // T [nt_max][hk]: K rows [64][dk], K^T and Q^T [dk][64] (backward)
   size_t ptb, mtb;    // T [nt_max][hv][64][64]: P^T, M^T (backward)
@@ -94,7 +94,6 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.ww = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * s.dk);
   L.ktw = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.q16w = off; off = align256(off + es * (size_t)L.nt_max * s.hk * CHUNK * s.dk);
-  L.k16w = off; off = align256(off + es * (size_t)L.nt_max * s.hk * CHUNK * s.dk);
   L.gw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.dw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.total_fwd = off;

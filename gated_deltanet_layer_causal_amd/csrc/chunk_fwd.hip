@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     double* __restrict__ gcum, typename Compute<T>::type* __restrict__ Mw,
     typename Compute<T>::type* __restrict__ Pw, typename Compute<T>::type* __restrict__ Ww,
     typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
-    typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw,
+    float* __restrict__ Gw, float* __restrict__ Dw,
     T* __restrict__ Kb, T* __restrict__ Ktb, T* __restrict__ Qtb, T* __restrict__ Ptb,
     T* __restrict__ Mtb, float* __restrict__ Tiw) {
   typedef typename Compute<T>::type CT;
@@ -100,8 +100,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   const int ccol = lane & 15;
   const int r16 = lane & 15;
   {
-    // Q and K rows (compute type, zero past the chunk end, columns in
-    // accumulator order) to the workspace, in 4-element pieces
+    // Q rows (compute type, zero past the chunk end, columns in accumulator
+    // order) to the workspace, in 4-element pieces; K rows in the storage
+    // type (backward)
     constexpr int PR = D / 4;
     const int64_t base = ((int64_t)c * (Hv / G) + kh) * CHUNK * D;
     for (int i = tid; i < CHUNK * PR; i += 256) {
@@ -109,7 +110,6 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       typedef CT v4 __attribute__((ext_vector_type(4)));
       const int dst = r * D + acc_col<CT>(c4);
       *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&sm.u.Q[r][c4]);
-      *reinterpret_cast<v4*>(K16w + base + dst) = *reinterpret_cast<const v4*>(&sm.K[r][c4]);
       if constexpr (BWD) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) Kb[base + dst + u] = from_f<T>(to_f(sm.K[r][c4 + u]));
@@ -183,13 +183,13 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     }
     __syncthreads();
     invert_unit_lower(sm.A, sm.Ti, sm.X, tid);
+    // M = Tinv diag(beta), columns in accumulator order, in 4-element pieces
     CT* Mout = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
-    for (int i = tid; i < CHUNK * 8; i += 256) {
-      const int t = i >> 3, s8 = (i & 7) * 8;
-      f8 v;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v.v[u] = sm.Ti[t][s8 + u] * sm.bet[s8 + u];
-      store8(Mout + t * CHUNK + s8, v);
+    for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
+      const int t = i / (CHUNK / 4), s4 = (i % (CHUNK / 4)) * 4;
+      const float4 ti = *reinterpret_cast<const float4*>(&sm.Ti[t][s4]);
+      store4(Mout + t * CHUNK + acc_col<CT>(s4), ti.x * sm.bet[s4], ti.y * sm.bet[s4 + 1],
+             ti.z * sm.bet[s4 + 2], ti.w * sm.bet[s4 + 3]);
     }
     if constexpr (BWD) {
       // Tinv (fp32) for the chunk gradients
@@ -263,8 +263,7 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        (typename Compute<T>::type*)(ws + Ly.pw),
                        (typename Compute<T>::type*)(ws + Ly.ww),
                        (typename Compute<T>::type*)(ws + Ly.ktw),
-                       (typename Compute<T>::type*)(ws + Ly.q16w),
-                       (typename Compute<T>::type*)(ws + Ly.k16w), (float*)(ws + Ly.gw),
+                       (typename Compute<T>::type*)(ws + Ly.q16w), (float*)(ws + Ly.gw),
                        (float*)(ws + Ly.dw), BWD ? (T*)(ws + Ly.kb) : nullptr,
                        BWD ? (T*)(ws + Ly.ktb) : nullptr, BWD ? (T*)(ws + Ly.qtb) : nullptr,
                        BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (T*)(ws + Ly.mtb) : nullptr,

@@ -5,9 +5,10 @@
 //   U     = M V                       (needs no state)
 //   Delta = U - W S^T
 //   S     <- Gam_L S + (diag(dec) Delta)^T K
-// and the outputs O = diag(Gam) scale Q S^T + P Delta (forward) or
-// R = V - diag(Gam) K S^T (backward).  Only the two products through S are
-// sequential; everything else hangs off them.
+// and the outputs O = diag(Gam) scale Q S^T + P Delta (MODE 0), or the
+// chunk-start states S themselves (MODE 1), from which chunk_out.hip forms
+// R, Delta and O chunk by chunk in parallel.  Only the two products through
+// S are sequential; everything else hangs off them.
 //
 // One workgroup per (sequence, value head, block of 16 * NW value rows of the
 // state); wave w owns 16 value rows and keeps its d_k x 16 slice of S^T in
@@ -18,7 +19,7 @@
 // LDS in the same (permuted) reduction order (AccOrder; the preparation
 // stores those operands with their columns in that order, acc_col).
 //
-// The chunk's shared operands (W, K^T, Q or K, M, P, V, Gam, dec) are copied
+// The chunk's shared operands (W, K^T, M, V, Gam, dec; Q and P in MODE 0) are copied
 // from memory straight into LDS (global_load_lds, no registers), into one of
 // two buffers: chunk c + 1 streams into one while chunk c computes from the
 // other, so a chunk step has a single barrier.  A direct copy writes 64
@@ -40,7 +41,7 @@ template <typename T, int D, int NW, int MODE> struct StateBuf {
   typedef Tile<T, CHUNK, BV, 3> TV;     // value rows (storage type)
   CT W[TW::PIECES * TW::EPP];
   CT Kt[TKt::PIECES * TKt::EPP];
-  CT X[TW::PIECES * TW::EPP];
+  CT X[MODE == 0 ? TW::PIECES * TW::EPP : 8];   // Q rows
   CT M[TM::PIECES * TM::EPP];
   CT P[MODE == 0 ? TM::PIECES * TM::EPP : 8];
   T V[TV::PIECES * TV::EPP];
@@ -55,7 +56,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     const typename Compute<T>::type* __restrict__ Ww, const typename Compute<T>::type* __restrict__ Ktw,
     const typename Compute<T>::type* __restrict__ Xw, const float* __restrict__ Gw,
     const float* __restrict__ Dw, const float* __restrict__ S0, float* __restrict__ S_final,
-    T* __restrict__ o, T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw, int n_items) {
+    T* __restrict__ o, T* __restrict__ hst, int n_items) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   typedef AccOrder<CT> AO;
@@ -108,16 +109,14 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
   // (row c16 of a 16-row tile; tile index and buffer enter as constants)
   // (16-bit: the eight values are the 16-byte piece 4 p + g of the row, the
   // columns being stored in accumulator order)
-  int rw[NSD], rk[NSC], rm[NSC];
+  int rw[NSD], rk[NSC];
 #pragma unroll
   for (int p = 0; p < NSD; ++p)
     rw[p] = KS == 4 ? TW::at(c16, 16 * (p >> 2) + g4 + (p & 3)) : TW::at(c16, 32 * p + 8 * g);
 #pragma unroll
-  for (int p = 0; p < NSC; ++p) {
+  for (int p = 0; p < NSC; ++p)
     rk[p] = KS == 4 ? TKt::at(c16, 16 * (p >> 2) + g4 + (p & 3)) : TKt::at(c16, 32 * p + 8 * g);
-    rm[p] = TM::at(c16, p * KS + (KS == 4 ? g : 8 * g));
-  }
-  // K^T and P rows both hold CHUNK elements, so rk addresses P as well
+  // K^T, M and P rows all hold CHUNK elements, so rk addresses M and P too
 
   // ---- chunk c's operands into buffer B (value rows past a sequence end
   // re-read its last row)
@@ -131,7 +130,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     const int Lc = rem < CHUNK ? (int)rem : CHUNK;
     const int64_t ch = (int64_t)c * Hv + h, ck_ = (int64_t)c * Hk + kh;
     copy_tile<TW, NW>(B.W, Ww + ch * CHUNK * D, cl, wave);
-    copy_tile<TW, NW>(B.X, Xw + ck_ * CHUNK * D, cl, wave);
+    if constexpr (MODE == 0) copy_tile<TW, NW>(B.X, Xw + ck_ * CHUNK * D, cl, wave);
     copy_tile<TKt, NW>(B.Kt, Ktw + ck_ * D * CHUNK, cl, wave);
     copy_tile<TM, NW>(B.M, Mw + ch * CHUNK * CHUNK, cl, wave);
     if constexpr (MODE == 0) copy_tile<TM, NW>(B.P, Pw + ch * CHUNK * CHUNK, cl, wave);
@@ -179,7 +178,8 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
           store_elem<T>(rs, hb + (uint32_t)((16 * kt + i) * D * sizeof(T)), S[kt][i]);
     }
 
-    // Delta = W (-S^T) + M V
+    // Delta = W (-S^T) + M V; V is gathered in accumulator order, as M's
+    // columns are stored
     floatx4 Dl[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -192,10 +192,11 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
 #pragma unroll
       for (int p = 0; p < NSC; ++p) {
         if constexpr (KS == 4) {
-          bv[p] = to_f(B.V[TV::at(p * KS + g, vcol)]);
+          bv[p] = to_f(B.V[TV::at(16 * (p >> 2) + g4 + (p & 3), vcol)]);
         } else {
 #pragma unroll
-          for (int j = 0; j < NV; ++j) bv[p][j] = (CT)to_f(B.V[TV::at(p * KS + 8 * g + j, vcol)]);
+          for (int j = 0; j < NV; ++j)
+            bv[p][j] = (CT)to_f(B.V[TV::at(32 * p + 16 * (j >> 2) + g4 + (j & 3), vcol)]);
         }
       }
 #pragma unroll
@@ -203,19 +204,21 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
 #pragma unroll
         for (int p = 0; p < NSC; ++p) {
           frag ma;
-          if constexpr (KS == 4) ma = B.M[16 * tt * CHUNK + rm[p]];
-          else ma = *reinterpret_cast<const frag*>(B.M + 16 * tt * CHUNK + rm[p]);
+          if constexpr (KS == 4) ma = B.M[16 * tt * CHUNK + rk[p]];
+          else ma = *reinterpret_cast<const frag*>(B.M + 16 * tt * CHUNK + rk[p]);
           Dl[tt] = MM::mma(ma, bv[p], Dl[tt]);
         }
     }
 
-    // X (-S^T): Q (MODE 0) or K (MODE 1) rows
+    // Q (-S^T) (MODE 0)
     floatx4 xs[4];
+    if constexpr (MODE == 0) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      xs[tt] = zero4();
+      for (int tt = 0; tt < 4; ++tt) {
+        xs[tt] = zero4();
 #pragma unroll
-      for (int p = 0; p < NSD; ++p) xs[tt] = MM::mma(arow(B.X, rw[p], 16 * tt * D), sbn[p], xs[tt]);
+        for (int p = 0; p < NSD; ++p) xs[tt] = MM::mma(arow(B.X, rw[p], 16 * tt * D), sbn[p], xs[tt]);
+      }
     }
 
     // state update: S^T <- Gam_L S^T + K^T diag(dec) Delta
@@ -260,23 +263,6 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
         for (int i = 0; i < 4; ++i)
           store_elem<T>(rs, so + (uint32_t)(16 * tt + i) * rowb, ov[i] - scale * gv[i] * xs[tt][i]);
       }
-    } else {
-      // R = V - diag(Gam) K S^T and Delta
-      // rows past the sequence end fall outside the buffers: dropped
-      const auto rr = buffer_of(Rw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
-      const auto rd = buffer_of(Dlw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
-        const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * tt + g4 + i;
-          const uint32_t off = so + (uint32_t)(16 * tt + i) * rowb;
-          store_elem<T>(rr, off, to_f(B.V[TV::at(t, vcol)]) + gv[i] * xs[tt][i]);
-          store_elem<T>(rd, off, Dl[tt][i]);
-        }
-      }
     }
   };
 
@@ -293,7 +279,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     }
   }
 
-  if (MODE == 0 && S_final) {
+  if (S_final) {
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -316,9 +302,9 @@ static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, fl
   hipLaunchKernelGGL(kern, dim3(n_items), dim3(64 * NW), 0, st, (const T*)v, ldv, cu,
                      (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
                      (const CT*)(ws + Ly.mw), (const CT*)(ws + Ly.pw), (const CT*)(ws + Ly.ww),
-                     (const CT*)(ws + Ly.ktw), (const CT*)(ws + (MODE == 0 ? Ly.q16w : Ly.k16w)),
+                     (const CT*)(ws + Ly.ktw), (const CT*)(ws + Ly.q16w),
                      (const float*)(ws + Ly.gw), (const float*)(ws + Ly.dw), S0, S_final, (T*)o,
-                     (T*)(ws + Ly.h), (T*)(ws + Ly.rw), (T*)(ws + Ly.dlw), n_items);
+                     (T*)(ws + Ly.h), n_items);
   return hipGetLastError();
 }
 
@@ -338,28 +324,29 @@ hipError_t launch_chunk_fwd_states_save(const gdn_shape& s, const void* q, const
                                         const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
                                         float scale, const float* S0, float* S_final,
                                         const int32_t* cu, void* o, void* ws, hipStream_t st) {
-  // the forward pass, then the pass that stores the backward's states (two
-  // launches over the same staged operands measured faster than one kernel
-  // doing both, which runs out of registers and LDS)
+  // the sequential pass stores the chunk-start states; R, Delta and O then
+  // follow chunk by chunk in parallel
   const ChunkLayout Ly = chunk_layout(s);
-  return dispatch_chunk(s, [&](auto c) {
+  hipError_t e = dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
-    constexpr int D = decltype(c)::d;
-    hipError_t e = chunk_state<T, D, 0>(s, v, ldv, scale, S0, S_final, cu, o, Ly, (char*)ws, st);
-    if (e != hipSuccess) return e;
-    return chunk_state<T, D, 1>(s, v, ldv, scale, S0, nullptr, cu, nullptr, Ly, (char*)ws, st);
+    return chunk_state<T, decltype(c)::d, 1>(s, v, ldv, scale, S0, S_final, cu, nullptr, Ly,
+                                             (char*)ws, st);
   });
+  if (e != hipSuccess) return e;
+  return launch_chunk_outputs(s, q, k, v, ldq, ldk, ldv, scale, cu, o, ws, st);
 }
 
 hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
                                    int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                    const float* S0, const int32_t* cu, void* ws, hipStream_t st) {
   const ChunkLayout Ly = chunk_layout(s);
-  return dispatch_chunk(s, [&](auto c) {
+  hipError_t e = dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
     return chunk_state<T, decltype(c)::d, 1>(s, v, ldv, scale, S0, nullptr, cu, nullptr, Ly,
                                              (char*)ws, st);
   });
+  if (e != hipSuccess) return e;
+  return launch_chunk_outputs(s, q, k, v, ldq, ldk, ldv, scale, cu, nullptr, ws, st);
 }
 
 }  // namespace gdn

@@ -69,6 +69,10 @@ hipError_t launch_chunk_fwd_states_save(const gdn_shape& s, const void* q, const
                                         const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
                                         float scale, const float* S0, float* S_final,
                                         const int32_t* cu, void* o, void* ws, hipStream_t st);
+// R, Delta (and O when o is given) from the saved chunk-start states
+hipError_t launch_chunk_outputs(const gdn_shape& s, const void* q, const void* k, const void* v,
+                                int64_t ldq, int64_t ldk, int64_t ldv, float scale,
+                                const int32_t* cu, void* o, void* ws, hipStream_t st);
 hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
                                    int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                    const float* S0, const int32_t* cu, void* ws, hipStream_t st);

@@ -146,8 +146,8 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
  * workspace).  Each phase reads what the previous phases left in `ws`, so
  * they must run in this order on one stream with the same shape, inputs and
  * workspace; gdn_chunk_fwd / gdn_chunk_bwd are exactly these sequences.
- * Besides letting a caller time or schedule the phases separately, every
- * phase after gdn_chunk_prepare is a single kernel launch.
+ * Besides letting a caller time or schedule the phases separately, each
+ * phase after gdn_chunk_prepare is one or two kernel launches.
  *   forward : gdn_chunk_prepare -> gdn_chunk_fwd_states
  *   backward: gdn_chunk_prepare_bwd -> gdn_chunk_bwd_states -> gdn_chunk_bwd_reverse
  *             -> gdn_chunk_bwd_grads
@@ -157,14 +157,16 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
  * gdn_chunk_prepare_bwd: the same, plus the transposed operands the reverse
  *   phase reads (backward workspace size).
  * gdn_chunk_fwd_states: sequential pass over chunks; writes o, S_final.
- * gdn_chunk_fwd_states_save: the same after gdn_chunk_prepare_bwd, also
- *   storing the chunk-start states, R and Delta in the (backward-size)
- *   workspace, i.e. what gdn_chunk_bwd_states would recompute (two kernel
- *   launches: the forward pass, then the state pass).  A training
- *   step can then run its backward as gdn_chunk_bwd_reverse ->
- *   gdn_chunk_bwd_grads on that workspace (same inputs, workspace untouched
- *   in between), skipping the preparation and the state pass.
- * gdn_chunk_bwd_states: same pass, storing chunk-start states and R, Delta.
+ * gdn_chunk_fwd_states_save: the same result after gdn_chunk_prepare_bwd,
+ *   also leaving in the (backward-size) workspace what gdn_chunk_bwd_states
+ *   would recompute.  Two kernel launches: a sequential pass that stores
+ *   the chunk-start states (and S_final), then a chunk-parallel pass that
+ *   forms R, Delta and o from them.  A training step can then run its
+ *   backward as gdn_chunk_bwd_reverse -> gdn_chunk_bwd_grads on that
+ *   workspace (same inputs, workspace untouched in between), skipping the
+ *   preparation and the state pass.
+ * gdn_chunk_bwd_states: the same two launches without o: chunk-start
+ *   states, R and Delta.
  * gdn_chunk_bwd_reverse: reverse pass over chunks; writes dv, dS0 and the
  *   chunk-end state gradients.
  * gdn_chunk_bwd_grads: chunk-parallel gradients; writes dq, dk, dg, dbeta
