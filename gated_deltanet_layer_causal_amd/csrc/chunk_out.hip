@@ -9,23 +9,32 @@
 // so these products leave the chunk-to-chunk chain and run with one
 // workgroup per (chunk, value head).
 //
-// Wave w owns value columns [32 w, 32 w + 32) for every token of the chunk.
-// R and Delta then stay in MFMA accumulators and enter the next product as
-// its B operand in accumulator order (M and P are stored with their columns
-// in that order, acc_col).  S^T is the B operand of K S^T and Q S^T: the wave
-// copies its d_k x 32 slice of S into its own LDS rows (padded so that the
-// four lane groups of a column read hit different banks) and gathers each
-// lane's reduction values from it.  K and Q rows are read straight from the
-// conv output with range-checked buffer loads, which return zero for rows
-// past the chunk's end.
+// Wave (vq, th) owns value columns [32 vq, 32 vq + 32) for tokens
+// [32 th, 32 th + 32) and forms the transposed products
+//   R^T = V^T - S K^T diag(Gam),  Delta^T = R^T M^T,
+//   O^T = S (scale Q)^T diag(Gam) + Delta^T P^T,
+// whose MFMA output tiles give each lane four consecutive value columns of
+// one token: every output leaves in 8-byte pieces, and V comes in the same
+// way.  S is the A operand of the first products: the two waves of a value
+// quarter copy its d_k x 32 slice of S (stored [k][v]) into LDS rows and
+// each gathers its lanes' k values from it.  R^T and Delta^T, A operands of
+// the products over all tokens, pass between the two token halves through a
+// padded LDS tile per value quarter; their gather follows the accumulator
+// order in which M and P store their columns (acc_col), so the B operands
+// (rows of K, Q, M, P) are plain 16-byte reads.  Every input a phase needs is
+// requested before the phase that precedes it, so load latencies overlap.
+// Rows of K, Q and V come straight from the conv output through
+// range-checked buffer loads, which return zero past the chunk's end.
 #include "chunk_stream.h"
 
 namespace gdn {
 
-template <typename T, int D> struct alignas(16) OutWave {
-  static constexpr int LDR = 32 + (sizeof(T) == 2 ? 2 : 1);   // padded row of 32 columns
-  T hs[D][LDR];       // S^T slice: row k, value column
-  T vs[CHUNK][LDR];   // V slice: row t, value column
+template <typename T, int D> struct alignas(16) OutQuarter {
+  typedef typename Compute<T>::type CT;
+  static constexpr int LDH = 32 + (sizeof(T) == 2 ? 2 : 1);    // S rows: groups 8 rows apart
+  static constexpr int LDX = 32 + (sizeof(CT) == 2 ? 4 : 2);   // R, Delta rows: groups 4 apart
+  T hs[D][LDH];        // S^T slice: row k, value column
+  CT xs[CHUNK][LDX];   // R, then Delta (compute type): row t, value column
 };
 
 // 32-bit words of the LDS slices: written as words, read as elements, so the
@@ -41,8 +50,32 @@ __device__ __forceinline__ typename Mma<T>::frag buffer_frag(__amdgpu_buffer_rsr
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
 }
 
+// Four consecutive elements of type T as floats / from floats, through a
+// range-checked buffer (8 bytes for 16-bit types, 16 for fp32).
+template <typename T>
+__device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    return floatx4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                   __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+  } else {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_t off, floatx4 x) {
+  if constexpr (sizeof(T) == 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = {pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+  } else {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
+  }
+}
+
 template <typename T, int D, bool WITH_O>
-__global__ void __launch_bounds__(2 * D) chunk_out_kernel(
+__global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_out_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t ldq,
     int64_t ldk, int64_t ldv, const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off,
     int n_seq, int Hv, int G, float scale, const typename Compute<T>::type* __restrict__ Mw,
@@ -51,18 +84,21 @@ __global__ void __launch_bounds__(2 * D) chunk_out_kernel(
     int n_items) {
   typedef typename Compute<T>::type CT;
   typedef Mma<T> MS;     // products with S (storage-type operands)
-  typedef Mma<CT> MC;    // products with R and Delta (accumulator order)
-  typedef AccOrder<CT> AO;
-  typedef OutWave<T, D> OW;
+  typedef Mma<CT> MC;    // products over tokens (compute type)
+  typedef OutQuarter<T, D> OQ;
+  typedef typename MS::frag sfrag;
+  typedef typename MC::frag cfrag;
   constexpr int KS = MS::KS;
   static_assert(Mma<CT>::KS == KS, "both operand types step alike");
-  constexpr int NW = D / 32;
+  constexpr int NQ = D / 32;                  // value quarters (of 32 columns)
   constexpr int NSD = D / KS, NSC = CHUNK / KS;
   constexpr int EPP = 16 / (int)sizeof(T), PPR = 32 / EPP;   // 16-byte pieces per 32-column row
-  __shared__ OW wv[NW];
+  constexpr int NH = D * PPR / 128;           // S pieces per lane (two waves per slice)
+  __shared__ OQ qs[NQ];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vq = wave % NQ, th = wave / NQ;
   const int item = xcd_item(blockIdx.x, n_items);
   const int64_t c = item / Hv;
   const int h = item % Hv, kh = h / G;
@@ -71,152 +107,200 @@ __global__ void __launch_bounds__(2 * D) chunk_out_kernel(
   int L;
   chunk_span(seq_off, cu, n_seq, c, t0, L);
   const int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
-  const int v0 = 32 * wave;
+  const int v0 = 32 * vq;
   const int64_t ch = c * Hv + h, HvD = (int64_t)Hv * D;
-  OW& W = wv[wave];
+  OQ& Q4 = qs[vq];
+  const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
+  const float* gam = Gw + ch * CHUNK;
+  const CT* Mc = Mw + ch * CHUNK * CHUNK;
+  const CT* Pc = Pw + ch * CHUNK * CHUNK;
 
-  // ---- the wave's slices of S^T and V into its LDS rows
+  // token tile j of this wave (j = 0, 1)
+  auto tok = [&](int j) { return 16 * (2 * th + j); };
+  // B operand of step p from token row r of X (K or Q rows): rows past the
+  // chunk end read zero
+  auto x_frag = [&](__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int r, int p) __attribute__((always_inline)) {
+    return buffer_frag<T>(rs, (uint32_t)r * ldb + (uint32_t)(p * KS + (KS == 4 ? g : 8 * g)) * sizeof(T));
+  };
+  // B operand of accumulator-order step p from token row r of a 64 x 64
+  // operand stored with its columns in accumulator order (M, P)
+  auto acc_row = [&](const CT* base, int r, int p) __attribute__((always_inline)) {
+    const CT* rp = base + r * CHUNK;
+    if constexpr (KS == 4) return rp[16 * (p >> 2) + g4 + (p & 3)];
+    else return *reinterpret_cast<const cfrag*>(rp + 32 * p + 8 * g);
+  };
+
+  // ---- inputs of R and Delta, all requested up front
+  uint4 hraw[NH];
   {
     const T* Sg = hst + ch * D * D + v0;
 #pragma unroll
-    for (int j = 0; j < D * PPR / 64; ++j) {
-      const int i = lane + 64 * j, r = i / PPR, pc = i % PPR;
-      const uint4 x = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * D + pc * EPP);
-      word_alias* d = reinterpret_cast<word_alias*>(&W.hs[r][pc * EPP]);
-      d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+    for (int j = 0; j < NH; ++j) {
+      const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
+      hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * D + pc * EPP);
     }
+  }
+  const uint32_t ldkb = (uint32_t)(ldk * sizeof(T)), ldqb = (uint32_t)(ldq * sizeof(T));
+  const auto rk = buffer_of(k + t0 * ldk + (int64_t)kh * D, (uint32_t)L * ldkb);
+  const auto rq = buffer_of(q + t0 * ldq + (int64_t)kh * D, (uint32_t)L * ldqb);
+  sfrag kb[2][NSD];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int p = 0; p < NSD; ++p) kb[j][p] = x_frag(rk, ldkb, tok(j) + c16, p);
+  floatx4 vv[2][2];
+  {
     const uint32_t ldb = (uint32_t)(ldv * sizeof(T));
     const auto rs = buffer_of(v + t0 * ldv + (int64_t)h * D + v0, (uint32_t)L * ldb);
 #pragma unroll
-    for (int j = 0; j < CHUNK * PPR / 64; ++j) {
-      const int i = lane + 64 * j, r = i / PPR, pc = i % PPR;
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)r * ldb + 16u * pc, 0, 0);
-      word_alias* d = reinterpret_cast<word_alias*>(&W.vs[r][pc * EPP]);
-      d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt)
+        vv[vt][j] = buffer_load4<T>(rs, (uint32_t)(tok(j) + c16) * ldb +
+                                            (uint32_t)((16 * vt + g4) * sizeof(T)));
   }
-  // S^T as B operands: column 16 vt + c16 of the slice, reduction index
-  // p KS + (8 g + j | g)
-  typename MS::frag sb[2][NSD];
+  float gm[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) gm[j] = gam[tok(j) + c16];
+  cfrag mb[2][NSC];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int p = 0; p < NSC; ++p) mb[j][p] = acc_row(Mc, tok(j) + c16, p);
+  issue_fence();
+
+  // ---- the quarter's slice of S^T into LDS; S (rows v = 16 vt + c16 of the
+  // slice) as A operands, reduction index p KS + (8 g + j | g)
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
+    word_alias* d = reinterpret_cast<word_alias*>(&Q4.hs[r][pc * EPP]);
+    d[0] = hraw[j].x; d[1] = hraw[j].y; d[2] = hraw[j].z; d[3] = hraw[j].w;
+  }
+  __syncthreads();
+  sfrag sa[2][NSD];
 #pragma unroll
   for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
     for (int p = 0; p < NSD; ++p) {
       if constexpr (KS == 4) {
-        sb[vt][p] = W.hs[p * KS + g][16 * vt + c16];
+        sa[vt][p] = Q4.hs[p * KS + g][16 * vt + c16];
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sb[vt][p][j] = W.hs[p * KS + 8 * g + j][16 * vt + c16];
+        for (int j = 0; j < 8; ++j) sa[vt][p][j] = Q4.hs[p * KS + 8 * g + j][16 * vt + c16];
       }
     }
 
-  // X S^T for the token rows of X (K or Q), rows past the chunk end zero
-  auto rows_times_st = [&](const T* X, int64_t ldx, floatx4 (&acc)[2][4]) __attribute__((always_inline)) {
-    const uint32_t ldb = (uint32_t)(ldx * sizeof(T));
-    const auto rs = buffer_of(X + t0 * ldx + (int64_t)kh * D, (uint32_t)L * ldb);
+  // A operand (rows v = 16 vt + c16) of accumulator-order step p from the
+  // quarter's transposed tile
+  auto xs_frag = [&](int vt, int p) __attribute__((always_inline)) {
+    const int col = 16 * vt + c16;
+    if constexpr (KS == 4) {
+      return (cfrag)Q4.xs[16 * (p >> 2) + g4 + (p & 3)][col];
+    } else {
+      cfrag f;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      typename MS::frag a[NSD];
-#pragma unroll
-      for (int p = 0; p < NSD; ++p)
-        a[p] = buffer_frag<T>(rs, (uint32_t)(16 * tt + c16) * ldb +
-                                      (uint32_t)(p * KS + (KS == 4 ? g : 8 * g)) * sizeof(T));
-#pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
-        acc[vt][tt] = zero4();
-#pragma unroll
-        for (int p = 0; p < NSD; ++p) acc[vt][tt] = MS::mma(a[p], sb[vt][p], acc[vt][tt]);
-      }
+      for (int j = 0; j < 8; ++j) f[j] = Q4.xs[32 * p + 16 * (j >> 2) + g4 + (j & 3)][col];
+      return f;
     }
   };
-  // A operand of accumulator-order step p from row 16 tt + c16 of a 64 x 64
-  // operand stored with its columns in accumulator order
-  auto acc_row = [&](const CT* base, int tt, int p) __attribute__((always_inline)) {
-    const CT* r = base + (16 * tt + c16) * CHUNK;
-    if constexpr (KS == 4) return r[16 * (p >> 2) + g4 + (p & 3)];
-    else return *reinterpret_cast<const typename MC::frag*>(r + 32 * p + 8 * g);
-  };
-
-  const float4* gam4 = reinterpret_cast<const float4*>(Gw + ch * CHUNK);
-  const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-  const uint32_t so = (uint32_t)(((int64_t)g4 * HvD + v0 + c16) * sizeof(T));
-
-  // ---- R = V - diag(Gam) K S^T
-  floatx4 R[2][4];
-  rows_times_st(k, ldk, R);
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const float4 gm = gam4[4 * tt + g];
-    const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+  // this wave's transposed tiles into the quarter's tile (four consecutive
+  // value columns per lane)
+  auto put_xs = [&](const floatx4 (&x)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        R[vt][tt][i] = to_f(W.vs[16 * tt + g4 + i][16 * vt + c16]) - gv[i] * R[vt][tt][i];
-  }
-  // rows past the chunk end fall outside the store buffers: dropped
-  const auto rr = buffer_of(Rw + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
+      for (int j = 0; j < 2; ++j) store4(&Q4.xs[tok(j) + c16][16 * vt + g4], x[vt][j][0],
+                                         x[vt][j][1], x[vt][j][2], x[vt][j][3]);
+  };
+  // byte offset of this lane's four value columns in token row c16
+  const uint32_t so = (uint32_t)(((int64_t)c16 * HvD + v0 + g4) * sizeof(T));
+  auto put_out = [&](T* base, const floatx4 (&x)[2][2]) __attribute__((always_inline)) {
+    // rows past the chunk end fall outside the buffer: dropped
+    const auto rs = buffer_of(base + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt)
+    for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store_elem<T>(rr, so + (uint32_t)(16 * tt + i) * rowb + 16u * vt * sizeof(T), R[vt][tt][i]);
+      for (int j = 0; j < 2; ++j)
+        buffer_store4<T>(rs, so + (uint32_t)tok(j) * rowb + (uint32_t)(16 * vt * sizeof(T)), x[vt][j]);
+  };
 
-  // ---- Delta = M R
-  const CT* Mc = Mw + ch * CHUNK * CHUNK;
-  floatx4 Dl[2][4];
+  // ---- R^T = V^T - S K^T diag(Gam): x[vt][j] holds value rows
+  // 16 vt + 4 g + i of token column tok(j) + c16
+  floatx4 R[2][2];
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt) {
-    typename MC::frag rb[NSC];
-#pragma unroll
-    for (int p = 0; p < NSC; ++p) rb[p] = AO::from_acc(R[vt], p);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      Dl[vt][tt] = zero4();
-#pragma unroll
-      for (int p = 0; p < NSC; ++p) Dl[vt][tt] = MC::mma(acc_row(Mc, tt, p), rb[p], Dl[vt][tt]);
-    }
-  }
-  const auto rd = buffer_of(Dlw + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
-#pragma unroll
-  for (int vt = 0; vt < 2; ++vt)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store_elem<T>(rd, so + (uint32_t)(16 * tt + i) * rowb + 16u * vt * sizeof(T), Dl[vt][tt][i]);
-
-  if constexpr (WITH_O) {
-    // ---- O = diag(Gam) scale Q S^T + P Delta
-    floatx4 O[2][4];
-    rows_times_st(q, ldq, O);
-    const CT* Pc = Pw + ch * CHUNK * CHUNK;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int vt = 0; vt < 2; ++vt) {
-      typename MC::frag db[NSC];
+      floatx4 acc = zero4();
 #pragma unroll
-      for (int p = 0; p < NSC; ++p) db[p] = AO::from_acc(Dl[vt], p);
+      for (int p = 0; p < NSD; ++p) acc = MS::mma(sa[vt][p], kb[j][p], acc);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const float4 gm = gam4[4 * tt + g];
-        const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
-        floatx4 pd = zero4();
-#pragma unroll
-        for (int p = 0; p < NSC; ++p) pd = MC::mma(acc_row(Pc, tt, p), db[p], pd);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[vt][tt][i] = pd[i] + scale * gv[i] * O[vt][tt][i];
-      }
+      for (int i = 0; i < 4; ++i) R[vt][j][i] = vv[vt][j][i] - gm[j] * acc[i];
     }
-    const auto ro = buffer_of(o + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
+  put_out(Rw, R);
+  put_xs(R);
+  __syncthreads();
+
+  // ---- Delta^T = R^T M^T
+  floatx4 Dl[2][2];
+  {
+    cfrag ra[2][NSC];
 #pragma unroll
     for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int p = 0; p < NSC; ++p) ra[vt][p] = xs_frag(vt, p);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store_elem<T>(ro, so + (uint32_t)(16 * tt + i) * rowb + 16u * vt * sizeof(T), O[vt][tt][i]);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt) {
+        Dl[vt][j] = zero4();
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) Dl[vt][j] = MC::mma(ra[vt][p], mb[j][p], Dl[vt][j]);
+      }
+  }
+  // Q and P for O, once K's and M's registers are free
+  sfrag qb[2][NSD];
+  cfrag pb[2][NSC];
+  if constexpr (WITH_O) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int p = 0; p < NSD; ++p) qb[j][p] = x_frag(rq, ldqb, tok(j) + c16, p);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) pb[j][p] = acc_row(Pc, tok(j) + c16, p);
+    issue_fence();
+  }
+  put_out(Dlw, Dl);
+
+  if constexpr (WITH_O) {
+    __syncthreads();   // both token halves have read R
+    put_xs(Dl);
+    __syncthreads();
+    // ---- O^T = S (scale Q)^T diag(Gam) + Delta^T P^T
+    cfrag da[2][NSC];
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) da[vt][p] = xs_frag(vt, p);
+    floatx4 O[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float sg = scale * gm[j];
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt) {
+        floatx4 sq = zero4(), pd = zero4();
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) sq = MS::mma(sa[vt][p], qb[j][p], sq);
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) pd = MC::mma(da[vt][p], pb[j][p], pd);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[vt][j][i] = pd[i] + sg * sq[i];
+      }
+    }
+    put_out(o, O);
   }
 }
 
@@ -233,7 +317,7 @@ hipError_t launch_chunk_outputs(const gdn_shape& s, const void* q, const void* k
     typedef typename Compute<T>::type CT;
     const int n_items = (int)(Ly.nt_max * s.hv);
     auto kern = o ? chunk_out_kernel<T, D, true> : chunk_out_kernel<T, D, false>;
-    hipLaunchKernelGGL(kern, dim3(n_items), dim3(2 * D), 0, st, (const T*)q, (const T*)k,
+    hipLaunchKernelGGL(kern, dim3(n_items), dim3(4 * D), 0, st, (const T*)q, (const T*)k,
                        (const T*)v, ldq, ldk, ldv, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
                        s.hv, s.hv / s.hk, scale, (const CT*)(ws + Ly.mw), (const CT*)(ws + Ly.pw),
                        (const float*)(ws + Ly.gw), (const T*)(ws + Ly.h), (T*)(ws + Ly.rw),

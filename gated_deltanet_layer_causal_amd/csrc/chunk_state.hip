@@ -145,10 +145,29 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
         copy_to_lds(rs, B.V + (j * NW + wave) * 64 * TV::EPP, off, 0);
       }
     }
-    if (wave == 0 && lane < 16) {   // Gam and dec, 64 floats each
-      copy_to_lds(buffer_of(Gw + ch * CHUNK, CHUNK * 4), B.G, 16u * lane, 0);
-      copy_to_lds(buffer_of(Dw + ch * CHUNK, CHUNK * 4), B.Dc, 16u * lane, 0);
+    // Gam and dec, 64 floats each: one copy per wave with two waves, so that
+    // every wave issues the same number of copies
+    if (lane < 16) {
+      if (wave == 0) copy_to_lds(buffer_of(Gw + ch * CHUNK, CHUNK * 4), B.G, 16u * lane, 0);
+      if (wave == NW - 1) copy_to_lds(buffer_of(Dw + ch * CHUNK, CHUNK * 4), B.Dc, 16u * lane, 0);
     }
+  };
+  // copies a wave issues per fetch, and stores per chunk (MODE 1)
+  constexpr int NCOPY = TW::PIECES / THREADS * (MODE == 0 ? 2 : 1) + TKt::PIECES / THREADS +
+                        TM::PIECES / THREADS * (MODE == 0 ? 2 : 1) + TV::PIECES / THREADS +
+                        (NW == 1 ? 2 : 1);
+  constexpr int NSTORE = NKT * 4;
+  static_assert(NW <= 2, "gate-factor copies are split over at most two waves");
+
+  // chunk-start state, [d_k][d_v] per (chunk, head) (MODE 1)
+  auto store_state = [&](int64_t c) __attribute__((always_inline)) {
+    const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
+    const uint32_t hb = (uint32_t)((g4 * D + vcol) * sizeof(T));
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_elem<T>(rs, hb + (uint32_t)((16 * kt + i) * D * sizeof(T)), S[kt][i]);
   };
 
   // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).
@@ -167,16 +186,6 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     frag sbn[NSD];
 #pragma unroll
     for (int p = 0; p < NSD; ++p) sbn[p] = -AO::from_acc(S, p);
-    if constexpr (MODE == 1) {
-      // chunk-start state, [d_k][d_v] per (chunk, head)
-      const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
-      const uint32_t hb = (uint32_t)((g4 * D + vcol) * sizeof(T));
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store_elem<T>(rs, hb + (uint32_t)((16 * kt + i) * D * sizeof(T)), S[kt][i]);
-    }
 
     // Delta = W (-S^T) + M V; V is gathered in accumulator order, as M's
     // columns are stored
@@ -266,16 +275,47 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     }
   };
 
-  if (c_begin < c_end) fetch(bufA, c_begin);
-  __syncthreads();
-  for (int64_t c = c_begin; c < c_end; c += 2) {
-    fetch(bufB, c + 1 < c_end ? c + 1 : c);   // a repeat of chunk c at the end
-    compute(bufA, c);
-    __syncthreads();   // waits for this wave's copies; then every wave's are visible
-    if (c + 1 < c_end) {
-      fetch(bufA, c + 2 < c_end ? c + 2 : c + 1);
-      compute(bufB, c + 1);
-      __syncthreads();
+  if constexpr (MODE == 0) {
+    // two buffers: the next chunk's copies are in flight while a chunk
+    // computes
+    if (c_begin < c_end) fetch(bufA, c_begin);
+    __syncthreads();
+    for (int64_t c = c_begin; c < c_end; c += 2) {
+      fetch(bufB, c + 1 < c_end ? c + 1 : c);   // a repeat of chunk c at the end
+      compute(bufA, c);
+      __syncthreads();   // waits for this wave's copies; then every wave's are visible
+      if (c + 1 < c_end) {
+        fetch(bufA, c + 2 < c_end ? c + 2 : c + 1);
+        compute(bufB, c + 1);
+        __syncthreads();
+      }
+    }
+  } else {
+    // three buffers: the copies run two chunks ahead.  A step issues the
+    // chunk's state stores, then the copies for chunk c + 2, then computes
+    // chunk c; it ends once this wave's copies for chunk c + 1 (issued a step
+    // earlier, followed by exactly NSTORE stores and NCOPY copies) are done,
+    // and a barrier makes every wave's visible.  Past the end the last chunk
+    // is copied again, so every step issues the same operations.
+    __shared__ SB bufC;
+    auto last = [&](int64_t x) { return x < c_end ? x : c_end - 1; };
+    auto step = [&](const SB& cur, SB& ahead, int64_t c) __attribute__((always_inline)) {
+      store_state(c);
+      fetch(ahead, last(c + 2));
+      compute(cur, c);
+      wait_vm_barrier<NSTORE + NCOPY>();
+    };
+    if (c_begin < c_end) {
+      fetch(bufA, c_begin);
+      fetch(bufB, last(c_begin + 1));
+    }
+    wait_vm_barrier<NCOPY>();
+    for (int64_t c = c_begin; c < c_end; c += 3) {
+      step(bufA, bufC, c);
+      if (c + 1 >= c_end) break;
+      step(bufB, bufA, c + 1);
+      if (c + 2 >= c_end) break;
+      step(bufC, bufB, c + 2);
     }
   }
 

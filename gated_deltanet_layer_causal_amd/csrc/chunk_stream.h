@@ -88,6 +88,16 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, uint32_t v
   }
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order) and all its LDS operations are done, then
+// meet the workgroup at a barrier.  Unlike __syncthreads() it leaves the
+// newest N operations (copies still streaming ahead) in flight; as an asm
+// statement with a memory clobber no memory access moves across it.
+template <int N> __device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Per-lane source offsets of direct copies: copy J of a tile with RP pieces
 // per row reads 1024 J + lane_pattern; the pattern depends only on RP (and on
 // J mod 4 when RP = 16).  With copy J = j NW + wave, the RP = 16 pattern of
