@@ -33,7 +33,7 @@ MULTI_KERNEL_CALLS = ("chunk_fwd_states", "chunk_prepare", "chunk_prepare_b", "c
 # HIP sources of the kernel behind each single-kernel call (HBM traffic taken
 # from committed counter summaries is used only while these are unchanged)
 KERNEL_SOURCES = {
-    "chunk_bwd_grads": ["chunk_bwd.hip", "chunk_common.h", "common.h", "launch.h"],
+    "chunk_bwd_grads": ["chunk_grad.hip", "chunk_stream.h", "chunk_common.h", "common.h", "launch.h"],
     "chunk_bwd_reverse": ["chunk_rev.hip", "chunk_stream.h", "chunk_common.h", "common.h",
                           "launch.h"],
     "conv_fwd": ["conv.hip", "common.h", "launch.h"],

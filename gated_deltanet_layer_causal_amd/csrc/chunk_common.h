@@ -61,7 +61,7 @@ struct ChunkLayout {
   size_t gw, dw;      // fp32 [nt_max][hv][64]: Gam_t and dec_t (clamped to the chunk length)
   size_t kb, ktb, qtb; // T [nt_max][hk]: K rows [64][dk], K^T and Q^T [dk][64] (backward)
   size_t ptb, mtb;    // T [nt_max][hv][64][64]: P^T, M^T (backward)
-  size_t tiw;         // fp32 [nt_max][hv][64][64]: Tinv (backward)
+  size_t tib;         // T [nt_max][hv][2][64][64]: Tinv (columns in accumulator order), Tinv^T (backward)
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
   size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
   size_t sink;        // SINK_ELEMS scratch floats: target of stores for padding rows
@@ -102,7 +102,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.qtb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.ptb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.mtb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
-  L.tiw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
+  L.tib = off; off = align256(off + es * (size_t)L.nt_max * s.hv * 2 * CHUNK * CHUNK);
   L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.dh = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.rw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);

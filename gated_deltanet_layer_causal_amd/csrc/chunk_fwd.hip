@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
     float* __restrict__ Gw, float* __restrict__ Dw,
     T* __restrict__ Kb, T* __restrict__ Ktb, T* __restrict__ Qtb, T* __restrict__ Ptb,
-    T* __restrict__ Mtb, float* __restrict__ Tiw) {
+    T* __restrict__ Mtb, T* __restrict__ Tib) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -192,10 +192,16 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
              ti.z * sm.bet[s4 + 2], ti.w * sm.bet[s4 + 3]);
     }
     if constexpr (BWD) {
-      // Tinv (fp32) for the chunk gradients
-      float4* to = reinterpret_cast<float4*>(Tiw + ((int64_t)c * Hv + h) * CHUNK * CHUNK);
-      for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256)
-        to[i] = *reinterpret_cast<const float4*>(&sm.Ti[i / (CHUNK / 4)][(i % (CHUNK / 4)) * 4]);
+      // Tinv in the storage type for the chunk gradients: rows t with the
+      // columns in accumulator order, then Tinv^T (rows u, natural order)
+      T* to = Tib + ((int64_t)c * Hv + h) * 2 * CHUNK * CHUNK;
+      for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
+        const int r = i / (CHUNK / 4), c4 = (i % (CHUNK / 4)) * 4;
+        const float4 ti = *reinterpret_cast<const float4*>(&sm.Ti[r][c4]);
+        store4(to + r * CHUNK + acc_col<T>(c4), ti.x, ti.y, ti.z, ti.w);
+        store4(to + CHUNK * CHUNK + r * CHUNK + c4, sm.Ti[c4][r], sm.Ti[c4 + 1][r], sm.Ti[c4 + 2][r],
+               sm.Ti[c4 + 3][r]);
+      }
       // M^T in the storage type, columns (tokens t) in accumulator order
       T* mo = Mtb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
       for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
@@ -267,7 +273,7 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        (float*)(ws + Ly.dw), BWD ? (T*)(ws + Ly.kb) : nullptr,
                        BWD ? (T*)(ws + Ly.ktb) : nullptr, BWD ? (T*)(ws + Ly.qtb) : nullptr,
                        BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (T*)(ws + Ly.mtb) : nullptr,
-                       BWD ? (float*)(ws + Ly.tiw) : nullptr);
+                       BWD ? (T*)(ws + Ly.tib) : nullptr);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,631 @@
+// Chunked gated delta rule, backward: the chunk-parallel gradients.
+//
+// Per chunk (notation of chunk_common.h), given dO, the reverse pass's dR
+// (= dv) and dDelta, the saved states S (entering the chunk) and dS' (the
+// gradient of the state leaving it), and R, Delta of the forward:
+//   dM = dDelta R^T,  dTinv = strictly-lower(dM diag(beta)),
+//   Y  = dTinv Tinv^T,  dA = strictly-lower(-Tinv^T Y),  dP = lower(dO Delta^T)
+//   WA = dA o (beta_t D),  WS = WA + WA^T  (symmetric)
+//   dq = scale [diag(Gam) dO S + (dP o D) K]
+//   dk = scale (dP o D)^T Q - diag(Gam) dR S + diag(dec) Delta dS' + WS K
+//   dbeta_s = sum_t dM[t,s] Tinv[t,s] + sum_u dA[s,u] D[s,u] k_s.k_u
+// and dg from every place gam enters, assembled without cancellation (the
+// last phase below).
+//
+// One workgroup of eight waves per (chunk, key head) walks the G value heads
+// of the group and sums dq, dk over them in registers (ascending head
+// order, no atomics).  Per head:
+//  - the token-major tiles dO, Delta, dR, R come into LDS by direct copies
+//    (issued while the previous head finishes);
+//  - phase A, pair products, as 64 x 64 tiles whose columns are a token t
+//    and rows the other token s (every lane holds four consecutive s of one
+//    t; waves w and w + 4 own the same 16 tokens t).  Waves 0-3 take the
+//    Tinv chain: dM^T, dTinv^T (kept in the accumulators and used from
+//    there as an A operand, accumulator order), Y (crossing waves once,
+//    through LDS), dA^T, and with them WA, the dA part of the pair terms of
+//    dg and dbeta.  Waves 4-7 take dP (both orientations), dP o D and the
+//    dP part of the pair terms.  The element-wise work needs no exchange;
+//  - phase B, token x key products: wave w owns 16 key columns of dq^T and
+//    dk^T (k x t tiles: four consecutive k of one token per lane, stored in
+//    8-byte pieces at the end).  The products with S and dS' take the
+//    wave's rows of the saved states as A operands; those with dP o D, its
+//    transpose and WS read LDS tiles written in phase A with their columns
+//    in accumulator order, matching K^T and Q^T from the preparation.
+// All MFMAs run on the storage type (bf16 operands for bf16 data, fp32 for
+// fp32 data).
+#include <type_traits>
+
+#include "chunk_stream.h"
+
+namespace gdn {
+
+template <typename T, int D> struct GradLds {
+  typedef Tile<T, CHUNK, D> TT;                               // token-major tile
+  static constexpr int LDP = CHUNK + 16 / (int)sizeof(T);     // padded 64-wide rows
+  static constexpr int NKT = D / 16;                          // key tiles (phase-B waves per token group)
+  T tO[TT::PIECES * TT::EPP];     // dO
+  T tDl[TT::PIECES * TT::EPP];    // Delta
+  T tdR[TT::PIECES * TT::EPP];    // dR
+  T tR[TT::PIECES * TT::EPP];     // R
+  T YT[CHUNK][LDP];               // Y^T: row s, column u
+  T dPD[CHUNK][LDP];              // dP o D: row t, columns s in accumulator order
+  T dPDt[CHUNK][LDP];             // scale (dP o D)^T: row s, columns t in accumulator order
+  T WA[CHUNK][LDP];               // WA: row t, column s
+  T WS[CHUNK][LDP];               // WA + WA^T: row x, columns u in accumulator order
+  float E[CHUNK][CHUNK + 1];      // pair terms of dg
+  // Tinv (columns in accumulator order) and Tinv^T, copied for 16-bit types
+  // (fp32 reads them from memory where used: the LDS holds no more)
+  static constexpr bool TIN_LDS = sizeof(T) == 2;
+  typedef Tile<T, CHUNK, CHUNK> TI;
+  T Tin[TIN_LDS ? 2 * CHUNK * CHUNK : 8];
+  double gam[CHUNK];
+  float bet[CHUNK], Gm[CHUNK], dc[CHUNK];
+  float colB[4][CHUNK], rowB[CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
+  float segE[4][CHUNK], boxE[4][CHUNK], red[8];
+};
+
+// Four consecutive elements as floats (8 bytes for 16-bit types).
+template <typename E> __device__ __forceinline__ floatx4 ld4(const E* p) {
+  if constexpr (sizeof(E) == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    return floatx4{v.x, v.y, v.z, v.w};
+  } else {
+    typedef E e4 __attribute__((ext_vector_type(4)));
+    const e4 v = *reinterpret_cast<const e4*>(p);
+    return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G,
+    float scale, const double* __restrict__ gcum, const float* __restrict__ beta,
+    const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ Tib,
+    const T* __restrict__ Ktb, const T* __restrict__ Qtb, const T* __restrict__ hst,
+    const T* __restrict__ dhst, const T* __restrict__ Rw, const T* __restrict__ Dlw,
+    const T* __restrict__ ddw, const T* __restrict__ dout, const T* __restrict__ dvo,
+    int64_t lddv, T* __restrict__ dq, T* __restrict__ dk, int64_t lddq, int64_t lddk,
+    float* __restrict__ dg, float* __restrict__ dbeta) {
+  typedef typename Compute<T>::type CT;
+  typedef Mma<T> MM;
+  typedef AccOrder<T> AO;
+  typedef typename MM::frag frag;
+  typedef GradLds<T, D> GL;
+  typedef typename GL::TT TT;
+  constexpr int KS = MM::KS;
+  constexpr int NSD = D / KS, NSC = CHUNK / KS;
+  constexpr int NKT = GL::NKT;            // phase B: key tiles; 8 / NKT token groups
+  constexpr int TTW = 4 * NKT / 8;        // phase B: token tiles per wave
+  static_assert(D == 32 || D == 128, "head dim 32 or 128");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  GL& sm = *reinterpret_cast<GL*>(smem_raw);
+
+  // Indices derived from the thread and wave numbers are recomputed at the
+  // top of every head (from laundered copies, below), so that the compiler
+  // does not hoist the addresses and masks built on them out of the loop
+  // as loop invariants, where they would be spilled.
+  int tid = threadIdx.x, lane = tid & 63;
+  int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
+  const int64_t c = blockIdx.x;
+  const int kh = blockIdx.y;
+  if (c >= seq_off[n_seq]) return;
+  int64_t t0;
+  int L;
+  chunk_span(seq_off, cu, n_seq, c, t0, L);
+  const int64_t HvD = (int64_t)Hv * D;
+  const int Hk = Hv / G;
+  int role = wave >> 2;                     // phase A: 0 Tinv chain, 1 dP side
+  int tw = wave & 3, tl = 16 * tw + c16;    // phase A: this lane's token
+  int kt = wave % NKT, tg = wave / NKT;     // phase B: key tile, token group
+  auto derive = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(tid));
+    asm volatile("" : "+s"(wave));
+    lane = tid & 63;
+    g = lane >> 4;
+    g4 = 4 * g;
+    c16 = lane & 15;
+    role = wave >> 2;
+    tw = wave & 3;
+    tl = 16 * tw + c16;
+    kt = wave % NKT;
+    tg = wave / NKT;
+  };
+
+  // element offset, in an operand row, of this lane's values for step p:
+  // natural order (both operands stored alike) ...
+  auto pcol = [&](int p) { return KS == 4 ? 4 * p + g : 32 * p + 8 * g; };
+  // ... or the accumulator order of AO::from_acc (the other operand stored
+  // with its columns in accumulator order)
+  auto acol = [&](int p) { return KS == 4 ? 16 * (p >> 2) + g4 + (p & 3) : 32 * p + 8 * g; };
+  auto rdf = [&](const T* rowp, int col) __attribute__((always_inline)) -> frag {
+    if constexpr (KS == 4) return rowp[col];
+    else return *reinterpret_cast<const frag*>(rowp + col);
+  };
+  // token-tile operand: row r, step p
+  auto tfr = [&](const T* tile, int r, int p) __attribute__((always_inline)) -> frag {
+    return rdf(tile, TT::at(r, pcol(p)));
+  };
+
+  // ---- per workgroup: k_s . k_t at the phase-A positions (Tinv-chain
+  // waves), the wave's row of K^T and Q^T tiles (phase-B A operands), and
+  // q, k at the phase-B positions
+  floatx4 kk[4];
+  if (role == 0) {
+    const uint32_t ldb = (uint32_t)(ldk * sizeof(T));
+    const auto rk = buffer_of(k + t0 * ldk + (int64_t)kh * D, (uint32_t)L * ldb);
+    frag kb[NSD];
+#pragma unroll
+    for (int p = 0; p < NSD; ++p) kb[p] = buffer_frag<T>(rk, (uint32_t)tl * ldb + (uint32_t)pcol(p) * sizeof(T));
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      kk[st] = zero4();
+#pragma unroll
+      for (int p = 0; p < NSD; ++p)
+        kk[st] = MM::mma(buffer_frag<T>(rk, (uint32_t)(16 * st + c16) * ldb + (uint32_t)pcol(p) * sizeof(T)),
+                         kb[p], kk[st]);
+    }
+  }
+  frag kta[NSC], qta[NSC];
+  {
+    const int64_t r = ((int64_t)c * Hk + kh) * D * CHUNK + (int64_t)(16 * kt + c16) * CHUNK;
+#pragma unroll
+    for (int p = 0; p < NSC; ++p) {
+      kta[p] = rdf(Ktb + r, pcol(p));
+      qta[p] = rdf(Qtb + r, pcol(p));
+    }
+  }
+  // (raw storage-type values, converted where used)
+  typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type raw4;
+  raw4 q4[TTW], k4[TTW];
+  auto raw_f4 = [&](const raw4& r) __attribute__((always_inline)) -> floatx4 {
+    if constexpr (sizeof(T) == 2)
+      return floatx4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+    else
+      return __builtin_bit_cast(floatx4, r);
+  };
+  {
+    const uint32_t ldkb = (uint32_t)(ldk * sizeof(T)), ldqb = (uint32_t)(ldq * sizeof(T));
+    const auto rk = buffer_of(k + t0 * ldk + (int64_t)kh * D, (uint32_t)L * ldkb);
+    const auto rq = buffer_of(q + t0 * ldq + (int64_t)kh * D, (uint32_t)L * ldqb);
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt) {
+      const int t = 16 * (tg * TTW + tt) + c16, kc = 16 * kt + g4;
+      if constexpr (sizeof(T) == 2) {
+        q4[tt] = __builtin_bit_cast(raw4, __builtin_amdgcn_raw_buffer_load_b64(rq, (uint32_t)t * ldqb + (uint32_t)kc * 2, 0, 0));
+        k4[tt] = __builtin_bit_cast(raw4, __builtin_amdgcn_raw_buffer_load_b64(rk, (uint32_t)t * ldkb + (uint32_t)kc * 2, 0, 0));
+      } else {
+        q4[tt] = __builtin_bit_cast(raw4, __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)t * ldqb + (uint32_t)kc * 4, 0, 0));
+        k4[tt] = __builtin_bit_cast(raw4, __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)t * ldkb + (uint32_t)kc * 4, 0, 0));
+      }
+    }
+  }
+  floatx4 dQa[TTW], dKa[TTW];
+#pragma unroll
+  for (int tt = 0; tt < TTW; ++tt) dQa[tt] = dKa[tt] = zero4();
+
+  // ---- per head: the token tiles (direct copies by the first NCW waves,
+  // rows past the chunk end re-read its last row) ...
+  constexpr int NCW = TT::PIECES / 64 < 8 ? TT::PIECES / 64 : 8;
+  auto copy_rows = [&](T* dst, const T* src, uint32_t ldb) __attribute__((always_inline)) {
+    if (wave < NCW) {
+      const auto rs = buffer_of(src, (uint32_t)L * ldb);
+#pragma unroll
+      for (int j = 0; j < TT::PIECES / (64 * NCW); ++j) {
+        const int s = (j * NCW + wave) * 64 + lane, r = s / TT::RP;
+        const uint32_t off = (uint32_t)(r < L ? r : L - 1) * ldb + (uint32_t)((s % TT::RP) ^ TT::swz(r)) * 16u;
+        copy_to_lds(rs, dst + (j * NCW + wave) * 64 * TT::EPP, off, 0);
+      }
+    }
+  };
+  auto copy_head = [&](int h) __attribute__((always_inline)) {
+    const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
+    const int64_t base = t0 * HvD + (int64_t)h * D;
+    copy_rows(sm.tO, dout + base, rowb);
+    copy_rows(sm.tDl, Dlw + base, rowb);
+    copy_rows(sm.tR, Rw + base, rowb);
+    copy_rows(sm.tdR, dvo + t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)));
+  };
+  // ... the gate values ...
+  auto load_gates = [&](int h) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const double gm = gcum[(t0 + (lane < L ? lane : L - 1)) * Hv + h];
+      sm.gam[lane] = gm;
+      sm.bet[lane] = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
+      // gam is flat past the chunk length, so these are the factors of
+      // token min(t, L - 1)
+      const double glast = __shfl(gm, CHUNK - 1, 64);
+      sm.Gm[lane] = dexp<T>(gm);
+      sm.dc[lane] = dexp<T>(glast - gm);
+    }
+  };
+  // ... Tinv and Tinv^T (16-bit types: into LDS, by direct copies) ...
+  typedef typename GL::TI TI;
+  auto copy_tinv = [&](int h) __attribute__((always_inline)) {
+    if constexpr (GL::TIN_LDS) {
+      const char* src = reinterpret_cast<const char*>(Tib + (c * Hv + h) * 2 * CHUNK * CHUNK);
+#pragma unroll
+      for (int j = 0; j < 2 * TI::PIECES / 512; ++j) {
+        const int s = (j * 8 + wave) * 64 + lane, r = s / TI::RP;   // r: row of both matrices
+        const uint32_t off = (uint32_t)(r * TI::RP + ((s % TI::RP) ^ TI::swz(r))) * 16u;
+        copy_to_lds(buffer_of(src, 2 * CHUNK * CHUNK * sizeof(T)), sm.Tin + (j * 8 + wave) * 64 * TI::EPP, off, 0);
+      }
+    }
+  };
+  // element (r, col) of Tinv (m = 0, columns in accumulator order) or Tinv^T (m = 1)
+  auto tin = [&](int h, int m, int r, int col) __attribute__((always_inline)) -> const T* {
+    if constexpr (GL::TIN_LDS) return sm.Tin + m * CHUNK * CHUNK + TI::at(r, col);
+    else return Tib + (c * Hv + h) * 2 * CHUNK * CHUNK + m * CHUNK * CHUNK + r * CHUNK + col;
+  };
+  // ... the Tinv-chain waves' rows of dDelta ...
+  frag ddB[NSD];
+  auto load_tinv = [&](int h) __attribute__((always_inline)) {
+    const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
+    const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
+#pragma unroll
+    for (int p = 0; p < NSD; ++p) ddB[p] = buffer_frag<T>(rs, (uint32_t)tl * rowb + (uint32_t)pcol(p) * sizeof(T));
+  };
+  // ... the dP-side waves' P values ...
+  floatx4 pE[4];
+  auto load_p = [&](int h) __attribute__((always_inline)) {
+    const CT* Pc = Pw + (c * Hv + h) * CHUNK * CHUNK + tl * CHUNK;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) pE[st] = ld4(Pc + acc_col<CT>(16 * st + g4));
+  };
+  // ... and every wave's rows of the saved states (phase B)
+  frag hA[NSD], dhA[NSD];
+  auto load_states = [&](int h) __attribute__((always_inline)) {
+    const int64_t r = (c * Hv + h) * D * D + (int64_t)(16 * kt + c16) * D;
+#pragma unroll
+    for (int p = 0; p < NSD; ++p) {
+      hA[p] = rdf(hst + r, pcol(p));
+      dhA[p] = rdf(dhst + r, pcol(p));
+    }
+  };
+  auto load_a = [&](int h) __attribute__((always_inline)) {
+    if (role == 0) load_tinv(h);
+    else load_p(h);
+  };
+
+  copy_head(kh * G);
+  copy_tinv(kh * G);
+  load_gates(kh * G);
+
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = kh * G + hh;
+    derive();
+    load_a(h);
+    issue_fence();
+    __syncthreads();   // this head's tiles, gates and phase-A operands are in
+    // =============== phase A: pair products (s x t tiles, t = tl)
+    const double gt = sm.gam[tl];
+    const float bt = sm.bet[tl];
+    floatx4 ep[4];
+    if (role == 0) {
+      // dM^T = R dDelta^T
+      floatx4 dMt[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        dMt[st] = zero4();
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) dMt[st] = MM::mma(tfr(sm.tR, 16 * st + c16, p), ddB[p], dMt[st]);
+      }
+      // the first dbeta term summed over t (the 16 lanes of a group: lane
+      // c16 of group g keeps the sum for s = 16 (c16 / 4) + 4 g + c16 % 4);
+      // then dTinv^T in place of dM^T
+      float cbm = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float4 bs = *reinterpret_cast<const float4*>(&sm.bet[16 * st + g4]);
+        const float bsv[4] = {bs.x, bs.y, bs.z, bs.w};
+        const floatx4 te = ld4(tin(h, 0, tl, acc_col<T>(16 * st + g4)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * st + g4 + i;
+          const float cb = lane_group_sum<16>(dMt[st][i] * te[i]);
+          cbm = c16 == 4 * st + i ? cb : cbm;
+          dMt[st][i] = s < tl ? dMt[st][i] * bsv[i] : 0.f;
+        }
+      }
+      sm.colB[tw][16 * (c16 >> 2) + g4 + (c16 & 3)] = cbm;
+      // Y = dTinv Tinv^T for tokens t of this wave (A from the accumulators),
+      // into Y^T rows
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        floatx4 y = zero4();
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) y = MM::mma(AO::from_acc(dMt, p), rdf(tin(h, 0, 16 * st + c16, acol(p)), 0), y);
+        store4(&sm.YT[16 * st + c16][16 * tw + g4], y[0], y[1], y[2], y[3]);
+      }
+    } else {
+      // dP^T = Delta dO^T and dP = dO Delta^T
+      floatx4 dPt[4], dPn[4];
+      {
+        frag ob[NSD];
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) ob[p] = tfr(sm.tO, tl, p);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          dPt[st] = dPn[st] = zero4();
+#pragma unroll
+          for (int p = 0; p < NSD; ++p) {
+            const frag da = tfr(sm.tDl, 16 * st + c16, p);
+            dPt[st] = MM::mma(da, ob[p], dPt[st]);
+            dPn[st] = MM::mma(ob[p], da, dPn[st]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // dP o D (rows t), the dP part of the pair terms (added to E once the
+      // Tinv-chain waves have written theirs)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float pd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * st + g4 + i;
+          const float Dts = s <= tl ? dexp<T>(gt - sm.gam[s]) : 0.f;
+          ep[st][i] = (s < tl && tl < L) ? dPt[st][i] * pE[st][i] : 0.f;
+          pd[i] = dPt[st][i] * Dts;
+        }
+        store4(&sm.dPD[tl][acc_col<T>(16 * st + g4)], pd[0], pd[1], pd[2], pd[3]);
+      }
+      // scale (dP o D)^T from the dP tiles: rows t = 16 tw + 4 g + i, column s
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int s = 16 * st + c16;
+        const double gs = sm.gam[s];
+        float pd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * tw + g4 + i;
+          pd[i] = s <= t ? scale * dPn[st][i] * dexp<T>(sm.gam[t] - gs) : 0.f;
+        }
+        store4(&sm.dPDt[s][acc_col<T>(16 * tw + g4)], pd[0], pd[1], pd[2], pd[3]);
+      }
+    }
+    load_states(h);
+    issue_fence();
+    __syncthreads();   // Y^T is complete
+    if (role == 0) {
+      // dA^T = -Y^T Tinv (rows s, column t = tl), then WA, the dA part of the
+      // pair terms and the second dbeta term
+      float rb = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        floatx4 da = zero4();
+#pragma unroll
+        for (int p = 0; p < NSC; ++p)
+          da = MM::mma(rdf(&sm.YT[16 * st + c16][0], pcol(p)), rdf(tin(h, 1, tl, pcol(p)), 0), da);
+        float wa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * st + g4 + i;
+          const bool lower = s < tl;
+          const float Dts = lower ? dexp<T>(gt - sm.gam[s]) : 0.f;
+          const float dA = lower ? -da[i] : 0.f;
+          const float dAD = dA * Dts;
+          sm.E[tl][s] = tl < L ? dAD * bt * kk[st][i] : 0.f;
+          rb += dAD * kk[st][i];
+          wa[i] = dAD * bt;
+        }
+        store4(&sm.WA[tl][16 * st + g4], wa[0], wa[1], wa[2], wa[3]);
+      }
+      rb += __shfl_xor(rb, 16, 64);
+      rb += __shfl_xor(rb, 32, 64);
+      if (g == 0) sm.rowB[tl] = rb;
+    }
+    __syncthreads();
+    if (role == 1) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.E[tl][16 * st + g4 + i] += ep[st][i];
+    }
+    // WS = WA + WA^T (columns in accumulator order)
+#pragma unroll
+    for (int j = 0; j < CHUNK * CHUNK / 4 / 512; ++j) {
+      const int it = tid + 512 * j, x = it / (CHUNK / 4), u4 = (it % (CHUNK / 4)) * 4;
+      const floatx4 a = ld4(&sm.WA[x][u4]);
+      store4(&sm.WS[x][acc_col<T>(u4)], a[0] + to_f(sm.WA[u4][x]), a[1] + to_f(sm.WA[u4 + 1][x]),
+             a[2] + to_f(sm.WA[u4 + 2][x]), a[3] + to_f(sm.WA[u4 + 3][x]));
+    }
+    __syncthreads();
+
+    // =============== phase B: token x key products (k x t tiles)
+    {
+      float ipv = 0.f;
+      if (tg == 0) {
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) {
+          if constexpr (KS == 4) {
+            ipv += to_f(hA[p]) * to_f(dhA[p]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ipv += (float)hA[p][j] * (float)dhA[p][j];
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < TTW; ++tt) {
+        const int t = 16 * (tg * TTW + tt) + c16;
+        floatx4 x1 = zero4(), x2 = zero4(), x3 = zero4();
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) {
+          x1 = MM::mma(hA[p], tfr(sm.tO, t, p), x1);
+          x2 = MM::mma(hA[p], tfr(sm.tdR, t, p), x2);
+          x3 = MM::mma(dhA[p], tfr(sm.tDl, t, p), x3);
+        }
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) {
+          dQa[tt] = MM::mma(kta[p], rdf(&sm.dPD[t][0], pcol(p)), dQa[tt]);
+          dKa[tt] = MM::mma(qta[p], rdf(&sm.dPDt[t][0], pcol(p)), dKa[tt]);
+          dKa[tt] = MM::mma(kta[p], rdf(&sm.WS[t][0], pcol(p)), dKa[tt]);
+        }
+        const float Gt = sm.Gm[t], dct = sm.dc[t];
+        const floatx4 qv = raw_f4(q4[tt]), kv = raw_f4(k4[tt]);
+        float rx = 0.f, rz = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dQa[tt][i] += Gt * x1[i];
+          dKa[tt][i] += dct * x3[i] - Gt * x2[i];
+          rx += Gt * (scale * x1[i] * qv[i] - x2[i] * kv[i]);
+          rz += dct * x3[i] * kv[i];
+        }
+        rx += __shfl_xor(rx, 16, 64);
+        rx += __shfl_xor(rx, 32, 64);
+        rz += __shfl_xor(rz, 16, 64);
+        rz += __shfl_xor(rz, 32, 64);
+        if (g == 0) {
+          sm.rowX[kt][t] = rx;
+          sm.rowZ[kt][t] = rz;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // bound live ranges: one token tile at a time
+      }
+      ipv = wave_sum(ipv);
+      if (lane == 0) sm.red[wave] = ipv;
+    }
+    __syncthreads();   // the token tiles are free; every partial is in
+    if (hh + 1 < G) {
+      copy_head(h + 1);
+      copy_tinv(h + 1);
+    }
+
+    // =============== dg, dbeta (waves 0-3).  With gamma the in-chunk
+    // cumulative gate, dg_i = sum_{t >= i} dgam_t.  Three parts, each a sum
+    // of terms that all carry the decay across token i, so no large terms
+    // cancel when that decay is strong:
+    //  - pair terms E[t][s] (s < t) add to dgam_t and subtract from dgam_s;
+    //    their part of dg_i is the box sum over t >= i > s, taken as column
+    //    suffix sums over rows, then row prefix sums;
+    //  - the chunk-start terms y_t (rowX, and the state term at the last
+    //    token) enter as the suffix sum over t >= i;
+    //  - the decay-to-chunk-end terms z_t enter dgam as -z_t and as +sum z
+    //    at the last token: their part is the prefix sum over t < i.
+    if (wave < 4) {
+      // column suffix sums within each 16-row block (wave = row block)
+      const int cidx = lane, rb0 = 16 * wave;
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 15; r >= 0; --r) {
+        acc += sm.E[rb0 + r][cidx];
+        sm.E[rb0 + r][cidx] = acc;
+      }
+      sm.segE[wave][cidx] = acc;
+    }
+    __syncthreads();
+    if (wave < 4) {
+      // add the later row blocks, then the row-prefix part of each box sum
+      const int cidx = lane, rb0 = 16 * wave;
+      float off = 0.f;
+      for (int w = 3; w > wave; --w) off += sm.segE[w][cidx];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.E[rb0 + r][cidx] += off;
+    }
+    __syncthreads();
+    if (wave < 4) {
+      // token i = lane sums columns s < i of the column block owned by this wave
+      const int i = lane, cb0 = 16 * wave;
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (cb0 + s < i) part += sm.E[i][cb0 + s];
+      sm.boxE[wave][i] = part;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int t = lane;
+      float y = 0.f, db = sm.rowB[t], zt = 0.f, ips = 0.f;
+      const float box = ((sm.boxE[0][t] + sm.boxE[1][t]) + sm.boxE[2][t]) + sm.boxE[3][t];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) db += sm.colB[w][t];
+#pragma unroll
+      for (int w = 0; w < NKT; ++w) {
+        y += sm.rowX[w][t];
+        zt += sm.rowZ[w][t];
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) ips += sm.red[w];
+      if (t == L - 1) y += dexp<T>(sm.gam[CHUNK - 1]) * ips;
+      if (t >= L) { y = 0.f; zt = 0.f; }
+      const float dgs = box + wave_suffix_scan(y, lane) + (wave_incl_scan_f(zt, lane) - zt);
+      if (t < L) {
+        dg[(t0 + t) * Hv + h] = dgs;
+        dbeta[(t0 + t) * Hv + h] = db;
+      }
+    }
+    __syncthreads();   // the gates of this head are no longer read
+    if (hh + 1 < G) load_gates(h + 1);
+  }
+
+  // ---- dq = scale dQ, dk: four consecutive key columns of one token per lane
+  derive();
+  {
+    const uint32_t rq = (uint32_t)(lddq * sizeof(T)), rk = (uint32_t)(lddk * sizeof(T));
+    const auto bq = buffer_of(dq + t0 * lddq + (int64_t)kh * D, (uint32_t)L * rq);
+    const auto bk = buffer_of(dk + t0 * lddk + (int64_t)kh * D, (uint32_t)L * rk);
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt) {
+      const int t = 16 * (tg * TTW + tt) + c16, kc = 16 * kt + g4;
+      floatx4 xq = dQa[tt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xq[i] *= scale;
+      buffer_store4<T>(bq, (uint32_t)t * rq + (uint32_t)kc * sizeof(T), xq);
+      buffer_store4<T>(bk, (uint32_t)t * rk + (uint32_t)kc * sizeof(T), dKa[tt]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
+                                  int64_t ldk, const float* beta, float scale, const int32_t* cu,
+                                  const void* dout, const void* dv, int64_t lddv, void* dq,
+                                  void* dk, int64_t lddq, int64_t lddk, float* dg, float* dbeta,
+                                  void* wsv, hipStream_t st) {
+  char* ws = (char*)wsv;
+  const ChunkLayout Ly = chunk_layout(s);
+  if (Ly.nt_max == 0 || s.total_tokens == 0) return hipSuccess;
+  return dispatch_chunk(s, [&](auto cf) {
+    using T = typename decltype(cf)::type;
+    constexpr int D = decltype(cf)::d;
+    static_assert(sizeof(GradLds<T, D>) <= 160 * 1024, "gradient kernel LDS budget");
+    const size_t shm = sizeof(GradLds<T, D>);
+    auto kern = chunk_grad_kernel<T, D>;
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hipLaunchKernelGGL(kern, dim3((unsigned)Ly.nt_max, s.hk), dim3(512), shm, st, (const T*)q,
+                       (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
+                       s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), beta,
+                       (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)(ws + Ly.tib),
+                       (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb), (const T*)(ws + Ly.h),
+                       (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw), (const T*)(ws + Ly.dlw),
+                       (const T*)(ws + Ly.ddw), (const T*)dout, (const T*)dv, lddv, (T*)dq,
+                       (T*)dk, lddq, lddk, dg, dbeta);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_chunk_bwd(const gdn_shape& s, const void* q, const void* k, const void* v,
+                            int64_t ldq, int64_t ldk, int64_t ldv, const float* g,
+                            const float* beta, float scale, const float* S0, const int32_t* cu,
+                            const void* dout, const float* dS_final, void* dq, void* dk, void* dv,
+                            int64_t lddq, int64_t lddk, int64_t lddv, float* dg, float* dbeta,
+                            float* dS0, void* ws, hipStream_t st) {
+  hipError_t e = launch_chunk_prepare(s, q, k, ldq, ldk, g, beta, scale, cu, ws, true, st);
+  if (e == hipSuccess) e = launch_chunk_bwd_states(s, q, k, v, ldq, ldk, ldv, scale, S0, cu, ws, st);
+  if (e == hipSuccess)
+    e = launch_chunk_bwd_reverse(s, q, k, ldq, ldk, scale, cu, dout, dS_final, dv, lddv, dS0, ws, st);
+  if (e == hipSuccess)
+    e = launch_chunk_bwd_grads(s, q, k, ldq, ldk, beta, scale, cu, dout, dv, lddv, dq, dk, lddq,
+                               lddk, dg, dbeta, ws, st);
+  return e;
+}
+
+}  // namespace gdn

@@ -88,6 +88,39 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, uint32_t v
   }
 }
 
+// 16-byte (16-bit types) or 4-byte (fp32) MFMA operand from a buffer.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag buffer_frag(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(T) == 2)
+    return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  else
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+
+// Four consecutive elements of type T as floats / from floats, through a
+// range-checked buffer (8 bytes for 16-bit types, 16 for fp32).
+template <typename T>
+__device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    return floatx4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                   __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+  } else {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_t off, floatx4 x) {
+  if constexpr (sizeof(T) == 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = {pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+  } else {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
+  }
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (they complete in issue order) and all its LDS operations are done, then
 // meet the workgroup at a barrier.  Unlike __syncthreads() it leaves the
