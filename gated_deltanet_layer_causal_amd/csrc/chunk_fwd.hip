@@ -90,11 +90,13 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   __syncthreads();
 
   // wave w owns rows [16w, 16w+16) of the 64 x 64 products
-  floatx4 kk[4], qk[4];
+  // (and K Q^T for the P rows: P values of four consecutive s per lane)
+  floatx4 kk[4], qk[4], kq[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     kk[j] = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
     qk[j] = tile_mma<CT, true, true>(zero4(), &sm.u.Q[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
+    kq[j] = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.u.Q[0][0], LD, 16 * wave, 16 * j, D, lane);
   }
   const int rbase = 16 * wave + 4 * (lane >> 4);
   const int ccol = lane & 15;
@@ -110,18 +112,17 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       typedef CT v4 __attribute__((ext_vector_type(4)));
       const int dst = r * D + acc_col<CT>(c4);
       *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&sm.u.Q[r][c4]);
-      if constexpr (BWD) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) Kb[base + dst + u] = from_f<T>(to_f(sm.K[r][c4 + u]));
-      }
+      if constexpr (BWD)
+        store4(Kb + base + dst, to_f(sm.K[r][c4]), to_f(sm.K[r][c4 + 1]), to_f(sm.K[r][c4 + 2]),
+               to_f(sm.K[r][c4 + 3]));
     }
     if constexpr (BWD) {
       // Q^T in the storage type, columns (tokens) in accumulator order
       T* qo = Qtb + base;
       for (int i = tid; i < D * (CHUNK / 4); i += 256) {
         const int kr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) qo[kr * CHUNK + acc_col<T>(t4) + u] = from_f<T>(to_f(sm.u.Q[t4 + u][kr]));
+        store4(qo + kr * CHUNK + acc_col<T>(t4), to_f(sm.u.Q[t4][kr]), to_f(sm.u.Q[t4 + 1][kr]),
+               to_f(sm.u.Q[t4 + 2][kr]), to_f(sm.u.Q[t4 + 3][kr]));
       }
     }
   }
@@ -142,9 +143,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
           *reinterpret_cast<const v4*>(&sm.u.Kt[kr][c4]);
       if constexpr (BWD) {
-        T* kb = Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) kb[u] = from_f<T>(to_f(sm.u.Kt[kr][c4 + u]));
+        store4(Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4),
+               to_f(sm.u.Kt[kr][c4]), to_f(sm.u.Kt[kr][c4 + 1]), to_f(sm.u.Kt[kr][c4 + 2]),
+               to_f(sm.u.Kt[kr][c4 + 3]));
       }
     }
   }
@@ -167,19 +168,30 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       Dw[((int64_t)c * Hv + h) * CHUNK + lane] = dexp<T>(glast - gm);
     }
     __syncthreads();
+    // A (rows t of this wave), P^T rows s (four consecutive t per lane) and
+    // P rows t (four consecutive s per lane, from K Q^T)
     CT* Pout = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = 16 * j + ccol;
+      float pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = rbase + e;
         const float dec = dexp<T>(sm.gam[t] - sm.gam[s <= t ? s : t]);  // masked before exp
         sm.A[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
-        const float pv = (s <= t) ? dec * scale * qk[j][e] : 0.f;
-        Pout[t * CHUNK + acc_col<CT>(s)] = from_f<CT>(pv);
-        if constexpr (BWD) Ptb[((int64_t)c * Hv + h) * CHUNK * CHUNK + s * CHUNK + acc_col<T>(t)] = from_f<T>(pv);
+        pv[e] = (s <= t) ? dec * scale * qk[j][e] : 0.f;
       }
+      if constexpr (BWD)
+        store4(Ptb + ((int64_t)c * Hv + h) * CHUNK * CHUNK + s * CHUNK + acc_col<T>(rbase), pv[0],
+               pv[1], pv[2], pv[3]);
+      const int t = 16 * j + ccol;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s2 = rbase + e;
+        pv[e] = (s2 <= t) ? dexp<T>(sm.gam[t] - sm.gam[s2]) * scale * kq[j][e] : 0.f;
+      }
+      store4(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();
     invert_unit_lower(sm.A, sm.Ti, sm.X, tid);
@@ -207,8 +219,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
         const int sr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
         const float b = sm.bet[sr];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) mo[sr * CHUNK + acc_col<T>(t4) + u] = from_f<T>(sm.Ti[t4 + u][sr] * b);
+        store4(mo + sr * CHUNK + acc_col<T>(t4), sm.Ti[t4][sr] * b, sm.Ti[t4 + 1][sr] * b,
+               sm.Ti[t4 + 2][sr] * b, sm.Ti[t4 + 3][sr] * b);
       }
     }
     // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead

@@ -226,13 +226,16 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       }
     }
   };
+  // (R is read in phase A only, so it comes with Tinv, a phase earlier)
   auto copy_head = [&](int h) __attribute__((always_inline)) {
     const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
     const int64_t base = t0 * HvD + (int64_t)h * D;
     copy_rows(sm.tO, dout + base, rowb);
     copy_rows(sm.tDl, Dlw + base, rowb);
-    copy_rows(sm.tR, Rw + base, rowb);
     copy_rows(sm.tdR, dvo + t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)));
+  };
+  auto copy_r = [&](int h) __attribute__((always_inline)) {
+    copy_rows(sm.tR, Rw + t0 * HvD + (int64_t)h * D, (uint32_t)(HvD * sizeof(T)));
   };
   // ... the gate values ...
   auto load_gates = [&](int h) __attribute__((always_inline)) {
@@ -296,6 +299,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   };
 
   copy_head(kh * G);
+  copy_r(kh * G);
   copy_tinv(kh * G);
   load_gates(kh * G);
 
@@ -439,6 +443,10 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
              a[2] + to_f(sm.WA[u4 + 2][x]), a[3] + to_f(sm.WA[u4 + 3][x]));
     }
     __syncthreads();
+    if (hh + 1 < G) {   // R and Tinv are no longer read for this head
+      copy_r(h + 1);
+      copy_tinv(h + 1);
+    }
 
     // =============== phase B: token x key products (k x t tiles)
     {
@@ -488,16 +496,12 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           sm.rowX[kt][t] = rx;
           sm.rowZ[kt][t] = rz;
         }
-        __builtin_amdgcn_sched_barrier(0);   // bound live ranges: one token tile at a time
       }
       ipv = wave_sum(ipv);
       if (lane == 0) sm.red[wave] = ipv;
     }
     __syncthreads();   // the token tiles are free; every partial is in
-    if (hh + 1 < G) {
-      copy_head(h + 1);
-      copy_tinv(h + 1);
-    }
+    if (hh + 1 < G) copy_head(h + 1);
 
     // =============== dg, dbeta (waves 0-3).  With gamma the in-chunk
     // cumulative gate, dg_i = sum_{t >= i} dgam_t.  Three parts, each a sum

@@ -83,10 +83,18 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
 
   CopyLanes cl;
   cl.init(lane, wave, NW);
-  const uint32_t so = (uint32_t)(((int64_t)g4 * HvD + vcol) * sizeof(T));   // rows of ddw
   const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-  const uint32_t sv = (uint32_t)(((int64_t)g4 * lddv + vcol) * sizeof(T));  // rows of dv
   const uint32_t rowv = (uint32_t)(lddv * sizeof(T));
+  const uint32_t rowh = (uint32_t)(D * sizeof(T));
+  // paired-column stores: this lane's offsets in ddw, dv and dS' rows
+  PairStore ps;
+  ps.init(lane);
+  const uint32_t wcol = (uint32_t)(16 * wave * sizeof(T));
+  const uint32_t so = wcol + ps.lane_off<T>(lane, rowb);
+  const uint32_t sv = wcol + ps.lane_off<T>(lane, rowv);
+  const uint32_t hb = wcol + ps.lane_off<T>(lane, rowh);
+  // stores a step issues per lane: dS', dDelta, dv (two rows per tile each)
+  constexpr int NSTORE = 2 * NKT + 2 * 4 + 2 * 4;
   // LDS read offsets (as in the state pass)
   int rw[NSD], rk[NSC];
 #pragma unroll
@@ -142,12 +150,8 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
     for (int p = 0; p < NSD; ++p) sb[p] = AO::from_acc(dS, p);
     {
       const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
-      const uint32_t hb = (uint32_t)((g4 * D + vcol) * sizeof(T));
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store_elem<T>(rs, hb + (uint32_t)((16 * kt + i) * D * sizeof(T)), dS[kt][i]);
+      for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, dS[kt]);
     }
 
     // dO as B operands over the chunk index, plain and scaled by scale Gam_t
@@ -189,9 +193,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
       // rows past the sequence end fall outside the buffer: dropped
       const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_elem<T>(rs, so + (uint32_t)(16 * tt + i) * rowb, dd[tt][i]);
+      for (int tt = 0; tt < 4; ++tt) ps.store<T>(rs, so + (uint32_t)(16 * tt) * rowb, rowb, dd[tt]);
     }
 
     // dR = M^T dDelta (= dv); then -diag(Gam) dR as B operands
@@ -211,8 +213,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
         gr[tt][1] = -gm.y * dr[1];
         gr[tt][2] = -gm.z * dr[2];
         gr[tt][3] = -gm.w * dr[3];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_elem<T>(rs, sv + (uint32_t)(16 * tt + i) * rowv, dr[i]);
+        ps.store<T>(rs, sv + (uint32_t)(16 * tt) * rowv, rowv, dr);
       }
     }
 
@@ -235,16 +236,22 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
     }
   };
 
+  // A step copies the next chunk's operands, then computes (and stores)
+  // this one; it ends once this wave's copies are done, leaving the step's
+  // NSTORE stores (issued after them) in flight, and a barrier makes every
+  // wave's copies visible.
   if (c_begin < c_end) fetch(bufA, c_end - 1);
   __syncthreads();
   for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
     fetch(bufB, c - 1 >= c_begin ? c - 1 : c);   // a repeat of chunk c at the start
+    issue_fence();   // the copies stay ahead of this step's stores
     compute(bufA, c);
-    __syncthreads();   // waits for this wave's copies; then every wave's are visible
+    wait_vm_barrier<NSTORE>();
     if (c - 1 >= c_begin) {
       fetch(bufA, c - 2 >= c_begin ? c - 2 : c - 1);
+      issue_fence();
       compute(bufB, c - 1);
-      __syncthreads();
+      wait_vm_barrier<NSTORE>();
     }
   }
 

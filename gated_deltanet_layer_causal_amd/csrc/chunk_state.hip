@@ -156,18 +156,19 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
   constexpr int NCOPY = TW::PIECES / THREADS * (MODE == 0 ? 2 : 1) + TKt::PIECES / THREADS +
                         TM::PIECES / THREADS * (MODE == 0 ? 2 : 1) + TV::PIECES / THREADS +
                         (NW == 1 ? 2 : 1);
-  constexpr int NSTORE = NKT * 4;
+  constexpr int NSTORE = NKT * 2;
   static_assert(NW <= 2, "gate-factor copies are split over at most two waves");
 
   // chunk-start state, [d_k][d_v] per (chunk, head) (MODE 1)
+  // (two adjacent value columns per store)
+  PairStore ps;
+  ps.init(lane);
+  const uint32_t rowh = (uint32_t)(D * sizeof(T));
+  const uint32_t hb = (uint32_t)(16 * wave * sizeof(T)) + ps.lane_off<T>(lane, rowh);
   auto store_state = [&](int64_t c) __attribute__((always_inline)) {
     const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
-    const uint32_t hb = (uint32_t)((g4 * D + vcol) * sizeof(T));
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store_elem<T>(rs, hb + (uint32_t)((16 * kt + i) * D * sizeof(T)), S[kt][i]);
+    for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, S[kt]);
   };
 
   // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).

@@ -121,6 +121,47 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_
   }
 }
 
+// Stores of 16 x 16 MFMA accumulator tiles (lane l holds rows 4 (l / 16) + i,
+// i < 4, of column l % 16) into a row-major matrix of the storage type, two
+// adjacent columns per store: lanes l and l ^ 1 trade half their values
+// (one DPP move), so lane l writes rows 4 (l / 16) + 2 (l & 1) + {0, 1} at
+// columns (l % 16) & ~1 and + 1.  Half the store instructions of one store
+// per element.
+struct PairStore {
+  uint32_t sel0, sel1;
+  bool odd;
+  __device__ __forceinline__ void init(int lane) {
+    odd = lane & 1;
+    // byte selectors of v_perm: (own, received) halves in column order
+    sel0 = odd ? 0x01000504u : 0x05040100u;
+    sel1 = odd ? 0x03020706u : 0x07060302u;
+  }
+  // byte offset of this lane's first element relative to the tile's
+  // (row 0, column 0), for a row stride of ldb bytes
+  template <typename T> __device__ __forceinline__ uint32_t lane_off(int lane, uint32_t ldb) const {
+    return (uint32_t)(4 * (lane >> 4) + 2 * (lane & 1)) * ldb + (uint32_t)((lane & 15) & ~1) * sizeof(T);
+  }
+  template <typename T>
+  __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t ldb,
+                                        floatx4 x) const {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t p01 = pack2_bf16(x[0], x[1]), p23 = pack2_bf16(x[2], x[3]);
+      const uint32_t own = odd ? p23 : p01, send = odd ? p01 : p23;
+      const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(recv, own, sel0), rs, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(recv, own, sel1), rs, off + ldb, 0, 0);
+    } else {
+      const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
+      const float r0 = dpp_f<0xB1>(s0), r1 = dpp_f<0xB1>(s1);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 w0 = {__float_as_uint(odd ? r0 : x[0]), __float_as_uint(odd ? x[2] : r0)};
+      const u32x2 w1 = {__float_as_uint(odd ? r1 : x[1]), __float_as_uint(odd ? x[3] : r1)};
+      __builtin_amdgcn_raw_buffer_store_b64(w0, rs, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w1, rs, off + ldb, 0, 0);
+    }
+  }
+};
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (they complete in issue order) and all its LDS operations are done, then
 // meet the workgroup at a barrier.  Unlike __syncthreads() it leaves the

@@ -3,15 +3,18 @@
 //
 // HBM-bound: every x / dy element is read once and every output written once.
 // Mapping: a wave owns one run of CONV_TT consecutive tokens; each lane owns 8
-// consecutive channels (one 16-byte bf16 vector) and walks the run keeping a
-// 3-token sliding window in registers, so x is read once plus a 3-token halo
-// per run.  A q or k head of D channels spans D/8 adjacent lanes; its L2 sum
-// is a shuffle reduction over those lanes.  Four waves (four runs) share a
-// workgroup so the backward's dw partial sums are combined in LDS before
-// they go to memory; a second kernel adds the per-workgroup partials in a
-// fixed order.
-#include "common.h"
-#include "launch.h"
+// consecutive channels (one 16-byte bf16 vector).  The run is cut where
+// sequences start, and each piece is walked keeping the 4-token window in a
+// 4-slot circular buffer, four tokens per loop iteration, so the window never
+// moves between registers (token u sits in slot (u - u0) mod 4 for the
+// group's first token u0).  Rows come through range-checked buffer accesses
+// over the piece's sequence, which read zero before its start (the causal
+// zero padding) and drop stores outside it.  A q or k head of D channels
+// spans D/8 adjacent lanes; its L2 sum is a lane-group reduction.  Four
+// waves (four runs) share a workgroup so the backward's dw partial sums are
+// combined in LDS before they go to memory; a second kernel adds the
+// per-workgroup partials in a fixed order.
+#include "chunk_stream.h"
 
 namespace gdn {
 
@@ -32,13 +35,40 @@ __device__ __forceinline__ float group_sum(float x) {
   return lane_group_sum<D / 8>(x);
 }
 
+// Eight consecutive elements of row r (relative to the buffer's first row)
+// at this lane's channel offset coff (bytes); zero outside the buffer.
 template <typename T>
-__device__ __forceinline__ f8 load8_or_zero(const T* p, bool ok) {
-  if (ok) return load8(p);
-  f8 r;
+__device__ __forceinline__ f8 row8(__amdgpu_buffer_rsrc_t rs, int64_t r, uint32_t ldb, uint32_t coff) {
+  const uint32_t off = (uint32_t)r * ldb + coff;   // r < 0 wraps far past the range
+  Raw8<T> raw;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.v[i] = 0.f;
-  return r;
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i)
+    raw.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * i, 0, 0));
+  return raw_f8(raw);
+}
+template <typename T>
+__device__ __forceinline__ void put_row8(__amdgpu_buffer_rsrc_t rs, int64_t r, uint32_t ldb,
+                                         uint32_t coff, const f8& v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint32_t off = (uint32_t)r * ldb + coff;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 w = {pack2_bf16(v.v[0], v.v[1]), pack2_bf16(v.v[2], v.v[3]),
+                     pack2_bf16(v.v[4], v.v[5]), pack2_bf16(v.v[6], v.v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, 0);
+  } else {
+    const u32x4 w0 = {__float_as_uint(v.v[0]), __float_as_uint(v.v[1]), __float_as_uint(v.v[2]),
+                      __float_as_uint(v.v[3])};
+    const u32x4 w1 = {__float_as_uint(v.v[4]), __float_as_uint(v.v[5]), __float_as_uint(v.v[6]),
+                      __float_as_uint(v.v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(w0, rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(w1, rs, off + 16u, 0, 0);
+  }
+}
+// Buffer over rows [lo, hi) of a row-major tensor (row stride ldb bytes).
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_of(const T* base, int64_t ld, int64_t lo,
+                                                          int64_t hi, uint32_t ldb) {
+  return buffer_of(base + lo * ld, (uint32_t)(hi > lo ? hi - lo : 0) * ldb);
 }
 
 template <typename T, int D>
@@ -55,6 +85,9 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(const T* __restrict__ x, 
   if (tb >= T_tok) return;  // whole wave exits together
   const int64_t te = tb + CONV_TT < T_tok ? tb + CONV_TT : T_tok;
   const bool l2 = c0 < n_l2;
+  // lanes past the channels read zero and store nothing
+  const uint32_t coff = active ? (uint32_t)c0 * sizeof(T) : 0x80000000u;
+  const uint32_t ldxb = (uint32_t)(ldx * sizeof(T)), ldyb = (uint32_t)(ldy * sizeof(T));
 
   float wr[8][4];
 #pragma unroll
@@ -62,40 +95,47 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(const T* __restrict__ x, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) wr[i][j] = active ? w[(int64_t)(c0 + i) * 4 + j] : 0.f;
 
+  // pieces [a, b) of the run, one per sequence, first to last
   int n = find_seq(cu, n_seq, tb);
-  int64_t ss = cu[n], se = cu[n + 1];
-  f8 x1, x2, x3;  // x[t-1], x[t-2], x[t-3]
-  x1 = load8_or_zero(x + (tb - 1) * ldx + c0, active && tb - 1 >= ss);
-  x2 = load8_or_zero(x + (tb - 2) * ldx + c0, active && tb - 2 >= ss);
-  x3 = load8_or_zero(x + (tb - 3) * ldx + c0, active && tb - 3 >= ss);
-
-  for (int64_t t = tb; t < te; ++t) {
-    while (t >= se) {  // next sequence (skips empty ones): restart the window
-      ++n;
-      ss = cu[n];
-      se = cu[n + 1];
+  for (int64_t a = tb; a < te;) {
+    const int64_t ss = cu[n], se = cu[n + 1];
+    const int64_t b = se < te ? se : te;
+    if (b > a) {
+      const int64_t lo = a - 3 > ss ? a - 3 : ss;
+      const auto rx = rows_of(x, ldx, lo, b, ldxb);
+      const auto ry = rows_of(y, ldy, a, b, ldyb);
+      f8 xs[4];   // x[u] in slot (u - u0) mod 4
+      xs[3] = row8<T>(rx, a - 1 - lo, ldxb, coff);
+      xs[2] = row8<T>(rx, a - 2 - lo, ldxb, coff);
+      xs[1] = row8<T>(rx, a - 3 - lo, ldxb, coff);
+      for (int64_t u0 = a; u0 < b; u0 += 4) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x1.v[i] = x2.v[i] = x3.v[i] = 0.f;
-    }
-    f8 x0 = load8_or_zero(x + t * ldx + c0, active);
-    f8 a;
-    float sq = 0.f;
+        for (int m = 0; m < 4; ++m) {
+          const int64_t t = u0 + m;
+          if (t < b) {
+            xs[m] = row8<T>(rx, t - lo, ldxb, coff);
+            const f8 &x0 = xs[m], &x1 = xs[(m + 3) & 3], &x2 = xs[(m + 2) & 3], &x3 = xs[(m + 1) & 3];
+            f8 av;
+            float sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float u = wr[i][0] * x3.v[i] + wr[i][1] * x2.v[i] + wr[i][2] * x1.v[i] + wr[i][3] * x0.v[i];
-      a.v[i] = u * sigmoidf_(u);
-      sq += a.v[i] * a.v[i];
-    }
-    sq = group_sum<D>(sq);
-    if (l2) {
-      float r = rsqrtf(sq + eps);
+            for (int i = 0; i < 8; ++i) {
+              float u = wr[i][0] * x3.v[i] + wr[i][1] * x2.v[i] + wr[i][2] * x1.v[i] + wr[i][3] * x0.v[i];
+              av.v[i] = u * sigmoidf_(u);
+              sq += av.v[i] * av.v[i];
+            }
+            sq = group_sum<D>(sq);
+            if (l2) {
+              const float r = rsqrtf(sq + eps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a.v[i] *= r;
+              for (int i = 0; i < 8; ++i) av.v[i] *= r;
+            }
+            put_row8<T>(ry, t - a, ldyb, coff, av);
+          }
+        }
+      }
     }
-    if (active) store8(y + t * ldy + c0, a);
-    x3 = x2;
-    x2 = x1;
-    x1 = x0;
+    a = b > a ? b : a;
+    ++n;
   }
 }
 
@@ -143,6 +183,10 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
   const int64_t run = (int64_t)blockIdx.x * CONV_RUNS_PER_BLOCK + wave;
   const int64_t tb = run * CONV_TT;
   const int64_t te = tb + CONV_TT < T_tok ? tb + CONV_TT : T_tok;
+  // lanes past the channels read zero and store nothing
+  const uint32_t coff = active ? (uint32_t)c0 * sizeof(T) : 0x80000000u;
+  const uint32_t ldxb = (uint32_t)(ldx * sizeof(T)), ldyb = (uint32_t)(lddy * sizeof(T));
+  const uint32_t ldob = (uint32_t)(lddx * sizeof(T));
 
   float wr[8][4];
 #pragma unroll
@@ -156,67 +200,62 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
     for (int j = 0; j < 4; ++j) dwa[i][j] = 0.f;
 
   if (tb < te) {
+    // pieces [a, b) of the run, one per sequence, last to first; each is
+    // walked from its end
     int n = find_seq(cu, n_seq, te - 1);
-    int64_t ss = cu[n], se = cu[n + 1];
-    auto ldx8 = [&](int64_t t, int64_t s0) { return load8_or_zero(x + t * ldx + c0, active && t >= s0); };
-    // du at te, te+1, te+2 (the tokens after the run) when in the same sequence
-    f8 d1, d2, d3;  // du[s+1], du[s+2], du[s+3]
-    {
-      f8 h[3];
+    for (int64_t b = te; b > tb;) {
+      const int64_t ss = cu[n], se = cu[n + 1];
+      const int64_t a = ss > tb ? ss : tb;
+      if (b > a) {
+        // x rows [max(a - 3, ss), min(b + 3, se)); dy rows [a, min(b + 3, se))
+        const int64_t lo = a - 3 > ss ? a - 3 : ss, hi = b + 3 < se ? b + 3 : se;
+        const auto rx = rows_of(x, ldx, lo, hi, ldxb);
+        const auto ry = rows_of(dy, lddy, a, hi, ldyb);
+        const auto ro = rows_of(dx, lddx, a, b, ldob);
+        auto xr = [&](int64_t t) __attribute__((always_inline)) { return row8<T>(rx, t - lo, ldxb, coff); };
+        // du at b, b + 1, b + 2 (the tokens after the piece) in slots 3, 2, 1
+        f8 xs[4], ds[4];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        int64_t t = te + j;
-        bool in = t < se;  // wave-uniform
-        if (in) {
-          f8 dyv = load8_or_zero(dy + t * lddy + c0, active);
-          h[j] = conv_du<D>(wr, ldx8(t, ss), ldx8(t - 1, ss), ldx8(t - 2, ss), ldx8(t - 3, ss), dyv,
-                            l2, eps);
-        } else {
+        for (int j = 0; j < 3; ++j) {
+          const int64_t t = b + j;
+          if (t < se) {   // wave-uniform
+            ds[3 - j] = conv_du<D>(wr, xr(t), xr(t - 1), xr(t - 2), xr(t - 3),
+                                   row8<T>(ry, t - a, ldyb, coff), l2, eps);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) h[j].v[i] = 0.f;
+            for (int i = 0; i < 8; ++i) ds[3 - j].v[i] = 0.f;
+          }
+        }
+        // x[b - 1 - j] in slot j (u0 = b - 1; token u in slot (u0 - u) mod 4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[j] = xr(b - 1 - j);
+        for (int64_t u0 = b - 1; u0 >= a; u0 -= 4) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int64_t s = u0 - m;
+            if (s >= a) {
+              const f8 &x0 = xs[m], &x1 = xs[(m + 1) & 3], &x2 = xs[(m + 2) & 3], &x3 = xs[(m + 3) & 3];
+              const f8 d0 = conv_du<D>(wr, x0, x1, x2, x3, row8<T>(ry, s - a, ldyb, coff), l2, eps);
+              const f8 &d1 = ds[(m + 3) & 3], &d2 = ds[(m + 2) & 3], &d3 = ds[(m + 1) & 3];
+              f8 o;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                // x[s] feeds u[s+3-j] through tap j
+                o.v[i] = wr[i][3] * d0.v[i] + wr[i][2] * d1.v[i] + wr[i][1] * d2.v[i] + wr[i][0] * d3.v[i];
+                dwa[i][0] += d0.v[i] * x3.v[i];
+                dwa[i][1] += d0.v[i] * x2.v[i];
+                dwa[i][2] += d0.v[i] * x1.v[i];
+                dwa[i][3] += d0.v[i] * x0.v[i];
+              }
+              put_row8<T>(ro, s - a, ldob, coff, o);
+              ds[m] = d0;
+              xs[m] = xr(s - 4);
+            }
+          }
         }
       }
-      d1 = h[0];
-      d2 = h[1];
-      d3 = h[2];
-    }
-    // window for s = te-1: x[s], x[s-1], x[s-2], x[s-3]
-    int64_t s = te - 1;
-    f8 x0 = ldx8(s, ss), x1 = ldx8(s - 1, ss), x2 = ldx8(s - 2, ss), x3 = ldx8(s - 3, ss);
-    for (; s >= tb; --s) {
-      if (s < ss) {  // moved into an earlier sequence: reset both windows
-        while (s < ss) {
-          --n;
-          ss = cu[n];
-          se = cu[n + 1];
-        }
-        x0 = ldx8(s, ss);
-        x1 = ldx8(s - 1, ss);
-        x2 = ldx8(s - 2, ss);
-        x3 = ldx8(s - 3, ss);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d1.v[i] = d2.v[i] = d3.v[i] = 0.f;
-      }
-      f8 dyv = load8_or_zero(dy + s * lddy + c0, active);
-      f8 d0 = conv_du<D>(wr, x0, x1, x2, x3, dyv, l2, eps);
-      f8 o;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // x[s] feeds u[s+3-j] through tap j
-        o.v[i] = wr[i][3] * d0.v[i] + wr[i][2] * d1.v[i] + wr[i][1] * d2.v[i] + wr[i][0] * d3.v[i];
-        dwa[i][0] += d0.v[i] * x3.v[i];
-        dwa[i][1] += d0.v[i] * x2.v[i];
-        dwa[i][2] += d0.v[i] * x1.v[i];
-        dwa[i][3] += d0.v[i] * x0.v[i];
-      }
-      if (active) store8(dx + s * lddx + c0, o);
-      d3 = d2;
-      d2 = d1;
-      d1 = d0;
-      x0 = x1;
-      x1 = x2;
-      x2 = x3;
-      x3 = ldx8(s - 4, ss);
+      b = a;
+      --n;
     }
   }
   // combine the four runs of this block in a fixed order
