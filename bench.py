@@ -119,7 +119,7 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     if name == "chunk_bwd_reverse":
         return "mfma", hv * (6 * d * d + 4 * C64 * d)
     if name == "chunk_bwd_grads":
-        return "mfma", hv * (6 * d * d + 12 * C64 * d + 4 * C64 * C64) + hk * 4 * C64 * d
+        return "mfma", hv * (6 * d * d + 12 * C64 * d + 4 * C64 * C64) + hk * 2 * C64 * d
     raise KeyError(name)
 
 
