@@ -103,15 +103,15 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   const int r16 = lane & 15;
   {
     // Q rows (compute type, zero past the chunk end, columns in accumulator
-    // order) to the workspace, in 4-element pieces; K rows in the storage
-    // type (backward)
+    // order; read only by the forward pass without saved states) to the
+    // workspace, in 4-element pieces; K rows in the storage type (backward)
     constexpr int PR = D / 4;
     const int64_t base = ((int64_t)c * (Hv / G) + kh) * CHUNK * D;
     for (int i = tid; i < CHUNK * PR; i += 256) {
       const int r = i / PR, c4 = (i % PR) * 4;
       typedef CT v4 __attribute__((ext_vector_type(4)));
       const int dst = r * D + acc_col<CT>(c4);
-      *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&sm.u.Q[r][c4]);
+      if constexpr (!BWD) *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&sm.u.Q[r][c4]);
       if constexpr (BWD)
         store4(Kb + base + dst, to_f(sm.K[r][c4]), to_f(sm.K[r][c4 + 1]), to_f(sm.K[r][c4 + 2]),
                to_f(sm.K[r][c4 + 3]));

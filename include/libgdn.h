@@ -154,8 +154,10 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
  * gdn_chunk_prepare: chunk table from cu_seqlens; per (chunk, value head)
  *   the in-chunk gate sums and the WY/UT factors M = (I + A)^-1 diag(beta)
  *   and P (masked decayed scale * Q K^T), A = strictly-lower(beta D K K^T).
- * gdn_chunk_prepare_bwd: the same, plus the transposed operands the reverse
- *   phase reads (backward workspace size).
+ * gdn_chunk_prepare_bwd: the same factors, plus the transposed operands the
+ *   reverse and gradient phases read (backward workspace size); it leaves out
+ *   the Q rows only gdn_chunk_fwd_states reads, so it is followed by
+ *   gdn_chunk_fwd_states_save or gdn_chunk_bwd_states, not gdn_chunk_fwd_states.
  * gdn_chunk_fwd_states: sequential pass over chunks; writes o, S_final.
  * gdn_chunk_fwd_states_save: the same result after gdn_chunk_prepare_bwd,
  *   also leaving in the (backward-size) workspace what gdn_chunk_bwd_states
