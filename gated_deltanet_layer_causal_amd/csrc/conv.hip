@@ -19,11 +19,16 @@
 namespace gdn {
 
 // Sequence containing token t: largest n with cu[n] <= t (cu non-decreasing).
+// Called with wave-uniform t; the result and the bounds read from cu are
+// made uniform explicitly so the row buffers built from them sit in scalar
+// registers (a per-lane buffer descriptor turns each access into a loop over
+// the distinct descriptors of the wave).
+__device__ __forceinline__ int32_t uniform_i32(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int find_seq(const int32_t* cu, int n_seq, int64_t t) {
   int lo = 0, hi = n_seq - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)cu[mid] <= t) lo = mid;
+    if ((int64_t)uniform_i32(cu[mid]) <= t) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -36,15 +41,21 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // Eight consecutive elements of row r (relative to the buffer's first row)
-// at this lane's channel offset coff (bytes); zero outside the buffer.
+// at this lane's channel offset coff (bytes), as stored; zero outside the
+// buffer.
 template <typename T>
-__device__ __forceinline__ f8 row8(__amdgpu_buffer_rsrc_t rs, int64_t r, uint32_t ldb, uint32_t coff) {
+__device__ __forceinline__ Raw8<T> raw_row8(__amdgpu_buffer_rsrc_t rs, int64_t r, uint32_t ldb,
+                                            uint32_t coff) {
   const uint32_t off = (uint32_t)r * ldb + coff;   // r < 0 wraps far past the range
   Raw8<T> raw;
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(T) / 2); ++i)
     raw.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * i, 0, 0));
-  return raw_f8(raw);
+  return raw;
+}
+template <typename T>
+__device__ __forceinline__ f8 row8(__amdgpu_buffer_rsrc_t rs, int64_t r, uint32_t ldb, uint32_t coff) {
+  return raw_f8(raw_row8<T>(rs, r, ldb, coff));
 }
 template <typename T>
 __device__ __forceinline__ void put_row8(__amdgpu_buffer_rsrc_t rs, int64_t r, uint32_t ldb,
@@ -77,7 +88,7 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(const T* __restrict__ x, 
                                                        const int32_t* __restrict__ cu, int n_seq,
                                                        int64_t T_tok, int C, int n_l2, float eps,
                                                        T* __restrict__ y, int64_t ldy) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   const bool active = c0 < C;
   const int64_t run = (int64_t)blockIdx.x * CONV_RUNS_PER_BLOCK + wave;
@@ -98,41 +109,49 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(const T* __restrict__ x, 
   // pieces [a, b) of the run, one per sequence, first to last
   int n = find_seq(cu, n_seq, tb);
   for (int64_t a = tb; a < te;) {
-    const int64_t ss = cu[n], se = cu[n + 1];
+    const int64_t ss = uniform_i32(cu[n]), se = uniform_i32(cu[n + 1]);
     const int64_t b = se < te ? se : te;
     if (b > a) {
       const int64_t lo = a - 3 > ss ? a - 3 : ss;
       const auto rx = rows_of(x, ldx, lo, b, ldxb);
       const auto ry = rows_of(y, ldy, a, b, ldyb);
-      f8 xs[4];   // x[u] in slot (u - u0) mod 4
+      f8 xs[4];        // x[u] in slot (u - u0) mod 4
+      Raw8<T> px[4];   // x[u + 4] in slot (u - u0) mod 4: rows load a group ahead
       xs[3] = row8<T>(rx, a - 1 - lo, ldxb, coff);
       xs[2] = row8<T>(rx, a - 2 - lo, ldxb, coff);
       xs[1] = row8<T>(rx, a - 3 - lo, ldxb, coff);
-      for (int64_t u0 = a; u0 < b; u0 += 4) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int64_t t = u0 + m;
-          if (t < b) {
-            xs[m] = row8<T>(rx, t - lo, ldxb, coff);
-            const f8 &x0 = xs[m], &x1 = xs[(m + 3) & 3], &x2 = xs[(m + 2) & 3], &x3 = xs[(m + 1) & 3];
-            f8 av;
-            float sq = 0.f;
+      for (int m = 0; m < 4; ++m) px[m] = raw_row8<T>(rx, a + m - lo, ldxb, coff);
+      auto token = [&](const int m, const int64_t t) __attribute__((always_inline)) {
+        xs[m] = raw_f8(px[m]);
+        px[m] = raw_row8<T>(rx, t + 4 - lo, ldxb, coff);   // past the piece: zero, unused
+        const f8 &x0 = xs[m], &x1 = xs[(m + 3) & 3], &x2 = xs[(m + 2) & 3], &x3 = xs[(m + 1) & 3];
+        f8 av;
+        float sq = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              float u = wr[i][0] * x3.v[i] + wr[i][1] * x2.v[i] + wr[i][2] * x1.v[i] + wr[i][3] * x0.v[i];
-              av.v[i] = u * sigmoidf_(u);
-              sq += av.v[i] * av.v[i];
-            }
-            sq = group_sum<D>(sq);
-            if (l2) {
-              const float r = rsqrtf(sq + eps);
-#pragma unroll
-              for (int i = 0; i < 8; ++i) av.v[i] *= r;
-            }
-            put_row8<T>(ry, t - a, ldyb, coff, av);
-          }
+        for (int i = 0; i < 8; ++i) {
+          float u = wr[i][0] * x3.v[i] + wr[i][1] * x2.v[i] + wr[i][2] * x1.v[i] + wr[i][3] * x0.v[i];
+          av.v[i] = u * sigmoidf_(u);
+          sq += av.v[i] * av.v[i];
         }
+        sq = group_sum<D>(sq);
+        if (l2) {
+          const float r = rsqrtf(sq + eps);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) av.v[i] *= r;
+        }
+        put_row8<T>(ry, t - a, ldyb, coff, av);
+      };
+      // whole groups of four with no per-token test (so the loads stay a
+      // group ahead across iterations), then the last one to three tokens
+      int64_t u0 = a;
+      for (; u0 + 4 <= b; u0 += 4) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) token(m, u0 + m);
       }
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+        if (u0 + m < b) token(m, u0 + m);
     }
     a = b > a ? b : a;
     ++n;
@@ -176,7 +195,7 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
     const T* __restrict__ dy, int64_t lddy, T* __restrict__ dx, int64_t lddx,
     float* __restrict__ partials) {
   __shared__ float red[CONV_RUNS_PER_BLOCK][64][33];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   const bool active = c0 < C;
   const bool l2 = c0 < n_l2;
@@ -204,7 +223,7 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
     // walked from its end
     int n = find_seq(cu, n_seq, te - 1);
     for (int64_t b = te; b > tb;) {
-      const int64_t ss = cu[n], se = cu[n + 1];
+      const int64_t ss = uniform_i32(cu[n]), se = uniform_i32(cu[n + 1]);
       const int64_t a = ss > tb ? ss : tb;
       if (b > a) {
         // x rows [max(a - 3, ss), min(b + 3, se)); dy rows [a, min(b + 3, se))
@@ -226,33 +245,47 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
             for (int i = 0; i < 8; ++i) ds[3 - j].v[i] = 0.f;
           }
         }
-        // x[b - 1 - j] in slot j (u0 = b - 1; token u in slot (u0 - u) mod 4)
+        // x[b - 1 - j] in slot j (u0 = b - 1; token u in slot (u0 - u) mod 4);
+        // the rows of the next group (x[u - 4], dy[u]) load a group ahead
+        // into raw slots; rows before the piece read zero and go unused
+        Raw8<T> px[4], pd[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xs[j] = xr(b - 1 - j);
-        for (int64_t u0 = b - 1; u0 >= a; u0 -= 4) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int64_t s = u0 - m;
-            if (s >= a) {
-              const f8 &x0 = xs[m], &x1 = xs[(m + 1) & 3], &x2 = xs[(m + 2) & 3], &x3 = xs[(m + 3) & 3];
-              const f8 d0 = conv_du<D>(wr, x0, x1, x2, x3, row8<T>(ry, s - a, ldyb, coff), l2, eps);
-              const f8 &d1 = ds[(m + 3) & 3], &d2 = ds[(m + 2) & 3], &d3 = ds[(m + 1) & 3];
-              f8 o;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                // x[s] feeds u[s+3-j] through tap j
-                o.v[i] = wr[i][3] * d0.v[i] + wr[i][2] * d1.v[i] + wr[i][1] * d2.v[i] + wr[i][0] * d3.v[i];
-                dwa[i][0] += d0.v[i] * x3.v[i];
-                dwa[i][1] += d0.v[i] * x2.v[i];
-                dwa[i][2] += d0.v[i] * x1.v[i];
-                dwa[i][3] += d0.v[i] * x0.v[i];
-              }
-              put_row8<T>(ro, s - a, ldob, coff, o);
-              ds[m] = d0;
-              xs[m] = xr(s - 4);
-            }
-          }
+        for (int j = 0; j < 4; ++j) {
+          xs[j] = xr(b - 1 - j);
+          px[j] = raw_row8<T>(rx, b - 5 - j - lo, ldxb, coff);
+          pd[j] = raw_row8<T>(ry, b - 1 - j - a, ldyb, coff);
         }
+        auto token = [&](const int m, const int64_t s) __attribute__((always_inline)) {
+          const f8 &x0 = xs[m], &x1 = xs[(m + 1) & 3], &x2 = xs[(m + 2) & 3], &x3 = xs[(m + 3) & 3];
+          const f8 dyv = raw_f8(pd[m]);
+          pd[m] = raw_row8<T>(ry, s - 4 - a, ldyb, coff);
+          const f8 d0 = conv_du<D>(wr, x0, x1, x2, x3, dyv, l2, eps);
+          const f8 &d1 = ds[(m + 3) & 3], &d2 = ds[(m + 2) & 3], &d3 = ds[(m + 1) & 3];
+          f8 o;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            // x[s] feeds u[s+3-j] through tap j
+            o.v[i] = wr[i][3] * d0.v[i] + wr[i][2] * d1.v[i] + wr[i][1] * d2.v[i] + wr[i][0] * d3.v[i];
+            dwa[i][0] += d0.v[i] * x3.v[i];
+            dwa[i][1] += d0.v[i] * x2.v[i];
+            dwa[i][2] += d0.v[i] * x1.v[i];
+            dwa[i][3] += d0.v[i] * x0.v[i];
+          }
+          put_row8<T>(ro, s - a, ldob, coff, o);
+          ds[m] = d0;
+          xs[m] = raw_f8(px[m]);
+          px[m] = raw_row8<T>(rx, s - 8 - lo, ldxb, coff);
+        };
+        // whole groups of four with no per-token test, then the last one to
+        // three tokens
+        int64_t u0 = b - 1;
+        for (; u0 - 3 >= a; u0 -= 4) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) token(m, u0 - m);
+        }
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+          if (u0 - m >= a) token(m, u0 - m);
       }
       b = a;
       --n;
