@@ -62,6 +62,11 @@ template <typename T, int D> struct GradLds {
   float bet[CHUNK], Gm[CHUNK], dc[CHUNK];
   float colB[4][CHUNK], rowB[CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
   float segE[4][CHUNK], boxE[4][CHUNK], red[8];
+  // k_s . k_t (row t, column s) for 16-bit types, in fp16 (|k_s . k_t| <= 1
+  // for the L2-normalised keys): there the Tinv-chain waves read it from LDS
+  // and leave their registers to phase B; fp32 keeps it in registers
+  static constexpr bool KK_LDS = sizeof(T) == 2;
+  fp16 KK[KK_LDS ? CHUNK : 1][CHUNK + 4];
 };
 
 // Four consecutive elements as floats (8 bytes for 16-bit types).
@@ -171,8 +176,15 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       for (int p = 0; p < NSD; ++p)
         kk[st] = MM::mma(buffer_frag<T>(rk, (uint32_t)(16 * st + c16) * ldb + (uint32_t)pcol(p) * sizeof(T)),
                          kb[p], kk[st]);
+      if constexpr (GL::KK_LDS)
+        store4(&sm.KK[tl][16 * st + g4], kk[st][0], kk[st][1], kk[st][2], kk[st][3]);
     }
   }
+  // (read back by the lane that wrote it: no barrier)
+  auto kkv = [&](int st) __attribute__((always_inline)) -> floatx4 {
+    if constexpr (GL::KK_LDS) return ld4(&sm.KK[tl][16 * st + g4]);
+    else return kk[st];
+  };
   frag kta[NSC], qta[NSC];
   {
     const int64_t r = ((int64_t)c * Hk + kh) * D * CHUNK + (int64_t)(16 * kt + c16) * CHUNK;
@@ -182,8 +194,12 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       qta[p] = rdf(Qtb + r, pcol(p));
     }
   }
-  // (raw storage-type values, converted where used)
-  typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type raw4;
+  // (raw storage-type values, converted where used: laundered there, so the
+  // converted values are not hoisted out of the head loop, where they would
+  // take twice the registers)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef typename std::conditional<sizeof(T) == 2, u32x2, u32x4>::type raw4;
   raw4 q4[TTW], k4[TTW];
   auto raw_f4 = [&](const raw4& r) __attribute__((always_inline)) -> floatx4 {
     if constexpr (sizeof(T) == 2)
@@ -215,9 +231,12 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   // ---- per head: the token tiles (direct copies by the first NCW waves,
   // rows past the chunk end re-read its last row) ...
   constexpr int NCW = TT::PIECES / 64 < 8 ? TT::PIECES / 64 : 8;
-  auto copy_rows = [&](T* dst, const T* src, uint32_t ldb) __attribute__((always_inline)) {
-    if (wave < NCW) {
-      const auto rs = buffer_of(src, (uint32_t)L * ldb);
+  // (live false: an empty source range, every copy reads zero and touches no
+  // memory; the requests are issued all the same, so the wait counts after
+  // them do not depend on whether a next head exists)
+  auto copy_rows = [&](T* dst, const T* src, uint32_t ldb, bool live) __attribute__((always_inline)) {
+    if (NCW == 8 || wave < NCW) {   // (a test the compiler can drop when all waves copy)
+      const auto rs = buffer_of(src, live ? (uint32_t)L * ldb : 0u);
 #pragma unroll
       for (int j = 0; j < TT::PIECES / (64 * NCW); ++j) {
         const int s = (j * NCW + wave) * 64 + lane, r = s / TT::RP;
@@ -227,39 +246,48 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     }
   };
   // (R is read in phase A only, so it comes with Tinv, a phase earlier)
-  auto copy_head = [&](int h) __attribute__((always_inline)) {
+  auto copy_head = [&](int h, bool live) __attribute__((always_inline)) {
     const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
     const int64_t base = t0 * HvD + (int64_t)h * D;
-    copy_rows(sm.tO, dout + base, rowb);
-    copy_rows(sm.tDl, Dlw + base, rowb);
-    copy_rows(sm.tdR, dvo + t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)));
+    copy_rows(sm.tO, dout + base, rowb, live);
+    copy_rows(sm.tDl, Dlw + base, rowb, live);
+    copy_rows(sm.tdR, dvo + t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)), live);
   };
-  auto copy_r = [&](int h) __attribute__((always_inline)) {
-    copy_rows(sm.tR, Rw + t0 * HvD + (int64_t)h * D, (uint32_t)(HvD * sizeof(T)));
+  auto copy_r = [&](int h, bool live) __attribute__((always_inline)) {
+    copy_rows(sm.tR, Rw + t0 * HvD + (int64_t)h * D, (uint32_t)(HvD * sizeof(T)), live);
   };
-  // ... the gate values ...
-  auto load_gates = [&](int h) __attribute__((always_inline)) {
+  // ... the gate values (wave 0: loaded into registers a phase before they
+  // go to LDS) ...
+  double gnext = 0.0;
+  float bnext = 0.f;
+  auto fetch_gates = [&](int h) __attribute__((always_inline)) {
     if (wave == 0) {
-      const double gm = gcum[(t0 + (lane < L ? lane : L - 1)) * Hv + h];
-      sm.gam[lane] = gm;
-      sm.bet[lane] = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
+      gnext = gcum[(t0 + (lane < L ? lane : L - 1)) * Hv + h];
+      bnext = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
+    }
+  };
+  auto put_gates = [&]() __attribute__((always_inline)) {
+    if (wave == 0) {
+      sm.gam[lane] = gnext;
+      sm.bet[lane] = bnext;
       // gam is flat past the chunk length, so these are the factors of
       // token min(t, L - 1)
-      const double glast = __shfl(gm, CHUNK - 1, 64);
-      sm.Gm[lane] = dexp<T>(gm);
-      sm.dc[lane] = dexp<T>(glast - gm);
+      const double glast = __shfl(gnext, CHUNK - 1, 64);
+      sm.Gm[lane] = dexp<T>(gnext);
+      sm.dc[lane] = dexp<T>(glast - gnext);
     }
   };
   // ... Tinv and Tinv^T (16-bit types: into LDS, by direct copies) ...
   typedef typename GL::TI TI;
-  auto copy_tinv = [&](int h) __attribute__((always_inline)) {
+  auto copy_tinv = [&](int h, bool live) __attribute__((always_inline)) {
     if constexpr (GL::TIN_LDS) {
       const char* src = reinterpret_cast<const char*>(Tib + (c * Hv + h) * 2 * CHUNK * CHUNK);
+      const uint32_t bytes = live ? 2 * CHUNK * CHUNK * sizeof(T) : 0u;
 #pragma unroll
       for (int j = 0; j < 2 * TI::PIECES / 512; ++j) {
         const int s = (j * 8 + wave) * 64 + lane, r = s / TI::RP;   // r: row of both matrices
         const uint32_t off = (uint32_t)(r * TI::RP + ((s % TI::RP) ^ TI::swz(r))) * 16u;
-        copy_to_lds(buffer_of(src, 2 * CHUNK * CHUNK * sizeof(T)), sm.Tin + (j * 8 + wave) * 64 * TI::EPP, off, 0);
+        copy_to_lds(buffer_of(src, bytes), sm.Tin + (j * 8 + wave) * 64 * TI::EPP, off, 0);
       }
     }
   };
@@ -268,20 +296,59 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     if constexpr (GL::TIN_LDS) return sm.Tin + m * CHUNK * CHUNK + TI::at(r, col);
     else return Tib + (c * Hv + h) * 2 * CHUNK * CHUNK + m * CHUNK * CHUNK + r * CHUNK + col;
   };
-  // ... the Tinv-chain waves' rows of dDelta ...
-  frag ddB[NSD];
-  auto load_tinv = [&](int h) __attribute__((always_inline)) {
+  // ... the phase-A operands: the Tinv-chain waves' rows of dDelta or the
+  // dP-side waves' P values, as loaded, in one register array for both roles
+  // (two arrays would each stay live across the head loop in the waves of
+  // the other role); converted where used, so that nothing waits for the
+  // loads where they are issued
+  constexpr int FR = (int)(sizeof(frag) / 4);     // dwords per operand fragment
+  constexpr int NAD = NSD * FR, NPD = 4 * (int)sizeof(CT);
+  constexpr int NA = NAD > NPD ? NAD : NPD;
+  uint32_t aop[NA];
+  auto load_tinv = [&](int h, bool live) __attribute__((always_inline)) {
     const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-    const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
+    const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D, live ? (uint32_t)L * rowb : 0u);
 #pragma unroll
-    for (int p = 0; p < NSD; ++p) ddB[p] = buffer_frag<T>(rs, (uint32_t)tl * rowb + (uint32_t)pcol(p) * sizeof(T));
+    for (int p = 0; p < NSD; ++p) {
+      const frag f = buffer_frag<T>(rs, (uint32_t)tl * rowb + (uint32_t)pcol(p) * sizeof(T));
+      if constexpr (FR == 4) {
+        const u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) aop[4 * p + j] = w[j];
+      } else {
+        aop[p] = __builtin_bit_cast(uint32_t, f);
+      }
+    }
   };
-  // ... the dP-side waves' P values ...
-  floatx4 pE[4];
-  auto load_p = [&](int h) __attribute__((always_inline)) {
-    const CT* Pc = Pw + (c * Hv + h) * CHUNK * CHUNK + tl * CHUNK;
+  auto ddB = [&](int p) __attribute__((always_inline)) -> frag {
+    if constexpr (FR == 4) return __builtin_bit_cast(frag, u32x4{aop[4 * p], aop[4 * p + 1], aop[4 * p + 2], aop[4 * p + 3]});
+    else return __builtin_bit_cast(frag, aop[p]);
+  };
+  auto load_p = [&](int h, bool live) __attribute__((always_inline)) {
+    const auto rs = buffer_of(Pw + (c * Hv + h) * CHUNK * CHUNK, live ? CHUNK * CHUNK * sizeof(CT) : 0u);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) pE[st] = ld4(Pc + acc_col<CT>(16 * st + g4));
+    for (int st = 0; st < 4; ++st) {
+      const uint32_t off = (uint32_t)(tl * CHUNK + acc_col<CT>(16 * st + g4)) * sizeof(CT);
+      if constexpr (sizeof(CT) == 2) {
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+        aop[2 * st] = w[0];
+        aop[2 * st + 1] = w[1];
+      } else {
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) aop[4 * st + j] = w[j];
+      }
+    }
+  };
+  auto pE = [&](int st) __attribute__((always_inline)) -> floatx4 {
+    if constexpr (sizeof(CT) == 2) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 a = __builtin_bit_cast(h2, aop[2 * st]), b = __builtin_bit_cast(h2, aop[2 * st + 1]);
+      return floatx4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+    } else {
+      return floatx4{__uint_as_float(aop[4 * st]), __uint_as_float(aop[4 * st + 1]),
+                     __uint_as_float(aop[4 * st + 2]), __uint_as_float(aop[4 * st + 3])};
+    }
   };
   // ... and every wave's rows of the saved states (phase B)
   frag hA[NSD], dhA[NSD];
@@ -293,20 +360,27 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       dhA[p] = rdf(dhst + r, pcol(p));
     }
   };
-  auto load_a = [&](int h) __attribute__((always_inline)) {
-    if (role == 0) load_tinv(h);
-    else load_p(h);
+  auto load_a = [&](int h, bool live) __attribute__((always_inline)) {
+    if (role == 0) load_tinv(h, live);
+    else load_p(h, live);
   };
 
-  copy_head(kh * G);
-  copy_r(kh * G);
-  copy_tinv(kh * G);
-  load_gates(kh * G);
+  copy_head(kh * G, true);
+  copy_r(kh * G, true);
+  copy_tinv(kh * G, true);
+  fetch_gates(kh * G);
+  load_a(kh * G, true);
+  put_gates();
 
+  // Every operand of head h + 1 is requested while head h finishes: R and
+  // Tinv before phase B, the other tiles, the phase-A operands and the gates
+  // after it.  The barriers they have to pass are LDS-only (a full barrier
+  // would wait for the copies); the one at the top of a head waits for all.
+  // After the last head the same requests go out with empty ranges (gates:
+  // the last head's again).
   for (int hh = 0; hh < G; ++hh) {
     const int h = kh * G + hh;
     derive();
-    load_a(h);
     issue_fence();
     __syncthreads();   // this head's tiles, gates and phase-A operands are in
     // =============== phase A: pair products (s x t tiles, t = tl)
@@ -320,7 +394,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       for (int st = 0; st < 4; ++st) {
         dMt[st] = zero4();
 #pragma unroll
-        for (int p = 0; p < NSD; ++p) dMt[st] = MM::mma(tfr(sm.tR, 16 * st + c16, p), ddB[p], dMt[st]);
+        for (int p = 0; p < NSD; ++p) dMt[st] = MM::mma(tfr(sm.tR, 16 * st + c16, p), ddB(p), dMt[st]);
       }
       // the first dbeta term summed over t (the 16 lanes of a group: lane
       // c16 of group g keeps the sum for s = 16 (c16 / 4) + 4 g + c16 % 4);
@@ -372,12 +446,13 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       // Tinv-chain waves have written theirs)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
+        const floatx4 pv = pE(st);
         float pd[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * st + g4 + i;
           const float Dts = s <= tl ? dexp<T>(gt - sm.gam[s]) : 0.f;
-          ep[st][i] = (s < tl && tl < L) ? dPt[st][i] * pE[st][i] : 0.f;
+          ep[st][i] = (s < tl && tl < L) ? dPt[st][i] * pv[i] : 0.f;
           pd[i] = dPt[st][i] * Dts;
         }
         store4(&sm.dPD[tl][acc_col<T>(16 * st + g4)], pd[0], pd[1], pd[2], pd[3]);
@@ -405,6 +480,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       float rb = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
+        const floatx4 kks = kkv(st);
         floatx4 da = zero4();
 #pragma unroll
         for (int p = 0; p < NSC; ++p)
@@ -417,8 +493,8 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           const float Dts = lower ? dexp<T>(gt - sm.gam[s]) : 0.f;
           const float dA = lower ? -da[i] : 0.f;
           const float dAD = dA * Dts;
-          sm.E[tl][s] = tl < L ? dAD * bt * kk[st][i] : 0.f;
-          rb += dAD * kk[st][i];
+          sm.E[tl][s] = tl < L ? dAD * bt * kks[i] : 0.f;
+          rb += dAD * kks[i];
           wa[i] = dAD * bt;
         }
         store4(&sm.WA[tl][16 * st + g4], wa[0], wa[1], wa[2], wa[3]);
@@ -443,9 +519,10 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
              a[2] + to_f(sm.WA[u4 + 2][x]), a[3] + to_f(sm.WA[u4 + 3][x]));
     }
     __syncthreads();
-    if (hh + 1 < G) {   // R and Tinv are no longer read for this head
-      copy_r(h + 1);
-      copy_tinv(h + 1);
+    {   // R and Tinv are no longer read for this head
+      const bool live = hh + 1 < G;
+      copy_r(live ? h + 1 : h, live);
+      copy_tinv(live ? h + 1 : h, live);
     }
 
     // =============== phase B: token x key products (k x t tiles)
@@ -479,7 +556,9 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           dKa[tt] = MM::mma(kta[p], rdf(&sm.WS[t][0], pcol(p)), dKa[tt]);
         }
         const float Gt = sm.Gm[t], dct = sm.dc[t];
-        const floatx4 qv = raw_f4(q4[tt]), kv = raw_f4(k4[tt]);
+        raw4 qr = q4[tt], kr = k4[tt];
+        asm volatile("" : "+v"(qr), "+v"(kr));
+        const floatx4 qv = raw_f4(qr), kv = raw_f4(kr);
         float rx = 0.f, rz = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -500,8 +579,13 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       ipv = wave_sum(ipv);
       if (lane == 0) sm.red[wave] = ipv;
     }
-    __syncthreads();   // the token tiles are free; every partial is in
-    if (hh + 1 < G) copy_head(h + 1);
+    lds_barrier();   // the token tiles are free; every partial is in
+    {
+      const bool live = hh + 1 < G;
+      copy_head(live ? h + 1 : h, live);
+      fetch_gates(live ? h + 1 : h);
+      load_a(live ? h + 1 : h, live);
+    }
 
     // =============== dg, dbeta (waves 0-3).  With gamma the in-chunk
     // cumulative gate, dg_i = sum_{t >= i} dgam_t.  Three parts, each a sum
@@ -525,7 +609,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       }
       sm.segE[wave][cidx] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave < 4) {
       // add the later row blocks, then the row-prefix part of each box sum
       const int cidx = lane, rb0 = 16 * wave;
@@ -534,7 +618,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) sm.E[rb0 + r][cidx] += off;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave < 4) {
       // token i = lane sums columns s < i of the column block owned by this wave
       const int i = lane, cb0 = 16 * wave;
@@ -544,7 +628,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         if (cb0 + s < i) part += sm.E[i][cb0 + s];
       sm.boxE[wave][i] = part;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
       const int t = lane;
       float y = 0.f, db = sm.rowB[t], zt = 0.f, ips = 0.f;
@@ -566,8 +650,8 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         dbeta[(t0 + t) * Hv + h] = db;
       }
     }
-    __syncthreads();   // the gates of this head are no longer read
-    if (hh + 1 < G) load_gates(h + 1);
+    lds_barrier();   // the gates of this head are no longer read
+    put_gates();
   }
 
   // ---- dq = scale dQ, dk: four consecutive key columns of one token per lane

@@ -172,6 +172,13 @@ template <int N> __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Barrier over LDS traffic only: this wave's LDS operations are done, while
+// its vector-memory operations (direct copies into LDS among them) stay in
+// flight.  For barriers that no copy still in flight needs to cross.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Per-lane source offsets of direct copies: copy J of a tile with RP pieces
 // per row reads 1024 J + lane_pattern; the pattern depends only on RP (and on
 // J mod 4 when RP = 16).  With copy J = j NW + wave, the RP = 16 pattern of
