@@ -197,8 +197,6 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   // (raw storage-type values, converted where used: laundered there, so the
   // converted values are not hoisted out of the head loop, where they would
   // take twice the registers)
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef typename std::conditional<sizeof(T) == 2, u32x2, u32x4>::type raw4;
   raw4 q4[TTW], k4[TTW];
   auto raw_f4 = [&](const raw4& r) __attribute__((always_inline)) -> floatx4 {

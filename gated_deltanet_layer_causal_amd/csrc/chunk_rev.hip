@@ -8,13 +8,14 @@
 // and dS0 at the sequence start.
 //
 // Same structure as the state pass (chunk_state.hip): one workgroup per
-// (sequence, value head, block of 16 * NW value rows); wave w keeps its
-// d_k x 16 slice of dS'^T in MFMA accumulators and feeds it straight back as
-// B operand; the chunk operands (K rows, K^T, Q^T, P^T, M^T from the
+// (sequence, value head, block of 16 * NW value rows); compute wave w keeps
+// its d_k x 16 slice of dS'^T in MFMA accumulators and feeds it straight
+// back as B operand; NW mover waves (on the SIMDs the compute waves leave
+// free) stream the chunk operands (K rows, K^T, Q^T, P^T, M^T from the
 // backward preparation, columns in accumulator order; the dO rows of the
-// block; Gam, dec) stream into one of two LDS buffers by direct copies while
-// the other buffer computes.  Operands are in the storage type (bf16 keeps
-// the range of dS).
+// block; Gam, dec) into one of two LDS buffers by direct copies while the
+// compute waves work on the other.  Operands are in the storage type (bf16
+// keeps the range of dS).
 #include "chunk_stream.h"
 
 namespace gdn {
@@ -35,7 +36,7 @@ template <typename T, int D, int NW> struct RevBuf {
 } __attribute__((aligned(16)));
 
 template <typename T, int D, int NW>
-__global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
+__global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
     const T* __restrict__ Kb, const T* __restrict__ Ktb, const T* __restrict__ Qtb,
     const T* __restrict__ Ptb, const T* __restrict__ Mtb, const float* __restrict__ Gw,
@@ -59,10 +60,15 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
                 TM::PIECES % (64 * NW) == 0 && TO::PIECES % (64 * NW) == 0,
                 "direct copies cover whole waves");
   __shared__ RB bufA, bufB;
+  // per wave: staged output rows (dS' rows k, then dDelta and dv rows t)
+  typedef StageRows<T> SR;
+  __shared__ __align__(16) char stg[NW * (D + 2 * CHUNK) * SR::SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
+  // waves [0, NW) compute, waves [NW, 2 NW) move the operands
   const int wave_ = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave = wave_;
+  const bool mover = wave_ >= NW;
+  const int wave = mover ? wave_ - NW : wave_;
   const int item = xcd_item(blockIdx.x, n_items);
   const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
   const int kh = h / G, Hk = Hv / G;
@@ -86,15 +92,11 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
   const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
   const uint32_t rowv = (uint32_t)(lddv * sizeof(T));
   const uint32_t rowh = (uint32_t)(D * sizeof(T));
-  // paired-column stores: this lane's offsets in ddw, dv and dS' rows
+  // outputs leave through the wave's LDS rows in 16-byte pieces
   PairStore ps;
   ps.init(lane);
   const uint32_t wcol = (uint32_t)(16 * wave * sizeof(T));
-  const uint32_t so = wcol + ps.lane_off<T>(lane, rowb);
-  const uint32_t sv = wcol + ps.lane_off<T>(lane, rowv);
-  const uint32_t hb = wcol + ps.lane_off<T>(lane, rowh);
-  // stores a step issues per lane: dS', dDelta, dv (two rows per tile each)
-  constexpr int NSTORE = 2 * NKT + 2 * 4 + 2 * 4;
+  char* const myst = stg + wave * (D + 2 * CHUNK) * SR::SB;
   // LDS read offsets (as in the state pass)
   int rw[NSD], rk[NSC];
 #pragma unroll
@@ -105,7 +107,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
     rk[p] = KS == 4 ? TKt::at(c16, 16 * (p >> 2) + g4 + (p & 3)) : TKt::at(c16, 32 * p + 8 * g);
 
   auto fetch = [&](RB& B, int64_t c) __attribute__((always_inline)) {
-    int wave = wave_;
+    int wave = wave_ - NW;   // (movers only)
     asm volatile("" : "+s"(wave));
     const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
     const int64_t rem = seq_t1 - t0;
@@ -134,6 +136,40 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
     }
   };
 
+  // The movers also touch every line of the chunk after the one they copy,
+  // a step ahead, so that its copies find the lines in L2: one 4-byte
+  // direct copy per line into a sink, each mover taking every other line
+  // (lanes past a tile read out of range, which touches no memory).
+  __shared__ float sink[64];
+  constexpr int TKB = CHUNK * D * (int)sizeof(T), TMB = CHUNK * CHUNK * (int)sizeof(T);
+  constexpr int NTK = (TKB / 128 + 127) / 128, NTM = (TMB / 128 + 127) / 128;   // touches per tile
+  auto touch_tile = [&](const void* base, int bytes, int n, int wave) __attribute__((always_inline)) {
+    const auto rs = buffer_of(base, (uint32_t)bytes);
+#pragma unroll
+    for (int j = 0; j < n; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)sink, 4,
+                                               (uint32_t)(2 * (64 * j + lane) + wave) * 128u, 0, 0, 0);
+  };
+  auto touch = [&](int64_t c) __attribute__((always_inline)) {
+    int wave = wave_ - NW;   // (movers only)
+    asm volatile("" : "+s"(wave));
+    const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - t0;
+    const int Lc = rem < CHUNK ? (int)rem : CHUNK;
+    const int64_t ch = (int64_t)c * Hv + h, ck = (int64_t)c * Hk + kh;
+    touch_tile(Kb + ck * CHUNK * D, TKB, NTK, wave);
+    touch_tile(Ktb + ck * D * CHUNK, TKB, NTK, wave);
+    touch_tile(Qtb + ck * D * CHUNK, TKB, NTK, wave);
+    touch_tile(Ptb + ch * CHUNK * CHUNK, TMB, NTM, wave);
+    touch_tile(Mtb + ch * CHUNK * CHUNK, TMB, NTM, wave);
+    // the block's dO rows (one line each)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        buffer_of(dout + t0 * HvD + (int64_t)h * D + v0, (uint32_t)Lc * rowb),
+        (__attribute__((address_space(3))) void*)sink, 4, (uint32_t)(2 * lane + wave) * rowb, 0, 0, 0);
+  };
+  // touches a mover issues per step
+  constexpr int NTOUCH = 3 * NTK + 2 * NTM + 1;
+
   auto arow = [&](const T* base, int o, int tile_elems) __attribute__((always_inline)) -> frag {
     if constexpr (KS == 4) return base[tile_elems + o];
     else return *reinterpret_cast<const frag*>(base + tile_elems + o);
@@ -151,7 +187,8 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
     {
       const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, dS[kt]);
+      for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, dS[kt]);
+      SR::flush(myst, 0, D, rs, wcol, rowh, lane);
     }
 
     // dO as B operands over the chunk index, plain and scaled by scale Gam_t
@@ -193,7 +230,8 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
       // rows past the sequence end fall outside the buffer: dropped
       const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) ps.store<T>(rs, so + (uint32_t)(16 * tt) * rowb, rowb, dd[tt]);
+      for (int tt = 0; tt < 4; ++tt) SR::put(myst, D + 16 * tt, ps, lane, dd[tt]);
+      SR::flush(myst, D, CHUNK, rs, wcol, rowb, lane);
     }
 
     // dR = M^T dDelta (= dv); then -diag(Gam) dR as B operands
@@ -213,8 +251,9 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
         gr[tt][1] = -gm.y * dr[1];
         gr[tt][2] = -gm.z * dr[2];
         gr[tt][3] = -gm.w * dr[3];
-        ps.store<T>(rs, sv + (uint32_t)(16 * tt) * rowv, rowv, dr);
+        SR::put(myst, D + CHUNK + 16 * tt, ps, lane, dr);
       }
+      SR::flush(myst, D + CHUNK, CHUNK, rs, wcol, rowv, lane);
     }
 
     // dS^T = Gam_L dS'^T + Q^T (scale diag(Gam) dO) - K^T (diag(Gam) dR)
@@ -236,31 +275,48 @@ __global__ void __launch_bounds__(64 * NW) chunk_rev_kernel(
     }
   };
 
-  // A step copies the next chunk's operands, then computes (and stores)
-  // this one; it ends once this wave's copies are done, leaving the step's
-  // NSTORE stores (issued after them) in flight, and a barrier makes every
-  // wave's copies visible.
-  if (c_begin < c_end) fetch(bufA, c_end - 1);
-  __syncthreads();
-  for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
-    fetch(bufB, c - 1 >= c_begin ? c - 1 : c);   // a repeat of chunk c at the start
-    issue_fence();   // the copies stay ahead of this step's stores
-    compute(bufA, c);
-    wait_vm_barrier<NSTORE>();
-    if (c - 1 >= c_begin) {
-      fetch(bufA, c - 2 >= c_begin ? c - 2 : c - 1);
-      issue_fence();
-      compute(bufB, c - 1);
-      wait_vm_barrier<NSTORE>();
+  // The movers copy the next chunk's operands into the buffer that the
+  // compute waves are not reading and end each step once their copies are
+  // in; the compute waves only compute and store, so the copies' issue and
+  // the waits for them stay off the recurrence.  One barrier per step: after
+  // it the buffer just computed is free and the next one is filled.
+  if (mover) {
+    // each step ends once the copies are in, the touches (issued after
+    // them) still in flight; at the end nothing is
+    auto first = [&](int64_t x) { return x >= c_begin ? x : c_begin; };
+    if (c_begin < c_end) {
+      fetch(bufA, c_end - 1);
+      touch(first(c_end - 2));
     }
-  }
-
-  if (dS0) {
+    wait_vm_barrier<NTOUCH>();
+    for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
+      fetch(bufB, c - 1 >= c_begin ? c - 1 : c);   // a repeat of chunk c at the start
+      touch(first(c - 2));
+      wait_vm_barrier<NTOUCH>();
+      if (c - 1 >= c_begin) {
+        fetch(bufA, c - 2 >= c_begin ? c - 2 : c - 1);
+        touch(first(c - 3));
+        wait_vm_barrier<NTOUCH>();
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    lds_barrier();
+    for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
+      compute(bufA, c);
+      lds_barrier();
+      if (c - 1 >= c_begin) {
+        compute(bufB, c - 1);
+        lds_barrier();
+      }
+    }
+    if (dS0) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dS0[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] = dS[kt][i];
+        for (int i = 0; i < 4; ++i)
+          dS0[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] = dS[kt][i];
+    }
   }
 }
 
@@ -273,7 +329,7 @@ static hipError_t chunk_rev(const gdn_shape& s, float scale, const int32_t* cu, 
                             const ChunkLayout& Ly, char* ws, hipStream_t st) {
   constexpr int NW = REV_NW, BV = 16 * NW;
   const int n_items = (D / BV) * s.hv * s.n_seq;
-  hipLaunchKernelGGL((chunk_rev_kernel<T, D, NW>), dim3(n_items), dim3(64 * NW), 0, st, cu,
+  hipLaunchKernelGGL((chunk_rev_kernel<T, D, NW>), dim3(n_items), dim3(128 * NW), 0, st, cu,
                      (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
                      (const T*)(ws + Ly.kb), (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb),
                      (const T*)(ws + Ly.ptb), (const T*)(ws + Ly.mtb), (const float*)(ws + Ly.gw),

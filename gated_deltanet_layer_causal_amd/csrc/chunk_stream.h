@@ -6,6 +6,9 @@
 
 namespace gdn {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Reduction order of an MFMA step whose B operand comes from accumulator
 // tiles x[0..] (rows = reduction index).
 //  16-bit operands (32 per step): step p uses tiles 2p and 2p + 1; lane l's
@@ -71,6 +74,10 @@ template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
 // wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
 // Buffer accesses are range-checked against the descriptor's size on the
 // per-lane offset (loads past it read zero, stores past it are dropped).
+// Byte offset in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
                                             uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
@@ -112,11 +119,9 @@ __device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t rs, uint3
 template <typename T>
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_t off, floatx4 x) {
   if constexpr (sizeof(T) == 2) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 w = {pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3])};
     __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
   } else {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
   }
 }
@@ -127,6 +132,10 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_
 // (one DPP move), so lane l writes rows 4 (l / 16) + 2 (l & 1) + {0, 1} at
 // columns (l % 16) & ~1 and + 1.  Half the store instructions of one store
 // per element.
+// 32-bit words of a paired row piece: two 16-bit elements, or two floats.
+template <typename T> struct PairWord { typedef uint32_t type; };
+template <> struct PairWord<float> { typedef u32x2 type; };
+
 struct PairStore {
   uint32_t sel0, sel1;
   bool odd;
@@ -141,23 +150,79 @@ struct PairStore {
   template <typename T> __device__ __forceinline__ uint32_t lane_off(int lane, uint32_t ldb) const {
     return (uint32_t)(4 * (lane >> 4) + 2 * (lane & 1)) * ldb + (uint32_t)((lane & 15) & ~1) * sizeof(T);
   }
+  // the tile's values for this lane's rows r0 = 4 (lane / 16) + 2 (lane % 2)
+  // and r0 + 1, columns (lane % 16) & ~1 and the next: lanes 2j and 2j + 1
+  // swap the halves of their four rows
   template <typename T>
-  __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t ldb,
-                                        floatx4 x) const {
+  __device__ __forceinline__ void pair(floatx4 x, typename PairWord<T>::type& w0,
+                                       typename PairWord<T>::type& w1) const {
     if constexpr (sizeof(T) == 2) {
       const uint32_t p01 = pack2_bf16(x[0], x[1]), p23 = pack2_bf16(x[2], x[3]);
       const uint32_t own = odd ? p23 : p01, send = odd ? p01 : p23;
       const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(recv, own, sel0), rs, off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(recv, own, sel1), rs, off + ldb, 0, 0);
+      w0 = __builtin_amdgcn_perm(recv, own, sel0);
+      w1 = __builtin_amdgcn_perm(recv, own, sel1);
     } else {
       const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
       const float r0 = dpp_f<0xB1>(s0), r1 = dpp_f<0xB1>(s1);
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 w0 = {__float_as_uint(odd ? r0 : x[0]), __float_as_uint(odd ? x[2] : r0)};
-      const u32x2 w1 = {__float_as_uint(odd ? r1 : x[1]), __float_as_uint(odd ? x[3] : r1)};
+      w0 = u32x2{__float_as_uint(odd ? r0 : x[0]), __float_as_uint(odd ? x[2] : r0)};
+      w1 = u32x2{__float_as_uint(odd ? r1 : x[1]), __float_as_uint(odd ? x[3] : r1)};
+    }
+  }
+  template <typename T>
+  __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t ldb,
+                                        floatx4 x) const {
+    typename PairWord<T>::type w0, w1;
+    pair<T>(x, w0, w1);
+    if constexpr (sizeof(T) == 2) {
+      __builtin_amdgcn_raw_buffer_store_b32(w0, rs, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(w1, rs, off + ldb, 0, 0);
+    } else {
       __builtin_amdgcn_raw_buffer_store_b64(w0, rs, off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b64(w1, rs, off + ldb, 0, 0);
+    }
+  }
+};
+
+// Output rows of a wave's 16 columns staged through LDS so that they leave
+// in 16-byte stores (64 / PPR rows per store instead of the 8 rows of a
+// PairStore pair).  Each wave owns its region of rows of 16 elements (SB
+// bytes); a wave's LDS accesses complete in order, so no barrier is needed.
+// The words go in through inline ds_write2 (two rows SB apart): the
+// compiler would otherwise order every LDS store after all direct copies
+// into LDS still in flight, not knowing that the region is apart from their
+// buffers; the asm's memory clobber keeps the read-back after it.
+template <typename T> struct StageRows {
+  static constexpr int SB = 16 * (int)sizeof(T);   // bytes per staged row
+  static constexpr int PPR = SB / 16;              // 16-byte pieces per row
+  static constexpr int RPI = 64 / PPR;             // rows per store
+  static_assert(SB / (int)sizeof(typename PairWord<T>::type) == 8, "ds_write2 offset1:8 is one row");
+  typedef u32x4 __attribute__((may_alias)) piece;
+  // store instructions per lane for n rows
+  static constexpr int stores(int n) { return n / RPI; }
+  // one 16 x 16 accumulator tile into rows row0.. of the region
+  __device__ __forceinline__ static void put(char* region, int row0, const PairStore& ps, int lane,
+                                             floatx4 x) {
+    typename PairWord<T>::type w0, w1;
+    ps.pair<T>(x, w0, w1);
+    const uint32_t a = lds_offset(region) + (uint32_t)((row0 + 4 * (lane >> 4) + 2 * (lane & 1)) * SB) +
+                       (uint32_t)(((lane & 15) & ~1) * (int)sizeof(T));
+    if constexpr (sizeof(T) == 2)
+      asm volatile("ds_write2_b32 %0, %1, %2 offset1:8" ::"v"(a), "v"(w0), "v"(w1) : "memory");
+    else
+      asm volatile("ds_write2_b64 %0, %1, %2 offset1:8" ::"v"(a), "v"(w0), "v"(w1) : "memory");
+  }
+  // rows [row0, row0 + n) of the region to rows 0.. of the buffer at byte
+  // offset col (the wave's columns), row stride ldb bytes; rows outside the
+  // buffer's range are dropped
+  __device__ __forceinline__ static void flush(const char* region, int row0, int n,
+                                               __amdgpu_buffer_rsrc_t rs, uint32_t col,
+                                               uint32_t ldb, int lane) {
+    const int r = lane / PPR, pc = lane % PPR;
+#pragma unroll
+    for (int j = 0; j < n / RPI; ++j) {
+      const u32x4 v = *reinterpret_cast<const piece*>(region + (row0 + j * RPI + r) * SB + pc * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, col + (uint32_t)(j * RPI + r) * ldb + (uint32_t)pc * 16u, 0, 0);
     }
   }
 };
