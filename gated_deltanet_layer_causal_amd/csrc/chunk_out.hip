@@ -17,11 +17,14 @@
 // one token: every output leaves in 8-byte pieces, and V comes in the same
 // way.  S is the A operand of the first products: the two waves of a value
 // quarter copy its d_k x 32 slice of S (stored [k][v]) into LDS rows and
-// each gathers its lanes' k values from it.  R^T and Delta^T, A operands of
+// each reads its lanes' k values from it.  R^T and Delta^T, A operands of
 // the products over all tokens, pass between the two token halves through a
-// padded LDS tile per value quarter; their gather follows the accumulator
+// padded LDS tile per value quarter; their reads follow the accumulator
 // order in which M and P store their columns (acc_col), so the B operands
-// (rows of K, Q, M, P) are plain 16-byte reads.  Every input a phase needs is
+// (rows of K, Q, M, P) are plain 16-byte reads.  With 16-bit operands both
+// tiles are read by transposing reads (four rows of a column per lane),
+// their rows 24 words apart so the four rows of a 16-lane group fall in
+// different banks.  Every input a phase needs is
 // requested before the phase that precedes it, so load latencies overlap.
 // Rows of K, Q and V come straight from the conv output through
 // range-checked buffer loads, which return zero past the chunk's end.
@@ -31,8 +34,8 @@ namespace gdn {
 
 template <typename T, int D> struct alignas(16) OutQuarter {
   typedef typename Compute<T>::type CT;
-  static constexpr int LDH = 32 + (sizeof(T) == 2 ? 2 : 1);    // S rows: groups 8 rows apart
-  static constexpr int LDX = 32 + (sizeof(CT) == 2 ? 4 : 2);   // R, Delta rows: groups 4 apart
+  static constexpr int LDH = sizeof(T) == 2 ? 48 : 33;    // S rows
+  static constexpr int LDX = sizeof(CT) == 2 ? 48 : 34;   // R, Delta rows
   T hs[D][LDH];        // S^T slice: row k, value column
   CT xs[CHUNK][LDX];   // R, then Delta (compute type): row t, value column
 };
@@ -153,8 +156,10 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
       if constexpr (KS == 4) {
         sa[vt][p] = Q4.hs[p * KS + g][16 * vt + c16];
       } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sa[vt][p][j] = Q4.hs[p * KS + 8 * g + j][16 * vt + c16];
+        // rows p KS + 8 g + (0..3 | 4..7) of column 16 vt + c16
+        const int r = p * KS + 8 * g + (c16 >> 2), col = 16 * vt + 4 * (c16 & 3);
+        const u32x2 lo = lds_read_tr4(&Q4.hs[r][col]), hi = lds_read_tr4(&Q4.hs[r + 4][col]);
+        sa[vt][p] = __builtin_bit_cast(sfrag, u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
     }
 
@@ -165,10 +170,10 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     if constexpr (KS == 4) {
       return (cfrag)Q4.xs[16 * (p >> 2) + g4 + (p & 3)][col];
     } else {
-      cfrag f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = Q4.xs[32 * p + 16 * (j >> 2) + g4 + (j & 3)][col];
-      return f;
+      // rows 32 p + 4 g + 0..3 and 32 p + 16 + 4 g + 0..3 of column col
+      const int r = 32 * p + g4 + (c16 >> 2), cc = 16 * vt + 4 * (c16 & 3);
+      const u32x2 lo = lds_read_tr4(&Q4.xs[r][cc]), hi = lds_read_tr4(&Q4.xs[r + 16][cc]);
+      return __builtin_bit_cast(cfrag, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
   };
   // this wave's transposed tiles into the quarter's tile (four consecutive

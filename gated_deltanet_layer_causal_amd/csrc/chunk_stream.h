@@ -74,6 +74,18 @@ template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
 // wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
 // Buffer accesses are range-checked against the descriptor's size on the
 // per-lane offset (loads past it read zero, stores past it are dropped).
+// Transposing LDS read of 16-bit elements: within each group of 16 lanes,
+// lane j passes the address of row k0 + j / 4, columns n0 + 4 (j % 4) .. + 3
+// of a row-major tile (8-byte aligned), and lane i receives rows k0 .. k0 + 3
+// of column n0 + i.  Two such reads give an MFMA operand of 16-bit values
+// (eight consecutive reduction indices of one row or column) from a tile
+// whose rows are the reduction index.
+__device__ __forceinline__ u32x2 lds_read_tr4(const void* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p));
+}
+
 // Byte offset in LDS of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
