@@ -26,8 +26,10 @@ template <typename T, int D, int NW> struct RevBuf {
   typedef Tile<T, D, CHUNK> TKt;       // K^T, Q^T
   typedef Tile<T, CHUNK, CHUNK> TM;    // P^T, M^T
   typedef Tile<T, CHUNK, BV, 3> TO;    // dO rows of this block
+  // 16-bit types read K^T from the K rows by transposing reads; fp32 copies it
+  static constexpr bool KT_TR = sizeof(T) == 2;
   T K[TK::PIECES * TK::EPP];
-  T Kt[TKt::PIECES * TKt::EPP];
+  T Kt[KT_TR ? 8 : TKt::PIECES * TKt::EPP];
   T Qt[TKt::PIECES * TKt::EPP];
   T Pt[TM::PIECES * TM::EPP];
   T Mt[TM::PIECES * TM::EPP];
@@ -114,7 +116,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int Lc = rem < CHUNK ? (int)rem : CHUNK;
     const int64_t ch = (int64_t)c * Hv + h, ck = (int64_t)c * Hk + kh;
     copy_tile<TK, NW>(B.K, Kb + ck * CHUNK * D, cl, wave);
-    copy_tile<TKt, NW>(B.Kt, Ktb + ck * D * CHUNK, cl, wave);
+    if constexpr (!RB::KT_TR) copy_tile<TKt, NW>(B.Kt, Ktb + ck * D * CHUNK, cl, wave);
     copy_tile<TKt, NW>(B.Qt, Qtb + ck * D * CHUNK, cl, wave);
     copy_tile<TM, NW>(B.Pt, Ptb + ch * CHUNK * CHUNK, cl, wave);
     copy_tile<TM, NW>(B.Mt, Mtb + ch * CHUNK * CHUNK, cl, wave);
@@ -158,7 +160,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int Lc = rem < CHUNK ? (int)rem : CHUNK;
     const int64_t ch = (int64_t)c * Hv + h, ck = (int64_t)c * Hk + kh;
     touch_tile(Kb + ck * CHUNK * D, TKB, NTK, wave);
-    touch_tile(Ktb + ck * D * CHUNK, TKB, NTK, wave);
+    if constexpr (!RB::KT_TR) touch_tile(Ktb + ck * D * CHUNK, TKB, NTK, wave);
     touch_tile(Qtb + ck * D * CHUNK, TKB, NTK, wave);
     touch_tile(Ptb + ch * CHUNK * CHUNK, TMB, NTM, wave);
     touch_tile(Mtb + ch * CHUNK * CHUNK, TMB, NTM, wave);
@@ -168,11 +170,25 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
         (__attribute__((address_space(3))) void*)sink, 4, (uint32_t)(2 * lane + wave) * rowb, 0, 0, 0);
   };
   // touches a mover issues per step
-  constexpr int NTOUCH = 3 * NTK + 2 * NTM + 1;
+  constexpr int NTOUCH = (RB::KT_TR ? 2 : 3) * NTK + 2 * NTM + 1;
 
   auto arow = [&](const T* base, int o, int tile_elems) __attribute__((always_inline)) -> frag {
     if constexpr (KS == 4) return base[tile_elems + o];
     else return *reinterpret_cast<const frag*>(base + tile_elems + o);
+  };
+  // A operand of step p from rows 16 kt + c16 of K^T (columns t in
+  // accumulator order).  16-bit: two transposing reads of the K rows, whose
+  // columns k are in accumulator order too: lanes 4a .. 4a + 3 of a group
+  // take stored columns 32 (kt / 2) + 8 a + 4 (kt % 2) .. + 3, and lane j of
+  // group g points at token row 32 p + 4 g + j / 4 (then 16 rows further).
+  auto kt_frag = [&](const RB& B, int kt, int p) __attribute__((always_inline)) -> frag {
+    if constexpr (RB::KT_TR) {
+      const int col = 32 * (kt >> 1) + 8 * (c16 & 3) + 4 * (kt & 1), r = 32 * p + g4 + (c16 >> 2);
+      const u32x2 lo = lds_read_tr4(B.K + TK::at(r, col)), hi = lds_read_tr4(B.K + TK::at(r + 16, col));
+      return __builtin_bit_cast(frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    } else {
+      return arow(B.Kt, rk[p], 16 * kt * CHUNK);
+    }
   };
 
   auto compute = [&](const RB& B, int64_t c) __attribute__((always_inline)) {
@@ -269,7 +285,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
 #pragma unroll
         for (int p = 0; p < NSC; ++p) {
           dS[kt] = MM::mma(arow(B.Qt, rk[p], 16 * kt * CHUNK), gob[p], dS[kt]);
-          dS[kt] = MM::mma(arow(B.Kt, rk[p], 16 * kt * CHUNK), gf[p], dS[kt]);
+          dS[kt] = MM::mma(kt_frag(B, kt, p), gf[p], dS[kt]);
         }
       }
     }

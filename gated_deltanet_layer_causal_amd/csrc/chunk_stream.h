@@ -70,10 +70,6 @@ template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
   }
 };
 
-// Direct copy of one 16-byte piece per lane from a buffer into LDS: the
-// wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
-// Buffer accesses are range-checked against the descriptor's size on the
-// per-lane offset (loads past it read zero, stores past it are dropped).
 // Transposing LDS read of 16-bit elements: within each group of 16 lanes,
 // lane j passes the address of row k0 + j / 4, columns n0 + 4 (j % 4) .. + 3
 // of a row-major tile (8-byte aligned), and lane i receives rows k0 .. k0 + 3
@@ -90,6 +86,10 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const void* p) {
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// Direct copy of one 16-byte piece per lane from a buffer into LDS: the
+// wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
+// Buffer accesses are range-checked against the descriptor's size on the
+// per-lane offset (loads past it read zero, stores past it are dropped).
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
                                             uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
