@@ -60,6 +60,8 @@ struct ChunkLayout {
   size_t q16w;        // CT [nt_max][hk][64][dk]: Q rows of each chunk (zero past its end)
   size_t gw, dw;      // fp32 [nt_max][hv][64]: Gam_t and dec_t (clamped to the chunk length)
   size_t kb, ktb, qtb; // T [nt_max][hk]: K rows [64][dk], K^T and Q^T [dk][64] (backward)
+  size_t k16w;        // CT [nt_max][hk][64][dk]: K rows, columns in accumulator order
+                      // (backward, 16-bit types: the saved-state pass reads these in place of W, K^T)
   size_t ptb, mtb;    // T [nt_max][hv][64][64]: P^T, M^T (backward)
   size_t tib;         // T [nt_max][hv][2][64][64]: Tinv (columns in accumulator order), Tinv^T (backward)
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
@@ -98,6 +100,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.dw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.total_fwd = off;
   L.kb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * CHUNK * s.dk);
+  L.k16w = off; off = align256(off + (es == 2 ? 2 * (size_t)L.nt_max * s.hk * CHUNK * s.dk : 0));
   L.ktb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.qtb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.ptb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);

@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     double* __restrict__ gcum, typename Compute<T>::type* __restrict__ Mw,
     typename Compute<T>::type* __restrict__ Pw, typename Compute<T>::type* __restrict__ Ww,
     typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
-    float* __restrict__ Gw, float* __restrict__ Dw,
+    typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw,
     T* __restrict__ Kb, T* __restrict__ Ktb, T* __restrict__ Qtb, T* __restrict__ Ptb,
     T* __restrict__ Mtb, T* __restrict__ Tib) {
   typedef typename Compute<T>::type CT;
@@ -77,6 +77,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   constexpr int LD = D + Pad<CT>::v;
   constexpr int KT_LD = PrepSmem<T, D>::KT_LD;
   constexpr int KS = MM::KS;
+  // backward, 16-bit types: the saved-state pass works from the K rows (in
+  // the compute type) and needs neither W nor the compute-type K^T
+  constexpr bool KROWS = BWD && sizeof(T) == 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x;
   const int kh = blockIdx.y;
@@ -105,6 +108,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     // Q rows (compute type, zero past the chunk end, columns in accumulator
     // order; read only by the forward pass without saved states) to the
     // workspace, in 4-element pieces; K rows in the storage type (backward)
+    // and, for 16-bit types, in the compute type
     constexpr int PR = D / 4;
     const int64_t base = ((int64_t)c * (Hv / G) + kh) * CHUNK * D;
     for (int i = tid; i < CHUNK * PR; i += 256) {
@@ -115,6 +119,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       if constexpr (BWD)
         store4(Kb + base + dst, to_f(sm.K[r][c4]), to_f(sm.K[r][c4 + 1]), to_f(sm.K[r][c4 + 2]),
                to_f(sm.K[r][c4 + 3]));
+      if constexpr (KROWS) *reinterpret_cast<v4*>(K16w + base + dst) = *reinterpret_cast<const v4*>(&sm.K[r][c4]);
     }
     if constexpr (BWD) {
       // Q^T in the storage type, columns (tokens) in accumulator order
@@ -140,8 +145,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     for (int i = tid; i < D * PR; i += 256) {
       const int kr = i / PR, c4 = (i % PR) * 4;
       typedef CT v4 __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
-          *reinterpret_cast<const v4*>(&sm.u.Kt[kr][c4]);
+      if constexpr (!KROWS)
+        *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
+            *reinterpret_cast<const v4*>(&sm.u.Kt[kr][c4]);
       if constexpr (BWD) {
         store4(Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4),
                to_f(sm.u.Kt[kr][c4]), to_f(sm.u.Kt[kr][c4 + 1]), to_f(sm.u.Kt[kr][c4 + 2]),
@@ -226,7 +232,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead
     // A storage (columns in accumulator order), then all rows go out in
     // 16-byte pieces.  beta Gam scales the A operand (Tinv columns).
-    {
+    if constexpr (!KROWS) {
       typedef typename MM::frag frag;
       frag ta[CHUNK / KS];
 #pragma unroll
@@ -281,7 +287,8 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        (typename Compute<T>::type*)(ws + Ly.pw),
                        (typename Compute<T>::type*)(ws + Ly.ww),
                        (typename Compute<T>::type*)(ws + Ly.ktw),
-                       (typename Compute<T>::type*)(ws + Ly.q16w), (float*)(ws + Ly.gw),
+                       (typename Compute<T>::type*)(ws + Ly.q16w),
+                       BWD ? (typename Compute<T>::type*)(ws + Ly.k16w) : nullptr, (float*)(ws + Ly.gw),
                        (float*)(ws + Ly.dw), BWD ? (T*)(ws + Ly.kb) : nullptr,
                        BWD ? (T*)(ws + Ly.ktb) : nullptr, BWD ? (T*)(ws + Ly.qtb) : nullptr,
                        BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (T*)(ws + Ly.mtb) : nullptr,

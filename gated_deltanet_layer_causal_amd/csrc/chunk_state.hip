@@ -8,7 +8,10 @@
 // and the outputs O = diag(Gam) scale Q S^T + P Delta (MODE 0), or the
 // chunk-start states S themselves (MODE 1), from which chunk_out.hip forms
 // R, Delta and O chunk by chunk in parallel.  Only the two products through
-// S are sequential; everything else hangs off them.
+// S are sequential; everything else hangs off them.  MODE 1 with 16-bit
+// types takes the K rows alone: Delta = M R with R = V - diag(Gam) K S^T
+// (W S^T = M diag(Gam) K S^T), and K^T for the update comes from the same
+// rows by transposing LDS reads, so a chunk copies K, M and V only.
 //
 // One workgroup per (sequence, value head, block of 16 * NW value rows of the
 // state); wave w owns 16 value rows and keeps its d_k x 16 slice of S^T in
@@ -39,8 +42,9 @@ template <typename T, int D, int NW, int MODE> struct StateBuf {
   typedef Tile<CT, D, CHUNK> TKt;       // K^T
   typedef Tile<CT, CHUNK, CHUNK> TM;    // M, P
   typedef Tile<T, CHUNK, BV, 3> TV;     // value rows (storage type)
-  CT W[TW::PIECES * TW::EPP];
-  CT Kt[TKt::PIECES * TKt::EPP];
+  static constexpr bool KR = MODE == 1 && sizeof(T) == 2;   // the K-rows form
+  CT W[TW::PIECES * TW::EPP];           // W, or the K rows (KR)
+  CT Kt[KR ? 8 : TKt::PIECES * TKt::EPP];
   CT X[MODE == 0 ? TW::PIECES * TW::EPP : 8];   // Q rows
   CT M[TM::PIECES * TM::EPP];
   CT P[MODE == 0 ? TM::PIECES * TM::EPP : 8];
@@ -129,9 +133,9 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     const int64_t rem = seq_t1 - t0;
     const int Lc = rem < CHUNK ? (int)rem : CHUNK;
     const int64_t ch = (int64_t)c * Hv + h, ck_ = (int64_t)c * Hk + kh;
-    copy_tile<TW, NW>(B.W, Ww + ch * CHUNK * D, cl, wave);
+    copy_tile<TW, NW>(B.W, Ww + (SB::KR ? ck_ : ch) * CHUNK * D, cl, wave);
     if constexpr (MODE == 0) copy_tile<TW, NW>(B.X, Xw + ck_ * CHUNK * D, cl, wave);
-    copy_tile<TKt, NW>(B.Kt, Ktw + ck_ * D * CHUNK, cl, wave);
+    if constexpr (!SB::KR) copy_tile<TKt, NW>(B.Kt, Ktw + ck_ * D * CHUNK, cl, wave);
     copy_tile<TM, NW>(B.M, Mw + ch * CHUNK * CHUNK, cl, wave);
     if constexpr (MODE == 0) copy_tile<TM, NW>(B.P, Pw + ch * CHUNK * CHUNK, cl, wave);
     {
@@ -153,7 +157,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     }
   };
   // copies a wave issues per fetch, and stores per chunk (MODE 1)
-  constexpr int NCOPY = TW::PIECES / THREADS * (MODE == 0 ? 2 : 1) + TKt::PIECES / THREADS +
+  constexpr int NCOPY = TW::PIECES / THREADS * (MODE == 0 ? 2 : 1) + (SB::KR ? 0 : TKt::PIECES / THREADS) +
                         TM::PIECES / THREADS * (MODE == 0 ? 2 : 1) + TV::PIECES / THREADS +
                         (NW == 1 ? 2 : 1);
   constexpr int NSTORE = NKT * 2;
@@ -177,12 +181,57 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
     else return *reinterpret_cast<const frag*>(base + tile_elems + o);
   };
 
+  // A operand of step p from rows 16 kt + c16 of K^T (columns t in
+  // accumulator order): the K^T tile, or in the K-rows form two transposing
+  // reads of the K rows (columns k in accumulator order): lanes 4a .. 4a + 3
+  // of a group take stored columns 32 (kt / 2) + 8 a + 4 (kt % 2) .. + 3, and
+  // lane j of group g points at token row 32 p + 4 g + j / 4 (then 16 rows
+  // further)
+  auto kt_frag = [&](const SB& B, int kt, int p) __attribute__((always_inline)) -> frag {
+    if constexpr (SB::KR) {
+      const int col = 32 * (kt >> 1) + 8 * (c16 & 3) + 4 * (kt & 1), r = 32 * p + g4 + (c16 >> 2);
+      const u32x2 lo = lds_read_tr4(B.W + TW::at(r, col)), hi = lds_read_tr4(B.W + TW::at(r + 16, col));
+      return __builtin_bit_cast(frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    } else {
+      return arow(B.Kt, rk[p], 16 * kt * CHUNK);
+    }
+  };
+
   // ---- one chunk from buffer B
   auto compute = [&](const SB& B, int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
     const int64_t rem = seq_t1 - t0;
     const int L = rem < CHUNK ? (int)rem : CHUNK;
 
+    floatx4 Dl[4];
+    if constexpr (SB::KR) {
+      // R = V - diag(Gam) K S^T (rows t = 16 tt + g4 + i, column vcol), then
+      // Delta = M R with R straight from the accumulators
+      frag sb[NSD];
+#pragma unroll
+      for (int p = 0; p < NSD; ++p) sb[p] = AO::from_acc(S, p);
+      floatx4 R[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        floatx4 kx = zero4();
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) kx = MM::mma(arow(B.W, rw[p], 16 * tt * D), sb[p], kx);
+        const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
+        const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R[tt][i] = to_f(B.V[TV::at(16 * tt + g4 + i, vcol)]) - gv[i] * kx[i];
+      }
+      frag rf[NSC];
+#pragma unroll
+      for (int p = 0; p < NSC; ++p) rf[p] = AO::from_acc(R, p);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        Dl[tt] = zero4();
+#pragma unroll
+        for (int p = 0; p < NSC; ++p)
+          Dl[tt] = MM::mma(*reinterpret_cast<const frag*>(B.M + 16 * tt * CHUNK + rk[p]), rf[p], Dl[tt]);
+      }
+    } else {
     // -S^T as B operands, straight from the accumulators
     frag sbn[NSD];
 #pragma unroll
@@ -190,7 +239,6 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
 
     // Delta = W (-S^T) + M V; V is gathered in accumulator order, as M's
     // columns are stored
-    floatx4 Dl[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       Dl[tt] = zero4();
@@ -219,10 +267,14 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
           Dl[tt] = MM::mma(ma, bv[p], Dl[tt]);
         }
     }
+    }
 
     // Q (-S^T) (MODE 0)
     floatx4 xs[4];
     if constexpr (MODE == 0) {
+      frag sbn[NSD];
+#pragma unroll
+      for (int p = 0; p < NSD; ++p) sbn[p] = -AO::from_acc(S, p);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         xs[tt] = zero4();
@@ -251,7 +303,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[kt][i] *= GL;
 #pragma unroll
-        for (int p = 0; p < NSC; ++p) S[kt] = MM::mma(arow(B.Kt, rk[p], 16 * kt * CHUNK), dsf[p], S[kt]);
+        for (int p = 0; p < NSC; ++p) S[kt] = MM::mma(kt_frag(B, kt, p), dsf[p], S[kt]);
       }
     }
 
@@ -342,7 +394,8 @@ static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, fl
   const int n_items = (D / BV) * s.hv * s.n_seq;
   hipLaunchKernelGGL(kern, dim3(n_items), dim3(64 * NW), 0, st, (const T*)v, ldv, cu,
                      (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
-                     (const CT*)(ws + Ly.mw), (const CT*)(ws + Ly.pw), (const CT*)(ws + Ly.ww),
+                     (const CT*)(ws + Ly.mw), (const CT*)(ws + Ly.pw),
+                     (const CT*)(ws + (StateBuf<T, D, NW, MODE>::KR ? Ly.k16w : Ly.ww)),
                      (const CT*)(ws + Ly.ktw), (const CT*)(ws + Ly.q16w),
                      (const float*)(ws + Ly.gw), (const float*)(ws + Ly.dw), S0, S_final, (T*)o,
                      (T*)(ws + Ly.h), n_items);
