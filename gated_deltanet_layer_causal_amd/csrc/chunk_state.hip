@@ -53,7 +53,7 @@ template <typename T, int D, int NW, int MODE> struct StateBuf {
 } __attribute__((aligned(16)));
 
 template <typename T, int D, int NW, int MODE>
-__global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
+__global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 * NW)) chunk_state_kernel(
     const T* __restrict__ v, int64_t ldv, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
     const typename Compute<T>::type* __restrict__ Mw, const typename Compute<T>::type* __restrict__ Pw,
@@ -83,8 +83,10 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
   __shared__ SB bufA, bufB;
 
   const int tid = threadIdx.x, lane = tid & 63;
+  // (K-rows form: waves [0, NW) compute, waves [NW, 2 NW) move the operands)
   const int wave_ = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave = wave_;
+  const bool mover = SB::KR && wave_ >= NW;
+  const int wave = mover ? wave_ - NW : wave_;
   const int item = xcd_item(blockIdx.x, n_items);
   const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
   const int kh = h / G, Hk = Hv / G;
@@ -127,7 +129,7 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
   auto fetch = [&](SB& B, int64_t c) __attribute__((always_inline)) {
     // LDS destinations derived from a laundered wave index are formed here
     // (one scalar add each) instead of being hoisted into scalar registers.
-    int wave = wave_;
+    int wave = SB::KR ? wave_ - NW : wave_;   // (K-rows form: movers only)
     asm volatile("" : "+s"(wave));
     const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
     const int64_t rem = seq_t1 - t0;
@@ -343,6 +345,47 @@ __global__ void __launch_bounds__(64 * NW) chunk_state_kernel(
         __syncthreads();
       }
     }
+  } else if constexpr (SB::KR) {
+    // three buffers, the copies two chunks ahead, issued by the movers: a
+    // step ends once the movers' copies for the next chunk (issued a step
+    // earlier) are in, this step's NCOPY still in flight; the compute waves
+    // only store the chunk's state and compute.  Past the end the last chunk
+    // is copied again.
+    __shared__ SB bufC;
+    auto last = [&](int64_t x) { return x < c_end ? x : c_end - 1; };
+    if (mover) {
+      if (c_begin < c_end) {
+        fetch(bufA, c_begin);
+        fetch(bufB, last(c_begin + 1));
+      }
+      wait_vm_barrier<NCOPY>();
+      for (int64_t c = c_begin; c < c_end; c += 3) {
+        fetch(bufC, last(c + 2));
+        wait_vm_barrier<NCOPY>();
+        if (c + 1 >= c_end) break;
+        fetch(bufA, last(c + 3));
+        wait_vm_barrier<NCOPY>();
+        if (c + 2 >= c_end) break;
+        fetch(bufB, last(c + 4));
+        wait_vm_barrier<NCOPY>();
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return;
+    }
+    lds_barrier();
+    for (int64_t c = c_begin; c < c_end; c += 3) {
+      store_state(c);
+      compute(bufA, c);
+      lds_barrier();
+      if (c + 1 >= c_end) break;
+      store_state(c + 1);
+      compute(bufB, c + 1);
+      lds_barrier();
+      if (c + 2 >= c_end) break;
+      store_state(c + 2);
+      compute(bufC, c + 2);
+      lds_barrier();
+    }
   } else {
     // three buffers: the copies run two chunks ahead.  A step issues the
     // chunk's state stores, then the copies for chunk c + 2, then computes
@@ -392,7 +435,8 @@ static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, fl
   typedef typename Compute<T>::type CT;
   auto kern = chunk_state_kernel<T, D, NW, MODE>;
   const int n_items = (D / BV) * s.hv * s.n_seq;
-  hipLaunchKernelGGL(kern, dim3(n_items), dim3(64 * NW), 0, st, (const T*)v, ldv, cu,
+  hipLaunchKernelGGL(kern, dim3(n_items), dim3((StateBuf<T, D, NW, MODE>::KR ? 128 : 64) * NW), 0, st,
+                     (const T*)v, ldv, cu,
                      (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
                      (const CT*)(ws + Ly.mw), (const CT*)(ws + Ly.pw),
                      (const CT*)(ws + (StateBuf<T, D, NW, MODE>::KR ? Ly.k16w : Ly.ww)),
