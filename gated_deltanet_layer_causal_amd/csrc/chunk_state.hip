@@ -176,6 +176,15 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, S[kt]);
   };
+  // (K-rows form: through the wave's LDS rows, in 16-byte stores)
+  typedef StageRows<T> SR;
+  auto stage_state = [&](char* stg, int64_t c) __attribute__((always_inline)) {
+    char* const myst = stg + wave * D * SR::SB;
+    const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, S[kt]);
+    SR::flush(myst, 0, D, rs, (uint32_t)(16 * wave * sizeof(T)), rowh, lane);
+  };
 
   // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).
   auto arow = [&](const CT* base, int o, int tile_elems) __attribute__((always_inline)) -> frag {
@@ -352,6 +361,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     // only store the chunk's state and compute.  Past the end the last chunk
     // is copied again.
     __shared__ SB bufC;
+    __shared__ __align__(16) char stg[NW * D * SR::SB];
     auto last = [&](int64_t x) { return x < c_end ? x : c_end - 1; };
     if (mover) {
       if (c_begin < c_end) {
@@ -374,15 +384,15 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     }
     lds_barrier();
     for (int64_t c = c_begin; c < c_end; c += 3) {
-      store_state(c);
+      stage_state(stg, c);
       compute(bufA, c);
       lds_barrier();
       if (c + 1 >= c_end) break;
-      store_state(c + 1);
+      stage_state(stg, c + 1);
       compute(bufB, c + 1);
       lds_barrier();
       if (c + 2 >= c_end) break;
-      store_state(c + 2);
+      stage_state(stg, c + 2);
       compute(bufC, c + 2);
       lds_barrier();
     }
