@@ -98,16 +98,25 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
         return "hbm", 3 * hv * d * E                  # read o, z; write y
     if name == "norm_bwd":
         return "hbm", 5 * hv * d * E                  # read o, z, dy; write do, dz
-    fwd_bytes = 2 * hk * d * E + 3 * hk * d * E + hv * (4 + 4 + 8 + 2 * C64 * E + d * E + 8)
-    bwd_extra = 3 * hk * d * E + hv * (2 * C64 * E + 4 * C64)
+    # preparation: reads q, k (per key head) and g, beta (per value head); per
+    # value head writes gamma (fp64), Gam and dec (fp32), M and P.  Forward
+    # mode adds, per key head, K^T and the Q rows in the compute type and, per
+    # value head, W.  Backward mode adds per key head the K rows, K^T and Q^T
+    # in the storage type and one more key-head tile (the K rows in the
+    # compute type for 16-bit data, the compute-type K^T for fp32), per value
+    # head P^T, M^T, Tinv and Tinv^T (and W for fp32).
+    per_hv = 4 + 4 + 8 + 8 + 2 * C64 * E
+    fwd_bytes = 2 * hk * d * E + 2 * hk * d * E + hv * (per_hv + d * E)
+    bwd_bytes = 2 * hk * d * E + 4 * hk * d * E + hv * (per_hv + 4 * C64 * E + (d * E if E == 4 else 0))
     if name == "chunk_prepare":
-        return "hbm", fwd_bytes + (bwd_extra if saved else 0)
+        return "hbm", bwd_bytes if saved else fwd_bytes
     if name == "chunk_prepare_b":
-        return "hbm", fwd_bytes + bwd_extra
+        return "hbm", bwd_bytes
     # products formed per v-head token: the forward pass without saved
-    # states (W S^T, Q S^T, update; M V, P Delta); the saved-state pass (W S^T,
-    # update; M V) and the chunk-parallel outputs (K S^T, Q S^T; M R, P Delta),
-    # whose O part the recompute flow leaves out
+    # states (W S^T, Q S^T, update; M V, P Delta); the saved-state pass (K S^T,
+    # update; M R for 16-bit data, W S^T, update; M V for fp32) and the
+    # chunk-parallel outputs (K S^T, Q S^T; M R, P Delta), whose O part the
+    # recompute flow leaves out
     fwd_states = hv * (6 * d * d + 4 * C64 * d)
     save_pass = hv * (4 * d * d + 2 * C64 * d)
     outputs = hv * (4 * d * d + 4 * C64 * d)
