@@ -156,11 +156,26 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     }
   }
 
+  // the gates of the next head load a head ahead (wave 0), out of the way
+  // of the barrier that follows their scan
+  float gnx = 0.f, bnx = 0.f;
+  auto load_gates = [&](int h) __attribute__((always_inline)) {
+    if (wave == 0 && lane < L) {
+      gnx = g[(t0 + lane) * Hv + h];
+      bnx = beta[(t0 + lane) * Hv + h];
+    }
+  };
+  load_gates(kh * G);
   for (int hh = 0; hh < G; ++hh) {
     const int h = kh * G + hh;
     if (wave == 0) {
-      const double gl = lane < L ? (double)g[(t0 + lane) * Hv + h] : 0.0;
-      const float bl = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
+      // (taken before the next head's loads go out, so the wait for them
+      // leaves those in flight)
+      float gcur = gnx, bcur = bnx;
+      asm volatile("" : "+v"(gcur), "+v"(bcur));
+      const double gl = lane < L ? (double)gcur : 0.0;
+      const float bl = lane < L ? bcur : 0.f;
+      if (hh + 1 < G) load_gates(h + 1);
       const double gm = wave_incl_scan(gl, lane);
       sm.gam[lane] = gm;
       sm.bet[lane] = bl;
