@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t* __restr
 // Tinv (fp32), and the MFMA operands M = Tinv diag(beta), P and
 // W = M diag(Gam) K, with the per-token factors Gam_t and dec_t.
 template <typename T, int D>
-struct PrepSmem {
+struct PrepStage {                 // the chunk's K and Q rows
   typedef typename Compute<T>::type CT;
   static constexpr int KT_LD = CHUNK + Pad<CT>::v;
   CT K[CHUNK][D + Pad<CT>::v];
@@ -49,18 +49,35 @@ struct PrepSmem {
     CT Q[CHUNK][D + Pad<CT>::v];   // until Q K^T is formed
     CT Kt[D][KT_LD];               // then K^T
   } u;
+};
+struct PrepHead {                  // per value head: A, then Tinv
   float A[CHUNK][68];
   float Ti[CHUNK][68];
+};
+// With OVERLAY (backward mode, 16-bit types: no W, so the head loop reads no
+// K row or K^T from LDS) A and Ti take the staging's storage once the key
+// head's outputs are out, which halves the block's LDS.
+template <typename T, int D, bool OVERLAY>
+struct PrepSmem {
+  typedef typename Compute<T>::type CT;
+  static constexpr int KT_LD = PrepStage<T, D>::KT_LD;
+  static constexpr size_t SB = sizeof(PrepStage<T, D>), HB = sizeof(PrepHead);
+  static constexpr size_t RAW = OVERLAY ? (SB > HB ? SB : HB) : SB + HB;
+  __align__(16) unsigned char raw[RAW];
   float X[16][17];
   double gam[CHUNK];
   float bet[CHUNK];
   float sbg[CHUNK];                // beta_s Gam_s
+  __device__ PrepStage<T, D>& st() { return *reinterpret_cast<PrepStage<T, D>*>(raw); }
+  __device__ PrepHead& hd() { return *reinterpret_cast<PrepHead*>(raw + (OVERLAY ? 0 : SB)); }
   static_assert(sizeof(CT) * CHUNK * (D + Pad<CT>::v) <= sizeof(float) * CHUNK * 68,
                 "W tile fits in the A storage");
 };
 
+// Three blocks per CU for 16-bit types (168 VGPRs; the backward mode's overlaid
+// LDS is 37 KB): the head loop is a chain of short phases between barriers.
 template <typename T, int D, bool BWD>
-__global__ void __launch_bounds__(256) chunk_prep_kernel(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1))) chunk_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G, float scale,
@@ -73,13 +90,18 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  PrepSmem<T, D>& sm = *reinterpret_cast<PrepSmem<T, D>*>(smem_raw);
-  constexpr int LD = D + Pad<CT>::v;
-  constexpr int KT_LD = PrepSmem<T, D>::KT_LD;
-  constexpr int KS = MM::KS;
   // backward, 16-bit types: the saved-state pass works from the K rows (in
   // the compute type) and needs neither W nor the compute-type K^T
   constexpr bool KROWS = BWD && sizeof(T) == 2;
+  typedef PrepSmem<T, D, KROWS> SM;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  auto& sK = sm.st().K;
+  auto& su = sm.st().u;
+  auto& sA = sm.hd().A;
+  auto& sTi = sm.hd().Ti;
+  constexpr int LD = D + Pad<CT>::v;
+  constexpr int KT_LD = SM::KT_LD;
+  constexpr int KS = MM::KS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x;
   const int kh = blockIdx.y;
@@ -88,8 +110,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   int L;
   chunk_span(seq_off, cu, n_seq, c, t0, L);
 
-  stage_rows<CT, D>(&sm.K[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-  stage_rows<CT, D>(&sm.u.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+  stage_rows<CT, D>(&sK[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
+  stage_rows<CT, D>(&su.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
   __syncthreads();
 
   // wave w owns rows [16w, 16w+16) of the 64 x 64 products
@@ -97,9 +119,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   floatx4 kk[4], qk[4], kq[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    kk[j] = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
-    qk[j] = tile_mma<CT, true, true>(zero4(), &sm.u.Q[0][0], LD, &sm.K[0][0], LD, 16 * wave, 16 * j, D, lane);
-    kq[j] = tile_mma<CT, true, true>(zero4(), &sm.K[0][0], LD, &sm.u.Q[0][0], LD, 16 * wave, 16 * j, D, lane);
+    kk[j] = tile_mma<CT, true, true>(zero4(), &sK[0][0], LD, &sK[0][0], LD, 16 * wave, 16 * j, D, lane);
+    qk[j] = tile_mma<CT, true, true>(zero4(), &su.Q[0][0], LD, &sK[0][0], LD, 16 * wave, 16 * j, D, lane);
+    kq[j] = tile_mma<CT, true, true>(zero4(), &sK[0][0], LD, &su.Q[0][0], LD, 16 * wave, 16 * j, D, lane);
   }
   const int rbase = 16 * wave + 4 * (lane >> 4);
   const int ccol = lane & 15;
@@ -115,29 +137,34 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       const int r = i / PR, c4 = (i % PR) * 4;
       typedef CT v4 __attribute__((ext_vector_type(4)));
       const int dst = r * D + acc_col<CT>(c4);
-      if constexpr (!BWD) *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&sm.u.Q[r][c4]);
+      if constexpr (!BWD) *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&su.Q[r][c4]);
       if constexpr (BWD)
-        store4(Kb + base + dst, to_f(sm.K[r][c4]), to_f(sm.K[r][c4 + 1]), to_f(sm.K[r][c4 + 2]),
-               to_f(sm.K[r][c4 + 3]));
-      if constexpr (KROWS) *reinterpret_cast<v4*>(K16w + base + dst) = *reinterpret_cast<const v4*>(&sm.K[r][c4]);
+        store4(Kb + base + dst, to_f(sK[r][c4]), to_f(sK[r][c4 + 1]), to_f(sK[r][c4 + 2]),
+               to_f(sK[r][c4 + 3]));
+      if constexpr (KROWS) *reinterpret_cast<v4*>(K16w + base + dst) = *reinterpret_cast<const v4*>(&sK[r][c4]);
     }
     if constexpr (BWD) {
       // Q^T in the storage type, columns (tokens) in accumulator order
       T* qo = Qtb + base;
       for (int i = tid; i < D * (CHUNK / 4); i += 256) {
         const int kr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
-        store4(qo + kr * CHUNK + acc_col<T>(t4), to_f(sm.u.Q[t4][kr]), to_f(sm.u.Q[t4 + 1][kr]),
-               to_f(sm.u.Q[t4 + 2][kr]), to_f(sm.u.Q[t4 + 3][kr]));
+        store4(qo + kr * CHUNK + acc_col<T>(t4), to_f(su.Q[t4][kr]), to_f(su.Q[t4 + 1][kr]),
+               to_f(su.Q[t4 + 2][kr]), to_f(su.Q[t4 + 3][kr]));
+        // K^T likewise, gathered from the K rows (no LDS transpose: A and
+        // Ti take this storage in the head loop, after its first barrier)
+        if constexpr (KROWS)
+          store4(Ktb + base + kr * CHUNK + acc_col<T>(t4), to_f(sK[t4][kr]), to_f(sK[t4 + 1][kr]),
+                 to_f(sK[t4 + 2][kr]), to_f(sK[t4 + 3][kr]));
       }
     }
   }
-  __syncthreads();  // Q is dead: its storage takes K^T
-  for (int i = tid; i < CHUNK * D; i += 256) {
-    const int kc = i % D, sr = i / D;
-    sm.u.Kt[kc][sr] = sm.K[sr][kc];
-  }
-  __syncthreads();
-  {
+  if constexpr (!KROWS) {
+    __syncthreads();  // Q is dead: its storage takes K^T
+    for (int i = tid; i < CHUNK * D; i += 256) {
+      const int kc = i % D, sr = i / D;
+      su.Kt[kc][sr] = sK[sr][kc];
+    }
+    __syncthreads();
     // K^T rows of 64 (columns in accumulator order) to the workspace, in
     // 4-element pieces
     constexpr int PR = CHUNK / 4;
@@ -145,13 +172,12 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
     for (int i = tid; i < D * PR; i += 256) {
       const int kr = i / PR, c4 = (i % PR) * 4;
       typedef CT v4 __attribute__((ext_vector_type(4)));
-      if constexpr (!KROWS)
-        *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
-            *reinterpret_cast<const v4*>(&sm.u.Kt[kr][c4]);
+      *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
+          *reinterpret_cast<const v4*>(&su.Kt[kr][c4]);
       if constexpr (BWD) {
         store4(Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4),
-               to_f(sm.u.Kt[kr][c4]), to_f(sm.u.Kt[kr][c4 + 1]), to_f(sm.u.Kt[kr][c4 + 2]),
-               to_f(sm.u.Kt[kr][c4 + 3]));
+               to_f(su.Kt[kr][c4]), to_f(su.Kt[kr][c4 + 1]), to_f(su.Kt[kr][c4 + 2]),
+               to_f(su.Kt[kr][c4 + 3]));
       }
     }
   }
@@ -200,7 +226,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       for (int e = 0; e < 4; ++e) {
         const int t = rbase + e;
         const float dec = dexp<T>(sm.gam[t] - sm.gam[s <= t ? s : t]);  // masked before exp
-        sm.A[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
+        sA[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
         pv[e] = (s <= t) ? dec * scale * qk[j][e] : 0.f;
       }
       if constexpr (BWD)
@@ -215,12 +241,12 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       store4(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();
-    invert_unit_lower(sm.A, sm.Ti, sm.X, tid);
+    invert_unit_lower(sA, sTi, sm.X, tid);
     // M = Tinv diag(beta), columns in accumulator order, in 4-element pieces
     CT* Mout = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
     for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
       const int t = i / (CHUNK / 4), s4 = (i % (CHUNK / 4)) * 4;
-      const float4 ti = *reinterpret_cast<const float4*>(&sm.Ti[t][s4]);
+      const float4 ti = *reinterpret_cast<const float4*>(&sTi[t][s4]);
       store4(Mout + t * CHUNK + acc_col<CT>(s4), ti.x * sm.bet[s4], ti.y * sm.bet[s4 + 1],
              ti.z * sm.bet[s4 + 2], ti.w * sm.bet[s4 + 3]);
     }
@@ -230,18 +256,18 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       T* to = Tib + ((int64_t)c * Hv + h) * 2 * CHUNK * CHUNK;
       for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
         const int r = i / (CHUNK / 4), c4 = (i % (CHUNK / 4)) * 4;
-        const float4 ti = *reinterpret_cast<const float4*>(&sm.Ti[r][c4]);
+        const float4 ti = *reinterpret_cast<const float4*>(&sTi[r][c4]);
         store4(to + r * CHUNK + acc_col<T>(c4), ti.x, ti.y, ti.z, ti.w);
-        store4(to + CHUNK * CHUNK + r * CHUNK + c4, sm.Ti[c4][r], sm.Ti[c4 + 1][r], sm.Ti[c4 + 2][r],
-               sm.Ti[c4 + 3][r]);
+        store4(to + CHUNK * CHUNK + r * CHUNK + c4, sTi[c4][r], sTi[c4 + 1][r], sTi[c4 + 2][r],
+               sTi[c4 + 3][r]);
       }
       // M^T in the storage type, columns (tokens t) in accumulator order
       T* mo = Mtb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
       for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
         const int sr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
         const float b = sm.bet[sr];
-        store4(mo + sr * CHUNK + acc_col<T>(t4), sm.Ti[t4][sr] * b, sm.Ti[t4 + 1][sr] * b,
-               sm.Ti[t4 + 2][sr] * b, sm.Ti[t4 + 3][sr] * b);
+        store4(mo + sr * CHUNK + acc_col<T>(t4), sTi[t4][sr] * b, sTi[t4 + 1][sr] * b,
+               sTi[t4 + 2][sr] * b, sTi[t4 + 3][sr] * b);
       }
     }
     // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead
@@ -254,22 +280,22 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
       for (int s0 = 0; s0 < CHUNK / KS; ++s0) {
         if constexpr (KS == 4) {
           const int sc = s0 * KS + (lane >> 4);
-          ta[s0] = sm.Ti[16 * wave + r16][sc] * sm.sbg[sc];
+          ta[s0] = sTi[16 * wave + r16][sc] * sm.sbg[sc];
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int sc = s0 * KS + 8 * (lane >> 4) + j;
-            ta[s0][j] = (CT)(sm.Ti[16 * wave + r16][sc] * sm.sbg[sc]);
+            ta[s0][j] = (CT)(sTi[16 * wave + r16][sc] * sm.sbg[sc]);
           }
         }
       }
-      CT (*Wl)[LD] = reinterpret_cast<CT (*)[LD]>(&sm.A[0][0]);
+      CT (*Wl)[LD] = reinterpret_cast<CT (*)[LD]>(&sA[0][0]);
 #pragma unroll
       for (int kt = 0; kt < D / 16; ++kt) {
         floatx4 acc = zero4();
 #pragma unroll
         for (int s0 = 0; s0 < CHUNK / KS; ++s0)
-          acc = MM::mma(ta[s0], MM::kc(&sm.u.Kt[16 * kt + r16][0], s0 * KS, lane), acc);
+          acc = MM::mma(ta[s0], MM::kc(&su.Kt[16 * kt + r16][0], s0 * KS, lane), acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Wl[rbase + e][acc_col<CT>(16 * kt + ccol)] = from_f<CT>(acc[e]);
       }
@@ -292,7 +318,7 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
   int32_t* seq_off = (int32_t*)(ws + Ly.seq_off);
   hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, st, cu, s.n_seq, seq_off);
   if (Ly.nt_max > 0 && s.total_tokens > 0) {
-    const size_t shm = sizeof(PrepSmem<T, D>);
+    const size_t shm = sizeof(PrepSmem<T, D, BWD && sizeof(T) == 2>);
     hipFuncSetAttribute((const void*)chunk_prep_kernel<T, D, BWD>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL((chunk_prep_kernel<T, D, BWD>), dim3((unsigned)Ly.nt_max, s.hk), dim3(256), shm,
