@@ -41,6 +41,16 @@ template <typename CT> __device__ __forceinline__ int acc_col(int c) {
     return (c & ~31) + 8 * ((w >> 2) & 3) + 4 * (w >> 4) + (w & 3);
   }
 }
+// The inverse per 16-byte piece: the source column of element j of stored
+// piece p (stored columns 8p..8p+7), so that acc_col(acc_piece_col(p, j))
+// == 8p + j.  Row stores in accumulator order then go out whole.
+template <typename CT> __device__ __forceinline__ int acc_piece_col(int p, int j) {
+  if constexpr (sizeof(CT) == 4) {
+    return 8 * p + j;
+  } else {
+    return 32 * (p >> 2) + 16 * (j >> 2) + 4 * (p & 3) + (j & 3);
+  }
+}
 
 // exp of an in-chunk gate-sum difference.  The sums are kept in fp64: with
 // strong decay they reach several hundred inside one chunk, where an fp32
@@ -53,7 +63,7 @@ template <> __device__ __forceinline__ float dexp<float>(double x) { return (flo
 struct ChunkLayout {
   int64_t nt_max;     // upper bound on the number of chunks: T/64 + n_seq
   size_t seq_off;     // int32 [n_seq + 1]: first chunk of each sequence; [n_seq] = #chunks
-  size_t gcum;        // fp64 [T][hv]: in-chunk cumulative gate
+  size_t gcum;        // fp64 [nt_max][hv][64]: in-chunk cumulative gate (flat past the chunk end)
   size_t mw, pw;      // CT [nt_max][hv][64][64]: M = Tinv diag(beta), P (accumulator column order)
   size_t ww;          // CT [nt_max][hv][64][dk]: W = M diag(Gam) K
   size_t ktw;         // CT [nt_max][hk][dk][64]: K^T of each chunk
@@ -90,7 +100,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   size_t off = 0;
   L.seq_off = off; off = align256(off + sizeof(int32_t) * (size_t)(s.n_seq + 1));
   L.sink = off; off = align256(off + sizeof(float) * SINK_ELEMS);
-  L.gcum = off; off = align256(off + sizeof(double) * (size_t)T * s.hv);
+  L.gcum = off; off = align256(off + sizeof(double) * (size_t)L.nt_max * s.hv * CHUNK);
   L.mw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.pw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.ww = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * s.dk);

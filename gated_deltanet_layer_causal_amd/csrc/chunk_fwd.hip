@@ -129,32 +129,45 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
   {
     // Q rows (compute type, zero past the chunk end, columns in accumulator
     // order; read only by the forward pass without saved states) to the
-    // workspace, in 4-element pieces; K rows in the storage type (backward)
-    // and, for 16-bit types, in the compute type
-    constexpr int PR = D / 4;
+    // workspace; K rows in the storage type (backward) and, for 16-bit
+    // types, in the compute type.  Every store is a whole 16-byte piece
+    // (eight stored columns; acc_piece_col names their sources), so each
+    // wave instruction writes whole 128-byte lines.
+    constexpr int PR = D / 8;
     const int64_t base = ((int64_t)c * (Hv / G) + kh) * CHUNK * D;
     for (int i = tid; i < CHUNK * PR; i += 256) {
-      const int r = i / PR, c4 = (i % PR) * 4;
-      typedef CT v4 __attribute__((ext_vector_type(4)));
-      const int dst = r * D + acc_col<CT>(c4);
-      if constexpr (!BWD) *reinterpret_cast<v4*>(Q16w + base + dst) = *reinterpret_cast<const v4*>(&su.Q[r][c4]);
-      if constexpr (BWD)
-        store4(Kb + base + dst, to_f(sK[r][c4]), to_f(sK[r][c4 + 1]), to_f(sK[r][c4 + 2]),
-               to_f(sK[r][c4 + 3]));
-      if constexpr (KROWS) *reinterpret_cast<v4*>(K16w + base + dst) = *reinterpret_cast<const v4*>(&sK[r][c4]);
+      const int r = i / PR, p = i % PR;
+      const int dst = r * D + 8 * p;
+      if constexpr (!BWD) {
+        f8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = to_f(su.Q[r][acc_piece_col<CT>(p, j)]);
+        store8(Q16w + base + dst, v);
+      }
+      if constexpr (BWD) {
+        f8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = to_f(sK[r][acc_piece_col<CT>(p, j)]);
+        store8(Kb + base + dst, v);
+        if constexpr (KROWS) store8(K16w + base + dst, v);
+      }
     }
     if constexpr (BWD) {
       // Q^T in the storage type, columns (tokens) in accumulator order
       T* qo = Qtb + base;
-      for (int i = tid; i < D * (CHUNK / 4); i += 256) {
-        const int kr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
-        store4(qo + kr * CHUNK + acc_col<T>(t4), to_f(su.Q[t4][kr]), to_f(su.Q[t4 + 1][kr]),
-               to_f(su.Q[t4 + 2][kr]), to_f(su.Q[t4 + 3][kr]));
+      for (int i = tid; i < D * (CHUNK / 8); i += 256) {
+        const int kr = i / (CHUNK / 8), p = i % (CHUNK / 8);
+        f8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = to_f(su.Q[acc_piece_col<T>(p, j)][kr]);
+        store8(qo + kr * CHUNK + 8 * p, v);
         // K^T likewise, gathered from the K rows (no LDS transpose: A and
         // Ti take this storage in the head loop, after its first barrier)
-        if constexpr (KROWS)
-          store4(Ktb + base + kr * CHUNK + acc_col<T>(t4), to_f(sK[t4][kr]), to_f(sK[t4 + 1][kr]),
-                 to_f(sK[t4 + 2][kr]), to_f(sK[t4 + 3][kr]));
+        if constexpr (KROWS) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v.v[j] = to_f(sK[acc_piece_col<T>(p, j)][kr]);
+          store8(Ktb + base + kr * CHUNK + 8 * p, v);
+        }
       }
     }
   }
@@ -205,7 +218,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
       const double gm = wave_incl_scan(gl, lane);
       sm.gam[lane] = gm;
       sm.bet[lane] = bl;
-      if (lane < L) gcum[(t0 + lane) * Hv + h] = gm;
+      gcum[((int64_t)c * Hv + h) * CHUNK + lane] = gm;
       // gam is flat past the chunk length (g = 0 there), so these are the
       // factors of token min(t, L - 1)
       const double glast = __shfl(gm, CHUNK - 1, 64);
@@ -242,32 +255,37 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     __syncthreads();
     invert_unit_lower(sA, sTi, sm.X, tid);
-    // M = Tinv diag(beta), columns in accumulator order, in 4-element pieces
+    // M = Tinv diag(beta), columns in accumulator order, in 16-byte pieces
     CT* Mout = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
-    for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
-      const int t = i / (CHUNK / 4), s4 = (i % (CHUNK / 4)) * 4;
-      const float4 ti = *reinterpret_cast<const float4*>(&sTi[t][s4]);
-      store4(Mout + t * CHUNK + acc_col<CT>(s4), ti.x * sm.bet[s4], ti.y * sm.bet[s4 + 1],
-             ti.z * sm.bet[s4 + 2], ti.w * sm.bet[s4 + 3]);
+    for (int i = tid; i < CHUNK * (CHUNK / 8); i += 256) {
+      const int t = i >> 3, p = i & 7;
+      f8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = acc_piece_col<CT>(p, j);
+        v.v[j] = sTi[t][s] * sm.bet[s];
+      }
+      store8(Mout + t * CHUNK + 8 * p, v);
     }
     if constexpr (BWD) {
       // Tinv in the storage type for the chunk gradients: rows t with the
-      // columns in accumulator order, then Tinv^T (rows u, natural order)
+      // columns in accumulator order, then Tinv^T (rows u, natural order);
+      // M^T with its columns (tokens t) in accumulator order
       T* to = Tib + ((int64_t)c * Hv + h) * 2 * CHUNK * CHUNK;
-      for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
-        const int r = i / (CHUNK / 4), c4 = (i % (CHUNK / 4)) * 4;
-        const float4 ti = *reinterpret_cast<const float4*>(&sTi[r][c4]);
-        store4(to + r * CHUNK + acc_col<T>(c4), ti.x, ti.y, ti.z, ti.w);
-        store4(to + CHUNK * CHUNK + r * CHUNK + c4, sTi[c4][r], sTi[c4 + 1][r], sTi[c4 + 2][r],
-               sTi[c4 + 3][r]);
-      }
-      // M^T in the storage type, columns (tokens t) in accumulator order
       T* mo = Mtb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
-      for (int i = tid; i < CHUNK * (CHUNK / 4); i += 256) {
-        const int sr = i / (CHUNK / 4), t4 = (i % (CHUNK / 4)) * 4;
-        const float b = sm.bet[sr];
-        store4(mo + sr * CHUNK + acc_col<T>(t4), sTi[t4][sr] * b, sTi[t4 + 1][sr] * b,
-               sTi[t4 + 2][sr] * b, sTi[t4 + 3][sr] * b);
+      for (int i = tid; i < CHUNK * (CHUNK / 8); i += 256) {
+        const int r = i >> 3, p = i & 7;
+        f8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = sTi[r][acc_piece_col<T>(p, j)];
+        store8(to + r * CHUNK + 8 * p, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = sTi[8 * p + j][r];
+        store8(to + CHUNK * CHUNK + r * CHUNK + 8 * p, v);
+        const float b = sm.bet[r];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = sTi[acc_piece_col<T>(p, j)][r] * b;
+        store8(mo + r * CHUNK + 8 * p, v);
       }
     }
     // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead

@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   float bnext = 0.f;
   auto fetch_gates = [&](int h) __attribute__((always_inline)) {
     if (wave == 0) {
-      gnext = gcum[(t0 + (lane < L ? lane : L - 1)) * Hv + h];
+      gnext = gcum[(c * Hv + h) * CHUNK + lane];
       bnext = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
     }
   };
