@@ -61,8 +61,17 @@ template <typename T, int D, bool OVERLAY>
 struct PrepSmem {
   typedef typename Compute<T>::type CT;
   static constexpr int KT_LD = PrepStage<T, D>::KT_LD;
+  // 16-bit types stage P (and in backward mode P^T) in the Ti storage,
+  // rows padded to PLD elements; in backward mode the two tiles reach past
+  // Ti, into the overlay's spare bytes
+  static constexpr bool STAGE_P = sizeof(T) == 2;
+  static constexpr int PLD = CHUNK + 8;
   static constexpr size_t SB = sizeof(PrepStage<T, D>), HB = sizeof(PrepHead);
-  static constexpr size_t RAW = OVERLAY ? (SB > HB ? SB : HB) : SB + HB;
+  static constexpr size_t HBS = sizeof(float) * CHUNK * 68 + (STAGE_P ? 2 * 2 * CHUNK * PLD : 0);
+  static constexpr size_t HB2 = HB > HBS ? HB : HBS;
+  static constexpr size_t RAW = OVERLAY ? (SB > HB2 ? SB : HB2) : SB + HB;
+  static_assert(OVERLAY || !STAGE_P || 2 * CHUNK * PLD <= sizeof(float) * CHUNK * 68,
+                "forward-mode P staging fits in Ti");
   __align__(16) unsigned char raw[RAW];
   float X[16][17];
   double gam[CHUNK];
@@ -229,8 +238,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     __syncthreads();
     // A (rows t of this wave), P^T rows s (four consecutive t per lane) and
-    // P rows t (four consecutive s per lane, from K Q^T)
+    // P rows t (four consecutive s per lane, from K Q^T).  For 16-bit types
+    // P and P^T are staged in the (not yet written) Ti storage in their
+    // stored column order and leave in whole 16-byte pieces.
     CT* Pout = Pw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+    T* PTout = Ptb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
+    CT (*Ps)[SM::PLD] = reinterpret_cast<CT (*)[SM::PLD]>(&sTi[0][0]);
+    T (*Pts)[SM::PLD] = reinterpret_cast<T (*)[SM::PLD]>(&sTi[0][0] + CHUNK * SM::PLD / 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = 16 * j + ccol;
@@ -242,18 +256,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         sA[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
         pv[e] = (s <= t) ? dec * scale * qk[j][e] : 0.f;
       }
-      if constexpr (BWD)
-        store4(Ptb + ((int64_t)c * Hv + h) * CHUNK * CHUNK + s * CHUNK + acc_col<T>(rbase), pv[0],
-               pv[1], pv[2], pv[3]);
+      if constexpr (BWD) {
+        if constexpr (SM::STAGE_P)
+          store4(&Pts[s][acc_col<T>(rbase)], pv[0], pv[1], pv[2], pv[3]);
+        else
+          store4(PTout + s * CHUNK + acc_col<T>(rbase), pv[0], pv[1], pv[2], pv[3]);
+      }
       const int t = 16 * j + ccol;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s2 = rbase + e;
         pv[e] = (s2 <= t) ? dexp<T>(sm.gam[t] - sm.gam[s2]) * scale * kq[j][e] : 0.f;
       }
-      store4(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
+      if constexpr (SM::STAGE_P)
+        store4(&Ps[t][acc_col<CT>(rbase)], pv[0], pv[1], pv[2], pv[3]);
+      else
+        store4(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();
+    if constexpr (SM::STAGE_P) {
+      for (int i = tid; i < CHUNK * (CHUNK / 8); i += 256) {
+        const int r = i >> 3, p = i & 7;
+        *reinterpret_cast<uint4*>(Pout + r * CHUNK + 8 * p) = *reinterpret_cast<const uint4*>(&Ps[r][8 * p]);
+        if constexpr (BWD)
+          *reinterpret_cast<uint4*>(PTout + r * CHUNK + 8 * p) = *reinterpret_cast<const uint4*>(&Pts[r][8 * p]);
+      }
+      __syncthreads();  // the inverse overwrites the staging
+    }
     invert_unit_lower(sA, sTi, sm.X, tid);
     // M = Tinv diag(beta), columns in accumulator order, in 16-byte pieces
     CT* Mout = Mw + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
