@@ -60,7 +60,8 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     const typename Compute<T>::type* __restrict__ Ww, const typename Compute<T>::type* __restrict__ Ktw,
     const typename Compute<T>::type* __restrict__ Xw, const float* __restrict__ Gw,
     const float* __restrict__ Dw, const float* __restrict__ S0, float* __restrict__ S_final,
-    T* __restrict__ o, T* __restrict__ hst, int n_items) {
+    T* __restrict__ o, T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw,
+    typename Compute<T>::type* __restrict__ Dl16w, int n_items) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   typedef AccOrder<CT> AO;
@@ -176,14 +177,44 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, S[kt]);
   };
-  // (K-rows form: through the wave's LDS rows, in 16-byte stores)
+  // (K-rows form) The compute waves put the chunk-start state, R, Delta and
+  // Delta in the compute type into LDS rows of their own (paired words,
+  // ds_write2); a step later the mover wave of the same index stores them in
+  // 16-byte pieces, so no store sits on the recurrence.  Two sets of rows,
+  // by chunk parity.
   typedef StageRows<T> SR;
-  auto stage_state = [&](char* stg, int64_t c) __attribute__((always_inline)) {
-    char* const myst = stg + wave * D * SR::SB;
-    const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
+  constexpr int SRR = D + 3 * CHUNK;   // staged rows per compute wave
+  constexpr int SROW_R = D, SROW_DL = D + CHUNK, SROW_D16 = D + 2 * CHUNK;
+  __shared__ __align__(16) char stg[SB::KR ? 2 * NW * SRR * SR::SB : 16];
+  auto stage_of = [&](int64_t c, int w) __attribute__((always_inline)) -> char* {
+    return stg + (int)((((c - c_begin) & 1) * NW + w) * SRR * SR::SB);
+  };
+  // a tile of 16 rows (rows 16 tt + 4 g + i, column vcol) as element type E
+  auto put_rows = [&](auto tag, char* st, int row0, const floatx4 (&x)[4]) __attribute__((always_inline)) {
+    typedef decltype(tag) E;
+    static_assert(sizeof(E) == sizeof(T), "same row layout");
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, S[kt]);
-    SR::flush(myst, 0, D, rs, (uint32_t)(16 * wave * sizeof(T)), rowh, lane);
+    for (int tt = 0; tt < 4; ++tt) StageRows<E>::put(st, row0 + 16 * tt, ps, lane, x[tt]);
+  };
+  // (movers) chunk cp's staged rows of compute wave `wave` to the state,
+  // R, Delta and Delta (compute type) buffers; token rows past the sequence
+  // end fall outside the buffers and are dropped.  With valid false every
+  // store is still issued but dropped (an empty range), so each step issues
+  // the same count.
+  constexpr int NFL = SR::stores(D) + 3 * SR::stores(CHUNK);
+  auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
+    const char* st = stage_of(cp, wave);
+    const int64_t ca = valid ? cp : c_begin;
+    const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
+    const int64_t rem = seq_t1 - t0p;
+    const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
+    const uint32_t col = (uint32_t)(16 * wave * sizeof(T));
+    const int64_t tok = t0p * HvD + (int64_t)h * D + v0;
+    SR::flush_async(st, 0, D, buffer_of(hst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
+              col, rowh, lane);
+    SR::flush_async(st, SROW_R, CHUNK, buffer_of(Rw + tok, (uint32_t)Lp * rowb), col, rowb, lane);
+    SR::flush_async(st, SROW_DL, CHUNK, buffer_of(Dlw + tok, (uint32_t)Lp * rowb), col, rowb, lane);
+    SR::flush_async(st, SROW_D16, CHUNK, buffer_of(Dl16w + tok, (uint32_t)Lp * rowb), col, rowb, lane);
   };
 
   // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).
@@ -209,7 +240,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   };
 
   // ---- one chunk from buffer B
-  auto compute = [&](const SB& B, int64_t c) __attribute__((always_inline)) {
+  auto compute = [&](const SB& B, int64_t c, char* stc) __attribute__((always_inline)) {
     const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
     const int64_t rem = seq_t1 - t0;
     const int L = rem < CHUNK ? (int)rem : CHUNK;
@@ -242,6 +273,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
         for (int p = 0; p < NSC; ++p)
           Dl[tt] = MM::mma(*reinterpret_cast<const frag*>(B.M + 16 * tt * CHUNK + rk[p]), rf[p], Dl[tt]);
       }
+      put_rows((T)0, stc, SROW_R, R);
     } else {
     // -S^T as B operands, straight from the accumulators
     frag sbn[NSD];
@@ -317,6 +349,10 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
         for (int p = 0; p < NSC; ++p) S[kt] = MM::mma(kt_frag(B, kt, p), dsf[p], S[kt]);
       }
     }
+    if constexpr (SB::KR) {
+      put_rows((T)0, stc, SROW_DL, Dl);
+      put_rows((CT)0, stc, SROW_D16, Dl);
+    }
 
     if constexpr (MODE == 0) {
       // O = diag(Gam) scale Q S^T + P Delta
@@ -346,54 +382,79 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     __syncthreads();
     for (int64_t c = c_begin; c < c_end; c += 2) {
       fetch(bufB, c + 1 < c_end ? c + 1 : c);   // a repeat of chunk c at the end
-      compute(bufA, c);
+      compute(bufA, c, nullptr);
       __syncthreads();   // waits for this wave's copies; then every wave's are visible
       if (c + 1 < c_end) {
         fetch(bufA, c + 2 < c_end ? c + 2 : c + 1);
-        compute(bufB, c + 1);
+        compute(bufB, c + 1, nullptr);
         __syncthreads();
       }
     }
   } else if constexpr (SB::KR) {
     // three buffers, the copies two chunks ahead, issued by the movers: a
     // step ends once the movers' copies for the next chunk (issued a step
-    // earlier) are in, this step's NCOPY still in flight; the compute waves
-    // only store the chunk's state and compute.  Past the end the last chunk
-    // is copied again.
+    // earlier) and their stores of the chunk before are done, this step's
+    // still in flight; the compute waves only compute and put the chunk's
+    // state, R and Delta into their staging rows.  Past the end the last
+    // chunk is copied again.
     __shared__ SB bufC;
-    __shared__ __align__(16) char stg[NW * D * SR::SB];
     auto last = [&](int64_t x) { return x < c_end ? x : c_end - 1; };
     if (mover) {
+      // A step issues the copies for chunk c + 2, then the stores of chunk
+      // c - 1 (staged during the previous step), then waits for chunk c + 1's
+      // copies: those were followed by the previous step's stores and this
+      // step's copies and stores, which stay in flight, so a store has two
+      // steps to complete.  The prologue issues (dropped) stores too, so that
+      // the count is the same from the first step on.
+      static_assert(NCOPY + 2 * NFL < 64, "vmcnt holds 6 bits");
       if (c_begin < c_end) {
         fetch(bufA, c_begin);
         fetch(bufB, last(c_begin + 1));
       }
-      wait_vm_barrier<NCOPY>();
+      flush_chunk(c_begin - 2, false);
+      wait_vm_barrier<NCOPY + NFL>();
       for (int64_t c = c_begin; c < c_end; c += 3) {
         fetch(bufC, last(c + 2));
-        wait_vm_barrier<NCOPY>();
+        flush_chunk(c - 1, c > c_begin);
+        wait_vm_barrier<NCOPY + 2 * NFL>();
         if (c + 1 >= c_end) break;
         fetch(bufA, last(c + 3));
-        wait_vm_barrier<NCOPY>();
+        flush_chunk(c, true);
+        wait_vm_barrier<NCOPY + 2 * NFL>();
         if (c + 2 >= c_end) break;
         fetch(bufB, last(c + 4));
-        wait_vm_barrier<NCOPY>();
+        flush_chunk(c + 1, true);
+        wait_vm_barrier<NCOPY + 2 * NFL>();
       }
+      // the last chunk's rows, staged before the last barrier
+      if (c_begin < c_end) flush_chunk(c_end - 1, true);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       return;
     }
     lds_barrier();
     for (int64_t c = c_begin; c < c_end; c += 3) {
-      stage_state(stg, c);
-      compute(bufA, c);
+      {
+        char* st = stage_of(c, wave);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+        compute(bufA, c, st);
+      }
       lds_barrier();
       if (c + 1 >= c_end) break;
-      stage_state(stg, c + 1);
-      compute(bufB, c + 1);
+      {
+        char* st = stage_of(c + 1, wave);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+        compute(bufB, c + 1, st);
+      }
       lds_barrier();
       if (c + 2 >= c_end) break;
-      stage_state(stg, c + 2);
-      compute(bufC, c + 2);
+      {
+        char* st = stage_of(c + 2, wave);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+        compute(bufC, c + 2, st);
+      }
       lds_barrier();
     }
   } else {
@@ -408,7 +469,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     auto step = [&](const SB& cur, SB& ahead, int64_t c) __attribute__((always_inline)) {
       store_state(c);
       fetch(ahead, last(c + 2));
-      compute(cur, c);
+      compute(cur, c, nullptr);
       wait_vm_barrier<NSTORE + NCOPY>();
     };
     if (c_begin < c_end) {
@@ -437,10 +498,13 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
 // ---------------------------------------------------------------------------
 constexpr int STATE_NW = 2;   // waves (16 value rows of the state each) per workgroup
 
+// With 16-bit MODE 1 (the K-rows form) the pass also stores R and Delta,
+// which it forms on the way.
 template <typename T, int D, int MODE>
 static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, float scale,
                               const float* S0, float* S_final, const int32_t* cu, void* o,
                               const ChunkLayout& Ly, char* ws, hipStream_t st) {
+  constexpr bool KR = StateBuf<T, D, STATE_NW, MODE>::KR;
   constexpr int NW = STATE_NW, BV = 16 * NW;
   typedef typename Compute<T>::type CT;
   auto kern = chunk_state_kernel<T, D, NW, MODE>;
@@ -452,7 +516,8 @@ static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, fl
                      (const CT*)(ws + (StateBuf<T, D, NW, MODE>::KR ? Ly.k16w : Ly.ww)),
                      (const CT*)(ws + Ly.ktw), (const CT*)(ws + Ly.q16w),
                      (const float*)(ws + Ly.gw), (const float*)(ws + Ly.dw), S0, S_final, (T*)o,
-                     (T*)(ws + Ly.h), n_items);
+                     (T*)(ws + Ly.h), KR ? (T*)(ws + Ly.rw) : nullptr,
+                     KR ? (T*)(ws + Ly.dlw) : nullptr, KR ? (CT*)(ws + Ly.dl16w) : nullptr, n_items);
   return hipGetLastError();
 }
 
@@ -472,8 +537,9 @@ hipError_t launch_chunk_fwd_states_save(const gdn_shape& s, const void* q, const
                                         const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
                                         float scale, const float* S0, float* S_final,
                                         const int32_t* cu, void* o, void* ws, hipStream_t st) {
-  // the sequential pass stores the chunk-start states; R, Delta and O then
-  // follow chunk by chunk in parallel
+  // the sequential pass stores the chunk-start states (and, with 16-bit
+  // types, R and Delta); O (and for fp32 R and Delta) then follow chunk by
+  // chunk in parallel
   const ChunkLayout Ly = chunk_layout(s);
   hipError_t e = dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;

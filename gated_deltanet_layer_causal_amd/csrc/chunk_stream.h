@@ -2,6 +2,8 @@
 // pass): MFMA operands taken straight from accumulator tiles, LDS tiles that
 // are filled by direct global -> LDS copies, and range-checked buffer stores.
 #pragma once
+#include <type_traits>
+
 #include "chunk_common.h"
 
 namespace gdn {
@@ -145,6 +147,16 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_
 // columns (l % 16) & ~1 and + 1.  Half the store instructions of one store
 // per element.
 // 32-bit words of a paired row piece: two 16-bit elements, or two floats.
+// two values as one 32-bit word of 16-bit elements (round to nearest even)
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (std::is_same<T, fp16>::value) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(fp16)a, (fp16)b});
+  } else {
+    return pack2_bf16(a, b);
+  }
+}
+
 template <typename T> struct PairWord { typedef uint32_t type; };
 template <> struct PairWord<float> { typedef u32x2 type; };
 
@@ -169,7 +181,7 @@ struct PairStore {
   __device__ __forceinline__ void pair(floatx4 x, typename PairWord<T>::type& w0,
                                        typename PairWord<T>::type& w1) const {
     if constexpr (sizeof(T) == 2) {
-      const uint32_t p01 = pack2_bf16(x[0], x[1]), p23 = pack2_bf16(x[2], x[3]);
+      const uint32_t p01 = pack2<T>(x[0], x[1]), p23 = pack2<T>(x[2], x[3]);
       const uint32_t own = odd ? p23 : p01, send = odd ? p01 : p23;
       const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
       w0 = __builtin_amdgcn_perm(recv, own, sel0);
@@ -235,6 +247,38 @@ template <typename T> struct StageRows {
     for (int j = 0; j < n / RPI; ++j) {
       const u32x4 v = *reinterpret_cast<const piece*>(region + (row0 + j * RPI + r) * SB + pc * 16);
       __builtin_amdgcn_raw_buffer_store_b128(v, rs, col + (uint32_t)(j * RPI + r) * ldb + (uint32_t)pc * 16u, 0, 0);
+    }
+  }
+  // flush() for a wave with direct copies into other LDS regions in flight:
+  // the reads are inline asm, which the compiler does not order after those
+  // copies (a plain LDS read would wait for all of them, vmcnt(0)); each
+  // asm block waits for its own reads before its outputs are used
+  __device__ __forceinline__ static void flush_async(const char* region, int row0, int n,
+                                                     __amdgpu_buffer_rsrc_t rs, uint32_t col,
+                                                     uint32_t ldb, int lane) {
+    const int r = lane / PPR, pc = lane % PPR;
+    const uint32_t a = lds_offset(region) + (uint32_t)((row0 + r) * SB + pc * 16);
+    constexpr uint32_t STEP = RPI * SB;   // LDS bytes between consecutive stores' rows
+    auto store = [&](const u32x4& v, int j) __attribute__((always_inline)) {
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, col + (uint32_t)(j * RPI + r) * ldb + (uint32_t)pc * 16u, 0, 0);
+    };
+#pragma unroll
+    for (int j = 0; j < n / RPI; j += 2) {
+      u32x4 v0, v1;
+      if (j + 1 < n / RPI) {
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v0), "=&v"(v1)
+                     : "v"(a + (uint32_t)j * STEP), "n"(STEP)
+                     : "memory");
+        store(v0, j);
+        store(v1, j + 1);
+      } else {
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v0)
+                     : "v"(a + (uint32_t)j * STEP)
+                     : "memory");
+        store(v0, j);
+      }
     }
   }
 };
