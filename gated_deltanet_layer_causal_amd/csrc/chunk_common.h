@@ -72,7 +72,8 @@ struct ChunkLayout {
   size_t kb, ktb, qtb; // T [nt_max][hk]: K rows [64][dk], K^T and Q^T [dk][64] (backward)
   size_t k16w;        // CT [nt_max][hk][64][dk]: K rows, columns in accumulator order
                       // (backward, 16-bit types: the saved-state pass reads these in place of W, K^T)
-  size_t ptb, mtb;    // T [nt_max][hv][64][64]: P^T, M^T (backward)
+  size_t ptb;         // T [nt_max][hv][64][64]: P^T (backward)
+  size_t bw;          // fp32 [nt_max][hv][64]: beta_t, zero past the chunk end (backward)
   size_t tib;         // T [nt_max][hv][2][64][64]: Tinv (columns in accumulator order), Tinv^T (backward)
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
   size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
@@ -115,7 +116,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.ktb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.qtb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.ptb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
-  L.mtb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
+  L.bw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.tib = off; off = align256(off + es * (size_t)L.nt_max * s.hv * 2 * CHUNK * CHUNK);
   L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.dh = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);

@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
     typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw,
     T* __restrict__ Kb, T* __restrict__ Ktb, T* __restrict__ Qtb, T* __restrict__ Ptb,
-    T* __restrict__ Mtb, T* __restrict__ Tib) {
+    float* __restrict__ Bw, T* __restrict__ Tib) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -235,6 +235,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
       sm.sbg[lane] = bl * Gm;
       Gw[((int64_t)c * Hv + h) * CHUNK + lane] = Gm;
       Dw[((int64_t)c * Hv + h) * CHUNK + lane] = dexp<T>(glast - gm);
+      if constexpr (BWD) Bw[((int64_t)c * Hv + h) * CHUNK + lane] = bl;
     }
     __syncthreads();
     // A (rows t of this wave), P^T rows s (four consecutive t per lane) and
@@ -298,10 +299,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     if constexpr (BWD) {
       // Tinv in the storage type for the chunk gradients: rows t with the
-      // columns in accumulator order, then Tinv^T (rows u, natural order);
-      // M^T with its columns (tokens t) in accumulator order
+      // columns in accumulator order, then Tinv^T (rows u, natural order;
+      // the reverse pass reads it as M^T = diag(beta) Tinv^T)
       T* to = Tib + ((int64_t)c * Hv + h) * 2 * CHUNK * CHUNK;
-      T* mo = Mtb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
       for (int i = tid; i < CHUNK * (CHUNK / 8); i += 256) {
         const int r = i >> 3, p = i & 7;
         f8 v;
@@ -311,10 +311,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
         for (int j = 0; j < 8; ++j) v.v[j] = sTi[8 * p + j][r];
         store8(to + CHUNK * CHUNK + r * CHUNK + 8 * p, v);
-        const float b = sm.bet[r];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v.v[j] = sTi[acc_piece_col<T>(p, j)][r] * b;
-        store8(mo + r * CHUNK + 8 * p, v);
       }
     }
     // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead
@@ -379,7 +375,7 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        BWD ? (typename Compute<T>::type*)(ws + Ly.k16w) : nullptr, (float*)(ws + Ly.gw),
                        (float*)(ws + Ly.dw), BWD ? (T*)(ws + Ly.kb) : nullptr,
                        BWD ? (T*)(ws + Ly.ktb) : nullptr, BWD ? (T*)(ws + Ly.qtb) : nullptr,
-                       BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (T*)(ws + Ly.mtb) : nullptr,
+                       BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (float*)(ws + Ly.bw) : nullptr,
                        BWD ? (T*)(ws + Ly.tib) : nullptr);
   }
   return hipGetLastError();

@@ -2,7 +2,7 @@
 // each sequence.  Per chunk, given dO and the gradient dS' of the state
 // leaving it:
 //   dDelta = P^T dO + diag(dec) K dS'^T
-//   dR     = M^T dDelta                                  (= dv)
+//   dR     = M^T dDelta = diag(beta) Tinv^T dDelta        (= dv)
 //   dS     = Gam_L dS' + (scale Q)^T diag(Gam) dO - K^T diag(Gam) dR
 // It stores dS' per chunk (for the chunk-parallel gradients), dDelta and dv,
 // and dS0 at the sequence start.
@@ -11,9 +11,9 @@
 // (sequence, value head, block of 16 * NW value rows); compute wave w keeps
 // its d_k x 16 slice of dS'^T in MFMA accumulators and feeds it straight
 // back as B operand; NW mover waves (on the SIMDs the compute waves leave
-// free) stream the chunk operands (K rows, K^T, Q^T, P^T, M^T from the
-// backward preparation, columns in accumulator order; the dO rows of the
-// block; Gam, dec) into one of two LDS buffers by direct copies while the
+// free) stream the chunk operands (K rows, K^T, Q^T, P^T from the backward
+// preparation, columns in accumulator order; Tinv^T in natural order; the
+// dO rows of the block; Gam, dec, beta) into one of two LDS buffers by direct copies while the
 // compute waves work on the other.  Operands are in the storage type (bf16
 // keeps the range of dS).
 #include "chunk_stream.h"
@@ -24,7 +24,7 @@ template <typename T, int D, int NW> struct RevBuf {
   static constexpr int BV = 16 * NW;
   typedef Tile<T, CHUNK, D> TK;        // K rows
   typedef Tile<T, D, CHUNK> TKt;       // K^T, Q^T
-  typedef Tile<T, CHUNK, CHUNK> TM;    // P^T, M^T
+  typedef Tile<T, CHUNK, CHUNK> TM;    // P^T, Tinv^T
   typedef Tile<T, CHUNK, BV, 3> TO;    // dO rows of this block
   // 16-bit types read K^T from the K rows by transposing reads; fp32 copies it
   static constexpr bool KT_TR = sizeof(T) == 2;
@@ -32,17 +32,17 @@ template <typename T, int D, int NW> struct RevBuf {
   T Kt[KT_TR ? 8 : TKt::PIECES * TKt::EPP];
   T Qt[TKt::PIECES * TKt::EPP];
   T Pt[TM::PIECES * TM::EPP];
-  T Mt[TM::PIECES * TM::EPP];
+  T Mt[TM::PIECES * TM::EPP];          // Tinv^T
   T dO[TO::PIECES * TO::EPP];
-  float G[CHUNK], Dc[CHUNK];           // Gam_t, dec_t
+  float G[CHUNK], Dc[CHUNK], Bt[CHUNK];   // Gam_t, dec_t, beta_t
 } __attribute__((aligned(16)));
 
 template <typename T, int D, int NW>
 __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
     const T* __restrict__ Kb, const T* __restrict__ Ktb, const T* __restrict__ Qtb,
-    const T* __restrict__ Ptb, const T* __restrict__ Mtb, const float* __restrict__ Gw,
-    const float* __restrict__ Dw, const T* __restrict__ dout, const float* __restrict__ dS_final,
+    const T* __restrict__ Ptb, const T* __restrict__ Tib, const float* __restrict__ Gw,
+    const float* __restrict__ Dw, const float* __restrict__ Bw, const T* __restrict__ dout, const float* __restrict__ dS_final,
     float* __restrict__ dS0, T* __restrict__ dhst, T* __restrict__ ddw, T* __restrict__ dvo,
     int64_t lddv, int n_items) {
   typedef Mma<T> MM;
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     if constexpr (!RB::KT_TR) copy_tile<TKt, NW>(B.Kt, Ktb + ck * D * CHUNK, cl, wave);
     copy_tile<TKt, NW>(B.Qt, Qtb + ck * D * CHUNK, cl, wave);
     copy_tile<TM, NW>(B.Pt, Ptb + ch * CHUNK * CHUNK, cl, wave);
-    copy_tile<TM, NW>(B.Mt, Mtb + ch * CHUNK * CHUNK, cl, wave);
+    copy_tile<TM, NW>(B.Mt, Tib + ch * 2 * CHUNK * CHUNK + CHUNK * CHUNK, cl, wave);
     {
       // dO rows past the sequence end re-read its last row (their products
       // meet zero rows and columns of P^T, Q^T)
@@ -136,6 +136,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
       copy_to_lds(buffer_of(Gw + ch * CHUNK, CHUNK * 4), B.G, 16u * lane, 0);
       copy_to_lds(buffer_of(Dw + ch * CHUNK, CHUNK * 4), B.Dc, 16u * lane, 0);
     }
+    if (wave == NW - 1 && lane < 16) copy_to_lds(buffer_of(Bw + ch * CHUNK, CHUNK * 4), B.Bt, 16u * lane, 0);
   };
 
   // The movers also touch every line of the chunk after the one they copy,
@@ -163,7 +164,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     if constexpr (!RB::KT_TR) touch_tile(Ktb + ck * D * CHUNK, TKB, NTK, wave);
     touch_tile(Qtb + ck * D * CHUNK, TKB, NTK, wave);
     touch_tile(Ptb + ch * CHUNK * CHUNK, TMB, NTM, wave);
-    touch_tile(Mtb + ch * CHUNK * CHUNK, TMB, NTM, wave);
+    touch_tile(Tib + ch * 2 * CHUNK * CHUNK + CHUNK * CHUNK, TMB, NTM, wave);
     // the block's dO rows (one line each)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         buffer_of(dout + t0 * HvD + (int64_t)h * D + v0, (uint32_t)Lc * rowb),
@@ -188,6 +189,21 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
       return __builtin_bit_cast(frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
     } else {
       return arow(B.Kt, rk[p], 16 * kt * CHUNK);
+    }
+  };
+
+  // A operand of step p from row 16 tt + c16 of Tinv^T, whose columns are in
+  // natural order: for 16-bit types the step's eight reduction indices
+  // 32 p + 4 g + (0..3) and 32 p + 16 + 4 g + (0..3) (accumulator order) are
+  // two 8-byte pieces; fp32 keeps one index per step (natural order)
+  auto tt_frag = [&](const RB& B, int tt, int p) __attribute__((always_inline)) -> frag {
+    if constexpr (KS == 4) {
+      return arow(B.Mt, rk[p], 16 * tt * CHUNK);
+    } else {
+      const int r = 16 * tt + c16;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(B.Mt + TM::at(r, 32 * p + g4));
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(B.Mt + TM::at(r, 32 * p + 16 + g4));
+      return __builtin_bit_cast(frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
   };
 
@@ -261,7 +277,12 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
       for (int tt = 0; tt < 4; ++tt) {
         floatx4 dr = zero4();
 #pragma unroll
-        for (int p = 0; p < NSC; ++p) dr = MM::mma(arow(B.Mt, rk[p], 16 * tt * CHUNK), df[p], dr);
+        for (int p = 0; p < NSC; ++p) dr = MM::mma(tt_frag(B, tt, p), df[p], dr);
+        const float4 bt = *reinterpret_cast<const float4*>(&B.Bt[16 * tt + g4]);
+        dr[0] *= bt.x;
+        dr[1] *= bt.y;
+        dr[2] *= bt.z;
+        dr[3] *= bt.w;
         const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
         gr[tt][0] = -gm.x * dr[0];
         gr[tt][1] = -gm.y * dr[1];
@@ -348,8 +369,8 @@ static hipError_t chunk_rev(const gdn_shape& s, float scale, const int32_t* cu, 
   hipLaunchKernelGGL((chunk_rev_kernel<T, D, NW>), dim3(n_items), dim3(128 * NW), 0, st, cu,
                      (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
                      (const T*)(ws + Ly.kb), (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb),
-                     (const T*)(ws + Ly.ptb), (const T*)(ws + Ly.mtb), (const float*)(ws + Ly.gw),
-                     (const float*)(ws + Ly.dw), (const T*)dout, dS_final, dS0, (T*)(ws + Ly.dh),
+                     (const T*)(ws + Ly.ptb), (const T*)(ws + Ly.tib), (const float*)(ws + Ly.gw),
+                     (const float*)(ws + Ly.dw), (const float*)(ws + Ly.bw), (const T*)dout, dS_final, dS0, (T*)(ws + Ly.dh),
                      (T*)(ws + Ly.ddw), (T*)dv, lddv, n_items);
   return hipGetLastError();
 }
