@@ -73,15 +73,18 @@ FP32_PEAK_TFLOPS = 157.3
 # The chunk phases count the dense contraction flops of the products they
 # form (chunk C = 64, head dim d, per value head unless noted):
 #   fwd_states : W S^T, Q S^T, S update (3 x 2 d^2) + M V, P Delta (2 x 2 C d)
-#   bwd_states : W S^T, K S^T, S update (3 x 2 d^2) + M V (2 C d)
-#   fwd_states_save: both of the above
+#   fwd_states_save: the saved-state pass, K S^T and the S update (2 x 2 d^2)
+#                + M R (2 C d), which also stores R and Delta for 16-bit data,
+#                then the outputs: Q S^T (2 d^2) + P Delta (2 C d) (fp32 data:
+#                K S^T, Q S^T (2 x 2 d^2) + M R, P Delta (2 x 2 C d))
+#   bwd_states : the saved-state pass (fp32 data: + K S^T, M R)
 #   bwd_reverse: K dS'^T, Q^T dO, K^T dR (3 x 2 d^2) + P^T dO, M^T dDelta (2 x 2 C d)
 #   bwd_grads  : dO S, dR S, Delta dS' (3 x 2 d^2); dM, dP, (dP o D) K,
 #                (dP o D)^T Q, (dA o bD) K, (dA o bD)^T K (6 x 2 C d);
 #                Tinv products (2 x 2 C^2); per key head K K^T, Q K^T (2 x 2 C d)
 # The preparation is bandwidth-bound: it reads q, k, g, beta and writes the
 # gate sums, per value head M, P, W, Gam, dec (and, in backward mode, P^T,
-# M^T, Tinv), per key head K^T and fp16 Q, K rows (backward mode: K, K^T,
+# Tinv, Tinv^T, beta), per key head K^T and fp16 Q, K rows (backward mode: K, K^T,
 # Q^T in the storage type).
 def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     C = 2 * hk * d + hv * d
@@ -104,10 +107,10 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     # value head, W.  Backward mode adds per key head the K rows, K^T and Q^T
     # in the storage type and one more key-head tile (the K rows in the
     # compute type for 16-bit data, the compute-type K^T for fp32), per value
-    # head P^T, M^T, Tinv and Tinv^T (and W for fp32).
+    # head P^T, Tinv, Tinv^T and beta (and W for fp32).
     per_hv = 4 + 4 + 8 + 8 + 2 * C64 * E
     fwd_bytes = 2 * hk * d * E + 2 * hk * d * E + hv * (per_hv + d * E)
-    bwd_bytes = 2 * hk * d * E + 4 * hk * d * E + hv * (per_hv + 4 * C64 * E + (d * E if E == 4 else 0))
+    bwd_bytes = 2 * hk * d * E + 4 * hk * d * E + hv * (per_hv + 4 + 3 * C64 * E + (d * E if E == 4 else 0))
     if name == "chunk_prepare":
         return "hbm", bwd_bytes if saved else fwd_bytes
     if name == "chunk_prepare_b":
@@ -115,12 +118,17 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     # products formed per v-head token: the forward pass without saved
     # states (W S^T, Q S^T, update; M V, P Delta); the saved-state pass (K S^T,
     # update; M R for 16-bit data, W S^T, update; M V for fp32) and the
-    # chunk-parallel outputs (K S^T, Q S^T; M R, P Delta), whose O part the
-    # recompute flow leaves out
+    # chunk-parallel outputs: for 16-bit data Q S^T and P Delta (the pass has
+    # stored R and Delta), for fp32 K S^T, Q S^T; M R, P Delta, whose O part
+    # the recompute flow leaves out
     fwd_states = hv * (6 * d * d + 4 * C64 * d)
     save_pass = hv * (4 * d * d + 2 * C64 * d)
-    outputs = hv * (4 * d * d + 4 * C64 * d)
-    outputs_no_o = hv * (2 * d * d + 2 * C64 * d)
+    if E == 2:   # the saved-state pass stores R and Delta: O alone remains
+        outputs = hv * (2 * d * d + 2 * C64 * d)
+        outputs_no_o = 0
+    else:
+        outputs = hv * (4 * d * d + 4 * C64 * d)
+        outputs_no_o = hv * (2 * d * d + 2 * C64 * d)
     if name == "chunk_fwd_states":
         return "mfma", (save_pass + outputs) if saved else fwd_states
     if name == "chunk_bwd_states":
