@@ -91,7 +91,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int n_seq, int Hv, int G,
-    float scale, const double* __restrict__ gcum, const float* __restrict__ beta,
+    float scale, const double* __restrict__ gcum, const float* __restrict__ bw,
     const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ Tib,
     const T* __restrict__ Ktb, const T* __restrict__ Qtb, const T* __restrict__ hst,
     const T* __restrict__ dhst, const T* __restrict__ Rw, const T* __restrict__ Dlw,
@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   auto fetch_gates = [&](int h) __attribute__((always_inline)) {
     if (wave == 0) {
       gnext = gcum[(c * Hv + h) * CHUNK + lane];
-      bnext = lane < L ? beta[(t0 + lane) * Hv + h] : 0.f;
+      bnext = bw[(c * Hv + h) * CHUNK + lane];   // (zero past the chunk end)
     }
   };
   auto put_gates = [&]() __attribute__((always_inline)) {
@@ -688,7 +688,7 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, dim3((unsigned)Ly.nt_max, s.hk), dim3(512), shm, st, (const T*)q,
                        (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
-                       s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), beta,
+                       s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), (const float*)(ws + Ly.bw),
                        (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)(ws + Ly.tib),
                        (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb), (const T*)(ws + Ly.h),
                        (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw), (const T*)(ws + Ly.dlw),

@@ -162,17 +162,20 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
  * gdn_chunk_fwd_states_save: the same result after gdn_chunk_prepare_bwd,
  *   also leaving in the (backward-size) workspace what gdn_chunk_bwd_states
  *   would recompute.  Two kernel launches: a sequential pass that stores
- *   the chunk-start states (and S_final), then a chunk-parallel pass that
- *   forms R, Delta and o from them.  A training step can then run its
+ *   the chunk-start states (and S_final; for bf16 data also R and Delta),
+ *   then a chunk-parallel pass that forms o (fp32 data: R, Delta and o)
+ *   from them.  A training step can then run its
  *   backward as gdn_chunk_bwd_reverse -> gdn_chunk_bwd_grads on that
  *   workspace (same inputs, workspace untouched in between), skipping the
  *   preparation and the state pass.
- * gdn_chunk_bwd_states: the same two launches without o: chunk-start
- *   states, R and Delta.
+ * gdn_chunk_bwd_states: the same without o: chunk-start states, R and
+ *   Delta (one launch for bf16 data, two for fp32).
  * gdn_chunk_bwd_reverse: reverse pass over chunks; writes dv, dS0 and the
  *   chunk-end state gradients.
  * gdn_chunk_bwd_grads: chunk-parallel gradients; writes dq, dk, dg, dbeta
- *   (reads dv written by the reverse phase).
+ *   (reads dv written by the reverse phase, and beta as the backward
+ *   preparation left it in the workspace: `beta` must be the array that
+ *   preparation read, and is validated but not read again).
  * ------------------------------------------------------------------------- */
 gdn_status gdn_chunk_prepare(const gdn_shape* shape, const void* q, const void* k, int64_t ldq,
                              int64_t ldk, const float* g, const float* beta, float scale,

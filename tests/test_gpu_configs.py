@@ -30,7 +30,7 @@ pytestmark = pytest.mark.gpu
 MARGIN = 64
 WINDOW = 1024
 DECAY_BOUND = 1e-12
-CONFIGS = ["next4k", "varlen16k", "tp4share", "long128k"]
+CONFIGS = ["next4k", "varlen16k", "tp4share", "flash64k", "long128k"]
 
 
 def _bf(t):
