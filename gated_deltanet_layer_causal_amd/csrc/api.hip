@@ -85,7 +85,8 @@ gdn_status gdn_conv_fwd(const gdn_shape* s, const void* x, int64_t ldx, const fl
 
 size_t gdn_conv_bwd_workspace(const gdn_shape* s) {
   if (check_shape(s) != GDN_OK) return 0;
-  return sizeof(float) * (size_t)conv_partials(s->total_tokens) * (size_t)channels(s) * 4;
+  return sizeof(float) * (size_t)conv_partials(s->total_tokens, conv_tt(s->total_tokens, channels(s))) *
+         (size_t)channels(s) * 4;
 }
 
 gdn_status gdn_conv_bwd(const gdn_shape* s, const void* x, int64_t ldx, const float* w,

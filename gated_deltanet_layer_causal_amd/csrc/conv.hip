@@ -2,7 +2,7 @@
 // normalisation of q and k, forward and backward.
 //
 // HBM-bound: every x / dy element is read once and every output written once.
-// Mapping: a wave owns one run of CONV_TT consecutive tokens; each lane owns 8
+// Mapping: a wave owns one run of tt consecutive tokens (conv_tt); each lane owns 8
 // consecutive channels (one 16-byte bf16 vector).  The run is cut where
 // sequences start, and each piece is walked keeping the 4-token window in a
 // 4-slot circular buffer, four tokens per loop iteration, so the window never
@@ -86,15 +86,15 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256) conv_fwd_kernel(const T* __restrict__ x, int64_t ldx,
                                                        const float* __restrict__ w,
                                                        const int32_t* __restrict__ cu, int n_seq,
-                                                       int64_t T_tok, int C, int n_l2, float eps,
+                                                       int64_t T_tok, int tt, int C, int n_l2, float eps,
                                                        T* __restrict__ y, int64_t ldy) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   const bool active = c0 < C;
   const int64_t run = (int64_t)blockIdx.x * CONV_RUNS_PER_BLOCK + wave;
-  const int64_t tb = run * CONV_TT;
+  const int64_t tb = run * tt;
   if (tb >= T_tok) return;  // whole wave exits together
-  const int64_t te = tb + CONV_TT < T_tok ? tb + CONV_TT : T_tok;
+  const int64_t te = tb + tt < T_tok ? tb + tt : T_tok;
   const bool l2 = c0 < n_l2;
   // lanes past the channels read zero and store nothing
   const uint32_t coff = active ? (uint32_t)c0 * sizeof(T) : 0x80000000u;
@@ -191,7 +191,7 @@ __device__ __forceinline__ f8 conv_du(const float (&wr)[8][4], const f8& x0, con
 template <typename T, int D>
 __global__ void __launch_bounds__(256) conv_bwd_kernel(
     const T* __restrict__ x, int64_t ldx, const float* __restrict__ w,
-    const int32_t* __restrict__ cu, int n_seq, int64_t T_tok, int C, int n_l2, float eps,
+    const int32_t* __restrict__ cu, int n_seq, int64_t T_tok, int tt, int C, int n_l2, float eps,
     const T* __restrict__ dy, int64_t lddy, T* __restrict__ dx, int64_t lddx,
     float* __restrict__ partials) {
   __shared__ float red[CONV_RUNS_PER_BLOCK][64][33];
@@ -200,8 +200,8 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
   const bool active = c0 < C;
   const bool l2 = c0 < n_l2;
   const int64_t run = (int64_t)blockIdx.x * CONV_RUNS_PER_BLOCK + wave;
-  const int64_t tb = run * CONV_TT;
-  const int64_t te = tb + CONV_TT < T_tok ? tb + CONV_TT : T_tok;
+  const int64_t tb = run * tt;
+  const int64_t te = tb + tt < T_tok ? tb + tt : T_tok;
   // lanes past the channels read zero and store nothing
   const uint32_t coff = active ? (uint32_t)c0 * sizeof(T) : 0x80000000u;
   const uint32_t ldxb = (uint32_t)(ldx * sizeof(T)), ldyb = (uint32_t)(lddy * sizeof(T));
@@ -365,9 +365,10 @@ static hipError_t conv_fwd_t(const gdn_shape& s, const void* x, int64_t ldx, con
   const int n_l2 = l2 ? 2 * s.hk * s.dk : 0;
   const int64_t nT = s.total_tokens;
   if (nT == 0) return hipSuccess;
-  dim3 grid((unsigned)conv_partials(nT), (C / 8 + 63) / 64);
+  const int tt = conv_tt(nT, C);
+  dim3 grid((unsigned)conv_partials(nT, tt), (C / 8 + 63) / 64);
   hipLaunchKernelGGL((conv_fwd_kernel<T, D>), grid, dim3(256), 0, st, (const T*)x, ldx, w, cu,
-                     s.n_seq, nT, C, n_l2, eps, (T*)y, ldy);
+                     s.n_seq, nT, tt, C, n_l2, eps, (T*)y, ldy);
   return hipGetLastError();
 }
 
@@ -378,11 +379,12 @@ static hipError_t conv_bwd_t(const gdn_shape& s, const void* x, int64_t ldx, con
   const int C = 2 * s.hk * s.dk + s.hv * s.dv;
   const int n_l2 = l2 ? 2 * s.hk * s.dk : 0;
   const int64_t nT = s.total_tokens;
-  const int64_t np = conv_partials(nT);
+  const int tt = conv_tt(nT, C);
+  const int64_t np = conv_partials(nT, tt);
   if (nT > 0) {
     dim3 grid((unsigned)np, (C / 8 + 63) / 64);
     hipLaunchKernelGGL((conv_bwd_kernel<T, D>), grid, dim3(256), 0, st, (const T*)x, ldx, w, cu,
-                       s.n_seq, nT, C, n_l2, eps, (const T*)dy, lddy, (T*)dx, lddx, partials);
+                       s.n_seq, nT, tt, C, n_l2, eps, (const T*)dy, lddy, (T*)dx, lddx, partials);
   }
   return launch_reduce_partials(partials, np, (int64_t)C * 4, dw, st);
 }
