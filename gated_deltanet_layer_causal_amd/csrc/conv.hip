@@ -83,7 +83,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_of(const T* base, int64_t
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) conv_fwd_kernel(const T* __restrict__ x, int64_t ldx,
+__global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_fwd_kernel(const T* __restrict__ x, int64_t ldx,
                                                        const float* __restrict__ w,
                                                        const int32_t* __restrict__ cu, int n_seq,
                                                        int64_t T_tok, int tt, int C, int n_l2, float eps,
@@ -189,7 +189,7 @@ __device__ __forceinline__ f8 conv_du(const float (&wr)[8][4], const f8& x0, con
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) conv_bwd_kernel(
+__global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
     const T* __restrict__ x, int64_t ldx, const float* __restrict__ w,
     const int32_t* __restrict__ cu, int n_seq, int64_t T_tok, int tt, int C, int n_l2, float eps,
     const T* __restrict__ dy, int64_t lddy, T* __restrict__ dx, int64_t lddx,
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(
       --n;
     }
   }
-  // combine the four runs of this block in a fixed order
+  // combine the runs of this block in a fixed order
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -367,7 +367,7 @@ static hipError_t conv_fwd_t(const gdn_shape& s, const void* x, int64_t ldx, con
   if (nT == 0) return hipSuccess;
   const int tt = conv_tt(nT, C);
   dim3 grid((unsigned)conv_partials(nT, tt), (C / 8 + 63) / 64);
-  hipLaunchKernelGGL((conv_fwd_kernel<T, D>), grid, dim3(256), 0, st, (const T*)x, ldx, w, cu,
+  hipLaunchKernelGGL((conv_fwd_kernel<T, D>), grid, dim3(64 * CONV_RUNS_PER_BLOCK), 0, st, (const T*)x, ldx, w, cu,
                      s.n_seq, nT, tt, C, n_l2, eps, (T*)y, ldy);
   return hipGetLastError();
 }
@@ -383,7 +383,7 @@ static hipError_t conv_bwd_t(const gdn_shape& s, const void* x, int64_t ldx, con
   const int64_t np = conv_partials(nT, tt);
   if (nT > 0) {
     dim3 grid((unsigned)np, (C / 8 + 63) / 64);
-    hipLaunchKernelGGL((conv_bwd_kernel<T, D>), grid, dim3(256), 0, st, (const T*)x, ldx, w, cu,
+    hipLaunchKernelGGL((conv_bwd_kernel<T, D>), grid, dim3(64 * CONV_RUNS_PER_BLOCK), 0, st, (const T*)x, ldx, w, cu,
                        s.n_seq, nT, tt, C, n_l2, eps, (const T*)dy, lddy, (T*)dx, lddx, partials);
   }
   return launch_reduce_partials(partials, np, (int64_t)C * 4, dw, st);
