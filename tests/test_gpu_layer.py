@@ -24,6 +24,14 @@ CASES = {
                                [40, 1, 90], (0.02, 0.3), L.GDN_ACT_SIGMOID),
     "bf16_small": (gi.Workload("bs", 0, 2, 6, 128, "bf16", seq="varlen", init_state=True,
                                final_state=True, seed=78), [300, 65, 7], None, L.GDN_ACT_SILU),
+    # empty sequences inside and at the end of the pack: their state passes
+    # through unchanged and so does its gradient
+    "bf16_empty_seqs": (gi.Workload("be", 0, 2, 4, 128, "bf16", seq="varlen", init_state=True,
+                                    final_state=True, seed=79), [70, 0, 64, 0, 5], None,
+                        L.GDN_ACT_SILU),
+    "fp32_empty_first": (gi.Workload("fe", 0, 1, 2, 32, "fp32", seq="varlen", init_state=True,
+                                     final_state=True, seed=80), [0, 40, 0, 3], (0.02, 0.3),
+                         L.GDN_ACT_SIGMOID),
 }
 
 
@@ -59,3 +67,9 @@ def test_layer_matches_oracle(name, save_states):
     print(name, "saved" if save_states else "recompute", " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
     for k, t, r, tol in checks:
         assert_close(k, host(t).reshape(np.shape(r)), r, tol)
+    # a sequence without tokens hands its initial state and the final state's
+    # gradient straight through (exactly: no arithmetic touches them)
+    for n, ln in enumerate(lens):
+        if ln == 0:
+            np.testing.assert_array_equal(host(f["S_final"])[n], np.float32(inp["S0"][n]))
+            np.testing.assert_array_equal(host(gb["dS0"])[n], np.float32(inp["dS_T"][n]))

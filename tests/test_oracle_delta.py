@@ -160,6 +160,28 @@ def test_I5_varlen_equals_separate_runs():
         np.testing.assert_array_equal(Sf[n], Sn[0])
 
 
+def test_empty_sequences_pass_state_through():
+    """A sequence without tokens applies no step of the recurrence: its final
+    state is its initial state and the gradient of its initial state is the
+    final state's gradient; the other sequences are the same as without it."""
+    rng = np.random.default_rng(15)
+    lens = [0, 9, 0, 6, 0]
+    q, k, v, g, beta, cu, s0 = _rand_case(rng, sum(lens), 1, 2, 5, lens, True)
+    o, Sf = oracle.delta_fwd(q, k, v, g, beta, cu, 0.6, s0)
+    dout = rng.standard_normal(o.shape)
+    dST = rng.standard_normal(Sf.shape)
+    *_, dS0 = oracle.delta_bwd(q, k, v, g, beta, cu, 0.6, dout, s0, dST)
+    keep = [n for n, ln in enumerate(lens) if ln > 0]
+    cu2 = np.concatenate([[0], np.cumsum([lens[n] for n in keep])]).astype(np.int32)
+    o2, Sf2 = oracle.delta_fwd(q, k, v, g, beta, cu2, 0.6, s0[keep])
+    for n, ln in enumerate(lens):
+        if ln == 0:
+            np.testing.assert_array_equal(Sf[n], s0[n])
+            np.testing.assert_array_equal(dS0[n], dST[n])
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(Sf[keep], Sf2)
+
+
 def test_I6_continuation_through_final_state():
     rng = np.random.default_rng(6)
     q, k, v, g, beta, cu, s0 = _rand_case(rng, 30, 1, 2, 5, [30], True)
