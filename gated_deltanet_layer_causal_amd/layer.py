@@ -173,3 +173,63 @@ class GDNCore:
         return {"do": do, "dz": dz, "dw_norm": dw_norm, "dy_conv": dy, "dg": dg, "dbeta": dbeta,
                 "dS0": dS0, "da": da, "db": db, "dA_log": dA_log, "ddt_bias": ddt, "dx": dx,
                 "dw_conv": dw_conv}
+
+
+class GDNLayer:
+    """The layer with its projections: hidden states X [T, H] -> in_proj ->
+    GDNCore -> out_proj -> Y [T, H], forward and backward.
+
+    The projections are plain GEMMs, left to the library (torch.matmul, which
+    runs hipBLASLt on ROCm); everything between them is GDNCore, i.e. libgdn.
+    in_proj is four products so that each core input is contiguous:
+    x = X W_x^T (q | k | v channels), z = X W_z^T, a = X W_a^T, b = X W_b^T;
+    out_proj is Y = out W_out^T.  Weights are held transposed ([in, out]),
+    so every right operand is a contiguous matrix."""
+
+    NAMES = ("x", "z", "a", "b", "out")
+
+    def __init__(self, cfg: CoreConfig, hidden: int, weights: dict, device="cuda"):
+        """weights: name -> [out, in] tensors (the nn.Linear convention)."""
+        self.core = GDNCore(cfg, device)
+        self.cfg = cfg
+        self.hidden = hidden
+        self.Wt = {k: weights[k].t().contiguous() for k in self.NAMES}   # [in, out]
+        self.W = {k: weights[k].contiguous() for k in self.NAMES}        # [out, in]
+
+    def forward(self, X, w_conv, A_log, dt_bias, w_norm, cu_seqlens, S0=None, want_final=False,
+                timer=None):
+        c = self.cfg
+        T = X.shape[0]
+        with _timed(timer, "in_proj"):
+            x = X @ self.Wt["x"]
+            z = (X @ self.Wt["z"]).view(T, c.hv, c.d)
+            a = X @ self.Wt["a"]
+            b = X @ self.Wt["b"]
+        f = self.core.forward(x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, S0=S0,
+                              want_final=want_final, timer=timer)
+        out = f["out"].view(T, c.hv * c.d)
+        with _timed(timer, "out_proj"):
+            Y = out @ self.Wt["out"]
+        f.update(x=x, z=z, a=a, b=b, Y=Y)
+        return f
+
+    def backward(self, saved, X, w_conv, A_log, dt_bias, w_norm, cu_seqlens, dY, S0=None,
+                 dS_final=None, timer=None):
+        c = self.cfg
+        T = X.shape[0]
+        with _timed(timer, "out_proj_bwd"):
+            dout = (dY @ self.W["out"]).view(T, c.hv, c.d)
+            dW_out = dY.t() @ saved["out"].view(T, c.hv * c.d)
+        g = self.core.backward(saved, saved["x"], w_conv, saved["a"], saved["b"], A_log, dt_bias,
+                               saved["z"], w_norm, cu_seqlens, dout, S0=S0, dS_final=dS_final,
+                               timer=timer)
+        with _timed(timer, "in_proj_bwd"):
+            gz = g["dz"].view(T, c.hv * c.d)
+            dX = g["dx"] @ self.W["x"]
+            dX.addmm_(gz, self.W["z"])
+            dX.addmm_(g["da"], self.W["a"])
+            dX.addmm_(g["db"], self.W["b"])
+            dW = {"x": g["dx"].t() @ X, "z": gz.t() @ X, "a": g["da"].t() @ X, "b": g["db"].t() @ X,
+                  "out": dW_out}
+        g.update(dX=dX, dW=dW, dout=dout)
+        return g

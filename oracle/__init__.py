@@ -236,3 +236,45 @@ def layer_bwd(inp: dict, fwd: dict, hk: int, hv: int, d: int, scale: float, act:
     return {"do": do, "dz": dz, "dw_norm": dw_norm, "dq": dq, "dk": dk, "dv": dv, "dg": dg,
             "dbeta": dbeta, "dS0": dS0, "dy_conv": dy_conv, "da": da, "db": db,
             "dA_log": dA_log, "ddt_bias": ddt_bias, "dx": dx, "dw_conv": dw_conv}
+
+
+# ---------------------------------------------------------------------------
+# The layer with its projections: hidden states X [T, H] go through plain
+# products to the core's inputs (x = X W_x^T with the q | k | v channels,
+# z = X W_z^T, a = X W_a^T, b = X W_b^T), the core runs as layer_fwd, and its
+# gated-norm output leaves through Y = out W_out^T.  The projections are the
+# plain definition (numpy products in fp64); ``round_fn`` marks the tensors
+# handed between calls in the storage dtype, as in layer_fwd.
+def proj_layer_fwd(X, W: dict, params: dict, cu, hk: int, hv: int, d: int, scale: float,
+                   act: int = ACT_SILU, round_fn=None, S0=None):
+    rf = (lambda a: a) if round_fn is None else round_fn
+    X = _f64(X)
+    T = X.shape[0]
+    inp = {"x": rf(X @ _f64(W["x"]).T), "z": rf(X @ _f64(W["z"]).T).reshape(T, hv, d),
+           "a": rf(X @ _f64(W["a"]).T), "b": rf(X @ _f64(W["b"]).T), "cu_seqlens": cu, "S0": S0}
+    inp.update(params)
+    f = layer_fwd(inp, hk, hv, d, scale, act, round_fn)
+    out = rf(f["out"]).reshape(T, hv * d)
+    f.update(inp=inp, out_flat=out, Y=out @ _f64(W["out"]).T)
+    return f
+
+
+def proj_layer_bwd(X, W: dict, fwd: dict, dY, hk: int, hv: int, d: int, scale: float,
+                   act: int = ACT_SILU, round_fn=None, dS_T=None):
+    """Backward of proj_layer_fwd for the upstream gradient dY [T, H]: the
+    core's backward between the products' transposes.  Weight gradients are
+    dW = (gradient of the product's output)^T (its input)."""
+    rf = (lambda a: a) if round_fn is None else round_fn
+    X, dY = _f64(X), _f64(dY)
+    T = X.shape[0]
+    inp = dict(fwd["inp"])
+    inp["dy"] = rf(dY @ _f64(W["out"])).reshape(T, hv, d)
+    inp["dS_T"] = dS_T
+    g = layer_bwd(inp, fwd, hk, hv, d, scale, act, round_fn)
+    gx, gz = g["dx"], g["dz"].reshape(T, hv * d)
+    ga, gb = g["da"], g["db"]
+    g["dX"] = gx @ _f64(W["x"]) + gz @ _f64(W["z"]) + ga @ _f64(W["a"]) + gb @ _f64(W["b"])
+    g["dW"] = {"x": gx.T @ X, "z": gz.T @ X, "a": ga.T @ X, "b": gb.T @ X,
+               "out": dY.T @ fwd["out_flat"]}
+    return g
+

@@ -11,7 +11,7 @@ import torch
 import oracle
 from gated_deltanet_layer_causal_amd import capi as L
 from gated_deltanet_layer_causal_amd import inputs as gi
-from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore
+from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore, GDNLayer
 from tests.gpu_util import DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_close, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -73,3 +73,47 @@ def test_layer_matches_oracle(name, save_states):
         if ln == 0:
             np.testing.assert_array_equal(host(f["S_final"])[n], np.float32(inp["S0"][n]))
             np.testing.assert_array_equal(host(gb["dS0"])[n], np.float32(inp["dS_T"][n]))
+
+
+def test_layer_with_projections_matches_oracle():
+    """The layer with its in/out projections (library GEMMs around libgdn)
+    against the oracle's composition (fp64 products around the core oracle,
+    rounded to bf16 where the layer hands tensors between calls)."""
+    hk, hv, d, H = 2, 4, 128, 256
+    w = gi.Workload("pl", 0, hk, hv, d, "bf16", seq="varlen", init_state=True, final_state=True,
+                    seed=81)
+    lens = [150, 64, 1]
+    inp = gi.make_inputs(w, seqlens=lens)
+    T = sum(lens)
+    rng = np.random.default_rng(82)
+    rb = gi.round_bf16
+    X = rb(rng.standard_normal((T, H)).astype(np.float32))
+    shapes = {"x": (w.channels, H), "z": (hv * d, H), "a": (hv, H), "b": (hv, H), "out": (H, hv * d)}
+    W = {k: rb((rng.standard_normal(s) / np.sqrt(s[1])).astype(np.float32)) for k, s in shapes.items()}
+    dY = rb(rng.standard_normal((T, H)).astype(np.float32))
+    params = {k: inp[k] for k in ("w_conv", "A_log", "dt_bias", "w_norm")}
+    bf = torch.bfloat16
+    layer = GDNLayer(CoreConfig(hk=hk, hv=hv, d=d, dtype=bf), H, {k: dev(v, bf) for k, v in W.items()},
+                     device=DEV)
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(DEV)
+    gargs = (dev(params["w_conv"]), dev(params["A_log"]), dev(params["dt_bias"]), dev(params["w_norm"]), cu)
+    S0, dST = dev(inp["S0"]), dev(inp["dS_T"])
+    f = layer.forward(dev(X, bf), *gargs, S0=S0, want_final=True)
+    g = layer.backward(f, dev(X, bf), *gargs, dev(dY, bf), S0=S0, dS_final=dST)
+    torch.cuda.synchronize()
+
+    sc = d ** -0.5
+    rf_ = oracle.proj_layer_fwd(X, W, params, inp["cu_seqlens"], hk, hv, d, sc, round_fn=rb,
+                                S0=inp["S0"])
+    rg = oracle.proj_layer_bwd(X, W, rf_, dY, hk, hv, d, sc, round_fn=rb, dS_T=inp["dS_T"])
+    checks = [("Y", f["Y"], rf_["Y"], FWD_TOL_BF16), ("S_final", f["S_final"], rf_["S_final"], FWD_TOL_BF16),
+              ("dX", g["dX"], rg["dX"], GRAD_TOL_BF16), ("dS0", g["dS0"], rg["dS0"], GRAD_TOL_BF16),
+              ("dw_conv", g["dw_conv"], rg["dw_conv"], GRAD_TOL_BF16),
+              ("dA_log", g["dA_log"], rg["dA_log"], GRAD_TOL_BF16),
+              ("ddt_bias", g["ddt_bias"], rg["ddt_bias"], GRAD_TOL_BF16),
+              ("dw_norm", g["dw_norm"], rg["dw_norm"], GRAD_TOL_BF16)]
+    checks += [(f"dW_{k}", g["dW"][k], rg["dW"][k], GRAD_TOL_BF16) for k in W]
+    errs = {k: rel_err(host(t).reshape(np.shape(r)), r) for k, t, r, _ in checks}
+    print("projections", " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    for k, t, r, tol in checks:
+        assert_close(k, host(t).reshape(np.shape(r)), r, tol)

@@ -221,3 +221,44 @@ def test_layer_backward_finite_differences():
             num = (L(key, x0 + h * u) - L(key, x0 - h * u)) / (2 * h)
             ana = float((bwd[gkey] * u).sum())
             assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (key, num, ana)
+
+
+def test_projection_layer_backward_finite_differences():
+    """The layer with its in/out projections: directional central differences
+    for the hidden states and every projection weight, against the composed
+    backward (the core's own gradients are pinned above)."""
+    w = gi.Workload("fdp", 10, 1, 2, 4, "fp32", seq="varlen", init_state=True, final_state=True,
+                    seed=6)
+    inp = gi.make_inputs(w, seqlens=[7, 3], A_range=(0.05, 0.5))
+    hk, hv, d, sc, H = 1, 2, 4, 0.5, 6
+    rng = np.random.default_rng(9)
+    T, C = 10, w.channels
+    X = rng.standard_normal((T, H))
+    W = {"x": rng.standard_normal((C, H)) / np.sqrt(H), "z": rng.standard_normal((hv * d, H)) / np.sqrt(H),
+         "a": rng.standard_normal((hv, H)) / np.sqrt(H), "b": rng.standard_normal((hv, H)) / np.sqrt(H),
+         "out": rng.standard_normal((H, hv * d)) / np.sqrt(hv * d)}
+    params = {k: inp[k].astype(np.float64) for k in ("w_conv", "A_log", "dt_bias", "w_norm")}
+    S0 = inp["S0"].astype(np.float64)
+    dY = rng.standard_normal((T, H))
+    dST = inp["dS_T"].astype(np.float64)
+    cu = inp["cu_seqlens"]
+    fwd = oracle.proj_layer_fwd(X, W, params, cu, hk, hv, d, sc, S0=S0)
+    bwd = oracle.proj_layer_bwd(X, W, fwd, dY, hk, hv, d, sc, dS_T=dST)
+
+    def L(X_, W_):
+        f = oracle.proj_layer_fwd(X_, W_, params, cu, hk, hv, d, sc, S0=S0)
+        return float((f["Y"] * dY).sum() + (f["S_final"] * dST).sum())
+
+    h = 1e-6
+    for _ in range(2):
+        u = rng.standard_normal(X.shape)
+        num = (L(X + h * u, W) - L(X - h * u, W)) / (2 * h)
+        ana = float((bwd["dX"] * u).sum())
+        assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), ("X", num, ana)
+    for key in W:
+        u = rng.standard_normal(W[key].shape)
+        Wp, Wm = dict(W), dict(W)
+        Wp[key], Wm[key] = W[key] + h * u, W[key] - h * u
+        num = (L(X, Wp) - L(X, Wm)) / (2 * h)
+        ana = float((bwd["dW"][key] * u).sum())
+        assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (key, num, ana)
