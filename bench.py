@@ -149,6 +149,9 @@ def parse():
     p.add_argument("--seed", type=int, default=1005)
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--proj-hidden", type=int, default=2560,
+                   help="hidden size of the layer with its in/out projections, timed beside the "
+                        "core (0: skip)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain bf16 device copy of MIB MiB three times (reference "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -216,6 +219,58 @@ class EventTimer:
             ts = [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs) - 1, 2)]
             out[name] = sum(ts) / len(ts)
         return out
+
+
+# Per-layer forward+backward of Qwen3.8-Flash's GDN layer (hidden 2560, 16 k /
+# 48 v heads) at TP=1 on one H200, 64k tokens, as printed on the miles page
+# (H200 results): another machine's figure, with the projections; context only.
+PAGES_H200_LAYER_MS_64K = 52.6
+
+
+def layer_with_projections(w, hidden, inp, steps, warmup, dev):
+    """The layer with its in/out projections (library GEMMs around the core),
+    forward+backward, timed like the core.  Returns the JSON object."""
+    import torch
+    from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNLayer
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    bf = torch.bfloat16
+    T, C, Hv, d = w.T, w.channels, w.hv, w.d
+    shapes = {"x": (C, hidden), "z": (Hv * d, hidden), "a": (Hv, hidden), "b": (Hv, hidden),
+              "out": (hidden, Hv * d)}
+    W = {k: (torch.randn(s, generator=g, device=dev) / math.sqrt(s[1])).to(bf) for k, s in shapes.items()}
+    layer = GDNLayer(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=bf), hidden, W, device=dev)
+    X = torch.randn((T, hidden), generator=g, device=dev).to(bf)
+    dY = torch.randn((T, hidden), generator=g, device=dev).to(bf)
+    pa = (inp["w_conv"], inp["A_log"], inp["dt_bias"], inp["w_norm"], inp["cu_seqlens"])
+    timer = EventTimer()
+
+    def step():
+        f = layer.forward(X, *pa, timer=timer)
+        layer.backward(f, X, *pa, dY, timer=timer)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.active = True
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    pc = timer.mean_ms()
+    gemm_ms = sum(pc[k] for k in ("in_proj", "out_proj", "in_proj_bwd", "out_proj_bwd"))
+    n_out = C + Hv * d + 2 * Hv
+    gemm_flop = 3 * 2 * T * hidden * (n_out + Hv * d)    # forward, input and weight gradients
+    return {"hidden": hidden, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1),
+            "gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(gemm_flop / (gemm_ms / 1e3) / 1e12, 1),
+            "gemm_frac_bf16_peak": round(gemm_flop / (gemm_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "gemms": "torch.matmul (hipBLASLt), bf16, fp32 accumulate",
+            "pages_h200_ms_per_layer": PAGES_H200_LAYER_MS_64K if T == 65536 else None,
+            "note": "in_proj -> core -> out_proj, forward and backward with all weight gradients; "
+                    "the pages' figure is another machine's (context, not a target)"}
 
 
 def cpu_baseline(w, sample_T):
@@ -311,6 +366,9 @@ def main():
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
         "calls": calls,
     }
+    if args.proj_hidden > 0 and w.dtype == "bf16":
+        out["layer_with_projections"] = layer_with_projections(w, args.proj_hidden, inp, args.steps,
+                                                               args.warmup, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
