@@ -290,9 +290,9 @@ def cpu_baseline(w, sample_T):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the layer core is head-parallel; a multi-GPU run would shard heads, see the "
-              "design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer core "
+              "is head-parallel: a multi-GPU run would give each GPU a group of key heads with "
+              "their value heads, with no exchange inside the core)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

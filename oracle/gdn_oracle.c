@@ -33,8 +33,7 @@
  *     o_t = S_t (scale * q_t),
  * with S a d_v x d_k matrix per (sequence, value head).
  *
- * Readings where the pages are silent (each one is a choice, listed in the
- * design notes):
+ * Readings where the pages are silent (each one is a choice):
  *  - conv: depthwise cross-correlation, taps w[c][0..K-1], w[c][K-1] on the
  *    current token, zero left padding at every sequence start, no bias,
  *    no state carried in or out; SiLU on every channel afterwards.
