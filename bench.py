@@ -149,9 +149,10 @@ def parse():
     p.add_argument("--seed", type=int, default=1005)
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--proj-hidden", type=int, default=2560,
+    p.add_argument("--proj-hidden", type=int, default=None,
                    help="hidden size of the layer with its in/out projections, timed beside the "
-                        "core (0: skip)")
+                        "core (0: skip; default: 2560 for the 16 k / 48 v-head shapes, the "
+                        "Qwen3.8-Flash layer, else skip)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain bf16 device copy of MIB MiB three times (reference "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -190,6 +191,12 @@ def make_gpu_inputs(w, seed, dev):
         "z": n((T, Hv, d), dt=bf), "w_norm": n((d,), 0.1), "dy": n((T, Hv, d), dt=bf),
         "cu_seqlens": torch.tensor([0, T], dtype=torch.int32, device=dev),
     }
+    if w.seq == "varlen":
+        # the packed lengths are drawn as the parity tests draw them
+        import numpy as np
+        from gated_deltanet_layer_causal_amd import inputs as gi
+        lens = gi.varlen_lengths(np.random.Generator(np.random.PCG64(w.seed)), T)
+        inp["cu_seqlens"] = torch.from_numpy(gi.cu_from_lengths(lens)).to(dev)
     if w.init_state:
         inp["S0"] = n((1, Hv, d, d), 0.1)
     if w.final_state:
@@ -357,7 +364,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded on-device draws with the workload's distributions)",
         "config": {"workload": f"{w.name}: GDN layer core fwd+bwd, {w.hk} k-heads / {w.hv} v-heads, "
-                               f"d={w.d}, {w.T} tokens, single sequence, chunk 64",
+                               f"d={w.d}, {w.T} tokens, "
+                               f"{'varlen pack' if w.seq == 'varlen' else 'single sequence'}, chunk 64",
                    "tokens": w.T, "hk": w.hk, "hv": w.hv, "d": w.d, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom),
@@ -366,8 +374,11 @@ def main():
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
         "calls": calls,
     }
-    if args.proj_hidden > 0 and w.dtype == "bf16":
-        out["layer_with_projections"] = layer_with_projections(w, args.proj_hidden, inp, args.steps,
+    hidden = args.proj_hidden
+    if hidden is None:
+        hidden = 2560 if (w.hk, w.hv, w.d) == (16, 48, 128) else 0
+    if hidden > 0 and w.dtype == "bf16":
+        out["layer_with_projections"] = layer_with_projections(w, hidden, inp, args.steps,
                                                                args.warmup, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
