@@ -298,9 +298,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
       store8(Mout + t * CHUNK + 8 * p, v);
     }
     if constexpr (BWD) {
-      // Tinv in the storage type for the chunk gradients: rows t with the
-      // columns in accumulator order, then Tinv^T (rows u, natural order;
-      // the reverse pass reads it as M^T = diag(beta) Tinv^T)
+      // Tinv in the storage type for the chunk gradients and the reverse pass
+      // (which reads M^T = diag(beta) Tinv^T): rows t with the columns in
+      // accumulator order, then, for fp32, Tinv^T (rows u, natural order)
       T* to = Tib + ((int64_t)c * Hv + h) * 2 * CHUNK * CHUNK;
       for (int i = tid; i < CHUNK * (CHUNK / 8); i += 256) {
         const int r = i >> 3, p = i & 7;
@@ -308,9 +308,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
         for (int j = 0; j < 8; ++j) v.v[j] = sTi[r][acc_piece_col<T>(p, j)];
         store8(to + r * CHUNK + 8 * p, v);
+        if constexpr (sizeof(T) == 4) {   // (16-bit readers transpose Tinv in LDS)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v.v[j] = sTi[8 * p + j][r];
-        store8(to + CHUNK * CHUNK + r * CHUNK + 8 * p, v);
+          for (int j = 0; j < 8; ++j) v.v[j] = sTi[8 * p + j][r];
+          store8(to + CHUNK * CHUNK + r * CHUNK + 8 * p, v);
+        }
       }
     }
     // W = Tinv diag(beta Gam) K: wave w forms rows [16w, 16w+16) in the dead

@@ -53,11 +53,12 @@ template <typename T, int D> struct GradLds {
   T WA[CHUNK][LDP];               // WA: row t, column s
   T WS[CHUNK][LDP];               // WA + WA^T: row x, columns u in accumulator order
   float E[CHUNK][CHUNK + 1];      // pair terms of dg
-  // Tinv (columns in accumulator order) and Tinv^T, copied for 16-bit types
-  // (fp32 reads them from memory where used: the LDS holds no more)
+  // Tinv (columns in accumulator order), copied for 16-bit types, whose
+  // Tinv^T operands are transposing reads of it (fp32 reads Tinv and Tinv^T
+  // from memory where used: the LDS holds no more)
   static constexpr bool TIN_LDS = sizeof(T) == 2;
   typedef Tile<T, CHUNK, CHUNK> TI;
-  T Tin[TIN_LDS ? 2 * CHUNK * CHUNK : 8];
+  T Tin[TIN_LDS ? CHUNK * CHUNK : 8];
   double gam[CHUNK];
   float bet[CHUNK], Gm[CHUNK], dc[CHUNK];
   float colB[4][CHUNK], rowB[CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
@@ -275,24 +276,39 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       sm.dc[lane] = dexp<T>(glast - gnext);
     }
   };
-  // ... Tinv and Tinv^T (16-bit types: into LDS, by direct copies) ...
+  // ... Tinv (16-bit types: into LDS, by direct copies) ...
   typedef typename GL::TI TI;
   auto copy_tinv = [&](int h, bool live) __attribute__((always_inline)) {
     if constexpr (GL::TIN_LDS) {
       const char* src = reinterpret_cast<const char*>(Tib + (c * Hv + h) * 2 * CHUNK * CHUNK);
-      const uint32_t bytes = live ? 2 * CHUNK * CHUNK * sizeof(T) : 0u;
+      const uint32_t bytes = live ? CHUNK * CHUNK * sizeof(T) : 0u;
 #pragma unroll
-      for (int j = 0; j < 2 * TI::PIECES / 512; ++j) {
-        const int s = (j * 8 + wave) * 64 + lane, r = s / TI::RP;   // r: row of both matrices
+      for (int j = 0; j < TI::PIECES / 512; ++j) {
+        const int s = (j * 8 + wave) * 64 + lane, r = s / TI::RP;
         const uint32_t off = (uint32_t)(r * TI::RP + ((s % TI::RP) ^ TI::swz(r))) * 16u;
         copy_to_lds(buffer_of(src, bytes), sm.Tin + (j * 8 + wave) * 64 * TI::EPP, off, 0);
       }
     }
   };
-  // element (r, col) of Tinv (m = 0, columns in accumulator order) or Tinv^T (m = 1)
+  // element (r, col) of Tinv (m = 0, columns in accumulator order) or, for
+  // fp32, Tinv^T (m = 1)
   auto tin = [&](int h, int m, int r, int col) __attribute__((always_inline)) -> const T* {
-    if constexpr (GL::TIN_LDS) return sm.Tin + m * CHUNK * CHUNK + TI::at(r, col);
+    if constexpr (GL::TIN_LDS) return sm.Tin + TI::at(r, col);
     else return Tib + (c * Hv + h) * 2 * CHUNK * CHUNK + m * CHUNK * CHUNK + r * CHUNK + col;
+  };
+  // B operand of step p from row tl of Tinv^T (reduction indices pcol(p)
+  // .. + 7, natural order).  16-bit: two transposing reads down column tl of
+  // Tinv, whose columns are in accumulator order: lanes 4a .. 4a + 3 of a
+  // group point at stored columns 32 (tw / 2) + 8 a + 4 (tw % 2) .. + 3, and
+  // lane j of group g at row 32 p + 8 g + j / 4 (then 4 rows further)
+  auto tinvt_frag = [&](int h, int p) __attribute__((always_inline)) -> frag {
+    if constexpr (GL::TIN_LDS) {
+      const int col = 32 * (tw >> 1) + 8 * (c16 & 3) + 4 * (tw & 1), r = 32 * p + 8 * g + (c16 >> 2);
+      const u32x2 lo = lds_read_tr4(sm.Tin + TI::at(r, col)), hi = lds_read_tr4(sm.Tin + TI::at(r + 4, col));
+      return __builtin_bit_cast(frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    } else {
+      return rdf(tin(h, 1, tl, pcol(p)), 0);
+    }
   };
   // ... the phase-A operands: the Tinv-chain waves' rows of dDelta or the
   // dP-side waves' P values, as loaded, in one register array for both roles
@@ -482,7 +498,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         floatx4 da = zero4();
 #pragma unroll
         for (int p = 0; p < NSC; ++p)
-          da = MM::mma(rdf(&sm.YT[16 * st + c16][0], pcol(p)), rdf(tin(h, 1, tl, pcol(p)), 0), da);
+          da = MM::mma(rdf(&sm.YT[16 * st + c16][0], pcol(p)), tinvt_frag(h, p), da);
         float wa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -11,10 +11,10 @@
 // (sequence, value head, block of 16 * NW value rows); compute wave w keeps
 // its d_k x 16 slice of dS'^T in MFMA accumulators and feeds it straight
 // back as B operand; NW mover waves (on the SIMDs the compute waves leave
-// free) stream the chunk operands (K rows, K^T, Q^T, P^T from the backward
-// preparation, columns in accumulator order; Tinv^T in natural order; the
-// dO rows of the block; Gam, dec, beta) into one of two LDS buffers by direct copies while the
-// compute waves work on the other.  Operands are in the storage type (bf16
+// free) stream the chunk operands (K rows, K^T, Q^T, P^T and Tinv from the
+// backward preparation, columns in accumulator order (fp32: Tinv^T); the dO
+// rows of the block; Gam, dec, beta) into one of two LDS buffers by direct
+// copies while the compute waves work on the other.  Operands are in the storage type (bf16
 // keeps the range of dS).
 #include "chunk_stream.h"
 
@@ -24,7 +24,7 @@ template <typename T, int D, int NW> struct RevBuf {
   static constexpr int BV = 16 * NW;
   typedef Tile<T, CHUNK, D> TK;        // K rows
   typedef Tile<T, D, CHUNK> TKt;       // K^T, Q^T
-  typedef Tile<T, CHUNK, CHUNK> TM;    // P^T, Tinv^T
+  typedef Tile<T, CHUNK, CHUNK> TM;    // P^T, Tinv (fp32: Tinv^T)
   typedef Tile<T, CHUNK, BV, 3> TO;    // dO rows of this block
   // 16-bit types read K^T from the K rows by transposing reads; fp32 copies it
   static constexpr bool KT_TR = sizeof(T) == 2;
@@ -32,7 +32,7 @@ template <typename T, int D, int NW> struct RevBuf {
   T Kt[KT_TR ? 8 : TKt::PIECES * TKt::EPP];
   T Qt[TKt::PIECES * TKt::EPP];
   T Pt[TM::PIECES * TM::EPP];
-  T Mt[TM::PIECES * TM::EPP];          // Tinv^T
+  T Mt[TM::PIECES * TM::EPP];          // Tinv (16-bit) or Tinv^T (fp32)
   T dO[TO::PIECES * TO::EPP];
   float G[CHUNK], Dc[CHUNK], Bt[CHUNK];   // Gam_t, dec_t, beta_t
 } __attribute__((aligned(16)));
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     if constexpr (!RB::KT_TR) copy_tile<TKt, NW>(B.Kt, Ktb + ck * D * CHUNK, cl, wave);
     copy_tile<TKt, NW>(B.Qt, Qtb + ck * D * CHUNK, cl, wave);
     copy_tile<TM, NW>(B.Pt, Ptb + ch * CHUNK * CHUNK, cl, wave);
-    copy_tile<TM, NW>(B.Mt, Tib + ch * 2 * CHUNK * CHUNK + CHUNK * CHUNK, cl, wave);
+    copy_tile<TM, NW>(B.Mt, Tib + ch * 2 * CHUNK * CHUNK + (RB::KT_TR ? 0 : CHUNK * CHUNK), cl, wave);
     {
       // dO rows past the sequence end re-read its last row (their products
       // meet zero rows and columns of P^T, Q^T)
@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     if constexpr (!RB::KT_TR) touch_tile(Ktb + ck * D * CHUNK, TKB, NTK, wave);
     touch_tile(Qtb + ck * D * CHUNK, TKB, NTK, wave);
     touch_tile(Ptb + ch * CHUNK * CHUNK, TMB, NTM, wave);
-    touch_tile(Tib + ch * 2 * CHUNK * CHUNK + CHUNK * CHUNK, TMB, NTM, wave);
+    touch_tile(Tib + ch * 2 * CHUNK * CHUNK + (RB::KT_TR ? 0 : CHUNK * CHUNK), TMB, NTM, wave);
     // the block's dO rows (one line each)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         buffer_of(dout + t0 * HvD + (int64_t)h * D + v0, (uint32_t)Lc * rowb),
@@ -192,17 +192,18 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     }
   };
 
-  // A operand of step p from row 16 tt + c16 of Tinv^T, whose columns are in
-  // natural order: for 16-bit types the step's eight reduction indices
-  // 32 p + 4 g + (0..3) and 32 p + 16 + 4 g + (0..3) (accumulator order) are
-  // two 8-byte pieces; fp32 keeps one index per step (natural order)
+  // A operand of step p from row 16 tt + c16 of Tinv^T.  16-bit: the tile
+  // holds Tinv (columns in accumulator order), read down column 16 tt + c16
+  // by two transposing reads, as kt_frag reads the K rows: lanes 4a .. 4a + 3
+  // of a group point at stored columns 32 (tt / 2) + 8 a + 4 (tt % 2) .. + 3,
+  // lane j of group g at row 32 p + 4 g + j / 4 (then 16 rows further).
+  // fp32: the tile holds Tinv^T (natural order), one index per step.
   auto tt_frag = [&](const RB& B, int tt, int p) __attribute__((always_inline)) -> frag {
     if constexpr (KS == 4) {
       return arow(B.Mt, rk[p], 16 * tt * CHUNK);
     } else {
-      const int r = 16 * tt + c16;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(B.Mt + TM::at(r, 32 * p + g4));
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(B.Mt + TM::at(r, 32 * p + 16 + g4));
+      const int col = 32 * (tt >> 1) + 8 * (c16 & 3) + 4 * (tt & 1), r = 32 * p + g4 + (c16 >> 2);
+      const u32x2 lo = lds_read_tr4(B.Mt + TM::at(r, col)), hi = lds_read_tr4(B.Mt + TM::at(r + 16, col));
       return __builtin_bit_cast(frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
   };
