@@ -76,8 +76,8 @@ struct ChunkLayout {
   size_t bw;          // fp32 [nt_max][hv][64]: beta_t, zero past the chunk end (backward)
   size_t tib;         // T [nt_max][hv][2][64][64]: Tinv (columns in accumulator order), Tinv^T (backward)
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
-  size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta, dDelta
-  size_t dl16w;       // CT [T][hv][dv]: Delta in the compute type (16-bit types: the chunk outputs' P Delta)
+  size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta (fp32 data only), dDelta
+  size_t dl16w;       // CT [T][hv][dv]: Delta in the compute type (16-bit data: for the outputs and the gradients)
   size_t sink;        // SINK_ELEMS scratch floats: target of stores for padding rows
   size_t total_fwd, total_bwd;
 };
@@ -121,7 +121,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.dh = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.rw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
-  L.dlw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
+  L.dlw = off; off = align256(off + (es == 4 ? es * (size_t)T * s.hv * s.dv : 0));
   L.ddw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
   L.dl16w = off; off = align256(off + (es == 2 ? 2 * (size_t)T * s.hv * s.dv : 0));
   L.total_bwd = off;

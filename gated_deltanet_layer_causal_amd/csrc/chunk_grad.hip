@@ -44,7 +44,7 @@ template <typename T, int D> struct GradLds {
   static constexpr int LDP = CHUNK + 16 / (int)sizeof(T);     // padded 64-wide rows
   static constexpr int NKT = D / 16;                          // key tiles (phase-B waves per token group)
   T tO[TT::PIECES * TT::EPP];     // dO
-  T tDl[TT::PIECES * TT::EPP];    // Delta
+  T tDl[TT::PIECES * TT::EPP];    // Delta (16-bit data: fp16 values, converted where read)
   T tdR[TT::PIECES * TT::EPP];    // dR
   T tR[TT::PIECES * TT::EPP];     // R
   T YT[CHUNK][LDP];               // Y^T: row s, column u
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     float scale, const double* __restrict__ gcum, const float* __restrict__ bw,
     const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ Tib,
     const T* __restrict__ Ktb, const T* __restrict__ Qtb, const T* __restrict__ hst,
-    const T* __restrict__ dhst, const T* __restrict__ Rw, const T* __restrict__ Dlw,
+    const T* __restrict__ dhst, const T* __restrict__ Rw, const void* __restrict__ Dlw,
     const T* __restrict__ ddw, const T* __restrict__ dout, const T* __restrict__ dvo,
     int64_t lddv, T* __restrict__ dq, T* __restrict__ dk, int64_t lddq, int64_t lddk,
     float* __restrict__ dg, float* __restrict__ dbeta) {
@@ -158,6 +158,20 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   // token-tile operand: row r, step p
   auto tfr = [&](const T* tile, int r, int p) __attribute__((always_inline)) -> frag {
     return rdf(tile, TT::at(r, pcol(p)));
+  };
+  // the same from the Delta tile, which for 16-bit data holds the fp16 Delta
+  // of the saved-state pass (one rounding more to bf16 here)
+  auto dlfr = [&](int r, int p) __attribute__((always_inline)) -> frag {
+    if constexpr (sizeof(T) == 2) {
+      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+      const h8 x = __builtin_bit_cast(h8, tfr(sm.tDl, r, p));
+      frag y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = (bf16)(float)x[j];
+      return y;
+    } else {
+      return tfr(sm.tDl, r, p);
+    }
   };
 
   // ---- per workgroup: k_s . k_t at the phase-A positions (Tinv-chain
@@ -249,7 +263,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
     const int64_t base = t0 * HvD + (int64_t)h * D;
     copy_rows(sm.tO, dout + base, rowb, live);
-    copy_rows(sm.tDl, Dlw + base, rowb, live);
+    copy_rows(sm.tDl, reinterpret_cast<const T*>(Dlw) + base, rowb, live);
     copy_rows(sm.tdR, dvo + t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)), live);
   };
   auto copy_r = [&](int h, bool live) __attribute__((always_inline)) {
@@ -449,7 +463,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           dPt[st] = dPn[st] = zero4();
 #pragma unroll
           for (int p = 0; p < NSD; ++p) {
-            const frag da = tfr(sm.tDl, 16 * st + c16, p);
+            const frag da = dlfr(16 * st + c16, p);
             dPt[st] = MM::mma(da, ob[p], dPt[st]);
             dPn[st] = MM::mma(ob[p], da, dPn[st]);
           }
@@ -561,7 +575,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         for (int p = 0; p < NSD; ++p) {
           x1 = MM::mma(hA[p], tfr(sm.tO, t, p), x1);
           x2 = MM::mma(hA[p], tfr(sm.tdR, t, p), x2);
-          x3 = MM::mma(dhA[p], tfr(sm.tDl, t, p), x3);
+          x3 = MM::mma(dhA[p], dlfr(t, p), x3);
         }
 #pragma unroll
         for (int p = 0; p < NSC; ++p) {
@@ -707,7 +721,8 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
                        s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), (const float*)(ws + Ly.bw),
                        (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)(ws + Ly.tib),
                        (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb), (const T*)(ws + Ly.h),
-                       (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw), (const T*)(ws + Ly.dlw),
+                       (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw),
+                       sizeof(T) == 2 ? (const void*)(ws + Ly.dl16w) : (const void*)(ws + Ly.dlw),
                        (const T*)(ws + Ly.ddw), (const T*)dout, (const T*)dv, lddv, (T*)dq,
                        (T*)dk, lddq, lddk, dg, dbeta);
     return hipGetLastError();

@@ -60,7 +60,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     const typename Compute<T>::type* __restrict__ Ww, const typename Compute<T>::type* __restrict__ Ktw,
     const typename Compute<T>::type* __restrict__ Xw, const float* __restrict__ Gw,
     const float* __restrict__ Dw, const float* __restrict__ S0, float* __restrict__ S_final,
-    T* __restrict__ o, T* __restrict__ hst, T* __restrict__ Rw, T* __restrict__ Dlw,
+    T* __restrict__ o, T* __restrict__ hst, T* __restrict__ Rw,
     typename Compute<T>::type* __restrict__ Dl16w, int n_items) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
@@ -177,14 +177,14 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, S[kt]);
   };
-  // (K-rows form) The compute waves put the chunk-start state, R, Delta and
-  // Delta in the compute type into LDS rows of their own (paired words,
-  // ds_write2); a step later the mover wave of the same index stores them in
-  // 16-byte pieces, so no store sits on the recurrence.  Two sets of rows,
-  // by chunk parity.
+  // (K-rows form) The compute waves put the chunk-start state, R and Delta
+  // (Delta in the compute type, which the outputs and the gradients read)
+  // into LDS rows of their own (paired words, ds_write2); a step later the
+  // mover wave of the same index stores them in 16-byte pieces, so no store
+  // sits on the recurrence.  Two sets of rows, by chunk parity.
   typedef StageRows<T> SR;
-  constexpr int SRR = D + 3 * CHUNK;   // staged rows per compute wave
-  constexpr int SROW_R = D, SROW_DL = D + CHUNK, SROW_D16 = D + 2 * CHUNK;
+  constexpr int SRR = D + 2 * CHUNK;   // staged rows per compute wave
+  constexpr int SROW_R = D, SROW_D16 = D + CHUNK;
   __shared__ __align__(16) char stg[SB::KR ? 2 * NW * SRR * SR::SB : 16];
   auto stage_of = [&](int64_t c, int w) __attribute__((always_inline)) -> char* {
     return stg + (int)((((c - c_begin) & 1) * NW + w) * SRR * SR::SB);
@@ -196,12 +196,12 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) StageRows<E>::put(st, row0 + 16 * tt, ps, lane, x[tt]);
   };
-  // (movers) chunk cp's staged rows of compute wave `wave` to the state,
-  // R, Delta and Delta (compute type) buffers; token rows past the sequence
+  // (movers) chunk cp's staged rows of compute wave `wave` to the state, R
+  // and Delta (compute type) buffers; token rows past the sequence
   // end fall outside the buffers and are dropped.  With valid false every
   // store is still issued but dropped (an empty range), so each step issues
   // the same count.
-  constexpr int NFL = SR::stores(D) + 3 * SR::stores(CHUNK);
+  constexpr int NFL = SR::stores(D) + 2 * SR::stores(CHUNK);
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
     const char* st = stage_of(cp, wave);
     const int64_t ca = valid ? cp : c_begin;
@@ -213,7 +213,6 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     SR::flush_async(st, 0, D, buffer_of(hst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
               col, rowh, lane);
     SR::flush_async(st, SROW_R, CHUNK, buffer_of(Rw + tok, (uint32_t)Lp * rowb), col, rowb, lane);
-    SR::flush_async(st, SROW_DL, CHUNK, buffer_of(Dlw + tok, (uint32_t)Lp * rowb), col, rowb, lane);
     SR::flush_async(st, SROW_D16, CHUNK, buffer_of(Dl16w + tok, (uint32_t)Lp * rowb), col, rowb, lane);
   };
 
@@ -350,7 +349,6 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
       }
     }
     if constexpr (SB::KR) {
-      put_rows((T)0, stc, SROW_DL, Dl);
       put_rows((CT)0, stc, SROW_D16, Dl);
     }
 
@@ -517,7 +515,7 @@ static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, fl
                      (const CT*)(ws + Ly.ktw), (const CT*)(ws + Ly.q16w),
                      (const float*)(ws + Ly.gw), (const float*)(ws + Ly.dw), S0, S_final, (T*)o,
                      (T*)(ws + Ly.h), KR ? (T*)(ws + Ly.rw) : nullptr,
-                     KR ? (T*)(ws + Ly.dlw) : nullptr, KR ? (CT*)(ws + Ly.dl16w) : nullptr, n_items);
+                     KR ? (CT*)(ws + Ly.dl16w) : nullptr, n_items);
   return hipGetLastError();
 }
 
