@@ -35,3 +35,39 @@ def assert_close(name, got, ref, tol):
     assert np.all(np.isfinite(np.asarray(got))), f"{name}: non-finite values"
     assert e <= tol, f"{name}: max rel err {e:.3e} > {tol:.1e}"
     return e
+
+
+FLOWS = ("composite", "saved")
+
+
+def run_chunk(flow, sh, q, k, v, g, beta, scale, S0, cu, dout, dS_final, ws):
+    """The chunked rule forward and backward through the C ABI, in one of the
+    two flows: "composite" (gdn_chunk_fwd, then gdn_chunk_bwd, which
+    recomputes the states) or "saved" (the training flow: backward-mode
+    preparation, the state pass that saves the chunk states with the
+    chunk-parallel outputs, then the reverse pass and the chunk gradients on
+    that workspace).  Returns the device tensors o, S_final, dq, dk, dv, dg,
+    dbeta, dS0 (dq, dk, dv as views into one [T, C] gradient tensor)."""
+    from gated_deltanet_layer_causal_amd import capi as L
+    T, n = sh.total_tokens, sh.n_seq
+    hk, hv, d = sh.hk, sh.hv, sh.dk
+    tdt = q.dtype
+    Sf = torch.empty((n, hv, d, d), dtype=torch.float32, device=q.device)
+    o = torch.empty((T, hv, d), dtype=tdt, device=q.device)
+    dy = torch.empty((T, 2 * hk * d + hv * d), dtype=tdt, device=q.device)
+    dq, dk, dv = dy[:, : hk * d], dy[:, hk * d: 2 * hk * d], dy[:, 2 * hk * d:]
+    dg, db = torch.empty_like(g), torch.empty_like(beta)
+    dS0 = torch.empty_like(Sf)
+    if flow == "composite":
+        L.gdn_chunk_fwd(sh, q, k, v, g, beta, scale, S0, Sf, cu, o, ws)
+        L.gdn_chunk_bwd(sh, q, k, v, g, beta, scale, S0, cu, dout, dS_final, dq, dk, dv, dg, db,
+                        dS0, ws)
+    elif flow == "saved":
+        L.gdn_chunk_prepare_bwd(sh, q, k, g, beta, scale, cu, ws)
+        L.gdn_chunk_fwd_states_save(sh, q, k, v, scale, S0, Sf, cu, o, ws)
+        L.gdn_chunk_bwd_reverse(sh, q, k, scale, cu, dout, dS_final, dv, dS0, ws)
+        L.gdn_chunk_bwd_grads(sh, q, k, beta, scale, cu, dout, dv, dq, dk, dg, db, ws)
+    else:
+        raise ValueError(flow)
+    return {"o": o, "S_final": Sf, "dq": dq, "dk": dk, "dv": dv, "dg": dg, "dbeta": db,
+            "dS0": dS0}

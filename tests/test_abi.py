@@ -80,3 +80,58 @@ def test_null_and_misaligned_pointers_rejected():
     assert st == 4
     # norm: unsupported row length
     assert lib.gdn_gated_norm_fwd(10, 64, 0, a16, a16, a16, ctypes.c_float(1e-6), 0, a16, None) == 2
+
+
+def test_stale_library_is_refused(tmp_path):
+    """load() checks that the library was built from the sources in the tree."""
+    import shutil
+    from gated_deltanet_layer_causal_amd import build as B
+    so = tmp_path / "libgdn.so"
+    shutil.copy(L.LIB_PATH, so)
+    with pytest.raises(RuntimeError, match="not built from"):
+        L._check_built(str(so))          # no digest beside it
+    (tmp_path / "libgdn.so.sources").write_text("0" * 64 + "\n")
+    with pytest.raises(RuntimeError, match="not built from"):
+        L._check_built(str(so))          # digest of other sources
+    (tmp_path / "libgdn.so.sources").write_text(B.source_digest() + "\n")
+    L._check_built(str(so))
+    with pytest.raises(RuntimeError, match="missing"):
+        L._check_built(str(tmp_path / "nothing.so"))
+
+
+def test_wrappers_check_tensors_before_the_call():
+    """Wrong dtype, size or layout is a Python error, raised before the
+    library sees a pointer; a correct host tensor is refused as not on the
+    device.  (Each case breaks the first tensor the wrapper checks.)"""
+    import torch
+    sh = _shape(total_tokens=100, hk=1, hv=2, d=32, dtype=L.GDN_FP32)
+    T, hv, d = 100, 2, 32
+    g = torch.zeros(T * hv)
+    Al = torch.zeros(hv)
+    a = torch.zeros(T, hv)
+    with pytest.raises(TypeError):
+        L.gdn_gate_fwd(sh, a.double(), a, Al, Al, g, g)
+    with pytest.raises(ValueError, match="elements"):
+        L.gdn_gate_fwd(sh, a[:-1], a, Al, Al, g, g)
+    with pytest.raises(ValueError, match="must be contiguous"):
+        L.gdn_gate_fwd(sh, a.t(), a, Al, Al, g, g)
+    with pytest.raises(ValueError, match="device"):
+        L.gdn_gate_fwd(sh, a, a, Al, Al, g, g)
+    y = torch.zeros(T, 4 * 32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    cu = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="contiguous rows"):
+        L.gdn_chunk_prepare(sh, y[:, ::4], y[:, 32:64], g, g, 0.1, cu, ws)
+    with pytest.raises(ValueError, match="matrix"):
+        L.gdn_chunk_fwd(sh, y[:-1, :32], y[:, 32:64], y[:, 64:], g, g, 0.1, None, None, cu,
+                        torch.zeros(T, hv, d), ws)
+    with pytest.raises(TypeError):
+        L.gdn_chunk_fwd(sh, y[:, :32].double(), y[:, 32:64], y[:, 64:], g, g, 0.1, None, None, cu,
+                        torch.zeros(T, hv, d), ws)
+    o = torch.zeros(10, 32)
+    with pytest.raises(ValueError, match="elements"):
+        L.gdn_gated_norm_fwd(o, o[:-1], torch.zeros(32), o)
+    with pytest.raises(ValueError, match="elements"):
+        L.gdn_gated_norm_fwd(o, o, torch.zeros(31), o)
+    with pytest.raises(ValueError, match="device"):
+        L.gdn_gated_norm_fwd(o, o, torch.zeros(32), o)

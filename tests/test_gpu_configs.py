@@ -23,7 +23,8 @@ import torch
 import oracle
 from gated_deltanet_layer_causal_amd import capi as L
 from gated_deltanet_layer_causal_amd import inputs as gi
-from tests.gpu_util import DEV, FWD_TOL_BF16, GRAD_TOL_BF16, assert_close, dev, host
+from tests.gpu_util import (DEV, FLOWS, FWD_TOL_BF16, GRAD_TOL_BF16, assert_close, dev, host,
+                             run_chunk)
 
 pytestmark = pytest.mark.gpu
 
@@ -158,39 +159,62 @@ def test_gate_and_norm_full_size(case):
 
 
 # ---------------------------------------------------------------------- chunked delta rule
-def test_chunk_full_size_windows(case):
-    w, inp = case
-    cu, T, d, hk, hv = inp["cu_seqlens"], inp["T"], w.d, w.hk, w.hv
-    scale = d ** -0.5
-    print(f"[config {w.name}] oracle conv + gate for chunk inputs", flush=True)
-    y = gi.round_bf16(oracle.conv_fwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d).astype(np.float32))
-    g, beta = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
-    g, beta = g.astype(np.float32), beta.astype(np.float32)
-    rng = np.random.default_rng(13)
-    dout = gi.round_bf16(rng.standard_normal((T, hv, d), dtype=np.float32))
-    S0, dSf = inp["S0"], inp["dS_T"]
+_Y_CACHE = {}
 
+
+def _chunk_inputs(w, inp):
+    """bf16 conv output y (oracle conv, rounded to bf16) for the workload;
+    cached per workload (several tests share it)."""
+    if w.name not in _Y_CACHE:
+        _Y_CACHE.clear()
+        print(f"[config {w.name}] oracle conv for chunk inputs", flush=True)
+        _Y_CACHE[w.name] = gi.round_bf16(
+            oracle.conv_fwd(inp["x"], inp["w_conv"], inp["cu_seqlens"], 2 * w.hk * w.d, w.d)
+            .astype(np.float32))
+    return _Y_CACHE[w.name]
+
+
+def _gpu_flows(w, inp, y, g, beta, dout, S0, dSf):
+    """Run both chunk flows on the full workload; host copies of their outputs."""
+    cu, T, d, hk, hv = inp["cu_seqlens"], inp["T"], w.d, w.hk, w.hv
     sh = L.make_shape(inp["N"], T, hk, hv, d, L.GDN_BF16)
     yt = dev(y, torch.bfloat16)
     qt, kt, vt = yt[:, : hk * d], yt[:, hk * d: 2 * hk * d], yt[:, 2 * hk * d:]
     gt, bt = dev(g), dev(beta)
     cut = torch.from_numpy(cu).to(DEV)
     S0t = dev(S0) if S0 is not None else None
-    Sf = torch.empty((inp["N"], hv, d, d), dtype=torch.float32, device=DEV)
-    o = torch.empty((T, hv, d), dtype=torch.bfloat16, device=DEV)
+    dSft = dev(dSf) if dSf is not None else None
+    dot = dev(dout, torch.bfloat16)
     ws = torch.empty(L.gdn_chunk_bwd_workspace(sh), dtype=torch.uint8, device=DEV)
-    L.gdn_chunk_fwd(sh, qt, kt, vt, gt, bt, scale, S0t, Sf, cut, o, ws)
-    dyc = torch.empty_like(yt)
-    dq, dk, dv = dyc[:, : hk * d], dyc[:, hk * d: 2 * hk * d], dyc[:, 2 * hk * d:]
-    dg, db = torch.empty_like(gt), torch.empty_like(bt)
-    dS0 = torch.empty_like(Sf)
-    L.gdn_chunk_bwd(sh, qt, kt, vt, gt, bt, scale, S0t, cut, dev(dout, torch.bfloat16),
-                    dev(dSf) if dSf is not None else None, dq, dk, dv, dg, db, dS0, ws)
-    torch.cuda.synchronize()
+    res = {}
+    for flow in FLOWS:
+        print(f"[config {w.name}] GPU chunk flow {flow}", flush=True)
+        r = run_chunk(flow, sh, qt, kt, vt, gt, bt, d ** -0.5, S0t, cut, dot, dSft, ws)
+        torch.cuda.synchronize()
+        res[flow] = {"o": host(r["o"]), "S_final": host(r["S_final"]),
+                     "dq": host(r["dq"]).reshape(T, hk, d), "dk": host(r["dk"]).reshape(T, hk, d),
+                     "dv": host(r["dv"]).reshape(T, hv, d), "dg": host(r["dg"]),
+                     "dbeta": host(r["dbeta"]), "dS0": host(r["dS0"])}
+        del r
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def test_chunk_full_size_windows(case):
+    """Both chunk flows (the composite calls, and the saved-state phases the
+    bench times) at the workload's full size, on sampled heads and windows."""
+    w, inp = case
+    cu, T, d, hk, hv = inp["cu_seqlens"], inp["T"], w.d, w.hk, w.hv
+    scale = d ** -0.5
+    y = _chunk_inputs(w, inp)
+    g, beta = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    g, beta = g.astype(np.float32), beta.astype(np.float32)
+    rng = np.random.default_rng(13)
+    dout = gi.round_bf16(rng.standard_normal((T, hv, d), dtype=np.float32))
+    S0, dSf = inp["S0"], inp["dS_T"]
+    res = _gpu_flows(w, inp, y, g, beta, dout, S0, dSf)
     q, k, v = gi.split_qkv(y, hk, hv, d)
-    o_h, Sf_h = host(o), host(Sf)
-    dq_h, dk_h = host(dq).reshape(T, hk, d), host(dk).reshape(T, hk, d)
-    dv_h, dg_h, db_h, dS0_h = host(dv).reshape(T, hv, d), host(dg), host(db), host(dS0)
     n_checked = 0
     for kh in _sample_kheads(w):
         vh = _vheads(w, kh)
@@ -206,10 +230,6 @@ def test_chunk_full_size_windows(case):
             assert bnd < DECAY_BOUND, f"decay margin too weak ({bnd:.2e})"
             o_r, Sf_r = oracle.delta_fwd(q[a:b, [kh]], k[a:b, [kh]], v[a:b, vh], g[a:b, vh],
                                          beta[a:b, vh], [0, b - a], scale, s0)
-            tag = f"{w.name} kh={kh} [{a},{b})"
-            assert_close(f"o {tag}", o_h[f0:b, vh], o_r[f0 - a:], FWD_TOL_BF16)
-            if is_end:
-                assert_close(f"S_final {tag}", Sf_h[n, vh], Sf_r[0], FWD_TOL_BF16)
             # backward: tokens [f0, b - MARGIN) unless the window ends the sequence
             g1 = b if is_end else b - MARGIN
             bnd = 0.0 if is_end else _decay_factor(g[:, vh], g1, b)
@@ -217,16 +237,66 @@ def test_chunk_full_size_windows(case):
             ref = oracle.delta_bwd(q[a:b, [kh]], k[a:b, [kh]], v[a:b, vh], g[a:b, vh],
                                    beta[a:b, vh], [0, b - a], scale, dout[a:b, vh], s0, dsf)
             sl = slice(f0 - a, g1 - a)
-            assert_close(f"dq {tag}", dq_h[f0:g1, kh], ref[0][sl, 0], GRAD_TOL_BF16)
-            assert_close(f"dk {tag}", dk_h[f0:g1, kh], ref[1][sl, 0], GRAD_TOL_BF16)
-            assert_close(f"dv {tag}", dv_h[f0:g1, vh], ref[2][sl], GRAD_TOL_BF16)
-            assert_close(f"dg {tag}", dg_h[f0:g1, vh], ref[3][sl], GRAD_TOL_BF16)
-            assert_close(f"dbeta {tag}", db_h[f0:g1, vh], ref[4][sl], GRAD_TOL_BF16)
-            if seq_start:
-                # dS0 gets contributions from every later token, damped by the
-                # gates: the window end must be far enough for the cut to vanish
-                bnd = 0.0 if is_end else _decay_factor(g[:, vh], a, b)
-                if bnd < DECAY_BOUND:
-                    assert_close(f"dS0 {tag}", dS0_h[n, vh], ref[5][0], GRAD_TOL_BF16)
+            for flow, r in res.items():
+                tag = f"{w.name} {flow} kh={kh} [{a},{b})"
+                errs = {
+                    "o": assert_close(f"o {tag}", r["o"][f0:b, vh], o_r[f0 - a:], FWD_TOL_BF16),
+                    "dq": assert_close(f"dq {tag}", r["dq"][f0:g1, kh], ref[0][sl, 0], GRAD_TOL_BF16),
+                    "dk": assert_close(f"dk {tag}", r["dk"][f0:g1, kh], ref[1][sl, 0], GRAD_TOL_BF16),
+                    "dv": assert_close(f"dv {tag}", r["dv"][f0:g1, vh], ref[2][sl], GRAD_TOL_BF16),
+                    "dg": assert_close(f"dg {tag}", r["dg"][f0:g1, vh], ref[3][sl], GRAD_TOL_BF16),
+                    "dbeta": assert_close(f"dbeta {tag}", r["dbeta"][f0:g1, vh], ref[4][sl],
+                                          GRAD_TOL_BF16)}
+                if is_end:
+                    errs["S_final"] = assert_close(f"S_final {tag}", r["S_final"][n, vh], Sf_r[0],
+                                                   FWD_TOL_BF16)
+                if seq_start:
+                    # dS0 gets contributions from every later token, damped by
+                    # the gates: the window end must be far enough for the cut
+                    # to vanish
+                    bnd = 0.0 if is_end else _decay_factor(g[:, vh], a, b)
+                    if bnd < DECAY_BOUND:
+                        errs["dS0"] = assert_close(f"dS0 {tag}", r["dS0"][n, vh], ref[5][0],
+                                                   GRAD_TOL_BF16)
+                print(tag, " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
             n_checked += 1
     assert n_checked >= 2
+
+
+def test_chunk_live_state_full_length():
+    """Mild decay (A ~ U(0.01, 0.1)) at the 64k-token, 16/48-head shape, with
+    an initial state and the final state's gradient: the state stays alive
+    from chunk to chunk, so every chunk step's error carries into the next.
+    Both flows run all heads; the first key head with its three value heads
+    is compared with the oracle over all 65536 tokens (heads are
+    independent, so the head-sliced oracle run is exact)."""
+    base = gi.WORKLOADS["flash64k"]
+    w = gi.Workload("flash64k_live", base.T, base.hk, base.hv, base.d, "bf16", init_state=True,
+                    final_state=True, seed=base.seed)
+    inp = gi.make_inputs(w, A_range=(0.01, 0.1))
+    T, d, hk, hv = inp["T"], w.d, w.hk, w.hv
+    cu = inp["cu_seqlens"]
+    y = _chunk_inputs(base, inp)     # same x and conv weights as the flash64k workload
+    g, beta = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    g, beta = g.astype(np.float32), beta.astype(np.float32)
+    # the state reaches across chunks: decay over one chunk stays far from 0
+    assert _decay_factor(g, 0, 64) > 1e-3
+    rng = np.random.default_rng(14)
+    dout = gi.round_bf16(rng.standard_normal((T, hv, d), dtype=np.float32))
+    res = _gpu_flows(w, inp, y, g, beta, dout, inp["S0"], inp["dS_T"])
+    q, k, v = gi.split_qkv(y, hk, hv, d)
+    kh, vh = 0, _vheads(w, 0)
+    print("[live] oracle forward and backward, one key head, 65536 tokens", flush=True)
+    o_r, Sf_r = oracle.delta_fwd(q[:, [kh]], k[:, [kh]], v[:, vh], g[:, vh], beta[:, vh], cu,
+                                 d ** -0.5, inp["S0"][:, vh])
+    ref = oracle.delta_bwd(q[:, [kh]], k[:, [kh]], v[:, vh], g[:, vh], beta[:, vh], cu, d ** -0.5,
+                           dout[:, vh], inp["S0"][:, vh], inp["dS_T"][:, vh])
+    for flow, r in res.items():
+        tag = f"live {flow}"
+        errs = {"o": assert_close(f"o {tag}", r["o"][:, vh], o_r, FWD_TOL_BF16),
+                "S_final": assert_close(f"S_final {tag}", r["S_final"][:, vh], Sf_r, FWD_TOL_BF16)}
+        for i, nm in enumerate(("dq", "dk", "dv", "dg", "dbeta", "dS0")):
+            got = r[nm]
+            got = got[:, [kh]] if nm in ("dq", "dk") else got[:, vh]
+            errs[nm] = assert_close(f"{nm} {tag}", got, ref[i], GRAD_TOL_BF16)
+        print(tag, " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)

@@ -192,3 +192,72 @@ def test_chunk_fwd_bwd(name):
     print(name, " ".join(f"{k}={v:.2e}" for k, v in report.items()))
     for nm, a, r, tol in checks:
         assert_close(nm, a, r, tol)
+
+
+# ------------------------------------------------------------------ chunk table (integer)
+@pytest.mark.parametrize("lens", [[70, 0, 64, 0, 5, 1, 128, 129], [3, 0], [1], [0, 0, 3],
+                                  [64] * 7 + [65]],
+                         ids=["mixed", "trailing_empty", "one", "leading_empty", "exact_chunks"])
+def test_chunk_table_exact(lens):
+    """The chunk table that the preparation builds from cu_seqlens at the head
+    of the workspace: int32 [n_seq + 1], entry n = number of 64-token chunks
+    of sequences 0 .. n-1.  Bit-exact against the plain count."""
+    hk, hv, d = 1, 2, 32
+    cu = gi.cu_from_lengths(lens)
+    T, N = int(cu[-1]), len(lens)
+    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16)
+    y = torch.zeros((T, 4 * d), dtype=torch.bfloat16, device=DEV)
+    g = torch.zeros((T, hv), dtype=torch.float32, device=DEV)
+    ws = torch.full((L.gdn_chunk_fwd_workspace(sh),), 0x5A, dtype=torch.uint8, device=DEV)
+    L.gdn_chunk_prepare(sh, y[:, :d], y[:, d:2 * d], g, g, 1.0, torch.from_numpy(cu).to(DEV), ws)
+    torch.cuda.synchronize()
+    got = ws[: 4 * (N + 1)].cpu().view(torch.int32).numpy()
+    want = np.zeros(N + 1, dtype=np.int32)
+    for n, ln in enumerate(lens):
+        want[n + 1] = want[n] + (ln + 63) // 64
+    np.testing.assert_array_equal(got, want)
+
+
+# ------------------------------------------------------------------ fp16 operand range
+@pytest.mark.parametrize("flow", ["composite", "saved"])
+def test_chunk_large_values_and_state(flow):
+    """The forward passes of bf16 data round v, the running state and the
+    delta-rule writes to fp16 for the MFMA (max 65504).  Values and initial
+    state ~1e3 times the workloads' (|v| up to ~4e3, S0 ~ N(0, 1e3)), the
+    range the header documents, still match the oracle."""
+    from tests.gpu_util import run_chunk
+    hk, hv, d, lens = 2, 4, 128, [150, 64, 90]
+    w = gi.Workload("big", sum(lens), hk, hv, d, "bf16", seq="varlen", init_state=True,
+                    final_state=True, seed=21)
+    inp = gi.make_inputs(w, seqlens=lens, A_range=(0.01, 0.1))
+    cu, T = inp["cu_seqlens"], inp["T"]
+    y = gi.round_bf16(oracle.conv_fwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d))
+    y[:, 2 * hk * d:] = gi.round_bf16(y[:, 2 * hk * d:] * 1000.0)
+    g, beta = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    g, beta = g.astype(np.float32), beta.astype(np.float32)
+    S0 = (inp["S0"] * 1e4).astype(np.float32)          # N(0, 0.1) -> N(0, 1e3)
+    rng = np.random.default_rng(22)
+    dout = gi.round_bf16(rng.standard_normal((T, hv, d), dtype=np.float32))
+    dSf = inp["dS_T"]
+    q, k, v = gi.split_qkv(y, hk, hv, d)
+    scale = d ** -0.5
+    o_ref, Sf_ref = oracle.delta_fwd(q, k, v, g, beta, cu, scale, S0)
+    ref = oracle.delta_bwd(q, k, v, g, beta, cu, scale, dout, S0, dSf)
+    assert np.max(np.abs(Sf_ref)) > 1e3 and np.max(np.abs(v)) > 2e3
+    sh = L.make_shape(inp["N"], T, hk, hv, d, L.GDN_BF16)
+    yt = dev(y, torch.bfloat16)
+    ws = torch.empty(L.gdn_chunk_bwd_workspace(sh), dtype=torch.uint8, device=DEV)
+    r = run_chunk(flow, sh, yt[:, : hk * d], yt[:, hk * d: 2 * hk * d], yt[:, 2 * hk * d:], dev(g),
+                  dev(beta), scale, dev(S0), torch.from_numpy(cu).to(DEV),
+                  dev(dout, torch.bfloat16), dev(dSf), ws)
+    torch.cuda.synchronize()
+    got = {"o": host(r["o"]), "S_final": host(r["S_final"]),
+           "dq": host(r["dq"]).reshape(T, hk, d), "dk": host(r["dk"]).reshape(T, hk, d),
+           "dv": host(r["dv"]).reshape(T, hv, d), "dg": host(r["dg"]), "dbeta": host(r["dbeta"]),
+           "dS0": host(r["dS0"])}
+    refs = {"o": o_ref, "S_final": Sf_ref, "dq": ref[0], "dk": ref[1], "dv": ref[2], "dg": ref[3],
+            "dbeta": ref[4], "dS0": ref[5]}
+    errs = {k: rel_err(got[k], refs[k]) for k in refs}
+    print(flow, " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    for k in refs:
+        assert_close(k, got[k], refs[k], FWD_TOL_BF16 if k in ("o", "S_final") else GRAD_TOL_BF16)
