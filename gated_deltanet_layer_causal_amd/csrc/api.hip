@@ -105,6 +105,20 @@ gdn_status gdn_conv_bwd(const gdn_shape* s, const void* x, int64_t ldx, const fl
                                   dw, (float*)ws, (hipStream_t)stream));
 }
 
+gdn_status gdn_conv_bwd_noalloc(const gdn_shape* s, const void* x, int64_t ldx, const float* w,
+                                const int32_t* cu, int l2norm_qk, float l2_eps, const void* dy,
+                                int64_t lddy, void* dx, int64_t lddx, float* dw, void* stream) {
+  GDN_TRY(check_shape(s));
+  GDN_TRY(check_ptrs({x, w, cu, dy, dx, dw}));
+  GDN_TRY(check_ld(ldx, channels(s)));
+  GDN_TRY(check_ld(lddy, channels(s)));
+  GDN_TRY(check_ld(lddx, channels(s)));
+  if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (gdn_conv_bwd_workspace(s) > CONV_BWD_NOALLOC_MAX_BYTES) return GDN_ERR_WORKSPACE;
+  return launched(launch_conv_bwd_noalloc(*s, x, ldx, w, cu, l2norm_qk != 0, l2_eps, dy, lddy,
+                                          dx, lddx, dw, (hipStream_t)stream));
+}
+
 gdn_status gdn_gate_fwd(const gdn_shape* s, const void* a, const void* b, const float* A_log,
                         const float* dt_bias, float* g, float* beta, void* stream) {
   GDN_TRY(check_shape(s));

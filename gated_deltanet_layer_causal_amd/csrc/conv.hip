@@ -14,6 +14,8 @@
 // waves (four runs) share a workgroup so the backward's dw partial sums are
 // combined in LDS before they go to memory; a second kernel adds the
 // per-workgroup partials in a fixed order.
+#include <mutex>
+
 #include "chunk_stream.h"
 
 namespace gdn {
@@ -387,6 +389,50 @@ static hipError_t conv_bwd_t(const gdn_shape& s, const void* x, int64_t ldx, con
                        s.n_seq, nT, tt, C, n_l2, eps, (const T*)dy, lddy, (T*)dx, lddx, partials);
   }
   return launch_reduce_partials(partials, np, (int64_t)C * 4, dw, st);
+}
+
+// ---- the conv backward without a workspace argument -------------------------
+// Its per-block dw partials go to `scratch`, a device array of this module
+// (each GPU holds its own copy for the life of the process).  In host code
+// the array's name stands for a host-side shadow, not a device address: the
+// device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and only that pointer is handed to the kernels.  The
+// backward kernel writes every partial that the reduction reads, so nothing
+// needs clearing between calls.
+static __device__ __align__(256) float scratch[CONV_BWD_NOALLOC_MAX_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_dev[kMaxDevices] = {};
+
+// This device's copy of `scratch`, looked up on the first call on the device.
+hipError_t scratch_of_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_conv_bwd_noalloc(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
+                                   const int32_t* cu, int l2, float eps, const void* dy,
+                                   int64_t lddy, void* dx, int64_t lddx, float* dw,
+                                   hipStream_t st) {
+  float* partials = nullptr;
+  const hipError_t e = scratch_of_current_device(&partials);
+  if (e != hipSuccess) return e;
+  return launch_conv_bwd(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw, partials, st);
 }
 
 hipError_t launch_conv_fwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,

@@ -41,6 +41,14 @@ hipError_t launch_conv_bwd(const gdn_shape& s, const void* x, int64_t ldx, const
                            const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
                            void* dx, int64_t lddx, float* dw, float* partials, hipStream_t st);
 
+constexpr size_t CONV_BWD_NOALLOC_MAX_BYTES = GDN_CONV_BWD_NOALLOC_MAX_BYTES;
+// the conv backward into the library's own scratch (no workspace argument);
+// partials of at most CONV_BWD_NOALLOC_MAX_BYTES
+hipError_t launch_conv_bwd_noalloc(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
+                                   const int32_t* cu, int l2, float eps, const void* dy,
+                                   int64_t lddy, void* dx, int64_t lddx, float* dw,
+                                   hipStream_t st);
+
 constexpr int GATE_TB = 64;      // tokens per gate-backward block
 inline int64_t gate_partials(int64_t T) { return (T + GATE_TB - 1) / GATE_TB; }
 hipError_t launch_gate_fwd(const gdn_shape& s, const void* a, const void* b, const float* A_log,

@@ -91,6 +91,26 @@ gdn_status gdn_conv_bwd(const gdn_shape* shape, const void* x, int64_t ldx, cons
                         size_t ws_bytes, void* stream);
 size_t gdn_conv_bwd_workspace(const gdn_shape* shape);
 
+/* gdn_conv_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as gdn_conv_bwd, without the workspace: its
+ * scratch (the per-block dw partial sums) is a device array of the library,
+ * GDN_CONV_BWD_NOALLOC_MAX_BYTES on every GPU the library runs on, held
+ * until the process ends.  This entry point calls no hipMalloc or hipFree.
+ * Shapes that need more scratch than that (gdn_conv_bwd_workspace(shape) >
+ * GDN_CONV_BWD_NOALLOC_MAX_BYTES, e.g. more than 131072 tokens at 10240
+ * channels) return GDN_ERR_WORKSPACE before anything is launched.  The
+ * array of the current device is used (the stream must belong to it); all
+ * calls on one GPU share it, so calls that overlap in time on one GPU
+ * (several streams or host threads) race and must be serialised by the
+ * caller.  Unlike the rest of the library this entry point keeps state: the
+ * device address of each GPU's array, looked up on its first call there. */
+#define GDN_CONV_BWD_NOALLOC_MAX_BYTES (32u << 20)
+gdn_status gdn_conv_bwd_noalloc(const gdn_shape* shape, const void* x, int64_t ldx,
+                                const float* w, const int32_t* cu_seqlens, int l2norm_qk,
+                                float l2_eps, const void* dy, int64_t lddy, void* dx,
+                                int64_t lddx, float* dw, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Gate (Megatron page, review comment: A_log stores log A and the forward
  * uses exp(A_log)):  g = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h]),

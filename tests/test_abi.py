@@ -135,3 +135,25 @@ def test_wrappers_check_tensors_before_the_call():
         L.gdn_gated_norm_fwd(o, o, torch.zeros(31), o)
     with pytest.raises(ValueError, match="device"):
         L.gdn_gated_norm_fwd(o, o, torch.zeros(32), o)
+
+
+def test_conv_bwd_noalloc_refuses_shapes_beyond_its_scratch():
+    """The workspace-free conv backward checks its fixed scratch size on the
+    host, before any device call (fake pointers are never dereferenced)."""
+    import re as _re
+    hdr = open(os.path.join(ROOT, "include", "libgdn.h")).read()
+    assert int(eval(_re.search(r"#define GDN_CONV_BWD_NOALLOC_MAX_BYTES \((.*?)\)", hdr).group(1)
+                    .replace("u", ""))) == L.CONV_BWD_NOALLOC_MAX_BYTES
+    lib = L.load()
+    a16 = ctypes.c_void_p(256)
+    ok = _shape(total_tokens=131072, hk=16, hv=48)
+    assert L.gdn_conv_bwd_workspace(ok) <= L.CONV_BWD_NOALLOC_MAX_BYTES
+    big = _shape(total_tokens=262144, hk=16, hv=48)
+    assert L.gdn_conv_bwd_workspace(big) > L.CONV_BWD_NOALLOC_MAX_BYTES
+    C = 2 * 16 * 128 + 48 * 128
+    st = lib.gdn_conv_bwd_noalloc(ctypes.byref(big), a16, C, a16, a16, 1, ctypes.c_float(1e-6), a16,
+                                  C, a16, C, a16, None)
+    assert st == 4          # GDN_ERR_WORKSPACE
+    st = lib.gdn_conv_bwd_noalloc(ctypes.byref(ok), None, C, a16, a16, 1, ctypes.c_float(1e-6), a16,
+                                  C, a16, C, a16, None)
+    assert st == 1          # null pointer: invalid argument
