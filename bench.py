@@ -149,6 +149,9 @@ def parse():
     p.add_argument("--seed", type=int, default=1005)
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--seg-chunks", type=int, default=0,
+                   help="segment length (chunks) of the segment-parallel state scan: 0 lets the "
+                        "library decide, < 0 keeps one sequential pass per sequence")
     p.add_argument("--proj-hidden", type=int, default=None,
                    help="hidden size of the layer with its in/out projections, timed beside the "
                         "core (0: skip; default: 2560 for the 16 k / 48 v-head shapes, the "
@@ -312,7 +315,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=dt), device=dev)
+    core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=dt, seg_chunks=args.seg_chunks),
+                   device=dev)
     inp = make_gpu_inputs(w, args.seed, dev)
     args_f = (inp["x"], inp["w_conv"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], inp["z"],
               inp["w_norm"], inp["cu_seqlens"])

@@ -39,7 +39,7 @@ EXPORTS = (
 class Shape(ctypes.Structure):
     _fields_ = [("n_seq", c_int32), ("total_tokens", c_int64), ("hk", c_int32), ("hv", c_int32),
                 ("dk", c_int32), ("dv", c_int32), ("conv_k", c_int32), ("chunk", c_int32),
-                ("dtype", c_int)]
+                ("dtype", c_int), ("seg_chunks", c_int32)]
 
 
 class GDNError(RuntimeError):
@@ -137,9 +137,11 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def make_shape(n_seq, total_tokens, hk, hv, d, dtype) -> Shape:
+def make_shape(n_seq, total_tokens, hk, hv, d, dtype, seg_chunks=0) -> Shape:
+    """seg_chunks: segment length of the segment-parallel state scan (0: the
+    library decides, > 0: forced, < 0: one sequential pass per sequence)."""
     dt = dtype if isinstance(dtype, int) else (GDN_BF16 if dtype == torch.bfloat16 else GDN_FP32)
-    return Shape(n_seq, total_tokens, hk, hv, d, d, 4, 64, dt)
+    return Shape(n_seq, total_tokens, hk, hv, d, d, 4, 64, dt, seg_chunks)
 
 
 def _ld(t):

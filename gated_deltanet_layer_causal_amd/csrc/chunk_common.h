@@ -59,10 +59,49 @@ template <typename CT> __device__ __forceinline__ int acc_piece_col(int p, int j
 template <typename T> __device__ __forceinline__ float dexp(double x) { return __expf((float)x); }
 template <> __device__ __forceinline__ float dexp<float>(double x) { return (float)exp(x); }
 
+// Segment length (in chunks) of the segment-parallel state scan, or 0 for
+// one sequential pass per sequence.  The sequential passes run one chain
+// per (sequence, value head, block of 32 value rows), one workgroup per CU;
+// when there are too few chains to fill the chip, each sequence is split
+// into segments that run in parallel: a pass from a zero state per segment
+// that also carries identity rows (giving the segment's end state B_s and its
+// transition Phi_s), a short sequential combine S_{s+1} = S_s Phi_s + B_s,
+// then the ordinary pass per segment from its true start state.  With ns
+// segments and at most SEG_TARGET_CHAINS chains per pass (measured: 224
+// one-per-CU workgroups run in one round on the 256 CUs, 256 take two),
+// the first pass (twice the chains) takes two rounds and the last one, so
+// the chain costs 3 / ns of the unsplit pass: the scan is used when ns >= 4.
+// shape.seg_chunks > 0 forces a segment length, < 0 forbids splitting.
+constexpr int SEG_TARGET_CHAINS = 224;
+constexpr int SEG_MIN_SEGMENTS = 4;
+constexpr int SEG_MIN_LEN = 8;
+inline int64_t seg_len(const gdn_shape& s) {
+  if (s.seg_chunks > 0) return s.seg_chunks;
+  if (s.seg_chunks < 0 || s.total_tokens == 0) return 0;
+  const int64_t chains = (int64_t)s.n_seq * s.hv * (s.dk / 32);
+  const int64_t nseg = SEG_TARGET_CHAINS / chains;
+  if (nseg < SEG_MIN_SEGMENTS) return 0;
+  const int64_t nt = s.total_tokens / CHUNK + s.n_seq;
+  const int64_t per_seq = (nt + s.n_seq - 1) / s.n_seq;
+  int64_t L = (per_seq + nseg - 1) / nseg;
+  if (L < SEG_MIN_LEN) L = SEG_MIN_LEN;
+  return L >= per_seq ? 0 : L;
+}
+
 // Workspace layout (byte offsets; every region 256-byte aligned).
 struct ChunkLayout {
   int64_t nt_max;     // upper bound on the number of chunks: T/64 + n_seq
+  int64_t seg;        // segment length in chunks (0: one span per sequence)
+  int64_t nspan_max;  // upper bound on the number of spans (segments)
   size_t seq_off;     // int32 [n_seq + 1]: first chunk of each sequence; [n_seq] = #chunks
+  size_t spans;       // int32 [nspan_max][4]: span = (first chunk, end chunk, token of its
+                      // first chunk, end token of its sequence) -- the unit of a sequential pass
+  size_t segb;        // int32 [n_seq + 1]: first span of each sequence; [n_seq] = #spans
+  size_t sumf;        // fp32 [nspan_max][hv][2 dv][dk]: a span's end state from zero (rows
+                      // < dv) and its transition Phi (rows >= dv) (segmented scan)
+  size_t sst;         // fp32 [nspan_max][hv][dv][dk]: start state of each span (segmented)
+  size_t sumr;        // fp32 [nspan_max][hv][dv][dk]: reverse pass from zero: dS at a span's start
+  size_t dse;         // fp32 [nspan_max][hv][dv][dk]: dS at each span's end (segmented)
   size_t gcum;        // fp64 [nt_max][hv][64]: in-chunk cumulative gate (flat past the chunk end)
   size_t mw, pw;      // CT [nt_max][hv][64][64]: M = Tinv diag(beta), P (accumulator column order)
   size_t ww;          // CT [nt_max][hv][64][dk]: W = M diag(Gam) K
@@ -99,8 +138,17 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   const size_t es = s.dtype == GDN_BF16 ? 2 : 4;
   const int64_t T = s.total_tokens;
   L.nt_max = T / CHUNK + s.n_seq;
+  L.seg = seg_len(s);
+  L.nspan_max = L.seg > 0 ? L.nt_max / L.seg + s.n_seq + 1 : s.n_seq;
+  const size_t st_bytes = L.seg > 0 ? sizeof(float) * (size_t)L.nspan_max * s.hv * s.dk * s.dv : 0;
   size_t off = 0;
   L.seq_off = off; off = align256(off + sizeof(int32_t) * (size_t)(s.n_seq + 1));
+  L.spans = off; off = align256(off + sizeof(int32_t) * 4 * (size_t)L.nspan_max);
+  L.segb = off; off = align256(off + sizeof(int32_t) * (size_t)(s.n_seq + 1));
+  L.sumf = off; off = align256(off + 2 * st_bytes);
+  L.sst = off; off = align256(off + st_bytes);
+  L.sumr = off; off = align256(off + st_bytes);
+  L.dse = off; off = align256(off + st_bytes);
   L.sink = off; off = align256(off + sizeof(float) * SINK_ELEMS);
   L.gcum = off; off = align256(off + sizeof(double) * (size_t)L.nt_max * s.hv * CHUNK);
   L.mw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
@@ -127,6 +175,13 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.total_bwd = off;
   return L;
 }
+
+// The combine of the segmented scan (chunk_scan.hip): forward (rev false)
+// from Sin = S0 (nullable) into the span start states and Sout = S_final
+// (nullable); reverse from Sin = dS_final into the span end gradients and
+// Sout = dS0.
+hipError_t launch_span_combine(const gdn_shape& s, const ChunkLayout& Ly, char* ws, bool rev,
+                               const float* Sin, float* Sout, hipStream_t st);
 
 // Instantiation selector for the chunk kernels: bf16 storage at head dim 32
 // or 128, fp32 storage at head dim 32 (the only combinations validated).

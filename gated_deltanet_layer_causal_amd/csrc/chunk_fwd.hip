@@ -4,35 +4,60 @@
 
 namespace gdn {
 
-// seq_off[n] = number of 64-token chunks of sequences 0..n-1 (one block scan).
+// The chunk and span tables (one block scan over the sequences):
+//   seq_off[n] = number of 64-token chunks of sequences 0..n-1;
+//   segb[n]    = number of spans of sequences 0..n-1, where a sequence is one
+//                span (seg == 0) or ceil(chunks / seg) segments of seg chunks
+//                (seg > 0; a sequence without tokens then has none);
+//   spans[i]   = (first chunk, end chunk, first token, end token of the
+//                sequence) of span i, the unit a sequential pass walks.
 __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t* __restrict__ cu, int n_seq,
-                                                          int32_t* __restrict__ seq_off) {
-  __shared__ int32_t buf[256];
-  __shared__ int32_t carry;
+                                                          int seg, int32_t* __restrict__ seq_off,
+                                                          int32_t* __restrict__ spans,
+                                                          int32_t* __restrict__ segb) {
+  __shared__ int32_t buf[2][256];
+  __shared__ int32_t carry[2];
   const int tid = threadIdx.x;
-  if (tid == 0) carry = 0;
+  if (tid < 2) carry[tid] = 0;
   __syncthreads();
   for (int base = 0; base < n_seq; base += 256) {
     const int n = base + tid;
-    int32_t v = 0;
+    int32_t v = 0, w = 0, t0 = 0, t1 = 0;
     if (n < n_seq) {
-      const int32_t len = cu[n + 1] - cu[n];
-      v = (len + CHUNK - 1) / CHUNK;
+      t0 = cu[n];
+      t1 = cu[n + 1];
+      v = (t1 - t0 + CHUNK - 1) / CHUNK;
+      w = seg > 0 ? (v + seg - 1) / seg : 1;
     }
-    buf[tid] = v;
+    buf[0][tid] = v;
+    buf[1][tid] = w;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // Hillis-Steele inclusive scan
-      int32_t y = tid >= off ? buf[tid - off] : 0;
+    for (int off = 1; off < 256; off <<= 1) {  // Hillis-Steele inclusive scans
+      const int32_t y0 = tid >= off ? buf[0][tid - off] : 0;
+      const int32_t y1 = tid >= off ? buf[1][tid - off] : 0;
       __syncthreads();
-      buf[tid] += y;
+      buf[0][tid] += y0;
+      buf[1][tid] += y1;
       __syncthreads();
     }
-    if (n < n_seq) seq_off[n] = carry + buf[tid] - v;
+    if (n < n_seq) {
+      const int32_t c0 = carry[0] + buf[0][tid] - v, s0 = carry[1] + buf[1][tid] - w;
+      seq_off[n] = c0;
+      segb[n] = s0;
+      for (int32_t j = 0; j < w; ++j) {
+        const int32_t cb = seg > 0 ? c0 + j * seg : c0;
+        const int32_t ce = seg > 0 ? (cb + seg < c0 + v ? cb + seg : c0 + v) : c0 + v;
+        reinterpret_cast<int4*>(spans)[s0 + j] = make_int4(cb, ce, t0 + CHUNK * (cb - c0), t1);
+      }
+    }
     __syncthreads();
-    if (tid == 255) carry += buf[255];
+    if (tid < 2) carry[tid] += buf[tid][255];
     __syncthreads();
   }
-  if (tid == 0) seq_off[n_seq] = carry;
+  if (tid == 0) {
+    seq_off[n_seq] = carry[0];
+    segb[n_seq] = carry[1];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -361,7 +386,8 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                                 const int32_t* cu, const ChunkLayout& Ly, char* ws,
                                 hipStream_t st) {
   int32_t* seq_off = (int32_t*)(ws + Ly.seq_off);
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, st, cu, s.n_seq, seq_off);
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, st, cu, s.n_seq, (int)Ly.seg, seq_off,
+                     (int32_t*)(ws + Ly.spans), (int32_t*)(ws + Ly.segb));
   if (Ly.nt_max > 0 && s.total_tokens > 0) {
     const size_t shm = sizeof(PrepSmem<T, D, BWD && sizeof(T) == 2>);
     hipFuncSetAttribute((const void*)chunk_prep_kernel<T, D, BWD>,

@@ -5,7 +5,9 @@
 //   dR     = M^T dDelta = diag(beta) Tinv^T dDelta        (= dv)
 //   dS     = Gam_L dS' + (scale Q)^T diag(Gam) dO - K^T diag(Gam) dR
 // It stores dS' per chunk (for the chunk-parallel gradients), dDelta and dv,
-// and dS0 at the sequence start.
+// and dS0 at the sequence start.  The DRY instantiation (the first pass of
+// the segmented scan, which only needs each segment's dS0) issues the same
+// stores with empty ranges, so they are dropped.
 //
 // Same structure as the state pass (chunk_state.hip): one workgroup per
 // (sequence, value head, block of 16 * NW value rows); compute wave w keeps
@@ -37,9 +39,10 @@ template <typename T, int D, int NW> struct RevBuf {
   float G[CHUNK], Dc[CHUNK], Bt[CHUNK];   // Gam_t, dec_t, beta_t
 } __attribute__((aligned(16)));
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool DRY>
 __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
+    const int32_t* __restrict__ spans, const int32_t* __restrict__ n_spans, int Hv, int G,
+    float scale,
     const T* __restrict__ Kb, const T* __restrict__ Ktb, const T* __restrict__ Qtb,
     const T* __restrict__ Ptb, const T* __restrict__ Tib, const float* __restrict__ Gw,
     const float* __restrict__ Dw, const float* __restrict__ Bw, const T* __restrict__ dout, const float* __restrict__ dS_final,
@@ -73,6 +76,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   const int wave = mover ? wave_ - NW : wave_;
   const int item = xcd_item(blockIdx.x, n_items);
   const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
+  if (n >= *n_spans) return;
   const int kh = h / G, Hk = Hv / G;
   const int v0 = vb * BV;
   const int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
@@ -86,8 +90,9 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     for (int i = 0; i < 4; ++i)
       dS[kt][i] = dS_final ? dS_final[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] : 0.f;
 
-  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
-  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
+  const int4 sp = reinterpret_cast<const int4*>(spans)[n];
+  const int64_t c_begin = sp.x, c_end = sp.y;
+  const int64_t seq_t0 = sp.z, seq_t1 = sp.w;
 
   CopyLanes cl;
   cl.init(lane, wave, NW);
@@ -218,7 +223,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
 #pragma unroll
     for (int p = 0; p < NSD; ++p) sb[p] = AO::from_acc(dS, p);
     {
-      const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
+      const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, DRY ? 0u : D * D * sizeof(T));
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, dS[kt]);
       SR::flush(myst, 0, D, rs, wcol, rowh, lane);
@@ -261,7 +266,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     }
     {
       // rows past the sequence end fall outside the buffer: dropped
-      const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+      const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D + v0, DRY ? 0u : (uint32_t)L * rowb);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) SR::put(myst, D + 16 * tt, ps, lane, dd[tt]);
       SR::flush(myst, D, CHUNK, rs, wcol, rowb, lane);
@@ -273,7 +278,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
       frag df[NSC];
 #pragma unroll
       for (int p = 0; p < NSC; ++p) df[p] = AO::from_acc(dd, p);
-      const auto rs = buffer_of(dvo + t0 * lddv + (int64_t)h * D + v0, (uint32_t)L * rowv);
+      const auto rs = buffer_of(dvo + t0 * lddv + (int64_t)h * D + v0, DRY ? 0u : (uint32_t)L * rowv);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         floatx4 dr = zero4();
@@ -361,19 +366,41 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
 // ---------------------------------------------------------------------------
 constexpr int REV_NW = 2;
 
+// One launch over all spans (stores dropped when dry).
 template <typename T, int D>
-static hipError_t chunk_rev(const gdn_shape& s, float scale, const int32_t* cu, const void* dout,
-                            const float* dS_final, void* dv, int64_t lddv, float* dS0,
-                            const ChunkLayout& Ly, char* ws, hipStream_t st) {
+static hipError_t chunk_rev_launch(const gdn_shape& s, float scale, const void* dout,
+                                   const float* dS_final, void* dv, int64_t lddv, float* dS0,
+                                   const ChunkLayout& Ly, char* ws, int dry, hipStream_t st) {
   constexpr int NW = REV_NW, BV = 16 * NW;
-  const int n_items = (D / BV) * s.hv * s.n_seq;
-  hipLaunchKernelGGL((chunk_rev_kernel<T, D, NW>), dim3(n_items), dim3(128 * NW), 0, st, cu,
-                     (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
+  const int n_items = (D / BV) * s.hv * (int)Ly.nspan_max;
+  auto kern = dry ? chunk_rev_kernel<T, D, NW, true> : chunk_rev_kernel<T, D, NW, false>;
+  hipLaunchKernelGGL(kern, dim3(n_items), dim3(128 * NW), 0, st,
+                     (const int32_t*)(ws + Ly.spans), (const int32_t*)(ws + Ly.segb) + s.n_seq,
+                     s.hv, s.hv / s.hk, scale,
                      (const T*)(ws + Ly.kb), (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb),
                      (const T*)(ws + Ly.ptb), (const T*)(ws + Ly.tib), (const float*)(ws + Ly.gw),
                      (const float*)(ws + Ly.dw), (const float*)(ws + Ly.bw), (const T*)dout, dS_final, dS0, (T*)(ws + Ly.dh),
                      (T*)(ws + Ly.ddw), (T*)dv, lddv, n_items);
   return hipGetLastError();
+}
+
+// The reverse pass over every sequence, or the segmented scan: the pass over
+// each segment from a zero gradient (its dB), the combine with the segments'
+// transitions that the state pass left in the workspace, then the pass over
+// each segment from the gradient at its end.
+template <typename T, int D>
+static hipError_t chunk_rev(const gdn_shape& s, float scale, const int32_t* cu, const void* dout,
+                            const float* dS_final, void* dv, int64_t lddv, float* dS0,
+                            const ChunkLayout& Ly, char* ws, hipStream_t st) {
+  if (Ly.seg == 0)
+    return chunk_rev_launch<T, D>(s, scale, dout, dS_final, dv, lddv, dS0, Ly, ws, 0, st);
+  hipError_t e = chunk_rev_launch<T, D>(s, scale, dout, nullptr, dv, lddv, (float*)(ws + Ly.sumr),
+                                        Ly, ws, 1, st);
+  if (e != hipSuccess) return e;
+  e = launch_span_combine(s, Ly, ws, true, dS_final, dS0, st);
+  if (e != hipSuccess) return e;
+  return chunk_rev_launch<T, D>(s, scale, dout, (const float*)(ws + Ly.dse), dv, lddv, nullptr, Ly,
+                                ws, 0, st);
 }
 
 hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const void* k, int64_t ldq,

@@ -31,6 +31,12 @@
 // (Tile).  Every address that varies by lane is computed once: copies go
 // through buffer resources (uniform base, per-lane offset) and LDS reads use
 // per-lane offsets plus constants.
+//
+// Row blocks past D / BV (nblk = 2 D / BV, the first pass of the segmented
+// scan) start from identity rows and read no values, so their rows end as the
+// span's transition Phi.  The DRY instantiation issues every store with an
+// empty range (dropped), so its memory-operation counts match the stored
+// pass.
 #include "chunk_stream.h"
 
 namespace gdn {
@@ -52,10 +58,10 @@ template <typename T, int D, int NW, int MODE> struct StateBuf {
   float G[CHUNK], Dc[CHUNK];            // Gam_t, dec_t
 } __attribute__((aligned(16)));
 
-template <typename T, int D, int NW, int MODE>
+template <typename T, int D, int NW, int MODE, bool DRY>
 __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 * NW)) chunk_state_kernel(
-    const T* __restrict__ v, int64_t ldv, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ seq_off, int Hv, int G, float scale,
+    const T* __restrict__ v, int64_t ldv, const int32_t* __restrict__ spans,
+    const int32_t* __restrict__ n_spans, int nblk, int Hv, int G, float scale,
     const typename Compute<T>::type* __restrict__ Mw, const typename Compute<T>::type* __restrict__ Pw,
     const typename Compute<T>::type* __restrict__ Ww, const typename Compute<T>::type* __restrict__ Ktw,
     const typename Compute<T>::type* __restrict__ Xw, const float* __restrict__ Gw,
@@ -88,8 +94,13 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   const int wave_ = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool mover = SB::KR && wave_ >= NW;
   const int wave = mover ? wave_ - NW : wave_;
+  // item -> (span n, value head h, row block vb); blocks vb >= D / BV (the
+  // first pass of the segmented scan) carry identity rows with no values:
+  // their state rows become the span's transition Phi
   const int item = xcd_item(blockIdx.x, n_items);
-  const int vb = item % (D / BV), h = (item / (D / BV)) % Hv, n = item / ((D / BV) * Hv);
+  const int vb = item % nblk, h = (item / nblk) % Hv, n = item / (nblk * Hv);
+  if (n >= *n_spans) return;
+  const bool phi = DRY && vb >= D / BV;   // (only the first pass has identity rows)
   const int kh = h / G, Hk = Hv / G;
   const int v0 = vb * BV;
   const int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
@@ -101,10 +112,12 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      S[kt][i] = S0 ? S0[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] : 0.f;
+      S[kt][i] = phi ? (v0 - D + vcol == 16 * kt + g4 + i ? 1.f : 0.f)
+                     : S0 ? S0[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] : 0.f;
 
-  const int64_t c_begin = seq_off[n], c_end = seq_off[n + 1];
-  const int64_t seq_t0 = cu[n], seq_t1 = cu[n + 1];
+  const int4 sp = reinterpret_cast<const int4*>(spans)[n];
+  const int64_t c_begin = sp.x, c_end = sp.y;
+  const int64_t seq_t0 = sp.z, seq_t1 = sp.w;
 
   // ---- per-lane offsets, the same for every chunk
   CopyLanes cl;
@@ -143,7 +156,9 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     if constexpr (MODE == 0) copy_tile<TM, NW>(B.P, Pw + ch * CHUNK * CHUNK, cl, wave);
     {
       const uint32_t ldb = (uint32_t)(ldv * sizeof(T));
-      const auto rs = buffer_of(v + t0 * ldv + (int64_t)h * D + v0, (uint32_t)Lc * ldb);
+      // (identity-row blocks copy the value rows of block vb - D / BV, which
+      // stay unused: their compute takes zero values)
+      const auto rs = buffer_of(v + t0 * ldv + (int64_t)h * D + (phi ? v0 - D : v0), (uint32_t)Lc * ldb);
 #pragma unroll
       for (int j = 0; j < TV::PIECES / THREADS; ++j) {
         const int s = (j * NW + wave) * 64 + lane, r = s / TV::RP;
@@ -173,7 +188,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   const uint32_t rowh = (uint32_t)(D * sizeof(T));
   const uint32_t hb = (uint32_t)(16 * wave * sizeof(T)) + ps.lane_off<T>(lane, rowh);
   auto store_state = [&](int64_t c) __attribute__((always_inline)) {
-    const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, D * D * sizeof(T));
+    const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, DRY ? 0u : D * D * sizeof(T));
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, S[kt]);
   };
@@ -203,6 +218,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   // the same count.
   constexpr int NFL = SR::stores(D) + 2 * SR::stores(CHUNK);
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
+    valid = valid && !DRY;
     const char* st = stage_of(cp, wave);
     const int64_t ca = valid ? cp : c_begin;
     const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
@@ -260,7 +276,8 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
         const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
         const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[tt][i] = to_f(B.V[TV::at(16 * tt + g4 + i, vcol)]) - gv[i] * kx[i];
+        for (int i = 0; i < 4; ++i)
+          R[tt][i] = (phi ? 0.f : to_f(B.V[TV::at(16 * tt + g4 + i, vcol)])) - gv[i] * kx[i];
       }
       frag rf[NSC];
 #pragma unroll
@@ -292,11 +309,11 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
 #pragma unroll
       for (int p = 0; p < NSC; ++p) {
         if constexpr (KS == 4) {
-          bv[p] = to_f(B.V[TV::at(16 * (p >> 2) + g4 + (p & 3), vcol)]);
+          bv[p] = phi ? 0.f : to_f(B.V[TV::at(16 * (p >> 2) + g4 + (p & 3), vcol)]);
         } else {
 #pragma unroll
           for (int j = 0; j < NV; ++j)
-            bv[p][j] = (CT)to_f(B.V[TV::at(32 * p + 16 * (j >> 2) + g4 + (j & 3), vcol)]);
+            bv[p][j] = phi ? (CT)0.f : (CT)to_f(B.V[TV::at(32 * p + 16 * (j >> 2) + g4 + (j & 3), vcol)]);
         }
       }
 #pragma unroll
@@ -358,7 +375,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
 #pragma unroll
       for (int p = 0; p < NSC; ++p) duf[p] = AO::from_acc(Dl, p);
       // rows past the sequence end fall outside the buffer: dropped
-      const auto rs = buffer_of(o + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+      const auto rs = buffer_of(o + t0 * HvD + (int64_t)h * D + v0, DRY ? 0u : (uint32_t)L * rowb);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         floatx4 ov = zero4();
@@ -484,39 +501,61 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     }
   }
 
-  if (S_final) {
+  if (S_final) {   // [span][head][nblk * BV rows][D]
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S_final[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] = S[kt][i];
+        S_final[(((int64_t)n * Hv + h) * (nblk * BV) + v0 + vcol) * D + 16 * kt + g4 + i] = S[kt][i];
   }
 }
 
 // ---------------------------------------------------------------------------
 constexpr int STATE_NW = 2;   // waves (16 value rows of the state each) per workgroup
 
-// With 16-bit MODE 1 (the K-rows form) the pass also stores R and Delta,
-// which it forms on the way.
+// One launch over all spans: nblk row blocks per (span, head) (D / BV, or
+// 2 D / BV for the first pass of the segmented scan, which carries the
+// identity rows), stores dropped when dry.  With 16-bit MODE 1 (the K-rows
+// form) the pass also stores R and Delta, which it forms on the way.
 template <typename T, int D, int MODE>
-static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, float scale,
-                              const float* S0, float* S_final, const int32_t* cu, void* o,
-                              const ChunkLayout& Ly, char* ws, hipStream_t st) {
+static hipError_t chunk_state_launch(const gdn_shape& s, const void* v, int64_t ldv, float scale,
+                                     const float* S0, float* S_final, void* o,
+                                     const ChunkLayout& Ly, char* ws, int nblk, int dry,
+                                     hipStream_t st) {
   constexpr bool KR = StateBuf<T, D, STATE_NW, MODE>::KR;
-  constexpr int NW = STATE_NW, BV = 16 * NW;
+  constexpr int NW = STATE_NW;
   typedef typename Compute<T>::type CT;
-  auto kern = chunk_state_kernel<T, D, NW, MODE>;
-  const int n_items = (D / BV) * s.hv * s.n_seq;
-  hipLaunchKernelGGL(kern, dim3(n_items), dim3((StateBuf<T, D, NW, MODE>::KR ? 128 : 64) * NW), 0, st,
-                     (const T*)v, ldv, cu,
-                     (const int32_t*)(ws + Ly.seq_off), s.hv, s.hv / s.hk, scale,
+  auto kern = dry ? chunk_state_kernel<T, D, NW, MODE, true> : chunk_state_kernel<T, D, NW, MODE, false>;
+  const int n_items = nblk * s.hv * (int)Ly.nspan_max;
+  hipLaunchKernelGGL(kern, dim3(n_items), dim3((KR ? 128 : 64) * NW), 0, st,
+                     (const T*)v, ldv, (const int32_t*)(ws + Ly.spans),
+                     (const int32_t*)(ws + Ly.segb) + s.n_seq, nblk, s.hv, s.hv / s.hk, scale,
                      (const CT*)(ws + Ly.mw), (const CT*)(ws + Ly.pw),
-                     (const CT*)(ws + (StateBuf<T, D, NW, MODE>::KR ? Ly.k16w : Ly.ww)),
+                     (const CT*)(ws + (KR ? Ly.k16w : Ly.ww)),
                      (const CT*)(ws + Ly.ktw), (const CT*)(ws + Ly.q16w),
                      (const float*)(ws + Ly.gw), (const float*)(ws + Ly.dw), S0, S_final, (T*)o,
                      (T*)(ws + Ly.h), KR ? (T*)(ws + Ly.rw) : nullptr,
                      KR ? (CT*)(ws + Ly.dl16w) : nullptr, n_items);
   return hipGetLastError();
+}
+
+// The state pass over every sequence: one chain per (sequence, head, row
+// block), or the segmented scan (first pass from zero with the identity rows,
+// the combine, then the pass per segment from its start state).
+template <typename T, int D, int MODE>
+static hipError_t chunk_state(const gdn_shape& s, const void* v, int64_t ldv, float scale,
+                              const float* S0, float* S_final, const int32_t* cu, void* o,
+                              const ChunkLayout& Ly, char* ws, hipStream_t st) {
+  constexpr int NB = D / (16 * STATE_NW);
+  if (Ly.seg == 0)
+    return chunk_state_launch<T, D, MODE>(s, v, ldv, scale, S0, S_final, o, Ly, ws, NB, 0, st);
+  hipError_t e = chunk_state_launch<T, D, MODE>(s, v, ldv, scale, nullptr, (float*)(ws + Ly.sumf),
+                                                o, Ly, ws, 2 * NB, 1, st);
+  if (e != hipSuccess) return e;
+  e = launch_span_combine(s, Ly, ws, false, S0, S_final, st);
+  if (e != hipSuccess) return e;
+  return chunk_state_launch<T, D, MODE>(s, v, ldv, scale, (const float*)(ws + Ly.sst), nullptr, o,
+                                        Ly, ws, NB, 0, st);
 }
 
 hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,

@@ -27,6 +27,7 @@ class CoreConfig:
     act: int = L.GDN_ACT_SILU            # output-gate activation
     l2_eps: float = 1e-6
     norm_eps: float = 1e-6
+    seg_chunks: int = 0                  # segment-parallel state scan (0: the library decides)
 
     @property
     def channels(self):
@@ -66,7 +67,7 @@ class GDNCore:
 
     def shape(self, T: int, n_seq: int) -> L.Shape:
         c = self.cfg
-        return L.make_shape(n_seq, T, c.hk, c.hv, c.d, c.dtype)
+        return L.make_shape(n_seq, T, c.hk, c.hv, c.d, c.dtype, c.seg_chunks)
 
     def workspace(self, shape: L.Shape, rows: int) -> torch.Tensor:
         need = max(L.gdn_conv_bwd_workspace(shape), L.gdn_gate_bwd_workspace(shape),

@@ -63,6 +63,11 @@ typedef struct {
   int32_t conv_k;       /* short-conv taps; supported: 4 */
   int32_t chunk;        /* chunk length of the WY/UT form; supported: 64 */
   gdn_dtype dtype;      /* storage type of token tensors */
+  int32_t seg_chunks;   /* segment-parallel state scan: 0 = the library decides (it splits
+                           sequences into segments when sequences x value heads are too few
+                           to fill the GPU), > 0 = segments of this many chunks, < 0 = never
+                           split.  Results are the same up to rounding; the chunk workspace
+                           size depends on it. */
 } gdn_shape;
 
 const char* gdn_status_string(gdn_status s);
@@ -191,7 +196,9 @@ size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
  * gdn_chunk_bwd_states: the same without o: chunk-start states, R and
  *   Delta (one launch for bf16 data, two for fp32).
  * gdn_chunk_bwd_reverse: reverse pass over chunks; writes dv, dS0 and the
- *   chunk-end state gradients.
+ *   chunk-end state gradients.  When the shape splits sequences into segments
+ *   (seg_chunks), it also reads the segments' state transitions that
+ *   gdn_chunk_fwd_states_save or gdn_chunk_bwd_states left in the workspace.
  * gdn_chunk_bwd_grads: chunk-parallel gradients; writes dq, dk, dg, dbeta
  *   (reads dv written by the reverse phase, and beta as the backward
  *   preparation left it in the workspace: `beta` must be the array that

@@ -135,3 +135,74 @@ def chunked_bwd(q, k, v, g, beta, cu, scale, dout, S0=None, dS_final=None, C=64)
                 dkk[c0:c1, kh] += dK
             dS0[n, h] = dS
     return dq, dkk, dvv, dg, dbeta, dS0
+
+
+# ---------------------------------------------------------------------------
+# Segment-parallel form of the state recurrences.  Over the chunks of one
+# segment the state map is affine, S_end = S_start Phi + B: B is the end state
+# reached from a zero start, Phi = A_1 ... A_L (A_c the chunk's map of the
+# state with no values) is reached by running the same chunks from identity
+# rows with zero values.  The state gradient maps through the transposes:
+# dS_start = dS_end Phi^T + dB, dB the start gradient reached from a zero
+# end gradient.
+
+def _chunks(c_lo, c_hi, C):
+    return [(c0, min(c0 + C, c_hi)) for c0 in range(c_lo, c_hi, C)]
+
+
+def _run_chunks(spans, Q, K, V, gg, bb, S):
+    for c0, c1 in spans:
+        _, S, _ = _chunk_fwd(Q[c0:c1], K[c0:c1], V[c0:c1], gg[c0:c1], bb[c0:c1], S)
+    return S
+
+
+def _rev_dS(spans, Q, K, V, gg, bb, dO, dSp):
+    """The reverse recurrence of the state gradient over `spans` (last chunk
+    first) from dSp at their end; returns the gradient at their start.  It
+    does not depend on the states."""
+    for c0, c1 in reversed(spans):
+        L = c1 - c0
+        _, _, c = _chunk_fwd(Q[c0:c1], K[c0:c1], np.zeros((L, dSp.shape[0])), gg[c0:c1],
+                             bb[c0:c1], np.zeros_like(dSp))
+        Gam, M, P, dec = c["Gam"], c["M"], c["P"], c["dec"]
+        dDl = P.T @ dO[c0:c1] + dec[:, None] * (K[c0:c1] @ dSp.T)
+        dR = M.T @ dDl
+        dSp = Gam[-1] * dSp + dO[c0:c1].T @ (Gam[:, None] * Q[c0:c1]) - (Gam[:, None] * dR).T @ K[c0:c1]
+    return dSp
+
+
+def segmented_scan(q, k, v, g, beta, cu, scale, dout, S0=None, dS_final=None, C=64, seg=2):
+    """Per (sequence, value head): the segment start states, S_final, the
+    state gradients at the segment ends and dS0, by the segmented scan
+    (summaries per segment, then the combines).  Returns
+    (starts, S_final, dS_ends, dS0), starts / dS_ends as {(n, h): [D x D]}."""
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1:]
+    G = Hv // Hk
+    N = len(cu) - 1
+    starts, ends = {}, {}
+    Sf = np.zeros((N, Hv, dv, dk))
+    dS0 = np.zeros((N, Hv, dv, dk))
+    for n in range(N):
+        chunks = _chunks(cu[n], cu[n + 1], C)
+        segs = [chunks[i:i + seg] for i in range(0, len(chunks), seg)]
+        for h in range(Hv):
+            kh = h // G
+            Q, K, V, gg, bb = scale * q[:, kh], k[:, kh], v[:, h], g[:, h], beta[:, h]
+            Z = np.zeros((T, dk))
+            B = [_run_chunks(sp, Q, K, V, gg, bb, np.zeros((dv, dk))) for sp in segs]
+            Phi = [_run_chunks(sp, Q, K, Z, gg, bb, np.eye(dk)) for sp in segs]
+            dB = [_rev_dS(sp, Q, K, V, gg, bb, dout[:, h], np.zeros((dv, dk))) for sp in segs]
+            S = np.zeros((dv, dk)) if S0 is None else S0[n, h].astype(np.float64)
+            starts[n, h] = []
+            for s in range(len(segs)):
+                starts[n, h].append(S)
+                S = S @ Phi[s] + B[s]
+            Sf[n, h] = S
+            dS = np.zeros((dv, dk)) if dS_final is None else dS_final[n, h].astype(np.float64)
+            ends[n, h] = [None] * len(segs)
+            for s in reversed(range(len(segs))):
+                ends[n, h][s] = dS
+                dS = dS @ Phi[s].T + dB[s]
+            dS0[n, h] = dS
+    return starts, Sf, ends, dS0

@@ -157,3 +157,18 @@ def test_conv_bwd_noalloc_refuses_shapes_beyond_its_scratch():
     st = lib.gdn_conv_bwd_noalloc(ctypes.byref(ok), None, C, a16, a16, 1, ctypes.c_float(1e-6), a16,
                                   C, a16, C, a16, None)
     assert st == 1          # null pointer: invalid argument
+
+
+def test_segmented_scan_workspace():
+    """The segment-parallel state scan's summaries live in the chunk
+    workspace: forcing segments grows it, forbidding them does not change
+    the unsplit size, and the library splits the 4 / 8-head 65536-token
+    shape (32 chains) but not the 16 / 48-head one (192 chains)."""
+    def ws(tokens, hk, hv, seg):
+        return L.gdn_chunk_fwd_workspace(L.make_shape(1, tokens, hk, hv, 128, L.GDN_BF16, seg))
+    assert ws(4096, 2, 4, 2) > ws(4096, 2, 4, -1)
+    assert ws(4096, 16, 48, 0) == ws(4096, 16, 48, -1)
+    assert ws(65536, 16, 48, 0) == ws(65536, 16, 48, -1)
+    assert ws(65536, 4, 8, 0) > ws(65536, 4, 8, -1)
+    assert L.gdn_chunk_bwd_workspace(L.make_shape(1, 65536, 4, 8, 128, L.GDN_BF16)) > \
+        L.gdn_chunk_fwd_workspace(L.make_shape(1, 65536, 4, 8, 128, L.GDN_BF16))

@@ -263,20 +263,22 @@ def test_chunk_full_size_windows(case):
     assert n_checked >= 2
 
 
-def test_chunk_live_state_full_length():
-    """Mild decay (A ~ U(0.01, 0.1)) at the 64k-token, 16/48-head shape, with
-    an initial state and the final state's gradient: the state stays alive
-    from chunk to chunk, so every chunk step's error carries into the next.
-    Both flows run all heads; the first key head with its three value heads
-    is compared with the oracle over all 65536 tokens (heads are
-    independent, so the head-sliced oracle run is exact)."""
-    base = gi.WORKLOADS["flash64k"]
-    w = gi.Workload("flash64k_live", base.T, base.hk, base.hv, base.d, "bf16", init_state=True,
+@pytest.mark.parametrize("wname", ["flash64k", "tp4share"])
+def test_chunk_live_state_full_length(wname):
+    """Mild decay (A ~ U(0.01, 0.1)) at a 64k-token shape, with an initial
+    state and the final state's gradient: the state stays alive from chunk to
+    chunk, so every chunk step's error carries into the next.  Both flows run
+    all heads; the first key head with its value heads is compared with the
+    oracle over all 65536 tokens (heads are independent, so the head-sliced
+    oracle run is exact).  At 4/8 heads the library splits the sequence for
+    the segment-parallel scan, so the live state also crosses segments."""
+    base = gi.WORKLOADS[wname]
+    w = gi.Workload(wname + "_live", base.T, base.hk, base.hv, base.d, "bf16", init_state=True,
                     final_state=True, seed=base.seed)
     inp = gi.make_inputs(w, A_range=(0.01, 0.1))
     T, d, hk, hv = inp["T"], w.d, w.hk, w.hv
     cu = inp["cu_seqlens"]
-    y = _chunk_inputs(base, inp)     # same x and conv weights as the flash64k workload
+    y = _chunk_inputs(base, inp)     # same x and conv weights as the base workload
     g, beta = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
     g, beta = g.astype(np.float32), beta.astype(np.float32)
     # the state reaches across chunks: decay over one chunk stays far from 0
@@ -286,13 +288,13 @@ def test_chunk_live_state_full_length():
     res = _gpu_flows(w, inp, y, g, beta, dout, inp["S0"], inp["dS_T"])
     q, k, v = gi.split_qkv(y, hk, hv, d)
     kh, vh = 0, _vheads(w, 0)
-    print("[live] oracle forward and backward, one key head, 65536 tokens", flush=True)
+    print(f"[live {wname}] oracle forward and backward, one key head, {T} tokens", flush=True)
     o_r, Sf_r = oracle.delta_fwd(q[:, [kh]], k[:, [kh]], v[:, vh], g[:, vh], beta[:, vh], cu,
                                  d ** -0.5, inp["S0"][:, vh])
     ref = oracle.delta_bwd(q[:, [kh]], k[:, [kh]], v[:, vh], g[:, vh], beta[:, vh], cu, d ** -0.5,
                            dout[:, vh], inp["S0"][:, vh], inp["dS_T"][:, vh])
     for flow, r in res.items():
-        tag = f"live {flow}"
+        tag = f"live {wname} {flow}"
         errs = {"o": assert_close(f"o {tag}", r["o"][:, vh], o_r, FWD_TOL_BF16),
                 "S_final": assert_close(f"S_final {tag}", r["S_final"][:, vh], Sf_r, FWD_TOL_BF16)}
         for i, nm in enumerate(("dq", "dk", "dv", "dg", "dbeta", "dS0")):

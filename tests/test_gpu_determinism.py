@@ -125,22 +125,25 @@ class Guarded:
 
 
 CANARY_CASES = {
-    # name: hk, hv, d, dtype, lens
-    "bf16_d128": (2, 6, 128, "bf16", [300, 65, 7, 1, 0, 130]),
-    "bf16_d32": (2, 4, 32, "bf16", [129, 64, 3]),
-    "fp32_d32": (1, 2, 32, "fp32", [100, 37, 1, 70]),
+    # name: hk, hv, d, dtype, lens, segment length of the state scan
+    "bf16_d128": (2, 6, 128, "bf16", [300, 65, 7, 1, 0, 130], 0),
+    "bf16_d128_seg": (2, 6, 128, "bf16", [300, 65, 7, 1, 0, 130], 2),
+    "bf16_d32": (2, 4, 32, "bf16", [129, 64, 3], 0),
+    "bf16_d32_seg": (2, 4, 32, "bf16", [129, 64, 3], 1),
+    "fp32_d32": (1, 2, 32, "fp32", [100, 37, 1, 70], 0),
+    "fp32_d32_seg": (1, 2, 32, "fp32", [100, 37, 1, 70], 1),
 }
 
 
 @pytest.mark.parametrize("name", list(CANARY_CASES))
 def test_every_entry_point_stays_in_bounds(name):
-    hk, hv, d, dt, lens = CANARY_CASES[name]
+    hk, hv, d, dt, lens, seg = CANARY_CASES[name]
     w = gi.Workload(name, sum(lens), hk, hv, d, dt, seq="varlen", init_state=True,
                     final_state=True, seed=91)
     inp = gi.make_inputs(w, seqlens=lens, A_range=(0.02, 0.3))
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     T, N, C = inp["T"], inp["N"], w.channels
-    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16 if dt == "bf16" else L.GDN_FP32)
+    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16 if dt == "bf16" else L.GDN_FP32, seg)
     G = Guarded()
     # inputs (checked afterwards to be unchanged)
     x = G.new("x", (T, C), tdt, dev(inp["x"], tdt))

@@ -17,15 +17,16 @@ from tests.gpu_util import DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_cl
 pytestmark = pytest.mark.gpu
 
 
-def _run(q, k, v, g, beta, lens, scale, S0=None, dtype="bf16", dout=None, dS_final=None):
+def _run(q, k, v, g, beta, lens, scale, S0=None, dtype="bf16", dout=None, dS_final=None, seg=0):
     """q, k [T, hk, d]; v [T, hv, d]; g, beta [T, hv] (float arrays, bf16-exact
-    for bf16).  Returns o, S_final (and dq, dk, dv, dg, dbeta, dS0 if dout)."""
+    for bf16).  Returns o, S_final (and dq, dk, dv, dg, dbeta, dS0 if dout).
+    seg > 0 runs the segment-parallel state scan with segments of seg chunks."""
     T, hk, d = q.shape
     hv = v.shape[1]
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     cu = gi.cu_from_lengths(lens)
     N = len(lens)
-    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16 if dtype == "bf16" else L.GDN_FP32)
+    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16 if dtype == "bf16" else L.GDN_FP32, seg)
     y = np.concatenate([q.reshape(T, -1), k.reshape(T, -1), v.reshape(T, -1)], axis=1)
     yt = dev(y, tdt)
     C = hk * d
@@ -69,7 +70,8 @@ CASES = [("fp32", 1, 2, 32, [64, 37]), ("bf16", 2, 4, 128, [150, 70])]
 
 
 @pytest.mark.parametrize("dtype,hk,hv,d,lens", CASES, ids=["fp32", "bf16"])
-def test_I1_no_write_no_decay_keeps_state(dtype, hk, hv, d, lens):
+@pytest.mark.parametrize("seg", [0, 1], ids=["seq", "seg1"])
+def test_I1_no_write_no_decay_keeps_state(dtype, hk, hv, d, lens, seg):
     """beta = 0 and g = 0: the state stays S0 (exactly: no term is added and
     the decay is 1) and o_t = S0 (scale q_t)."""
     rng = np.random.default_rng(21)
@@ -80,7 +82,7 @@ def test_I1_no_write_no_decay_keeps_state(dtype, hk, hv, d, lens):
     z = np.zeros((T, hv), np.float32)
     S0 = (0.3 * rng.standard_normal((len(lens), hv, d, d))).astype(np.float32)
     sc = d ** -0.5
-    r = _run(q, k, v, z, z, lens, sc, S0, dtype)
+    r = _run(q, k, v, z, z, lens, sc, S0, dtype, seg=seg)
     np.testing.assert_array_equal(r["S_final"], S0.astype(np.float64))
     cu = gi.cu_from_lengths(lens)
     ref = np.zeros((T, hv, d))
@@ -108,7 +110,8 @@ def test_I2_exact_recall_with_orthonormal_keys():
 
 
 @pytest.mark.parametrize("dtype,hk,hv,d,lens", CASES, ids=["fp32", "bf16"])
-def test_I3_unit_key_full_write_overwrites(dtype, hk, hv, d, lens):
+@pytest.mark.parametrize("seg", [0, 1], ids=["seq", "seg1"])
+def test_I3_unit_key_full_write_overwrites(dtype, hk, hv, d, lens, seg):
     """Unit k_t and beta_t = 1: S_t k_t = v_t whatever g_t and S_{t-1}; so the
     final state maps each sequence's last key to its last value."""
     rng = np.random.default_rng(23)
@@ -119,7 +122,7 @@ def test_I3_unit_key_full_write_overwrites(dtype, hk, hv, d, lens):
     v = _rb(rng.standard_normal((T, hv, d)), dtype)
     g = -rng.uniform(0.0, 0.5, (T, hv)).astype(np.float32)
     S0 = (0.3 * rng.standard_normal((len(lens), hv, d, d))).astype(np.float32)
-    r = _run(q, k, v, g, np.ones((T, hv), np.float32), lens, d ** -0.5, S0, dtype)
+    r = _run(q, k, v, g, np.ones((T, hv), np.float32), lens, d ** -0.5, S0, dtype, seg=seg)
     cu = gi.cu_from_lengths(lens)
     for n in range(len(lens)):
         t = cu[n + 1] - 1
@@ -132,7 +135,8 @@ def test_I3_unit_key_full_write_overwrites(dtype, hk, hv, d, lens):
 
 
 @pytest.mark.parametrize("dtype,hk,hv,d,lens", CASES, ids=["fp32", "bf16"])
-def test_I4_infinite_decay_is_local(dtype, hk, hv, d, lens):
+@pytest.mark.parametrize("seg", [0, 1], ids=["seq", "seg1"])
+def test_I4_infinite_decay_is_local(dtype, hk, hv, d, lens, seg):
     """g -> -infinity (the decay underflows to zero): nothing of the past
     reaches token t, o_t = beta_t (k_t . scale q_t) v_t, and the final state is
     the last write."""
@@ -145,7 +149,7 @@ def test_I4_infinite_decay_is_local(dtype, hk, hv, d, lens):
     beta = rng.uniform(0.1, 0.9, (T, hv)).astype(np.float32)
     S0 = (0.3 * rng.standard_normal((len(lens), hv, d, d))).astype(np.float32)
     sc = d ** -0.5
-    r = _run(q, k, v, g, beta, lens, sc, S0, dtype)
+    r = _run(q, k, v, g, beta, lens, sc, S0, dtype, seg=seg)
     q64, k64, v64, b64 = (a.astype(np.float64) for a in (q, k, v, beta))
     ref = np.zeros((T, hv, d))
     for h in range(hv):
@@ -160,9 +164,12 @@ def test_I4_infinite_decay_is_local(dtype, hk, hv, d, lens):
             assert_close(f"S_final (seq {n}, head {h})", r["S_final"][n, h], last, _tol(dtype))
 
 
-def test_I6_continuation_through_the_final_state():
+@pytest.mark.parametrize("seg", [0, 1], ids=["seq", "seg1"])
+def test_I6_continuation_through_the_final_state(seg):
     """Splitting a sequence inside a chunk and feeding the first part's final
-    state in as the second part's initial state reproduces o and S_final."""
+    state in as the second part's initial state reproduces o and S_final
+    (also with the segmented scan, whose segments are then a third way of
+    cutting the same sequence)."""
     rng = np.random.default_rng(26)
     hk, hv, d, T, cut = 2, 4, 128, 300, 130
     q = _rb(_unit(rng.standard_normal((T, hk, d))), "bf16")
@@ -173,14 +180,15 @@ def test_I6_continuation_through_the_final_state():
     S0 = (0.3 * rng.standard_normal((1, hv, d, d))).astype(np.float32)
     sc = d ** -0.5
     whole = _run(q, k, v, g, beta, [T], sc, S0)
-    a = _run(q[:cut], k[:cut], v[:cut], g[:cut], beta[:cut], [cut], sc, S0)
+    a = _run(q[:cut], k[:cut], v[:cut], g[:cut], beta[:cut], [cut], sc, S0, seg=seg)
     b = _run(q[cut:], k[cut:], v[cut:], g[cut:], beta[cut:], [T - cut], sc,
-             a["S_final"].astype(np.float32))
+             a["S_final"].astype(np.float32), seg=seg)
     assert_close("o", np.concatenate([a["o"], b["o"]]), whole["o"], FWD_TOL_BF16)
     assert_close("S_final", b["S_final"], whole["S_final"], FWD_TOL_BF16)
 
 
-def test_I7_grouped_values_equal_repeated_keys():
+@pytest.mark.parametrize("seg", [0, 1], ids=["seq", "seg1"])
+def test_I7_grouped_values_equal_repeated_keys(seg):
     """Grouped values (2 key heads for 4 value heads) equal explicitly
     repeated q and k (4 key heads), forward and backward, with dq and dk of
     the grouped run the sums over each group."""
@@ -196,7 +204,7 @@ def test_I7_grouped_values_equal_repeated_keys():
     dout = _rb(rng.standard_normal((T, hv, d)), "bf16")
     dSf = rng.standard_normal((len(lens), hv, d, d)).astype(np.float32)
     sc = d ** -0.5
-    grp = _run(q, k, v, g, beta, lens, sc, S0, dout=dout, dS_final=dSf)
+    grp = _run(q, k, v, g, beta, lens, sc, S0, dout=dout, dS_final=dSf, seg=seg)
     rep = _run(np.repeat(q, G, axis=1), np.repeat(k, G, axis=1), v, g, beta, lens, sc, S0,
                dout=dout, dS_final=dSf)
     for key in ("o", "S_final"):

@@ -35,16 +35,20 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("seg", [0, 2], ids=["seq", "seg2"])
 @pytest.mark.parametrize("save_states", [True, False], ids=["saved", "recompute"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_layer_matches_oracle(name, save_states):
-    """Both backward flows: states saved by the forward, or recomputed."""
+def test_layer_matches_oracle(name, save_states, seg):
+    """Both backward flows: states saved by the forward, or recomputed; one
+    sequential pass per sequence, or the segment-parallel scan with segments
+    of two chunks."""
     w, lens, A_range, act = CASES[name]
     inp = gi.make_inputs(w, seqlens=lens, A_range=A_range)
     bf = w.dtype == "bf16"
     tdt = torch.bfloat16 if bf else torch.float32
     rf = gi.round_bf16 if bf else None
-    core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=tdt, act=act), device=DEV)
+    core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=tdt, act=act, seg_chunks=seg),
+                   device=DEV)
     cu = torch.from_numpy(inp["cu_seqlens"]).to(DEV)
     args = (dev(inp["x"], tdt), dev(inp["w_conv"]), dev(inp["a"], tdt), dev(inp["b"], tdt),
             dev(inp["A_log"]), dev(inp["dt_bias"]), dev(inp["z"], tdt), dev(inp["w_norm"]), cu)
@@ -64,7 +68,7 @@ def test_layer_matches_oracle(name, save_states):
     # every error is printed before the first assertion, so a failure shows
     # where along the layer the difference enters
     errs = {k: rel_err(host(t).reshape(np.shape(r)), r) for k, t, r, _ in checks}
-    print(name, "saved" if save_states else "recompute", " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    print(name, "saved" if save_states else "recompute", f"seg={seg}", " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
     for k, t, r, tol in checks:
         assert_close(k, host(t).reshape(np.shape(r)), r, tol)
     # a sequence without tokens hands its initial state and the final state's

@@ -151,6 +151,11 @@ def _delta_inputs(name, seed=7):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_chunk_fwd_bwd(name):
+    """Both chunk flows, each with one sequential pass per sequence (seg 0 at
+    these sizes) and with the segment-parallel scan forced to segments of 1
+    and 3 chunks (so sequences of several chunks combine several segments,
+    and short ones have one)."""
+    from tests.gpu_util import FLOWS, run_chunk
     w, inp, y, g, beta = _delta_inputs(name)
     dt, cu, hk, hv, d = w.dtype, inp["cu_seqlens"], w.hk, w.hv, w.d
     scale = d ** -0.5
@@ -162,60 +167,85 @@ def test_chunk_fwd_bwd(name):
     dout = _rnd(rng.standard_normal(o_ref.shape), dt)
     dSf = inp["dS_T"]
     ref = oracle.delta_bwd(q, k, v, g, beta, cu, scale, dout, S0, dSf)
+    refs = {"o": o_ref, "S_final": Sf_ref, "dq": ref[0], "dk": ref[1], "dv": ref[2], "dg": ref[3],
+            "dbeta": ref[4], "dS0": ref[5]}
 
-    sh = _shape(w, inp)
     yt = dev(y, _tdt(dt))
     qt, kt, vt = yt[:, : hk * d], yt[:, hk * d: 2 * hk * d], yt[:, 2 * hk * d:]
     gt, bt = dev(g), dev(beta)
     cut = torch.from_numpy(cu).to(DEV)
     S0t = dev(S0) if S0 is not None else None
-    Sf = torch.empty((inp["N"], hv, d, d), dtype=torch.float32, device=DEV)
-    o = torch.empty((T, hv, d), dtype=_tdt(dt), device=DEV)
-    ws = torch.empty(max(L.gdn_chunk_fwd_workspace(sh), L.gdn_chunk_bwd_workspace(sh)),
-                     dtype=torch.uint8, device=DEV)
-    L.gdn_chunk_fwd(sh, qt, kt, vt, gt, bt, scale, S0t, Sf, cut, o, ws)
-    dy = torch.empty_like(yt)
-    dq, dk, dv = dy[:, : hk * d], dy[:, hk * d: 2 * hk * d], dy[:, 2 * hk * d:]
-    dg = torch.empty_like(gt)
-    db = torch.empty_like(bt)
-    dS0 = torch.empty_like(Sf)
     dSft = dev(dSf) if dSf is not None else None
-    L.gdn_chunk_bwd(sh, qt, kt, vt, gt, bt, scale, S0t, cut, dev(dout, _tdt(dt)), dSft, dq, dk, dv,
-                    dg, db, dS0, ws)
-    torch.cuda.synchronize()
-    got = (host(dq).reshape(T, hk, d), host(dk).reshape(T, hk, d), host(dv).reshape(T, hv, d),
-           host(dg), host(db), host(dS0))
-    checks = [("o", host(o), o_ref, _tol(dt)), ("S_final", host(Sf), Sf_ref, _tol(dt))]
-    checks += [(nm, a, r, _tol(dt, True))
-               for nm, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref)]
-    report = {nm: rel_err(a, r) for nm, a, r, _ in checks}
-    print(name, " ".join(f"{k}={v:.2e}" for k, v in report.items()))
-    for nm, a, r, tol in checks:
-        assert_close(nm, a, r, tol)
+    dot = dev(dout, _tdt(dt))
+    for seg in (0, 1, 3):
+        sh = L.make_shape(inp["N"], T, hk, hv, d, L.GDN_BF16 if dt == "bf16" else L.GDN_FP32, seg)
+        ws = torch.empty(L.gdn_chunk_bwd_workspace(sh), dtype=torch.uint8, device=DEV)
+        for flow in FLOWS:
+            r = run_chunk(flow, sh, qt, kt, vt, gt, bt, scale, S0t, cut, dot, dSft, ws)
+            torch.cuda.synchronize()
+            got = {"o": host(r["o"]), "S_final": host(r["S_final"]),
+                   "dq": host(r["dq"]).reshape(T, hk, d), "dk": host(r["dk"]).reshape(T, hk, d),
+                   "dv": host(r["dv"]).reshape(T, hv, d), "dg": host(r["dg"]),
+                   "dbeta": host(r["dbeta"]), "dS0": host(r["dS0"])}
+            report = {nm: rel_err(got[nm], refs[nm]) for nm in refs}
+            print(name, flow, f"seg={seg}", " ".join(f"{k}={v:.2e}" for k, v in report.items()),
+                  flush=True)
+            for nm in refs:
+                assert_close(f"{nm} ({flow}, seg {seg})", got[nm], refs[nm],
+                             _tol(dt, nm not in ("o", "S_final")))
 
 
 # ------------------------------------------------------------------ chunk table (integer)
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("seg", [0, 1, 3], ids=["seq", "seg1", "seg3"])
 @pytest.mark.parametrize("lens", [[70, 0, 64, 0, 5, 1, 128, 129], [3, 0], [1], [0, 0, 3],
-                                  [64] * 7 + [65]],
-                         ids=["mixed", "trailing_empty", "one", "leading_empty", "exact_chunks"])
-def test_chunk_table_exact(lens):
-    """The chunk table that the preparation builds from cu_seqlens at the head
-    of the workspace: int32 [n_seq + 1], entry n = number of 64-token chunks
-    of sequences 0 .. n-1.  Bit-exact against the plain count."""
+                                  [64] * 7 + [65], [64 * 7]],
+                         ids=["mixed", "trailing_empty", "one", "leading_empty", "exact_chunks",
+                              "one_long"])
+def test_chunk_table_exact(lens, seg):
+    """The tables the preparation builds from cu_seqlens, bit-exact against
+    plain counts.  At the head of the workspace: int32 [n_seq + 1], entry n =
+    number of 64-token chunks of sequences 0 .. n-1.  Then (each region
+    256-byte aligned) the spans the sequential passes walk, int32 [.][4] =
+    (first chunk, end chunk, first token, end token of the sequence): one per
+    sequence, or with the segmented scan ceil(chunks / seg) per sequence
+    (none for an empty sequence); then int32 [n_seq + 1], the first span of
+    each sequence."""
     hk, hv, d = 1, 2, 32
     cu = gi.cu_from_lengths(lens)
     T, N = int(cu[-1]), len(lens)
-    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16)
+    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16, seg)
     y = torch.zeros((T, 4 * d), dtype=torch.bfloat16, device=DEV)
     g = torch.zeros((T, hv), dtype=torch.float32, device=DEV)
     ws = torch.full((L.gdn_chunk_fwd_workspace(sh),), 0x5A, dtype=torch.uint8, device=DEV)
     L.gdn_chunk_prepare(sh, y[:, :d], y[:, d:2 * d], g, g, 1.0, torch.from_numpy(cu).to(DEV), ws)
     torch.cuda.synchronize()
-    got = ws[: 4 * (N + 1)].cpu().view(torch.int32).numpy()
+    raw = ws.cpu()
     want = np.zeros(N + 1, dtype=np.int32)
     for n, ln in enumerate(lens):
         want[n + 1] = want[n] + (ln + 63) // 64
-    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(raw[: 4 * (N + 1)].view(torch.int32).numpy(), want)
+    spans, segb = [], [0]
+    for n, ln in enumerate(lens):
+        nc = (ln + 63) // 64
+        if seg == 0:
+            spans.append((want[n], want[n + 1], cu[n], cu[n + 1]))
+        else:
+            for c0 in range(0, nc, seg):
+                spans.append((want[n] + c0, want[n] + min(c0 + seg, nc), cu[n] + 64 * c0, cu[n + 1]))
+        segb.append(len(spans))
+    nt_max = T // 64 + N
+    nspan_max = nt_max // seg + N + 1 if seg else N
+    assert len(spans) <= nspan_max
+    o_sp = _align256(4 * (N + 1))
+    o_sb = o_sp + _align256(16 * nspan_max)
+    got_sp = raw[o_sp: o_sp + 16 * len(spans)].view(torch.int32).numpy().reshape(-1, 4)
+    np.testing.assert_array_equal(got_sp, np.array(spans, dtype=np.int32).reshape(-1, 4))
+    np.testing.assert_array_equal(raw[o_sb: o_sb + 4 * (N + 1)].view(torch.int32).numpy(),
+                                  np.array(segb, dtype=np.int32))
 
 
 # ------------------------------------------------------------------ fp16 operand range

@@ -291,3 +291,44 @@ def test_long_sequence_checkpoint_segments():
         got = chunked_bwd(q, k, v, g, beta, cu, 0.5, dout, s0, None, C=C)
         for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref):
             np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-10, err_msg=name)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3])
+def test_segmented_scan_equals_sequential(seg):
+    """The segment-parallel scan's algebra (segment summaries B, Phi and dB,
+    then S_{s+1} = S_s Phi_s + B_s forward and dS_{s-1} = dS_s Phi_s^T + dB_s
+    backward) reproduces the oracle's S_final and dS0 and the sequential
+    states and state gradients at every segment boundary, with mild decay so
+    that the state crosses segments, several sequences and ragged tails."""
+    from tests.chunked_model import _chunks, _rev_dS, _run_chunks, segmented_scan
+    rng = np.random.default_rng(40 + seg)
+    hk, hv, d, C = 1, 2, 8, 4
+    lens = [23, 1, 9, 0, 17]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, hk, d))
+    k = rng.standard_normal((T, hk, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, hv, d))
+    g = -rng.uniform(0.0, 0.2, (T, hv))
+    beta = rng.uniform(0.2, 0.9, (T, hv))
+    S0 = rng.standard_normal((len(lens), hv, d, d))
+    dSf = rng.standard_normal((len(lens), hv, d, d))
+    dout = rng.standard_normal((T, hv, d))
+    sc = 0.5
+    starts, Sf, ends, dS0 = segmented_scan(q, k, v, g, beta, cu, sc, dout, S0, dSf, C=C, seg=seg)
+    _, Sf_ref = oracle.delta_fwd(q, k, v, g, beta, cu, sc, S0)
+    ref = oracle.delta_bwd(q, k, v, g, beta, cu, sc, dout, S0, dSf)
+    np.testing.assert_allclose(Sf, Sf_ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(dS0, ref[5], rtol=1e-10, atol=1e-10)
+    for n in range(len(lens)):
+        chunks = _chunks(cu[n], cu[n + 1], C)
+        for h in range(hv):
+            Q, K, V = sc * q[:, 0], k[:, 0], v[:, h]
+            for s in range(len(starts[n, h])):
+                before = chunks[: s * seg]
+                S = _run_chunks(before, Q, K, V, g[:, h], beta[:, h], S0[n, h])
+                np.testing.assert_allclose(starts[n, h][s], S, rtol=1e-10, atol=1e-10)
+                after = chunks[(s + 1) * seg:]
+                dS = _rev_dS(after, Q, K, V, g[:, h], beta[:, h], dout[:, h], dSf[n, h])
+                np.testing.assert_allclose(ends[n, h][s], dS, rtol=1e-10, atol=1e-10)
