@@ -51,6 +51,9 @@ def _load():
     i64, i32, f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
     lib.oracle_conv_fwd.argtypes = [i64, i32, i32, D, D, I, i32, i32, i32, f64, D]
     lib.oracle_conv_bwd.argtypes = [i64, i32, i32, D, D, I, i32, i32, i32, f64, D, D, D]
+    lib.oracle_conv_state_fwd.argtypes = [i64, i32, i32, D, D, I, i32, i32, i32, f64, D, D, D]
+    lib.oracle_conv_state_bwd.argtypes = [i64, i32, i32, D, D, I, i32, i32, i32, f64, D, D, D, D,
+                                          D, D]
     lib.oracle_gate_fwd.argtypes = [i64, i32, D, D, D, D, D, D]
     lib.oracle_gate_bwd.argtypes = [i64, i32, D, D, D, D, D, D, D, D, D, D]
     lib.oracle_delta_fwd.argtypes = [i64, i32, I, i32, i32, i32, i32, D, D, D, D, D, f64, D, D, D]
@@ -59,7 +62,8 @@ def _load():
     lib.oracle_norm_fwd.argtypes = [i64, i32, D, D, D, f64, ctypes.c_int, D]
     lib.oracle_norm_bwd.argtypes = [i64, i32, D, D, D, f64, ctypes.c_int, D, D, D, D]
     lib.oracle_max_threads.argtypes = []
-    for name in ("oracle_conv_fwd", "oracle_conv_bwd", "oracle_gate_fwd", "oracle_gate_bwd",
+    for name in ("oracle_conv_fwd", "oracle_conv_bwd", "oracle_conv_state_fwd",
+                 "oracle_conv_state_bwd", "oracle_gate_fwd", "oracle_gate_bwd",
                  "oracle_delta_fwd", "oracle_delta_bwd", "oracle_norm_fwd", "oracle_norm_bwd",
                  "oracle_max_threads"):
         getattr(lib, name).restype = ctypes.c_int
@@ -114,6 +118,40 @@ def conv_bwd(x, w, cu, n_l2: int, dk: int, dy, eps: float = L2_EPS):
     _check(_load().oracle_conv_bwd(T, C, w.shape[1], _d(x), _d(w), cup, len(cu) - 1, n_l2, dk,
                                    eps, _d(dy), _d(dx), _d(dw)), "conv_bwd")
     return dx, dw
+
+
+def conv_state_fwd(x, w, cu, n_l2: int, dk: int, cs_in=None, eps: float = L2_EPS):
+    """The convolution with a carried conv state: cs_in [N, K-1, C] holds the
+    K-1 input rows before each sequence (None: zeros).  Returns y [T, C] and
+    the final state [N, K-1, C] (the last K-1 input rows of each sequence,
+    reaching into cs_in for short ones)."""
+    x, w, cs_in = _f64(x), _f64(w), _f64(cs_in)
+    T, C = x.shape
+    K = w.shape[1]
+    cu, cup = _cu(cu)
+    N = len(cu) - 1
+    y = np.empty_like(x)
+    cs_out = np.empty((N, K - 1, C))
+    _check(_load().oracle_conv_state_fwd(T, C, K, _d(x), _d(w), cup, N, n_l2, dk, eps, _d(cs_in),
+                                         _d(y), _d(cs_out)), "conv_state_fwd")
+    return y, cs_out
+
+
+def conv_state_bwd(x, w, cu, n_l2: int, dk: int, dy, cs_in=None, dcs_out=None,
+                   eps: float = L2_EPS):
+    """Backward of conv_state_fwd: returns dx, dw, dcs_in."""
+    x, w, dy, cs_in, dcs_out = _f64(x), _f64(w), _f64(dy), _f64(cs_in), _f64(dcs_out)
+    T, C = x.shape
+    K = w.shape[1]
+    cu, cup = _cu(cu)
+    N = len(cu) - 1
+    dx = np.empty_like(x)
+    dw = np.empty_like(w)
+    dcs_in = np.empty((N, K - 1, C))
+    _check(_load().oracle_conv_state_bwd(T, C, K, _d(x), _d(w), cup, N, n_l2, dk, eps, _d(cs_in),
+                                         _d(dy), _d(dcs_out), _d(dx), _d(dw), _d(dcs_in)),
+           "conv_state_bwd")
+    return dx, dw, dcs_in
 
 
 # ---------------------------------------------------------------- gate

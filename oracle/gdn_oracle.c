@@ -115,6 +115,145 @@ int oracle_conv_fwd(int64_t T, int32_t C, int32_t K, const double* x, const doub
   return OR_OK;
 }
 
+/* ---------------------------------------------------------------------------
+ * The same convolution with a carried conv state (prime-rl page, "Summary":
+ * causal_conv1d takes initial_state and output_final_state).  The state of
+ * sequence n is the K-1 input rows just before its first token, oldest first:
+ * cs_in[n][r][c] stands for x at position t0 - (K-1) + r (NULL: zeros, the
+ * stateless convolution).  cs_out[n][r][c] is the input at position
+ * t1 - (K-1) + r, taken from cs_in where that position precedes t0 (short
+ * sequences), so that feeding it to the next call continues the sequence.
+ * ------------------------------------------------------------------------- */
+
+/* x at position p of sequence n (tokens [t0, t1)), reading the carried state
+ * for positions before t0 */
+static double x_or_state(int64_t p, int64_t t0, int32_t n, int32_t C, int32_t K, int32_t c,
+                         const double* x, const double* cs_in) {
+  if (p >= t0) return x[p * C + c];
+  int64_t r = p - t0 + (K - 1);
+  if (!cs_in || r < 0) return 0.0;
+  return cs_in[((int64_t)n * (K - 1) + r) * C + c];
+}
+
+static void conv_silu_row_state(int64_t t, int64_t t0, int32_t n, int32_t C, int32_t K,
+                                const double* x, const double* w, const double* cs_in, double* u,
+                                double* a) {
+  for (int32_t c = 0; c < C; ++c) {
+    double acc = 0.0;
+    for (int32_t j = 0; j < K; ++j)
+      acc += w[(int64_t)c * K + j] * x_or_state(t - (K - 1) + j, t0, n, C, K, c, x, cs_in);
+    u[c] = acc;
+    a[c] = acc * sigm(acc);
+  }
+}
+
+int oracle_conv_state_fwd(int64_t T, int32_t C, int32_t K, const double* x, const double* w,
+                          const int32_t* cu, int32_t N, int32_t n_l2, int32_t dk, double eps,
+                          const double* cs_in, double* y, double* cs_out) {
+  if (T < 0 || C <= 0 || K <= 1 || N < 0 || n_l2 < 0 || n_l2 > C || (n_l2 && (dk <= 0 || n_l2 % dk)))
+    return OR_ERR;
+  for (int32_t n = 0; n < N; ++n) {
+    int64_t t0 = cu[n], t1 = cu[n + 1];
+#pragma omp parallel for schedule(static)
+    for (int64_t t = t0; t < t1; ++t) {
+      double* u = (double*)malloc(sizeof(double) * C);
+      double* a = (double*)malloc(sizeof(double) * C);
+      conv_silu_row_state(t, t0, n, C, K, x, w, cs_in, u, a);
+      for (int32_t c = 0; c < C; ++c) y[t * C + c] = a[c];
+      for (int32_t h0 = 0; h0 < n_l2; h0 += dk) {
+        double ss = 0.0;
+        for (int32_t i = 0; i < dk; ++i) ss += a[h0 + i] * a[h0 + i];
+        double r = sqrt(ss + eps);
+        for (int32_t i = 0; i < dk; ++i) y[t * C + h0 + i] = a[h0 + i] / r;
+      }
+      free(u);
+      free(a);
+    }
+    if (cs_out)
+      for (int32_t r = 0; r < K - 1; ++r)
+        for (int32_t c = 0; c < C; ++c)
+          cs_out[((int64_t)n * (K - 1) + r) * C + c] =
+              x_or_state(t1 - (K - 1) + r, t0, n, C, K, c, x, cs_in);
+  }
+  return OR_OK;
+}
+
+/* Backward of oracle_conv_state_fwd: dy [T][C] and dcs_out [N][K-1][C] (NULL:
+ * zero) -> dx [T][C], dw [C][K], dcs_in [N][K-1][C] (NULL: not wanted).
+ * Input position p of sequence n feeds u at tokens p + (K-1) - j (tap j) of
+ * the sequence, and the final state when p >= t1 - (K-1). */
+int oracle_conv_state_bwd(int64_t T, int32_t C, int32_t K, const double* x, const double* w,
+                          const int32_t* cu, int32_t N, int32_t n_l2, int32_t dk, double eps,
+                          const double* cs_in, const double* dy, const double* dcs_out,
+                          double* dx, double* dw, double* dcs_in) {
+  if (T < 0 || C <= 0 || K <= 1 || N < 0 || n_l2 < 0 || n_l2 > C || (n_l2 && (dk <= 0 || n_l2 % dk)))
+    return OR_ERR;
+  double* du = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * C);
+  for (int32_t n = 0; n < N; ++n) {
+    int64_t t0 = cu[n], t1 = cu[n + 1];
+#pragma omp parallel for schedule(static)
+    for (int64_t t = t0; t < t1; ++t) {
+      double* u = (double*)malloc(sizeof(double) * C);
+      double* a = (double*)malloc(sizeof(double) * C);
+      double* da = (double*)malloc(sizeof(double) * C);
+      conv_silu_row_state(t, t0, n, C, K, x, w, cs_in, u, a);
+      for (int32_t c = 0; c < C; ++c) da[c] = dy[t * C + c];
+      /* L2 backward: y = a / r, r = sqrt(sum a^2 + eps)
+       *   da = dy / r - a (a . dy) / r^3 */
+      for (int32_t h0 = 0; h0 < n_l2; h0 += dk) {
+        double ss = 0.0, ady = 0.0;
+        for (int32_t i = 0; i < dk; ++i) {
+          ss += a[h0 + i] * a[h0 + i];
+          ady += a[h0 + i] * dy[t * C + h0 + i];
+        }
+        double r2 = ss + eps, r = sqrt(r2);
+        for (int32_t i = 0; i < dk; ++i)
+          da[h0 + i] = dy[t * C + h0 + i] / r - a[h0 + i] * ady / (r2 * r);
+      }
+      for (int32_t c = 0; c < C; ++c) {
+        double sg = sigm(u[c]);
+        du[t * C + c] = da[c] * sg * (1.0 + u[c] * (1.0 - sg));
+      }
+      free(u);
+      free(a);
+      free(da);
+    }
+  }
+  /* gradient of input position p of sequence n (a token, or a state row) */
+  for (int32_t n = 0; n < N; ++n) {
+    int64_t t0 = cu[n], t1 = cu[n + 1];
+#pragma omp parallel for schedule(static)
+    for (int64_t p = t0 - (K - 1); p < t1; ++p) {
+      for (int32_t c = 0; c < C; ++c) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < K; ++j) {
+          int64_t t = p + (K - 1) - j;
+          if (t >= t0 && t < t1) acc += w[(int64_t)c * K + j] * du[t * C + c];
+        }
+        int64_t rf = p - (t1 - (K - 1));   /* row of the final state holding p */
+        if (dcs_out && rf >= 0) acc += dcs_out[((int64_t)n * (K - 1) + rf) * C + c];
+        if (p >= t0) dx[p * C + c] = acc;
+        else if (dcs_in) dcs_in[((int64_t)n * (K - 1) + (p - t0 + (K - 1))) * C + c] = acc;
+      }
+    }
+  }
+  /* dw[c][j] = sum over sequences, tokens t of du[t][c] x~[t-(K-1)+j][c] */
+#pragma omp parallel for schedule(static)
+  for (int32_t c = 0; c < C; ++c) {
+    for (int32_t j = 0; j < K; ++j) {
+      double acc = 0.0;
+      for (int32_t n = 0; n < N; ++n) {
+        int64_t t0 = cu[n], t1 = cu[n + 1];
+        for (int64_t t = t0; t < t1; ++t)
+          acc += du[t * C + c] * x_or_state(t - (K - 1) + j, t0, n, C, K, c, x, cs_in);
+      }
+      dw[(int64_t)c * K + j] = acc;
+    }
+  }
+  free(du);
+  return OR_OK;
+}
+
 /* Backward of oracle_conv_fwd.  dy: [T][C] -> dx: [T][C], dw: [C][K]. */
 int oracle_conv_bwd(int64_t T, int32_t C, int32_t K, const double* x, const double* w,
                     const int32_t* cu, int32_t N, int32_t n_l2, int32_t dk, double eps,

@@ -190,6 +190,106 @@ def test_conv_backward_finite_differences():
         np.testing.assert_allclose(grad, num, rtol=1e-7, atol=1e-8, err_msg=name)
 
 
+# ------------------------------------------------------------------ conv with a carried state
+def _state_case(seed, lens, hk=2, hv=3, d=4):
+    rng = np.random.default_rng(seed)
+    C = 2 * hk * d + hv * d
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    x = rng.standard_normal((T, C))
+    w = 0.3 * rng.standard_normal((C, 4))
+    cs = rng.standard_normal((len(lens), 3, C))
+    return x, w, cu, cs, 2 * hk * d, d
+
+
+def test_conv_state_zero_equals_stateless():
+    """No state (or a zero state) is the stateless convolution, exactly."""
+    x, w, cu, cs, n_l2, d = _state_case(30, [9, 1, 0, 14])
+    y0 = oracle.conv_fwd(x, w, cu, n_l2, d)
+    for cs_in in (None, np.zeros_like(cs)):
+        y, _ = oracle.conv_state_fwd(x, w, cu, n_l2, d, cs_in)
+        np.testing.assert_array_equal(y, y0)
+    dy = np.random.default_rng(31).standard_normal(x.shape)
+    dx0, dw0 = oracle.conv_bwd(x, w, cu, n_l2, d, dy)
+    dx, dw, _ = oracle.conv_state_bwd(x, w, cu, n_l2, d, dy)
+    np.testing.assert_allclose(dx, dx0, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(dw, dw0, rtol=1e-14, atol=1e-15)
+
+
+def test_conv_state_matches_numpy_convolve_with_state_prepended():
+    """Per channel the pre-activation is numpy.convolve over the state rows
+    followed by the sequence (the state stands for the three inputs before
+    it), and the final state is the last three inputs of that extended
+    sequence (reaching into the initial state for sequences shorter than
+    three)."""
+    x, w, cu, cs, n_l2, d = _state_case(32, [9, 2, 0, 1, 14])
+    y, cs_out = oracle.conv_state_fwd(x, w, cu, n_l2, d, cs)
+    C = x.shape[1]
+    for n in range(len(cu) - 1):
+        a, b = cu[n], cu[n + 1]
+        ext = np.concatenate([cs[n], x[a:b]], axis=0)            # [3 + L, C]
+        u = np.stack([np.convolve(ext[:, c], w[c, ::-1])[3: 3 + b - a] for c in range(C)], axis=1)
+        act = u * sp.expit(u)
+        qk = act[:, :n_l2].reshape(b - a, n_l2 // d, d)
+        nrm = np.sqrt((np.linalg.norm(qk, axis=-1, keepdims=True)) ** 2 + 1e-6)
+        ref = np.concatenate([(qk / nrm).reshape(b - a, n_l2), act[:, n_l2:]], axis=1)
+        np.testing.assert_allclose(y[a:b], ref, rtol=1e-12, atol=1e-14)
+        np.testing.assert_array_equal(cs_out[n], ext[-3:])
+
+
+@pytest.mark.parametrize("cut", [1, 2, 3, 7])
+def test_conv_state_continuation(cut):
+    """Splitting every sequence after `cut` tokens and feeding the first
+    call's final state to the second call reproduces the whole call: outputs
+    and final state exactly, and backward (the second call's state gradient
+    fed back as the first call's final-state gradient) the input and state
+    gradients, with dw the sum of the two calls'."""
+    lens = [12, 9, 15]
+    x, w, cu, cs, n_l2, d = _state_case(33 + cut, lens)
+    rng = np.random.default_rng(40 + cut)
+    dy = rng.standard_normal(x.shape)
+    dcs = rng.standard_normal(cs.shape)
+    y, cs_out = oracle.conv_state_fwd(x, w, cu, n_l2, d, cs)
+    dx, dw, dcs_in = oracle.conv_state_bwd(x, w, cu, n_l2, d, dy, cs, dcs)
+    ia = np.concatenate([np.arange(cu[n], cu[n] + cut) for n in range(len(lens))])
+    ib = np.concatenate([np.arange(cu[n] + cut, cu[n + 1]) for n in range(len(lens))])
+    cua = np.arange(len(lens) + 1, dtype=np.int32) * cut
+    cub = np.concatenate([[0], np.cumsum([ln - cut for ln in lens])]).astype(np.int32)
+    ya, csa = oracle.conv_state_fwd(x[ia], w, cua, n_l2, d, cs)
+    yb, csb = oracle.conv_state_fwd(x[ib], w, cub, n_l2, d, csa)
+    np.testing.assert_array_equal(np.concatenate([ya, yb])[np.argsort(np.concatenate([ia, ib]))], y)
+    np.testing.assert_array_equal(csb, cs_out)
+    dxb, dwb, dcsb = oracle.conv_state_bwd(x[ib], w, cub, n_l2, d, dy[ib], csa, dcs)
+    dxa, dwa, dcsa = oracle.conv_state_bwd(x[ia], w, cua, n_l2, d, dy[ia], cs, dcsb)
+    np.testing.assert_allclose(np.concatenate([dxa, dxb])[np.argsort(np.concatenate([ia, ib]))], dx,
+                               rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dcsa, dcs_in, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dwa + dwb, dw, rtol=1e-12, atol=1e-12)
+
+
+def test_conv_state_backward_finite_differences():
+    x, w, cu, cs, n_l2, d = _state_case(34, [5, 1, 0, 3], hk=1, hv=1, d=3)
+    rng = np.random.default_rng(35)
+    dy = rng.standard_normal(x.shape)
+    dcs = rng.standard_normal(cs.shape)
+    dx, dw, dcs_in = oracle.conv_state_bwd(x, w, cu, n_l2, d, dy, cs, dcs)
+
+    def L(x_, w_, cs_):
+        y, co = oracle.conv_state_fwd(x_, w_, cu, n_l2, d, cs_)
+        return float((y * dy).sum() + (co * dcs).sum())
+
+    h = 1e-6
+    for name, grad, idx in (("x", dx, 0), ("w", dw, 1), ("cs_in", dcs_in, 2)):
+        base = [x, w, cs]
+        num = np.zeros_like(grad)
+        for i in np.ndindex(grad.shape):
+            p, m = [a.copy() for a in base], [a.copy() for a in base]
+            p[idx][i] += h
+            m[idx][i] -= h
+            num[i] = (L(*p) - L(*m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-7, atol=1e-8, err_msg=name)
+
+
 # ------------------------------------------------------------------ whole layer
 def test_layer_backward_finite_differences():
     """Directional central differences through conv -> gate -> delta -> norm
