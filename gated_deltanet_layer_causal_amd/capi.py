@@ -27,7 +27,7 @@ GDN_BF16, GDN_FP32 = 0, 1
 GDN_ACT_SILU, GDN_ACT_SIGMOID = 0, 1
 EXPORTS = (
     "gdn_status_string", "gdn_conv_fwd", "gdn_conv_bwd", "gdn_conv_bwd_workspace",
-    "gdn_conv_bwd_noalloc", "gdn_gate_fwd",
+    "gdn_conv_bwd_noalloc", "gdn_conv_fwd_state", "gdn_conv_bwd_state", "gdn_gate_fwd",
     "gdn_gate_bwd", "gdn_gate_bwd_workspace", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace",
     "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd",
     "gdn_gated_norm_bwd_workspace", "gdn_chunk_prepare", "gdn_chunk_prepare_bwd",
@@ -77,6 +77,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_conv_fwd.argtypes = [SP, V, I64, V, V, c_int, F, V, I64, V]
     lib.gdn_conv_bwd.argtypes = [SP, V, I64, V, V, c_int, F, V, I64, V, I64, V, V, c_size_t, V]
     lib.gdn_conv_bwd_noalloc.argtypes = [SP, V, I64, V, V, c_int, F, V, I64, V, I64, V, V]
+    lib.gdn_conv_fwd_state.argtypes = [SP, V, I64, V, V, c_int, F, V, V, I64, V, V]
+    lib.gdn_conv_bwd_state.argtypes = [SP, V, I64, V, V, c_int, F, V, V, I64, V, V, I64, V, V, V,
+                                       c_size_t, V]
     lib.gdn_gate_fwd.argtypes = [SP, V, V, V, V, V, V, V]
     lib.gdn_gate_bwd.argtypes = [SP, V, V, V, V, V, V, V, V, V, V, V, c_size_t, V]
     lib.gdn_chunk_fwd.argtypes = [SP, V, V, V, I64, I64, I64, V, V, F, V, V, V, V, V, c_size_t, V]
@@ -99,7 +102,8 @@ def load(path: str = LIB_PATH):
         getattr(lib, name).restype = c_size_t
     lib.gdn_gated_norm_bwd_workspace.argtypes = [I64, c_int32]
     lib.gdn_gated_norm_bwd_workspace.restype = c_size_t
-    for name in ("gdn_conv_fwd", "gdn_conv_bwd", "gdn_conv_bwd_noalloc", "gdn_gate_fwd", "gdn_gate_bwd", "gdn_chunk_fwd",
+    for name in ("gdn_conv_fwd", "gdn_conv_bwd", "gdn_conv_bwd_noalloc", "gdn_conv_fwd_state",
+                 "gdn_conv_bwd_state", "gdn_gate_fwd", "gdn_gate_bwd", "gdn_chunk_fwd",
                  "gdn_chunk_bwd", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd", "gdn_chunk_prepare",
                  "gdn_chunk_prepare_bwd", "gdn_chunk_fwd_states", "gdn_chunk_fwd_states_save",
                  "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse",
@@ -259,6 +263,39 @@ def gdn_conv_bwd(shape, x, w, cu_seqlens, dy, dx, dw, ws, l2norm_qk=True, l2_eps
                                             int(l2norm_qk), l2_eps, _p(dy), _ld(dy), _p(dx),
                                             _ld(dx), _p(dw), _p(ws), ws.numel() if ws is not None else 0,
                                             _stream(stream)))
+
+
+def _conv_state(name, shape, t):
+    _need(name, t, _tdt(shape), shape.n_seq * 3 * (2 * shape.hk * shape.dk + shape.hv * shape.dv),
+          optional=True)
+
+
+def gdn_conv_fwd_state(shape, x, w, cu_seqlens, y, conv_state_in=None, conv_state_out=None,
+                       l2norm_qk=True, l2_eps=1e-6, stream=None):
+    C = _conv_ok(shape, x, w, cu_seqlens)
+    _rows("y", y, _tdt(shape), shape.total_tokens, C)
+    _conv_state("conv_state_in", shape, conv_state_in)
+    _conv_state("conv_state_out", shape, conv_state_out)
+    _ok("gdn_conv_fwd_state", load().gdn_conv_fwd_state(
+        byref(shape), _p(x), _ld(x), _p(w), _p(cu_seqlens), int(l2norm_qk), l2_eps,
+        _p(conv_state_in), _p(y), _ld(y), _p(conv_state_out), _stream(stream)))
+
+
+def gdn_conv_bwd_state(shape, x, w, cu_seqlens, dy, dx, dw, ws, conv_state_in=None,
+                       d_conv_state_out=None, d_conv_state_in=None, l2norm_qk=True, l2_eps=1e-6,
+                       stream=None):
+    C = _conv_ok(shape, x, w, cu_seqlens)
+    _rows("dy", dy, _tdt(shape), shape.total_tokens, C)
+    _rows("dx", dx, _tdt(shape), shape.total_tokens, C)
+    _need("dw", dw, torch.float32, C * 4)
+    for nm, t in (("conv_state_in", conv_state_in), ("d_conv_state_out", d_conv_state_out),
+                  ("d_conv_state_in", d_conv_state_in)):
+        _conv_state(nm, shape, t)
+    _ws(ws)
+    _ok("gdn_conv_bwd_state", load().gdn_conv_bwd_state(
+        byref(shape), _p(x), _ld(x), _p(w), _p(cu_seqlens), int(l2norm_qk), l2_eps,
+        _p(conv_state_in), _p(dy), _ld(dy), _p(d_conv_state_out), _p(dx), _ld(dx), _p(dw),
+        _p(d_conv_state_in), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 CONV_BWD_NOALLOC_MAX_BYTES = 32 << 20   # GDN_CONV_BWD_NOALLOC_MAX_BYTES in libgdn.h

@@ -79,8 +79,8 @@ gdn_status gdn_conv_fwd(const gdn_shape* s, const void* x, int64_t ldx, const fl
   GDN_TRY(check_ld(ldx, channels(s)));
   GDN_TRY(check_ld(ldy, channels(s)));
   if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
-  return launched(launch_conv_fwd(*s, x, ldx, w, cu, l2norm_qk != 0, l2_eps, y, ldy,
-                                  (hipStream_t)stream));
+  return launched(launch_conv_fwd(*s, x, ldx, w, cu, l2norm_qk != 0, l2_eps, y, ldy, nullptr,
+                                  nullptr, (hipStream_t)stream));
 }
 
 size_t gdn_conv_bwd_workspace(const gdn_shape* s) {
@@ -102,7 +102,42 @@ gdn_status gdn_conv_bwd(const gdn_shape* s, const void* x, int64_t ldx, const fl
   const size_t need = gdn_conv_bwd_workspace(s);
   if (need && (!ws || ws_bytes < need || !aligned16(ws))) return GDN_ERR_WORKSPACE;
   return launched(launch_conv_bwd(*s, x, ldx, w, cu, l2norm_qk != 0, l2_eps, dy, lddy, dx, lddx,
-                                  dw, (float*)ws, (hipStream_t)stream));
+                                  dw, (float*)ws, nullptr, nullptr, nullptr, (hipStream_t)stream));
+}
+
+gdn_status gdn_conv_fwd_state(const gdn_shape* s, const void* x, int64_t ldx, const float* w,
+                              const int32_t* cu, int l2norm_qk, float l2_eps,
+                              const void* conv_state_in, void* y, int64_t ldy,
+                              void* conv_state_out, void* stream) {
+  GDN_TRY(check_shape(s));
+  GDN_TRY(check_ptrs({x, w, cu, y}));
+  GDN_TRY(check_ld(ldx, channels(s)));
+  GDN_TRY(check_ld(ldy, channels(s)));
+  if ((conv_state_in && !aligned16(conv_state_in)) || (conv_state_out && !aligned16(conv_state_out)))
+    return GDN_ERR_ALIGNMENT;
+  if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  return launched(launch_conv_fwd(*s, x, ldx, w, cu, l2norm_qk != 0, l2_eps, y, ldy, conv_state_in,
+                                  conv_state_out, (hipStream_t)stream));
+}
+
+gdn_status gdn_conv_bwd_state(const gdn_shape* s, const void* x, int64_t ldx, const float* w,
+                              const int32_t* cu, int l2norm_qk, float l2_eps,
+                              const void* conv_state_in, const void* dy, int64_t lddy,
+                              const void* d_conv_state_out, void* dx, int64_t lddx, float* dw,
+                              void* d_conv_state_in, void* ws, size_t ws_bytes, void* stream) {
+  GDN_TRY(check_shape(s));
+  GDN_TRY(check_ptrs({x, w, cu, dy, dx, dw}));
+  GDN_TRY(check_ld(ldx, channels(s)));
+  GDN_TRY(check_ld(lddy, channels(s)));
+  GDN_TRY(check_ld(lddx, channels(s)));
+  for (const void* p : {conv_state_in, d_conv_state_out, (const void*)d_conv_state_in})
+    if (p && !aligned16(p)) return GDN_ERR_ALIGNMENT;
+  if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  const size_t need = gdn_conv_bwd_workspace(s);
+  if (need && (!ws || ws_bytes < need || !aligned16(ws))) return GDN_ERR_WORKSPACE;
+  return launched(launch_conv_bwd(*s, x, ldx, w, cu, l2norm_qk != 0, l2_eps, dy, lddy, dx, lddx,
+                                  dw, (float*)ws, conv_state_in, d_conv_state_out, d_conv_state_in,
+                                  (hipStream_t)stream));
 }
 
 gdn_status gdn_conv_bwd_noalloc(const gdn_shape* s, const void* x, int64_t ldx, const float* w,

@@ -84,12 +84,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_of(const T* base, int64_t
   return buffer_of(base + lo * ld, (uint32_t)(hi > lo ? hi - lo : 0) * ldb);
 }
 
-template <typename T, int D>
+// HAS_STATE: cs_in [n_seq][3][C] holds the three input rows before each
+// sequence (the carried conv state), read where a window reaches before the
+// sequence start instead of the zero padding.
+template <typename T, int D, bool HAS_STATE>
 __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_fwd_kernel(const T* __restrict__ x, int64_t ldx,
                                                        const float* __restrict__ w,
                                                        const int32_t* __restrict__ cu, int n_seq,
                                                        int64_t T_tok, int tt, int C, int n_l2, float eps,
-                                                       T* __restrict__ y, int64_t ldy) {
+                                                       T* __restrict__ y, int64_t ldy,
+                                                       const T* __restrict__ cs_in) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   const bool active = c0 < C;
@@ -117,11 +121,21 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_fwd_kernel(cons
       const int64_t lo = a - 3 > ss ? a - 3 : ss;
       const auto rx = rows_of(x, ldx, lo, b, ldxb);
       const auto ry = rows_of(y, ldy, a, b, ldyb);
+      // the rows before the piece: x, or (before the sequence start) the
+      // carried state rows of sequence n, or the zero padding
+      auto prev = [&](int64_t t) __attribute__((always_inline)) -> f8 {
+        if constexpr (HAS_STATE) {
+          if (t < ss)
+            return row8<T>(buffer_of(cs_in + (int64_t)n * 3 * C, 3u * (uint32_t)C * sizeof(T)),
+                           t - ss + 3, (uint32_t)C * sizeof(T), coff);
+        }
+        return row8<T>(rx, t - lo, ldxb, coff);
+      };
       f8 xs[4];        // x[u] in slot (u - u0) mod 4
       Raw8<T> px[4];   // x[u + 4] in slot (u - u0) mod 4: rows load a group ahead
-      xs[3] = row8<T>(rx, a - 1 - lo, ldxb, coff);
-      xs[2] = row8<T>(rx, a - 2 - lo, ldxb, coff);
-      xs[1] = row8<T>(rx, a - 3 - lo, ldxb, coff);
+      xs[3] = prev(a - 1);
+      xs[2] = prev(a - 2);
+      xs[1] = prev(a - 3);
 #pragma unroll
       for (int m = 0; m < 4; ++m) px[m] = raw_row8<T>(rx, a + m - lo, ldxb, coff);
       auto token = [&](const int m, const int64_t t) __attribute__((always_inline)) {
@@ -190,12 +204,17 @@ __device__ __forceinline__ f8 conv_du(const float (&wr)[8][4], const f8& x0, con
   return du;
 }
 
-template <typename T, int D>
+// HAS_STATE: windows reaching before a sequence start read the carried state
+// rows cs_in [n_seq][3][C], and dcs_out [n_seq][3][C] (nullable), the
+// gradient of the final state (the last three input rows of each sequence),
+// adds to dx of those rows.  The gradient of cs_in itself comes from
+// conv_state_dgrad_kernel.
+template <typename T, int D, bool HAS_STATE>
 __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
     const T* __restrict__ x, int64_t ldx, const float* __restrict__ w,
     const int32_t* __restrict__ cu, int n_seq, int64_t T_tok, int tt, int C, int n_l2, float eps,
     const T* __restrict__ dy, int64_t lddy, T* __restrict__ dx, int64_t lddx,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, const T* __restrict__ cs_in, const T* __restrict__ dcs_out) {
   __shared__ float red[CONV_RUNS_PER_BLOCK][64][33];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
@@ -233,7 +252,15 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
         const auto rx = rows_of(x, ldx, lo, hi, ldxb);
         const auto ry = rows_of(dy, lddy, a, hi, ldyb);
         const auto ro = rows_of(dx, lddx, a, b, ldob);
-        auto xr = [&](int64_t t) __attribute__((always_inline)) { return row8<T>(rx, t - lo, ldxb, coff); };
+        const uint32_t ldsb = (uint32_t)C * sizeof(T);
+        // x rows, or (before the sequence start) the carried state rows
+        auto xraw = [&](int64_t t) __attribute__((always_inline)) -> Raw8<T> {
+          if constexpr (HAS_STATE) {
+            if (t < ss) return raw_row8<T>(buffer_of(cs_in + (int64_t)n * 3 * C, 3u * ldsb), t - ss + 3, ldsb, coff);
+          }
+          return raw_row8<T>(rx, t - lo, ldxb, coff);
+        };
+        auto xr = [&](int64_t t) __attribute__((always_inline)) { return raw_f8(xraw(t)); };
         // du at b, b + 1, b + 2 (the tokens after the piece) in slots 3, 2, 1
         f8 xs[4], ds[4];
 #pragma unroll
@@ -254,7 +281,7 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           xs[j] = xr(b - 1 - j);
-          px[j] = raw_row8<T>(rx, b - 5 - j - lo, ldxb, coff);
+          px[j] = xraw(b - 5 - j);
           pd[j] = raw_row8<T>(ry, b - 1 - j - a, ldyb, coff);
         }
         auto token = [&](const int m, const int64_t s) __attribute__((always_inline)) {
@@ -273,10 +300,18 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
             dwa[i][2] += d0.v[i] * x1.v[i];
             dwa[i][3] += d0.v[i] * x0.v[i];
           }
+          if constexpr (HAS_STATE) {
+            // the last three rows also feed the final state
+            if (dcs_out && s >= se - 3) {
+              const f8 gf = row8<T>(buffer_of(dcs_out + (int64_t)n * 3 * C, 3u * ldsb), s - se + 3, ldsb, coff);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) o.v[i] += gf.v[i];
+            }
+          }
           put_row8<T>(ro, s - a, ldob, coff, o);
           ds[m] = d0;
           xs[m] = raw_f8(px[m]);
-          px[m] = raw_row8<T>(rx, s - 8 - lo, ldxb, coff);
+          px[m] = xraw(s - 8);
         };
         // whole groups of four with no per-token test, then the last one to
         // three tokens
@@ -308,6 +343,89 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
       for (int r = 1; r < CONV_RUNS_PER_BLOCK; ++r) acc += red[r][lane][e];
       out[e] = acc;
     }
+  }
+}
+
+// The final conv state: cs_out[n][r] = the input row at position
+// cu[n + 1] - 3 + r, from x, or from cs_in (zeros when null) where that
+// position precedes the sequence start.  One wave per (sequence, row, 512
+// channels), 16-byte copies.
+template <typename T>
+__global__ void __launch_bounds__(64) conv_state_out_kernel(const T* __restrict__ x, int64_t ldx,
+                                                            const int32_t* __restrict__ cu, int C,
+                                                            const T* __restrict__ cs_in,
+                                                            T* __restrict__ cs_out) {
+  const int n = blockIdx.x, r = blockIdx.y, c0 = (blockIdx.z * 64 + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  const int64_t ss = cu[n], se = cu[n + 1], t = se - 3 + r;
+  Raw8<T> v;
+  if (t >= ss) v = ld_raw8(x + t * ldx + c0);
+  else if (cs_in) v = ld_raw8(cs_in + ((int64_t)n * 3 + (t - ss + 3)) * C + c0);
+  else v = zero_raw8<T>();
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i)
+    reinterpret_cast<uint4*>(cs_out + ((int64_t)n * 3 + r) * C + c0)[i] = v.v[i];
+}
+
+// Gradient of the carried state: input position p = cu[n] - 3 + r feeds u at
+// tokens cu[n] + r - j through tap j, and the final state when the sequence
+// is shorter than 3 - r.  du of the first three tokens is recomputed here from
+// their windows (state rows included) and dy.  One wave per (sequence, 512
+// channels), as the conv kernels lay out lanes.
+template <typename T, int D>
+__global__ void __launch_bounds__(64) conv_state_dgrad_kernel(
+    const T* __restrict__ x, int64_t ldx, const float* __restrict__ w,
+    const int32_t* __restrict__ cu, int C, int n_l2, float eps, const T* __restrict__ cs_in,
+    const T* __restrict__ dy, int64_t lddy, const T* __restrict__ dcs_out, T* __restrict__ dcs_in) {
+  const int lane = threadIdx.x, n = blockIdx.x;
+  const int c0 = (blockIdx.y * 64 + lane) * 8;
+  const bool active = c0 < C, l2 = c0 < n_l2;
+  const uint32_t coff = active ? (uint32_t)c0 * sizeof(T) : 0x80000000u;
+  const uint32_t ldxb = (uint32_t)(ldx * sizeof(T)), ldyb = (uint32_t)(lddy * sizeof(T));
+  const uint32_t ldsb = (uint32_t)C * sizeof(T);
+  const int64_t ss = uniform_i32(cu[n]), se = uniform_i32(cu[n + 1]);
+  const int64_t L = se - ss;
+  float wr[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wr[i][j] = active ? w[(int64_t)(c0 + i) * 4 + j] : 0.f;
+  const auto rx = rows_of(x, ldx, ss, se, ldxb);
+  const auto ry = rows_of(dy, lddy, ss, se, ldyb);
+  const auto rst = buffer_of(cs_in + (int64_t)n * 3 * C, cs_in ? 3u * ldsb : 0u);
+  auto xrow = [&](int64_t t) __attribute__((always_inline)) -> f8 {
+    return t >= ss ? row8<T>(rx, t - ss, ldxb, coff) : row8<T>(rst, t - ss + 3, ldsb, coff);
+  };
+  f8 du[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int64_t t = ss + k;
+    if (k < L) {   // wave-uniform
+      du[k] = conv_du<D>(wr, xrow(t), xrow(t - 1), xrow(t - 2), xrow(t - 3), row8<T>(ry, t - ss, ldyb, coff),
+                         l2, eps);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) du[k].v[i] = 0.f;
+    }
+  }
+  const auto rdo = buffer_of(dcs_out + (int64_t)n * 3 * C, dcs_out ? 3u * ldsb : 0u);
+  const auto rdi = buffer_of(dcs_in + (int64_t)n * 3 * C, 3u * ldsb);
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    f8 gsum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j <= r; ++j) acc += wr[i][j] * du[r - j].v[i];
+      gsum.v[i] = acc;
+    }
+    if (r >= L) {   // the position also sits in the final state
+      const f8 gf = row8<T>(rdo, r - L, ldsb, coff);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gsum.v[i] += gf.v[i];
+    }
+    put_row8<T>(rdi, r, ldsb, coff, gsum);
   }
 }
 
@@ -362,33 +480,72 @@ hipError_t launch_reduce_partials(const float* partials, int64_t n_part, int64_t
 template <typename T, int D>
 static hipError_t conv_fwd_t(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
                              const int32_t* cu, int l2, float eps, void* y, int64_t ldy,
-                             hipStream_t st) {
+                             const void* cs_in, void* cs_out, hipStream_t st) {
   const int C = 2 * s.hk * s.dk + s.hv * s.dv;
   const int n_l2 = l2 ? 2 * s.hk * s.dk : 0;
   const int64_t nT = s.total_tokens;
-  if (nT == 0) return hipSuccess;
-  const int tt = conv_tt(nT, C);
-  dim3 grid((unsigned)conv_partials(nT, tt), (C / 8 + 63) / 64);
-  hipLaunchKernelGGL((conv_fwd_kernel<T, D>), grid, dim3(64 * CONV_RUNS_PER_BLOCK), 0, st, (const T*)x, ldx, w, cu,
-                     s.n_seq, nT, tt, C, n_l2, eps, (T*)y, ldy);
+  if (nT > 0) {
+    const int tt = conv_tt(nT, C);
+    dim3 grid((unsigned)conv_partials(nT, tt), (C / 8 + 63) / 64);
+    auto kern = cs_in ? conv_fwd_kernel<T, D, true> : conv_fwd_kernel<T, D, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * CONV_RUNS_PER_BLOCK), 0, st, (const T*)x, ldx, w, cu,
+                       s.n_seq, nT, tt, C, n_l2, eps, (T*)y, ldy, (const T*)cs_in);
+  }
+  if (cs_out)
+    hipLaunchKernelGGL(conv_state_out_kernel<T>, dim3(s.n_seq, 3, (C / 8 + 63) / 64), dim3(64), 0,
+                       st, (const T*)x, ldx, cu, C, (const T*)cs_in, (T*)cs_out);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t conv_bwd_t(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
                              const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
-                             void* dx, int64_t lddx, float* dw, float* partials, hipStream_t st) {
+                             void* dx, int64_t lddx, float* dw, float* partials,
+                             const void* cs_in, const void* dcs_out, void* dcs_in,
+                             hipStream_t st) {
   const int C = 2 * s.hk * s.dk + s.hv * s.dv;
   const int n_l2 = l2 ? 2 * s.hk * s.dk : 0;
   const int64_t nT = s.total_tokens;
   const int tt = conv_tt(nT, C);
   const int64_t np = conv_partials(nT, tt);
+  const bool stateful = cs_in || dcs_out || dcs_in;
   if (nT > 0) {
     dim3 grid((unsigned)np, (C / 8 + 63) / 64);
-    hipLaunchKernelGGL((conv_bwd_kernel<T, D>), grid, dim3(64 * CONV_RUNS_PER_BLOCK), 0, st, (const T*)x, ldx, w, cu,
-                       s.n_seq, nT, tt, C, n_l2, eps, (const T*)dy, lddy, (T*)dx, lddx, partials);
+    auto kern = stateful ? conv_bwd_kernel<T, D, true> : conv_bwd_kernel<T, D, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * CONV_RUNS_PER_BLOCK), 0, st, (const T*)x, ldx, w, cu,
+                       s.n_seq, nT, tt, C, n_l2, eps, (const T*)dy, lddy, (T*)dx, lddx, partials,
+                       (const T*)cs_in, (const T*)dcs_out);
   }
+  if (dcs_in)
+    hipLaunchKernelGGL((conv_state_dgrad_kernel<T, D>), dim3(s.n_seq, (C / 8 + 63) / 64), dim3(64), 0,
+                       st, (const T*)x, ldx, w, cu, C, n_l2, eps, (const T*)cs_in, (const T*)dy,
+                       lddy, (const T*)dcs_out, (T*)dcs_in);
   return launch_reduce_partials(partials, np, (int64_t)C * 4, dw, st);
+}
+
+hipError_t launch_conv_fwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
+                           const int32_t* cu, int l2, float eps, void* y, int64_t ldy,
+                           const void* cs_in, void* cs_out, hipStream_t st) {
+  if (s.dtype == GDN_BF16)
+    return s.dk == 128 ? conv_fwd_t<bf16, 128>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st)
+                       : conv_fwd_t<bf16, 32>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st);
+  return s.dk == 128 ? conv_fwd_t<float, 128>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st)
+                     : conv_fwd_t<float, 32>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st);
+}
+
+hipError_t launch_conv_bwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
+                           const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
+                           void* dx, int64_t lddx, float* dw, float* partials, const void* cs_in,
+                           const void* dcs_out, void* dcs_in, hipStream_t st) {
+  if (s.dtype == GDN_BF16)
+    return s.dk == 128 ? conv_bwd_t<bf16, 128>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw,
+                                                partials, cs_in, dcs_out, dcs_in, st)
+                       : conv_bwd_t<bf16, 32>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw,
+                                               partials, cs_in, dcs_out, dcs_in, st);
+  return s.dk == 128 ? conv_bwd_t<float, 128>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw,
+                                               partials, cs_in, dcs_out, dcs_in, st)
+                     : conv_bwd_t<float, 32>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw,
+                                              partials, cs_in, dcs_out, dcs_in, st);
 }
 
 // ---- the conv backward without a workspace argument -------------------------
@@ -432,29 +589,8 @@ hipError_t launch_conv_bwd_noalloc(const gdn_shape& s, const void* x, int64_t ld
   float* partials = nullptr;
   const hipError_t e = scratch_of_current_device(&partials);
   if (e != hipSuccess) return e;
-  return launch_conv_bwd(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw, partials, st);
-}
-
-hipError_t launch_conv_fwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
-                           const int32_t* cu, int l2, float eps, void* y, int64_t ldy,
-                           hipStream_t st) {
-  if (s.dtype == GDN_BF16)
-    return s.dk == 128 ? conv_fwd_t<bf16, 128>(s, x, ldx, w, cu, l2, eps, y, ldy, st)
-                       : conv_fwd_t<bf16, 32>(s, x, ldx, w, cu, l2, eps, y, ldy, st);
-  return s.dk == 128 ? conv_fwd_t<float, 128>(s, x, ldx, w, cu, l2, eps, y, ldy, st)
-                     : conv_fwd_t<float, 32>(s, x, ldx, w, cu, l2, eps, y, ldy, st);
-}
-
-hipError_t launch_conv_bwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
-                           const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
-                           void* dx, int64_t lddx, float* dw, float* partials, hipStream_t st) {
-  if (s.dtype == GDN_BF16)
-    return s.dk == 128
-               ? conv_bwd_t<bf16, 128>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw, partials, st)
-               : conv_bwd_t<bf16, 32>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw, partials, st);
-  return s.dk == 128
-             ? conv_bwd_t<float, 128>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw, partials, st)
-             : conv_bwd_t<float, 32>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw, partials, st);
+  return launch_conv_bwd(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw, partials, nullptr,
+                         nullptr, nullptr, st);
 }
 
 }  // namespace gdn

@@ -34,12 +34,14 @@ inline int64_t conv_partials(int64_t T, int tt) {
   return (conv_runs(T, tt) + CONV_RUNS_PER_BLOCK - 1) / CONV_RUNS_PER_BLOCK;
 }
 
+// cs_in, cs_out, dcs_out, dcs_in: carried conv states [n_seq][3][C] (nullable)
 hipError_t launch_conv_fwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
                            const int32_t* cu, int l2, float eps, void* y, int64_t ldy,
-                           hipStream_t st);
+                           const void* cs_in, void* cs_out, hipStream_t st);
 hipError_t launch_conv_bwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
                            const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
-                           void* dx, int64_t lddx, float* dw, float* partials, hipStream_t st);
+                           void* dx, int64_t lddx, float* dw, float* partials, const void* cs_in,
+                           const void* dcs_out, void* dcs_in, hipStream_t st);
 
 constexpr size_t CONV_BWD_NOALLOC_MAX_BYTES = GDN_CONV_BWD_NOALLOC_MAX_BYTES;
 // the conv backward into the library's own scratch (no workspace argument);

@@ -92,7 +92,13 @@ class GDNCore:
         return q, k, v
 
     def forward(self, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, S0=None,
-                want_final=False, timer=None, save_states=True):
+                want_final=False, timer=None, save_states=True, conv_state=None,
+                want_conv_state=False):
+        """conv_state [n_seq, 3, C] (optional): the carried conv state, the
+        three input rows before each sequence; with want_conv_state the
+        returned dict holds the final one under "conv_state_out" (the last
+        three input rows of each sequence), so that a later call continues
+        the sequences (feed S_final and conv_state_out back in)."""
         c = self.cfg
         T = x.shape[0]
         n_seq = cu_seqlens.numel() - 1
@@ -101,8 +107,14 @@ class GDNCore:
         wc = self.chunk_workspace(sh, fresh=save_states)
         dev, dt = x.device, c.dtype
         y = torch.empty((T, c.channels), dtype=dt, device=dev)
+        cs_out = (torch.empty((n_seq, 3, c.channels), dtype=dt, device=dev) if want_conv_state
+                  else None)
         with _timed(timer, "conv_fwd"):
-            L.gdn_conv_fwd(sh, x, w_conv, cu_seqlens, y, True, c.l2_eps)
+            if conv_state is None and cs_out is None:
+                L.gdn_conv_fwd(sh, x, w_conv, cu_seqlens, y, True, c.l2_eps)
+            else:
+                L.gdn_conv_fwd_state(sh, x, w_conv, cu_seqlens, y, conv_state, cs_out, True,
+                                     c.l2_eps)
         g = torch.empty((T, c.hv), dtype=torch.float32, device=dev)
         beta = torch.empty_like(g)
         with _timed(timer, "gate_fwd"):
@@ -123,13 +135,17 @@ class GDNCore:
         out = torch.empty_like(o)
         with _timed(timer, "norm_fwd"):
             L.gdn_gated_norm_fwd(o, z, w_norm, out, c.norm_eps, c.act)
-        saved = {"y": y, "g": g, "beta": beta, "o": o, "out": out, "S_final": Sf}
+        saved = {"y": y, "g": g, "beta": beta, "o": o, "out": out, "S_final": Sf,
+                 "conv_state_out": cs_out}
         if save_states:
             saved["chunk_ws"] = wc
         return saved
 
     def backward(self, saved, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, dout,
-                 S0=None, dS_final=None, timer=None):
+                 S0=None, dS_final=None, timer=None, conv_state=None, d_conv_state=None):
+        """conv_state: the forward's; d_conv_state: the gradient of its final
+        conv state.  With either, the result holds "d_conv_state" (the
+        gradient of the carried conv state that came in)."""
         c = self.cfg
         T = x.shape[0]
         n_seq = cu_seqlens.numel() - 1
@@ -169,11 +185,17 @@ class GDNCore:
             L.gdn_gate_bwd(sh, a, b, A_log, dt_bias, dg, dbeta, da, db, dA_log, ddt, ws)
         dx = torch.empty((T, c.channels), dtype=dt, device=dev)
         dw_conv = torch.empty((c.channels, 4), dtype=torch.float32, device=dev)
+        dcs_in = None
         with _timed(timer, "conv_bwd"):
-            L.gdn_conv_bwd(sh, x, w_conv, cu_seqlens, dy, dx, dw_conv, ws, True, c.l2_eps)
+            if conv_state is None and d_conv_state is None:
+                L.gdn_conv_bwd(sh, x, w_conv, cu_seqlens, dy, dx, dw_conv, ws, True, c.l2_eps)
+            else:
+                dcs_in = torch.empty((n_seq, 3, c.channels), dtype=dt, device=dev)
+                L.gdn_conv_bwd_state(sh, x, w_conv, cu_seqlens, dy, dx, dw_conv, ws, conv_state,
+                                     d_conv_state, dcs_in, True, c.l2_eps)
         return {"do": do, "dz": dz, "dw_norm": dw_norm, "dy_conv": dy, "dg": dg, "dbeta": dbeta,
                 "dS0": dS0, "da": da, "db": db, "dA_log": dA_log, "ddt_bias": ddt, "dx": dx,
-                "dw_conv": dw_conv}
+                "dw_conv": dw_conv, "d_conv_state": dcs_in}
 
 
 class GDNLayer:

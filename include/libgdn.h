@@ -96,6 +96,33 @@ gdn_status gdn_conv_bwd(const gdn_shape* shape, const void* x, int64_t ldx, cons
                         size_t ws_bytes, void* stream);
 size_t gdn_conv_bwd_workspace(const gdn_shape* shape);
 
+/* The convolution with a carried conv state, so that a sequence can be fed in
+ * pieces over several calls (prime-rl page, "Summary": causal_conv1d with
+ * initial_state and output_final_state).  The state of sequence n is the
+ * three input rows just before its first token, oldest first, in the
+ * storage type: conv_state [n_seq][3][C_ch] (dense rows of C_ch channels,
+ * 16-byte aligned).  conv_state_in (NULL: zeros, as gdn_conv_fwd) stands for
+ * x at positions cu[n] - 3 .. cu[n] - 1; conv_state_out (NULL: not written)
+ * receives the input rows at positions cu[n+1] - 3 .. cu[n+1] - 1, taken from
+ * conv_state_in where a sequence is shorter than three tokens (an empty one
+ * passes its state through).  Feeding conv_state_out of one call as
+ * conv_state_in of the next continues every sequence exactly.  Other
+ * arguments as gdn_conv_fwd. */
+gdn_status gdn_conv_fwd_state(const gdn_shape* shape, const void* x, int64_t ldx, const float* w,
+                              const int32_t* cu_seqlens, int l2norm_qk, float l2_eps,
+                              const void* conv_state_in, void* y, int64_t ldy,
+                              void* conv_state_out, void* stream);
+
+/* Backward of gdn_conv_fwd_state: dy and d_conv_state_out (the gradient of
+ * conv_state_out; NULL: zero) -> dx, dw and d_conv_state_in (the gradient of
+ * conv_state_in, [n_seq][3][C_ch] in the storage type; NULL: not written).
+ * conv_state_in must be the forward's.  Workspace as gdn_conv_bwd. */
+gdn_status gdn_conv_bwd_state(const gdn_shape* shape, const void* x, int64_t ldx, const float* w,
+                              const int32_t* cu_seqlens, int l2norm_qk, float l2_eps,
+                              const void* conv_state_in, const void* dy, int64_t lddy,
+                              const void* d_conv_state_out, void* dx, int64_t lddx, float* dw,
+                              void* d_conv_state_in, void* ws, size_t ws_bytes, void* stream);
+
 /* gdn_conv_bwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments and results as gdn_conv_bwd, without the workspace: its

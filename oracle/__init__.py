@@ -246,14 +246,19 @@ def layer_fwd(inp: dict, hk: int, hv: int, d: int, scale: float, act: int = ACT_
     the storage dtype.  Returns a dict of every intermediate."""
     rf = (lambda a: a) if round_fn is None else round_fn
     cu = inp["cu_seqlens"]
-    y = rf(conv_fwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d))
+    cs_out = None
+    if inp.get("conv_state") is not None:    # carried conv state in and out
+        y, cs_out = conv_state_fwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d, inp["conv_state"])
+        y = rf(y)
+    else:
+        y = rf(conv_fwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d))
     q, k, v = _split(y, hk, hv, d)
     g, beta = gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
     o, Sf = delta_fwd(q, k, v, g, beta, cu, scale, inp.get("S0"))
     o = rf(o)
     out = norm_fwd(o, inp["z"], inp["w_norm"], act)
     return {"y": y, "q": q, "k": k, "v": v, "g": g, "beta": beta, "o": o, "S_final": Sf,
-            "out": out}
+            "out": out, "conv_state_out": cs_out}
 
 
 def layer_bwd(inp: dict, fwd: dict, hk: int, hv: int, d: int, scale: float, act: int = ACT_SILU,
@@ -270,10 +275,16 @@ def layer_bwd(inp: dict, fwd: dict, hk: int, hv: int, d: int, scale: float, act:
                                            scale, do, inp.get("S0"), inp.get("dS_T"))
     dy_conv = rf(np.concatenate([dq.reshape(T, -1), dk.reshape(T, -1), dv.reshape(T, -1)], axis=1))
     da, db, dA_log, ddt_bias = gate_bwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], dg, dbeta)
-    dx, dw_conv = conv_bwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d, dy_conv)
+    dcs_in = None
+    if inp.get("conv_state") is not None:    # carried conv state (and its gradient d_conv_state)
+        dx, dw_conv, dcs_in = conv_state_bwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d, dy_conv,
+                                             inp["conv_state"], inp.get("d_conv_state"))
+    else:
+        dx, dw_conv = conv_bwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d, dy_conv)
     return {"do": do, "dz": dz, "dw_norm": dw_norm, "dq": dq, "dk": dk, "dv": dv, "dg": dg,
             "dbeta": dbeta, "dS0": dS0, "dy_conv": dy_conv, "da": da, "db": db,
-            "dA_log": dA_log, "ddt_bias": ddt_bias, "dx": dx, "dw_conv": dw_conv}
+            "dA_log": dA_log, "ddt_bias": ddt_bias, "dx": dx, "dw_conv": dw_conv,
+            "d_conv_state": dcs_in}
 
 
 # ---------------------------------------------------------------------------

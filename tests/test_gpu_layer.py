@@ -121,3 +121,85 @@ def test_layer_with_projections_matches_oracle():
     print("projections", " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
     for k, t, r, tol in checks:
         assert_close(k, host(t).reshape(np.shape(r)), r, tol)
+
+
+SPLIT_CASES = {
+    # name: workload, lengths, cut per sequence (tokens in the first call), A range
+    "bf16": (gi.Workload("sc", 0, 2, 4, 128, "bf16", seq="varlen", init_state=True,
+                         final_state=True, seed=83), [300, 130, 5], [170, 2, 5], (0.02, 0.3)),
+    "fp32": (gi.Workload("scf", 0, 1, 2, 32, "fp32", seq="varlen", init_state=True,
+                         final_state=True, seed=84), [90, 40], [1, 37], (0.02, 0.3)),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_layer_split_and_continue(name):
+    """A pack fed in two calls, each carrying the recurrent state and the
+    conv state into the next (and, backward, their gradients back), against
+    the oracle's single call over the whole pack: outputs and input
+    gradients concatenate, parameter gradients add up, and the gradients of
+    the initial states come out of the first call.  Cuts fall inside chunks
+    and inside the conv window (a piece of 1 or 2 tokens)."""
+    w, lens, cuts, A_range = SPLIT_CASES[name]
+    inp = gi.make_inputs(w, seqlens=lens, A_range=A_range)
+    bf = w.dtype == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+    rf = gi.round_bf16 if bf else None
+    rng = np.random.default_rng(85)
+    C = w.channels
+    cs0 = rng.standard_normal((len(lens), 3, C)).astype(np.float32)
+    dcs = rng.standard_normal((len(lens), 3, C)).astype(np.float32)
+    if bf:
+        cs0, dcs = gi.round_bf16(cs0), gi.round_bf16(dcs)
+    cu = inp["cu_seqlens"]
+    parts = []
+    for first in (True, False):
+        idx = np.concatenate([np.arange(cu[n], cu[n] + cuts[n]) if first else
+                              np.arange(cu[n] + cuts[n], cu[n + 1]) for n in range(len(lens))])
+        plens = [cuts[n] if first else lens[n] - cuts[n] for n in range(len(lens))]
+        parts.append((idx, gi.cu_from_lengths(plens)))
+    core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=tdt), device=DEV)
+
+    def targs(idx, pcu):
+        return (dev(inp["x"][idx], tdt), dev(inp["w_conv"]), dev(inp["a"][idx], tdt),
+                dev(inp["b"][idx], tdt), dev(inp["A_log"]), dev(inp["dt_bias"]),
+                dev(inp["z"][idx], tdt), dev(inp["w_norm"]), torch.from_numpy(pcu).to(DEV))
+
+    a_args, b_args = targs(*parts[0]), targs(*parts[1])
+    fa = core.forward(*a_args, S0=dev(inp["S0"]), want_final=True, conv_state=dev(cs0, tdt),
+                      want_conv_state=True)
+    fb = core.forward(*b_args, S0=fa["S_final"], want_final=True, conv_state=fa["conv_state_out"],
+                      want_conv_state=True)
+    ia, ib = parts[0][0], parts[1][0]
+    gb = core.backward(fb, *b_args, dev(inp["dy"][ib], tdt), S0=fa["S_final"],
+                       dS_final=dev(inp["dS_T"]), conv_state=fa["conv_state_out"],
+                       d_conv_state=dev(dcs, tdt))
+    ga = core.backward(fa, *a_args, dev(inp["dy"][ia], tdt), S0=dev(inp["S0"]), dS_final=gb["dS0"],
+                       conv_state=dev(cs0, tdt), d_conv_state=gb["d_conv_state"])
+    torch.cuda.synchronize()
+
+    whole = dict(inp, conv_state=cs0, d_conv_state=dcs)
+    sc = w.d ** -0.5
+    rfw = oracle.layer_fwd(whole, w.hk, w.hv, w.d, sc, round_fn=rf)
+    rbw = oracle.layer_bwd(whole, rfw, w.hk, w.hv, w.d, sc, round_fn=rf)
+    order = np.argsort(np.concatenate([ia, ib]))
+
+    def cat(k, a, b):
+        return np.concatenate([host(a[k]).reshape(len(ia), -1), host(b[k]).reshape(len(ib), -1)])[order]
+
+    ft = FWD_TOL_BF16 if bf else TOL_FP32
+    gt = GRAD_TOL_BF16 if bf else TOL_FP32
+    checks = [("out", cat("out", fa, fb), rfw["out"].reshape(len(order), -1), ft),
+              ("S_final", host(fb["S_final"]), rfw["S_final"], ft),
+              ("conv_state_out", host(fb["conv_state_out"]), rfw["conv_state_out"], ft),
+              ("dx", cat("dx", ga, gb), rbw["dx"], gt),
+              ("dz", cat("dz", ga, gb), rbw["dz"].reshape(len(order), -1), gt),
+              ("da", cat("da", ga, gb), rbw["da"], gt), ("db", cat("db", ga, gb), rbw["db"], gt),
+              ("dS0", host(ga["dS0"]), rbw["dS0"], gt),
+              ("d_conv_state", host(ga["d_conv_state"]), rbw["d_conv_state"], gt)]
+    for k in ("dw_conv", "dw_norm", "dA_log", "ddt_bias"):
+        checks.append((k, host(ga[k]) + host(gb[k]), rbw[k], gt))
+    errs = {k: rel_err(g_, r) for k, g_, r, _ in checks}
+    print(name, " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    for k, g_, r, tol in checks:
+        assert_close(k, g_, r, tol)

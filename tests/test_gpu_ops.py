@@ -291,3 +291,44 @@ def test_chunk_large_values_and_state(flow):
     print(flow, " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
     for k in refs:
         assert_close(k, got[k], refs[k], FWD_TOL_BF16 if k in ("o", "S_final") else GRAD_TOL_BF16)
+
+
+# ------------------------------------------------------------------ conv with a carried state
+@pytest.mark.parametrize("name", ["fp32_ragged", "bf16_g2_mild", "bf16_d32"])
+def test_conv_state_fwd_bwd(name):
+    """gdn_conv_fwd_state / gdn_conv_bwd_state against the oracle, with a
+    random carried state in and a random gradient of the final state; the
+    final state is a copy of input rows, so it is compared exactly."""
+    w, inp = _case(name)
+    dt = w.dtype
+    cu = inp["cu_seqlens"]
+    lens = np.diff(cu)
+    n_l2 = 2 * w.hk * w.d
+    rng = np.random.default_rng(8)
+    C = w.channels
+    cs = _rnd(rng.standard_normal((len(lens), 3, C)), dt)
+    dcs = _rnd(rng.standard_normal((len(lens), 3, C)), dt)
+    y_ref, cs_ref = oracle.conv_state_fwd(inp["x"], inp["w_conv"], cu, n_l2, w.d, cs)
+    dy = _rnd(rng.standard_normal(y_ref.shape), dt)
+    dx_ref, dw_ref, dcs_ref = oracle.conv_state_bwd(inp["x"], inp["w_conv"], cu, n_l2, w.d, dy, cs,
+                                                    dcs)
+    sh = _shape(w, inp)
+    x = dev(inp["x"], _tdt(dt))
+    wc = dev(inp["w_conv"])
+    cut = torch.from_numpy(cu).to(DEV)
+    cst = dev(cs, _tdt(dt))
+    y = torch.empty_like(x)
+    cs_out = torch.empty_like(cst)
+    L.gdn_conv_fwd_state(sh, x, wc, cut, y, cst, cs_out)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(wc)
+    dcs_in = torch.empty_like(cst)
+    ws = torch.empty(max(L.gdn_conv_bwd_workspace(sh), 16), dtype=torch.uint8, device=DEV)
+    L.gdn_conv_bwd_state(sh, x, wc, cut, dev(dy, _tdt(dt)), dx, dw, ws, cst, dev(dcs, _tdt(dt)),
+                         dcs_in)
+    torch.cuda.synchronize()
+    assert_close("y", host(y), y_ref, _tol(dt))
+    np.testing.assert_array_equal(host(cs_out), cs_ref)
+    assert_close("dx", host(dx), dx_ref, _tol(dt, True))
+    assert_close("dw", host(dw), dw_ref, _tol(dt, True))
+    assert_close("d_conv_state", host(dcs_in), dcs_ref, _tol(dt, True))
