@@ -23,7 +23,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
-GDN_BF16, GDN_FP32 = 0, 1
+GDN_BF16, GDN_FP32, GDN_FP16 = 0, 1, 2
 GDN_ACT_SILU, GDN_ACT_SIGMOID = 0, 1
 EXPORTS = (
     "gdn_status_string", "gdn_conv_fwd", "gdn_conv_bwd", "gdn_conv_bwd_workspace",
@@ -133,18 +133,19 @@ def _ok(name, st):
         raise GDNError(name, st, load().gdn_status_string(st).decode())
 
 
+_GDN_DT = {torch.bfloat16: GDN_BF16, torch.float32: GDN_FP32, torch.float16: GDN_FP16}
+
+
 def _dt(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
-        return GDN_BF16
-    if t.dtype == torch.float32:
-        return GDN_FP32
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dtype not in _GDN_DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _GDN_DT[t.dtype]
 
 
 def make_shape(n_seq, total_tokens, hk, hv, d, dtype, seg_chunks=0) -> Shape:
     """seg_chunks: segment length of the segment-parallel state scan (0: the
     library decides, > 0: forced, < 0: one sequential pass per sequence)."""
-    dt = dtype if isinstance(dtype, int) else (GDN_BF16 if dtype == torch.bfloat16 else GDN_FP32)
+    dt = dtype if isinstance(dtype, int) else _GDN_DT[dtype]
     return Shape(n_seq, total_tokens, hk, hv, d, d, 4, 64, dt, seg_chunks)
 
 
@@ -174,7 +175,7 @@ def gdn_gated_norm_bwd_workspace(rows, dv):
 
 
 # ---------------------------------------------------------------- argument checks
-_TDT = {GDN_BF16: torch.bfloat16, GDN_FP32: torch.float32}
+_TDT = {GDN_BF16: torch.bfloat16, GDN_FP32: torch.float32, GDN_FP16: torch.float16}
 
 
 def _tdt(shape) -> torch.dtype:

@@ -11,12 +11,13 @@ namespace {
 constexpr int64_t kMaxTokens = 0x7fffffffLL;  // cu_seqlens is int32
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-size_t esize(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
+size_t esize(gdn_dtype d) { return d == GDN_FP32 ? 4 : 2; }
+bool dtype_ok(gdn_dtype d) { return d == GDN_BF16 || d == GDN_FP32 || d == GDN_FP16; }
 
 gdn_status check_shape(const gdn_shape* s) {
   if (!s) return GDN_ERR_INVALID_ARG;
   if (s->n_seq < 1 || s->total_tokens < 0 || s->total_tokens > kMaxTokens || s->hk < 1 ||
-      s->hv < 1 || s->dk < 1 || s->dv < 1 || (s->dtype != GDN_BF16 && s->dtype != GDN_FP32))
+      s->hv < 1 || s->dk < 1 || s->dv < 1 || !dtype_ok(s->dtype))
     return GDN_ERR_INVALID_ARG;
   if (s->hv % s->hk != 0) return GDN_ERR_INVALID_ARG;
   if (s->dk != s->dv || (s->dk != 32 && s->dk != 128)) return GDN_ERR_UNSUPPORTED;
@@ -42,7 +43,7 @@ gdn_status check_ptrs(std::initializer_list<const void*> ps) {
 }
 
 gdn_status chunk_supported(const gdn_shape* s) {
-  // fp32 storage is supported at head dim 32 (the fp32 workload); bf16 at 32 and 128
+  // fp32 storage is supported at head dim 32 (the fp32 workload); bf16 and fp16 at 32 and 128
   if (s->dtype == GDN_FP32 && s->dk != 32) return GDN_ERR_UNSUPPORTED;
   return GDN_OK;
 }
@@ -337,7 +338,7 @@ gdn_status gdn_chunk_bwd_grads(const gdn_shape* s, const void* q, const void* k,
 
 gdn_status gdn_gated_norm_fwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
                               const float* w, float eps, gdn_act act, void* y, void* stream) {
-  if (rows < 0 || (dt != GDN_BF16 && dt != GDN_FP32) || (act != GDN_ACT_SILU && act != GDN_ACT_SIGMOID))
+  if (rows < 0 || !dtype_ok(dt) || (act != GDN_ACT_SILU && act != GDN_ACT_SIGMOID))
     return GDN_ERR_INVALID_ARG;
   if (dv != 32 && dv != 128) return GDN_ERR_UNSUPPORTED;
   GDN_TRY(check_ptrs({o, z, w, y}));
@@ -353,7 +354,7 @@ size_t gdn_gated_norm_bwd_workspace(int64_t rows, int32_t dv) {
 gdn_status gdn_gated_norm_bwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
                               const float* w, float eps, gdn_act act, const void* dy, void* dout,
                               void* dz, float* dw, void* ws, size_t ws_bytes, void* stream) {
-  if (rows < 0 || (dt != GDN_BF16 && dt != GDN_FP32) || (act != GDN_ACT_SILU && act != GDN_ACT_SIGMOID))
+  if (rows < 0 || !dtype_ok(dt) || (act != GDN_ACT_SILU && act != GDN_ACT_SIGMOID))
     return GDN_ERR_INVALID_ARG;
   if (dv != 32 && dv != 128) return GDN_ERR_UNSUPPORTED;
   GDN_TRY(check_ptrs({o, z, w, dy, dout, dz, dw}));

@@ -22,8 +22,9 @@ namespace gdn {
 template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };
 
 // MFMA operand type of the forward-state kernels for a storage type: fp16 for
-// bf16 storage (bf16 inputs convert exactly; 11-bit mantissa for the
-// intermediates), fp32 for fp32 storage.
+// 16-bit storage (11-bit significands for the operands and intermediates;
+// the fp16 range, |x| <= 65504, bounds the values: see the range contract in
+// libgdn.h), fp32 for fp32 storage.
 template <typename T> struct Compute { typedef fp16 type; };
 template <> struct Compute<float> { typedef float type; };
 
@@ -135,7 +136,7 @@ __device__ __forceinline__ T* row_or_sink(T* p, bool valid, void* sink, int tid)
 
 inline ChunkLayout chunk_layout(const gdn_shape& s) {
   ChunkLayout L;
-  const size_t es = s.dtype == GDN_BF16 ? 2 : 4;
+  const size_t es = s.dtype == GDN_FP32 ? 4 : 2;
   const int64_t T = s.total_tokens;
   L.nt_max = T / CHUNK + s.n_seq;
   L.seg = seg_len(s);
@@ -188,6 +189,7 @@ hipError_t launch_span_combine(const gdn_shape& s, const ChunkLayout& Ly, char* 
 template <typename T, int D> struct ChunkCfg { typedef T type; static constexpr int d = D; };
 template <typename F> hipError_t dispatch_chunk(const gdn_shape& s, F&& f) {
   if (s.dtype == GDN_BF16) return s.dk == 128 ? f(ChunkCfg<bf16, 128>{}) : f(ChunkCfg<bf16, 32>{});
+  if (s.dtype == GDN_FP16) return s.dk == 128 ? f(ChunkCfg<fp16, 128>{}) : f(ChunkCfg<fp16, 32>{});
   return f(ChunkCfg<float, 32>{});
 }
 

@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       const h8 x = __builtin_bit_cast(h8, tfr(sm.tDl, r, p));
       frag y;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = (bf16)(float)x[j];
+      for (int j = 0; j < 8; ++j) y[j] = (T)(float)x[j];
       return y;
     } else {
       return tfr(sm.tDl, r, p);
@@ -216,8 +216,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   raw4 q4[TTW], k4[TTW];
   auto raw_f4 = [&](const raw4& r) __attribute__((always_inline)) -> floatx4 {
     if constexpr (sizeof(T) == 2)
-      return floatx4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+      return floatx4{lo16<T>(r.x), hi16<T>(r.x), lo16<T>(r.y), hi16<T>(r.y)};
     else
       return __builtin_bit_cast(floatx4, r);
   };

@@ -124,8 +124,7 @@ template <typename T>
 __device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   if constexpr (sizeof(T) == 2) {
     const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-    return floatx4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
-                   __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+    return floatx4{lo16<T>(w[0]), hi16<T>(w[0]), lo16<T>(w[1]), hi16<T>(w[1])};
   } else {
     return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
   }
@@ -133,7 +132,7 @@ __device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t rs, uint3
 template <typename T>
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_t off, floatx4 x) {
   if constexpr (sizeof(T) == 2) {
-    const u32x2 w = {pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3])};
+    const u32x2 w = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3])};
     __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
   } else {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
@@ -147,15 +146,6 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_
 // columns (l % 16) & ~1 and + 1.  Half the store instructions of one store
 // per element.
 // 32-bit words of a paired row piece: two 16-bit elements, or two floats.
-// two values as one 32-bit word of 16-bit elements (round to nearest even)
-template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (std::is_same<T, fp16>::value) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, h2{(fp16)a, (fp16)b});
-  } else {
-    return pack2_bf16(a, b);
-  }
-}
 
 template <typename T> struct PairWord { typedef uint32_t type; };
 template <> struct PairWord<float> { typedef u32x2 type; };

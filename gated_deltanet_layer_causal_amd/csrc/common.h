@@ -85,6 +85,24 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
+// Two 16-bit storage elements (bf16 or fp16) in one 32-bit word, low half
+// first: to floats, and from floats (round to nearest even).
+template <typename T> __device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (__is_same(T, bf16)) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(fp16, (uint16_t)(w & 0xffffu));
+}
+template <typename T> __device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (__is_same(T, bf16)) return __uint_as_float(w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(fp16, (uint16_t)(w >> 16));
+}
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (__is_same(T, bf16)) {
+    return pack2_bf16(a, b);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(fp16)a, (fp16)b});
+  }
+}
 __device__ __forceinline__ void store8(bf16* p, const f8& r) {
   uint4 raw;
   raw.x = pack2_bf16(r.v[0], r.v[1]);

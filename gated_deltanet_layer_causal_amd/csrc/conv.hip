@@ -65,8 +65,8 @@ __device__ __forceinline__ void put_row8(__amdgpu_buffer_rsrc_t rs, int64_t r, u
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const uint32_t off = (uint32_t)r * ldb + coff;
   if constexpr (sizeof(T) == 2) {
-    const u32x4 w = {pack2_bf16(v.v[0], v.v[1]), pack2_bf16(v.v[2], v.v[3]),
-                     pack2_bf16(v.v[4], v.v[5]), pack2_bf16(v.v[6], v.v[7])};
+    const u32x4 w = {pack2<T>(v.v[0], v.v[1]), pack2<T>(v.v[2], v.v[3]),
+                     pack2<T>(v.v[4], v.v[5]), pack2<T>(v.v[6], v.v[7])};
     __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, 0);
   } else {
     const u32x4 w0 = {__float_as_uint(v.v[0]), __float_as_uint(v.v[1]), __float_as_uint(v.v[2]),
@@ -526,6 +526,9 @@ static hipError_t conv_bwd_t(const gdn_shape& s, const void* x, int64_t ldx, con
 hipError_t launch_conv_fwd(const gdn_shape& s, const void* x, int64_t ldx, const float* w,
                            const int32_t* cu, int l2, float eps, void* y, int64_t ldy,
                            const void* cs_in, void* cs_out, hipStream_t st) {
+  if (s.dtype == GDN_FP16)
+    return s.dk == 128 ? conv_fwd_t<fp16, 128>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st)
+                       : conv_fwd_t<fp16, 32>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st);
   if (s.dtype == GDN_BF16)
     return s.dk == 128 ? conv_fwd_t<bf16, 128>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st)
                        : conv_fwd_t<bf16, 32>(s, x, ldx, w, cu, l2, eps, y, ldy, cs_in, cs_out, st);
@@ -537,6 +540,11 @@ hipError_t launch_conv_bwd(const gdn_shape& s, const void* x, int64_t ldx, const
                            const int32_t* cu, int l2, float eps, const void* dy, int64_t lddy,
                            void* dx, int64_t lddx, float* dw, float* partials, const void* cs_in,
                            const void* dcs_out, void* dcs_in, hipStream_t st) {
+  if (s.dtype == GDN_FP16)
+    return s.dk == 128 ? conv_bwd_t<fp16, 128>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw,
+                                                partials, cs_in, dcs_out, dcs_in, st)
+                       : conv_bwd_t<fp16, 32>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw,
+                                               partials, cs_in, dcs_out, dcs_in, st);
   if (s.dtype == GDN_BF16)
     return s.dk == 128 ? conv_bwd_t<bf16, 128>(s, x, ldx, w, cu, l2, eps, dy, lddy, dx, lddx, dw,
                                                 partials, cs_in, dcs_out, dcs_in, st)

@@ -79,6 +79,9 @@ hipError_t launch_gate_fwd(const gdn_shape& s, const void* a, const void* b, con
   if (s.dtype == GDN_BF16)
     hipLaunchKernelGGL(gate_fwd_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, st,
                        (const bf16*)a, (const bf16*)b, A_log, dt_bias, n, s.hv, g, beta);
+  else if (s.dtype == GDN_FP16)
+    hipLaunchKernelGGL(gate_fwd_kernel<fp16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const fp16*)a, (const fp16*)b, A_log, dt_bias, n, s.hv, g, beta);
   else
     hipLaunchKernelGGL(gate_fwd_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
                        (const float*)a, (const float*)b, A_log, dt_bias, n, s.hv, g, beta);
@@ -95,6 +98,10 @@ hipError_t launch_gate_bwd(const gdn_shape& s, const void* a, const void* b, con
       hipLaunchKernelGGL(gate_bwd_kernel<bf16>, dim3((unsigned)np), dim3(256), 0, st,
                          (const bf16*)a, (const bf16*)b, A_log, dt_bias, dg, dbeta, s.total_tokens,
                          s.hv, (bf16*)da, (bf16*)db, partials);
+    else if (s.dtype == GDN_FP16)
+      hipLaunchKernelGGL(gate_bwd_kernel<fp16>, dim3((unsigned)np), dim3(256), 0, st,
+                         (const fp16*)a, (const fp16*)b, A_log, dt_bias, dg, dbeta, s.total_tokens,
+                         s.hv, (fp16*)da, (fp16*)db, partials);
     else
       hipLaunchKernelGGL(gate_bwd_kernel<float>, dim3((unsigned)np), dim3(256), 0, st,
                          (const float*)a, (const float*)b, A_log, dt_bias, dg, dbeta,

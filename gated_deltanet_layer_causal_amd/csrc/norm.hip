@@ -153,6 +153,7 @@ static hipError_t norm_bwd_t(int64_t rows, int32_t dv, const void* o, const void
 hipError_t launch_norm_fwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
                            const float* w, float eps, int act, void* y, hipStream_t st) {
   if (rows == 0) return hipSuccess;
+  if (dt == GDN_FP16) return norm_fwd_t<fp16>(rows, dv, o, z, w, eps, act, y, st);
   return dt == GDN_BF16 ? norm_fwd_t<bf16>(rows, dv, o, z, w, eps, act, y, st)
                         : norm_fwd_t<float>(rows, dv, o, z, w, eps, act, y, st);
 }
@@ -160,6 +161,8 @@ hipError_t launch_norm_fwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o
 hipError_t launch_norm_bwd(int64_t rows, int32_t dv, gdn_dtype dt, const void* o, const void* z,
                            const float* w, float eps, int act, const void* dy, void* dout,
                            void* dz, float* dw, float* partials, hipStream_t st) {
+  if (dt == GDN_FP16)
+    return norm_bwd_t<fp16>(rows, dv, o, z, w, eps, act, dy, dout, dz, dw, partials, st);
   return dt == GDN_BF16
              ? norm_bwd_t<bf16>(rows, dv, o, z, w, eps, act, dy, dout, dz, dw, partials, st)
              : norm_bwd_t<float>(rows, dv, o, z, w, eps, act, dy, dout, dz, dw, partials, st);

@@ -45,7 +45,7 @@ class Workload:
     hk: int
     hv: int
     d: int
-    dtype: str               # "bf16" or "fp32": storage type of token tensors
+    dtype: str               # "bf16", "fp16" or "fp32": storage type of token tensors
     seq: str = "single"      # "single" or "varlen"
     init_state: bool = False  # nonzero S0 ~ N(0, 0.1)
     final_state: bool = False  # S_final returned, upstream grad dS_T ~ N(0, 1)
@@ -76,6 +76,18 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
     r = (u + bias) & np.uint32(0xFFFF0000)
     return r.view(np.float32)
+
+
+def round_fp16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest float16 (ties to even); returns
+    float32 values exactly representable in float16 (|x| > 65504 -> inf)."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def round_to(dtype: str):
+    """The rounding of token tensors stored as `dtype` ("bf16", "fp16",
+    "fp32"), or None for fp32."""
+    return {"bf16": round_bf16, "fp16": round_fp16, "fp32": None}[dtype]
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -114,7 +126,7 @@ def make_inputs(w: Workload, T: Optional[int] = None, seqlens=None, seed: Option
     ``T`` / ``seqlens`` override the token count (for scaled-down parity
     cases); ``A_range`` overrides the gate's A distribution (mild decay keeps
     state alive across many chunks).  All token tensors are float32 arrays;
-    for bf16 workloads they are bf16-exact.
+    for bf16 / fp16 workloads they are exact in that type.
     """
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
     dt = w.dtype if dtype is None else dtype
@@ -152,9 +164,10 @@ def make_inputs(w: Workload, T: Optional[int] = None, seqlens=None, seed: Option
     out["S0"] = f32((N, Hv, d, d), 0.1) if w.init_state else None
     out["dy"] = f32((T, Hv, d))
     out["dS_T"] = f32((N, Hv, d, d)) if w.final_state else None
-    if dt == "bf16":
+    rnd = round_to(dt)
+    if rnd is not None:
         for key in ("x", "a", "b", "z", "dy"):
-            out[key] = round_bf16(out[key])
+            out[key] = rnd(out[key])
     out["dtype"] = dt
     return out
 

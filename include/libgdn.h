@@ -52,7 +52,7 @@ typedef enum {
   GDN_ERR_LAUNCH = 5       /* HIP reported an error at launch */
 } gdn_status;
 
-typedef enum { GDN_BF16 = 0, GDN_FP32 = 1 } gdn_dtype; /* token tensors; params/state are fp32 */
+typedef enum { GDN_BF16 = 0, GDN_FP32 = 1, GDN_FP16 = 2 } gdn_dtype; /* token tensors; params/state are fp32 */
 typedef enum { GDN_ACT_SILU = 0, GDN_ACT_SIGMOID = 1 } gdn_act;
 
 typedef struct {
@@ -170,6 +170,15 @@ size_t gdn_gate_bwd_workspace(const gdn_shape* shape);
  * The result equals the token-by-token recurrence up to rounding; chunks of
  * 64 tokens never straddle a sequence boundary.  g must be <= 0 (as the gate
  * produces); then every exponential evaluated is <= 1.
+ * Range: with 16-bit data (bf16, fp16) the MFMA operands of the passes over
+ * the state are fp16 in the forward (v, the running state S, the writes
+ * R = V - diag(Gam) K S^T and Delta) and in the storage type in the
+ * backward (fp16 data: also the state gradient), so these must stay below
+ * 65504 in magnitude: keys L2-normalised (|k| <= 1, as gdn_conv_fwd's
+ * l2norm_qk gives; unnormalised keys make the recurrence grow without
+ * bound), and entries of v and S0 up to ~1e3 (checked against the oracle with
+ * |v| up to 4e3 and S0 ~ N(0, 1e3)).  Beyond that the results overflow to
+ * inf; fp32 data has no such limit.
  * q, k, v in shape->dtype (row strides ldq, ldk, ldv, multiples of 8);
  * o [T][hv*dv] in shape->dtype; S_final may be NULL.
  * ------------------------------------------------------------------------- */

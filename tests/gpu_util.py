@@ -9,6 +9,21 @@ DEV = "cuda:0"
 FWD_TOL_BF16 = 5e-3
 GRAD_TOL_BF16 = 1e-2
 TOL_FP32 = 1e-5
+# 16-bit storage (bf16 or fp16) is held to the bf16 bars
+
+
+def torch_dtype(dtype):
+    return {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+
+
+def gdn_dtype(dtype):
+    from gated_deltanet_layer_causal_amd import capi as L
+    return {"bf16": L.GDN_BF16, "fp16": L.GDN_FP16, "fp32": L.GDN_FP32}[dtype]
+
+
+def tols(dtype):
+    """(forward, gradient) tolerance for a storage dtype"""
+    return (TOL_FP32, TOL_FP32) if dtype == "fp32" else (FWD_TOL_BF16, GRAD_TOL_BF16)
 
 
 def dev(a, dtype=torch.float32):

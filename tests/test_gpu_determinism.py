@@ -17,7 +17,7 @@ import torch
 from gated_deltanet_layer_causal_amd import capi as L
 from gated_deltanet_layer_causal_amd import inputs as gi
 from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore
-from tests.gpu_util import DEV, dev
+from tests.gpu_util import DEV, dev, gdn_dtype, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +132,7 @@ CANARY_CASES = {
     "bf16_d32_seg": (2, 4, 32, "bf16", [129, 64, 3], 1),
     "fp32_d32": (1, 2, 32, "fp32", [100, 37, 1, 70], 0),
     "fp32_d32_seg": (1, 2, 32, "fp32", [100, 37, 1, 70], 1),
+    "fp16_d128_seg": (2, 6, 128, "fp16", [300, 65, 7, 1, 0, 130], 2),
 }
 
 
@@ -141,9 +142,9 @@ def test_every_entry_point_stays_in_bounds(name):
     w = gi.Workload(name, sum(lens), hk, hv, d, dt, seq="varlen", init_state=True,
                     final_state=True, seed=91)
     inp = gi.make_inputs(w, seqlens=lens, A_range=(0.02, 0.3))
-    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tdt = torch_dtype(dt)
     T, N, C = inp["T"], inp["N"], w.channels
-    sh = L.make_shape(N, T, hk, hv, d, L.GDN_BF16 if dt == "bf16" else L.GDN_FP32, seg)
+    sh = L.make_shape(N, T, hk, hv, d, gdn_dtype(dt), seg)
     G = Guarded()
     # inputs (checked afterwards to be unchanged)
     x = G.new("x", (T, C), tdt, dev(inp["x"], tdt))

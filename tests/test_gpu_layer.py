@@ -12,7 +12,8 @@ import oracle
 from gated_deltanet_layer_causal_amd import capi as L
 from gated_deltanet_layer_causal_amd import inputs as gi
 from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore, GDNLayer
-from tests.gpu_util import DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_close, dev, host, rel_err
+from tests.gpu_util import (DEV, FWD_TOL_BF16, GRAD_TOL_BF16, TOL_FP32, assert_close, dev, host,
+                            rel_err, tols, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,6 +33,11 @@ CASES = {
     "fp32_empty_first": (gi.Workload("fe", 0, 1, 2, 32, "fp32", seq="varlen", init_state=True,
                                      final_state=True, seed=80), [0, 40, 0, 3], (0.02, 0.3),
                          L.GDN_ACT_SIGMOID),
+    "fp16_small": (gi.Workload("hs", 0, 2, 6, 128, "fp16", seq="varlen", init_state=True,
+                               final_state=True, seed=86), [300, 65, 7], None, L.GDN_ACT_SILU),
+    "fp16_d32_mild": (gi.Workload("hm", 0, 2, 4, 32, "fp16", seq="varlen", init_state=True,
+                                  final_state=True, seed=87), [129, 0, 64], (0.02, 0.3),
+                      L.GDN_ACT_SIGMOID),
 }
 
 
@@ -44,9 +50,8 @@ def test_layer_matches_oracle(name, save_states, seg):
     of two chunks."""
     w, lens, A_range, act = CASES[name]
     inp = gi.make_inputs(w, seqlens=lens, A_range=A_range)
-    bf = w.dtype == "bf16"
-    tdt = torch.bfloat16 if bf else torch.float32
-    rf = gi.round_bf16 if bf else None
+    tdt = torch_dtype(w.dtype)
+    rf = gi.round_to(w.dtype)
     core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=tdt, act=act, seg_chunks=seg),
                    device=DEV)
     cu = torch.from_numpy(inp["cu_seqlens"]).to(DEV)
@@ -60,8 +65,7 @@ def test_layer_matches_oracle(name, save_states, seg):
     sc = w.d ** -0.5
     rf_ = f_ = oracle.layer_fwd(inp, w.hk, w.hv, w.d, sc, act=act, round_fn=rf)
     rb = oracle.layer_bwd(inp, rf_, w.hk, w.hv, w.d, sc, act=act, round_fn=rf)
-    ft = TOL_FP32 if not bf else FWD_TOL_BF16
-    gt = TOL_FP32 if not bf else GRAD_TOL_BF16
+    ft, gt = tols(w.dtype)
     checks = [(k, f[k], f_[k], ft) for k in ("y", "g", "beta", "o", "out", "S_final")]
     checks += [(k, gb[k], rb[k], gt) for k in ("do", "dg", "dbeta", "dy_conv", "dx", "dw_conv", "da",
                                                "db", "dA_log", "ddt_bias", "dz", "dw_norm", "dS0")]

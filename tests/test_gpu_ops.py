@@ -24,6 +24,8 @@ CASES = {
     "bf16_g2_mild": (2, 4, 128, "bf16", [150, 64, 1, 90], (0.01, 0.1), True),
     "bf16_g3_strong": (2, 6, 128, "bf16", [200, 7, 130], (1.0, 16.0), False),
     "bf16_d32": (2, 4, 32, "bf16", [129, 64], (0.05, 0.5), True),
+    "fp16_g2_mild": (2, 4, 128, "fp16", [150, 64, 1, 90], (0.01, 0.1), True),
+    "fp16_d32": (2, 4, 32, "fp16", [129, 64, 2], (0.05, 0.5), True),
 }
 
 
@@ -35,11 +37,16 @@ def _tol(dtype, grad=False):
 
 def _rnd(a, dtype):
     a = np.asarray(a, dtype=np.float32)
-    return gi.round_bf16(a) if dtype == "bf16" else a
+    r = gi.round_to(dtype)
+    return a if r is None else r(a)
 
 
 def _tdt(dtype):
-    return torch.bfloat16 if dtype == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+
+
+def _gdt(dtype):
+    return {"bf16": L.GDN_BF16, "fp16": L.GDN_FP16, "fp32": L.GDN_FP32}[dtype]
 
 
 def _case(name, seed=7):
@@ -51,8 +58,7 @@ def _case(name, seed=7):
 
 
 def _shape(w, inp):
-    return L.make_shape(inp["N"], inp["T"], w.hk, w.hv, w.d,
-                        L.GDN_BF16 if w.dtype == "bf16" else L.GDN_FP32)
+    return L.make_shape(inp["N"], inp["T"], w.hk, w.hv, w.d, _gdt(w.dtype))
 
 
 # ------------------------------------------------------------------ conv
@@ -85,7 +91,7 @@ def test_conv_fwd_bwd(name):
 
 
 # ------------------------------------------------------------------ gate
-@pytest.mark.parametrize("name", ["fp32_tiny", "bf16_g3_strong"])
+@pytest.mark.parametrize("name", ["fp32_tiny", "bf16_g3_strong", "fp16_g2_mild"])
 def test_gate_fwd_bwd(name):
     w, inp = _case(name)
     dt = w.dtype
@@ -114,7 +120,7 @@ def test_gate_fwd_bwd(name):
 
 
 # ------------------------------------------------------------------ gated norm
-@pytest.mark.parametrize("name", ["fp32_tiny", "bf16_g2_mild", "bf16_d32"])
+@pytest.mark.parametrize("name", ["fp32_tiny", "bf16_g2_mild", "bf16_d32", "fp16_g2_mild", "fp16_d32"])
 @pytest.mark.parametrize("act", [L.GDN_ACT_SILU, L.GDN_ACT_SIGMOID])
 def test_gated_norm_fwd_bwd(name, act):
     w, inp = _case(name)
@@ -178,7 +184,7 @@ def test_chunk_fwd_bwd(name):
     dSft = dev(dSf) if dSf is not None else None
     dot = dev(dout, _tdt(dt))
     for seg in (0, 1, 3):
-        sh = L.make_shape(inp["N"], T, hk, hv, d, L.GDN_BF16 if dt == "bf16" else L.GDN_FP32, seg)
+        sh = L.make_shape(inp["N"], T, hk, hv, d, _gdt(dt), seg)
         ws = torch.empty(L.gdn_chunk_bwd_workspace(sh), dtype=torch.uint8, device=DEV)
         for flow in FLOWS:
             r = run_chunk(flow, sh, qt, kt, vt, gt, bt, scale, S0t, cut, dot, dSft, ws)
@@ -249,37 +255,38 @@ def test_chunk_table_exact(lens, seg):
 
 
 # ------------------------------------------------------------------ fp16 operand range
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("flow", ["composite", "saved"])
-def test_chunk_large_values_and_state(flow):
+def test_chunk_large_values_and_state(flow, dt):
     """The forward passes of bf16 data round v, the running state and the
     delta-rule writes to fp16 for the MFMA (max 65504).  Values and initial
     state ~1e3 times the workloads' (|v| up to ~4e3, S0 ~ N(0, 1e3)), the
     range the header documents, still match the oracle."""
     from tests.gpu_util import run_chunk
     hk, hv, d, lens = 2, 4, 128, [150, 64, 90]
-    w = gi.Workload("big", sum(lens), hk, hv, d, "bf16", seq="varlen", init_state=True,
+    w = gi.Workload("big", sum(lens), hk, hv, d, dt, seq="varlen", init_state=True,
                     final_state=True, seed=21)
     inp = gi.make_inputs(w, seqlens=lens, A_range=(0.01, 0.1))
     cu, T = inp["cu_seqlens"], inp["T"]
-    y = gi.round_bf16(oracle.conv_fwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d))
-    y[:, 2 * hk * d:] = gi.round_bf16(y[:, 2 * hk * d:] * 1000.0)
+    y = _rnd(oracle.conv_fwd(inp["x"], inp["w_conv"], cu, 2 * hk * d, d), dt)
+    y[:, 2 * hk * d:] = _rnd(y[:, 2 * hk * d:] * 1000.0, dt)
     g, beta = oracle.gate_fwd(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
     g, beta = g.astype(np.float32), beta.astype(np.float32)
     S0 = (inp["S0"] * 1e4).astype(np.float32)          # N(0, 0.1) -> N(0, 1e3)
     rng = np.random.default_rng(22)
-    dout = gi.round_bf16(rng.standard_normal((T, hv, d), dtype=np.float32))
+    dout = _rnd(rng.standard_normal((T, hv, d), dtype=np.float32), dt)
     dSf = inp["dS_T"]
     q, k, v = gi.split_qkv(y, hk, hv, d)
     scale = d ** -0.5
     o_ref, Sf_ref = oracle.delta_fwd(q, k, v, g, beta, cu, scale, S0)
     ref = oracle.delta_bwd(q, k, v, g, beta, cu, scale, dout, S0, dSf)
     assert np.max(np.abs(Sf_ref)) > 1e3 and np.max(np.abs(v)) > 2e3
-    sh = L.make_shape(inp["N"], T, hk, hv, d, L.GDN_BF16)
-    yt = dev(y, torch.bfloat16)
+    sh = L.make_shape(inp["N"], T, hk, hv, d, _gdt(dt))
+    yt = dev(y, _tdt(dt))
     ws = torch.empty(L.gdn_chunk_bwd_workspace(sh), dtype=torch.uint8, device=DEV)
     r = run_chunk(flow, sh, yt[:, : hk * d], yt[:, hk * d: 2 * hk * d], yt[:, 2 * hk * d:], dev(g),
                   dev(beta), scale, dev(S0), torch.from_numpy(cu).to(DEV),
-                  dev(dout, torch.bfloat16), dev(dSf), ws)
+                  dev(dout, _tdt(dt)), dev(dSf), ws)
     torch.cuda.synchronize()
     got = {"o": host(r["o"]), "S_final": host(r["S_final"]),
            "dq": host(r["dq"]).reshape(T, hk, d), "dk": host(r["dk"]).reshape(T, hk, d),
@@ -294,7 +301,7 @@ def test_chunk_large_values_and_state(flow):
 
 
 # ------------------------------------------------------------------ conv with a carried state
-@pytest.mark.parametrize("name", ["fp32_ragged", "bf16_g2_mild", "bf16_d32"])
+@pytest.mark.parametrize("name", ["fp32_ragged", "bf16_g2_mild", "bf16_d32", "fp16_d32"])
 def test_conv_state_fwd_bwd(name):
     """gdn_conv_fwd_state / gdn_conv_bwd_state against the oracle, with a
     random carried state in and a random gradient of the final state; the
