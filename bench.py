@@ -82,10 +82,8 @@ FP32_PEAK_TFLOPS = 157.3
 #   bwd_grads  : dO S, dR S, Delta dS' (3 x 2 d^2); dM, dP, (dP o D) K,
 #                (dP o D)^T Q, (dA o bD) K, (dA o bD)^T K (6 x 2 C d);
 #                Tinv products (2 x 2 C^2); per key head K K^T, Q K^T (2 x 2 C d)
-# The preparation is bandwidth-bound: it reads q, k, g, beta and writes the
-# gate sums, per value head M, P, W, Gam, dec (and, in backward mode, P^T,
-# Tinv, Tinv^T, beta), per key head K^T and fp16 Q, K rows (backward mode: K, K^T,
-# Q^T in the storage type).
+# The preparation is bandwidth-bound; its algorithmic bytes are its inputs
+# q, k, g, beta (its writes are intermediates).
 def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     C = 2 * hk * d + hv * d
     C64 = 64
@@ -108,13 +106,11 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     # in the storage type and one more key-head tile (the K rows in the
     # compute type for 16-bit data, the compute-type K^T for fp32), per value
     # head P^T, Tinv, Tinv^T and beta (and W for fp32).
-    per_hv = 4 + 4 + 8 + 8 + 2 * C64 * E
-    fwd_bytes = 2 * hk * d * E + 2 * hk * d * E + hv * (per_hv + d * E)
-    bwd_bytes = 2 * hk * d * E + 4 * hk * d * E + hv * (per_hv + 4 + 3 * C64 * E + (d * E if E == 4 else 0))
-    if name == "chunk_prepare":
-        return "hbm", bwd_bytes if saved else fwd_bytes
-    if name == "chunk_prepare_b":
-        return "hbm", bwd_bytes
+    # The method needs only q, k, g and beta from memory here: everything the
+    # preparation writes is an intermediate of this implementation, so it
+    # counts none of it (its traffic is reported beside, from the counters).
+    if name in ("chunk_prepare", "chunk_prepare_b"):
+        return "hbm", 2 * hk * d * E + 2 * hv * 4
     # products formed per v-head token: the forward pass without saved
     # states (W S^T, Q S^T, update; M V, P Delta); the saved-state pass (K S^T,
     # update; M R for 16-bit data, W S^T, update; M V for fp32) and the
@@ -138,6 +134,64 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     if name == "chunk_bwd_grads":
         return "mfma", hv * (6 * d * d + 12 * C64 * d + 4 * C64 * C64) + hk * 2 * C64 * d
     raise KeyError(name)
+
+
+# Floors of the layer at 100% of peak (the scope table's per-token counts):
+#   chunked rule, per value head and token: forward 10 C d + 6 d^2 + 2/3 C^2,
+#     backward 30 C d + 16 d^2 flop (dense tiles, C = 64); bytes: q, k, v, g,
+#     beta in and o out (forward), q, k, v, g, beta, do in and dq, dk, dv, dg,
+#     dbeta out (backward);
+#   conv fwd+bwd 5 C_ch E, gate hv (6 E + 16), norm 8 hv d E + 4 hv bytes.
+def layer_floor(hk, hv, d, E, T, peak_tflops):
+    C64 = 64
+    chunk_flop = hv * (10 * C64 * d + 6 * d * d + 2 * C64 * C64 / 3 + 30 * C64 * d + 16 * d * d)
+    chunk_bytes = (2 * hk * d * E + 2 * hv * d * E + 8 * hv) + \
+                  (2 * hk * d * E + 2 * hv * d * E + 8 * hv + 2 * hk * d * E + hv * d * E + 8 * hv)
+    Cch = 2 * hk * d + hv * d
+    hbm_bytes = 5 * Cch * E + hv * (6 * E + 16) + 8 * hv * d * E + 4 * hv
+    chunk_ms = max(chunk_flop * T / (peak_tflops * 1e12), chunk_bytes * T / (HBM_PEAK_GBS * 1e9)) * 1e3
+    other_ms = hbm_bytes * T / (HBM_PEAK_GBS * 1e9) * 1e3
+    return {"chunk_ms": chunk_ms, "conv_gate_norm_ms": other_ms, "layer_ms": chunk_ms + other_ms,
+            "chunk_mflop_per_token": chunk_flop / 1e6, "chunk_bytes_per_token": chunk_bytes}
+
+
+# Counter summaries of the chunk kernels (MFMA busy fraction and executed
+# MFMA flops per launch, from rocprofv3 --pmc), used while the kernel's
+# sources are unchanged since they were taken.
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_flash64k.txt")
+KERNEL_FILES = {
+    "chunk_grad": ["chunk_grad.hip"], "chunk_rev": ["chunk_rev.hip"],
+    "chunk_state[m1]": ["chunk_state.hip"], "chunk_o": ["chunk_out.hip"],
+    "chunk_prep[bwd]": ["chunk_fwd.hip"],
+}
+CALL_KERNELS = {"chunk_bwd_grads": ["chunk_grad"], "chunk_bwd_reverse": ["chunk_rev"],
+                "chunk_fwd_states": ["chunk_state[m1]", "chunk_o"],
+                "chunk_prepare": ["chunk_prep[bwd]"]}
+
+
+def kernel_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_FILES[kernel] + ["chunk_stream.h", "chunk_common.h", "common.h", "launch.h"]:
+        with open(os.path.join(ROOT, "gated_deltanet_layer_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def mfma_counters():
+    """kernel -> {"mfma_util": %, "exec_flop": flop per launch} from the
+    committed summary, for kernels whose sources still match."""
+    out = {}
+    if not os.path.exists(MFMA_FILE):
+        return out
+    for line in open(MFMA_FILE):
+        if not line.startswith("kernel="):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split())
+        kname = kv["kernel"]
+        if kname in KERNEL_FILES and kv.get("sources") == kernel_digest(kname):
+            out[kname] = {"mfma_util": float(kv["mfma_util"]), "exec_flop": float(kv["exec_flop"])}
+    return out
 
 
 def parse():
@@ -283,18 +337,44 @@ def layer_with_projections(w, hidden, inp, steps, warmup, dev):
                     "the pages' figure is another machine's (context, not a target)"}
 
 
-def cpu_baseline(w, sample_T):
+def cpu_baseline(w, sample_T, core, dev):
+    """The oracle's layer forward+backward on the first sample_T tokens of the
+    workload (timed), and the GPU core on the same inputs (outside every
+    timed region) compared with it: per-tensor max relative error,
+    max|gpu - oracle| / max|oracle|."""
     import numpy as np
+    import torch
     import oracle
     from gated_deltanet_layer_causal_amd import inputs as gi
     inp = gi.make_inputs(w, T=sample_T)
+    rf = gi.round_to(w.dtype)
     t0 = time.perf_counter()
-    f = oracle.layer_fwd(inp, w.hk, w.hv, w.d, w.d ** -0.5, round_fn=gi.round_bf16)
-    oracle.layer_bwd(inp, f, w.hk, w.hv, w.d, w.d ** -0.5, round_fn=gi.round_bf16)
+    f = oracle.layer_fwd(inp, w.hk, w.hv, w.d, w.d ** -0.5, round_fn=rf)
+    b = oracle.layer_bwd(inp, f, w.hk, w.hv, w.d, w.d ** -0.5, round_fn=rf)
     dt = time.perf_counter() - t0
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+
+    def t(a, dtype=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(dtype)
+
+    args = (t(inp["x"], tdt), t(inp["w_conv"]), t(inp["a"], tdt), t(inp["b"], tdt),
+            t(inp["A_log"]), t(inp["dt_bias"]), t(inp["z"], tdt), t(inp["w_norm"]),
+            torch.from_numpy(inp["cu_seqlens"]).to(dev))
+    S0 = t(inp["S0"]) if inp["S0"] is not None else None
+    dST = t(inp["dS_T"]) if inp["dS_T"] is not None else None
+    gf = core.forward(*args, S0=S0, want_final=True)
+    gb = core.backward(gf, *args, t(inp["dy"], tdt), S0=S0, dS_final=dST)
+    torch.cuda.synchronize()
+    errs = {}
+    for key, got, ref in [(k, gf[k], f[k]) for k in ("y", "o", "out", "S_final")] + \
+                         [(k, gb[k], b[k]) for k in ("dy_conv", "dx", "dw_conv", "dz", "da", "db",
+                                                     "dA_log", "ddt_bias", "dw_norm", "dS0")]:
+        g_ = got.detach().float().cpu().numpy().astype(np.float64).reshape(np.shape(ref))
+        errs[key] = float(np.max(np.abs(g_ - ref)) / max(np.max(np.abs(ref)), 1e-300))
     return {"value": sample_T / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"layer fwd+bwd on the first {sample_T} tokens of the {w.name} shape "
-                      f"({w.hk}k/{w.hv}v heads, d={w.d}), fp64 token-by-token, {dt:.1f} s"}
+                      f"({w.hk}k/{w.hv}v heads, d={w.d}), fp64 token-by-token, {dt:.1f} s",
+            "max_rel_err_gpu_vs_oracle": {k: float(f"{v:.3e}") for k, v in errs.items()}}
 
 
 def main():
@@ -314,7 +394,7 @@ def main():
     w = gi.WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
     core = GDNCore(CoreConfig(hk=w.hk, hv=w.hv, d=w.d, dtype=dt, seg_chunks=args.seg_chunks),
                    device=dev)
     inp = make_gpu_inputs(w, args.seed, dev)
@@ -330,19 +410,36 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed region: exactly `steps` steps between two events, with an
+    # event at every step boundary for the median
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     timer.active = True
-    start.record()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         step()
-    stop.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     timer.active = False
-    ms = start.elapsed_time(stop) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     value = w.T / (ms / 1e3)
     per_call = timer.mean_ms()
+    # the same steps with the 256 MB last-level cache flushed before each
+    # (a 512 MB write between steps), timed per step only
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flushed = []
+    for _ in range(args.steps):
+        flush.zero_()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        step()
+        b_.record()
+        flushed.append((a_, b_))
+    torch.cuda.synchronize()
+    flushed_ms = sorted(a_.elapsed_time(b_) for a_, b_ in flushed)
+    del flush
 
-    E = 2 if w.dtype == "bf16" else 4
+    E = 4 if w.dtype == "fp32" else 2
     single = {k: v for k, v in per_call.items() if k not in MULTI_KERNEL_CALLS}
     dom = max(single, key=single.get)
     bound, per_tok = algorithmic_per_token(dom, w.hk, w.hv, w.d, E)
@@ -356,12 +453,20 @@ def main():
     fwd_ms = sum(t for k, t in per_call.items() if k in FORWARD_CALLS)
     bwd_ms = sum(t for k, t in per_call.items() if k not in FORWARD_CALLS)
     calls = {}
+    counters = mfma_counters() if (w.name, w.dtype) == ("flash64k", "bf16") else {}
     for name, t in sorted(per_call.items(), key=lambda kv: -kv[1]):
         b, pt = algorithmic_per_token(name, w.hk, w.hv, w.d, E)
         rate = pt * w.T / (t / 1e3) / (1e9 if b == "hbm" else 1e12)
         pk = HBM_PEAK_GBS if b == "hbm" else (BF16_PEAK_TFLOPS if E == 2 else FP32_PEAK_TFLOPS)
         calls[name] = {"ms": round(t, 4), "bound": b, "achieved": round(rate, 2),
                        "frac": round(rate / pk, 4)}
+        # counter figures of the call's kernels (MFMA busy %, executed MFMA
+        # flops per launch), where the committed summary matches the sources
+        ks = [k for k in CALL_KERNELS.get(name, []) if k in counters]
+        if ks:
+            calls[name]["counters"] = {k: counters[k] for k in ks}
+    peak_mm = BF16_PEAK_TFLOPS if E == 2 else FP32_PEAK_TFLOPS
+    floor = layer_floor(w.hk, w.hv, w.d, E, w.T, peak_mm)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -374,6 +479,13 @@ def main():
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom),
                      "kernel": dom, "ms_per_launch": round(per_call[dom], 4)},
+        "median_ms_per_step": round(step_ms[len(step_ms) // 2], 4),
+        "median_ms_per_step_llc_flushed": round(flushed_ms[len(flushed_ms) // 2], 4),
+        "floor": {"layer_ms": round(floor["layer_ms"], 4), "chunk_ms": round(floor["chunk_ms"], 4),
+                  "conv_gate_norm_ms": round(floor["conv_gate_norm_ms"], 4),
+                  "frac": round(floor["layer_ms"] / ms, 4),
+                  "note": "layer floor at 100% of MFMA/HBM peak from the algorithmic per-token "
+                          "counts, over the measured step"},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
         "calls": calls,
@@ -385,7 +497,7 @@ def main():
         out["layer_with_projections"] = layer_with_projections(w, hidden, inp, args.steps,
                                                                args.warmup, dev)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens, core, dev)
     print(json.dumps(out), flush=True)
 
 

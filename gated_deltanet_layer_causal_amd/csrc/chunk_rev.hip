@@ -6,8 +6,8 @@
 //   dS     = Gam_L dS' + (scale Q)^T diag(Gam) dO - K^T diag(Gam) dR
 // It stores dS' per chunk (for the chunk-parallel gradients), dDelta and dv,
 // and dS0 at the sequence start.  The DRY instantiation (the first pass of
-// the segmented scan, which only needs each segment's dS0) issues the same
-// stores with empty ranges, so they are dropped.
+// the segmented scan, which only needs each segment's dS0) stages and stores
+// nothing.
 //
 // Same structure as the state pass (chunk_state.hip): one workgroup per
 // (sequence, value head, block of 16 * NW value rows); compute wave w keeps
@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   __shared__ RB bufA, bufB;
   // per wave: staged output rows (dS' rows k, then dDelta and dv rows t)
   typedef StageRows<T> SR;
-  __shared__ __align__(16) char stg[NW * (D + 2 * CHUNK) * SR::SB];
+  __shared__ __align__(16) char stg[DRY ? 16 : NW * (D + 2 * CHUNK) * SR::SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // waves [0, NW) compute, waves [NW, 2 NW) move the operands
@@ -224,9 +224,11 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     for (int p = 0; p < NSD; ++p) sb[p] = AO::from_acc(dS, p);
     {
       const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, DRY ? 0u : D * D * sizeof(T));
+      if constexpr (!DRY) {
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, dS[kt]);
-      SR::flush(myst, 0, D, rs, wcol, rowh, lane);
+        for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, dS[kt]);
+        SR::flush(myst, 0, D, rs, wcol, rowh, lane);
+      }
     }
 
     // dO as B operands over the chunk index, plain and scaled by scale Gam_t
@@ -267,9 +269,11 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     {
       // rows past the sequence end fall outside the buffer: dropped
       const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D + v0, DRY ? 0u : (uint32_t)L * rowb);
+      if constexpr (!DRY) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) SR::put(myst, D + 16 * tt, ps, lane, dd[tt]);
-      SR::flush(myst, D, CHUNK, rs, wcol, rowb, lane);
+        for (int tt = 0; tt < 4; ++tt) SR::put(myst, D + 16 * tt, ps, lane, dd[tt]);
+        SR::flush(myst, D, CHUNK, rs, wcol, rowb, lane);
+      }
     }
 
     // dR = M^T dDelta (= dv); then -diag(Gam) dR as B operands
@@ -294,9 +298,9 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
         gr[tt][1] = -gm.y * dr[1];
         gr[tt][2] = -gm.z * dr[2];
         gr[tt][3] = -gm.w * dr[3];
-        SR::put(myst, D + CHUNK + 16 * tt, ps, lane, dr);
+        if constexpr (!DRY) SR::put(myst, D + CHUNK + 16 * tt, ps, lane, dr);
       }
-      SR::flush(myst, D + CHUNK, CHUNK, rs, wcol, rowv, lane);
+      if constexpr (!DRY) SR::flush(myst, D + CHUNK, CHUNK, rs, wcol, rowv, lane);
     }
 
     // dS^T = Gam_L dS'^T + Q^T (scale diag(Gam) dO) - K^T (diag(Gam) dR)

@@ -16,7 +16,7 @@
 // last segment back and stores every dS_s (the gradient at the end of
 // segment s) and dS0.  Plain fp32 products in a fixed order.
 
-// One block per (sequence, value head, 32 state rows) walks the segments in
+// One block per (sequence, value head, RB state rows) walks the segments in
 // order.  Thread (row group, column group) keeps an RPT x 4 tile of the
 // state rows in registers; per segment the block stages the state rows and
 // Phi (transposed for the reverse, so both directions read Ph[k][4 cg .. +3]
@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(256) span_combine_kernel(
     const int32_t* __restrict__ segb, int Hv, const float* __restrict__ sumf,
     const float* __restrict__ sumr, const float* __restrict__ Sin, float* __restrict__ sspan,
     float* __restrict__ Sout) {
-  constexpr int RB = 32;               // state rows per block
+  constexpr int RB = D == 128 ? 16 : 32;   // state rows per block
   constexpr int NRB = D / RB;
   constexpr int CG = D / 4;            // column groups (four columns each)
   constexpr int RG = 256 / CG;         // row groups
@@ -119,7 +119,7 @@ hipError_t launch_span_combine(const gdn_shape& s, const ChunkLayout& Ly, char* 
   const float* sumr = (const float*)(ws + Ly.sumr);
   float* sspan = (float*)(ws + (rev ? Ly.dse : Ly.sst));
   auto go = [&](auto kern, int D) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)(s.n_seq * s.hv * (D / 32))), dim3(256), 0, st, segb,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(s.n_seq * s.hv * (D / (D == 128 ? 16 : 32)))), dim3(256), 0, st, segb,
                        s.hv, sumf, sumr, Sin, sspan, Sout);
     return hipGetLastError();
   };

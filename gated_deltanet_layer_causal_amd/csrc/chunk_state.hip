@@ -34,9 +34,10 @@
 //
 // Row blocks past D / BV (nblk = 2 D / BV, the first pass of the segmented
 // scan) start from identity rows and read no values, so their rows end as the
-// span's transition Phi.  The DRY instantiation issues every store with an
-// empty range (dropped), so its memory-operation counts match the stored
-// pass.
+// span's transition Phi.  The DRY instantiation (that first pass, which only
+// needs S_final) stages and stores nothing: in the K-rows form its movers'
+// counted waits leave out the stores (NFL = 0); elsewhere its stores go out
+// with empty ranges (dropped).
 #include "chunk_stream.h"
 
 namespace gdn {
@@ -200,7 +201,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   typedef StageRows<T> SR;
   constexpr int SRR = D + 2 * CHUNK;   // staged rows per compute wave
   constexpr int SROW_R = D, SROW_D16 = D + CHUNK;
-  __shared__ __align__(16) char stg[SB::KR ? 2 * NW * SRR * SR::SB : 16];
+  __shared__ __align__(16) char stg[SB::KR && !DRY ? 2 * NW * SRR * SR::SB : 16];
   auto stage_of = [&](int64_t c, int w) __attribute__((always_inline)) -> char* {
     return stg + (int)((((c - c_begin) & 1) * NW + w) * SRR * SR::SB);
   };
@@ -208,17 +209,19 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   auto put_rows = [&](auto tag, char* st, int row0, const floatx4 (&x)[4]) __attribute__((always_inline)) {
     typedef decltype(tag) E;
     static_assert(sizeof(E) == sizeof(T), "same row layout");
+    if constexpr (!DRY) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) StageRows<E>::put(st, row0 + 16 * tt, ps, lane, x[tt]);
+      for (int tt = 0; tt < 4; ++tt) StageRows<E>::put(st, row0 + 16 * tt, ps, lane, x[tt]);
+    }
   };
   // (movers) chunk cp's staged rows of compute wave `wave` to the state, R
   // and Delta (compute type) buffers; token rows past the sequence
   // end fall outside the buffers and are dropped.  With valid false every
   // store is still issued but dropped (an empty range), so each step issues
-  // the same count.
-  constexpr int NFL = SR::stores(D) + 2 * SR::stores(CHUNK);
+  // the same count.  The dry pass stages and stores nothing (NFL = 0).
+  constexpr int NFL = DRY ? 0 : SR::stores(D) + 2 * SR::stores(CHUNK);
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
-    valid = valid && !DRY;
+    if constexpr (DRY) return;
     const char* st = stage_of(cp, wave);
     const int64_t ca = valid ? cp : c_begin;
     const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
@@ -450,24 +453,30 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     for (int64_t c = c_begin; c < c_end; c += 3) {
       {
         char* st = stage_of(c, wave);
+        if constexpr (!DRY) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+          for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+        }
         compute(bufA, c, st);
       }
       lds_barrier();
       if (c + 1 >= c_end) break;
       {
         char* st = stage_of(c + 1, wave);
+        if constexpr (!DRY) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+          for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+        }
         compute(bufB, c + 1, st);
       }
       lds_barrier();
       if (c + 2 >= c_end) break;
       {
         char* st = stage_of(c + 2, wave);
+        if constexpr (!DRY) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+          for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
+        }
         compute(bufC, c + 2, st);
       }
       lds_barrier();
