@@ -5,7 +5,8 @@
 // gradient of the state leaving it), and R, Delta of the forward:
 //   dM = dDelta R^T,  dTinv = strictly-lower(dM diag(beta)),
 //   Y  = dTinv Tinv^T,  dA = strictly-lower(-Tinv^T Y),  dP = lower(dO Delta^T)
-//   WA = dA o (beta_t D),  WS = WA + WA^T  (symmetric)
+//   WA = dA o (beta_t D),  WS = WA + WA^T  (symmetric; WA is strictly lower,
+//   so WS takes WA in its lower and WA^T in its upper triangle)
 //   dq = scale [diag(Gam) dO S + (dP o D) K]
 //   dk = scale (dP o D)^T Q - diag(Gam) dR S + diag(dec) Delta dS' + WS K
 //   dbeta_s = sum_t dM[t,s] Tinv[t,s] + sum_u dA[s,u] D[s,u] k_s.k_u
@@ -16,7 +17,8 @@
 // of the group and sums dq, dk over them in registers (ascending head
 // order, no atomics).  Per head:
 //  - the token-major tiles dO, Delta, dR, R come into LDS by direct copies
-//    (issued while the previous head finishes);
+//    (issued while the previous head finishes); for bf16 data the fp16 Delta
+//    of the saved-state pass is rounded to bf16 in place, once;
 //  - phase A, pair products, as 64 x 64 tiles whose columns are a token t
 //    and rows the other token s (every lane holds four consecutive s of one
 //    t; waves w and w + 4 own the same 16 tokens t).  Waves 0-3 take the
@@ -44,13 +46,12 @@ template <typename T, int D> struct GradLds {
   static constexpr int LDP = CHUNK + 16 / (int)sizeof(T);     // padded 64-wide rows
   static constexpr int NKT = D / 16;                          // key tiles (phase-B waves per token group)
   T tO[TT::PIECES * TT::EPP];     // dO
-  T tDl[TT::PIECES * TT::EPP];    // Delta (16-bit data: fp16 values, converted where read)
+  T tDl[TT::PIECES * TT::EPP];    // Delta (bf16 data: the fp16 values, rounded to bf16 in place)
   T tdR[TT::PIECES * TT::EPP];    // dR
   T tR[TT::PIECES * TT::EPP];     // R
   T YT[CHUNK][LDP];               // Y^T: row s, column u
   T dPD[CHUNK][LDP];              // dP o D: row t, columns s in accumulator order
   T dPDt[CHUNK][LDP];             // scale (dP o D)^T: row s, columns t in accumulator order
-  T WA[CHUNK][LDP];               // WA: row t, column s
   T WS[CHUNK][LDP];               // WA + WA^T: row x, columns u in accumulator order
   float E[CHUNK][CHUNK + 1];      // pair terms of dg
   // Tinv (columns in accumulator order), copied for 16-bit types, whose
@@ -159,19 +160,9 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   auto tfr = [&](const T* tile, int r, int p) __attribute__((always_inline)) -> frag {
     return rdf(tile, TT::at(r, pcol(p)));
   };
-  // the same from the Delta tile, which for 16-bit data holds the fp16 Delta
-  // of the saved-state pass (one rounding more to bf16 here)
+  // the same from the Delta tile (in the storage type once converted)
   auto dlfr = [&](int r, int p) __attribute__((always_inline)) -> frag {
-    if constexpr (sizeof(T) == 2) {
-      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-      const h8 x = __builtin_bit_cast(h8, tfr(sm.tDl, r, p));
-      frag y;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = (T)(float)x[j];
-      return y;
-    } else {
-      return tfr(sm.tDl, r, p);
-    }
+    return tfr(sm.tDl, r, p);
   };
 
   // ---- per workgroup: k_s . k_t at the phase-A positions (Tinv-chain
@@ -410,6 +401,21 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     derive();
     issue_fence();
     __syncthreads();   // this head's tiles, gates and phase-A operands are in
+    if constexpr (__is_same(T, bf16)) {
+      // the saved-state pass's fp16 Delta, rounded to bf16 in place (one
+      // 16-byte piece per thread and step), before any wave reads it
+#pragma unroll
+      for (int j = 0; j < (TT::PIECES + 511) / 512; ++j) {
+        if (TT::PIECES % 512 != 0 && tid + 512 * j >= TT::PIECES) break;
+        u32x4* pp = reinterpret_cast<u32x4*>(sm.tDl) + tid + 512 * j;
+        const u32x4 w = *pp;
+        u32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = pack2<bf16>(lo16<fp16>(w[e]), hi16<fp16>(w[e]));
+        *pp = y;
+      }
+      lds_barrier();
+    }
     // =============== phase A: pair products (s x t tiles, t = tl)
     const double gt = sm.gam[tl];
     const float bt = sm.bet[tl];
@@ -524,28 +530,31 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           rb += dAD * kks[i];
           wa[i] = dAD * bt;
         }
-        store4(&sm.WA[tl][16 * st + g4], wa[0], wa[1], wa[2], wa[3]);
+        // WS: row tl takes wa for s <= tl (zero on the diagonal), row s
+        // takes it at column tl for s < tl; every element has one writer
+        const int s0 = 16 * st + g4;
+        if (s0 + 3 <= tl) {
+          store4(&sm.WS[tl][acc_col<T>(s0)], wa[0], wa[1], wa[2], wa[3]);
+        } else if (s0 <= tl) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (s0 + i <= tl) sm.WS[tl][acc_col<T>(s0) + i] = (T)wa[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (s0 + i < tl) sm.WS[s0 + i][acc_col<T>(tl)] = (T)wa[i];
       }
       rb += __shfl_xor(rb, 16, 64);
       rb += __shfl_xor(rb, 32, 64);
       if (g == 0) sm.rowB[tl] = rb;
     }
-    __syncthreads();
-    if (role == 1) {
+    __syncthreads();   // WS and the dA part of the pair terms are in
+    if (role == 1) {   // (E is read after phase B's barrier)
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.E[tl][16 * st + g4 + i] += ep[st][i];
     }
-    // WS = WA + WA^T (columns in accumulator order)
-#pragma unroll
-    for (int j = 0; j < CHUNK * CHUNK / 4 / 512; ++j) {
-      const int it = tid + 512 * j, x = it / (CHUNK / 4), u4 = (it % (CHUNK / 4)) * 4;
-      const floatx4 a = ld4(&sm.WA[x][u4]);
-      store4(&sm.WS[x][acc_col<T>(u4)], a[0] + to_f(sm.WA[u4][x]), a[1] + to_f(sm.WA[u4 + 1][x]),
-             a[2] + to_f(sm.WA[u4 + 2][x]), a[3] + to_f(sm.WA[u4 + 3][x]));
-    }
-    __syncthreads();
     {   // R and Tinv are no longer read for this head
       const bool live = hh + 1 < G;
       copy_r(live ? h + 1 : h, live);
