@@ -63,7 +63,7 @@ template <typename T, int D> struct GradLds {
   double gam[CHUNK];
   float bet[CHUNK], Gm[CHUNK], dc[CHUNK];
   float colB[4][CHUNK], rowB[CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
-  float segE[4][CHUNK], boxE[4][CHUNK], red[8];
+  float boxE[4][CHUNK], red[8];
   // k_s . k_t (row t, column s) for 16-bit types, in fp16 (|k_s . k_t| <= 1
   // for the L2-normalised keys): there the Tinv-chain waves read it from LDS
   // and leave their registers to phase B; fp32 keeps it in registers
@@ -629,40 +629,44 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     // cancel when that decay is strong:
     //  - pair terms E[t][s] (s < t) add to dgam_t and subtract from dgam_s;
     //    their part of dg_i is the box sum over t >= i > s, taken as column
-    //    suffix sums over rows, then row prefix sums;
+    //    suffix sums over rows, then sums along rows;
     //  - the chunk-start terms y_t (rowX, and the state term at the last
     //    token) enter as the suffix sum over t >= i;
     //  - the decay-to-chunk-end terms z_t enter dgam as -z_t and as +sum z
     //    at the last token: their part is the prefix sum over t < i.
     if (wave < 4) {
-      // column suffix sums within each 16-row block (wave = row block)
-      const int cidx = lane, rb0 = 16 * wave;
-      float acc = 0.f;
+      // Wave w takes columns s = 16 w + j of E (j = lane % 16) over rows
+      // 16 q .. 16 q + 15 (q = lane / 16).  Suffix sums down the quarter plus
+      // the later quarters' column totals give C[i][s] = sum_{t >= i} E[t][s];
+      // the block's part of the box sum of row i is the sum of C[i][s] over
+      // its columns s < i, for the quarter's 16 rows at once: a
+      // reduce-scatter over the 16 lanes, four DPP swaps that each pair lanes
+      // differing in one bit (a lane keeps the half of its rows whose bit
+      // matches its own and adds the partner's copy), leaving row 16 q + j in
+      // lane j.
+      const int j = lane & 15, q = lane >> 4, s = 16 * wave + j;
+      float x[16];
 #pragma unroll
-      for (int r = 15; r >= 0; --r) {
-        acc += sm.E[rb0 + r][cidx];
-        sm.E[rb0 + r][cidx] = acc;
-      }
-      sm.segE[wave][cidx] = acc;
-    }
-    lds_barrier();
-    if (wave < 4) {
-      // add the later row blocks, then the row-prefix part of each box sum
-      const int cidx = lane, rb0 = 16 * wave;
-      float off = 0.f;
-      for (int w = 3; w > wave; --w) off += sm.segE[w][cidx];
+      for (int r = 0; r < 16; ++r) x[r] = sm.E[16 * q + r][s];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.E[rb0 + r][cidx] += off;
-    }
-    lds_barrier();
-    if (wave < 4) {
-      // token i = lane sums columns s < i of the column block owned by this wave
-      const int i = lane, cb0 = 16 * wave;
-      float part = 0.f;
+      for (int r = 14; r >= 0; --r) x[r] += x[r + 1];
+      const float c1 = __shfl(x[0], j + 16, 64), c2 = __shfl(x[0], j + 32, 64),
+                  c3 = __shfl(x[0], j + 48, 64);
+      const float off = q == 0 ? (c3 + c2) + c1 : q == 1 ? c3 + c2 : q == 2 ? c3 : 0.f;
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-        if (cb0 + s < i) part += sm.E[i][cb0 + s];
-      sm.boxE[wave][i] = part;
+      for (int r = 0; r < 16; ++r) x[r] = s < 16 * q + r ? x[r] + off : 0.f;
+      auto split = [&](auto ctrl, int half, bool hi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < half; ++r) {
+          const float send = hi ? x[r] : x[r + half], keep = hi ? x[r + half] : x[r];
+          x[r] = keep + dpp_f<decltype(ctrl)::value>(send);
+        }
+      };
+      split(std::integral_constant<int, 0x140>{}, 8, (j & 8) != 0);   // row_mirror: bit 3
+      split(std::integral_constant<int, 0x141>{}, 4, (j & 4) != 0);   // row_half_mirror: bit 2
+      split(std::integral_constant<int, 0x4E>{}, 2, (j & 2) != 0);    // lane ^ 2
+      split(std::integral_constant<int, 0xB1>{}, 1, (j & 1) != 0);    // lane ^ 1
+      sm.boxE[wave][16 * q + j] = x[0];
     }
     lds_barrier();
     if (wave == 0) {
@@ -686,7 +690,8 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         dbeta[(t0 + t) * Hv + h] = db;
       }
     }
-    lds_barrier();   // the gates of this head are no longer read
+    // (since phase B's barrier only wave 0 reads the gates, and it alone
+    // writes the next head's)
     put_gates();
   }
 
