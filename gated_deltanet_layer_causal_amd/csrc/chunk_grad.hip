@@ -164,6 +164,19 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   auto dlfr = [&](int r, int p) __attribute__((always_inline)) -> frag {
     return tfr(sm.tDl, r, p);
   };
+  // gam of tokens s0 .. s0 + 3 (s0 % 4 == 0), and the decay factor
+  // e^(a - b) where keep holds, else 0.  Branch free: the masked exponent is
+  // a large negative number, so every lane evaluates the exponential
+  // (otherwise the compiler puts each masked gam load and exponential
+  // behind a branch of its own, serialising the loads).
+  typedef double d2 __attribute__((ext_vector_type(2)));
+  auto gam4 = [&](int s0, double (&o)[4]) __attribute__((always_inline)) {
+    const d2 a = *reinterpret_cast<const d2*>(&sm.gam[s0]), b = *reinterpret_cast<const d2*>(&sm.gam[s0 + 2]);
+    o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+  };
+  auto decay = [&](double a, double b, bool keep) __attribute__((always_inline)) -> float {
+    return dexp<T>(keep ? a - b : -1e30);
+  };
 
   // ---- per workgroup: k_s . k_t at the phase-A positions (Tinv-chain
   // waves), the wave's row of K^T and Q^T tiles (phase-B A operands), and
@@ -480,17 +493,21 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const floatx4 pv = pE(st);
+        double gs[4];
+        gam4(16 * st + g4, gs);
         float pd[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * st + g4 + i;
-          const float Dts = s <= tl ? dexp<T>(gt - sm.gam[s]) : 0.f;
+          const float Dts = decay(gt, gs[i], s <= tl);
           ep[st][i] = (s < tl && tl < L) ? dPt[st][i] * pv[i] : 0.f;
           pd[i] = dPt[st][i] * Dts;
         }
         store4(&sm.dPD[tl][acc_col<T>(16 * st + g4)], pd[0], pd[1], pd[2], pd[3]);
       }
       // scale (dP o D)^T from the dP tiles: rows t = 16 tw + 4 g + i, column s
+      double gtt[4];
+      gam4(16 * tw + g4, gtt);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int s = 16 * st + c16;
@@ -499,7 +516,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * tw + g4 + i;
-          pd[i] = s <= t ? scale * dPn[st][i] * dexp<T>(sm.gam[t] - gs) : 0.f;
+          pd[i] = scale * dPn[st][i] * decay(gtt[i], gs, s <= t);
         }
         store4(&sm.dPDt[s][acc_col<T>(16 * tw + g4)], pd[0], pd[1], pd[2], pd[3]);
       }
@@ -514,6 +531,8 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const floatx4 kks = kkv(st);
+        double gs[4];
+        gam4(16 * st + g4, gs);
         floatx4 da = zero4();
 #pragma unroll
         for (int p = 0; p < NSC; ++p)
@@ -523,7 +542,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * st + g4 + i;
           const bool lower = s < tl;
-          const float Dts = lower ? dexp<T>(gt - sm.gam[s]) : 0.f;
+          const float Dts = decay(gt, gs[i], lower);
           const float dA = lower ? -da[i] : 0.f;
           const float dAD = dA * Dts;
           sm.E[tl][s] = tl < L ? dAD * bt * kks[i] : 0.f;
