@@ -129,6 +129,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
   constexpr bool KROWS = BWD && sizeof(T) == 2;
   typedef PrepSmem<T, D, KROWS> SM;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  static_assert(offsetof(SM, gam) % 16 == 0 && offsetof(SM, bet) % 16 == 0, "16-byte reads of gam, bet");
   auto& sK = sm.st().K;
   auto& su = sm.st().u;
   auto& sA = sm.hd().A;
@@ -271,15 +272,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     T* PTout = Ptb + ((int64_t)c * Hv + h) * CHUNK * CHUNK;
     CT (*Ps)[SM::PLD] = reinterpret_cast<CT (*)[SM::PLD]>(&sTi[0][0]);
     T (*Pts)[SM::PLD] = reinterpret_cast<T (*)[SM::PLD]>(&sTi[0][0] + CHUNK * SM::PLD / 2);
+    // (the gam values of this lane's rows are read once, and masked
+    // exponents are clamped rather than branched around: a branch per
+    // element would serialise the gam loads)
+    typedef double d2 __attribute__((ext_vector_type(2)));
+    const d2 gra = *reinterpret_cast<const d2*>(&sm.gam[rbase]), grb = *reinterpret_cast<const d2*>(&sm.gam[rbase + 2]);
+    const double gr[4] = {gra[0], gra[1], grb[0], grb[1]};
+    const float4 br = *reinterpret_cast<const float4*>(&sm.bet[rbase]);
+    const float brv[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = 16 * j + ccol;
+      const double gsj = sm.gam[s];
       float pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = rbase + e;
-        const float dec = dexp<T>(sm.gam[t] - sm.gam[s <= t ? s : t]);  // masked before exp
-        sA[t][s] = (s < t) ? sm.bet[t] * dec * kk[j][e] : 0.f;
+        const float dec = dexp<T>(s <= t ? gr[e] - gsj : 0.0);  // masked before exp
+        sA[t][s] = (s < t) ? brv[e] * dec * kk[j][e] : 0.f;
         pv[e] = (s <= t) ? dec * scale * qk[j][e] : 0.f;
       }
       if constexpr (BWD) {
@@ -288,11 +298,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         else
           store4(PTout + s * CHUNK + acc_col<T>(rbase), pv[0], pv[1], pv[2], pv[3]);
       }
-      const int t = 16 * j + ccol;
+      const int t = 16 * j + ccol;   // (= s: gam[t] is gsj)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s2 = rbase + e;
-        pv[e] = (s2 <= t) ? dexp<T>(sm.gam[t] - sm.gam[s2]) * scale * kq[j][e] : 0.f;
+        pv[e] = dexp<T>(s2 <= t ? gsj - gr[e] : -1e30) * scale * kq[j][e];
       }
       if constexpr (SM::STAGE_P)
         store4(&Ps[t][acc_col<CT>(rbase)], pv[0], pv[1], pv[2], pv[3]);

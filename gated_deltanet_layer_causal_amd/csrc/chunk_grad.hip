@@ -113,6 +113,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   static_assert(D == 32 || D == 128, "head dim 32 or 128");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   GL& sm = *reinterpret_cast<GL*>(smem_raw);
+  static_assert(offsetof(GL, gam) % 16 == 0, "16-byte reads of gam");
 
   // Indices derived from the thread and wave numbers are recomputed at the
   // top of every head (from laundered copies, below), so that the compiler

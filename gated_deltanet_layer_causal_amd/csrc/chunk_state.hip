@@ -109,12 +109,20 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   const int64_t HvD = (int64_t)Hv * D;
 
   floatx4 S[NKT];   // S^T tiles: rows k = 16 kt + g4 + i, column v0 + vcol
+  // (one uniform branch around all the loads, so that they are issued
+  // together rather than each behind a branch and a wait of its own)
+  if (S0 && !phi) {
+    const float* s0r = S0 + (((int64_t)n * Hv + h) * D + v0 + vcol) * D + g4;
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[kt][i] = phi ? (v0 - D + vcol == 16 * kt + g4 + i ? 1.f : 0.f)
-                     : S0 ? S0[(((int64_t)n * Hv + h) * D + v0 + vcol) * D + 16 * kt + g4 + i] : 0.f;
+      for (int i = 0; i < 4; ++i) S[kt][i] = s0r[16 * kt + i];
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[kt][i] = phi && v0 - D + vcol == 16 * kt + g4 + i ? 1.f : 0.f;
+  }
 
   const int4 sp = reinterpret_cast<const int4*>(spans)[n];
   const int64_t c_begin = sp.x, c_end = sp.y;
