@@ -551,18 +551,15 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           wa[i] = dAD * bt;
         }
         // WS: row tl takes wa for s <= tl (zero on the diagonal), row s
-        // takes it at column tl for s < tl; every element has one writer
-        const int s0 = 16 * st + g4;
-        if (s0 + 3 <= tl) {
-          store4(&sm.WS[tl][acc_col<T>(s0)], wa[0], wa[1], wa[2], wa[3]);
-        } else if (s0 <= tl) {
+        // takes it at column tl for s < tl; every element has one writer.
+        // A store that is not this lane's goes to a padding column of the
+        // same row instead (branch free).
+        const int s0 = 16 * st + g4, padc = CHUNK + (c16 & (GL::LDP - CHUNK - 1));
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (s0 + i <= tl) sm.WS[tl][acc_col<T>(s0) + i] = (T)wa[i];
+        for (int i = 0; i < 4; ++i) {
+          sm.WS[tl][s0 + i <= tl ? acc_col<T>(s0) + i : padc] = (T)wa[i];
+          sm.WS[s0 + i][s0 + i < tl ? acc_col<T>(tl) : padc] = (T)wa[i];
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (s0 + i < tl) sm.WS[s0 + i][acc_col<T>(tl)] = (T)wa[i];
       }
       rb += __shfl_xor(rb, 16, 64);
       rb += __shfl_xor(rb, 32, 64);
