@@ -113,6 +113,7 @@ struct ChunkLayout {
   size_t k16w;        // CT [nt_max][hk][64][dk]: K rows, columns in accumulator order
                       // (backward, 16-bit types: the saved-state pass reads these in place of W, K^T)
   size_t ptb;         // T [nt_max][hv][64][64]: P^T (backward)
+  size_t kkw;         // CT [nt_max][hk][64][64]: K K^T of each chunk (backward)
   size_t bw;          // fp32 [nt_max][hv][64]: beta_t, zero past the chunk end (backward)
   size_t tib;         // T [nt_max][hv][2][64][64]: Tinv (columns in accumulator order), Tinv^T (backward)
   size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
@@ -165,6 +166,7 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.ktb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.qtb = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
   L.ptb = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
+  L.kkw = off; off = align256(off + es * (size_t)L.nt_max * s.hk * CHUNK * CHUNK);
   L.bw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.tib = off; off = align256(off + es * (size_t)L.nt_max * s.hv * 2 * CHUNK * CHUNK);
   L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);

@@ -62,7 +62,8 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t* __restr
 
 // ---------------------------------------------------------------------------
 // Preparation, one workgroup per (chunk, key head): K K^T and Q K^T once
-// (MFMA) and K^T to the workspace, then per value head of the group: gam, A,
+// (MFMA) and K^T (and in backward mode K K^T) to the workspace, then per
+// value head of the group: gam, A,
 // Tinv (fp32), and the MFMA operands M = Tinv diag(beta), P and
 // W = M diag(Gam) K, with the per-token factors Gam_t and dec_t.
 template <typename T, int D>
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     typename Compute<T>::type* __restrict__ Ktw, typename Compute<T>::type* __restrict__ Q16w,
     typename Compute<T>::type* __restrict__ K16w, float* __restrict__ Gw, float* __restrict__ Dw,
     T* __restrict__ Kb, T* __restrict__ Ktb, T* __restrict__ Qtb, T* __restrict__ Ptb,
-    float* __restrict__ Bw, T* __restrict__ Tib) {
+    float* __restrict__ Bw, T* __restrict__ Tib, typename Compute<T>::type* __restrict__ KKw) {
   typedef typename Compute<T>::type CT;
   typedef Mma<CT> MM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -161,6 +162,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
   const int rbase = 16 * wave + 4 * (lane >> 4);
   const int ccol = lane & 15;
   const int r16 = lane & 15;
+  if constexpr (BWD) {
+    // K K^T (compute type) for the chunk gradients, in 16 x 16 blocks of 256
+    // contiguous elements: block (R, C) at 256 (4 R + C), element (r, c) of
+    // a block at 4 (16 (c / 4) + r) + c % 4.  K K^T is symmetric, so this
+    // lane's tile values k_{rbase+e} . k_s (s = 16 j + ccol) are row s,
+    // columns rbase .. rbase + 3: block (j, wave), offset 4 lane + e -- each
+    // wave writes whole 512-byte blocks.
+    typename Compute<T>::type* ko = KKw + ((int64_t)c * (Hv / G) + kh) * CHUNK * CHUNK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store4(ko + (4 * j + wave) * 256 + 4 * lane, kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
+  }
   {
     // Q rows (compute type, zero past the chunk end, columns in accumulator
     // order; read only by the forward pass without saved states) to the
@@ -414,7 +426,8 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
                        (float*)(ws + Ly.dw), BWD ? (T*)(ws + Ly.kb) : nullptr,
                        BWD ? (T*)(ws + Ly.ktb) : nullptr, BWD ? (T*)(ws + Ly.qtb) : nullptr,
                        BWD ? (T*)(ws + Ly.ptb) : nullptr, BWD ? (float*)(ws + Ly.bw) : nullptr,
-                       BWD ? (T*)(ws + Ly.tib) : nullptr);
+                       BWD ? (T*)(ws + Ly.tib) : nullptr,
+                       BWD ? (typename Compute<T>::type*)(ws + Ly.kkw) : nullptr);
   }
   return hipGetLastError();
 }

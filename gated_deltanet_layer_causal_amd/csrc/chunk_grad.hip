@@ -13,9 +13,12 @@
 // and dg from every place gam enters, assembled without cancellation (the
 // last phase below).
 //
-// One workgroup of eight waves per (chunk, key head) walks the G value heads
-// of the group and sums dq, dk over them in registers (ascending head
-// order, no atomics).  Per head:
+// One workgroup of eight waves per (GRAD_ITEMS consecutive chunks, key head)
+// walks, for each chunk, the G value heads of the group and sums dq, dk over
+// them in registers (ascending head order, no atomics).  The operands of the
+// next head are requested while a head finishes, across chunk boundaries
+// too (K K^T, the K^T and Q^T rows and q, k of the next chunk with its first
+// head), so only a workgroup's first head waits for memory.  Per head:
 //  - the token-major tiles dO, Delta, dR, R come into LDS by direct copies
 //    (issued while the previous head finishes); for bf16 data the fp16 Delta
 //    of the saved-state pass is rounded to bf16 in place, once;
@@ -41,6 +44,9 @@
 
 namespace gdn {
 
+// Consecutive chunks per workgroup of the gradient kernel.
+constexpr int GRAD_ITEMS = 4;
+
 template <typename T, int D> struct GradLds {
   typedef Tile<T, CHUNK, D> TT;                               // token-major tile
   static constexpr int LDP = CHUNK + 16 / (int)sizeof(T);     // padded 64-wide rows
@@ -64,11 +70,12 @@ template <typename T, int D> struct GradLds {
   float bet[CHUNK], Gm[CHUNK], dc[CHUNK];
   float colB[4][CHUNK], rowB[CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
   float boxE[4][CHUNK], red[8];
-  // k_s . k_t (row t, column s) for 16-bit types, in fp16 (|k_s . k_t| <= 1
-  // for the L2-normalised keys): there the Tinv-chain waves read it from LDS
-  // and leave their registers to phase B; fp32 keeps it in registers
-  static constexpr bool KK_LDS = sizeof(T) == 2;
-  fp16 KK[KK_LDS ? CHUNK : 1][CHUNK + 4];
+  // k_t . k_s, the preparation's K K^T in the compute type (fp16 for 16-bit
+  // data: |k_t . k_s| <= 1 for the L2-normalised keys) and in its layout of
+  // 16 x 16 blocks (element (t, s) at 256 (4 (t / 16) + s / 16) +
+  // 4 (16 ((s % 16) / 4) + t % 16) + s % 4), by plain direct copy
+  typedef typename Compute<T>::type KKT;
+  KKT KK[CHUNK * CHUNK];
 };
 
 // Four consecutive elements as floats (8 bytes for 16-bit types).
@@ -97,7 +104,8 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     const typename Compute<T>::type* __restrict__ Pw, const T* __restrict__ Tib,
     const T* __restrict__ Ktb, const T* __restrict__ Qtb, const T* __restrict__ hst,
     const T* __restrict__ dhst, const T* __restrict__ Rw, const void* __restrict__ Dlw,
-    const T* __restrict__ ddw, const T* __restrict__ dout, const T* __restrict__ dvo,
+    const T* __restrict__ ddw, const typename Compute<T>::type* __restrict__ KKw,
+    const T* __restrict__ dout, const T* __restrict__ dvo,
     int64_t lddv, T* __restrict__ dq, T* __restrict__ dk, int64_t lddq, int64_t lddk,
     float* __restrict__ dg, float* __restrict__ dbeta) {
   typedef typename Compute<T>::type CT;
@@ -122,12 +130,20 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   int tid = threadIdx.x, lane = tid & 63;
   int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
-  const int64_t c = blockIdx.x;
   const int kh = blockIdx.y;
-  if (c >= seq_off[n_seq]) return;
-  int64_t t0;
-  int L;
-  chunk_span(seq_off, cu, n_seq, c, t0, L);
+  const int64_t n_chunks = seq_off[n_seq];
+  const int64_t c_first = (int64_t)blockIdx.x * GRAD_ITEMS;
+  if (c_first >= n_chunks) return;
+  const int n_items = (int)(n_chunks - c_first < GRAD_ITEMS ? n_chunks - c_first : GRAD_ITEMS);
+  // a work item: chunk c, its first token, its length
+  struct Item { int64_t c, t0; int L; };
+  auto item_of = [&](int64_t cc) __attribute__((always_inline)) -> Item {
+    Item it;
+    it.c = cc;
+    chunk_span(seq_off, cu, n_seq, cc, it.t0, it.L);
+    return it;
+  };
+  Item cur = item_of(c_first);   // the item being computed
   const int64_t HvD = (int64_t)Hv * D;
   const int Hk = Hv / G;
   int role = wave >> 2;                     // phase A: 0 Tinv chain, 1 dP side
@@ -179,44 +195,27 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     return dexp<T>(keep ? a - b : -1e30);
   };
 
-  // ---- per workgroup: k_s . k_t at the phase-A positions (Tinv-chain
-  // waves), the wave's row of K^T and Q^T tiles (phase-B A operands), and
-  // q, k at the phase-B positions
-  floatx4 kk[4];
-  if (role == 0) {
-    const uint32_t ldb = (uint32_t)(ldk * sizeof(T));
-    const auto rk = buffer_of(k + t0 * ldk + (int64_t)kh * D, (uint32_t)L * ldb);
-    frag kb[NSD];
+  // ---- per item: K K^T into LDS (direct copies, read at the phase-A
+  // positions by the Tinv-chain waves) ...
+  constexpr int KKE = 16 / (int)sizeof(typename GL::KKT);   // elements per 16-byte piece
+  auto copy_kk = [&](const Item& it, bool live) __attribute__((always_inline)) {
+    const char* src = reinterpret_cast<const char*>(KKw + (it.c * Hk + kh) * CHUNK * CHUNK);
+    const uint32_t bytes = live ? CHUNK * CHUNK * sizeof(typename GL::KKT) : 0u;
 #pragma unroll
-    for (int p = 0; p < NSD; ++p) kb[p] = buffer_frag<T>(rk, (uint32_t)tl * ldb + (uint32_t)pcol(p) * sizeof(T));
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      kk[st] = zero4();
-#pragma unroll
-      for (int p = 0; p < NSD; ++p)
-        kk[st] = MM::mma(buffer_frag<T>(rk, (uint32_t)(16 * st + c16) * ldb + (uint32_t)pcol(p) * sizeof(T)),
-                         kb[p], kk[st]);
-      if constexpr (GL::KK_LDS)
-        store4(&sm.KK[tl][16 * st + g4], kk[st][0], kk[st][1], kk[st][2], kk[st][3]);
+    for (int j = 0; j < CHUNK * CHUNK / KKE / 512; ++j) {
+      const int s = (j * 8 + wave) * 64 + lane;
+      copy_to_lds(buffer_of(src, bytes), sm.KK + (j * 8 + wave) * 64 * KKE, (uint32_t)s * 16u, 0);
     }
-  }
-  // (read back by the lane that wrote it: no barrier)
-  auto kkv = [&](int st) __attribute__((always_inline)) -> floatx4 {
-    if constexpr (GL::KK_LDS) return ld4(&sm.KK[tl][16 * st + g4]);
-    else return kk[st];
   };
+  // k_tl . k_s for s = 16 st + g4 .. + 3: block (tw, st), offset 4 lane
+  auto kkv = [&](int st) __attribute__((always_inline)) -> floatx4 {
+    return ld4(sm.KK + 256 * (4 * tw + st) + 4 * lane);
+  };
+  // ... the wave's rows of the K^T and Q^T tiles (phase-B A operands) and
+  // q, k at the phase-B positions (raw storage-type values, converted where
+  // used: laundered there, so the converted values are not hoisted out of
+  // the head loop, where they would take twice the registers)
   frag kta[NSC], qta[NSC];
-  {
-    const int64_t r = ((int64_t)c * Hk + kh) * D * CHUNK + (int64_t)(16 * kt + c16) * CHUNK;
-#pragma unroll
-    for (int p = 0; p < NSC; ++p) {
-      kta[p] = rdf(Ktb + r, pcol(p));
-      qta[p] = rdf(Qtb + r, pcol(p));
-    }
-  }
-  // (raw storage-type values, converted where used: laundered there, so the
-  // converted values are not hoisted out of the head loop, where they would
-  // take twice the registers)
   typedef typename std::conditional<sizeof(T) == 2, u32x2, u32x4>::type raw4;
   raw4 q4[TTW], k4[TTW];
   auto raw_f4 = [&](const raw4& r) __attribute__((always_inline)) -> floatx4 {
@@ -225,10 +224,16 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     else
       return __builtin_bit_cast(floatx4, r);
   };
-  {
+  auto load_item = [&](const Item& it) __attribute__((always_inline)) {
+    const int64_t r = ((int64_t)it.c * Hk + kh) * D * CHUNK + (int64_t)(16 * kt + c16) * CHUNK;
+#pragma unroll
+    for (int p = 0; p < NSC; ++p) {
+      kta[p] = rdf(Ktb + r, pcol(p));
+      qta[p] = rdf(Qtb + r, pcol(p));
+    }
     const uint32_t ldkb = (uint32_t)(ldk * sizeof(T)), ldqb = (uint32_t)(ldq * sizeof(T));
-    const auto rk = buffer_of(k + t0 * ldk + (int64_t)kh * D, (uint32_t)L * ldkb);
-    const auto rq = buffer_of(q + t0 * ldq + (int64_t)kh * D, (uint32_t)L * ldqb);
+    const auto rk = buffer_of(k + it.t0 * ldk + (int64_t)kh * D, (uint32_t)it.L * ldkb);
+    const auto rq = buffer_of(q + it.t0 * ldq + (int64_t)kh * D, (uint32_t)it.L * ldqb);
 #pragma unroll
     for (int tt = 0; tt < TTW; ++tt) {
       const int t = 16 * (tg * TTW + tt) + c16, kc = 16 * kt + g4;
@@ -240,18 +245,14 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         k4[tt] = __builtin_bit_cast(raw4, __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)t * ldkb + (uint32_t)kc * 4, 0, 0));
       }
     }
-  }
-  floatx4 dQa[TTW], dKa[TTW];
-#pragma unroll
-  for (int tt = 0; tt < TTW; ++tt) dQa[tt] = dKa[tt] = zero4();
-
+  };
   // ---- per head: the token tiles (direct copies by the first NCW waves,
   // rows past the chunk end re-read its last row) ...
   constexpr int NCW = TT::PIECES / 64 < 8 ? TT::PIECES / 64 : 8;
   // (live false: an empty source range, every copy reads zero and touches no
   // memory; the requests are issued all the same, so the wait counts after
   // them do not depend on whether a next head exists)
-  auto copy_rows = [&](T* dst, const T* src, uint32_t ldb, bool live) __attribute__((always_inline)) {
+  auto copy_rows = [&](T* dst, const T* src, uint32_t ldb, int L, bool live) __attribute__((always_inline)) {
     if (NCW == 8 || wave < NCW) {   // (a test the compiler can drop when all waves copy)
       const auto rs = buffer_of(src, live ? (uint32_t)L * ldb : 0u);
 #pragma unroll
@@ -263,24 +264,24 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     }
   };
   // (R is read in phase A only, so it comes with Tinv, a phase earlier)
-  auto copy_head = [&](int h, bool live) __attribute__((always_inline)) {
+  auto copy_head = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
     const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-    const int64_t base = t0 * HvD + (int64_t)h * D;
-    copy_rows(sm.tO, dout + base, rowb, live);
-    copy_rows(sm.tDl, reinterpret_cast<const T*>(Dlw) + base, rowb, live);
-    copy_rows(sm.tdR, dvo + t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)), live);
+    const int64_t base = it.t0 * HvD + (int64_t)h * D;
+    copy_rows(sm.tO, dout + base, rowb, it.L, live);
+    copy_rows(sm.tDl, reinterpret_cast<const T*>(Dlw) + base, rowb, it.L, live);
+    copy_rows(sm.tdR, dvo + it.t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)), it.L, live);
   };
-  auto copy_r = [&](int h, bool live) __attribute__((always_inline)) {
-    copy_rows(sm.tR, Rw + t0 * HvD + (int64_t)h * D, (uint32_t)(HvD * sizeof(T)), live);
+  auto copy_r = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
+    copy_rows(sm.tR, Rw + it.t0 * HvD + (int64_t)h * D, (uint32_t)(HvD * sizeof(T)), it.L, live);
   };
   // ... the gate values (wave 0: loaded into registers a phase before they
   // go to LDS) ...
   double gnext = 0.0;
   float bnext = 0.f;
-  auto fetch_gates = [&](int h) __attribute__((always_inline)) {
+  auto fetch_gates = [&](const Item& it, int h) __attribute__((always_inline)) {
     if (wave == 0) {
-      gnext = gcum[(c * Hv + h) * CHUNK + lane];
-      bnext = bw[(c * Hv + h) * CHUNK + lane];   // (zero past the chunk end)
+      gnext = gcum[(it.c * Hv + h) * CHUNK + lane];
+      bnext = bw[(it.c * Hv + h) * CHUNK + lane];   // (zero past the chunk end)
     }
   };
   auto put_gates = [&]() __attribute__((always_inline)) {
@@ -296,9 +297,9 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   };
   // ... Tinv (16-bit types: into LDS, by direct copies) ...
   typedef typename GL::TI TI;
-  auto copy_tinv = [&](int h, bool live) __attribute__((always_inline)) {
+  auto copy_tinv = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
     if constexpr (GL::TIN_LDS) {
-      const char* src = reinterpret_cast<const char*>(Tib + (c * Hv + h) * 2 * CHUNK * CHUNK);
+      const char* src = reinterpret_cast<const char*>(Tib + (it.c * Hv + h) * 2 * CHUNK * CHUNK);
       const uint32_t bytes = live ? CHUNK * CHUNK * sizeof(T) : 0u;
 #pragma unroll
       for (int j = 0; j < TI::PIECES / 512; ++j) {
@@ -312,7 +313,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   // fp32, Tinv^T (m = 1)
   auto tin = [&](int h, int m, int r, int col) __attribute__((always_inline)) -> const T* {
     if constexpr (GL::TIN_LDS) return sm.Tin + TI::at(r, col);
-    else return Tib + (c * Hv + h) * 2 * CHUNK * CHUNK + m * CHUNK * CHUNK + r * CHUNK + col;
+    else return Tib + (cur.c * Hv + h) * 2 * CHUNK * CHUNK + m * CHUNK * CHUNK + r * CHUNK + col;
   };
   // B operand of step p from row tl of Tinv^T (reduction indices pcol(p)
   // .. + 7, natural order).  16-bit: two transposing reads down column tl of
@@ -337,9 +338,9 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   constexpr int NAD = NSD * FR, NPD = 4 * (int)sizeof(CT);
   constexpr int NA = NAD > NPD ? NAD : NPD;
   uint32_t aop[NA];
-  auto load_tinv = [&](int h, bool live) __attribute__((always_inline)) {
+  auto load_tinv = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
     const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-    const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D, live ? (uint32_t)L * rowb : 0u);
+    const auto rs = buffer_of(ddw + it.t0 * HvD + (int64_t)h * D, live ? (uint32_t)it.L * rowb : 0u);
 #pragma unroll
     for (int p = 0; p < NSD; ++p) {
       const frag f = buffer_frag<T>(rs, (uint32_t)tl * rowb + (uint32_t)pcol(p) * sizeof(T));
@@ -356,8 +357,8 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     if constexpr (FR == 4) return __builtin_bit_cast(frag, u32x4{aop[4 * p], aop[4 * p + 1], aop[4 * p + 2], aop[4 * p + 3]});
     else return __builtin_bit_cast(frag, aop[p]);
   };
-  auto load_p = [&](int h, bool live) __attribute__((always_inline)) {
-    const auto rs = buffer_of(Pw + (c * Hv + h) * CHUNK * CHUNK, live ? CHUNK * CHUNK * sizeof(CT) : 0u);
+  auto load_p = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
+    const auto rs = buffer_of(Pw + (it.c * Hv + h) * CHUNK * CHUNK, live ? CHUNK * CHUNK * sizeof(CT) : 0u);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const uint32_t off = (uint32_t)(tl * CHUNK + acc_col<CT>(16 * st + g4)) * sizeof(CT);
@@ -385,33 +386,44 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   // ... and every wave's rows of the saved states (phase B)
   frag hA[NSD], dhA[NSD];
   auto load_states = [&](int h) __attribute__((always_inline)) {
-    const int64_t r = (c * Hv + h) * D * D + (int64_t)(16 * kt + c16) * D;
+    const int64_t r = (cur.c * Hv + h) * D * D + (int64_t)(16 * kt + c16) * D;
 #pragma unroll
     for (int p = 0; p < NSD; ++p) {
       hA[p] = rdf(hst + r, pcol(p));
       dhA[p] = rdf(dhst + r, pcol(p));
     }
   };
-  auto load_a = [&](int h, bool live) __attribute__((always_inline)) {
-    if (role == 0) load_tinv(h, live);
-    else load_p(h, live);
+  auto load_a = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
+    if (role == 0) load_tinv(it, h, live);
+    else load_p(it, h, live);
   };
 
-  copy_head(kh * G, true);
-  copy_r(kh * G, true);
-  copy_tinv(kh * G, true);
-  fetch_gates(kh * G);
-  load_a(kh * G, true);
+  load_item(cur);
+  copy_kk(cur, true);
+  copy_head(cur, kh * G, true);
+  copy_r(cur, kh * G, true);
+  copy_tinv(cur, kh * G, true);
+  fetch_gates(cur, kh * G);
+  load_a(cur, kh * G, true);
   put_gates();
+  floatx4 dQa[TTW], dKa[TTW];
+#pragma unroll
+  for (int tt = 0; tt < TTW; ++tt) dQa[tt] = dKa[tt] = zero4();
 
-  // Every operand of head h + 1 is requested while head h finishes: R and
-  // Tinv before phase B, the other tiles, the phase-A operands and the gates
-  // after it.  The barriers they have to pass are LDS-only (a full barrier
-  // would wait for the copies); the one at the top of a head waits for all.
-  // After the last head the same requests go out with empty ranges (gates:
-  // the last head's again).
-  for (int hh = 0; hh < G; ++hh) {
+  // Every operand of the next head (head h + 1, or the first head of the
+  // next item) is requested while head h finishes: R, Tinv (and K K^T)
+  // before phase B, the other tiles, the phase-A operands, the gates (and
+  // the item's registers) after it.  The barriers they have to pass are
+  // LDS-only (a full barrier would wait for the copies); the one at the top
+  // of a head waits for all.  After the last head the same requests go out
+  // with empty ranges (gates: the last head's again).
+  const int n_steps = n_items * G;
+  for (int step = 0, hh = 0; step < n_steps; ++step) {
     const int h = kh * G + hh;
+    const bool last = hh + 1 == G;           // the item's last head
+    const bool live = step + 1 < n_steps;    // a next head exists
+    const Item nx = last && live ? item_of(cur.c + 1) : cur;
+    const int hn = !live ? h : last ? kh * G : h + 1;
     derive();
     issue_fence();
     __syncthreads();   // this head's tiles, gates and phase-A operands are in
@@ -501,7 +513,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * st + g4 + i;
           const float Dts = decay(gt, gs[i], s <= tl);
-          ep[st][i] = (s < tl && tl < L) ? dPt[st][i] * pv[i] : 0.f;
+          ep[st][i] = (s < tl && tl < cur.L) ? dPt[st][i] * pv[i] : 0.f;
           pd[i] = dPt[st][i] * Dts;
         }
         store4(&sm.dPD[tl][acc_col<T>(16 * st + g4)], pd[0], pd[1], pd[2], pd[3]);
@@ -546,7 +558,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           const float Dts = decay(gt, gs[i], lower);
           const float dA = lower ? -da[i] : 0.f;
           const float dAD = dA * Dts;
-          sm.E[tl][s] = tl < L ? dAD * bt * kks[i] : 0.f;
+          sm.E[tl][s] = tl < cur.L ? dAD * bt * kks[i] : 0.f;
           rb += dAD * kks[i];
           wa[i] = dAD * bt;
         }
@@ -572,11 +584,10 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.E[tl][16 * st + g4 + i] += ep[st][i];
     }
-    {   // R and Tinv are no longer read for this head
-      const bool live = hh + 1 < G;
-      copy_r(live ? h + 1 : h, live);
-      copy_tinv(live ? h + 1 : h, live);
-    }
+    // R and Tinv (and on the item's last head K K^T) are no longer read
+    copy_r(nx, hn, live);
+    copy_tinv(nx, hn, live);
+    if (last) copy_kk(nx, live);
 
     // =============== phase B: token x key products (k x t tiles)
     {
@@ -633,12 +644,27 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       if (lane == 0) sm.red[wave] = ipv;
     }
     lds_barrier();   // the token tiles are free; every partial is in
-    {
-      const bool live = hh + 1 < G;
-      copy_head(live ? h + 1 : h, live);
-      fetch_gates(live ? h + 1 : h);
-      load_a(live ? h + 1 : h, live);
+    if (last) {
+      // dq = scale dQ, dk of the item (four consecutive key columns of one
+      // token per lane), then the next item's registers
+      const uint32_t rq = (uint32_t)(lddq * sizeof(T)), rk = (uint32_t)(lddk * sizeof(T));
+      const auto bq = buffer_of(dq + cur.t0 * lddq + (int64_t)kh * D, (uint32_t)cur.L * rq);
+      const auto bk = buffer_of(dk + cur.t0 * lddk + (int64_t)kh * D, (uint32_t)cur.L * rk);
+#pragma unroll
+      for (int tt = 0; tt < TTW; ++tt) {
+        const int t = 16 * (tg * TTW + tt) + c16, kc = 16 * kt + g4;
+        floatx4 xq = dQa[tt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xq[i] *= scale;
+        buffer_store4<T>(bq, (uint32_t)t * rq + (uint32_t)kc * sizeof(T), xq);
+        buffer_store4<T>(bk, (uint32_t)t * rk + (uint32_t)kc * sizeof(T), dKa[tt]);
+        dQa[tt] = dKa[tt] = zero4();
+      }
+      if (live) load_item(nx);
     }
+    copy_head(nx, hn, live);
+    fetch_gates(nx, hn);
+    load_a(nx, hn, live);
 
     // =============== dg, dbeta (waves 0-3).  With gamma the in-chunk
     // cumulative gate, dg_i = sum_{t >= i} dgam_t.  Three parts, each a sum
@@ -699,34 +725,19 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       }
 #pragma unroll
       for (int w = 0; w < 8; ++w) ips += sm.red[w];
-      if (t == L - 1) y += dexp<T>(sm.gam[CHUNK - 1]) * ips;
-      if (t >= L) { y = 0.f; zt = 0.f; }
+      if (t == cur.L - 1) y += dexp<T>(sm.gam[CHUNK - 1]) * ips;
+      if (t >= cur.L) { y = 0.f; zt = 0.f; }
       const float dgs = box + wave_suffix_scan(y, lane) + (wave_incl_scan_f(zt, lane) - zt);
-      if (t < L) {
-        dg[(t0 + t) * Hv + h] = dgs;
-        dbeta[(t0 + t) * Hv + h] = db;
+      if (t < cur.L) {
+        dg[(cur.t0 + t) * Hv + h] = dgs;
+        dbeta[(cur.t0 + t) * Hv + h] = db;
       }
     }
     // (since phase B's barrier only wave 0 reads the gates, and it alone
     // writes the next head's)
     put_gates();
-  }
-
-  // ---- dq = scale dQ, dk: four consecutive key columns of one token per lane
-  derive();
-  {
-    const uint32_t rq = (uint32_t)(lddq * sizeof(T)), rk = (uint32_t)(lddk * sizeof(T));
-    const auto bq = buffer_of(dq + t0 * lddq + (int64_t)kh * D, (uint32_t)L * rq);
-    const auto bk = buffer_of(dk + t0 * lddk + (int64_t)kh * D, (uint32_t)L * rk);
-#pragma unroll
-    for (int tt = 0; tt < TTW; ++tt) {
-      const int t = 16 * (tg * TTW + tt) + c16, kc = 16 * kt + g4;
-      floatx4 xq = dQa[tt];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xq[i] *= scale;
-      buffer_store4<T>(bq, (uint32_t)t * rq + (uint32_t)kc * sizeof(T), xq);
-      buffer_store4<T>(bk, (uint32_t)t * rk + (uint32_t)kc * sizeof(T), dKa[tt]);
-    }
+    if (last) cur = nx;
+    hh = last ? 0 : hh + 1;
   }
 }
 
@@ -746,14 +757,15 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
     const size_t shm = sizeof(GradLds<T, D>);
     auto kern = chunk_grad_kernel<T, D>;
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(kern, dim3((unsigned)Ly.nt_max, s.hk), dim3(512), shm, st, (const T*)q,
+    hipLaunchKernelGGL(kern, dim3((unsigned)((Ly.nt_max + GRAD_ITEMS - 1) / GRAD_ITEMS), s.hk), dim3(512), shm, st, (const T*)q,
                        (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
                        s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), (const float*)(ws + Ly.bw),
                        (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)(ws + Ly.tib),
                        (const T*)(ws + Ly.ktb), (const T*)(ws + Ly.qtb), (const T*)(ws + Ly.h),
                        (const T*)(ws + Ly.dh), (const T*)(ws + Ly.rw),
                        sizeof(T) == 2 ? (const void*)(ws + Ly.dl16w) : (const void*)(ws + Ly.dlw),
-                       (const T*)(ws + Ly.ddw), (const T*)dout, (const T*)dv, lddv, (T*)dq,
+                       (const T*)(ws + Ly.ddw), (const typename Compute<T>::type*)(ws + Ly.kkw),
+                       (const T*)dout, (const T*)dv, lddv, (T*)dq,
                        (T*)dk, lddq, lddk, dg, dbeta);
     return hipGetLastError();
   });
