@@ -48,7 +48,7 @@ namespace gdn {
 constexpr int GRAD_ITEMS = 4;
 
 template <typename T, int D> struct GradLds {
-  typedef Tile<T, CHUNK, D> TT;                               // token-major tile
+  typedef Tile<T, CHUNK, D, -1> TT;                           // token-major tile
   static constexpr int LDP = CHUNK + 16 / (int)sizeof(T);     // padded 64-wide rows
   static constexpr int NKT = D / 16;                          // key tiles (phase-B waves per token group)
   T tO[TT::PIECES * TT::EPP];     // dO

@@ -45,7 +45,10 @@ template <int RP> __device__ __forceinline__ int row_swz(int r) {
 
 // An LDS tile of ROWS rows of COLS elements of type E, unpadded, with the
 // 16-byte pieces of row r permuted: piece q lives at slot q ^ swz(r), where
-// swz = row_swz (SWZ_SHIFT = 0) or (r >> SWZ_SHIFT) mod RP.
+// swz = row_swz (SWZ_SHIFT = 0), (r >> SWZ_SHIFT) mod RP, or r mod RP
+// (SWZ_SHIFT < 0: 16-byte reads of one piece column by 16 consecutive rows
+// hit 16 different slots, which measured free of bank conflicts on gfx950,
+// where row_swz with RP = 16 costs four extra cycles per wave read).
 template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
   static constexpr int EPP = 16 / sizeof(E);         // elements per piece
   static constexpr int RP = COLS / EPP;              // pieces per row
@@ -53,6 +56,7 @@ template <typename E, int ROWS, int COLS, int SWZ_SHIFT = 0> struct Tile {
   static_assert(RP == 4 || RP == 8 || RP == 16, "pieces per row");
   __device__ __forceinline__ static int swz(int r) {
     if constexpr (SWZ_SHIFT == 0) return row_swz<RP>(r);
+    else if constexpr (SWZ_SHIFT < 0) return r & (RP - 1);
     else return (r >> SWZ_SHIFT) & (RP - 1);
   }
   // element offset of (r, col)
