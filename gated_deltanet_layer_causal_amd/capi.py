@@ -33,6 +33,7 @@ EXPORTS = (
     "gdn_gated_norm_bwd_workspace", "gdn_chunk_prepare", "gdn_chunk_prepare_bwd",
     "gdn_chunk_fwd_states", "gdn_chunk_fwd_states_save",
     "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse", "gdn_chunk_bwd_grads",
+    "gdn_check_cu_seqlens",
 )
 
 
@@ -94,6 +95,7 @@ def load(path: str = LIB_PATH):
     lib.gdn_chunk_bwd_grads.argtypes = [SP, V, V, I64, I64, V, F, V, V, V, I64, V, V, I64, I64, V,
                                         V, V, c_size_t, V]
     lib.gdn_gated_norm_fwd.argtypes = [I64, c_int32, c_int, V, V, V, F, c_int, V, V]
+    lib.gdn_check_cu_seqlens.argtypes = [SP, V, V, V]
     lib.gdn_gated_norm_bwd.argtypes = [I64, c_int32, c_int, V, V, V, F, c_int, V, V, V, V, V,
                                        c_size_t, V]
     for name in ("gdn_conv_bwd_workspace", "gdn_gate_bwd_workspace", "gdn_chunk_fwd_workspace",
@@ -107,7 +109,7 @@ def load(path: str = LIB_PATH):
                  "gdn_chunk_bwd", "gdn_gated_norm_fwd", "gdn_gated_norm_bwd", "gdn_chunk_prepare",
                  "gdn_chunk_prepare_bwd", "gdn_chunk_fwd_states", "gdn_chunk_fwd_states_save",
                  "gdn_chunk_bwd_states", "gdn_chunk_bwd_reverse",
-                 "gdn_chunk_bwd_grads"):
+                 "gdn_chunk_bwd_grads", "gdn_check_cu_seqlens"):
         getattr(lib, name).restype = c_int
     _lib = lib
     return lib
@@ -320,6 +322,19 @@ def _gate_ok(shape, a, b, A_log, dt_bias):
     _per_token("b", shape, b, _tdt(shape))
     _need("A_log", A_log, torch.float32, shape.hv)
     _need("dt_bias", dt_bias, torch.float32, shape.hv)
+
+
+CU_BAD_START, CU_BAD_END, CU_DECREASING = 1, 2, 4
+
+
+def gdn_check_cu_seqlens(shape, cu_seqlens, violations, stream=None):
+    """Writes to violations (an int32 device tensor of one element) the bit
+    mask of the cu_seqlens contract's violations (CU_BAD_START, CU_BAD_END,
+    CU_DECREASING; 0 when valid), asynchronously."""
+    _cu_ok(shape, cu_seqlens)
+    _need("violations", violations, torch.int32, 1)
+    _ok("gdn_check_cu_seqlens", load().gdn_check_cu_seqlens(byref(shape), _p(cu_seqlens),
+                                                            _p(violations), _stream(stream)))
 
 
 def gdn_gate_fwd(shape, a, b, A_log, dt_bias, g, beta, stream=None):

@@ -365,4 +365,12 @@ gdn_status gdn_gated_norm_bwd(int64_t rows, int32_t dv, gdn_dtype dt, const void
                                   (float*)ws, (hipStream_t)stream));
 }
 
+gdn_status gdn_check_cu_seqlens(const gdn_shape* s, const int32_t* cu, int32_t* violations,
+                                void* stream) {
+  GDN_TRY(check_shape(s));
+  if (!cu || !violations) return GDN_ERR_INVALID_ARG;
+  if (((uintptr_t)violations & 3u) != 0) return GDN_ERR_ALIGNMENT;
+  return launched(gdn::launch_check_cu(*s, cu, violations, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -61,6 +61,31 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// The cu_seqlens contract, checked: one block ORs the violations it sees
+// into an LDS word (bits: 1 cu[0] != 0, 2 cu[n_seq] != T, 4 a decrease).
+__global__ void __launch_bounds__(256) check_cu_kernel(const int32_t* __restrict__ cu, int n_seq,
+                                                       int64_t T, int32_t* __restrict__ out) {
+  __shared__ int32_t acc;
+  if (threadIdx.x == 0) acc = 0;
+  __syncthreads();
+  int32_t bad = 0;
+  for (int n = threadIdx.x; n < n_seq; n += 256)
+    if (cu[n + 1] < cu[n]) bad |= 4;
+  if (threadIdx.x == 0) {
+    if (cu[0] != 0) bad |= 1;
+    if ((int64_t)cu[n_seq] != T) bad |= 2;
+  }
+  if (bad) atomicOr(&acc, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = acc;
+}
+
+hipError_t launch_check_cu(const gdn_shape& s, const int32_t* cu, int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, st, cu, s.n_seq, s.total_tokens, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Preparation, one workgroup per (chunk, key head): K K^T and Q K^T once
 // (MFMA) and K^T (and in backward mode K K^T) to the workspace, then per
 // value head of the group: gam, A,

@@ -111,4 +111,6 @@ hipError_t launch_chunk_bwd(const gdn_shape& s, const void* q, const void* k, co
                             int64_t lddq, int64_t lddk, int64_t lddv, float* dg, float* dbeta,
                             float* dS0, void* ws, hipStream_t st);
 
+hipError_t launch_check_cu(const gdn_shape& s, const int32_t* cu, int32_t* out, hipStream_t st);
+
 }  // namespace gdn

@@ -28,6 +28,7 @@ class CoreConfig:
     l2_eps: float = 1e-6
     norm_eps: float = 1e-6
     seg_chunks: int = 0                  # segment-parallel state scan (0: the library decides)
+    check_cu_seqlens: bool = False       # debug: check the cu_seqlens contract (synchronises)
 
     @property
     def channels(self):
@@ -103,6 +104,8 @@ class GDNCore:
         T = x.shape[0]
         n_seq = cu_seqlens.numel() - 1
         sh = self.shape(T, n_seq)
+        if c.check_cu_seqlens:
+            self.check_cu_seqlens(sh, cu_seqlens)
         ws = self.workspace(sh, T * c.hv)
         wc = self.chunk_workspace(sh, fresh=save_states)
         dev, dt = x.device, c.dtype
@@ -140,6 +143,19 @@ class GDNCore:
         if save_states:
             saved["chunk_ws"] = wc
         return saved
+
+    def check_cu_seqlens(self, sh, cu_seqlens):
+        """Runs gdn_check_cu_seqlens and raises ValueError naming each broken
+        part of the contract (this waits for the stream)."""
+        out = torch.empty(1, dtype=torch.int32, device=cu_seqlens.device)
+        L.gdn_check_cu_seqlens(sh, cu_seqlens, out)
+        bad = int(out.item())
+        if bad:
+            why = [msg for bit, msg in ((L.CU_BAD_START, "cu_seqlens[0] != 0"),
+                                        (L.CU_BAD_END, "cu_seqlens[-1] != the token count"),
+                                        (L.CU_DECREASING, "cu_seqlens decreases"))
+                   if bad & bit]
+            raise ValueError("invalid cu_seqlens: " + "; ".join(why))
 
     def backward(self, saved, x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, dout,
                  S0=None, dS_final=None, timer=None, conv_state=None, d_conv_state=None):

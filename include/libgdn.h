@@ -288,6 +288,22 @@ gdn_status gdn_gated_norm_bwd(int64_t rows, int32_t dv, gdn_dtype dtype, const v
                               size_t ws_bytes, void* stream);
 size_t gdn_gated_norm_bwd_workspace(int64_t rows, int32_t dv);
 
+/* ---------------------------------------------------------------------------
+ * Check of cu_seqlens (prime-rl page, "Summary": the conv and the rule take
+ * cu_seqlens).  Every entry point that takes cu_seqlens assumes, without
+ * checking it on the device, cu[0] = 0, cu[n_seq] = total_tokens and cu
+ * non-decreasing; a table that breaks this is undefined behaviour there.
+ * This call runs one small kernel that reads cu_seqlens[0 .. n_seq] (device
+ * int32) and writes to *violations (device int32, caller-owned) a bit mask:
+ * 1 = cu[0] != 0, 2 = cu[n_seq] != total_tokens, 4 = a decrease somewhere;
+ * 0 for a valid table.  Like every call it is asynchronous: read
+ * *violations once the stream has run it.  It reads nothing else and needs
+ * no workspace.  Errors: GDN_ERR_INVALID_ARG for a bad shape or a null
+ * pointer, GDN_ERR_ALIGNMENT for a violations pointer not 4-byte aligned.
+ * ------------------------------------------------------------------------- */
+gdn_status gdn_check_cu_seqlens(const gdn_shape* shape, const int32_t* cu_seqlens,
+                                int32_t* violations, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

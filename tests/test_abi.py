@@ -74,6 +74,11 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.gdn_conv_fwd(ctypes.byref(sh), ctypes.c_void_p(258), C, a16, a16, 1, 1e-6, a16, C,
                             None) == 3
     assert lib.gdn_conv_fwd(ctypes.byref(sh), a16, C - 8, a16, a16, 1, 1e-6, a16, C, None) == 1
+    # the cu_seqlens check: null or misaligned result pointers, bad shapes
+    assert lib.gdn_check_cu_seqlens(ctypes.byref(sh), a16, None, None) == 1
+    assert lib.gdn_check_cu_seqlens(ctypes.byref(sh), None, a16, None) == 1
+    assert lib.gdn_check_cu_seqlens(ctypes.byref(sh), a16, ctypes.c_void_p(258), None) == 3
+    assert lib.gdn_check_cu_seqlens(ctypes.byref(_shape(n_seq=0)), a16, a16, None) == 1
     # chunk op with a workspace that is too small
     st = lib.gdn_chunk_fwd(ctypes.byref(sh), a16, a16, a16, 1024, 1024, 1024, a16, a16,
                            ctypes.c_float(0.1), None, None, a16, a16, a16, 16, None)

@@ -255,6 +255,49 @@ def test_chunk_table_exact(lens, seg):
 
 
 # ------------------------------------------------------------------ fp16 operand range
+@pytest.mark.parametrize("cu,total,want", [
+    ([0, 70, 70, 134, 200], 200, 0),
+    ([0, 0, 0], 0, 0),
+    ([1, 70, 200], 200, L.CU_BAD_START),
+    ([0, 70, 199], 200, L.CU_BAD_END),
+    ([0, 70, 60, 200], 200, L.CU_DECREASING),
+    ([5, 3, 2], 9, L.CU_BAD_START | L.CU_BAD_END | L.CU_DECREASING),
+    (list(range(0, 4001, 4)) + [3999], 3999, L.CU_DECREASING),   # past one block of 256 threads
+])
+def test_check_cu_seqlens(cu, total, want):
+    """gdn_check_cu_seqlens reports each broken part of the cu_seqlens
+    contract (bit-exact mask), and nothing for valid tables (empty
+    sequences included)."""
+    n_seq = len(cu) - 1
+    print(f"[check_cu_seqlens] n_seq={n_seq} T={total}", flush=True)
+    sh = L.make_shape(n_seq, total, 1, 2, 128, L.GDN_BF16)
+    cut = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    out = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    L.gdn_check_cu_seqlens(sh, cut, out)
+    torch.cuda.synchronize()
+    assert int(out.item()) == want
+
+
+def test_layer_refuses_bad_cu_seqlens_when_checking():
+    """CoreConfig(check_cu_seqlens=True): a broken table raises before any
+    other call is launched; a valid one runs."""
+    from gated_deltanet_layer_causal_amd.layer import CoreConfig, GDNCore
+    core = GDNCore(CoreConfig(hk=1, hv=2, d=32, dtype=torch.bfloat16, check_cu_seqlens=True),
+                   device=DEV)
+    T, C = 100, core.cfg.channels
+    x = torch.randn(T, C, device=DEV).to(torch.bfloat16)
+    wc = torch.randn(C, 4, device=DEV) * 0.5
+    a, b = torch.randn(T, 2, device=DEV).to(torch.bfloat16), torch.randn(T, 2, device=DEV).to(torch.bfloat16)
+    A_log, dtb = torch.zeros(2, device=DEV), torch.zeros(2, device=DEV)
+    z = torch.randn(T, 2, 32, device=DEV).to(torch.bfloat16)
+    wn = torch.zeros(32, device=DEV)
+    good = torch.tensor([0, 40, 100], dtype=torch.int32, device=DEV)
+    core.forward(x, wc, a, b, A_log, dtb, z, wn, good)
+    bad = torch.tensor([0, 60, 40, 100], dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="decreases"):
+        core.forward(x, wc, a, b, A_log, dtb, z, wn, bad)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("flow", ["composite", "saved"])
 def test_chunk_large_values_and_state(flow, dt):
