@@ -79,9 +79,11 @@ FP32_PEAK_TFLOPS = 157.3
 #                K S^T, Q S^T (2 x 2 d^2) + M R, P Delta (2 x 2 C d))
 #   bwd_states : the saved-state pass (fp32 data: + K S^T, M R)
 #   bwd_reverse: K dS'^T, Q^T dO, K^T dR (3 x 2 d^2) + P^T dO, M^T dDelta (2 x 2 C d)
-#   bwd_grads  : dO S, dR S, Delta dS' (3 x 2 d^2); dM, dP, (dP o D) K,
-#                (dP o D)^T Q, (dA o bD) K, (dA o bD)^T K (6 x 2 C d);
-#                Tinv products (2 x 2 C^2); per key head K K^T, Q K^T (2 x 2 C d)
+#   bwd_grads  : dO S, dR S, Delta dS' (3 x 2 d^2); dM, dP in both
+#                orientations, (dP o D) K, (dP o D)^T Q and WS K, WS = WA + WA^T
+#                forming (dA o bD) K + (dA o bD)^T K in one product
+#                (6 x 2 C d); Tinv products (2 x 2 C^2); K K^T comes from the
+#                preparation
 # The preparation is bandwidth-bound; its algorithmic bytes are its inputs
 # q, k, g, beta (its writes are intermediates).
 def algorithmic_per_token(name, hk, hv, d, E, saved=True):
@@ -132,7 +134,7 @@ def algorithmic_per_token(name, hk, hv, d, E, saved=True):
     if name == "chunk_bwd_reverse":
         return "mfma", hv * (6 * d * d + 4 * C64 * d)
     if name == "chunk_bwd_grads":
-        return "mfma", hv * (6 * d * d + 12 * C64 * d + 4 * C64 * C64) + hk * 2 * C64 * d
+        return "mfma", hv * (6 * d * d + 12 * C64 * d + 4 * C64 * C64)
     raise KeyError(name)
 
 
