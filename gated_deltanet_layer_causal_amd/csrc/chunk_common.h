@@ -135,9 +135,20 @@ __device__ __forceinline__ T* row_or_sink(T* p, bool valid, void* sink, int tid)
   return valid ? p : reinterpret_cast<T*>(sink) + (tid & (SINK_ELEMS - 1));
 }
 
-inline ChunkLayout chunk_layout(const gdn_shape& s) {
+// The workspace of the forward-only flow (preparation in forward mode, then
+// the MODE 0 pass) or of the backward / saved-state flow.  The backward flow
+// has no use for the Q rows in the compute type, nor, with 16-bit data
+// (whose saved-state pass works from the K rows), for W and the compute-type
+// K^T: those regions are empty there.  Every launcher of one flow uses the
+// same layout.
+enum class ChunkFlow { Fwd, Bwd };
+
+inline ChunkLayout chunk_layout(const gdn_shape& s, ChunkFlow flow) {
   ChunkLayout L;
   const size_t es = s.dtype == GDN_FP32 ? 4 : 2;
+  const bool bwd = flow == ChunkFlow::Bwd;
+  const size_t es_w = bwd && es == 2 ? 0 : es;   // W and the compute-type K^T
+  const size_t es_q = bwd ? 0 : es;               // Q rows in the compute type
   const int64_t T = s.total_tokens;
   L.nt_max = T / CHUNK + s.n_seq;
   L.seg = seg_len(s);
@@ -155,9 +166,9 @@ inline ChunkLayout chunk_layout(const gdn_shape& s) {
   L.gcum = off; off = align256(off + sizeof(double) * (size_t)L.nt_max * s.hv * CHUNK);
   L.mw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
   L.pw = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * CHUNK);
-  L.ww = off; off = align256(off + es * (size_t)L.nt_max * s.hv * CHUNK * s.dk);
-  L.ktw = off; off = align256(off + es * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
-  L.q16w = off; off = align256(off + es * (size_t)L.nt_max * s.hk * CHUNK * s.dk);
+  L.ww = off; off = align256(off + es_w * (size_t)L.nt_max * s.hv * CHUNK * s.dk);
+  L.ktw = off; off = align256(off + es_w * (size_t)L.nt_max * s.hk * s.dk * CHUNK);
+  L.q16w = off; off = align256(off + es_q * (size_t)L.nt_max * s.hk * CHUNK * s.dk);
   L.gw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.dw = off; off = align256(off + sizeof(float) * (size_t)L.nt_max * s.hv * CHUNK);
   L.total_fwd = off;

@@ -457,13 +457,13 @@ static hipError_t chunk_prepare(const gdn_shape& s, const void* q, const void* k
   return hipGetLastError();
 }
 
-size_t chunk_fwd_ws_bytes(const gdn_shape& s) { return chunk_layout(s).total_fwd; }
-size_t chunk_bwd_ws_bytes(const gdn_shape& s) { return chunk_layout(s).total_bwd; }
+size_t chunk_fwd_ws_bytes(const gdn_shape& s) { return chunk_layout(s, ChunkFlow::Fwd).total_fwd; }
+size_t chunk_bwd_ws_bytes(const gdn_shape& s) { return chunk_layout(s, ChunkFlow::Bwd).total_bwd; }
 
 hipError_t launch_chunk_prepare(const gdn_shape& s, const void* q, const void* k, int64_t ldq,
                                 int64_t ldk, const float* g, const float* beta, float scale,
                                 const int32_t* cu, void* ws, bool bwd, hipStream_t st) {
-  const ChunkLayout Ly = chunk_layout(s);
+  const ChunkLayout Ly = chunk_layout(s, bwd ? ChunkFlow::Bwd : ChunkFlow::Fwd);
   return dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
     constexpr int D = decltype(c)::d;

@@ -748,7 +748,7 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
                                   void* dk, int64_t lddq, int64_t lddk, float* dg, float* dbeta,
                                   void* wsv, hipStream_t st) {
   char* ws = (char*)wsv;
-  const ChunkLayout Ly = chunk_layout(s);
+  const ChunkLayout Ly = chunk_layout(s, ChunkFlow::Bwd);
   if (Ly.nt_max == 0 || s.total_tokens == 0) return hipSuccess;
   return dispatch_chunk(s, [&](auto cf) {
     using T = typename decltype(cf)::type;

@@ -420,7 +420,7 @@ hipError_t launch_chunk_outputs(const gdn_shape& s, const void* q, const void* k
                                 int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                 const int32_t* cu, void* o, void* wsv, hipStream_t st) {
   char* ws = (char*)wsv;
-  const ChunkLayout Ly = chunk_layout(s);
+  const ChunkLayout Ly = chunk_layout(s, ChunkFlow::Bwd);   // (saved-state and backward flows only)
   if (Ly.nt_max == 0 || s.total_tokens == 0) return hipSuccess;
   return dispatch_chunk(s, [&](auto cf) {
     using T = typename decltype(cf)::type;

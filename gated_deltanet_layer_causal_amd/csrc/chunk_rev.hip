@@ -411,7 +411,7 @@ hipError_t launch_chunk_bwd_reverse(const gdn_shape& s, const void* q, const voi
                                     int64_t ldk, float scale, const int32_t* cu, const void* dout,
                                     const float* dS_final, void* dv, int64_t lddv, float* dS0,
                                     void* ws, hipStream_t st) {
-  const ChunkLayout Ly = chunk_layout(s);
+  const ChunkLayout Ly = chunk_layout(s, ChunkFlow::Bwd);
   return dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
     return chunk_rev<T, decltype(c)::d>(s, scale, cu, dout, dS_final, dv, lddv, dS0, Ly, (char*)ws,

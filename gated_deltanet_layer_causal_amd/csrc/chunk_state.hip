@@ -579,7 +579,7 @@ hipError_t launch_chunk_fwd_states(const gdn_shape& s, const void* q, const void
                                    int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                    const float* S0, float* S_final, const int32_t* cu, void* o,
                                    void* ws, hipStream_t st) {
-  const ChunkLayout Ly = chunk_layout(s);
+  const ChunkLayout Ly = chunk_layout(s, ChunkFlow::Fwd);
   return dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
     return chunk_state<T, decltype(c)::d, 0>(s, v, ldv, scale, S0, S_final, cu, o, Ly, (char*)ws,
@@ -594,7 +594,7 @@ hipError_t launch_chunk_fwd_states_save(const gdn_shape& s, const void* q, const
   // the sequential pass stores the chunk-start states (and, with 16-bit
   // types, R and Delta); O (and for fp32 R and Delta) then follow chunk by
   // chunk in parallel
-  const ChunkLayout Ly = chunk_layout(s);
+  const ChunkLayout Ly = chunk_layout(s, ChunkFlow::Bwd);
   hipError_t e = dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
     return chunk_state<T, decltype(c)::d, 1>(s, v, ldv, scale, S0, S_final, cu, nullptr, Ly,
@@ -607,7 +607,7 @@ hipError_t launch_chunk_fwd_states_save(const gdn_shape& s, const void* q, const
 hipError_t launch_chunk_bwd_states(const gdn_shape& s, const void* q, const void* k, const void* v,
                                    int64_t ldq, int64_t ldk, int64_t ldv, float scale,
                                    const float* S0, const int32_t* cu, void* ws, hipStream_t st) {
-  const ChunkLayout Ly = chunk_layout(s);
+  const ChunkLayout Ly = chunk_layout(s, ChunkFlow::Bwd);
   hipError_t e = dispatch_chunk(s, [&](auto c) {
     using T = typename decltype(c)::type;
     return chunk_state<T, decltype(c)::d, 1>(s, v, ldv, scale, S0, nullptr, cu, nullptr, Ly,
