@@ -226,21 +226,46 @@ __device__ __forceinline__ void chunk_span(const int32_t* seq_off, const int32_t
   L = rem < CHUNK ? (int)rem : CHUNK;
 }
 
-// Stage rows [0, 64) x [0, W) of a token-major tensor into LDS (row stride ld_s),
-// zero-filling rows >= L.  Source row r is at src + r * ld_g.
+// Stage rows [0, 64) x [0, W) of two token-major tensors into LDS (row
+// stride ld_s), zero-filling rows >= L (1 <= L <= 64).  Source row r of
+// tensor a is at sa + r * lda.  Every load is issued before the first store
+// (rows >= L re-read row L - 1, which is valid memory, and are zeroed where
+// stored), so their latencies overlap: a loop that stored each piece as it
+// arrived waited for every load in turn.
 template <typename TD, int W, typename TS>
-__device__ __forceinline__ void stage_rows(TD* dst, int ld_s, const TS* src, int64_t ld_g, int L,
-                                           int tid) {
-  constexpr int G8 = W / 8;
-  for (int i = tid; i < CHUNK * G8; i += 256) {
-    const int r = i / G8, c8 = (i % G8) * 8;
-    f8 v;
-    if (r < L) v = load8(src + (int64_t)r * ld_g + c8);
-    else {
+__device__ __forceinline__ void stage_rows2(TD* da, const TS* sa, int64_t lda, TD* db,
+                                            const TS* sb, int64_t ldb, int ld_s, int L, int tid) {
+  constexpr int G8 = W / 8, ITEMS = CHUNK * G8;
+  constexpr int N = (ITEMS + 255) / 256;
+  constexpr int Q = (int)sizeof(TS) / 2;   // 16-byte words per 8 elements
+  uint4 ra[N][Q], rb[N][Q];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v.v[j] = 0.f;
+  for (int j = 0; j < N; ++j) {
+    const int i = tid + 256 * j, r = i / G8, c8 = (i % G8) * 8;
+    const int rr = r < L ? r : L - 1;
+    if (ITEMS % 256 == 0 || i < ITEMS) {
+      const uint4* pa = reinterpret_cast<const uint4*>(sa + (int64_t)rr * lda + c8);
+      const uint4* pb = reinterpret_cast<const uint4*>(sb + (int64_t)rr * ldb + c8);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        ra[j][q] = pa[q];
+        rb[j][q] = pb[q];
+      }
     }
-    store8(dst + r * ld_s + c8, v);
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int i = tid + 256 * j, r = i / G8, c8 = (i % G8) * 8;
+    if (ITEMS % 256 == 0 || i < ITEMS) {
+      f8 va = load8(reinterpret_cast<const TS*>(&ra[j][0]));
+      f8 vb = load8(reinterpret_cast<const TS*>(&rb[j][0]));
+      if (r >= L) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) va.v[e] = vb.v[e] = 0.f;
+      }
+      store8(da + r * ld_s + c8, va);
+      store8(db + r * ld_s + c8, vb);
+    }
   }
 }
 

@@ -171,8 +171,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
   int L;
   chunk_span(seq_off, cu, n_seq, c, t0, L);
 
-  stage_rows<CT, D>(&sK[0][0], LD, k + t0 * ldk + (int64_t)kh * D, ldk, L, tid);
-  stage_rows<CT, D>(&su.Q[0][0], LD, q + t0 * ldq + (int64_t)kh * D, ldq, L, tid);
+  stage_rows2<CT, D>(&sK[0][0], k + t0 * ldk + (int64_t)kh * D, ldk, &su.Q[0][0],
+                     q + t0 * ldq + (int64_t)kh * D, ldq, LD, L, tid);
   __syncthreads();
 
   // wave w owns rows [16w, 16w+16) of the 64 x 64 products
