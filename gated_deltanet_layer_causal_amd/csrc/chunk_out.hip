@@ -281,9 +281,12 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 // way (it forms both on the chain), and Delta once more in the compute type
 // for this product: per (chunk, value head)
 //   O^T = S (scale Q)^T diag(Gam) + Delta^T P^T
-// with the wave layout of chunk_out_kernel.  Delta (compute type) enters the
-// quarter's LDS tile as chunk_out_kernel puts its own.  Rows past the chunk end read zero (their
-// P entries are zero anyway).
+// with the wave layout of chunk_out_kernel.  One workgroup per (chunk, key
+// head) walks the G value heads of the group, so the Q rows (a B operand of
+// every head) are loaded once for the group: loading them per value head
+// was a fifth of the kernel's time.  Delta (compute type) enters the
+// quarter's LDS tile as chunk_out_kernel puts its own.  Rows past the chunk
+// end read zero (their P entries are zero anyway).
 template <typename T, int D>
 __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_o_kernel(
     const T* __restrict__ q, int64_t ldq, const int32_t* __restrict__ cu,
@@ -308,32 +311,22 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int vq = wave % NQ, th = wave / NQ;
+  const int Hk = Hv / G;
   const int item = xcd_item(blockIdx.x, n_items);
-  const int64_t c = item / Hv;
-  const int h = item % Hv, kh = h / G;
+  const int64_t c = item / Hk;
+  const int kh = item % Hk;
   if (c >= seq_off[n_seq]) return;
   int64_t t0;
   int L;
   chunk_span(seq_off, cu, n_seq, c, t0, L);
   const int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
   const int v0 = 32 * vq;
-  const int64_t ch = c * Hv + h, HvD = (int64_t)Hv * D;
+  const int64_t HvD = (int64_t)Hv * D;
   OQ& Q4 = qs[vq];
   const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-  const float* gam = Gw + ch * CHUNK;
-  const CT* Pc = Pw + ch * CHUNK * CHUNK;
   auto tok = [&](int j) { return 16 * (2 * th + j); };
 
-  // ---- every input requested up front: S slice, Q and P rows, Delta rows
-  uint4 hraw[NH];
-  {
-    const T* Sg = hst + ch * D * D + v0;
-#pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
-      hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * D + pc * EPP);
-    }
-  }
+  // ---- the Q rows of this wave's tokens, once for the group
   const uint32_t ldqb = (uint32_t)(ldq * sizeof(T));
   const auto rq = buffer_of(q + t0 * ldq + (int64_t)kh * D, (uint32_t)L * ldqb);
   sfrag qb[2][NSD];
@@ -342,75 +335,91 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
     for (int p = 0; p < NSD; ++p)
       qb[j][p] = buffer_frag<T>(rq, (uint32_t)(tok(j) + c16) * ldqb + (uint32_t)(p * KS + 8 * g) * sizeof(T));
-  cfrag pb[2][NSC];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int p = 0; p < NSC; ++p)
-      pb[j][p] = *reinterpret_cast<const cfrag*>(Pc + (tok(j) + c16) * CHUNK + 32 * p + 8 * g);
-  // this wave's 32 tokens of the quarter's Delta columns: 4 pieces per row
-  cfrag draw[2];
-  const auto rd = buffer_of(Dlw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = lane + 64 * j, r = 32 * th + i / PPR, pc = i % PPR;
-    draw[j] = buffer_frag<CT>(rd, (uint32_t)r * rowb + (uint32_t)(pc * 16));
-  }
-  float gm[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) gm[j] = gam[tok(j) + c16];
-  issue_fence();
-
-  // ---- S^T slice and Delta (compute type) into the quarter's LDS tiles
-#pragma unroll
-  for (int j = 0; j < NH; ++j) {
-    const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
-    word_alias* d = reinterpret_cast<word_alias*>(&Q4.hs[r][pc * EPP]);
-    d[0] = hraw[j].x; d[1] = hraw[j].y; d[2] = hraw[j].z; d[3] = hraw[j].w;
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = lane + 64 * j, r = 32 * th + i / PPR, pc = i % PPR;
-    *reinterpret_cast<cfrag*>(&Q4.xs[r][pc * EPP]) = draw[j];
-  }
-  __syncthreads();
-  sfrag sa[2][NSD];
-#pragma unroll
-  for (int vt = 0; vt < 2; ++vt)
-#pragma unroll
-    for (int p = 0; p < NSD; ++p) {
-      const int r = p * KS + 8 * g + (c16 >> 2), col = 16 * vt + 4 * (c16 & 3);
-      const u32x2 lo = lds_read_tr4(&Q4.hs[r][col]), hi = lds_read_tr4(&Q4.hs[r + 4][col]);
-      sa[vt][p] = __builtin_bit_cast(sfrag, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-  cfrag da[2][NSC];
-#pragma unroll
-  for (int vt = 0; vt < 2; ++vt)
-#pragma unroll
-    for (int p = 0; p < NSC; ++p) {
-      const int r = 32 * p + g4 + (c16 >> 2), cc = 16 * vt + 4 * (c16 & 3);
-      const u32x2 lo = lds_read_tr4(&Q4.xs[r][cc]), hi = lds_read_tr4(&Q4.xs[r + 16][cc]);
-      da[vt][p] = __builtin_bit_cast(cfrag, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-
-  // ---- O^T = S (scale Q)^T diag(Gam) + Delta^T P^T: value rows 16 vt + 4 g
-  // + i of token column tok(j) + c16, out in 8-byte pieces
   const uint32_t so = (uint32_t)(((int64_t)c16 * HvD + v0 + g4) * sizeof(T));
-  const auto rs = buffer_of(o + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
+
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = kh * G + hh;
+    const int64_t ch = c * Hv + h;
+    const float* gam = Gw + ch * CHUNK;
+    const CT* Pc = Pw + ch * CHUNK * CHUNK;
+    // ---- this head's inputs, requested up front: S slice, P rows, Delta rows
+    uint4 hraw[NH];
+    {
+      const T* Sg = hst + ch * D * D + v0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float sg = scale * gm[j];
+      for (int j = 0; j < NH; ++j) {
+        const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
+        hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * D + pc * EPP);
+      }
+    }
+    cfrag pb[2][NSC];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int p = 0; p < NSC; ++p)
+        pb[j][p] = *reinterpret_cast<const cfrag*>(Pc + (tok(j) + c16) * CHUNK + 32 * p + 8 * g);
+    // this wave's 32 tokens of the quarter's Delta columns: 4 pieces per row
+    cfrag draw[2];
+    const auto rd = buffer_of(Dlw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + 64 * j, r = 32 * th + i / PPR, pc = i % PPR;
+      draw[j] = buffer_frag<CT>(rd, (uint32_t)r * rowb + (uint32_t)(pc * 16));
+    }
+    float gm[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) gm[j] = gam[tok(j) + c16];
+    issue_fence();
+    if (hh > 0) __syncthreads();   // the previous head's LDS tiles are read
+
+    // ---- S^T slice and Delta (compute type) into the quarter's LDS tiles
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
+      word_alias* d = reinterpret_cast<word_alias*>(&Q4.hs[r][pc * EPP]);
+      d[0] = hraw[j].x; d[1] = hraw[j].y; d[2] = hraw[j].z; d[3] = hraw[j].w;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + 64 * j, r = 32 * th + i / PPR, pc = i % PPR;
+      *reinterpret_cast<cfrag*>(&Q4.xs[r][pc * EPP]) = draw[j];
+    }
+    __syncthreads();
+
+    // ---- O^T = S (scale Q)^T diag(Gam) + Delta^T P^T: value rows 16 vt + 4 g
+    // + i of token column tok(j) + c16, out in 8-byte pieces; the A operands
+    // (transposing reads) one value tile at a time, which keeps the group's Q
+    // operands in registers without spills
+    const auto rs = buffer_of(o + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
 #pragma unroll
     for (int vt = 0; vt < 2; ++vt) {
-      floatx4 sq = zero4(), pd = zero4();
+      sfrag sa[NSD];
 #pragma unroll
-      for (int p = 0; p < NSD; ++p) sq = MS::mma(sa[vt][p], qb[j][p], sq);
+      for (int p = 0; p < NSD; ++p) {
+        const int r = p * KS + 8 * g + (c16 >> 2), col = 16 * vt + 4 * (c16 & 3);
+        const u32x2 lo = lds_read_tr4(&Q4.hs[r][col]), hi = lds_read_tr4(&Q4.hs[r + 4][col]);
+        sa[p] = __builtin_bit_cast(sfrag, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+      cfrag da[NSC];
 #pragma unroll
-      for (int p = 0; p < NSC; ++p) pd = MC::mma(da[vt][p], pb[j][p], pd);
-      floatx4 ov;
+      for (int p = 0; p < NSC; ++p) {
+        const int r = 32 * p + g4 + (c16 >> 2), cc = 16 * vt + 4 * (c16 & 3);
+        const u32x2 lo = lds_read_tr4(&Q4.xs[r][cc]), hi = lds_read_tr4(&Q4.xs[r + 16][cc]);
+        da[p] = __builtin_bit_cast(cfrag, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = pd[i] + sg * sq[i];
-      buffer_store4<T>(rs, so + (uint32_t)tok(j) * rowb + (uint32_t)(16 * vt * sizeof(T)), ov);
+      for (int j = 0; j < 2; ++j) {
+        floatx4 sq = zero4(), pd = zero4();
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) sq = MS::mma(sa[p], qb[j][p], sq);
+#pragma unroll
+        for (int p = 0; p < NSC; ++p) pd = MC::mma(da[p], pb[j][p], pd);
+        const float sg = scale * gm[j];
+        floatx4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = pd[i] + sg * sq[i];
+        buffer_store4<T>(rs, so + (uint32_t)tok(j) * rowb + (uint32_t)(16 * vt * sizeof(T)), ov);
+      }
     }
   }
 }
@@ -430,10 +439,11 @@ hipError_t launch_chunk_outputs(const gdn_shape& s, const void* q, const void* k
     if constexpr (sizeof(T) == 2) {
       // the saved-state pass has stored R and Delta: O alone, if wanted
       if (!o) return hipSuccess;
-      hipLaunchKernelGGL((chunk_o_kernel<T, D>), dim3(n_items), dim3(4 * D), 0, st, (const T*)q, ldq,
-                         cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq, s.hv, s.hv / s.hk, scale,
-                         (const CT*)(ws + Ly.pw), (const float*)(ws + Ly.gw), (const T*)(ws + Ly.h),
-                         (const CT*)(ws + Ly.dl16w), (T*)o, n_items);
+      const int n_group_items = (int)(Ly.nt_max * s.hk);   // (chunk, key head)
+      hipLaunchKernelGGL((chunk_o_kernel<T, D>), dim3(n_group_items), dim3(4 * D), 0, st, (const T*)q,
+                         ldq, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq, s.hv, s.hv / s.hk,
+                         scale, (const CT*)(ws + Ly.pw), (const float*)(ws + Ly.gw),
+                         (const T*)(ws + Ly.h), (const CT*)(ws + Ly.dl16w), (T*)o, n_group_items);
       return hipGetLastError();
     }
     auto kern = o ? chunk_out_kernel<T, D, true> : chunk_out_kernel<T, D, false>;
