@@ -13,7 +13,7 @@
 // and dg from every place gam enters, assembled without cancellation (the
 // last phase below).
 //
-// One workgroup of eight waves per (GRAD_ITEMS consecutive chunks, key head)
+// One workgroup of eight waves per (up to four consecutive chunks, key head)
 // walks, for each chunk, the G value heads of the group and sums dq, dk over
 // them in registers (ascending head order, no atomics).  The operands of the
 // next head are requested while a head finishes, across chunk boundaries
@@ -44,8 +44,15 @@
 
 namespace gdn {
 
-// Consecutive chunks per workgroup of the gradient kernel.
-constexpr int GRAD_ITEMS = 4;
+// Consecutive chunks per workgroup of the gradient kernel: up to four, as
+// long as the launch keeps at least eight workgroups per CU (a few chunks
+// per workgroup amortise its first head's wait for memory; fewer
+// workgroups than that leave CUs idle on short inputs).
+constexpr int GRAD_MAX_ITEMS = 4;
+inline int grad_items(int64_t nt_max, int hk) {
+  const int64_t per = nt_max * hk / (8 * 256);
+  return per < 1 ? 1 : per > GRAD_MAX_ITEMS ? GRAD_MAX_ITEMS : (int)per;
+}
 
 template <typename T, int D> struct GradLds {
   typedef Tile<T, CHUNK, D, -1> TT;                           // token-major tile
@@ -107,7 +114,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     const T* __restrict__ ddw, const typename Compute<T>::type* __restrict__ KKw,
     const T* __restrict__ dout, const T* __restrict__ dvo,
     int64_t lddv, T* __restrict__ dq, T* __restrict__ dk, int64_t lddq, int64_t lddk,
-    float* __restrict__ dg, float* __restrict__ dbeta) {
+    float* __restrict__ dg, float* __restrict__ dbeta, int items) {
   typedef typename Compute<T>::type CT;
   typedef Mma<T> MM;
   typedef AccOrder<T> AO;
@@ -132,9 +139,9 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   int g = lane >> 4, g4 = 4 * g, c16 = lane & 15;
   const int kh = blockIdx.y;
   const int64_t n_chunks = seq_off[n_seq];
-  const int64_t c_first = (int64_t)blockIdx.x * GRAD_ITEMS;
+  const int64_t c_first = (int64_t)blockIdx.x * items;
   if (c_first >= n_chunks) return;
-  const int n_items = (int)(n_chunks - c_first < GRAD_ITEMS ? n_chunks - c_first : GRAD_ITEMS);
+  const int n_items = (int)(n_chunks - c_first < items ? n_chunks - c_first : items);
   // a work item: chunk c, its first token, its length
   struct Item { int64_t c, t0; int L; };
   auto item_of = [&](int64_t cc) __attribute__((always_inline)) -> Item {
@@ -757,7 +764,8 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
     const size_t shm = sizeof(GradLds<T, D>);
     auto kern = chunk_grad_kernel<T, D>;
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(kern, dim3((unsigned)((Ly.nt_max + GRAD_ITEMS - 1) / GRAD_ITEMS), s.hk), dim3(512), shm, st, (const T*)q,
+    const int items = grad_items(Ly.nt_max, s.hk);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((Ly.nt_max + items - 1) / items), s.hk), dim3(512), shm, st, (const T*)q,
                        (const T*)k, ldq, ldk, cu, (const int32_t*)(ws + Ly.seq_off), s.n_seq,
                        s.hv, s.hv / s.hk, scale, (const double*)(ws + Ly.gcum), (const float*)(ws + Ly.bw),
                        (const typename Compute<T>::type*)(ws + Ly.pw), (const T*)(ws + Ly.tib),
@@ -766,7 +774,7 @@ hipError_t launch_chunk_bwd_grads(const gdn_shape& s, const void* q, const void*
                        sizeof(T) == 2 ? (const void*)(ws + Ly.dl16w) : (const void*)(ws + Ly.dlw),
                        (const T*)(ws + Ly.ddw), (const typename Compute<T>::type*)(ws + Ly.kkw),
                        (const T*)dout, (const T*)dv, lddv, (T*)dq,
-                       (T*)dk, lddq, lddk, dg, dbeta);
+                       (T*)dk, lddq, lddk, dg, dbeta, items);
     return hipGetLastError();
   });
 }
