@@ -75,7 +75,7 @@ template <typename T, int D> struct GradLds {
   T Tin[TIN_LDS ? CHUNK * CHUNK : 8];
   double gam[CHUNK];
   float bet[CHUNK], Gm[CHUNK], dc[CHUNK];
-  float colB[4][CHUNK], rowB[CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
+  float colB[4][CHUNK], rowB[2][CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
   float boxE[4][CHUNK], red[8];
   // k_t . k_s, the preparation's K K^T in the compute type (fp16 for 16-bit
   // data: |k_t . k_s| <= 1 for the L2-normalised keys) and in its layout of
@@ -544,12 +544,14 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     load_states(h);
     issue_fence();
     __syncthreads();   // Y^T is complete
-    if (role == 0) {
+    {
       // dA^T = -Y^T Tinv (rows s, column t = tl), then WA, the dA part of the
-      // pair terms and the second dbeta term
+      // pair terms and the second dbeta term; the Tinv-chain waves take row
+      // blocks s of 0 .. 31, the dP waves (the same columns t) 32 .. 63
       float rb = 0.f;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int sj = 0; sj < 2; ++sj) {
+        const int st = 2 * role + sj;
         const floatx4 kks = kkv(st);
         double gs[4];
         gam4(16 * st + g4, gs);
@@ -582,7 +584,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       }
       rb += __shfl_xor(rb, 16, 64);
       rb += __shfl_xor(rb, 32, 64);
-      if (g == 0) sm.rowB[tl] = rb;
+      if (g == 0) sm.rowB[role][tl] = rb;
     }
     __syncthreads();   // WS and the dA part of the pair terms are in
     if (role == 1) {   // (E is read after phase B's barrier)
@@ -721,7 +723,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     lds_barrier();
     if (wave == 0) {
       const int t = lane;
-      float y = 0.f, db = sm.rowB[t], zt = 0.f, ips = 0.f;
+      float y = 0.f, db = sm.rowB[0][t] + sm.rowB[1][t], zt = 0.f, ips = 0.f;
       const float box = ((sm.boxE[0][t] + sm.boxE[1][t]) + sm.boxE[2][t]) + sm.boxE[3][t];
 #pragma unroll
       for (int w = 0; w < 4; ++w) db += sm.colB[w][t];

@@ -65,9 +65,15 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
                 TM::PIECES % (64 * NW) == 0 && TO::PIECES % (64 * NW) == 0,
                 "direct copies cover whole waves");
   __shared__ RB bufA, bufB;
-  // per wave: staged output rows (dS' rows k, then dDelta and dv rows t)
+  // per wave: staged output rows (dS' rows k, then dDelta and dv rows t).
+  // 16-bit data: two sets by step parity; the compute waves put a chunk's
+  // rows and a step later the mover wave of the same index stores them, so
+  // no store (nor the read-back before it) sits on the recurrence.  fp32
+  // (one set, no room for two) stores from the compute waves.
   typedef StageRows<T> SR;
-  __shared__ __align__(16) char stg[DRY ? 16 : NW * (D + 2 * CHUNK) * SR::SB];
+  constexpr bool MSTORE = sizeof(T) == 2;
+  constexpr int SRR = D + 2 * CHUNK;   // staged rows per compute wave
+  __shared__ __align__(16) char stg[DRY ? 16 : (MSTORE ? 2 : 1) * NW * SRR * SR::SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // waves [0, NW) compute, waves [NW, 2 NW) move the operands
@@ -103,7 +109,10 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   PairStore ps;
   ps.init(lane);
   const uint32_t wcol = (uint32_t)(16 * wave * sizeof(T));
-  char* const myst = stg + wave * (D + 2 * CHUNK) * SR::SB;
+  // a chunk's staging rows of wave w
+  auto stage_of = [&](int64_t c, int w) __attribute__((always_inline)) -> char* {
+    return stg + (int)((((MSTORE ? (c_end - 1 - c) & 1 : 0) * NW) + w) * SRR * SR::SB);
+  };
   // LDS read offsets (as in the state pass)
   int rw[NSD], rk[NSC];
 #pragma unroll
@@ -177,6 +186,28 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   };
   // touches a mover issues per step
   constexpr int NTOUCH = (RB::KT_TR ? 2 : 3) * NTK + 2 * NTM + 1;
+  // (movers, 16-bit data) chunk cp's rows staged by compute wave `wave` to
+  // dS', dDelta and dv; token rows past the sequence end fall outside the
+  // buffers and are dropped; with valid false every store is issued into an
+  // empty range.  The reads are asm that waits for its own results (a plain
+  // LDS read would wait for every direct copy in flight).
+  constexpr int NFL = DRY || !MSTORE ? 0 : SR::stores(D) + 2 * SR::stores(CHUNK);
+  static_assert(NTOUCH + NFL < 64, "vmcnt holds 6 bits");
+  auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
+    if constexpr (NFL == 0) return;
+    const char* st = stage_of(cp, wave);
+    const int64_t ca = valid ? cp : c_begin;
+    const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
+    const int64_t rem = seq_t1 - t0p;
+    const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
+    SR::flush_async(st, 0, D, buffer_of(dhst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
+                    wcol, rowh, lane);
+    SR::flush_async(st, D, CHUNK, buffer_of(ddw + t0p * HvD + (int64_t)h * D + v0, (uint32_t)Lp * rowb),
+                    wcol, rowb, lane);
+    SR::flush_async(st, D + CHUNK, CHUNK,
+                    buffer_of(dvo + t0p * lddv + (int64_t)h * D + v0, (uint32_t)Lp * rowv), wcol, rowv,
+                    lane);
+  };
 
   auto arow = [&](const T* base, int o, int tile_elems) __attribute__((always_inline)) -> frag {
     if constexpr (KS == 4) return base[tile_elems + o];
@@ -217,17 +248,27 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
     const int64_t rem = seq_t1 - t0;
     const int L = rem < CHUNK ? (int)rem : CHUNK;
+    char* const myst = stage_of(c, wave);
 
     // dS'^T as B operands; dS' to the workspace ([d_k][d_v] per chunk, head)
     frag sb[NSD];
 #pragma unroll
     for (int p = 0; p < NSD; ++p) sb[p] = AO::from_acc(dS, p);
+    // diag(dec) K dS'^T first: it is on the recurrence; dS' is staged and
+    // stored while these products run
+    floatx4 kd[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      kd[tt] = zero4();
+#pragma unroll
+      for (int p = 0; p < NSD; ++p) kd[tt] = MM::mma(arow(B.K, rw[p], 16 * tt * D), sb[p], kd[tt]);
+    }
     {
       const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, DRY ? 0u : D * D * sizeof(T));
       if constexpr (!DRY) {
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, dS[kt]);
-        SR::flush(myst, 0, D, rs, wcol, rowh, lane);
+        if constexpr (!MSTORE) SR::flush(myst, 0, D, rs, wcol, rowh, lane);
       }
     }
 
@@ -255,16 +296,14 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     floatx4 dd[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      floatx4 kd = zero4(), pt = zero4();
-#pragma unroll
-      for (int p = 0; p < NSD; ++p) kd = MM::mma(arow(B.K, rw[p], 16 * tt * D), sb[p], kd);
+      floatx4 pt = zero4();
 #pragma unroll
       for (int p = 0; p < NSC; ++p) pt = MM::mma(arow(B.Pt, rk[p], 16 * tt * CHUNK), ob[p], pt);
       const float4 dc = *reinterpret_cast<const float4*>(&B.Dc[16 * tt + g4]);
-      dd[tt][0] = pt[0] + dc.x * kd[0];
-      dd[tt][1] = pt[1] + dc.y * kd[1];
-      dd[tt][2] = pt[2] + dc.z * kd[2];
-      dd[tt][3] = pt[3] + dc.w * kd[3];
+      dd[tt][0] = pt[0] + dc.x * kd[tt][0];
+      dd[tt][1] = pt[1] + dc.y * kd[tt][1];
+      dd[tt][2] = pt[2] + dc.z * kd[tt][2];
+      dd[tt][3] = pt[3] + dc.w * kd[tt][3];
     }
     {
       // rows past the sequence end fall outside the buffer: dropped
@@ -272,7 +311,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
       if constexpr (!DRY) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) SR::put(myst, D + 16 * tt, ps, lane, dd[tt]);
-        SR::flush(myst, D, CHUNK, rs, wcol, rowb, lane);
+        if constexpr (!MSTORE) SR::flush(myst, D, CHUNK, rs, wcol, rowb, lane);
       }
     }
 
@@ -300,7 +339,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
         gr[tt][3] = -gm.w * dr[3];
         if constexpr (!DRY) SR::put(myst, D + CHUNK + 16 * tt, ps, lane, dr);
       }
-      if constexpr (!DRY) SR::flush(myst, D + CHUNK, CHUNK, rs, wcol, rowv, lane);
+      if constexpr (!DRY && !MSTORE) SR::flush(myst, D + CHUNK, CHUNK, rs, wcol, rowv, lane);
     }
 
     // dS^T = Gam_L dS'^T + Q^T (scale diag(Gam) dO) - K^T (diag(Gam) dR)
@@ -330,6 +369,10 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   if (mover) {
     // each step ends once the copies are in, the touches (issued after
     // them) still in flight; at the end nothing is
+    // (16-bit data) a step also stores the rows that the compute waves
+    // staged in the step before, after its copies and touches; the stores
+    // stay in flight until the next step's wait.  The first step's stores
+    // go to an empty range, so that every step issues the same count.
     auto first = [&](int64_t x) { return x >= c_begin ? x : c_begin; };
     if (c_begin < c_end) {
       fetch(bufA, c_end - 1);
@@ -339,13 +382,17 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
       fetch(bufB, c - 1 >= c_begin ? c - 1 : c);   // a repeat of chunk c at the start
       touch(first(c - 2));
-      wait_vm_barrier<NTOUCH>();
+      flush_chunk(c + 1, c + 1 < c_end);
+      wait_vm_barrier<NTOUCH + NFL>();
       if (c - 1 >= c_begin) {
         fetch(bufA, c - 2 >= c_begin ? c - 2 : c - 1);
         touch(first(c - 3));
-        wait_vm_barrier<NTOUCH>();
+        flush_chunk(c, true);
+        wait_vm_barrier<NTOUCH + NFL>();
       }
     }
+    // the first chunk's rows, staged before the last barrier
+    if (c_begin < c_end) flush_chunk(c_begin, true);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
     lds_barrier();

@@ -278,17 +278,27 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
       frag sb[NSD];
 #pragma unroll
       for (int p = 0; p < NSD; ++p) sb[p] = AO::from_acc(S, p);
+      floatx4 kx[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        kx[tt] = zero4();
+#pragma unroll
+        for (int p = 0; p < NSD; ++p) kx[tt] = MM::mma(arow(B.W, rw[p], 16 * tt * D), sb[p], kx[tt]);
+      }
+      // the chunk-start state goes to its staging rows while the products
+      // run (the puts are ordered after the K-row reads above)
+      if constexpr (!DRY) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) SR::put(stc, 16 * kt, ps, lane, S[kt]);
+      }
       floatx4 R[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        floatx4 kx = zero4();
-#pragma unroll
-        for (int p = 0; p < NSD; ++p) kx = MM::mma(arow(B.W, rw[p], 16 * tt * D), sb[p], kx);
         const float4 gm = *reinterpret_cast<const float4*>(&B.G[16 * tt + g4]);
         const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          R[tt][i] = (phi ? 0.f : to_f(B.V[TV::at(16 * tt + g4 + i, vcol)])) - gv[i] * kx[i];
+          R[tt][i] = (phi ? 0.f : to_f(B.V[TV::at(16 * tt + g4 + i, vcol)])) - gv[i] * kx[tt][i];
       }
       frag rf[NSC];
 #pragma unroll
@@ -461,30 +471,18 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     for (int64_t c = c_begin; c < c_end; c += 3) {
       {
         char* st = stage_of(c, wave);
-        if constexpr (!DRY) {
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
-        }
         compute(bufA, c, st);
       }
       lds_barrier();
       if (c + 1 >= c_end) break;
       {
         char* st = stage_of(c + 1, wave);
-        if constexpr (!DRY) {
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
-        }
         compute(bufB, c + 1, st);
       }
       lds_barrier();
       if (c + 2 >= c_end) break;
       {
         char* st = stage_of(c + 2, wave);
-        if constexpr (!DRY) {
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt) SR::put(st, 16 * kt, ps, lane, S[kt]);
-        }
         compute(bufC, c + 2, st);
       }
       lds_barrier();

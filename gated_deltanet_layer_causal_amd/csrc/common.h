@@ -81,9 +81,13 @@ __device__ __forceinline__ f8 load8(const float* p) {
   r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
   return r;
 }
+// Two floats to bf16 (round to nearest even) in one word, low half first.
+// Converted as a pair, so that it is one v_cvt_pk_bf16_f32; two scalar
+// conversions cost a conversion each plus a shift and an or.
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-  bf16 x = (bf16)a, y = (bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 // Two 16-bit storage elements (bf16 or fp16) in one 32-bit word, low half
 // first: to floats, and from floats (round to nearest even).
