@@ -153,46 +153,13 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     if (wave == NW - 1 && lane < 16) copy_to_lds(buffer_of(Bw + ch * CHUNK, CHUNK * 4), B.Bt, 16u * lane, 0);
   };
 
-  // The movers also touch every line of the chunk after the one they copy,
-  // a step ahead, so that its copies find the lines in L2: one 4-byte
-  // direct copy per line into a sink, each mover taking every other line
-  // (lanes past a tile read out of range, which touches no memory).
-  __shared__ float sink[64];
-  constexpr int TKB = CHUNK * D * (int)sizeof(T), TMB = CHUNK * CHUNK * (int)sizeof(T);
-  constexpr int NTK = (TKB / 128 + 127) / 128, NTM = (TMB / 128 + 127) / 128;   // touches per tile
-  auto touch_tile = [&](const void* base, int bytes, int n, int wave) __attribute__((always_inline)) {
-    const auto rs = buffer_of(base, (uint32_t)bytes);
-#pragma unroll
-    for (int j = 0; j < n; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)sink, 4,
-                                               (uint32_t)(2 * (64 * j + lane) + wave) * 128u, 0, 0, 0);
-  };
-  auto touch = [&](int64_t c) __attribute__((always_inline)) {
-    int wave = wave_ - NW;   // (movers only)
-    asm volatile("" : "+s"(wave));
-    const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
-    const int64_t rem = seq_t1 - t0;
-    const int Lc = rem < CHUNK ? (int)rem : CHUNK;
-    const int64_t ch = (int64_t)c * Hv + h, ck = (int64_t)c * Hk + kh;
-    touch_tile(Kb + ck * CHUNK * D, TKB, NTK, wave);
-    if constexpr (!RB::KT_TR) touch_tile(Ktb + ck * D * CHUNK, TKB, NTK, wave);
-    touch_tile(Qtb + ck * D * CHUNK, TKB, NTK, wave);
-    touch_tile(Ptb + ch * CHUNK * CHUNK, TMB, NTM, wave);
-    touch_tile(Tib + ch * 2 * CHUNK * CHUNK + (RB::KT_TR ? 0 : CHUNK * CHUNK), TMB, NTM, wave);
-    // the block's dO rows (one line each)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        buffer_of(dout + t0 * HvD + (int64_t)h * D + v0, (uint32_t)Lc * rowb),
-        (__attribute__((address_space(3))) void*)sink, 4, (uint32_t)(2 * lane + wave) * rowb, 0, 0, 0);
-  };
-  // touches a mover issues per step
-  constexpr int NTOUCH = (RB::KT_TR ? 2 : 3) * NTK + 2 * NTM + 1;
   // (movers, 16-bit data) chunk cp's rows staged by compute wave `wave` to
   // dS', dDelta and dv; token rows past the sequence end fall outside the
   // buffers and are dropped; with valid false every store is issued into an
   // empty range.  The reads are asm that waits for its own results (a plain
   // LDS read would wait for every direct copy in flight).
   constexpr int NFL = DRY || !MSTORE ? 0 : SR::stores(D) + 2 * SR::stores(CHUNK);
-  static_assert(NTOUCH + NFL < 64, "vmcnt holds 6 bits");
+  static_assert(NFL < 64, "vmcnt holds 6 bits");
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
     if constexpr (NFL == 0) return;
     const char* st = stage_of(cp, wave);
@@ -200,11 +167,11 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
     const int64_t rem = seq_t1 - t0p;
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
-    SR::flush_async(st, 0, D, buffer_of(dhst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
+    SR::template flush_async<CACHE_NT>(st, 0, D, buffer_of(dhst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
                     wcol, rowh, lane);
-    SR::flush_async(st, D, CHUNK, buffer_of(ddw + t0p * HvD + (int64_t)h * D + v0, (uint32_t)Lp * rowb),
+    SR::template flush_async<CACHE_NT>(st, D, CHUNK, buffer_of(ddw + t0p * HvD + (int64_t)h * D + v0, (uint32_t)Lp * rowb),
                     wcol, rowb, lane);
-    SR::flush_async(st, D + CHUNK, CHUNK,
+    SR::template flush_async<CACHE_NT>(st, D + CHUNK, CHUNK,
                     buffer_of(dvo + t0p * lddv + (int64_t)h * D + v0, (uint32_t)Lp * rowv), wcol, rowv,
                     lane);
   };
@@ -367,28 +334,21 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   // the waits for them stay off the recurrence.  One barrier per step: after
   // it the buffer just computed is free and the next one is filled.
   if (mover) {
-    // each step ends once the copies are in, the touches (issued after
-    // them) still in flight; at the end nothing is
-    // (16-bit data) a step also stores the rows that the compute waves
-    // staged in the step before, after its copies and touches; the stores
-    // stay in flight until the next step's wait.  The first step's stores
-    // go to an empty range, so that every step issues the same count.
-    auto first = [&](int64_t x) { return x >= c_begin ? x : c_begin; };
-    if (c_begin < c_end) {
-      fetch(bufA, c_end - 1);
-      touch(first(c_end - 2));
-    }
-    wait_vm_barrier<NTOUCH>();
+    // each step ends once the copies are in; at the end nothing is in
+    // flight.  (16-bit data) a step also stores the rows that the compute waves
+    // staged in the step before, after its copies; the stores stay in
+    // flight until the next step's wait.  The first step's stores go to an
+    // empty range, so that every step issues the same count.
+    if (c_begin < c_end) fetch(bufA, c_end - 1);
+    wait_vm_barrier<0>();
     for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
       fetch(bufB, c - 1 >= c_begin ? c - 1 : c);   // a repeat of chunk c at the start
-      touch(first(c - 2));
       flush_chunk(c + 1, c + 1 < c_end);
-      wait_vm_barrier<NTOUCH + NFL>();
+      wait_vm_barrier<NFL>();
       if (c - 1 >= c_begin) {
         fetch(bufA, c - 2 >= c_begin ? c - 2 : c - 1);
-        touch(first(c - 3));
         flush_chunk(c, true);
-        wait_vm_barrier<NTOUCH + NFL>();
+        wait_vm_barrier<NFL>();
       }
     }
     // the first chunk's rows, staged before the last barrier

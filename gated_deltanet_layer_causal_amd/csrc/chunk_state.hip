@@ -237,10 +237,10 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
     const uint32_t col = (uint32_t)(16 * wave * sizeof(T));
     const int64_t tok = t0p * HvD + (int64_t)h * D + v0;
-    SR::flush_async(st, 0, D, buffer_of(hst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
+    SR::template flush_async<CACHE_NT>(st, 0, D, buffer_of(hst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
               col, rowh, lane);
-    SR::flush_async(st, SROW_R, CHUNK, buffer_of(Rw + tok, (uint32_t)Lp * rowb), col, rowb, lane);
-    SR::flush_async(st, SROW_D16, CHUNK, buffer_of(Dl16w + tok, (uint32_t)Lp * rowb), col, rowb, lane);
+    SR::template flush_async<CACHE_NT>(st, SROW_R, CHUNK, buffer_of(Rw + tok, (uint32_t)Lp * rowb), col, rowb, lane);
+    SR::template flush_async<CACHE_NT>(st, SROW_D16, CHUNK, buffer_of(Dl16w + tok, (uint32_t)Lp * rowb), col, rowb, lane);
   };
 
   // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).

@@ -96,10 +96,15 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // wave's 64 pieces land at consecutive 16-byte slots from `lds` (uniform).
 // Buffer accesses are range-checked against the descriptor's size on the
 // per-lane offset (loads past it read zero, stores past it are dropped).
+// Cache policy of a buffer access (the instruction's aux bits on gfx950):
+// non-temporal, for data streamed past the caches that no later access of
+// the same kernel reads (rows stored for another kernel).
+constexpr int CACHE_NT = 2;
+template <int AUX = 0>
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
                                             uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
+                                           voff, soff, 0, AUX);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -246,7 +251,9 @@ template <typename T> struct StageRows {
   // flush() for a wave with direct copies into other LDS regions in flight:
   // the reads are inline asm, which the compiler does not order after those
   // copies (a plain LDS read would wait for all of them, vmcnt(0)); each
-  // asm block waits for its own reads before its outputs are used
+  // asm block waits for its own reads before its outputs are used; AUX is
+  // the stores' cache policy
+  template <int AUX = 0>
   __device__ __forceinline__ static void flush_async(const char* region, int row0, int n,
                                                      __amdgpu_buffer_rsrc_t rs, uint32_t col,
                                                      uint32_t ldb, int lane) {
@@ -254,7 +261,7 @@ template <typename T> struct StageRows {
     const uint32_t a = lds_offset(region) + (uint32_t)((row0 + r) * SB + pc * 16);
     constexpr uint32_t STEP = RPI * SB;   // LDS bytes between consecutive stores' rows
     auto store = [&](const u32x4& v, int j) __attribute__((always_inline)) {
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs, col + (uint32_t)(j * RPI + r) * ldb + (uint32_t)pc * 16u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, col + (uint32_t)(j * RPI + r) * ldb + (uint32_t)pc * 16u, 0, AUX);
     };
 #pragma unroll
     for (int j = 0; j < n / RPI; j += 2) {
