@@ -153,13 +153,48 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     if (wave == NW - 1 && lane < 16) copy_to_lds(buffer_of(Bw + ch * CHUNK, CHUNK * 4), B.Bt, 16u * lane, 0);
   };
 
+  // (16-bit data) The movers also bring the lines of the chunk after the
+  // one they copy into L2, a step ahead, so that its copies find them
+  // there: one 4-byte direct copy per 128-byte line into a sink.  The four
+  // workgroups of a head share the tiles of the chunk (they run on one XCD),
+  // so each touches every fourth line of them: mover 0 of K and Q^T, mover
+  // 1 of P^T and Tinv; and each mover every other row of its block's dO.
+  // Lanes past a tile read out of range, which touches no memory.
+  __shared__ float sink[64];
+  constexpr int NTOUCH = MSTORE ? 3 : 0;   // touches a mover issues per step
+  auto touch_tile = [&](const void* base, int bytes) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_of(base, (uint32_t)bytes),
+                                             (__attribute__((address_space(3))) void*)sink, 4,
+                                             (uint32_t)(4 * lane + vb) * 128u, 0, 0, 0);
+  };
+  auto touch = [&](int64_t c) __attribute__((always_inline)) {
+    if constexpr (NTOUCH == 0) return;
+    int wave = wave_ - NW;   // (movers only)
+    asm volatile("" : "+s"(wave));
+    const int64_t t0 = seq_t0 + CHUNK * (c - c_begin);
+    const int64_t rem = seq_t1 - t0;
+    const int Lc = rem < CHUNK ? (int)rem : CHUNK;
+    const int64_t ch = (int64_t)c * Hv + h, ck = (int64_t)c * Hk + kh;
+    constexpr int TKB = CHUNK * D * (int)sizeof(T), TMB = CHUNK * CHUNK * (int)sizeof(T);
+    static_assert(TKB <= 4 * 64 * 128 && NW == 2, "one touch per tile and mover");
+    if (wave == 0) {
+      touch_tile(Kb + ck * CHUNK * D, TKB);
+      touch_tile(Qtb + ck * D * CHUNK, TKB);
+    } else {
+      touch_tile(Ptb + ch * CHUNK * CHUNK, TMB);
+      touch_tile(Tib + ch * 2 * CHUNK * CHUNK, TMB);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        buffer_of(dout + t0 * HvD + (int64_t)h * D + v0, (uint32_t)Lc * rowb),
+        (__attribute__((address_space(3))) void*)sink, 4, (uint32_t)(2 * lane + wave) * rowb, 0, 0, 0);
+  };
   // (movers, 16-bit data) chunk cp's rows staged by compute wave `wave` to
   // dS', dDelta and dv; token rows past the sequence end fall outside the
   // buffers and are dropped; with valid false every store is issued into an
   // empty range.  The reads are asm that waits for its own results (a plain
   // LDS read would wait for every direct copy in flight).
   constexpr int NFL = DRY || !MSTORE ? 0 : SR::stores(D) + 2 * SR::stores(CHUNK);
-  static_assert(NFL < 64, "vmcnt holds 6 bits");
+  static_assert(NTOUCH + NFL < 64, "vmcnt holds 6 bits");
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
     if constexpr (NFL == 0) return;
     const char* st = stage_of(cp, wave);
@@ -334,21 +369,27 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   // the waits for them stay off the recurrence.  One barrier per step: after
   // it the buffer just computed is free and the next one is filled.
   if (mover) {
-    // each step ends once the copies are in; at the end nothing is in
-    // flight.  (16-bit data) a step also stores the rows that the compute waves
+    // each step ends once the copies are in, the touches (issued after
+    // them) still in flight; at the end nothing is.  (16-bit data) a step also stores the rows that the compute waves
     // staged in the step before, after its copies; the stores stay in
     // flight until the next step's wait.  The first step's stores go to an
     // empty range, so that every step issues the same count.
-    if (c_begin < c_end) fetch(bufA, c_end - 1);
-    wait_vm_barrier<0>();
+    auto first = [&](int64_t x) { return x >= c_begin ? x : c_begin; };
+    if (c_begin < c_end) {
+      fetch(bufA, c_end - 1);
+      touch(first(c_end - 2));
+    }
+    wait_vm_barrier<NTOUCH>();
     for (int64_t c = c_end - 1; c >= c_begin; c -= 2) {
       fetch(bufB, c - 1 >= c_begin ? c - 1 : c);   // a repeat of chunk c at the start
+      touch(first(c - 2));
       flush_chunk(c + 1, c + 1 < c_end);
-      wait_vm_barrier<NFL>();
+      wait_vm_barrier<NTOUCH + NFL>();
       if (c - 1 >= c_begin) {
         fetch(bufA, c - 2 >= c_begin ? c - 2 : c - 1);
+        touch(first(c - 3));
         flush_chunk(c, true);
-        wait_vm_barrier<NFL>();
+        wait_vm_barrier<NTOUCH + NFL>();
       }
     }
     // the first chunk's rows, staged before the last barrier
