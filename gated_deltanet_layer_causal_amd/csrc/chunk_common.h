@@ -90,6 +90,19 @@ inline int64_t seg_len(const gdn_shape& s) {
 }
 
 // Workspace layout (byte offsets; every region 256-byte aligned).
+// The per-chunk intermediates that the sequential passes store (chunk-start
+// states and their gradients, R, Delta, dDelta) keep each block of SBV value
+// columns together: a sequential-pass workgroup owns SBV value columns, so
+// it writes whole lines rather than a quarter of each row of the head.
+//   states:     [chunk][head][dv / SBV][dk][SBV]
+//   token rows: [chunk][head][dv / SBV][64][SBV] (row t: token t of the chunk)
+constexpr int SBV = 32;
+// element offset, in a (chunk, head) block of n rows, of row r and value
+// column v (a run of up to 8 columns from v stays in one block when v % 8 == 0)
+__host__ __device__ constexpr int64_t blk_at(int r, int v, int n) {
+  return (int64_t)(v / SBV) * n * SBV + (int64_t)r * SBV + v % SBV;
+}
+
 struct ChunkLayout {
   int64_t nt_max;     // upper bound on the number of chunks: T/64 + n_seq
   int64_t seg;        // segment length in chunks (0: one span per sequence)
@@ -116,9 +129,10 @@ struct ChunkLayout {
   size_t kkw;         // CT [nt_max][hk][64][64]: K K^T of each chunk (backward)
   size_t bw;          // fp32 [nt_max][hv][64]: beta_t, zero past the chunk end (backward)
   size_t tib;         // T [nt_max][hv][2][64][64]: Tinv (columns in accumulator order), Tinv^T (backward)
-  size_t h, dh;       // T [nt_max][hv][dk][dv]: chunk-start state, chunk-end state gradient
-  size_t rw, dlw, ddw;  // T [T][hv][dv]: R, Delta (fp32 data only), dDelta
-  size_t dl16w;       // CT [T][hv][dv]: Delta in the compute type (16-bit data: for the outputs and the gradients)
+  size_t h, dh;       // T [nt_max][hv][dv / SBV][dk][SBV]: chunk-start state, chunk-end state gradient
+  size_t rw, dlw, ddw;  // T [nt_max][hv][dv / SBV][64][SBV]: R, Delta (fp32 data only), dDelta
+  size_t dl16w;       // CT [nt_max][hv][dv / SBV][64][SBV]: Delta in the compute type (16-bit data:
+                      // for the outputs and the gradients)
   size_t sink;        // SINK_ELEMS scratch floats: target of stores for padding rows
   size_t total_fwd, total_bwd;
 };
@@ -182,10 +196,11 @@ inline ChunkLayout chunk_layout(const gdn_shape& s, ChunkFlow flow) {
   L.tib = off; off = align256(off + es * (size_t)L.nt_max * s.hv * 2 * CHUNK * CHUNK);
   L.h = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
   L.dh = off; off = align256(off + es * (size_t)L.nt_max * s.hv * s.dk * s.dv);
-  L.rw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
-  L.dlw = off; off = align256(off + (es == 4 ? es * (size_t)T * s.hv * s.dv : 0));
-  L.ddw = off; off = align256(off + es * (size_t)T * s.hv * s.dv);
-  L.dl16w = off; off = align256(off + (es == 2 ? 2 * (size_t)T * s.hv * s.dv : 0));
+  const size_t rows = (size_t)L.nt_max * CHUNK * s.hv * s.dv;   // per-chunk token rows
+  L.rw = off; off = align256(off + es * rows);
+  L.dlw = off; off = align256(off + (es == 4 ? es * rows : 0));
+  L.ddw = off; off = align256(off + es * rows);
+  L.dl16w = off; off = align256(off + (es == 2 ? 2 * rows : 0));
   L.total_bwd = off;
   return L;
 }

@@ -270,16 +270,30 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       }
     }
   };
+  // ... the same from a chunk's blocks of SBV-column rows (R, Delta): piece
+  // q of a row lies in block q / PPB
+  auto copy_blk = [&](T* dst, const T* blk0, int L, bool live) __attribute__((always_inline)) {
+    constexpr int PPB = SBV * (int)sizeof(T) / 16;   // pieces per block row
+    if (NCW == 8 || wave < NCW) {
+      const auto rs = buffer_of(blk0, live ? (uint32_t)(CHUNK * D * sizeof(T)) : 0u);
+#pragma unroll
+      for (int j = 0; j < TT::PIECES / (64 * NCW); ++j) {
+        const int s = (j * NCW + wave) * 64 + lane, r = s / TT::RP, q = (s % TT::RP) ^ TT::swz(r);
+        const uint32_t off = (uint32_t)(q / PPB) * (uint32_t)(CHUNK * SBV * sizeof(T)) +
+                             (uint32_t)(r < L ? r : L - 1) * (uint32_t)(SBV * sizeof(T)) + (uint32_t)(q % PPB) * 16u;
+        copy_to_lds(rs, dst + (j * NCW + wave) * 64 * TT::EPP, off, 0);
+      }
+    }
+  };
   // (R is read in phase A only, so it comes with Tinv, a phase earlier)
   auto copy_head = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
     const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-    const int64_t base = it.t0 * HvD + (int64_t)h * D;
-    copy_rows(sm.tO, dout + base, rowb, it.L, live);
-    copy_rows(sm.tDl, reinterpret_cast<const T*>(Dlw) + base, rowb, it.L, live);
+    copy_rows(sm.tO, dout + it.t0 * HvD + (int64_t)h * D, rowb, it.L, live);
+    copy_blk(sm.tDl, reinterpret_cast<const T*>(Dlw) + (it.c * Hv + h) * CHUNK * D, it.L, live);
     copy_rows(sm.tdR, dvo + it.t0 * lddv + (int64_t)h * D, (uint32_t)(lddv * sizeof(T)), it.L, live);
   };
   auto copy_r = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
-    copy_rows(sm.tR, Rw + it.t0 * HvD + (int64_t)h * D, (uint32_t)(HvD * sizeof(T)), it.L, live);
+    copy_blk(sm.tR, Rw + (it.c * Hv + h) * CHUNK * D, it.L, live);
   };
   // ... the gate values (wave 0: loaded into registers a phase before they
   // go to LDS) ...
@@ -345,12 +359,16 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   constexpr int NAD = NSD * FR, NPD = 4 * (int)sizeof(CT);
   constexpr int NA = NAD > NPD ? NAD : NPD;
   uint32_t aop[NA];
+  // (dDelta: row tl of the chunk's blocks of SBV columns, one buffer per
+  // block, so that rows past the chunk end read zero)
   auto load_tinv = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
-    const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
-    const auto rs = buffer_of(ddw + it.t0 * HvD + (int64_t)h * D, live ? (uint32_t)it.L * rowb : 0u);
+    constexpr uint32_t rowb = (uint32_t)(SBV * sizeof(T));
+    const T* blk0 = ddw + (it.c * Hv + h) * CHUNK * D;
 #pragma unroll
     for (int p = 0; p < NSD; ++p) {
-      const frag f = buffer_frag<T>(rs, (uint32_t)tl * rowb + (uint32_t)pcol(p) * sizeof(T));
+      const int b = p * KS / SBV;   // the block of columns pcol(p) .. (the same for every lane)
+      const auto rs = buffer_of(blk0 + (int64_t)b * CHUNK * SBV, live ? (uint32_t)it.L * rowb : 0u);
+      const frag f = buffer_frag<T>(rs, (uint32_t)tl * rowb + (uint32_t)(pcol(p) - b * SBV) * sizeof(T));
       if constexpr (FR == 4) {
         const u32x4 w = __builtin_bit_cast(u32x4, f);
 #pragma unroll
@@ -393,11 +411,12 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   // ... and every wave's rows of the saved states (phase B)
   frag hA[NSD], dhA[NSD];
   auto load_states = [&](int h) __attribute__((always_inline)) {
-    const int64_t r = (cur.c * Hv + h) * D * D + (int64_t)(16 * kt + c16) * D;
+    const int64_t r = (cur.c * Hv + h) * D * D;
 #pragma unroll
     for (int p = 0; p < NSD; ++p) {
-      hA[p] = rdf(hst + r, pcol(p));
-      dhA[p] = rdf(dhst + r, pcol(p));
+      const int64_t e = r + blk_at(16 * kt + c16, pcol(p), D);
+      hA[p] = rdf(hst + e, 0);
+      dhA[p] = rdf(dhst + e, 0);
     }
   };
   auto load_a = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {

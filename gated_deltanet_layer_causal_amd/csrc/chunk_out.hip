@@ -103,11 +103,11 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
   // ---- inputs of R and Delta, all requested up front
   uint4 hraw[NH];
   {
-    const T* Sg = hst + ch * D * D + v0;
+    const T* Sg = hst + ch * D * D + (int64_t)v0 * D;   // the quarter's block of the state
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
       const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
-      hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * D + pc * EPP);
+      hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * SBV + pc * EPP);
     }
   }
   const uint32_t ldkb = (uint32_t)(ldk * sizeof(T)), ldqb = (uint32_t)(ldq * sizeof(T));
@@ -187,6 +187,18 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
   };
   // byte offset of this lane's four value columns in token row c16
   const uint32_t so = (uint32_t)(((int64_t)c16 * HvD + v0 + g4) * sizeof(T));
+  // ... and in the quarter's block of SBV-column rows of a stored
+  // intermediate (R, Delta)
+  static_assert(SBV == 32, "a quarter is one block of stored value columns");
+  auto put_blk = [&](T* base, const floatx4 (&x)[2][2]) __attribute__((always_inline)) {
+    const uint32_t rb = (uint32_t)(SBV * sizeof(T));
+    const auto rs = buffer_of(base + ch * CHUNK * D + (int64_t)v0 * CHUNK, (uint32_t)L * rb);
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        buffer_store4<T>(rs, (uint32_t)(tok(j) + c16) * rb + (uint32_t)((16 * vt + g4) * sizeof(T)), x[vt][j]);
+  };
   auto put_out = [&](T* base, const floatx4 (&x)[2][2]) __attribute__((always_inline)) {
     // rows past the chunk end fall outside the buffer: dropped
     const auto rs = buffer_of(base + t0 * HvD + (int64_t)h * D, (uint32_t)L * rowb);
@@ -210,7 +222,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
       for (int i = 0; i < 4; ++i) R[vt][j][i] = vv[vt][j][i] - gm[j] * acc[i];
     }
-  put_out(Rw, R);
+  put_blk(Rw, R);
   put_xs(R);
   __syncthreads();
 
@@ -245,7 +257,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
       for (int p = 0; p < NSC; ++p) pb[j][p] = acc_row(Pc, tok(j) + c16, p);
     issue_fence();
   }
-  put_out(Dlw, Dl);
+  put_blk(Dlw, Dl);
 
   if constexpr (WITH_O) {
     __syncthreads();   // both token halves have read R
@@ -345,11 +357,11 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     // ---- this head's inputs, requested up front: S slice, P rows, Delta rows
     uint4 hraw[NH];
     {
-      const T* Sg = hst + ch * D * D + v0;
+      const T* Sg = hst + ch * D * D + (int64_t)v0 * D;   // the quarter's block of the state
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
-        hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * D + pc * EPP);
+        hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * SBV + pc * EPP);
       }
     }
     cfrag pb[2][NSC];
@@ -360,11 +372,12 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         pb[j][p] = *reinterpret_cast<const cfrag*>(Pc + (tok(j) + c16) * CHUNK + 32 * p + 8 * g);
     // this wave's 32 tokens of the quarter's Delta columns: 4 pieces per row
     cfrag draw[2];
-    const auto rd = buffer_of(Dlw + t0 * HvD + (int64_t)h * D + v0, (uint32_t)L * rowb);
+    const uint32_t rdb = (uint32_t)(SBV * sizeof(CT));
+    const auto rd = buffer_of(Dlw + ch * CHUNK * D + (int64_t)v0 * CHUNK, (uint32_t)L * rdb);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = lane + 64 * j, r = 32 * th + i / PPR, pc = i % PPR;
-      draw[j] = buffer_frag<CT>(rd, (uint32_t)r * rowb + (uint32_t)(pc * 16));
+      draw[j] = buffer_frag<CT>(rd, (uint32_t)r * rdb + (uint32_t)(pc * 16));
     }
     float gm[2];
 #pragma unroll

@@ -104,7 +104,10 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   cl.init(lane, wave, NW);
   const uint32_t rowb = (uint32_t)(HvD * sizeof(T));
   const uint32_t rowv = (uint32_t)(lddv * sizeof(T));
-  const uint32_t rowh = (uint32_t)(D * sizeof(T));
+  // dS' and dDelta of this block of value columns (SBV = BV of them) are
+  // stored as SBV-column rows
+  static_assert(BV == SBV, "a workgroup owns one block of stored value columns");
+  const uint32_t rowh = (uint32_t)(SBV * sizeof(T));
   // outputs leave through the wave's LDS rows in 16-byte pieces
   PairStore ps;
   ps.init(lane);
@@ -202,10 +205,11 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
     const int64_t rem = seq_t1 - t0p;
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
-    SR::template flush_async<CACHE_NT>(st, 0, D, buffer_of(dhst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
-                    wcol, rowh, lane);
-    SR::template flush_async<CACHE_NT>(st, D, CHUNK, buffer_of(ddw + t0p * HvD + (int64_t)h * D + v0, (uint32_t)Lp * rowb),
-                    wcol, rowb, lane);
+    SR::template flush_async<CACHE_NT>(st, 0, D,
+        buffer_of(dhst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), wcol, rowh,
+        lane);
+    SR::template flush_async<CACHE_NT>(st, D, CHUNK,
+        buffer_of(ddw + (ca * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK, (uint32_t)Lp * rowh), wcol, rowh, lane);
     SR::template flush_async<CACHE_NT>(st, D + CHUNK, CHUNK,
                     buffer_of(dvo + t0p * lddv + (int64_t)h * D + v0, (uint32_t)Lp * rowv), wcol, rowv,
                     lane);
@@ -266,7 +270,8 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
       for (int p = 0; p < NSD; ++p) kd[tt] = MM::mma(arow(B.K, rw[p], 16 * tt * D), sb[p], kd[tt]);
     }
     {
-      const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + v0, DRY ? 0u : D * D * sizeof(T));
+      const auto rs = buffer_of(dhst + ((int64_t)c * Hv + h) * D * D + (int64_t)v0 * D,
+                                DRY ? 0u : D * SBV * sizeof(T));
       if constexpr (!DRY) {
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, dS[kt]);
@@ -309,11 +314,12 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     }
     {
       // rows past the sequence end fall outside the buffer: dropped
-      const auto rs = buffer_of(ddw + t0 * HvD + (int64_t)h * D + v0, DRY ? 0u : (uint32_t)L * rowb);
+      const auto rs = buffer_of(ddw + ((int64_t)c * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK,
+                                DRY ? 0u : (uint32_t)L * rowh);
       if constexpr (!DRY) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) SR::put(myst, D + 16 * tt, ps, lane, dd[tt]);
-        if constexpr (!MSTORE) SR::flush(myst, D, CHUNK, rs, wcol, rowb, lane);
+        if constexpr (!MSTORE) SR::flush(myst, D, CHUNK, rs, wcol, rowh, lane);
       }
     }
 

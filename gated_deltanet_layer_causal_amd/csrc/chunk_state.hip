@@ -194,10 +194,14 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   // (two adjacent value columns per store)
   PairStore ps;
   ps.init(lane);
-  const uint32_t rowh = (uint32_t)(D * sizeof(T));
+  // the state and the token rows of this block of value columns (SBV = BV
+  // of them) are stored as SBV-column rows
+  static_assert(BV == SBV, "a workgroup owns one block of stored value columns");
+  const uint32_t rowh = (uint32_t)(SBV * sizeof(T));
   const uint32_t hb = (uint32_t)(16 * wave * sizeof(T)) + ps.lane_off<T>(lane, rowh);
   auto store_state = [&](int64_t c) __attribute__((always_inline)) {
-    const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + v0, DRY ? 0u : D * D * sizeof(T));
+    const auto rs = buffer_of(hst + ((int64_t)c * Hv + h) * D * D + (int64_t)v0 * D,
+                              DRY ? 0u : D * SBV * sizeof(T));
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) ps.store<T>(rs, hb + (uint32_t)(16 * kt) * rowh, rowh, S[kt]);
   };
@@ -236,11 +240,13 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     const int64_t rem = seq_t1 - t0p;
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
     const uint32_t col = (uint32_t)(16 * wave * sizeof(T));
-    const int64_t tok = t0p * HvD + (int64_t)h * D + v0;
-    SR::template flush_async<CACHE_NT>(st, 0, D, buffer_of(hst + (ca * Hv + h) * D * D + v0, valid ? D * D * sizeof(T) : 0u),
-              col, rowh, lane);
-    SR::template flush_async<CACHE_NT>(st, SROW_R, CHUNK, buffer_of(Rw + tok, (uint32_t)Lp * rowb), col, rowb, lane);
-    SR::template flush_async<CACHE_NT>(st, SROW_D16, CHUNK, buffer_of(Dl16w + tok, (uint32_t)Lp * rowb), col, rowb, lane);
+    const int64_t blk = (ca * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK;
+    SR::template flush_async<CACHE_NT>(st, 0, D,
+        buffer_of(hst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), col, rowh,
+        lane);
+    SR::template flush_async<CACHE_NT>(st, SROW_R, CHUNK, buffer_of(Rw + blk, (uint32_t)Lp * rowh), col, rowh, lane);
+    SR::template flush_async<CACHE_NT>(st, SROW_D16, CHUNK, buffer_of(Dl16w + blk, (uint32_t)Lp * rowh), col, rowh,
+                                       lane);
   };
 
   // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).
