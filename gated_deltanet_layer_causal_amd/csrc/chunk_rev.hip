@@ -70,10 +70,12 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   // rows and a step later the mover wave of the same index stores them, so
   // no store (nor the read-back before it) sits on the recurrence.  fp32
   // (one set, no room for two) stores from the compute waves.
-  typedef StageRows<T> SR;
+  typedef StageRows<T> SR;        // (fp32: one set of row-major staging, stored by the compute waves)
   constexpr bool MSTORE = sizeof(T) == 2;
   constexpr int SRR = D + 2 * CHUNK;   // staged rows per compute wave
-  __shared__ __align__(16) char stg[DRY ? 16 : (MSTORE ? 2 : 1) * NW * SRR * SR::SB];
+  typedef StageCols<SRR> SC;       // (16-bit: two sets of column-major staging, stored by the movers)
+  constexpr int SWB = MSTORE ? SC::BYTES : SRR * SR::SB;   // staging bytes per wave and set
+  __shared__ __align__(16) char stg[DRY ? 16 : (MSTORE ? 2 : 1) * NW * SWB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // waves [0, NW) compute, waves [NW, 2 NW) move the operands
@@ -112,9 +114,14 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   PairStore ps;
   ps.init(lane);
   const uint32_t wcol = (uint32_t)(16 * wave * sizeof(T));
+  // one accumulator tile into rows row0.. of a wave's staging
+  auto put = [&](char* st, int row0, const floatx4& x) __attribute__((always_inline)) {
+    if constexpr (MSTORE) SC::template put<T>(st, row0, lane, x);
+    else SR::put(st, row0, ps, lane, x);
+  };
   // a chunk's staging rows of wave w
   auto stage_of = [&](int64_t c, int w) __attribute__((always_inline)) -> char* {
-    return stg + (int)((((MSTORE ? (c_end - 1 - c) & 1 : 0) * NW) + w) * SRR * SR::SB);
+    return stg + (int)((((MSTORE ? (c_end - 1 - c) & 1 : 0) * NW) + w) * SWB);
   };
   // LDS read offsets (as in the state pass)
   int rw[NSD], rk[NSC];
@@ -196,7 +203,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
   // buffers and are dropped; with valid false every store is issued into an
   // empty range.  The reads are asm that waits for its own results (a plain
   // LDS read would wait for every direct copy in flight).
-  constexpr int NFL = DRY || !MSTORE ? 0 : SR::stores(D) + 2 * SR::stores(CHUNK);
+  constexpr int NFL = DRY || !MSTORE ? 0 : SC::stores(D) + 2 * SC::stores(CHUNK);
   static_assert(NTOUCH + NFL < 64, "vmcnt holds 6 bits");
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
     if constexpr (NFL == 0) return;
@@ -205,12 +212,12 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
     const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
     const int64_t rem = seq_t1 - t0p;
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
-    SR::template flush_async<CACHE_NT>(st, 0, D,
+    SC::template flush_async<CACHE_NT>(st, 0, D,
         buffer_of(dhst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), wcol, rowh,
         lane);
-    SR::template flush_async<CACHE_NT>(st, D, CHUNK,
+    SC::template flush_async<CACHE_NT>(st, D, CHUNK,
         buffer_of(ddw + (ca * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK, (uint32_t)Lp * rowh), wcol, rowh, lane);
-    SR::template flush_async<CACHE_NT>(st, D + CHUNK, CHUNK,
+    SC::template flush_async<CACHE_NT>(st, D + CHUNK, CHUNK,
                     buffer_of(dvo + t0p * lddv + (int64_t)h * D + v0, (uint32_t)Lp * rowv), wcol, rowv,
                     lane);
   };
@@ -274,7 +281,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
                                 DRY ? 0u : D * SBV * sizeof(T));
       if constexpr (!DRY) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) SR::put(myst, 16 * kt, ps, lane, dS[kt]);
+        for (int kt = 0; kt < NKT; ++kt) put(myst, 16 * kt, dS[kt]);
         if constexpr (!MSTORE) SR::flush(myst, 0, D, rs, wcol, rowh, lane);
       }
     }
@@ -318,7 +325,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
                                 DRY ? 0u : (uint32_t)L * rowh);
       if constexpr (!DRY) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) SR::put(myst, D + 16 * tt, ps, lane, dd[tt]);
+        for (int tt = 0; tt < 4; ++tt) put(myst, D + 16 * tt, dd[tt]);
         if constexpr (!MSTORE) SR::flush(myst, D, CHUNK, rs, wcol, rowh, lane);
       }
     }
@@ -345,7 +352,7 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
         gr[tt][1] = -gm.y * dr[1];
         gr[tt][2] = -gm.z * dr[2];
         gr[tt][3] = -gm.w * dr[3];
-        if constexpr (!DRY) SR::put(myst, D + CHUNK + 16 * tt, ps, lane, dr);
+        if constexpr (!DRY) put(myst, D + CHUNK + 16 * tt, dr);
       }
       if constexpr (!DRY && !MSTORE) SR::flush(myst, D + CHUNK, CHUNK, rs, wcol, rowv, lane);
     }

@@ -210,12 +210,12 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
   // into LDS rows of their own (paired words, ds_write2); a step later the
   // mover wave of the same index stores them in 16-byte pieces, so no store
   // sits on the recurrence.  Two sets of rows, by chunk parity.
-  typedef StageRows<T> SR;
   constexpr int SRR = D + 2 * CHUNK;   // staged rows per compute wave
+  typedef StageCols<SRR> SR;
   constexpr int SROW_R = D, SROW_D16 = D + CHUNK;
-  __shared__ __align__(16) char stg[SB::KR && !DRY ? 2 * NW * SRR * SR::SB : 16];
+  __shared__ __align__(16) char stg[SB::KR && !DRY ? 2 * NW * SR::BYTES : 16];
   auto stage_of = [&](int64_t c, int w) __attribute__((always_inline)) -> char* {
-    return stg + (int)((((c - c_begin) & 1) * NW + w) * SRR * SR::SB);
+    return stg + (int)((((c - c_begin) & 1) * NW + w) * SR::BYTES);
   };
   // a tile of 16 rows (rows 16 tt + 4 g + i, column vcol) as element type E
   auto put_rows = [&](auto tag, char* st, int row0, const floatx4 (&x)[4]) __attribute__((always_inline)) {
@@ -223,7 +223,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     static_assert(sizeof(E) == sizeof(T), "same row layout");
     if constexpr (!DRY) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) StageRows<E>::put(st, row0 + 16 * tt, ps, lane, x[tt]);
+      for (int tt = 0; tt < 4; ++tt) SR::template put<E>(st, row0 + 16 * tt, lane, x[tt]);
     }
   };
   // (movers) chunk cp's staged rows of compute wave `wave` to the state, R
@@ -295,7 +295,7 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
       // run (the puts are ordered after the K-row reads above)
       if constexpr (!DRY) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) SR::put(stc, 16 * kt, ps, lane, S[kt]);
+        for (int kt = 0; kt < NKT; ++kt) SR::template put<T>(stc, 16 * kt, lane, S[kt]);
       }
       floatx4 R[4];
 #pragma unroll

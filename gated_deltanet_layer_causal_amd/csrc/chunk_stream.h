@@ -284,6 +284,69 @@ template <typename T> struct StageRows {
   }
 };
 
+// The same staging for 16-bit types with the region column-major: a lane
+// puts its four rows of one column of an accumulator tile as one 8-byte LDS
+// write (no trade of halves between lanes), and the mover turns the columns
+// back into 16-byte row pieces with transposing reads (ds_read_b64_tr_b16
+// gives lane i of a 16-lane group four consecutive columns of row r0 + i,
+// lane j passing the address of column c0 + j / 4 at rows r0 + 4 (j % 4)
+// .. + 3).  A wave's region holds its 16 columns of NR rows, CS bytes per
+// column: NR 16-bit rows padded so that CS / 4 = 8 (mod 64), which spreads
+// the 64 lanes of a put over all banks, two dwords per bank.
+template <int NR> struct StageCols {
+  static constexpr int CS = NR * 2 + 4 * ((8 - NR / 2 % 64 + 64) % 64);   // bytes per column
+  static constexpr int BYTES = 16 * CS;                                    // per wave
+  static_assert(NR % 32 == 0 && CS / 4 % 64 == 8, "padded columns");
+  static constexpr int stores(int n) { return n / 32; }   // store instructions per lane for n rows
+  // one 16 x 16 accumulator tile (lane l: rows 4 (l / 16) + i of column
+  // l % 16) into rows row0.. of the region, as 16-bit E
+  template <typename E>
+  __device__ __forceinline__ static void put(char* region, int row0, int lane, floatx4 x) {
+    static_assert(sizeof(E) == 2, "16-bit staging");
+    const u32x2 w = {pack2<E>(x[0], x[1]), pack2<E>(x[2], x[3])};
+    const uint32_t a = lds_offset(region) + (uint32_t)((lane & 15) * CS + (row0 + 4 * (lane >> 4)) * 2);
+    asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(w) : "memory");
+  }
+  // rows [row0, row0 + n) of the region to rows 0.. of the buffer at byte
+  // offset col (the wave's columns), row stride ldb bytes, with cache policy
+  // AUX; rows outside the buffer's range are dropped.  A store covers 32
+  // rows: lane l takes row 16 ((l / 16) % 2) + l % 16 of them, columns
+  // 8 (l / 32) .. + 7.  The reads are inline asm that waits for its own
+  // results (a plain LDS read would wait for the direct copies in flight).
+  template <int AUX = 0>
+  __device__ __forceinline__ static void flush_async(const char* region, int row0, int n,
+                                                     __amdgpu_buffer_rsrc_t rs, uint32_t col,
+                                                     uint32_t ldb, int lane) {
+    const int i = lane & 15, q = lane >> 4, rr = 16 * (q & 1) + i, o = q >> 1;
+    const uint32_t a = lds_offset(region) + (uint32_t)((8 * o + i / 4) * CS + (row0 + 16 * (q & 1) + 4 * (i % 4)) * 2);
+    constexpr uint32_t STEP = 64, HALF = 4 * CS;   // bytes to the next 32 rows; to columns + 4
+    auto store = [&](const u32x2& lo, const u32x2& hi, int j) __attribute__((always_inline)) {
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, rs,
+                                             col + (uint32_t)(32 * j + rr) * ldb + (uint32_t)o * 16u, 0, AUX);
+    };
+#pragma unroll
+    for (int j = 0; j < n / 32; j += 2) {
+      u32x2 a0, a1, b0, b1;
+      if (j + 1 < n / 32) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %4 offset:%5\n\t"
+            "ds_read_b64_tr_b16 %2, %4 offset:%6\n\tds_read_b64_tr_b16 %3, %4 offset:%7\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+            : "v"(a + (uint32_t)j * STEP), "n"(HALF), "n"(STEP), "n"(STEP + HALF)
+            : "memory");
+        store(a0, a1, j);
+        store(b0, b1, j + 1);
+      } else {
+        asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(a0), "=&v"(a1)
+                     : "v"(a + (uint32_t)j * STEP), "n"(HALF)
+                     : "memory");
+        store(a0, a1, j);
+      }
+    }
+  }
+};
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (they complete in issue order) and all its LDS operations are done, then
 // meet the workgroup at a barrier.  Unlike __syncthreads() it leaves the
