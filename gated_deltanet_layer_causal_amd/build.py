@@ -36,6 +36,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-variable",
     "-Wno-unused-but-set-variable", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Rpass-analysis=kernel-resource-usage",
+    # MFMA results and accumulators in ordinary VGPRs: the sequential passes
+    # keep their state in accumulators and scale it every chunk, which with
+    # AGPRs costs a read and a write per element around each multiply
+    "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1",
 ]
 
 
