@@ -198,28 +198,27 @@ __global__ void __launch_bounds__(128 * NW) chunk_rev_kernel(
         buffer_of(dout + t0 * HvD + (int64_t)h * D + v0, (uint32_t)Lc * rowb),
         (__attribute__((address_space(3))) void*)sink, 4, (uint32_t)(2 * lane + wave) * rowb, 0, 0, 0);
   };
-  // (movers, 16-bit data) chunk cp's rows staged by compute wave `wave` to
-  // dS', dDelta and dv; token rows past the sequence end fall outside the
-  // buffers and are dropped; with valid false every store is issued into an
-  // empty range.  The reads are asm that waits for its own results (a plain
+  // (movers, 16-bit data) chunk cp's rows staged by the compute waves to
+  // dS', dDelta and dv, half of them per mover; token rows past the
+  // sequence end fall outside the buffers and are dropped; with valid false
+  // every store is issued into an empty range.  The reads are asm that waits for its own results (a plain
   // LDS read would wait for every direct copy in flight).
   constexpr int NFL = DRY || !MSTORE ? 0 : SC::stores(D) + 2 * SC::stores(CHUNK);
   static_assert(NTOUCH + NFL < 64, "vmcnt holds 6 bits");
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
     if constexpr (NFL == 0) return;
-    const char* st = stage_of(cp, wave);
+    const char* st = stage_of(cp, 0);   // both compute waves' rows: mover `wave` takes half of them
     const int64_t ca = valid ? cp : c_begin;
     const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
     const int64_t rem = seq_t1 - t0p;
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
-    SC::template flush_async<CACHE_NT>(st, 0, D,
-        buffer_of(dhst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), wcol, rowh,
-        lane);
-    SC::template flush_async<CACHE_NT>(st, D, CHUNK,
-        buffer_of(ddw + (ca * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK, (uint32_t)Lp * rowh), wcol, rowh, lane);
-    SC::template flush_async<CACHE_NT>(st, D + CHUNK, CHUNK,
-                    buffer_of(dvo + t0p * lddv + (int64_t)h * D + v0, (uint32_t)Lp * rowv), wcol, rowv,
-                    lane);
+    SC::template flush_pair_async<CACHE_NT>(st, 0, D,
+        buffer_of(dhst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), rowh, lane,
+        wave);
+    SC::template flush_pair_async<CACHE_NT>(st, D, CHUNK,
+        buffer_of(ddw + (ca * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK, (uint32_t)Lp * rowh), rowh, lane, wave);
+    SC::template flush_pair_async<CACHE_NT>(st, D + CHUNK, CHUNK,
+        buffer_of(dvo + t0p * lddv + (int64_t)h * D + v0, (uint32_t)Lp * rowv), rowv, lane, wave);
   };
 
   auto arow = [&](const T* base, int o, int tile_elems) __attribute__((always_inline)) -> frag {

@@ -226,27 +226,27 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
       for (int tt = 0; tt < 4; ++tt) SR::template put<E>(st, row0 + 16 * tt, lane, x[tt]);
     }
   };
-  // (movers) chunk cp's staged rows of compute wave `wave` to the state, R
-  // and Delta (compute type) buffers; token rows past the sequence
+  // (movers) chunk cp's staged rows to the state, R and Delta (compute
+  // type) buffers, half of them per mover; token rows past the sequence
   // end fall outside the buffers and are dropped.  With valid false every
   // store is still issued but dropped (an empty range), so each step issues
   // the same count.  The dry pass stages and stores nothing (NFL = 0).
   constexpr int NFL = DRY ? 0 : SR::stores(D) + 2 * SR::stores(CHUNK);
   auto flush_chunk = [&](int64_t cp, bool valid) __attribute__((always_inline)) {
     if constexpr (DRY) return;
-    const char* st = stage_of(cp, wave);
+    const char* st = stage_of(cp, 0);   // both compute waves' rows: mover `wave` takes half of them
     const int64_t ca = valid ? cp : c_begin;
     const int64_t t0p = seq_t0 + CHUNK * (ca - c_begin);
     const int64_t rem = seq_t1 - t0p;
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
-    const uint32_t col = (uint32_t)(16 * wave * sizeof(T));
     const int64_t blk = (ca * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK;
-    SR::template flush_async<CACHE_NT>(st, 0, D,
-        buffer_of(hst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), col, rowh,
-        lane);
-    SR::template flush_async<CACHE_NT>(st, SROW_R, CHUNK, buffer_of(Rw + blk, (uint32_t)Lp * rowh), col, rowh, lane);
-    SR::template flush_async<CACHE_NT>(st, SROW_D16, CHUNK, buffer_of(Dl16w + blk, (uint32_t)Lp * rowh), col, rowh,
-                                       lane);
+    SR::template flush_pair_async<CACHE_NT>(st, 0, D,
+        buffer_of(hst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), rowh, lane,
+        wave);
+    SR::template flush_pair_async<CACHE_NT>(st, SROW_R, CHUNK, buffer_of(Rw + blk, (uint32_t)Lp * rowh), rowh, lane,
+                                            wave);
+    SR::template flush_pair_async<CACHE_NT>(st, SROW_D16, CHUNK, buffer_of(Dl16w + blk, (uint32_t)Lp * rowh), rowh,
+                                            lane, wave);
   };
 
   // A operand of MFMA step p from row 16 * tile + c16 of a tile (offset o).

@@ -345,6 +345,45 @@ template <int NR> struct StageCols {
       }
     }
   }
+  // The rows of both compute waves' regions (wave 1's region BYTES after
+  // wave 0's at w0), as whole 2 x 16-column rows: mover m of the two takes
+  // rows [row0 + m n / 2, row0 + (m + 1) n / 2) to rows m n / 2.. of the
+  // buffer, 16 rows per store, lane l row l % 16 of them and columns
+  // 8 (l / 16) .. + 7 (wave (l / 16) / 2's columns), so that each store
+  // writes whole lines.
+  template <int AUX = 0>
+  __device__ __forceinline__ static void flush_pair_async(const char* w0, int row0, int n,
+                                                          __amdgpu_buffer_rsrc_t rs, uint32_t ldb,
+                                                          int lane, int m) {
+    const int i = lane & 15, p = lane >> 4, o = p & 1, h0 = m * (n / 2);
+    const uint32_t a = lds_offset(w0) + (uint32_t)((p >> 1) * BYTES + (8 * o + i / 4) * CS +
+                                                   (row0 + h0 + 4 * (i % 4)) * 2);
+    constexpr uint32_t STEP = 32, HALF = 4 * CS;   // bytes to the next 16 rows; to columns + 4
+    auto store = [&](const u32x2& lo, const u32x2& hi, int j) __attribute__((always_inline)) {
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, rs,
+                                             (uint32_t)(h0 + 16 * j + i) * ldb + (uint32_t)p * 16u, 0, AUX);
+    };
+#pragma unroll
+    for (int j = 0; j < n / 32; j += 2) {
+      u32x2 a0, a1, b0, b1;
+      if (j + 1 < n / 32) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %4 offset:%5\n\t"
+            "ds_read_b64_tr_b16 %2, %4 offset:%6\n\tds_read_b64_tr_b16 %3, %4 offset:%7\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+            : "v"(a + (uint32_t)j * STEP), "n"(HALF), "n"(STEP), "n"(STEP + HALF)
+            : "memory");
+        store(a0, a1, j);
+        store(b0, b1, j + 1);
+      } else {
+        asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(a0), "=&v"(a1)
+                     : "v"(a + (uint32_t)j * STEP), "n"(HALF)
+                     : "memory");
+        store(a0, a1, j);
+      }
+    }
+  }
 };
 
 // Wait until at most N vector-memory operations of this wave are outstanding
