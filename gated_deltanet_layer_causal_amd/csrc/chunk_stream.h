@@ -299,13 +299,17 @@ template <int NR> struct StageCols {
   static_assert(NR % 32 == 0 && CS / 4 % 64 == 8, "padded columns");
   static constexpr int stores(int n) { return n / 32; }   // store instructions per lane for n rows
   // one 16 x 16 accumulator tile (lane l: rows 4 (l / 16) + i of column
-  // l % 16) into rows row0.. of the region, as 16-bit E
+  // l % 16) into rows row0.. of the region, as 16-bit E.  A plain store:
+  // the waves that put issue no direct copies into LDS, so the compiler
+  // needs no wait before it, keeps its own counts of outstanding LDS
+  // operations exact (an asm write, which it cannot count, made it wait for
+  // more than it had to at every later operand read) and pairs puts into
+  // ds_write2_b64.
   template <typename E>
   __device__ __forceinline__ static void put(char* region, int row0, int lane, floatx4 x) {
     static_assert(sizeof(E) == 2, "16-bit staging");
     const u32x2 w = {pack2<E>(x[0], x[1]), pack2<E>(x[2], x[3])};
-    const uint32_t a = lds_offset(region) + (uint32_t)((lane & 15) * CS + (row0 + 4 * (lane >> 4)) * 2);
-    asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(w) : "memory");
+    *reinterpret_cast<u32x2*>(region + (lane & 15) * CS + (row0 + 4 * (lane >> 4)) * 2) = w;
   }
   // rows [row0, row0 + n) of the region to rows 0.. of the buffer at byte
   // offset col (the wave's columns), row stride ldb bytes, with cache policy
