@@ -240,12 +240,12 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     const int64_t rem = seq_t1 - t0p;
     const int Lp = valid ? (rem < CHUNK ? (int)rem : CHUNK) : 0;
     const int64_t blk = (ca * Hv + h) * CHUNK * D + (int64_t)v0 * CHUNK;
-    SR::template flush_pair_async<CACHE_NT>(st, 0, D,
+    SR::template flush_pair_async<CACHE_NT | CACHE_SC1>(st, 0, D,
         buffer_of(hst + (ca * Hv + h) * D * D + (int64_t)v0 * D, valid ? D * SBV * sizeof(T) : 0u), rowh, lane,
         wave);
-    SR::template flush_pair_async<CACHE_NT>(st, SROW_R, CHUNK, buffer_of(Rw + blk, (uint32_t)Lp * rowh), rowh, lane,
+    SR::template flush_pair_async<CACHE_NT | CACHE_SC1>(st, SROW_R, CHUNK, buffer_of(Rw + blk, (uint32_t)Lp * rowh), rowh, lane,
                                             wave);
-    SR::template flush_pair_async<CACHE_NT>(st, SROW_D16, CHUNK, buffer_of(Dl16w + blk, (uint32_t)Lp * rowh), rowh,
+    SR::template flush_pair_async<CACHE_NT | CACHE_SC1>(st, SROW_D16, CHUNK, buffer_of(Dl16w + blk, (uint32_t)Lp * rowh), rowh,
                                             lane, wave);
   };
 

@@ -98,8 +98,11 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // per-lane offset (loads past it read zero, stores past it are dropped).
 // Cache policy of a buffer access (the instruction's aux bits on gfx950):
 // non-temporal, for data streamed past the caches that no later access of
-// the same kernel reads (rows stored for another kernel).
-constexpr int CACHE_NT = 2;
+// the same kernel reads (rows stored for another kernel); and the sc1 scope
+// bit, which with it writes through to memory (chosen per pass by
+// measurement: the state pass's stores run faster with it, the reverse
+// pass's slower).
+constexpr int CACHE_NT = 2, CACHE_SC1 = 16;
 template <int AUX = 0>
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
                                             uint32_t soff) {
