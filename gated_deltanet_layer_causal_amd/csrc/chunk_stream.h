@@ -294,12 +294,16 @@ template <typename T> struct StageRows {
 // gives lane i of a 16-lane group four consecutive columns of row r0 + i,
 // lane j passing the address of column c0 + j / 4 at rows r0 + 4 (j % 4)
 // .. + 3).  A wave's region holds its 16 columns of NR rows, CS bytes per
-// column: NR 16-bit rows padded so that CS / 4 = 8 (mod 64), which spreads
-// the 64 lanes of a put over all banks, two dwords per bank.
+// column: NR 16-bit rows padded to CS / 4 = 10 (mod 64) dwords.  The LDS
+// bank-conflict counter of a one-wave probe, per 64-lane instruction, for
+// the puts (16 columns CS apart, four 8-byte pieces per column) and the
+// movers' transposing reads, by CS / 4 mod 64: 2: 0 and 6 cycles; 4: 4 and
+// 2; 6: 0 and 4; 8: 12 and 2; 10: 0 and 2; 12: 4 and 2 (the same at every
+// base offset tried).
 template <int NR> struct StageCols {
-  static constexpr int CS = NR * 2 + 4 * ((8 - NR / 2 % 64 + 64) % 64);   // bytes per column
-  static constexpr int BYTES = 16 * CS;                                    // per wave
-  static_assert(NR % 32 == 0 && CS / 4 % 64 == 8, "padded columns");
+  static constexpr int CS = NR * 2 + 4 * ((10 - NR / 2 % 64 + 64) % 64);   // bytes per column
+  static constexpr int BYTES = 16 * CS;                                     // per wave
+  static_assert(NR % 32 == 0 && CS / 4 % 64 == 10, "padded columns");
   static constexpr int stores(int n) { return n / 32; }   // store instructions per lane for n rows
   // one 16 x 16 accumulator tile (lane l: rows 4 (l / 16) + i of column
   // l % 16) into rows row0.. of the region, as 16-bit E.  A plain store:
