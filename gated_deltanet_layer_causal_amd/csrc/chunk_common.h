@@ -484,6 +484,50 @@ __device__ __forceinline__ float wave_incl_scan_f(float x, int lane) {
   return x;
 }
 
+// The same sums without LDS: DPP shifts within rows of 16 lanes (lanes
+// without a source read zero), then the other rows' totals, read from one
+// lane of each row.  Inclusive prefix sum:
+__device__ __forceinline__ float wave_prefix_dpp(float x, int lane) {
+  x += dpp_f<0x111>(x);   // row_shr:1
+  x += dpp_f<0x112>(x);   // row_shr:2
+  x += dpp_f<0x114>(x);   // row_shr:4
+  x += dpp_f<0x118>(x);   // row_shr:8
+  const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+  const int row = lane >> 4;
+  float e = 0.f;   // the earlier rows' totals
+  if (row >= 1) e = t0;
+  if (row >= 2) e += t1;
+  if (row >= 3) e += t2;
+  return x + e;
+}
+// ... and inclusive suffix sum.
+__device__ __forceinline__ float wave_suffix_dpp(float x, int lane) {
+  x += dpp_f<0x101>(x);   // row_shl:1
+  x += dpp_f<0x102>(x);   // row_shl:2
+  x += dpp_f<0x104>(x);   // row_shl:4
+  x += dpp_f<0x108>(x);   // row_shl:8
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float t3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  const int row = lane >> 4;
+  float e = 0.f;   // the later rows' totals
+  if (row <= 2) e = t3;
+  if (row <= 1) e += t2;
+  if (row <= 0) e += t1;
+  return x + e;
+}
+// ... and the sum over the wave, in every lane.
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x = lane_group_sum<16>(x);
+  const int v = __builtin_bit_cast(int, x);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 48)));
+}
+
 // Inclusive suffix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_suffix_scan(float x, int lane) {
 #pragma unroll

@@ -668,7 +668,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           sm.rowZ[kt][t] = rz;
         }
       }
-      ipv = wave_sum(ipv);
+      ipv = wave_sum_dpp(ipv);
       if (lane == 0) sm.red[wave] = ipv;
     }
     lds_barrier();   // the token tiles are free; every partial is in
@@ -755,7 +755,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       for (int w = 0; w < 8; ++w) ips += sm.red[w];
       if (t == cur.L - 1) y += dexp<T>(sm.gam[CHUNK - 1]) * ips;
       if (t >= cur.L) { y = 0.f; zt = 0.f; }
-      const float dgs = box + wave_suffix_scan(y, lane) + (wave_incl_scan_f(zt, lane) - zt);
+      const float dgs = box + wave_suffix_dpp(y, lane) + (wave_prefix_dpp(zt, lane) - zt);
       if (t < cur.L) {
         dg[(cur.t0 + t) * Hv + h] = dgs;
         dbeta[(cur.t0 + t) * Hv + h] = db;
