@@ -475,14 +475,6 @@ __device__ __forceinline__ double wave_incl_scan(double x, int lane) {
   return x;
 }
 
-__device__ __forceinline__ float wave_incl_scan_f(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
 
 // The same sums without LDS: DPP shifts within rows of 16 lanes (lanes
 // without a source read zero), then the other rows' totals, read from one
@@ -526,16 +518,6 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 16))) +
          (__builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 32)) +
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 48)));
-}
-
-// Inclusive suffix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_suffix_scan(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float y = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += y;
-  }
-  return x;
 }
 
 }  // namespace gdn

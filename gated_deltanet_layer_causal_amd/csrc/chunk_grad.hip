@@ -97,12 +97,6 @@ template <typename E> __device__ __forceinline__ floatx4 ld4(const E* p) {
   }
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
 template <typename T, int D>
 __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int64_t ldq, int64_t ldk,

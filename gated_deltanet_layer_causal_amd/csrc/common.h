@@ -239,14 +239,4 @@ __device__ __forceinline__ floatx4 tile_mma(floatx4 acc, const SA* A, int lda, c
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
-// Row sum of an MFMA output tile: the 16 lanes with equal l>>4 hold the same
-// 4 rows (columns l%16); reduce a per-lane value over those 16 lanes.
-__device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
-  return x;
-}
-
 }  // namespace gdn
