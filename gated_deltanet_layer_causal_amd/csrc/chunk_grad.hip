@@ -75,8 +75,10 @@ template <typename T, int D> struct GradLds {
   T Tin[TIN_LDS ? CHUNK * CHUNK : 8];
   double gam[CHUNK];
   float bet[CHUNK], Gm[CHUNK], dc[CHUNK];
-  float colB[4][CHUNK], rowB[2][CHUNK], rowX[NKT][CHUNK], rowZ[NKT][CHUNK];
-  float boxE[4][CHUNK], red[8];
+  // the per-head partials of dg and dbeta, two sets by head parity (a head's
+  // are summed and scanned while the next head runs)
+  float colB[2][4][CHUNK], rowB[2][2][CHUNK], rowX[2][NKT][CHUNK], rowZ[2][NKT][CHUNK];
+  float boxE[2][4][CHUNK], red[2][8];
   // k_t . k_s, the preparation's K K^T in the compute type (fp16 for 16-bit
   // data: |k_t . k_s| <= 1 for the L2-normalised keys) and in its layout of
   // 16 x 16 blocks (element (t, s) at 256 (4 (t / 16) + s / 16) +
@@ -437,6 +439,34 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
   // LDS-only (a full barrier would wait for the copies); the one at the top
   // of a head waits for all.  After the last head the same requests go out
   // with empty ranges (gates: the last head's again).
+  // dg and dbeta of a head from its partials (set p): the box sums, the
+  // suffix sum of the chunk-start terms and the exclusive prefix sum of the
+  // chunk-end terms, one token per lane
+  struct Prev { int64_t t0; int L, h; double glast; };
+  Prev prev{0, 0, 0, 0.0};
+  constexpr int TAIL_WAVE = 4;
+  auto dg_tail = [&](int p, const Prev& pv) __attribute__((always_inline)) {
+    const int t = lane;
+    float y = 0.f, db = sm.rowB[p][0][t] + sm.rowB[p][1][t], zt = 0.f, ips = 0.f;
+    const float box = ((sm.boxE[p][0][t] + sm.boxE[p][1][t]) + sm.boxE[p][2][t]) + sm.boxE[p][3][t];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) db += sm.colB[p][w][t];
+#pragma unroll
+    for (int w = 0; w < NKT; ++w) {
+      y += sm.rowX[p][w][t];
+      zt += sm.rowZ[p][w][t];
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) ips += sm.red[p][w];
+    if (t == pv.L - 1) y += dexp<T>(pv.glast) * ips;
+    if (t >= pv.L) { y = 0.f; zt = 0.f; }
+    const float dgs = box + wave_suffix_dpp(y, lane) + (wave_prefix_dpp(zt, lane) - zt);
+    if (t < pv.L) {
+      dg[(pv.t0 + t) * Hv + pv.h] = dgs;
+      dbeta[(pv.t0 + t) * Hv + pv.h] = db;
+    }
+  };
+
   const int n_steps = n_items * G;
   for (int step = 0, hh = 0; step < n_steps; ++step) {
     const int h = kh * G + hh;
@@ -463,8 +493,13 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       lds_barrier();
     }
     // =============== phase A: pair products (s x t tiles, t = tl)
+    const int par = step & 1;                 // this head's set of dg partials
     const double gt = sm.gam[tl];
+    const double gl_head = sm.gam[CHUNK - 1];
     const float bt = sm.bet[tl];
+    // the previous head's dg and dbeta, on a dP-side wave (that side has
+    // slack in phase A; the Tinv chain does not)
+    if (wave == TAIL_WAVE && step > 0) dg_tail(par ^ 1, prev);
     floatx4 ep[4];
     if (role == 0) {
       // dM^T = R dDelta^T
@@ -492,7 +527,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
           dMt[st][i] = s < tl ? dMt[st][i] * bsv[i] : 0.f;
         }
       }
-      sm.colB[tw][16 * (c16 >> 2) + g4 + (c16 & 3)] = cbm;
+      sm.colB[par][tw][16 * (c16 >> 2) + g4 + (c16 & 3)] = cbm;
       // Y = dTinv Tinv^T for tokens t of this wave (A from the accumulators),
       // into Y^T rows
 #pragma unroll
@@ -597,7 +632,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       }
       rb += __shfl_xor(rb, 16, 64);
       rb += __shfl_xor(rb, 32, 64);
-      if (g == 0) sm.rowB[role][tl] = rb;
+      if (g == 0) sm.rowB[par][role][tl] = rb;
     }
     __syncthreads();   // WS and the dA part of the pair terms are in
     if (role == 1) {   // (E is read after phase B's barrier)
@@ -658,12 +693,12 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         rz += __shfl_xor(rz, 16, 64);
         rz += __shfl_xor(rz, 32, 64);
         if (g == 0) {
-          sm.rowX[kt][t] = rx;
-          sm.rowZ[kt][t] = rz;
+          sm.rowX[par][kt][t] = rx;
+          sm.rowZ[par][kt][t] = rz;
         }
       }
       ipv = wave_sum_dpp(ipv);
-      if (lane == 0) sm.red[wave] = ipv;
+      if (lane == 0) sm.red[par][wave] = ipv;
     }
     lds_barrier();   // the token tiles are free; every partial is in
     if (last) {
@@ -731,36 +766,19 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       split(std::integral_constant<int, 0x141>{}, 4, (j & 4) != 0);   // row_half_mirror: bit 2
       split(std::integral_constant<int, 0x4E>{}, 2, (j & 2) != 0);    // lane ^ 2
       split(std::integral_constant<int, 0xB1>{}, 1, (j & 1) != 0);    // lane ^ 1
-      sm.boxE[wave][16 * q + j] = x[0];
+      sm.boxE[par][wave][16 * q + j] = x[0];
     }
     lds_barrier();
-    if (wave == 0) {
-      const int t = lane;
-      float y = 0.f, db = sm.rowB[0][t] + sm.rowB[1][t], zt = 0.f, ips = 0.f;
-      const float box = ((sm.boxE[0][t] + sm.boxE[1][t]) + sm.boxE[2][t]) + sm.boxE[3][t];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) db += sm.colB[w][t];
-#pragma unroll
-      for (int w = 0; w < NKT; ++w) {
-        y += sm.rowX[w][t];
-        zt += sm.rowZ[w][t];
-      }
-#pragma unroll
-      for (int w = 0; w < 8; ++w) ips += sm.red[w];
-      if (t == cur.L - 1) y += dexp<T>(sm.gam[CHUNK - 1]) * ips;
-      if (t >= cur.L) { y = 0.f; zt = 0.f; }
-      const float dgs = box + wave_suffix_dpp(y, lane) + (wave_prefix_dpp(zt, lane) - zt);
-      if (t < cur.L) {
-        dg[(cur.t0 + t) * Hv + h] = dgs;
-        dbeta[(cur.t0 + t) * Hv + h] = db;
-      }
-    }
     // (since phase B's barrier only wave 0 reads the gates, and it alone
     // writes the next head's)
     put_gates();
+    prev = Prev{cur.t0, cur.L, h, gl_head};
     if (last) cur = nx;
     hh = last ? 0 : hh + 1;
   }
+  // the last head's dg and dbeta (its partials are in since the loop's last
+  // barrier)
+  if (wave == TAIL_WAVE && n_steps > 0) dg_tail((n_steps - 1) & 1, prev);
 }
 
 // ---------------------------------------------------------------------------
