@@ -66,6 +66,12 @@ template <typename T, int D> struct GradLds {
   T dPD[CHUNK][LDP];              // dP o D: row t, columns s in accumulator order
   T dPDt[CHUNK][LDP];             // scale (dP o D)^T: row s, columns t in accumulator order
   T WS[CHUNK][LDP];               // WA + WA^T: row x, columns u in accumulator order
+  // (after phase B of an item's last head, YT .. WS hold its dq and dk rows,
+  // QKR elements apart: 16 bytes of padding keep the rows 16-byte aligned
+  // and spread a wave's puts of 16 rows x 4 consecutive pieces over the
+  // banks)
+  static constexpr int QKR = D + 16 / (int)sizeof(T);
+  static_assert(2 * QKR <= 4 * LDP, "dq and dk rows fit in the pair tiles");
   float E[CHUNK][CHUNK + 1];      // pair terms of dg
   // Tinv (columns in accumulator order), copied for 16-bit types, whose
   // Tinv^T operands are transposing reads of it (fp32 reads Tinv and Tinv^T
@@ -702,20 +708,40 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     }
     lds_barrier();   // the token tiles are free; every partial is in
     if (last) {
-      // dq = scale dQ, dk of the item (four consecutive key columns of one
-      // token per lane), then the next item's registers
-      const uint32_t rq = (uint32_t)(lddq * sizeof(T)), rk = (uint32_t)(lddk * sizeof(T));
-      const auto bq = buffer_of(dq + cur.t0 * lddq + (int64_t)kh * D, (uint32_t)cur.L * rq);
-      const auto bk = buffer_of(dk + cur.t0 * lddk + (int64_t)kh * D, (uint32_t)cur.L * rk);
+      // dq = scale dQ, dk of the item: each wave puts its four consecutive
+      // key columns of a token per lane into rows of the pair tiles (free
+      // until the next head's phase A), and after a barrier the rows leave
+      // whole, 16 bytes per lane; then the next item's registers.  (Stores
+      // straight from the accumulators wrote 32 bytes of each row per wave.)
+      T* const stq = &sm.YT[0][0];
+      T* const stk = stq + CHUNK * GL::QKR;
 #pragma unroll
       for (int tt = 0; tt < TTW; ++tt) {
         const int t = 16 * (tg * TTW + tt) + c16, kc = 16 * kt + g4;
-        floatx4 xq = dQa[tt];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xq[i] *= scale;
-        buffer_store4<T>(bq, (uint32_t)t * rq + (uint32_t)kc * sizeof(T), xq);
-        buffer_store4<T>(bk, (uint32_t)t * rk + (uint32_t)kc * sizeof(T), dKa[tt]);
+        const floatx4 xq = dQa[tt], xk = dKa[tt];
+        store4(stq + t * GL::QKR + kc, scale * xq[0], scale * xq[1], scale * xq[2], scale * xq[3]);
+        store4(stk + t * GL::QKR + kc, xk[0], xk[1], xk[2], xk[3]);
         dQa[tt] = dKa[tt] = zero4();
+      }
+      lds_barrier();
+      const uint32_t rq = (uint32_t)(lddq * sizeof(T)), rk = (uint32_t)(lddk * sizeof(T));
+      const auto bq = buffer_of(dq + cur.t0 * lddq + (int64_t)kh * D, (uint32_t)cur.L * rq);
+      const auto bk = buffer_of(dk + cur.t0 * lddk + (int64_t)kh * D, (uint32_t)cur.L * rk);
+      constexpr int PPRW = D * (int)sizeof(T) / 16;   // 16-byte pieces per row
+      constexpr int NP = CHUNK * PPRW;                 // pieces per tile
+#pragma unroll
+      for (int j = 0; j < (NP + 511) / 512; ++j) {
+        const int i = tid + 512 * j, r = i / PPRW, pc = i % PPRW;
+        if (NP % 512 != 0 && i >= NP) break;
+        // (inline asm reads, each waiting for itself: a plain LDS read here
+        // would wait for the direct copies still in flight)
+        u32x4 vq, vk;
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(vq), "=&v"(vk)
+                     : "v"(lds_offset(stq + r * GL::QKR) + 16u * pc), "v"(lds_offset(stk + r * GL::QKR) + 16u * pc)
+                     : "memory");
+        __builtin_amdgcn_raw_buffer_store_b128(vq, bq, (uint32_t)r * rq + 16u * pc, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vk, bk, (uint32_t)r * rk + 16u * pc, 0, 0);
       }
       if (live) load_item(nx);
     }
