@@ -42,6 +42,16 @@ __device__ __forceinline__ float group_sum(float x) {
   return lane_group_sum<D / 8>(x);
 }
 
+// Which lanes of this block's channel group (512 channels) normalise: 1 all,
+// 0 none, 2 some (the group that straddles the end of the q and k channels).
+// Uniform over the block, so each conv kernel runs one of three bodies and the
+// v channels (most of them) skip the L2 work instead of computing and
+// discarding it.
+__device__ __forceinline__ int l2_mode(int C, int n_l2) {
+  const int lo = blockIdx.y * 512, hi = lo + 512 < C ? lo + 512 : C;
+  return hi <= n_l2 ? 1 : lo >= n_l2 ? 0 : 2;
+}
+
 // Eight consecutive elements of row r (relative to the buffer's first row)
 // at this lane's channel offset coff (bytes), as stored; zero outside the
 // buffer.
@@ -87,13 +97,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_of(const T* base, int64_t
 // HAS_STATE: cs_in [n_seq][3][C] holds the three input rows before each
 // sequence (the carried conv state), read where a window reaches before the
 // sequence start instead of the zero padding.
-template <typename T, int D, bool HAS_STATE>
-__global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_fwd_kernel(const T* __restrict__ x, int64_t ldx,
-                                                       const float* __restrict__ w,
-                                                       const int32_t* __restrict__ cu, int n_seq,
-                                                       int64_t T_tok, int tt, int C, int n_l2, float eps,
-                                                       T* __restrict__ y, int64_t ldy,
-                                                       const T* __restrict__ cs_in) {
+// L2M: the block's l2_mode.
+template <typename T, int D, bool HAS_STATE, int L2M>
+__device__ __forceinline__ void conv_fwd_run(const T* __restrict__ x, int64_t ldx,
+                                             const float* __restrict__ w,
+                                             const int32_t* __restrict__ cu, int n_seq,
+                                             int64_t T_tok, int tt, int C, int n_l2, float eps,
+                                             T* __restrict__ y, int64_t ldy,
+                                             const T* __restrict__ cs_in) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   const bool active = c0 < C;
@@ -148,13 +159,15 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_fwd_kernel(cons
         for (int i = 0; i < 8; ++i) {
           float u = wr[i][0] * x3.v[i] + wr[i][1] * x2.v[i] + wr[i][2] * x1.v[i] + wr[i][3] * x0.v[i];
           av.v[i] = u * sigmoidf_(u);
-          sq += av.v[i] * av.v[i];
+          if constexpr (L2M != 0) sq += av.v[i] * av.v[i];
         }
-        sq = group_sum<D>(sq);
-        if (l2) {
-          const float r = rsqrtf(sq + eps);
+        if constexpr (L2M != 0) {
+          sq = group_sum<D>(sq);
+          if (L2M == 1 || l2) {
+            const float r = rsqrtf(sq + eps);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) av.v[i] *= r;
+            for (int i = 0; i < 8; ++i) av.v[i] *= r;
+          }
         }
         put_row8<T>(ry, t - a, ldyb, coff, av);
       };
@@ -174,32 +187,60 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_fwd_kernel(cons
   }
 }
 
-// du for one token from its window x0..x3 (x[t], x[t-1], x[t-2], x[t-3]) and dy.
-template <int D>
+template <typename T, int D, bool HAS_STATE>
+__global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_fwd_kernel(const T* __restrict__ x, int64_t ldx,
+                                                       const float* __restrict__ w,
+                                                       const int32_t* __restrict__ cu, int n_seq,
+                                                       int64_t T_tok, int tt, int C, int n_l2, float eps,
+                                                       T* __restrict__ y, int64_t ldy,
+                                                       const T* __restrict__ cs_in) {
+  const int mode = l2_mode(C, n_l2);
+  if (mode == 1)
+    conv_fwd_run<T, D, HAS_STATE, 1>(x, ldx, w, cu, n_seq, T_tok, tt, C, n_l2, eps, y, ldy, cs_in);
+  else if (mode == 0)
+    conv_fwd_run<T, D, HAS_STATE, 0>(x, ldx, w, cu, n_seq, T_tok, tt, C, n_l2, eps, y, ldy, cs_in);
+  else
+    conv_fwd_run<T, D, HAS_STATE, 2>(x, ldx, w, cu, n_seq, T_tok, tt, C, n_l2, eps, y, ldy, cs_in);
+}
+
+// du for one token from its window x0..x3 (x[t], x[t-1], x[t-2], x[t-3]) and
+// dy.  With a = SiLU(u), s = sigmoid(u) and, on normalising lanes, y = a r
+// with r = (|a|^2 + eps)^(-1/2) over the head:
+//   da = r dy - a r^3 (a . dy),   du = da SiLU'(u),   SiLU'(u) = s + a (1 - s).
+// L2M as l2_mode; with L2M = 2 the lanes that do not normalise take r = 1
+// and r^3 (a . dy) = 0, so one formula serves every lane.
+template <int D, int L2M>
 __device__ __forceinline__ f8 conv_du(const float (&wr)[8][4], const f8& x0, const f8& x1,
                                       const f8& x2, const f8& x3, const f8& dy, bool l2,
                                       float eps) {
-  float u[8], a[8], sg[8];
-  float sq = 0.f;
+  float a[8], sg[8];
+  float sq = 0.f, sd = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    u[i] = wr[i][0] * x3.v[i] + wr[i][1] * x2.v[i] + wr[i][2] * x1.v[i] + wr[i][3] * x0.v[i];
-    sg[i] = sigmoidf_(u[i]);
-    a[i] = u[i] * sg[i];
-    sq += a[i] * a[i];
+    const float u = wr[i][0] * x3.v[i] + wr[i][1] * x2.v[i] + wr[i][2] * x1.v[i] + wr[i][3] * x0.v[i];
+    sg[i] = sigmoidf_(u);
+    a[i] = u * sg[i];
+    if constexpr (L2M != 0) {
+      sq += a[i] * a[i];
+      sd += a[i] * dy.v[i];
+    }
   }
-  sq = group_sum<D>(sq);
-  float r = rsqrtf(sq + eps);
-  float yd = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) yd += a[i] * r * dy.v[i];
-  yd = group_sum<D>(yd);
+  float r = 1.f, c = 0.f;
+  if constexpr (L2M != 0) {
+    sq = group_sum<D>(sq);
+    sd = group_sum<D>(sd);
+    r = rsqrtf(sq + eps);
+    c = r * r * r * sd;
+    if constexpr (L2M == 2) {
+      r = l2 ? r : 1.f;
+      c = l2 ? c : 0.f;
+    }
+  }
   f8 du;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // L2: y = a r  ->  da = r (dy - y (y . dy));  SiLU': s (1 + u (1 - s))
-    float da = l2 ? r * (dy.v[i] - a[i] * r * yd) : dy.v[i];
-    du.v[i] = da * sg[i] * (1.f + u[i] * (1.f - sg[i]));
+    const float da = L2M != 0 ? fmaf(-a[i], c, r * dy.v[i]) : dy.v[i];
+    du.v[i] = da * fmaf(a[i], 1.f - sg[i], sg[i]);
   }
   return du;
 }
@@ -209,13 +250,14 @@ __device__ __forceinline__ f8 conv_du(const float (&wr)[8][4], const f8& x0, con
 // gradient of the final state (the last three input rows of each sequence),
 // adds to dx of those rows.  The gradient of cs_in itself comes from
 // conv_state_dgrad_kernel.
-template <typename T, int D, bool HAS_STATE>
-__global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
+typedef float ConvRed[CONV_RUNS_PER_BLOCK][64][33];
+template <typename T, int D, bool HAS_STATE, int L2M>
+__device__ __forceinline__ void conv_bwd_run(
     const T* __restrict__ x, int64_t ldx, const float* __restrict__ w,
     const int32_t* __restrict__ cu, int n_seq, int64_t T_tok, int tt, int C, int n_l2, float eps,
     const T* __restrict__ dy, int64_t lddy, T* __restrict__ dx, int64_t lddx,
-    float* __restrict__ partials, const T* __restrict__ cs_in, const T* __restrict__ dcs_out) {
-  __shared__ float red[CONV_RUNS_PER_BLOCK][64][33];
+    float* __restrict__ partials, const T* __restrict__ cs_in, const T* __restrict__ dcs_out,
+    ConvRed& red) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   const bool active = c0 < C;
@@ -267,7 +309,7 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
         for (int j = 0; j < 3; ++j) {
           const int64_t t = b + j;
           if (t < se) {   // wave-uniform
-            ds[3 - j] = conv_du<D>(wr, xr(t), xr(t - 1), xr(t - 2), xr(t - 3),
+            ds[3 - j] = conv_du<D, L2M>(wr, xr(t), xr(t - 1), xr(t - 2), xr(t - 3),
                                    row8<T>(ry, t - a, ldyb, coff), l2, eps);
           } else {
 #pragma unroll
@@ -288,7 +330,7 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
           const f8 &x0 = xs[m], &x1 = xs[(m + 1) & 3], &x2 = xs[(m + 2) & 3], &x3 = xs[(m + 3) & 3];
           const f8 dyv = raw_f8(pd[m]);
           pd[m] = raw_row8<T>(ry, s - 4 - a, ldyb, coff);
-          const f8 d0 = conv_du<D>(wr, x0, x1, x2, x3, dyv, l2, eps);
+          const f8 d0 = conv_du<D, L2M>(wr, x0, x1, x2, x3, dyv, l2, eps);
           const f8 &d1 = ds[(m + 3) & 3], &d2 = ds[(m + 2) & 3], &d3 = ds[(m + 1) & 3];
           f8 o;
 #pragma unroll
@@ -346,6 +388,25 @@ __global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
   }
 }
 
+template <typename T, int D, bool HAS_STATE>
+__global__ void __launch_bounds__(64 * CONV_RUNS_PER_BLOCK) conv_bwd_kernel(
+    const T* __restrict__ x, int64_t ldx, const float* __restrict__ w,
+    const int32_t* __restrict__ cu, int n_seq, int64_t T_tok, int tt, int C, int n_l2, float eps,
+    const T* __restrict__ dy, int64_t lddy, T* __restrict__ dx, int64_t lddx,
+    float* __restrict__ partials, const T* __restrict__ cs_in, const T* __restrict__ dcs_out) {
+  __shared__ ConvRed red;
+  const int mode = l2_mode(C, n_l2);
+  if (mode == 1)
+    conv_bwd_run<T, D, HAS_STATE, 1>(x, ldx, w, cu, n_seq, T_tok, tt, C, n_l2, eps, dy, lddy, dx,
+                                     lddx, partials, cs_in, dcs_out, red);
+  else if (mode == 0)
+    conv_bwd_run<T, D, HAS_STATE, 0>(x, ldx, w, cu, n_seq, T_tok, tt, C, n_l2, eps, dy, lddy, dx,
+                                     lddx, partials, cs_in, dcs_out, red);
+  else
+    conv_bwd_run<T, D, HAS_STATE, 2>(x, ldx, w, cu, n_seq, T_tok, tt, C, n_l2, eps, dy, lddy, dx,
+                                     lddx, partials, cs_in, dcs_out, red);
+}
+
 // The final conv state: cs_out[n][r] = the input row at position
 // cu[n + 1] - 3 + r, from x, or from cs_in (zeros when null) where that
 // position precedes the sequence start.  One wave per (sequence, row, 512
@@ -401,7 +462,7 @@ __global__ void __launch_bounds__(64) conv_state_dgrad_kernel(
   for (int k = 0; k < 3; ++k) {
     const int64_t t = ss + k;
     if (k < L) {   // wave-uniform
-      du[k] = conv_du<D>(wr, xrow(t), xrow(t - 1), xrow(t - 2), xrow(t - 3), row8<T>(ry, t - ss, ldyb, coff),
+      du[k] = conv_du<D, 2>(wr, xrow(t), xrow(t - 1), xrow(t - 2), xrow(t - 3), row8<T>(ry, t - ss, ldyb, coff),
                          l2, eps);
     } else {
 #pragma unroll
