@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     // wave writes whole 512-byte blocks.
     typename Compute<T>::type* ko = KKw + ((int64_t)c * (Hv / G) + kh) * CHUNK * CHUNK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store4(ko + (4 * j + wave) * 256 + 4 * lane, kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
+    for (int j = 0; j < 4; ++j) store4_nt(ko + (4 * j + wave) * 256 + 4 * lane, kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
   }
   {
     // Q rows (compute type, zero past the chunk end, columns in accumulator
@@ -214,14 +214,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         f8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j) v.v[j] = to_f(su.Q[r][acc_piece_col<CT>(p, j)]);
-        store8(Q16w + base + dst, v);
+        store8_nt(Q16w + base + dst, v);
       }
       if constexpr (BWD) {
         f8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j) v.v[j] = to_f(sK[r][acc_piece_col<CT>(p, j)]);
-        store8(Kb + base + dst, v);
-        if constexpr (KROWS) store8(K16w + base + dst, v);
+        store8_nt(Kb + base + dst, v);
+        if constexpr (KROWS) store8_nt(K16w + base + dst, v);
       }
     }
     if constexpr (BWD) {
@@ -232,13 +232,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         f8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j) v.v[j] = to_f(su.Q[acc_piece_col<T>(p, j)][kr]);
-        store8(qo + kr * CHUNK + 8 * p, v);
+        store8_nt(qo + kr * CHUNK + 8 * p, v);
         // K^T likewise, gathered from the K rows (no LDS transpose: A and
         // Ti take this storage in the head loop, after its first barrier)
         if constexpr (KROWS) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) v.v[j] = to_f(sK[acc_piece_col<T>(p, j)][kr]);
-          store8(Ktb + base + kr * CHUNK + 8 * p, v);
+          store8_nt(Ktb + base + kr * CHUNK + 8 * p, v);
         }
       }
     }
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
       *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
           *reinterpret_cast<const v4*>(&su.Kt[kr][c4]);
       if constexpr (BWD) {
-        store4(Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4),
+        store4_nt(Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4),
                to_f(su.Kt[kr][c4]), to_f(su.Kt[kr][c4 + 1]), to_f(su.Kt[kr][c4 + 2]),
                to_f(su.Kt[kr][c4 + 3]));
       }
@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         if constexpr (SM::STAGE_P)
           store4(&Pts[s][acc_col<T>(rbase)], pv[0], pv[1], pv[2], pv[3]);
         else
-          store4(PTout + s * CHUNK + acc_col<T>(rbase), pv[0], pv[1], pv[2], pv[3]);
+          store4_nt(PTout + s * CHUNK + acc_col<T>(rbase), pv[0], pv[1], pv[2], pv[3]);
       }
       const int t = 16 * j + ccol;   // (= s: gam[t] is gsj)
 #pragma unroll
@@ -344,7 +344,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
       if constexpr (SM::STAGE_P)
         store4(&Ps[t][acc_col<CT>(rbase)], pv[0], pv[1], pv[2], pv[3]);
       else
-        store4(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
+        store4_nt(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();
     if constexpr (SM::STAGE_P) {
@@ -367,7 +367,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         const int s = acc_piece_col<CT>(p, j);
         v.v[j] = sTi[t][s] * sm.bet[s];
       }
-      store8(Mout + t * CHUNK + 8 * p, v);
+      store8_nt(Mout + t * CHUNK + 8 * p, v);
     }
     if constexpr (BWD) {
       // Tinv in the storage type for the chunk gradients and the reverse pass
@@ -379,11 +379,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         f8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j) v.v[j] = sTi[r][acc_piece_col<T>(p, j)];
-        store8(to + r * CHUNK + 8 * p, v);
+        store8_nt(to + r * CHUNK + 8 * p, v);
         if constexpr (sizeof(T) == 4) {   // (16-bit readers transpose Tinv in LDS)
 #pragma unroll
           for (int j = 0; j < 8; ++j) v.v[j] = sTi[8 * p + j][r];
-          store8(to + CHUNK * CHUNK + r * CHUNK + 8 * p, v);
+          store8_nt(to + CHUNK * CHUNK + r * CHUNK + 8 * p, v);
         }
       }
     }

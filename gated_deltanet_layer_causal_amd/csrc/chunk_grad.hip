@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
 #pragma unroll
     for (int j = 0; j < CHUNK * CHUNK / KKE / 512; ++j) {
       const int s = (j * 8 + wave) * 64 + lane;
-      copy_to_lds(buffer_of(src, bytes), sm.KK + (j * 8 + wave) * 64 * KKE, (uint32_t)s * 16u, 0);
+      copy_to_lds<CACHE_NT>(buffer_of(src, bytes), sm.KK + (j * 8 + wave) * 64 * KKE, (uint32_t)s * 16u, 0);
     }
   };
   // k_tl . k_s for s = 16 st + g4 .. + 3: block (tw, st), offset 4 lane
@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       for (int j = 0; j < TT::PIECES / (64 * NCW); ++j) {
         const int s = (j * NCW + wave) * 64 + lane, r = s / TT::RP;
         const uint32_t off = (uint32_t)(r < L ? r : L - 1) * ldb + (uint32_t)((s % TT::RP) ^ TT::swz(r)) * 16u;
-        copy_to_lds(rs, dst + (j * NCW + wave) * 64 * TT::EPP, off, 0);
+        copy_to_lds<CACHE_NT>(rs, dst + (j * NCW + wave) * 64 * TT::EPP, off, 0);
       }
     }
   };
@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
         const int s = (j * NCW + wave) * 64 + lane, r = s / TT::RP, q = (s % TT::RP) ^ TT::swz(r);
         const uint32_t off = (uint32_t)(q / PPB) * (uint32_t)(CHUNK * SBV * sizeof(T)) +
                              (uint32_t)(r < L ? r : L - 1) * (uint32_t)(SBV * sizeof(T)) + (uint32_t)(q % PPB) * 16u;
-        copy_to_lds(rs, dst + (j * NCW + wave) * 64 * TT::EPP, off, 0);
+        copy_to_lds<CACHE_NT>(rs, dst + (j * NCW + wave) * 64 * TT::EPP, off, 0);
       }
     }
   };
@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
       for (int j = 0; j < TI::PIECES / 512; ++j) {
         const int s = (j * 8 + wave) * 64 + lane, r = s / TI::RP;
         const uint32_t off = (uint32_t)(r * TI::RP + ((s % TI::RP) ^ TI::swz(r))) * 16u;
-        copy_to_lds(buffer_of(src, bytes), sm.Tin + (j * 8 + wave) * 64 * TI::EPP, off, 0);
+        copy_to_lds<CACHE_NT>(buffer_of(src, bytes), sm.Tin + (j * 8 + wave) * 64 * TI::EPP, off, 0);
       }
     }
   };
@@ -390,11 +390,11 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
     for (int st = 0; st < 4; ++st) {
       const uint32_t off = (uint32_t)(tl * CHUNK + acc_col<CT>(16 * st + g4)) * sizeof(CT);
       if constexpr (sizeof(CT) == 2) {
-        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, CACHE_NT));
         aop[2 * st] = w[0];
         aop[2 * st + 1] = w[1];
       } else {
-        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CACHE_NT));
 #pragma unroll
         for (int j = 0; j < 4; ++j) aop[4 * st + j] = w[j];
       }
