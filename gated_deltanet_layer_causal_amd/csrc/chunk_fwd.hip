@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     // wave writes whole 512-byte blocks.
     typename Compute<T>::type* ko = KKw + ((int64_t)c * (Hv / G) + kh) * CHUNK * CHUNK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store4_nt(ko + (4 * j + wave) * 256 + 4 * lane, kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
+    for (int j = 0; j < 4; ++j) store4(ko + (4 * j + wave) * 256 + 4 * lane, kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
   }
   {
     // Q rows (compute type, zero past the chunk end, columns in accumulator
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
       *reinterpret_cast<v4*>(ko + kr * CHUNK + acc_col<CT>(c4)) =
           *reinterpret_cast<const v4*>(&su.Kt[kr][c4]);
       if constexpr (BWD) {
-        store4_nt(Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4),
+        store4(Ktb + ((int64_t)c * (Hv / G) + kh) * D * CHUNK + kr * CHUNK + acc_col<T>(c4),
                to_f(su.Kt[kr][c4]), to_f(su.Kt[kr][c4 + 1]), to_f(su.Kt[kr][c4 + 2]),
                to_f(su.Kt[kr][c4 + 3]));
       }
@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
         if constexpr (SM::STAGE_P)
           store4(&Pts[s][acc_col<T>(rbase)], pv[0], pv[1], pv[2], pv[3]);
         else
-          store4_nt(PTout + s * CHUNK + acc_col<T>(rbase), pv[0], pv[1], pv[2], pv[3]);
+          store4(PTout + s * CHUNK + acc_col<T>(rbase), pv[0], pv[1], pv[2], pv[3]);
       }
       const int t = 16 * j + ccol;   // (= s: gam[t] is gsj)
 #pragma unroll
@@ -344,7 +344,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
       if constexpr (SM::STAGE_P)
         store4(&Ps[t][acc_col<CT>(rbase)], pv[0], pv[1], pv[2], pv[3]);
       else
-        store4_nt(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
+        store4(Pout + t * CHUNK + acc_col<CT>(rbase), pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();
     if constexpr (SM::STAGE_P) {

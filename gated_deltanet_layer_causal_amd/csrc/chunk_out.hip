@@ -355,13 +355,15 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     const float* gam = Gw + ch * CHUNK;
     const CT* Pc = Pw + ch * CHUNK * CHUNK;
     // ---- this head's inputs, requested up front: S slice, P rows, Delta rows
+    // (the S slice and Delta rows, read once, with the non-temporal hint; P is
+    // read by every quarter)
     uint4 hraw[NH];
     {
       const T* Sg = hst + ch * D * D + (int64_t)v0 * D;   // the quarter's block of the state
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const int i = lane + 64 * (2 * j + th), r = i / PPR, pc = i % PPR;
-        hraw[j] = *reinterpret_cast<const uint4*>(Sg + (int64_t)r * SBV + pc * EPP);
+        hraw[j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(Sg + (int64_t)r * SBV + pc * EPP)));
       }
     }
     cfrag pb[2][NSC];
@@ -377,7 +379,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = lane + 64 * j, r = 32 * th + i / PPR, pc = i % PPR;
-      draw[j] = buffer_frag<CT>(rd, (uint32_t)r * rdb + (uint32_t)(pc * 16));
+      draw[j] = buffer_frag<CT, CACHE_NT>(rd, (uint32_t)r * rdb + (uint32_t)(pc * 16));
     }
     float gm[2];
 #pragma unroll

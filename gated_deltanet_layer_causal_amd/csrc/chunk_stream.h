@@ -122,12 +122,12 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, uint32_t v
 }
 
 // 16-byte (16-bit types) or 4-byte (fp32) MFMA operand from a buffer.
-template <typename T>
+template <typename T, int AUX = 0>
 __device__ __forceinline__ typename Mma<T>::frag buffer_frag(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   if constexpr (sizeof(T) == 2)
-    return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX));
   else
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, AUX));
 }
 
 // Four consecutive elements of type T as floats / from floats, through a
@@ -141,13 +141,13 @@ __device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t rs, uint3
     return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
   }
 }
-template <typename T>
+template <typename T, int AUX = 0>
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t rs, uint32_t off, floatx4 x) {
   if constexpr (sizeof(T) == 2) {
     const u32x2 w = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3])};
-    __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, AUX);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, AUX);
   }
 }
 

@@ -160,9 +160,10 @@ template <typename T> __device__ __forceinline__ f8 raw_f8(const Raw8<T>& r) {
 }
 
 // The same 8-element loads and stores with the non-temporal hint, for global
-// data that a kernel streams through once.
+// data that a kernel streams through once.  Only for stores that write whole
+// 128-byte lines per wave: partial-line non-temporal stores measured several
+// times slower than plain ones.
 typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
 template <typename T>
 __device__ __forceinline__ f8 load8_nt(const T* p) {
   Raw8<T> r;
@@ -178,16 +179,6 @@ __device__ __forceinline__ void store8_nt(T* p, const f8& v) {
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(T) / 2); ++i)
     __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, r.v[i]), reinterpret_cast<nt_u32x4*>(p) + i);
-}
-template <typename T>
-__device__ __forceinline__ void store4_nt(T* p, float a, float b, float c, float d) {
-  if constexpr (sizeof(T) == 2) {
-    const nt_u32x2 w = {pack2<T>(a, b), pack2<T>(c, d)};
-    __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x2*>(p));
-  } else {
-    __builtin_nontemporal_store(nt_u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)},
-                                reinterpret_cast<nt_u32x4*>(p));
-  }
 }
 
 // ---- MFMA operand fragments -------------------------------------------------
