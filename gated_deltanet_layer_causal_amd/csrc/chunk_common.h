@@ -246,7 +246,8 @@ __device__ __forceinline__ void chunk_span(const int32_t* seq_off, const int32_t
 // tensor a is at sa + r * lda.  Every load is issued before the first store
 // (rows >= L re-read row L - 1, which is valid memory, and are zeroed where
 // stored), so their latencies overlap: a loop that stored each piece as it
-// arrived waited for every load in turn.
+// arrived waited for every load in turn.  The rows are read once, with the
+// non-temporal hint.
 template <typename TD, int W, typename TS>
 __device__ __forceinline__ void stage_rows2(TD* da, const TS* sa, int64_t lda, TD* db,
                                             const TS* sb, int64_t ldb, int ld_s, int L, int tid) {
@@ -263,8 +264,8 @@ __device__ __forceinline__ void stage_rows2(TD* da, const TS* sa, int64_t lda, T
       const uint4* pb = reinterpret_cast<const uint4*>(sb + (int64_t)rr * ldb + c8);
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        ra[j][q] = pa[q];
-        rb[j][q] = pb[q];
+        ra[j][q] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(pa) + q));
+        rb[j][q] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(pb) + q));
       }
     }
   }

@@ -193,10 +193,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     // a block at 4 (16 (c / 4) + r) + c % 4.  K K^T is symmetric, so this
     // lane's tile values k_{rbase+e} . k_s (s = 16 j + ccol) are row s,
     // columns rbase .. rbase + 3: block (j, wave), offset 4 lane + e -- each
-    // wave writes whole 512-byte blocks.
+    // wave writes whole 512-byte blocks (so the non-temporal hint is safe:
+    // it is slow only on stores of part of a line).
     typename Compute<T>::type* ko = KKw + ((int64_t)c * (Hv / G) + kh) * CHUNK * CHUNK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store4(ko + (4 * j + wave) * 256 + 4 * lane, kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
+    for (int j = 0; j < 4; ++j) store4_nt(ko + (4 * j + wave) * 256 + 4 * lane, kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
   }
   {
     // Q rows (compute type, zero past the chunk end, columns in accumulator
@@ -350,9 +351,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof
     if constexpr (SM::STAGE_P) {
       for (int i = tid; i < CHUNK * (CHUNK / 8); i += 256) {
         const int r = i >> 3, p = i & 7;
-        *reinterpret_cast<uint4*>(Pout + r * CHUNK + 8 * p) = *reinterpret_cast<const uint4*>(&Ps[r][8 * p]);
+        store16_nt(Pout + r * CHUNK + 8 * p, *reinterpret_cast<const uint4*>(&Ps[r][8 * p]));
         if constexpr (BWD)
-          *reinterpret_cast<uint4*>(PTout + r * CHUNK + 8 * p) = *reinterpret_cast<const uint4*>(&Pts[r][8 * p]);
+          store16_nt(PTout + r * CHUNK + 8 * p, *reinterpret_cast<const uint4*>(&Pts[r][8 * p]));
       }
       __syncthreads();  // the inverse overwrites the staging
     }

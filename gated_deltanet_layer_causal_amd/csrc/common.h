@@ -173,6 +173,21 @@ __device__ __forceinline__ f8 load8_nt(const T* p) {
   return raw_f8(r);
 }
 template <typename T>
+__device__ __forceinline__ void store4_nt(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+    const nt_u32x2 w = {pack2<T>(a, b), pack2<T>(c, d)};
+    __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x2*>(p));
+  } else {
+    __builtin_nontemporal_store(nt_u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)},
+                                reinterpret_cast<nt_u32x4*>(p));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store16_nt(T* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, v), reinterpret_cast<nt_u32x4*>(p));
+}
+template <typename T>
 __device__ __forceinline__ void store8_nt(T* p, const f8& v) {
   Raw8<T> r;
   store8(reinterpret_cast<T*>(&r.v[0]), v);
