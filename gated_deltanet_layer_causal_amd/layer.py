@@ -222,8 +222,12 @@ class GDNLayer:
     runs hipBLASLt on ROCm); everything between them is GDNCore, i.e. libgdn.
     in_proj is four products so that each core input is contiguous:
     x = X W_x^T (q | k | v channels), z = X W_z^T, a = X W_a^T, b = X W_b^T;
-    out_proj is Y = out W_out^T.  Weights are held transposed ([in, out]),
-    so every right operand is a contiguous matrix."""
+    out_proj is Y = out W_out^T.  Weights are held in both layouts, [out, in]
+    and [in, out], and each product takes the operand order that the library
+    runs fastest (measured at 65536 tokens, hidden 2560, bf16): the forward
+    as X (W)^T and dX as G (W^T)^T, i.e. the right operand a transposed view,
+    and dW as (X^T G)^T; 19.7 ms for the layer's fifteen products against
+    21.5 ms with contiguous right operands."""
 
     NAMES = ("x", "z", "a", "b", "out")
 
@@ -240,15 +244,15 @@ class GDNLayer:
         c = self.cfg
         T = X.shape[0]
         with _timed(timer, "in_proj"):
-            x = X @ self.Wt["x"]
-            z = (X @ self.Wt["z"]).view(T, c.hv, c.d)
-            a = X @ self.Wt["a"]
-            b = X @ self.Wt["b"]
+            x = X @ self.W["x"].t()
+            z = (X @ self.W["z"].t()).view(T, c.hv, c.d)
+            a = X @ self.W["a"].t()
+            b = X @ self.W["b"].t()
         f = self.core.forward(x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, S0=S0,
                               want_final=want_final, timer=timer)
         out = f["out"].view(T, c.hv * c.d)
         with _timed(timer, "out_proj"):
-            Y = out @ self.Wt["out"]
+            Y = out @ self.W["out"].t()
         f.update(x=x, z=z, a=a, b=b, Y=Y)
         return f
 
@@ -257,18 +261,19 @@ class GDNLayer:
         c = self.cfg
         T = X.shape[0]
         with _timed(timer, "out_proj_bwd"):
-            dout = (dY @ self.W["out"]).view(T, c.hv, c.d)
-            dW_out = dY.t() @ saved["out"].view(T, c.hv * c.d)
+            dout = (dY @ self.Wt["out"].t()).view(T, c.hv, c.d)
+            dW_out = (saved["out"].view(T, c.hv * c.d).t() @ dY).t()
         g = self.core.backward(saved, saved["x"], w_conv, saved["a"], saved["b"], A_log, dt_bias,
                                saved["z"], w_norm, cu_seqlens, dout, S0=S0, dS_final=dS_final,
                                timer=timer)
         with _timed(timer, "in_proj_bwd"):
             gz = g["dz"].view(T, c.hv * c.d)
-            dX = g["dx"] @ self.W["x"]
-            dX.addmm_(gz, self.W["z"])
-            dX.addmm_(g["da"], self.W["a"])
-            dX.addmm_(g["db"], self.W["b"])
-            dW = {"x": g["dx"].t() @ X, "z": gz.t() @ X, "a": g["da"].t() @ X, "b": g["db"].t() @ X,
-                  "out": dW_out}
+            dX = g["dx"] @ self.Wt["x"].t()
+            dX.addmm_(gz, self.Wt["z"].t())
+            dX.addmm_(g["da"], self.Wt["a"].t())
+            dX.addmm_(g["db"], self.Wt["b"].t())
+            Xt = X.t()
+            dW = {"x": (Xt @ g["dx"]).t(), "z": (Xt @ gz).t(), "a": (Xt @ g["da"]).t(),
+                  "b": (Xt @ g["db"]).t(), "out": dW_out}
         g.update(dX=dX, dW=dW, dout=dout)
         return g
