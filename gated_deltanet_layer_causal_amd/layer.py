@@ -220,8 +220,9 @@ class GDNLayer:
 
     The projections are plain GEMMs, left to the library (torch.matmul, which
     runs hipBLASLt on ROCm); everything between them is GDNCore, i.e. libgdn.
-    in_proj is four products so that each core input is contiguous:
-    x = X W_x^T (q | k | v channels), z = X W_z^T, a = X W_a^T, b = X W_b^T;
+    in_proj is three products so that each core input is contiguous:
+    x = X W_x^T (q | k | v channels), z = X W_z^T and [a | b] = X [W_a | W_b]^T
+    (a and b, hv columns each, are then copied apart);
     out_proj is Y = out W_out^T.  Weights are held in both layouts, [out, in]
     and [in, out], and each product takes the operand order that the library
     runs fastest (measured at 65536 tokens, hidden 2560, bf16): the forward
@@ -236,8 +237,11 @@ class GDNLayer:
         self.core = GDNCore(cfg, device)
         self.cfg = cfg
         self.hidden = hidden
-        self.Wt = {k: weights[k].t().contiguous() for k in self.NAMES}   # [in, out]
         self.W = {k: weights[k].contiguous() for k in self.NAMES}        # [out, in]
+        # a and b (hv outputs each) as one product, so that X is read once for
+        # both and the gradients make one pass each
+        self.W["ab"] = torch.cat([self.W["a"], self.W["b"]], 0)
+        self.Wt = {k: w.t().contiguous() for k, w in self.W.items()}      # [in, out]
 
     def forward(self, X, w_conv, A_log, dt_bias, w_norm, cu_seqlens, S0=None, want_final=False,
                 timer=None):
@@ -246,8 +250,9 @@ class GDNLayer:
         with _timed(timer, "in_proj"):
             x = X @ self.W["x"].t()
             z = (X @ self.W["z"].t()).view(T, c.hv, c.d)
-            a = X @ self.W["a"].t()
-            b = X @ self.W["b"].t()
+            ab = X @ self.W["ab"].t()
+            a = ab[:, :c.hv].contiguous()
+            b = ab[:, c.hv:].contiguous()
         f = self.core.forward(x, w_conv, a, b, A_log, dt_bias, z, w_norm, cu_seqlens, S0=S0,
                               want_final=want_final, timer=timer)
         out = f["out"].view(T, c.hv * c.d)
@@ -270,10 +275,11 @@ class GDNLayer:
             gz = g["dz"].view(T, c.hv * c.d)
             dX = g["dx"] @ self.Wt["x"].t()
             dX.addmm_(gz, self.Wt["z"].t())
-            dX.addmm_(g["da"], self.Wt["a"].t())
-            dX.addmm_(g["db"], self.Wt["b"].t())
+            dab = torch.cat([g["da"], g["db"]], 1)
+            dX.addmm_(dab, self.Wt["ab"].t())
             Xt = X.t()
-            dW = {"x": (Xt @ g["dx"]).t(), "z": (Xt @ gz).t(), "a": (Xt @ g["da"]).t(),
-                  "b": (Xt @ g["db"]).t(), "out": dW_out}
+            dW_ab = (Xt @ dab).t()
+            dW = {"x": (Xt @ g["dx"]).t(), "z": (Xt @ gz).t(), "a": dW_ab[:c.hv], "b": dW_ab[c.hv:],
+                  "out": dW_out}
         g.update(dX=dX, dW=dW, dout=dout)
         return g
