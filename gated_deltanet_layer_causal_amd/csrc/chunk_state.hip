@@ -166,14 +166,15 @@ __global__ void __launch_bounds__((StateBuf<T, D, NW, MODE>::KR ? 128 * NW : 64 
     {
       const uint32_t ldb = (uint32_t)(ldv * sizeof(T));
       // (identity-row blocks copy the value rows of block vb - D / BV, which
-      // stay unused: their compute takes zero values)
+      // stay unused: their compute takes zero values); the block's value rows
+      // are read by this workgroup alone, so with the non-temporal hint
       const auto rs = buffer_of(v + t0 * ldv + (int64_t)h * D + (phi ? v0 - D : v0), (uint32_t)Lc * ldb);
 #pragma unroll
       for (int j = 0; j < TV::PIECES / THREADS; ++j) {
         const int s = (j * NW + wave) * 64 + lane, r = s / TV::RP;
         const uint32_t off = (uint32_t)(r < Lc ? r : Lc - 1) * ldb +
                              (uint32_t)((s % TV::RP) ^ TV::swz(r)) * 16u;
-        copy_to_lds(rs, B.V + (j * NW + wave) * 64 * TV::EPP, off, 0);
+        copy_to_lds<CACHE_NT>(rs, B.V + (j * NW + wave) * 64 * TV::EPP, off, 0);
       }
     }
     // Gam and dec, 64 floats each: one copy per wave with two waves, so that
