@@ -417,8 +417,13 @@ __global__ void __launch_bounds__(512, 1) chunk_grad_kernel(
 #pragma unroll
     for (int p = 0; p < NSD; ++p) {
       const int64_t e = r + blk_at(16 * kt + c16, pcol(p), D);
-      hA[p] = rdf(hst + e, 0);
-      dhA[p] = rdf(dhst + e, 0);
+      if constexpr (KS == 4) {
+        hA[p] = rdf(hst + e, 0);
+        dhA[p] = rdf(dhst + e, 0);
+      } else {   // read once, a kilobyte of whole lines per wave: non-temporal
+        hA[p] = __builtin_nontemporal_load(reinterpret_cast<const frag*>(hst + e));
+        dhA[p] = __builtin_nontemporal_load(reinterpret_cast<const frag*>(dhst + e));
+      }
     }
   };
   auto load_a = [&](const Item& it, int h, bool live) __attribute__((always_inline)) {
