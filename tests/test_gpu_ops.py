@@ -27,6 +27,12 @@ CASES = {
     "fp16_g2_mild": (2, 4, 128, "fp16", [150, 64, 1, 90], (0.01, 0.1), True),
     "fp16_d32": (2, 4, 32, "fp16", [129, 64, 2], (0.05, 0.5), True),
 }
+# conv only: 3 k-heads of 128 put the end of the q and k channels (768) inside
+# the second 512-channel block, so one launch runs every L2 mode of the conv
+# kernels (all lanes normalise, some do, none do)
+CONV_EXTRA = {
+    "bf16_l2mix": (3, 3, 128, "bf16", [150, 3, 70], (0.01, 0.1), False),
+}
 
 
 def _tol(dtype, grad=False):
@@ -50,7 +56,7 @@ def _gdt(dtype):
 
 
 def _case(name, seed=7):
-    hk, hv, d, dtype, lens, A_range, state = CASES[name]
+    hk, hv, d, dtype, lens, A_range, state = CASES[name] if name in CASES else CONV_EXTRA[name]
     w = gi.Workload(name, sum(lens), hk, hv, d, dtype, seq="varlen", init_state=state,
                     final_state=state, seed=seed)
     inp = gi.make_inputs(w, seqlens=lens, A_range=A_range)
@@ -62,7 +68,7 @@ def _shape(w, inp):
 
 
 # ------------------------------------------------------------------ conv
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name", list(CASES) + list(CONV_EXTRA))
 def test_conv_fwd_bwd(name):
     w, inp = _case(name)
     dt = w.dtype
